@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""NSA forward benchmark on one MI355X (gfx950).
+
+One step = one nsa_fwd_prefill call over the 64k workload (batch 1, 65536
+tokens, 64 query heads in 4 KV groups, head_dim 128, blocks of 64, top-k 16,
+window 512; bf16), the pages' 64k setting (NSA how-to, qwbw.cn/news/106443,
+section 3). Inputs are seeded synthetic tensors already resident in HBM.
+
+Prints ONE JSON line: tokens/s for prefill (the headline value), a roofline
+object for the dominant kernel (algorithmic FLOPs over its HIP-event-timed
+duration against the bf16 dense MFMA peak), the decode workload (64
+sequences x 65536-token cache) as achieved HBM bandwidth, and the float64
+CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+PREFILL_STAGES = ["k_prep", "k_cmp", "k_sw"]
+DECODE_STAGES = ["k_dec_scan", "k_dec_select", "k_dec_sel", "k_dec_combine"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- algorithmic work
+
+def pair_counts(L: int, block: int, top_k: int, window: int):
+    """(query, key) pairs per head of one sequence for each branch, from the
+    causal definitions: compressed floor((t+1)/l); selected the own block's
+    t mod l + 1 tokens plus min(n-1, t//l) full earlier blocks; window
+    min(t+1, w)."""
+    t = np.arange(L, dtype=np.int64)
+    cmp = int(((t + 1) // block).sum())
+    slc = int(((t % block) + 1 + block * np.minimum(top_k - 1, t // block)).sum())
+    win = int(np.minimum(t + 1, window).sum())
+    return cmp, slc, win
+
+
+def prefill_flops(cfg):
+    cmp, slc, win = pair_counts(cfg.seqlen, cfg.block, cfg.top_k, cfg.window)
+    per_pair = cfg.batch * cfg.n_q_heads * 4 * cfg.head_dim  # QK^T + PV
+    return {"cmp": cmp * per_pair, "slc": slc * per_pair, "win": win * per_pair}
+
+
+def decode_unique_bytes(cfg, idx: np.ndarray, lens: np.ndarray) -> int:
+    """Bytes the decode step must touch: block-mean cache, selected blocks
+    (tokens inside the window counted once), window, q, gates, out, idx."""
+    D, G, Hq, el = cfg.head_dim, cfg.n_kv_heads, cfg.n_q_heads, 2
+    total = 0
+    for b in range(cfg.batch):
+        s = int(lens[b])
+        t = s - 1
+        wlo = max(0, s - cfg.window)
+        nvis = s // cfg.block
+        for g in range(G):
+            toks = set(range(wlo, s))
+            for j in idx[b, g]:
+                if 0 <= j <= t // cfg.block:
+                    toks.update(range(j * cfg.block, min(j * cfg.block + cfg.block, s)))
+            total += (nvis * D * 2 + len(toks) * D * 2) * el
+        total += Hq * D * el * 2 + Hq * 3 * el + G * cfg.top_k * 4
+    return total
+
+
+# ---------------------------------------------------------------- HIP events
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime already loaded by torch."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e)
+        self.arr = (ctypes.c_void_p * n)(*[e.value for e in self.ev])
+
+    def array(self, first: int, count: int):
+        return ctypes.cast(ctypes.byref(self.arr, first * ctypes.sizeof(ctypes.c_void_p)),
+                           ctypes.POINTER(ctypes.c_void_p))
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+# ---------------------------------------------------------------- traffic from committed counters
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_sparse_fwd_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
+    if taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_digest:\s*(\w+)", text)
+    if not m or m.group(1) != kernel_source_digest():
+        return None
+    m = re.search(rf"traffic_bytes_per_launch\s+{kernel}:\s*([0-9.eE+]+)", text)
+    return float(m.group(1)) if m else None
+
+
+# ---------------------------------------------------------------- CPU oracle baseline
+
+class _LazyBf16:
+    def __init__(self, arr):
+        self.arr, self.shape = arr, arr.shape
+
+    def __getitem__(self, key):
+        from long_context_sparse_fwd_amd import inputs
+        return inputs.bf16_bits_to_f32(self.arr[key])
+
+
+def cpu_baseline(cfg, raw, seconds: float):
+    """The float64 oracle on evenly spaced query rows of the same workload."""
+    from oracle import nsa_ref
+    try:
+        ncores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        ncores = os.cpu_count() or 1
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=ncores)
+    except Exception:  # pragma: no cover
+        limiter = None
+    lz = {n: _LazyBf16(raw[n]) for n in raw}
+
+    def run(rows):
+        t0 = time.perf_counter()
+        nsa_ref.prefill(lz["q"], lz["k"], lz["v"], lz["gates"], block=cfg.block, top_k=cfg.top_k,
+                        window=cfg.window, rows=rows)
+        return time.perf_counter() - t0
+
+    L = cfg.seqlen
+    probe = run(np.linspace(0, L - 1, 4).astype(np.int64))
+    n_rows = int(max(8, min(4096, 4 * (seconds - probe) / max(probe, 1e-3))))
+    rows = np.linspace(0, L - 1, n_rows).astype(np.int64)
+    dt = run(rows)
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    return {"value": n_rows * cfg.batch / dt, "unit": "tokens/s", "cores": ncores, "kind": "oracle",
+            "sample": f"{n_rows} evenly spaced query rows of the {cfg.name} workload (full "
+                      f"{L}-token context, all {cfg.n_q_heads} heads), float64 numpy, {dt:.1f} s"}
+
+
+# ---------------------------------------------------------------- benchmark legs
+
+def bench_prefill(cfg, steps, warmup, torch, inputs, nsa):
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    raw = inputs.make_prefill_inputs(cfg)
+    log(f"[bench] inputs {cfg.name} generated in {time.perf_counter() - t0:.1f} s")
+    up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v, g = (up(raw[n]) for n in ("q", "k", "v", "gates"))
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    nbytes = nsa.prefill_workspace_bytes(q, k, v, g, out, top_k=cfg.top_k, window=cfg.window)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    call = lambda: nsa.prefill(q, k, v, g, top_k=cfg.top_k, window=cfg.window, out=out, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    log(f"[bench] prefill {cfg.name}: {wall_ms:.3f} ms/step over {steps} steps")
+
+    # per-kernel durations: the timed entry point records HIP events on the stream
+    ns = len(PREFILL_STAGES) + 1
+    ev = HipEvents(ns * steps)
+    desc = nsa.prefill_desc(q, k, v, g, out)
+    params = nsa.make_params(cfg.top_k, cfg.window)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    for i in range(steps):
+        nsa.check(nsa.lib().nsa_fwd_prefill_timed(
+            ctypes.byref(desc), ctypes.byref(params), ctypes.c_void_p(q.data_ptr()),
+            ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(g.data_ptr()),
+            ctypes.c_void_p(out.data_ptr()), None, nsa.NSA_IDX_COMPUTE, ctypes.c_void_p(ws.data_ptr()),
+            ws.numel(), stream, ev.array(i * ns, ns)))
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([ev.elapsed_ms(i * ns + s, i * ns + s + 1) for i in range(steps)]))
+                for s, name in enumerate(PREFILL_STAGES)}
+    ev.close()
+    return raw, wall_ms, stage_ms
+
+
+def bench_decode(cfg, steps, warmup, torch, inputs, nsa):
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    raw = inputs.make_decode_inputs(cfg)
+    log(f"[bench] inputs {cfg.name} generated in {time.perf_counter() - t0:.1f} s")
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    q, g = up(raw["q"]), up(raw["gates"])
+    kc = up(raw["k_cache"])
+    vc = up(raw["v_cache"])
+    del raw["k_cache"], raw["v_cache"]
+    lens = torch.from_numpy(raw["seqlens"]).to(dev)
+    kb, vb = nsa.compress_kv(kc, vc)        # the block-mean cache, built by the library
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((cfg.batch, cfg.n_kv_heads, cfg.top_k), dtype=torch.int32, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)   # > the 256 MB Infinity Cache
+    call = lambda: nsa.decode(q, kc, vc, kb, vb, lens, g, top_k=cfg.top_k, window=cfg.window, out=out,
+                              idx=idx)
+    for _ in range(warmup):
+        call()
+    ns = len(DECODE_STAGES) + 1
+    ev = HipEvents(ns * steps)
+    desc = nsa.decode_desc(q, kc, vc, kb, vb, g, out)
+    params = nsa.make_params(cfg.top_k, cfg.window)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    nbytes = ctypes.c_size_t()
+    nsa.check(nsa.lib().nsa_decode_workspace_bytes(ctypes.byref(desc), ctypes.byref(params), ctypes.byref(nbytes)))
+    ws = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    for i in range(steps):
+        flush.zero_()                          # evict the previous step's data from the caches
+        nsa.check(nsa.lib().nsa_fwd_decode_timed(
+            ctypes.byref(desc), ctypes.byref(params), P(q), P(kc), P(vc), P(kb), P(vb), P(lens), P(g),
+            P(out), P(idx), nsa.NSA_IDX_COMPUTE, P(ws), ws.numel(), stream, ev.array(i * ns, ns)))
+    torch.cuda.synchronize()
+    step_ms = [ev.elapsed_ms(i * ns, i * ns + ns - 1) for i in range(steps)]
+    stage_ms = {name: float(np.mean([ev.elapsed_ms(i * ns + s, i * ns + s + 1) for i in range(steps)]))
+                for s, name in enumerate(DECODE_STAGES)}
+    ev.close()
+    ubytes = decode_unique_bytes(cfg, idx.cpu().numpy(), raw["seqlens"])
+    ms = float(np.median(step_ms))
+    gbps = ubytes / (ms * 1e-3) / 1e9
+    log(f"[bench] decode {cfg.name}: {ms * 1e3:.1f} us/step, {gbps:.0f} GB/s")
+    return {"workload": cfg.name, "ms_per_step": ms, "step_ms_samples": step_ms,
+            "sequences_per_s": cfg.batch / (ms * 1e-3), "unique_bytes_per_step": ubytes,
+            "achieved_GBps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS, "kernels_ms": stage_ms,
+            "cache_flush": "1 GiB write between steps"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="p64k", choices=["p8k", "p32k", "p64k"])
+    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the NSA path here is single-GPU; sharding is described in the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from long_context_sparse_fwd_amd import inputs, nsa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    nsa.lib()
+    cfg = inputs.CONFIGS[args.config]
+    raw, wall_ms, stage_ms = bench_prefill(cfg, args.steps, args.warmup, torch, inputs, nsa)
+    fl = prefill_flops(cfg)
+    total_fl = sum(fl.values())
+    tokens_per_s = cfg.batch * cfg.seqlen / (wall_ms * 1e-3)
+
+    kernel_flops = {"k_cmp": fl["cmp"], "k_sw": fl["slc"] + fl["win"]}
+    dominant = max(stage_ms, key=stage_ms.get)
+    if dominant in kernel_flops:
+        achieved = kernel_flops[dominant] / (stage_ms[dominant] * 1e-3) / 1e12
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": committed_traffic(dominant, cfg.name),
+                "work_per_launch": kernel_flops[dominant], "avg_launch_ms": stage_ms[dominant]}
+    else:
+        prep_bytes = 4 * cfg.batch * cfg.seqlen * cfg.n_kv_heads * cfg.head_dim * 2
+        achieved = prep_bytes / (stage_ms[dominant] * 1e-3) / 1e9
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                "traffic": committed_traffic(dominant, cfg.name),
+                "work_per_launch": prep_bytes, "avg_launch_ms": stage_ms[dominant]}
+
+    result = {
+        "metric": "NSA fwd prefill tokens/s & MFMA % peak at 64k; decode HBM GB/s % peak",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v, sigmoid(N(0,1)) gates)",
+        "config": {"workload": f"nsa_prefill_{cfg.name}", "batch": cfg.batch, "seqlen": cfg.seqlen,
+                   "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
+                   "compress_block_size": cfg.block, "select_block_size": cfg.block,
+                   "select_top_k": cfg.top_k, "sliding_window": cfg.window},
+        "roofline": roof,
+        "prefill": {"tflops": total_fl / (wall_ms * 1e-3) / 1e12,
+                    "mfma_frac": total_fl / (wall_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                    "algorithmic_flops": fl, "kernels_ms": stage_ms},
+    }
+    if not args.no_decode:
+        result["decode"] = bench_decode(inputs.CONFIGS["d64k"], args.decode_steps, 3, torch, inputs, nsa)
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(cfg, raw, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

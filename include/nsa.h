@@ -1,0 +1,224 @@
+/*
+ * nsa.h -- C ABI of libnsa, a Native Sparse Attention (NSA) forward library
+ * for one AMD Instinct MI355X (gfx950).
+ *
+ * The method: attention split into three parallel branches whose outputs are
+ * merged by per-head gates -- a compressed branch (coarse, over block
+ * summaries of the keys and values), a selected branch (fine-grained, over the
+ * key blocks a query ranks highest) and a sliding-window branch (the most
+ * recent tokens). NSA how-to (qwbw.cn/news/106443), section 1; its
+ * parameters are the [model.nsa] fields of section 3 of the same page:
+ * compress_block_size, select_block_size, select_top_k, sliding_window and a
+ * learned gate (here: gate values passed in as a tensor).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor arguments are DEVICE pointers owned by the caller; the library
+ *    never allocates device memory, never frees, keeps no state between calls
+ *    and never synchronises. Scratch memory is the caller's `workspace`, sized
+ *    by the matching *_workspace_bytes call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls enqueue their kernels on it and return; results are ready when the
+ *    stream reaches that point.
+ *  - Arguments are validated on the host before anything is enqueued. On any
+ *    error nothing is launched, nothing is written, and a status code is
+ *    returned; nsa_last_error() then holds a message (per calling thread).
+ *    There is no silent fallback (no dense path, no clamping).
+ *  - Strides are in ELEMENTS; the head dimension is always contiguous.
+ *  - Element types: in_dtype applies to q, k, v, caches and gates; out_dtype
+ *    to out. Supported: (bf16 in, bf16 out), (bf16 in, f32 out),
+ *    (f32 in, f32 out). Block summaries and matrix products use the input
+ *    type as operands with fp32 accumulation; softmax, block scores, top-k and
+ *    the gate combination run in fp32.
+ *  - Supported geometry: compress_block_size == select_block_size == 64;
+ *    head_dim in {64, 128}; n_q_heads a multiple of n_kv_heads with at most 16
+ *    query heads per KV head; 1 <= select_top_k <= 64; sliding_window >= 1;
+ *    any seqlen >= 1 (a trailing partial block is allowed).
+ *  - Query head h reads KV head h / (n_q_heads / n_kv_heads).
+ *  - Calls are reentrant; two calls that share a workspace or an output
+ *    buffer must be ordered by the caller.
+ */
+#ifndef NSA_H
+#define NSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NSA_OK = 0,
+  NSA_ERR_INVALID_ARGUMENT = 1,    /* null pointer, bad size, bad stride, ... */
+  NSA_ERR_UNSUPPORTED = 2,         /* valid NSA geometry this build does not run */
+  NSA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the required size */
+  NSA_ERR_HIP = 4                  /* a HIP launch reported an error */
+} nsa_status_t;
+
+typedef enum { NSA_F32 = 0, NSA_BF16 = 1 } nsa_dtype_t;
+
+typedef enum {
+  NSA_IDX_COMPUTE = 0, /* select blocks; write them to idx when idx != NULL */
+  NSA_IDX_INJECT = 1   /* read the selection from idx; no selection is run */
+} nsa_idx_mode_t;
+
+/* The [model.nsa] parameters of the NSA how-to (qwbw.cn/news/106443), section 3. */
+typedef struct {
+  int32_t compress_block_size; /* l: tokens per compressed block; stride l, no overlap */
+  int32_t select_block_size;   /* l': tokens per selectable block; must equal l */
+  int32_t select_top_k;        /* n: blocks each query attends to, its own block included */
+  int32_t sliding_window;      /* w: window length in tokens, the query itself included */
+  float softmax_scale;         /* <= 0 selects 1/sqrt(head_dim); used by all three branches */
+} nsa_params_t;
+
+/*
+ * Prefill: every position t of every sequence is a query that attends
+ * causally within its own sequence.
+ *   q     [B, L, Hq, D]  strides q_stride  = (b, t, head)
+ *   k, v  [B, L, G,  D]  strides k_stride, v_stride = (b, t, kv head)
+ *   gates [B, L, Hq, 3]  strides g_stride  = (b, t, head); the three values
+ *                        (compressed, selected, window) are contiguous and are
+ *                        used as given (already through their sigmoid).
+ *   out   [B, L, Hq, D]  strides o_stride  = (b, t, head)
+ *   idx   [B, L, G, n]   int32, dense row-major (no strides).
+ */
+typedef struct {
+  int32_t batch, seqlen, n_q_heads, n_kv_heads, head_dim;
+  nsa_dtype_t in_dtype, out_dtype;
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t g_stride[3];
+  int64_t o_stride[3];
+} nsa_prefill_desc_t;
+
+/*
+ * Decode: one new query per sequence b, at position seqlens[b]-1, whose K/V
+ * are already in the caches.
+ *   q        [B, Hq, D]          strides q_stride  = (b, head)
+ *   k_cache, v_cache [B, G, max_seqlen, D]  strides (b, kv head, t)
+ *   kc_cache, vc_cache [B, G, max_blocks, D] strides (b, kv head, j): entry j
+ *            holds the mean of cache tokens [j*l, j*l+l) (see nsa_compress_kv);
+ *            entries j < seqlens[b]/l are read, as given.
+ *   seqlens  [B] int32 DEVICE array; each value must lie in [1, max_seqlen].
+ *            A sequence with a value outside that range gets out = 0 and idx
+ *            = -1 and no cache entry of it is read.
+ *   gates    [B, Hq, 3]          strides g_stride = (b, head)
+ *   out      [B, Hq, D]          strides o_stride = (b, head)
+ *   idx      [B, G, n]           int32, dense row-major.
+ */
+typedef struct {
+  int32_t batch, max_seqlen, max_blocks, n_q_heads, n_kv_heads, head_dim;
+  nsa_dtype_t in_dtype, out_dtype;
+  int64_t q_stride[2];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t kc_stride[3];
+  int64_t vc_stride[3];
+  int64_t g_stride[2];
+  int64_t o_stride[2];
+} nsa_decode_desc_t;
+
+/* Required workspace size in bytes for a prefill / decode call with these
+ * arguments (idx presence does not matter: the bound covers both).
+ * Returns NSA_OK and writes *bytes, or an error status (see conventions). */
+nsa_status_t nsa_prefill_workspace_bytes(const nsa_prefill_desc_t* desc,
+                                         const nsa_params_t* params, size_t* bytes);
+nsa_status_t nsa_decode_workspace_bytes(const nsa_decode_desc_t* desc,
+                                        const nsa_params_t* params, size_t* bytes);
+
+/*
+ * NSA forward over whole sequences.
+ *
+ * Computes, for each (b, t, head h in KV group g):
+ *   compressed: softmax attention over the means of the key/value blocks
+ *               [j*l, j*l+l) that lie wholly at or before t (none -> 0);
+ *   selection:  block scores = compressed-attention probabilities summed over
+ *               the query heads of group g; the chosen set is the own block
+ *               t/l plus the n-1 best-scoring blocks before it (ties to the
+ *               lower index; fewer candidates -> all of them). The set is
+ *               shared by the group. The score -> top-k -> gather dataflow
+ *               is the selector described in the NSA factory write-up
+ *               (chencunli.com, "DeepSeek NSA on the Siemens 840D manual"),
+ *               section "What dynamic sparsity actually sparsifies";
+ *   selected:   softmax attention over the tokens of the chosen blocks at or
+ *               before t;
+ *   window:     softmax attention over tokens [max(0, t-w+1), t];
+ *   out = g_cmp*compressed + g_slc*selected + g_win*window.
+ *
+ * idx_mode NSA_IDX_COMPUTE: the selection is computed; if idx != NULL it is
+ *   written there, each row ascending and padded with -1.
+ * idx_mode NSA_IDX_INJECT: idx (required) supplies the selection. Entries
+ *   outside [0, t/l] are skipped, duplicates count twice, and a row with no
+ *   usable entry gives a selected-branch output of 0.
+ * `out` is also used as scratch while the call runs.
+ */
+nsa_status_t nsa_fwd_prefill(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                             const void* q, const void* k, const void* v, const void* gates,
+                             void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * NSA forward for one new token per sequence over a KV cache and a block
+ * cache (the decode phase, measured apart from prefill as the NSA how-to
+ * advises, section 5). Same arithmetic as one prefill row at t = seqlens[b]-1;
+ * idx/idx_mode as for prefill, idx shaped [B, G, n].
+ */
+nsa_status_t nsa_fwd_decode(const nsa_decode_desc_t* desc, const nsa_params_t* params,
+                            const void* q, const void* k_cache, const void* v_cache,
+                            const void* kc_cache, const void* vc_cache, const int32_t* seqlens,
+                            const void* gates, void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Block compression used by both phases: kc[b, g, j] = mean of k[b, g, t] over
+ * t in [j*block_size, (j+1)*block_size), for j < n_tokens / block_size (only
+ * complete blocks), and the same for v -> vc. Summation in fp32, one rounding
+ * to dtype. k, v are [B, G, n_tokens, D] with strides (b, kv head, t); kc, vc
+ * [B, G, n_tokens/block_size, D] with strides (b, kv head, j). block_size must
+ * be 64. Writes nothing when n_tokens < block_size.
+ */
+nsa_status_t nsa_compress_kv(int32_t batch, int32_t n_kv_heads, int32_t n_tokens,
+                             int32_t head_dim, nsa_dtype_t dtype, int32_t block_size,
+                             const void* k, const int64_t k_stride[3],
+                             const void* v, const int64_t v_stride[3],
+                             void* kc, const int64_t kc_stride[3],
+                             void* vc, const int64_t vc_stride[3], void* stream);
+
+/*
+ * Timed variants, for per-kernel measurement. Identical to nsa_fwd_prefill /
+ * nsa_fwd_decode, and additionally record caller-created hipEvent_t handles
+ * (passed as void*) on the stream: before each of the call's kernels and
+ * after the last one. Prefill runs 3 kernels (block compression + re-layout;
+ * compressed branch + block selection; selected + window branches + gate
+ * combination), so stage_events holds 4 events; decode runs 4 kernels
+ * (compressed and window chunks; selection; selected chunks; combination),
+ * so it holds 5. A NULL array or entry is NSA_ERR_INVALID_ARGUMENT.
+ */
+nsa_status_t nsa_fwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                                   const void* q, const void* k, const void* v, const void* gates,
+                                   void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   void* const* stage_events);
+nsa_status_t nsa_fwd_decode_timed(const nsa_decode_desc_t* desc, const nsa_params_t* params,
+                                  const void* q, const void* k_cache, const void* v_cache,
+                                  const void* kc_cache, const void* vc_cache,
+                                  const int32_t* seqlens, const void* gates, void* out,
+                                  int32_t* idx, nsa_idx_mode_t idx_mode, void* workspace,
+                                  size_t workspace_bytes, void* stream, void* const* stage_events);
+
+/* Static name of a status code. */
+const char* nsa_status_string(nsa_status_t status);
+
+/* Message describing the last failing call on this thread ("" if none). */
+const char* nsa_last_error(void);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int32_t nsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSA_H */

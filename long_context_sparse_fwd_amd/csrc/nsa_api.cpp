@@ -1,0 +1,469 @@
+// Host side of libnsa: argument validation, workspace layout and the launch
+// sequence of each entry point. Every check runs before anything is
+// enqueued; a failing call launches nothing and writes nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "nsa.h"
+#include "nsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+nsa_status_t fail(nsa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+nsa_status_t ok() {
+  g_last_error.clear();
+  return NSA_OK;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dtype_ok(nsa_dtype_t d) { return d == NSA_F32 || d == NSA_BF16; }
+
+nsa_status_t check_params(const nsa_params_t* p, int head_dim) {
+  if (p == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "params is NULL");
+  if (p->compress_block_size < 1 || p->select_block_size < 1)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "block sizes must be >= 1 (got %d, %d)",
+                p->compress_block_size, p->select_block_size);
+  if (p->select_top_k < 1)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "select_top_k must be >= 1 (got %d)", p->select_top_k);
+  if (p->sliding_window < 1)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "sliding_window must be >= 1 (got %d)", p->sliding_window);
+  if (!std::isfinite(p->softmax_scale))
+    return fail(NSA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
+  if (p->compress_block_size != nsa::kBlock || p->select_block_size != nsa::kBlock)
+    return fail(NSA_ERR_UNSUPPORTED, "only compress_block_size == select_block_size == 64 is supported "
+                                     "(got %d, %d)", p->compress_block_size, p->select_block_size);
+  if (p->select_top_k > 64)
+    return fail(NSA_ERR_UNSUPPORTED, "select_top_k > 64 is not supported (got %d)", p->select_top_k);
+  (void)head_dim;
+  return NSA_OK;
+}
+
+nsa_status_t check_heads(int hq, int g, int d) {
+  if (hq < 1 || g < 1 || d < 1)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "n_q_heads, n_kv_heads, head_dim must be >= 1");
+  if (hq % g != 0)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", hq, g);
+  if (hq / g > 16)
+    return fail(NSA_ERR_UNSUPPORTED, "more than 16 query heads per KV head (%d) is not supported", hq / g);
+  if (d != 64 && d != 128)
+    return fail(NSA_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", d);
+  return NSA_OK;
+}
+
+nsa_status_t check_dtypes(nsa_dtype_t in, nsa_dtype_t out) {
+  if (!dtype_ok(in) || !dtype_ok(out)) return fail(NSA_ERR_INVALID_ARGUMENT, "unknown dtype");
+  if (in == NSA_F32 && out == NSA_BF16)
+    return fail(NSA_ERR_UNSUPPORTED, "f32 input with bf16 output is not supported");
+  return NSA_OK;
+}
+
+nsa_status_t check_strides(const char* name, const int64_t* s, int n, bool vec8) {
+  for (int i = 0; i < n; ++i) {
+    if (s[i] < 0) return fail(NSA_ERR_INVALID_ARGUMENT, "%s stride[%d] is negative", name, i);
+    if (vec8 && (s[i] % 8) != 0)
+      return fail(NSA_ERR_INVALID_ARGUMENT, "%s stride[%d] = %lld is not a multiple of 8 elements",
+                  name, i, static_cast<long long>(s[i]));
+  }
+  return NSA_OK;
+}
+
+nsa_status_t check_ptr(const char* name, const void* p, bool need16) {
+  if (p == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (need16 && !aligned16(p)) return fail(NSA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  return NSA_OK;
+}
+
+#define NSA_TRY(expr)              \
+  do {                             \
+    nsa_status_t st_ = (expr);     \
+    if (st_ != NSA_OK) return st_; \
+  } while (0)
+
+// ------------------------------------------------------------------ prefill
+
+struct PrefillPlan {
+  int Nb, Nc, NcT, cmp_waves, cmp_tiles, sw_tiles;
+  size_t off_kt, off_vt, off_kct, off_vct, off_idx, total;
+};
+
+nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, PrefillPlan* pl) {
+  if (d == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->batch < 0 || d->seqlen < 0)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "batch and seqlen must be >= 0");
+  NSA_TRY(check_heads(d->n_q_heads, d->n_kv_heads, d->head_dim));
+  NSA_TRY(check_dtypes(d->in_dtype, d->out_dtype));
+  NSA_TRY(check_params(p, d->head_dim));
+  NSA_TRY(check_strides("q", d->q_stride, 3, true));
+  NSA_TRY(check_strides("k", d->k_stride, 3, true));
+  NSA_TRY(check_strides("v", d->v_stride, 3, true));
+  NSA_TRY(check_strides("gates", d->g_stride, 3, false));
+  NSA_TRY(check_strides("out", d->o_stride, 3, true));
+  const int64_t B = d->batch, L = d->seqlen, G = d->n_kv_heads, D = d->head_dim;
+  if (B * L * d->n_q_heads > INT32_MAX || B * L * G * p->select_top_k > INT32_MAX ||
+      B * G * ((L + 63) / 64) * 64 > INT32_MAX)
+    return fail(NSA_ERR_UNSUPPORTED, "problem too large for 32-bit work indexing");
+  pl->Nb = static_cast<int>((L + 63) / 64);
+  pl->Nc = static_cast<int>(L / 64);
+  pl->NcT = (pl->Nc + 63) / 64;
+  pl->cmp_waves = 0;
+  for (int w = 4; w >= 1; w /= 2)
+    if (nsa::cmp_lds_bytes(w, pl->NcT) <= static_cast<size_t>(nsa::kMaxLds)) {
+      pl->cmp_waves = w;
+      break;
+    }
+  if (pl->cmp_waves == 0)
+    return fail(NSA_ERR_UNSUPPORTED, "seqlen %lld needs more LDS for block scores than a CU has",
+                static_cast<long long>(L));
+  const int64_t tok_cmp = static_cast<int64_t>(pl->cmp_waves) * nsa::kCmpTPW;
+  const int64_t tok_sw = static_cast<int64_t>(nsa::kSwWaves) * nsa::kSwTPW;
+  pl->cmp_tiles = static_cast<int>((L + tok_cmp - 1) / tok_cmp);
+  pl->sw_tiles = static_cast<int>((L + tok_sw - 1) / tok_sw);
+  const size_t elem = d->in_dtype == NSA_BF16 ? 2 : 4;
+  const size_t tile = 64 * static_cast<size_t>(D) * elem;
+  size_t off = 0;
+  pl->off_kt = off;
+  off = align_up(off + static_cast<size_t>(B * G) * pl->Nb * tile);
+  pl->off_vt = off;
+  off = align_up(off + static_cast<size_t>(B * G) * pl->Nb * tile);
+  pl->off_kct = off;
+  off = align_up(off + static_cast<size_t>(B * G) * pl->NcT * tile);
+  pl->off_vct = off;
+  off = align_up(off + static_cast<size_t>(B * G) * pl->NcT * tile);
+  pl->off_idx = off;
+  off = align_up(off + static_cast<size_t>(B * L * G) * p->select_top_k * sizeof(int32_t));
+  pl->total = off;
+  return NSA_OK;
+}
+
+// ------------------------------------------------------------------ decode
+
+struct DecodePlan {
+  int SC, SW, SS, NmaxPad, nslots;
+  size_t off_part, off_logits, off_idx, total;
+};
+
+nsa_status_t plan_decode(const nsa_decode_desc_t* d, const nsa_params_t* p, DecodePlan* pl) {
+  if (d == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->batch < 0) return fail(NSA_ERR_INVALID_ARGUMENT, "batch must be >= 0");
+  if (d->max_seqlen < 1) return fail(NSA_ERR_INVALID_ARGUMENT, "max_seqlen must be >= 1");
+  if (d->max_blocks < 0) return fail(NSA_ERR_INVALID_ARGUMENT, "max_blocks must be >= 0");
+  NSA_TRY(check_heads(d->n_q_heads, d->n_kv_heads, d->head_dim));
+  NSA_TRY(check_dtypes(d->in_dtype, d->out_dtype));
+  NSA_TRY(check_params(p, d->head_dim));
+  if (d->max_blocks < d->max_seqlen / 64)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "max_blocks (%d) < max_seqlen / 64 (%d)", d->max_blocks,
+                d->max_seqlen / 64);
+  NSA_TRY(check_strides("q", d->q_stride, 2, true));
+  NSA_TRY(check_strides("k_cache", d->k_stride, 3, true));
+  NSA_TRY(check_strides("v_cache", d->v_stride, 3, true));
+  NSA_TRY(check_strides("kc_cache", d->kc_stride, 3, true));
+  NSA_TRY(check_strides("vc_cache", d->vc_stride, 3, true));
+  NSA_TRY(check_strides("gates", d->g_stride, 2, false));
+  NSA_TRY(check_strides("out", d->o_stride, 2, false));
+  const int64_t B = d->batch, G = d->n_kv_heads, D = d->head_dim;
+  const int nv = d->max_seqlen / 64;
+  pl->SC = (nv + nsa::kDecSplitKeys - 1) / nsa::kDecSplitKeys;
+  const int wv = p->sliding_window < d->max_seqlen ? p->sliding_window : d->max_seqlen;
+  pl->SW = (wv + nsa::kDecSplitKeys - 1) / nsa::kDecSplitKeys;
+  pl->SS = (p->select_top_k + 3) / 4;
+  pl->NmaxPad = pl->SC * nsa::kDecSplitKeys;
+  pl->nslots = 4 * (pl->SC + pl->SW + pl->SS) + 1;
+  if (B * G > INT32_MAX / 16)
+    return fail(NSA_ERR_UNSUPPORTED, "batch * n_kv_heads too large");
+  const size_t lds_sel = pl->NmaxPad * sizeof(float) + nsa::kSurvCap * 8 + 64 * 4 + 48 * 4;
+  if (lds_sel > static_cast<size_t>(nsa::kMaxLds))
+    return fail(NSA_ERR_UNSUPPORTED, "max_seqlen %d needs more LDS for block scores than a CU has",
+                d->max_seqlen);
+  size_t off = 0;
+  pl->off_part = off;
+  off = align_up(off + static_cast<size_t>(B * G) * pl->nslots * (32 + 16 * D) * sizeof(float));
+  pl->off_logits = off;
+  off = align_up(off + static_cast<size_t>(B * G) * 16 * pl->NmaxPad * sizeof(float));
+  pl->off_idx = off;
+  off = align_up(off + static_cast<size_t>(B * G) * p->select_top_k * sizeof(int32_t));
+  pl->total = off;
+  return NSA_OK;
+}
+
+float scale_log2(const nsa_params_t* p, int D) {
+  const float s = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt(static_cast<float>(D));
+  return s * nsa::kLog2eHost;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nsa_status_string(nsa_status_t status) {
+  switch (status) {
+    case NSA_OK:
+      return "NSA_OK";
+    case NSA_ERR_INVALID_ARGUMENT:
+      return "NSA_ERR_INVALID_ARGUMENT";
+    case NSA_ERR_UNSUPPORTED:
+      return "NSA_ERR_UNSUPPORTED";
+    case NSA_ERR_WORKSPACE_TOO_SMALL:
+      return "NSA_ERR_WORKSPACE_TOO_SMALL";
+    case NSA_ERR_HIP:
+      return "NSA_ERR_HIP";
+  }
+  return "NSA_ERR_UNKNOWN";
+}
+
+const char* nsa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t nsa_version(void) { return 100; }
+
+nsa_status_t nsa_prefill_workspace_bytes(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                                         size_t* bytes) {
+  if (bytes == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  PrefillPlan pl;
+  NSA_TRY(plan_prefill(desc, params, &pl));
+  *bytes = pl.total;
+  return ok();
+}
+
+nsa_status_t nsa_decode_workspace_bytes(const nsa_decode_desc_t* desc, const nsa_params_t* params,
+                                        size_t* bytes) {
+  if (bytes == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  DecodePlan pl;
+  NSA_TRY(plan_decode(desc, params, &pl));
+  *bytes = pl.total;
+  return ok();
+}
+
+static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                                 const void* q, const void* k, const void* v, const void* gates,
+                                 void* out, int32_t* idx, nsa_idx_mode_t idx_mode, void* workspace,
+                                 size_t workspace_bytes, void* stream, void* const* events) {
+  PrefillPlan pl;
+  NSA_TRY(plan_prefill(desc, params, &pl));
+  if (idx_mode != NSA_IDX_COMPUTE && idx_mode != NSA_IDX_INJECT)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "unknown idx_mode %d", static_cast<int>(idx_mode));
+  if (desc->batch == 0 || desc->seqlen == 0) return ok();  // empty input: nothing to do
+  NSA_TRY(check_ptr("q", q, true));
+  NSA_TRY(check_ptr("k", k, true));
+  NSA_TRY(check_ptr("v", v, true));
+  NSA_TRY(check_ptr("gates", gates, false));
+  NSA_TRY(check_ptr("out", out, true));
+  NSA_TRY(check_ptr("workspace", workspace, true));
+  if (idx_mode == NSA_IDX_INJECT && idx == nullptr)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "NSA_IDX_INJECT needs idx");
+  if (idx != nullptr && (reinterpret_cast<uintptr_t>(idx) & 3u) != 0)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "idx is not 4-byte aligned");
+  const size_t gal = desc->in_dtype == NSA_BF16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(gates) % gal) != 0)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "gates is not aligned to its element size");
+  if (workspace_bytes < pl.total)
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", pl.total,
+                workspace_bytes);
+
+  nsa::PrefillArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = desc->batch;
+  a.L = desc->seqlen;
+  a.Hq = desc->n_q_heads;
+  a.G = desc->n_kv_heads;
+  a.Hg = a.Hq / a.G;
+  a.D = desc->head_dim;
+  a.n = params->select_top_k;
+  a.w = params->sliding_window;
+  a.Nb = pl.Nb;
+  a.Nc = pl.Nc;
+  a.NcT = pl.NcT;
+  a.cmp_waves = pl.cmp_waves;
+  a.cmp_tiles = pl.cmp_tiles;
+  a.sw_tiles = pl.sw_tiles;
+  a.scale_log2 = scale_log2(params, a.D);
+  a.inject = idx_mode == NSA_IDX_INJECT ? 1 : 0;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.gates = gates;
+  a.out = out;
+  char* ws = static_cast<char*>(workspace);
+  a.idx = idx != nullptr ? idx : reinterpret_cast<int32_t*>(ws + pl.off_idx);
+  a.kt = ws + pl.off_kt;
+  a.vt = ws + pl.off_vt;
+  a.kct = ws + pl.off_kct;
+  a.vct = ws + pl.off_vct;
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = desc->q_stride[i];
+    a.ks[i] = desc->k_stride[i];
+    a.vs[i] = desc->v_stride[i];
+    a.gs[i] = desc->g_stride[i];
+    a.os[i] = desc->o_stride[i];
+  }
+  hipError_t e = nsa::launch_prefill(a, desc->in_dtype == NSA_BF16, desc->out_dtype == NSA_BF16,
+                                     static_cast<hipStream_t>(stream),
+                                     reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)));
+  if (e != hipSuccess) return fail(NSA_ERR_HIP, "HIP error in prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+nsa_status_t nsa_fwd_prefill(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                             const void* q, const void* k, const void* v, const void* gates,
+                             void* out, int32_t* idx, nsa_idx_mode_t idx_mode, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return prefill_impl(desc, params, q, k, v, gates, out, idx, idx_mode, workspace, workspace_bytes,
+                      stream, nullptr);
+}
+
+nsa_status_t nsa_fwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                                   const void* q, const void* k, const void* v, const void* gates,
+                                   void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   void* const* stage_events) {
+  if (stage_events == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "stage_events is NULL");
+  for (int i = 0; i <= nsa::kPrefillStages; ++i)
+    if (stage_events[i] == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "stage_events[%d] is NULL", i);
+  return prefill_impl(desc, params, q, k, v, gates, out, idx, idx_mode, workspace, workspace_bytes,
+                      stream, stage_events);
+}
+
+static nsa_status_t decode_impl(const nsa_decode_desc_t* desc, const nsa_params_t* params,
+                                const void* q, const void* k_cache, const void* v_cache,
+                                const void* kc_cache, const void* vc_cache, const int32_t* seqlens,
+                                const void* gates, void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                void* const* events) {
+  DecodePlan pl;
+  NSA_TRY(plan_decode(desc, params, &pl));
+  if (idx_mode != NSA_IDX_COMPUTE && idx_mode != NSA_IDX_INJECT)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "unknown idx_mode %d", static_cast<int>(idx_mode));
+  if (desc->batch == 0) return ok();
+  NSA_TRY(check_ptr("q", q, true));
+  NSA_TRY(check_ptr("k_cache", k_cache, true));
+  NSA_TRY(check_ptr("v_cache", v_cache, true));
+  NSA_TRY(check_ptr("kc_cache", kc_cache, true));
+  NSA_TRY(check_ptr("vc_cache", vc_cache, true));
+  NSA_TRY(check_ptr("seqlens", seqlens, false));
+  NSA_TRY(check_ptr("gates", gates, false));
+  NSA_TRY(check_ptr("out", out, false));
+  NSA_TRY(check_ptr("workspace", workspace, true));
+  if (idx_mode == NSA_IDX_INJECT && idx == nullptr)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "NSA_IDX_INJECT needs idx");
+  if (idx != nullptr && (reinterpret_cast<uintptr_t>(idx) & 3u) != 0)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "idx is not 4-byte aligned");
+  if (workspace_bytes < pl.total)
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", pl.total,
+                workspace_bytes);
+  nsa::DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = desc->batch;
+  a.Lmax = desc->max_seqlen;
+  a.Nmax = desc->max_blocks;
+  a.Hq = desc->n_q_heads;
+  a.G = desc->n_kv_heads;
+  a.Hg = a.Hq / a.G;
+  a.D = desc->head_dim;
+  a.n = params->select_top_k;
+  a.w = params->sliding_window;
+  a.SC = pl.SC;
+  a.SW = pl.SW;
+  a.SS = pl.SS;
+  a.NmaxPad = pl.NmaxPad;
+  a.scale_log2 = scale_log2(params, a.D);
+  a.inject = idx_mode == NSA_IDX_INJECT ? 1 : 0;
+  a.q = q;
+  a.kcache = k_cache;
+  a.vcache = v_cache;
+  a.kccache = kc_cache;
+  a.vccache = vc_cache;
+  a.seqlens = seqlens;
+  a.gates = gates;
+  a.out = out;
+  char* ws = static_cast<char*>(workspace);
+  a.part = reinterpret_cast<float*>(ws + pl.off_part);
+  a.logits = reinterpret_cast<float*>(ws + pl.off_logits);
+  a.idx = idx != nullptr ? idx : reinterpret_cast<int32_t*>(ws + pl.off_idx);
+  for (int i = 0; i < 2; ++i) {
+    a.qs[i] = desc->q_stride[i];
+    a.gs[i] = desc->g_stride[i];
+    a.os[i] = desc->o_stride[i];
+  }
+  for (int i = 0; i < 3; ++i) {
+    a.ks[i] = desc->k_stride[i];
+    a.vs[i] = desc->v_stride[i];
+    a.kcs[i] = desc->kc_stride[i];
+    a.vcs[i] = desc->vc_stride[i];
+  }
+  hipError_t e = nsa::launch_decode(a, desc->in_dtype == NSA_BF16, desc->out_dtype == NSA_BF16,
+                                    static_cast<hipStream_t>(stream),
+                                    reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)));
+  if (e != hipSuccess) return fail(NSA_ERR_HIP, "HIP error in decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+nsa_status_t nsa_fwd_decode(const nsa_decode_desc_t* desc, const nsa_params_t* params,
+                            const void* q, const void* k_cache, const void* v_cache,
+                            const void* kc_cache, const void* vc_cache, const int32_t* seqlens,
+                            const void* gates, void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(desc, params, q, k_cache, v_cache, kc_cache, vc_cache, seqlens, gates, out, idx,
+                     idx_mode, workspace, workspace_bytes, stream, nullptr);
+}
+
+nsa_status_t nsa_fwd_decode_timed(const nsa_decode_desc_t* desc, const nsa_params_t* params,
+                                  const void* q, const void* k_cache, const void* v_cache,
+                                  const void* kc_cache, const void* vc_cache,
+                                  const int32_t* seqlens, const void* gates, void* out,
+                                  int32_t* idx, nsa_idx_mode_t idx_mode, void* workspace,
+                                  size_t workspace_bytes, void* stream, void* const* stage_events) {
+  if (stage_events == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "stage_events is NULL");
+  for (int i = 0; i <= nsa::kDecodeStages; ++i)
+    if (stage_events[i] == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "stage_events[%d] is NULL", i);
+  return decode_impl(desc, params, q, k_cache, v_cache, kc_cache, vc_cache, seqlens, gates, out, idx,
+                     idx_mode, workspace, workspace_bytes, stream, stage_events);
+}
+
+nsa_status_t nsa_compress_kv(int32_t batch, int32_t n_kv_heads, int32_t n_tokens, int32_t head_dim,
+                             nsa_dtype_t dtype, int32_t block_size, const void* k,
+                             const int64_t k_stride[3], const void* v, const int64_t v_stride[3],
+                             void* kc, const int64_t kc_stride[3], void* vc,
+                             const int64_t vc_stride[3], void* stream) {
+  if (batch < 0 || n_kv_heads < 1 || n_tokens < 0 || head_dim < 1)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "batch, n_tokens >= 0 and n_kv_heads, head_dim >= 1 required");
+  if (!dtype_ok(dtype)) return fail(NSA_ERR_INVALID_ARGUMENT, "unknown dtype");
+  if (block_size < 1) return fail(NSA_ERR_INVALID_ARGUMENT, "block_size must be >= 1");
+  if (block_size != nsa::kBlock) return fail(NSA_ERR_UNSUPPORTED, "only block_size 64 is supported");
+  if (head_dim > 1024) return fail(NSA_ERR_UNSUPPORTED, "head_dim > 1024 is not supported");
+  if (k_stride == nullptr || v_stride == nullptr || kc_stride == nullptr || vc_stride == nullptr)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "stride array is NULL");
+  NSA_TRY(check_strides("k", k_stride, 3, false));
+  NSA_TRY(check_strides("v", v_stride, 3, false));
+  NSA_TRY(check_strides("kc", kc_stride, 3, false));
+  NSA_TRY(check_strides("vc", vc_stride, 3, false));
+  const int nc = n_tokens / 64;
+  if (batch == 0 || nc == 0) return ok();
+  NSA_TRY(check_ptr("k", k, false));
+  NSA_TRY(check_ptr("v", v, false));
+  NSA_TRY(check_ptr("kc", kc, false));
+  NSA_TRY(check_ptr("vc", vc, false));
+  hipError_t e = nsa::launch_compress(batch, n_kv_heads, nc, head_dim, dtype == NSA_BF16, k, k_stride,
+                                      v, v_stride, kc, kc_stride, vc, vc_stride,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(NSA_ERR_HIP, "HIP error in compress launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,235 @@
+// Device helpers shared by the libnsa kernels (gfx950 / CDNA4, wave64).
+//
+// Matrix products use v_mfma_f32_16x16x32_bf16 for bf16 operands and eight
+// v_mfma_f32_16x16x4_f32 for fp32 operands. Both consume the same "fragment":
+// lane l of a wave holds 8 consecutive k-values of one operand row or column,
+//   A (16 x 32):  lane l holds A[m = l % 16][k = 8*(l/16) + j], j = 0..7
+//   B (32 x 16):  lane l holds B[k = 8*(l/16) + j][n = l % 16]
+//   C (16 x 16):  lane l holds C[m = 4*(l/16) + i][n = l % 16], i = 0..3
+// For fp32 the j-th of the eight 16x16x4 products takes value j of both
+// operands; it contracts over k-slots {8a + j}, so the eight together cover
+// all 32 k-slots, which is all a contraction needs.
+//
+// Attention is computed transposed (S^T = K Q^T, O^T = V^T P^T) so that the
+// C layout of S^T (keys along registers, queries along lanes) is, after a
+// fixed permutation of the 32 keys of one k-step, already the B operand of the
+// P.V product. The permutation is baked into the stored V tiles (see
+// vtile_off), so no data moves between the two products.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nsa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Element type tags.
+struct BF16 {
+  using storage = uint16_t;
+};
+struct F32 {
+  using storage = float;
+};
+
+template <class T>
+struct Frag;
+template <>
+struct Frag<BF16> {
+  u32x4 v;
+};
+template <>
+struct Frag<F32> {
+  f32x4 lo, hi;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <class T>
+__device__ __forceinline__ float to_f32(typename T::storage x);
+template <>
+__device__ __forceinline__ float to_f32<BF16>(uint16_t x) {
+  return bf16_to_f32(x);
+}
+template <>
+__device__ __forceinline__ float to_f32<F32>(float x) {
+  return x;
+}
+
+template <class T>
+__device__ __forceinline__ typename T::storage from_f32(float x);
+template <>
+__device__ __forceinline__ uint16_t from_f32<BF16>(float x) {
+  return static_cast<uint16_t>(f32_to_bf16_bits(x));
+}
+template <>
+__device__ __forceinline__ float from_f32<F32>(float x) {
+  return x;
+}
+
+template <class T>
+__device__ __forceinline__ Frag<T> frag_zero();
+template <>
+__device__ __forceinline__ Frag<BF16> frag_zero<BF16>() {
+  Frag<BF16> f;
+  f.v = u32x4{0u, 0u, 0u, 0u};
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<F32> frag_zero<F32>() {
+  Frag<F32> f;
+  f.lo = f32x4{0.f, 0.f, 0.f, 0.f};
+  f.hi = f.lo;
+  return f;
+}
+
+// 8 consecutive elements (16 B for bf16, 32 B for fp32); p must be aligned to that.
+template <class T>
+__device__ __forceinline__ Frag<T> frag_load(const typename T::storage* p);
+template <>
+__device__ __forceinline__ Frag<BF16> frag_load<BF16>(const uint16_t* p) {
+  Frag<BF16> f;
+  f.v = *reinterpret_cast<const u32x4*>(p);
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<F32> frag_load<F32>(const float* p) {
+  Frag<F32> f;
+  f.lo = *reinterpret_cast<const f32x4*>(p);
+  f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+  return f;
+}
+
+template <class T>
+__device__ __forceinline__ void frag_store(typename T::storage* p, const Frag<T>& f);
+template <>
+__device__ __forceinline__ void frag_store<BF16>(uint16_t* p, const Frag<BF16>& f) {
+  *reinterpret_cast<u32x4*>(p) = f.v;
+}
+template <>
+__device__ __forceinline__ void frag_store<F32>(float* p, const Frag<F32>& f) {
+  *reinterpret_cast<f32x4*>(p) = f.lo;
+  *reinterpret_cast<f32x4*>(p + 4) = f.hi;
+}
+
+// c += A.B for one 16x16x32 step.
+__device__ __forceinline__ void mma(f32x4& c, const Frag<BF16>& a, const Frag<BF16>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                               __builtin_bit_cast(bf16x8, b.v), c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& c, const Frag<F32>& a, const Frag<F32>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.z, b.lo.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.w, b.lo.w, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.x, b.hi.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.y, b.hi.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.z, b.hi.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, c, 0, 0, 0);
+}
+
+// Two C-layout tiles of probabilities (keys 0..15 and 16..31 of one k-step)
+// -> the B operand of the P.V product, in the permuted key order of vtile_off.
+template <class T>
+__device__ __forceinline__ Frag<T> pack_p(const f32x4& a, const f32x4& b);
+template <>
+__device__ __forceinline__ Frag<BF16> pack_p<BF16>(const f32x4& a, const f32x4& b) {
+  Frag<BF16> f;
+  f.v.x = f32_to_bf16_bits(a.x) | (f32_to_bf16_bits(a.y) << 16);
+  f.v.y = f32_to_bf16_bits(a.z) | (f32_to_bf16_bits(a.w) << 16);
+  f.v.z = f32_to_bf16_bits(b.x) | (f32_to_bf16_bits(b.y) << 16);
+  f.v.w = f32_to_bf16_bits(b.z) | (f32_to_bf16_bits(b.w) << 16);
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<F32> pack_p<F32>(const f32x4& a, const f32x4& b) {
+  Frag<F32> f;
+  f.lo = a;
+  f.hi = b;
+  return f;
+}
+
+// ---------------------------------------------------------------- tile layouts
+//
+// A 64-key chunk of K (64 x D) is stored "fragment-major": the A-operand
+// fragment (key-tile kt, k-step s) of lane l is 8 contiguous elements at
+// ((kt * D/32 + s) * 64 + l) * 8, holding K[16 kt + l%16][32 s + 8 (l/16) + j].
+// One fragment load of a wave is therefore 64 x 8 contiguous elements.
+__host__ __device__ __forceinline__ int ktile_off(int r, int d, int D) {
+  const int kt = r >> 4, s = d >> 5;
+  const int lane = (r & 15) + 16 * ((d & 31) >> 3);
+  return ((kt * (D >> 5) + s) * 64 + lane) * 8 + (d & 7);
+}
+__host__ __device__ __forceinline__ int ktile_frag(int kt, int s, int lane, int D) {
+  return ((kt * (D >> 5) + s) * 64 + lane) * 8;
+}
+
+// A 64-key chunk of V^T (D x 64): the A-operand fragment (d-tile dt, k-step s)
+// of lane l is 8 contiguous elements at ((dt * 2 + s) * 64 + l) * 8 holding
+// V[32 s + kappa(l/16, j)][16 dt + l%16], kappa(a, j) = 4a + j for j < 4 and
+// 16 + 4a + (j - 4) otherwise: exactly the keys whose probabilities lane l
+// holds in the C layout of the two S^T tiles of that k-step.
+__host__ __device__ __forceinline__ int vtile_off(int r, int d) {
+  const int s = r >> 5, rr = r & 31;
+  const int half = rr >> 4, a = (rr & 15) >> 2, i = rr & 3;
+  const int lane = (d & 15) + 16 * a;
+  return (((d >> 4) * 2 + s) * 64 + lane) * 8 + 4 * half + i;
+}
+__host__ __device__ __forceinline__ int vtile_frag(int dt, int s, int lane) {
+  return ((dt * 2 + s) * 64 + lane) * 8;
+}
+
+// ---------------------------------------------------------------- wave helpers
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of each DPP row (row_ror butterfly); every lane of the
+// row receives the row total.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<0x128>(v);  // row_ror:8
+  v += dpp_f<0x124>(v);  // row_ror:4
+  v += dpp_f<0x122>(v);  // row_ror:2
+  v += dpp_f<0x121>(v);  // row_ror:1
+  return v;
+}
+
+__device__ __forceinline__ float xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// Reductions over the four lanes l, l^16, l^32, l^48 (same column, all keys).
+__device__ __forceinline__ float col_max4(float v) {
+  v = fmaxf(v, xor_f(v, 16));
+  return fmaxf(v, xor_f(v, 32));
+}
+__device__ __forceinline__ float col_sum4(float v) {
+  v += xor_f(v, 16);
+  return v + xor_f(v, 32);
+}
+
+// Orders this wave's LDS accesses before the following ones.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+}  // namespace nsa

@@ -1,0 +1,84 @@
+// Internal interface between the host API (nsa_api.cpp) and the kernel
+// launchers (*.hip). Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nsa {
+
+constexpr int kBlock = 64;         // compress / select block size supported
+constexpr int kSurvCap = 256;      // top-k survivor buffer per wave (entries)
+constexpr int kCmpTPW = 4;         // tokens per wave, compressed+selection kernel
+constexpr int kSwTPW = 2;          // tokens per wave, selected+window kernel
+constexpr int kSwWaves = 4;        // waves per workgroup, selected+window kernel
+constexpr int kMaxLds = 160 * 1024;
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// Everything a prefill launch needs; passed by value to every kernel.
+struct PrefillArgs {
+  int B, L, Hq, G, Hg, D, n, w;
+  int Nb;   // selectable blocks = ceil(L / 64)
+  int Nc;   // complete (compressed) blocks = L / 64
+  int NcT;  // 64-row chunks of the compressed tiles = ceil(Nc / 64)
+  int cmp_waves, cmp_tiles, sw_tiles;
+  float scale_log2;  // softmax scale * log2(e)
+  int inject;        // 1: idx holds the selection; 0: compute it into idx
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* gates;
+  void* out;
+  int32_t* idx;
+  void* kt;   // [B][G][Nb] 64-key K tiles (fragment-major)
+  void* vt;   // [B][G][Nb] 64-key V^T tiles
+  void* kct;  // [B][G][NcT] 64-block tiles of block means of K
+  void* vct;  // same for V
+  int64_t qs[3], ks[3], vs[3], gs[3], os[3];
+};
+
+struct DecodeArgs {
+  int B, Lmax, Nmax, Hq, G, Hg, D, n, w;
+  int SC;  // compressed splits per (b, g), each kDecSplitKeys blocks
+  int SW;  // window splits per (b, g), each kDecSplitKeys tokens
+  int SS;  // selected splits per (b, g), each 4 blocks
+  int NmaxPad;
+  float scale_log2;
+  int inject;
+  const void* q;
+  const void* kcache;
+  const void* vcache;
+  const void* kccache;
+  const void* vccache;
+  const int32_t* seqlens;
+  const void* gates;
+  void* out;
+  int32_t* idx;
+  float* part;    // partial softmax states, [B*G][SC+SW+SS+1][Hg=16][2 + D]
+  float* logits;  // compressed logits (log2 domain), [B*G][16][NmaxPad]
+  int64_t qs[2], ks[3], vs[3], kcs[3], vcs[3], gs[2], os[2];
+};
+
+constexpr int kDecSplitKeys = 256;  // keys (or blocks) per decode workgroup: 4 waves x 64
+
+// ev (nullable): kPrefillStages+1 / kDecodeStages+1 events recorded on st
+// before each kernel and after the last one.
+constexpr int kPrefillStages = 3;
+constexpr int kDecodeStages = 4;
+hipError_t launch_prefill(const PrefillArgs& a, bool in_bf16, bool out_bf16, hipStream_t st,
+                          hipEvent_t* ev);
+hipError_t launch_decode(const DecodeArgs& a, bool in_bf16, bool out_bf16, hipStream_t st,
+                         hipEvent_t* ev);
+hipError_t launch_compress(int B, int G, int Nc, int D, bool bf16, const void* k, const int64_t* ks,
+                           const void* v, const int64_t* vs, void* kc, const int64_t* kcs,
+                           void* vc, const int64_t* vcs, hipStream_t st);
+
+// LDS bytes of the compressed+selection kernel for a given number of waves.
+inline size_t cmp_lds_bytes(int waves, int NcT) {
+  return static_cast<size_t>(waves) *
+         (static_cast<size_t>(kCmpTPW) * NcT * 64 * sizeof(float) + kSurvCap * sizeof(uint64_t) +
+          64 * sizeof(int));
+}
+
+}  // namespace nsa

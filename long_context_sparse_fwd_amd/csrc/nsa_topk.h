@@ -1,0 +1,120 @@
+// Wave-level block selection: the query's own block plus the n-1 best-scoring
+// earlier blocks, ties to the lower block index, written ascending and padded
+// with -1. The score -> top-k -> gather dataflow follows the selector of the
+// NSA factory write-up (chencunli.com, "DeepSeek NSA on the Siemens 840D
+// manual"), section "What dynamic sparsity actually sparsifies"; the own-block
+// rule and the tie rule are the readings stated in nsa.h.
+//
+// Method (exact, no approximation):
+//  1. keys: score bits (scores are >= 0, so the unsigned bit pattern orders
+//     like the float) with the top bit set to mark a real candidate, and, for
+//     ordering, the 64-bit key (bits << 32) | (~j) which breaks ties to the
+//     lower j;
+//  2. theta = the (n-1)-th largest of the 64 per-lane maxima (bitonic sort
+//     across lanes). At least n-1 candidates are >= theta, so every member of
+//     the answer is >= theta;
+//  3. the candidates >= theta (typically ~20) are compacted into LDS and each
+//     is ranked by counting larger keys; ranks < n-1 are the answer. If more
+//     than kSurvCap survive (heavy ties), n-1 rounds of wave-wide argmax over
+//     all candidates are used instead;
+//  4. the n chosen indices are sorted ascending by rank counting.
+#pragma once
+
+#include "nsa_device.h"
+#include "nsa_internal.h"
+
+namespace nsa {
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, 64);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, 64);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// sc: scores of blocks [0, own) in LDS (read by all lanes). out: n entries.
+// surv: kSurvCap u64 of LDS scratch; selb: 64 ints of LDS scratch.
+// Must be called by a whole wave with uniform arguments.
+__device__ inline void topk_wave(const float* sc, int own, int n, int32_t* out, uint64_t* surv,
+                                 int* selb, int lane) {
+  const int n1 = n - 1;
+  if (own <= n1) {
+    if (lane < n) out[lane] = lane <= own ? lane : -1;
+    return;
+  }
+  if (n1 == 0) {
+    if (lane == 0) out[0] = own;
+    return;
+  }
+  const int R = (own + 63) >> 6;
+  uint32_t lmax = 0;
+  for (int r = 0; r < R; ++r) {
+    const int j = lane + 64 * r;
+    if (j < own) lmax = max(lmax, __float_as_uint(sc[j]) | 0x80000000u);
+  }
+  // bitonic sort of the lane maxima, descending across lanes
+  uint32_t v = lmax;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      const uint32_t o = __shfl_xor(v, jj, 64);
+      const bool keep_max = ((lane & jj) == 0) == ((lane & k) == 0);
+      v = keep_max ? max(v, o) : min(v, o);
+    }
+  }
+  const uint32_t theta = __shfl(v, n1 - 1, 64);
+
+  int cnt = 0;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int r = 0; r < R; ++r) {
+    const int j = lane + 64 * r;
+    const uint32_t key = (j < own) ? (__float_as_uint(sc[j]) | 0x80000000u) : 0u;
+    const bool f = (j < own) && key >= theta;
+    const uint64_t bal = __ballot(f);
+    const int pos = cnt + __popcll(bal & below);
+    if (f && pos < kSurvCap)
+      surv[pos] = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - j);
+    cnt += __popcll(bal);
+  }
+  wave_lds_sync();
+  if (cnt <= kSurvCap) {
+    for (int i = lane; i < cnt; i += 64) {
+      const uint64_t mine = surv[i];
+      int rank = 0;
+      for (int k = 0; k < cnt; ++k) rank += surv[k] > mine ? 1 : 0;
+      if (rank < n1) selb[rank] = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(mine));
+    }
+  } else {
+    uint64_t prev = ~0ull;
+    for (int rr = 0; rr < n1; ++rr) {
+      uint64_t best = 0;
+      for (int r = 0; r < R; ++r) {
+        const int j = lane + 64 * r;
+        if (j < own) {
+          const uint64_t k64 =
+              (static_cast<uint64_t>(__float_as_uint(sc[j]) | 0x80000000u) << 32) |
+              static_cast<uint32_t>(0xFFFFFFFFu - j);
+          if (k64 < prev && k64 > best) best = k64;
+        }
+      }
+#pragma unroll
+      for (int m = 32; m > 0; m >>= 1) {
+        const uint64_t o = shfl_xor_u64(best, m);
+        best = o > best ? o : best;
+      }
+      prev = best;
+      if (lane == 0) selb[rr] = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
+    }
+  }
+  if (lane == 0) selb[n1] = own;
+  wave_lds_sync();
+  if (lane < n) {
+    const int vj = selb[lane];
+    int pos = 0;
+    for (int k = 0; k < n; ++k) pos += selb[k] < vj ? 1 : 0;
+    out[pos] = vj;
+  }
+  wave_lds_sync();
+}
+
+}  // namespace nsa

@@ -1,0 +1,259 @@
+"""Thin ctypes binding of libnsa (include/nsa.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libnsa.so. PyTorch supplies device memory and the current stream.
+There is no CPU fallback: calling into the library without the built .so or
+without a GPU raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnsa.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "nsa.h")
+
+NSA_OK, NSA_ERR_INVALID_ARGUMENT, NSA_ERR_UNSUPPORTED, NSA_ERR_WORKSPACE_TOO_SMALL, NSA_ERR_HIP = range(5)
+NSA_F32, NSA_BF16 = 0, 1
+NSA_IDX_COMPUTE, NSA_IDX_INJECT = 0, 1
+
+c_i32, c_i64, c_f32, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+
+
+class NsaParams(ctypes.Structure):
+    _fields_ = [("compress_block_size", c_i32), ("select_block_size", c_i32),
+                ("select_top_k", c_i32), ("sliding_window", c_i32), ("softmax_scale", c_f32)]
+
+
+class PrefillDesc(ctypes.Structure):
+    _fields_ = [("batch", c_i32), ("seqlen", c_i32), ("n_q_heads", c_i32), ("n_kv_heads", c_i32),
+                ("head_dim", c_i32), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("q_stride", c_i64 * 3), ("k_stride", c_i64 * 3), ("v_stride", c_i64 * 3),
+                ("g_stride", c_i64 * 3), ("o_stride", c_i64 * 3)]
+
+
+class DecodeDesc(ctypes.Structure):
+    _fields_ = [("batch", c_i32), ("max_seqlen", c_i32), ("max_blocks", c_i32),
+                ("n_q_heads", c_i32), ("n_kv_heads", c_i32), ("head_dim", c_i32),
+                ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("q_stride", c_i64 * 2), ("k_stride", c_i64 * 3), ("v_stride", c_i64 * 3),
+                ("kc_stride", c_i64 * 3), ("vc_stride", c_i64 * 3), ("g_stride", c_i64 * 2),
+                ("o_stride", c_i64 * 2)]
+
+
+class NsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libnsa.so (built in-tree by long_context_sparse_fwd_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m long_context_sparse_fwd_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    L.nsa_status_string.restype = ctypes.c_char_p
+    L.nsa_status_string.argtypes = [ctypes.c_int]
+    L.nsa_last_error.restype = ctypes.c_char_p
+    L.nsa_last_error.argtypes = []
+    L.nsa_version.restype = c_i32
+    L.nsa_prefill_workspace_bytes.restype = ctypes.c_int
+    L.nsa_prefill_workspace_bytes.argtypes = [P(PrefillDesc), P(NsaParams), P(ctypes.c_size_t)]
+    L.nsa_decode_workspace_bytes.restype = ctypes.c_int
+    L.nsa_decode_workspace_bytes.argtypes = [P(DecodeDesc), P(NsaParams), P(ctypes.c_size_t)]
+    L.nsa_fwd_prefill.restype = ctypes.c_int
+    L.nsa_fwd_prefill.argtypes = [P(PrefillDesc), P(NsaParams), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                  ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
+    L.nsa_fwd_decode.restype = ctypes.c_int
+    L.nsa_fwd_decode.argtypes = [P(DecodeDesc), P(NsaParams), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                 c_vp, c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
+    L.nsa_compress_kv.restype = ctypes.c_int
+    L.nsa_compress_kv.argtypes = [c_i32, c_i32, c_i32, c_i32, ctypes.c_int, c_i32, c_vp, P(c_i64),
+                                  c_vp, P(c_i64), c_vp, P(c_i64), c_vp, P(c_i64), c_vp]
+    _lib = L
+    return L
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/nsa.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def check(status: int) -> None:
+    if status != NSA_OK:
+        L = lib()
+        raise NsaError(status, f"{L.nsa_status_string(status).decode()}: {L.nsa_last_error().decode()}")
+
+
+def make_params(top_k: int, window: int, block: int = 64, select_block: int | None = None,
+                scale: float = 0.0) -> NsaParams:
+    return NsaParams(block, block if select_block is None else select_block, top_k, window, scale)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return NSA_BF16
+    if dt == torch.float32:
+        return NSA_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _stream_of(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise RuntimeError("libnsa runs on the GPU only: pass device tensors")
+        if t.stride(-1) != 1:
+            raise ValueError("the last dimension must be contiguous")
+
+
+def prefill_desc(q, k, v, gates, out) -> PrefillDesc:
+    B, L, Hq, D = q.shape
+    G = k.shape[2]
+    d = PrefillDesc()
+    d.batch, d.seqlen, d.n_q_heads, d.n_kv_heads, d.head_dim = B, L, Hq, G, D
+    d.in_dtype, d.out_dtype = _dtype_code(q.dtype), _dtype_code(out.dtype)
+    d.q_stride[:] = q.stride()[:3]
+    d.k_stride[:] = k.stride()[:3]
+    d.v_stride[:] = v.stride()[:3]
+    d.g_stride[:] = gates.stride()[:3]
+    d.o_stride[:] = out.stride()[:3]
+    return d
+
+
+def prefill(q, k, v, gates, *, top_k: int, window: int, block: int = 64, select_block=None,
+            scale: float = 0.0, out=None, out_dtype=None, idx=None, inject: bool = False,
+            return_idx: bool = False, workspace=None):
+    """NSA prefill. q [B,L,Hq,D], k/v [B,L,G,D], gates [B,L,Hq,3] (device tensors).
+
+    Returns out (and idx [B,L,G,top_k] int32 when return_idx or idx is given).
+    With inject=True, idx supplies the block selection.
+    """
+    _require_gpu(q, k, v, gates)
+    B, L, Hq, D = q.shape
+    G = k.shape[2]
+    if k.shape != (B, L, G, D) or v.shape != k.shape or gates.shape != (B, L, Hq, 3):
+        raise ValueError("shape mismatch among q, k, v, gates")
+    if not (q.dtype == k.dtype == v.dtype == gates.dtype):
+        raise TypeError("q, k, v and gates must share one dtype")
+    if out is None:
+        out = torch.empty((B, L, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if inject and idx is None:
+        raise ValueError("inject=True needs idx")
+    if idx is None and return_idx:
+        idx = torch.empty((B, L, G, top_k), dtype=torch.int32, device=q.device)
+    if idx is not None and (idx.dtype != torch.int32 or not idx.is_contiguous()
+                            or tuple(idx.shape) != (B, L, G, top_k)):
+        raise ValueError("idx must be a contiguous int32 [B, L, G, top_k] tensor")
+    desc = prefill_desc(q, k, v, gates, out)
+    params = make_params(top_k, window, block, select_block, scale)
+    L_ = lib()
+    nbytes = ctypes.c_size_t()
+    check(L_.nsa_prefill_workspace_bytes(ctypes.byref(desc), ctypes.byref(params), ctypes.byref(nbytes)))
+    if workspace is None or workspace.numel() < nbytes.value:
+        workspace = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=q.device)
+    check(L_.nsa_fwd_prefill(ctypes.byref(desc), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v),
+                             _ptr(gates), _ptr(out), _ptr(idx),
+                             NSA_IDX_INJECT if inject else NSA_IDX_COMPUTE, _ptr(workspace),
+                             workspace.numel(), _stream_of(q)))
+    if idx is not None:
+        return out, idx
+    return out
+
+
+def prefill_workspace_bytes(q, k, v, gates, out, *, top_k, window, block=64) -> int:
+    desc = prefill_desc(q, k, v, gates, out)
+    params = make_params(top_k, window, block)
+    nbytes = ctypes.c_size_t()
+    check(lib().nsa_prefill_workspace_bytes(ctypes.byref(desc), ctypes.byref(params), ctypes.byref(nbytes)))
+    return nbytes.value
+
+
+def decode_desc(q, k_cache, v_cache, kc_cache, vc_cache, gates, out) -> DecodeDesc:
+    B, Hq, D = q.shape
+    _, G, Lmax, _ = k_cache.shape
+    d = DecodeDesc()
+    d.batch, d.max_seqlen, d.max_blocks = B, Lmax, kc_cache.shape[2]
+    d.n_q_heads, d.n_kv_heads, d.head_dim = Hq, G, D
+    d.in_dtype, d.out_dtype = _dtype_code(q.dtype), _dtype_code(out.dtype)
+    d.q_stride[:] = q.stride()[:2]
+    d.k_stride[:] = k_cache.stride()[:3]
+    d.v_stride[:] = v_cache.stride()[:3]
+    d.kc_stride[:] = kc_cache.stride()[:3]
+    d.vc_stride[:] = vc_cache.stride()[:3]
+    d.g_stride[:] = gates.stride()[:2]
+    d.o_stride[:] = out.stride()[:2]
+    return d
+
+
+def decode(q, k_cache, v_cache, kc_cache, vc_cache, seqlens, gates, *, top_k: int, window: int,
+           block: int = 64, select_block=None, scale: float = 0.0, out=None, out_dtype=None,
+           idx=None, inject: bool = False, return_idx: bool = False, workspace=None):
+    """NSA decode. q [B,Hq,D]; caches [B,G,Lmax,D]; block caches [B,G,Nmax,D];
+    seqlens [B] int32 (device); gates [B,Hq,3]. Returns out (and idx [B,G,top_k])."""
+    _require_gpu(q, k_cache, v_cache, kc_cache, vc_cache, gates)
+    B, Hq, D = q.shape
+    G = k_cache.shape[1]
+    if seqlens.dtype != torch.int32 or not seqlens.is_cuda or seqlens.shape != (B,):
+        raise ValueError("seqlens must be an int32 device tensor of shape [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if inject and idx is None:
+        raise ValueError("inject=True needs idx")
+    if idx is None and return_idx:
+        idx = torch.empty((B, G, top_k), dtype=torch.int32, device=q.device)
+    if idx is not None and (idx.dtype != torch.int32 or not idx.is_contiguous()
+                            or tuple(idx.shape) != (B, G, top_k)):
+        raise ValueError("idx must be a contiguous int32 [B, G, top_k] tensor")
+    desc = decode_desc(q, k_cache, v_cache, kc_cache, vc_cache, gates, out)
+    params = make_params(top_k, window, block, select_block, scale)
+    L_ = lib()
+    nbytes = ctypes.c_size_t()
+    check(L_.nsa_decode_workspace_bytes(ctypes.byref(desc), ctypes.byref(params), ctypes.byref(nbytes)))
+    if workspace is None or workspace.numel() < nbytes.value:
+        workspace = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=q.device)
+    check(L_.nsa_fwd_decode(ctypes.byref(desc), ctypes.byref(params), _ptr(q), _ptr(k_cache),
+                            _ptr(v_cache), _ptr(kc_cache), _ptr(vc_cache), _ptr(seqlens),
+                            _ptr(gates), _ptr(out), _ptr(idx),
+                            NSA_IDX_INJECT if inject else NSA_IDX_COMPUTE, _ptr(workspace),
+                            workspace.numel(), _stream_of(q)))
+    if idx is not None:
+        return out, idx
+    return out
+
+
+def compress_kv(k, v, kc=None, vc=None, *, block: int = 64):
+    """Block means of a [B,G,L,D] K/V cache -> kc, vc [B,G,L//block,D] (or given tensors)."""
+    _require_gpu(k, v)
+    B, G, L, D = k.shape
+    nc = L // block
+    if kc is None:
+        kc = torch.empty((B, G, nc, D), dtype=k.dtype, device=k.device)
+    if vc is None:
+        vc = torch.empty((B, G, nc, D), dtype=v.dtype, device=v.device)
+    arr = lambda t: (c_i64 * 3)(*t.stride()[:3])
+    check(lib().nsa_compress_kv(B, G, L, D, _dtype_code(k.dtype), block, _ptr(k), arr(k), _ptr(v),
+                                arr(v), _ptr(kc), arr(kc), _ptr(vc), arr(vc), _stream_of(k)))
+    return kc, vc

@@ -164,7 +164,8 @@ def _check_blocks(block: int, select_block):
 
 
 def prefill(q, k, v, gates, *, block: int = 64, select_block=None, top_k: int, window: int,
-            scale=None, inject_idx=None, rows=None, branches: bool = False) -> dict:
+            scale=None, inject_idx=None, rows=None, branches: bool = False,
+            scores: bool = False) -> dict:
     """NSA prefill: every query position attends causally within its sequence.
 
     q [B, L, Hq, D]; k, v [B, L, G, D]; gates [B, L, Hq, 3]; any float dtype
@@ -172,7 +173,8 @@ def prefill(q, k, v, gates, *, block: int = 64, select_block=None, top_k: int, w
     query positions (all positions by default); K/V always span the full
     sequence. ``inject_idx`` [B, L, G, top_k] replaces the selection.
     Returns out [B, R, Hq, D], idx [B, R, G, top_k], lse [B, R, Hq] and
-    gap [B, R, G] (plus the three branch outputs when ``branches``).
+    gap [B, R, G] (plus the three branch outputs when ``branches``, and the
+    block scores [B, R, G, L // block] when ``scores``, NaN where undefined).
     """
     _check_blocks(block, select_block)
     B, L, Hq, D = q.shape
@@ -188,6 +190,9 @@ def prefill(q, k, v, gates, *, block: int = 64, select_block=None, top_k: int, w
     if branches:
         for name in ("o_cmp", "o_slc", "o_win"):
             res[name] = np.zeros((B, R, Hq, D))
+    fixed = list(res)
+    if scores:
+        res["scores"] = np.full((B, R, G, L // block), np.nan)
     for b in range(B):
         K = np.asarray(k[b], dtype=np.float64)
         V = np.asarray(v[b], dtype=np.float64)
@@ -198,8 +203,11 @@ def prefill(q, k, v, gates, *, block: int = 64, select_block=None, top_k: int, w
             inj = None if inject_idx is None else inject_idx[b, t]
             one = nsa_token(q[b, t], K, V, Kc, Vc, t, gates[b, t], block=block, top_k=top_k,
                             window=window, scale=scale, inject=inj)
-            for name in res:
+            for name in fixed:
                 res[name][b, r] = one[name]
+            if scores:
+                for g, sg in enumerate(one["scores"]):
+                    res["scores"][b, r, g, : len(sg)] = sg
     return res
 
 
@@ -211,7 +219,8 @@ def decode(q, k_cache, v_cache, kc_cache, vc_cache, seqlens, gates, *, block: in
     q [B, Hq, D]; k_cache, v_cache [B, G, Lmax, D] already holding the new
     token; kc_cache, vc_cache [B, G, Nmax, D] holding the block means of the
     complete blocks (used as given); seqlens [B]; gates [B, Hq, 3].
-    Returns out [B, Hq, D], idx [B, G, top_k], lse [B, Hq], gap [B, G].
+    Returns out [B, Hq, D], idx [B, G, top_k], lse [B, Hq], gap [B, G] and the
+    block scores [B, G, Nmax] (NaN where undefined).
     """
     _check_blocks(block, select_block)
     B, Hq, D = q.shape
@@ -223,6 +232,8 @@ def decode(q, k_cache, v_cache, kc_cache, vc_cache, seqlens, gates, *, block: in
     if branches:
         for name in ("o_cmp", "o_slc", "o_win"):
             res[name] = np.zeros((B, Hq, D))
+    fixed = list(res)
+    res["scores"] = np.full((B, G, kc_cache.shape[2]), np.nan)
     for b in range(B):
         t = int(seqlens[b]) - 1
         nvis = (t + 1) // block
@@ -233,6 +244,8 @@ def decode(q, k_cache, v_cache, kc_cache, vc_cache, seqlens, gates, *, block: in
         inj = None if inject_idx is None else inject_idx[b]
         one = nsa_token(q[b], K, V, Kc, Vc, t, gates[b], block=block, top_k=top_k,
                         window=window, scale=scale, inject=inj)
-        for name in res:
+        for name in fixed:
             res[name][b] = one[name]
+        for g, sg in enumerate(one["scores"]):
+            res["scores"][b, g, : len(sg)] = sg
     return res

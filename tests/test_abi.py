@@ -1,0 +1,184 @@
+"""CPU-only checks of the C ABI: the library loads, exports what include/nsa.h
+declares, and rejects every invalid call on the host before any launch.
+
+No call here reaches a kernel launch: each either fails validation or has an
+empty problem (batch 0, fewer tokens than a block), which returns before
+touching the GPU.
+"""
+
+import ctypes
+
+import pytest
+
+from long_context_sparse_fwd_amd import nsa
+
+OK, INV, UNS, WS = (nsa.NSA_OK, nsa.NSA_ERR_INVALID_ARGUMENT, nsa.NSA_ERR_UNSUPPORTED,
+                    nsa.NSA_ERR_WORKSPACE_TOO_SMALL)
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced by these calls
+
+
+@pytest.fixture(scope="module")
+def L():
+    return nsa.lib()
+
+
+def test_library_exports_every_declared_function(L):
+    names = nsa.header_functions()
+    assert {"nsa_fwd_prefill", "nsa_fwd_decode", "nsa_compress_kv", "nsa_prefill_workspace_bytes",
+            "nsa_decode_workspace_bytes", "nsa_status_string", "nsa_last_error", "nsa_version",
+            "nsa_fwd_prefill_timed", "nsa_fwd_decode_timed"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.nsa_version() >= 100
+
+
+def test_status_strings(L):
+    for code, name in [(0, "NSA_OK"), (1, "NSA_ERR_INVALID_ARGUMENT"), (2, "NSA_ERR_UNSUPPORTED"),
+                       (3, "NSA_ERR_WORKSPACE_TOO_SMALL"), (4, "NSA_ERR_HIP")]:
+        assert L.nsa_status_string(code).decode() == name
+
+
+def pdesc(B=1, Lq=65536, Hq=64, G=4, D=128, dt=nsa.NSA_BF16, odt=nsa.NSA_BF16):
+    d = nsa.PrefillDesc()
+    d.batch, d.seqlen, d.n_q_heads, d.n_kv_heads, d.head_dim = B, Lq, Hq, G, D
+    d.in_dtype, d.out_dtype = dt, odt
+    d.q_stride[:] = (Lq * Hq * D, Hq * D, D)
+    d.k_stride[:] = (Lq * G * D, G * D, D)
+    d.v_stride[:] = (Lq * G * D, G * D, D)
+    d.g_stride[:] = (Lq * Hq * 3, Hq * 3, 3)
+    d.o_stride[:] = (Lq * Hq * D, Hq * D, D)
+    return d
+
+
+def ddesc(B=64, Lm=65536, Hq=64, G=4, D=128, nmax=None):
+    d = nsa.DecodeDesc()
+    d.batch, d.max_seqlen = B, Lm
+    d.max_blocks = Lm // 64 if nmax is None else nmax
+    d.n_q_heads, d.n_kv_heads, d.head_dim = Hq, G, D
+    d.in_dtype = d.out_dtype = nsa.NSA_BF16
+    d.q_stride[:] = (Hq * D, D)
+    d.k_stride[:] = (G * Lm * D, Lm * D, D)
+    d.v_stride[:] = (G * Lm * D, Lm * D, D)
+    d.kc_stride[:] = (G * d.max_blocks * D, d.max_blocks * D, D)
+    d.vc_stride[:] = (G * d.max_blocks * D, d.max_blocks * D, D)
+    d.g_stride[:] = (Hq * 3, 3)
+    d.o_stride[:] = (Hq * D, D)
+    return d
+
+
+def ws_prefill(L, d, p):
+    n = ctypes.c_size_t(0)
+    st = L.nsa_prefill_workspace_bytes(ctypes.byref(d), ctypes.byref(p), ctypes.byref(n))
+    return st, n.value
+
+
+def test_prefill_workspace_size_is_the_sum_of_its_parts(L):
+    st, n = ws_prefill(L, pdesc(), nsa.make_params(16, 512))
+    assert st == OK
+    tiles = 2 * 4 * 1024 * 64 * 128 * 2          # K and V tiles
+    ctiles = 2 * 4 * 16 * 64 * 128 * 2           # block-mean tiles
+    idx = 65536 * 4 * 16 * 4
+    assert n == tiles + ctiles + idx
+
+
+@pytest.mark.parametrize("mut,code", [
+    (lambda d, p: setattr(d, "n_q_heads", 65), INV),          # not a multiple of G
+    (lambda d, p: setattr(d, "n_kv_heads", 2), UNS),          # 32 heads per group
+    (lambda d, p: setattr(d, "head_dim", 96), UNS),
+    (lambda d, p: setattr(d, "head_dim", 0), INV),
+    (lambda d, p: setattr(d, "batch", -1), INV),
+    (lambda d, p: setattr(d, "in_dtype", 7), INV),
+    (lambda d, p: setattr(d, "in_dtype", nsa.NSA_F32), UNS),  # f32 in, bf16 out
+    (lambda d, p: d.q_stride.__setitem__(1, 8 * 1000 + 4), INV),
+    (lambda d, p: d.k_stride.__setitem__(0, -8), INV),
+    (lambda d, p: setattr(p, "compress_block_size", 32), UNS),
+    (lambda d, p: setattr(p, "select_block_size", 128), UNS),
+    (lambda d, p: setattr(p, "select_block_size", 0), INV),
+    (lambda d, p: setattr(p, "select_top_k", 0), INV),
+    (lambda d, p: setattr(p, "select_top_k", 65), UNS),
+    (lambda d, p: setattr(p, "sliding_window", 0), INV),
+    (lambda d, p: setattr(p, "softmax_scale", float("nan")), INV),
+])
+def test_prefill_validation(L, mut, code):
+    d, p = pdesc(), nsa.make_params(16, 512)
+    mut(d, p)
+    st, _ = ws_prefill(L, d, p)
+    assert st == code, L.nsa_last_error()
+    st = L.nsa_fwd_prefill(ctypes.byref(d), ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                           FAKE, 1 << 40, None)
+    assert st == code
+    assert L.nsa_last_error().decode() != ""
+
+
+def test_prefill_pointer_and_workspace_checks(L):
+    d, p = pdesc(Lq=4096), nsa.make_params(16, 512)
+    _, need = ws_prefill(L, d, p)
+    call = lambda q=FAKE, out=FAKE, idx=None, mode=0, ws=FAKE, nb=need: L.nsa_fwd_prefill(
+        ctypes.byref(d), ctypes.byref(p), q, FAKE, FAKE, FAKE, out, idx, mode, ws, nb, None)
+    assert call(q=None) == INV
+    assert call(q=FAKE + 2) == INV            # misaligned
+    assert call(out=None) == INV
+    assert call(ws=None) == INV
+    assert call(mode=1) == INV                # inject without idx
+    assert call(mode=5) == INV
+    assert call(idx=FAKE + 2) == INV
+    assert call(nb=need - 1) == WS
+    assert "workspace" in L.nsa_last_error().decode()
+
+
+def test_prefill_empty_problem_is_ok_without_launch(L):
+    p = nsa.make_params(16, 512)
+    for d in (pdesc(B=0), pdesc(Lq=0)):
+        assert L.nsa_fwd_prefill(ctypes.byref(d), ctypes.byref(p), None, None, None, None, None, None,
+                                 0, None, 0, None) == OK
+
+
+def test_timed_variants_need_events(L):
+    d, p = pdesc(Lq=256), nsa.make_params(4, 64)
+    assert L.nsa_fwd_prefill_timed(ctypes.byref(d), ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None, 0, FAKE, 1 << 40, None, None) == INV
+    ev = (ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)
+    assert L.nsa_fwd_prefill_timed(ctypes.byref(d), ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None, 0, FAKE, 1 << 40, None, ev) == INV
+    dd = ddesc(B=2, Lm=512)
+    assert L.nsa_fwd_decode_timed(ctypes.byref(dd), ctypes.byref(p), *([FAKE] * 8), None, 0, FAKE,
+                                  1 << 40, None, None) == INV
+
+
+def test_decode_workspace_and_validation(L):
+    p = nsa.make_params(16, 512)
+    n = ctypes.c_size_t()
+    d = ddesc()
+    assert L.nsa_decode_workspace_bytes(ctypes.byref(d), ctypes.byref(p), ctypes.byref(n)) == OK
+    # partial states: 4 slots per split; splits: 4 compressed + 2 window + 4 selected, + 1 merged
+    nslots = 4 * (4 + 2 + 4) + 1
+    part = 64 * 4 * nslots * (32 + 16 * 128) * 4
+    logits = 64 * 4 * 16 * 1024 * 4
+    assert n.value == part + logits + 64 * 4 * 16 * 4
+    bad = ddesc(nmax=1000)                       # block cache shorter than Lmax/64
+    assert L.nsa_decode_workspace_bytes(ctypes.byref(bad), ctypes.byref(p), ctypes.byref(n)) == INV
+    bad = ddesc()
+    bad.max_seqlen = 0
+    assert L.nsa_decode_workspace_bytes(ctypes.byref(bad), ctypes.byref(p), ctypes.byref(n)) == INV
+    call = lambda d, ptrs, nb=n.value: L.nsa_fwd_decode(ctypes.byref(d), ctypes.byref(p), *ptrs, None, 0,
+                                                       FAKE, nb, None)
+    good = [FAKE] * 8
+    for i in range(8):
+        ptrs = list(good)
+        ptrs[i] = None
+        assert call(d, ptrs) == INV, i
+    assert call(d, good, nb=10) == WS
+    assert call(ddesc(B=0), [None] * 8) == OK
+
+
+def test_compress_validation(L):
+    s = (ctypes.c_int64 * 3)(4 * 128 * 128, 128 * 128, 128)
+    f = lambda B=1, G=4, T=128, D=128, dt=1, bs=64, k=FAKE: L.nsa_compress_kv(
+        B, G, T, D, dt, bs, k, s, FAKE, s, FAKE, s, FAKE, s, None)
+    assert f(bs=32) == UNS
+    assert f(bs=0) == INV
+    assert f(G=0) == INV
+    assert f(dt=9) == INV
+    assert f(k=None) == INV
+    assert f(T=63) == OK          # no complete block: nothing to do
+    assert f(B=0) == OK

@@ -1,0 +1,196 @@
+"""GPU parity of nsa_fwd_prefill against the float64 oracle (through the C ABI).
+
+Small cases are compared on every row; the 8k / 32k / 64k workloads run in
+full on the GPU, exactly as the benchmark launches them, and are compared on
+sampled rows that the oracle computes one by one, plus row-format properties
+that must hold on every row.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_fwd_amd import inputs, nsa
+from oracle import nsa_ref
+from tests.parity import TOL, Lazy, check_indices, dev, maxabs
+
+pytestmark = pytest.mark.gpu
+
+
+def _upload(cfg, raw):
+    return [dev(raw[n], cfg.dtype) for n in ("q", "k", "v", "gates")]
+
+
+def _oracle(cfg, raw, rows, inject=None):
+    lz = {n: Lazy(raw[n], cfg.dtype) for n in raw}
+    return nsa_ref.prefill(lz["q"], lz["k"], lz["v"], lz["gates"], block=cfg.block, top_k=cfg.top_k,
+                           window=cfg.window, rows=rows, inject_idx=inject, scores=inject is None)
+
+
+def run_case(cfg, rows=None, check_c=True):
+    """Checks A, B and C for one prefill workload; returns a small report."""
+    raw = inputs.make_prefill_inputs(cfg)
+    q, k, v, g = _upload(cfg, raw)
+    print(f"[prefill] {cfg}", flush=True)
+    out, idx = nsa.prefill(q, k, v, g, top_k=cfg.top_k, window=cfg.window, out_dtype=torch.float32,
+                           return_idx=True)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    go = out.cpu().numpy().astype(np.float64)
+    B, L, G, n = gi.shape
+    rows = np.arange(L) if rows is None else np.asarray(sorted(set(int(r) for r in rows if 0 <= r < L)))
+    orc = _oracle(cfg, raw, rows)
+
+    # Check A on the sampled rows
+    gsel = gi[:, rows]                                      # [B, R, G, n]
+    own = np.broadcast_to((rows // cfg.block)[None, :, None], gsel.shape[:3])
+    exact, excused, bad = check_indices(gsel.reshape(-1, n), orc["idx"].reshape(-1, n),
+                                        orc["gap"].reshape(-1), orc["scores"].reshape(-1, orc["scores"].shape[-1]),
+                                        own.reshape(-1), n)
+    assert not bad, f"index mismatches: {bad[:5]}"
+
+    # Check B: matching rows against the oracle, differing (excused) rows against
+    # the oracle re-run with the GPU's selection injected
+    expect = orc["out"].copy()
+    differ = np.argwhere(np.any(gsel != orc["idx"], axis=(2, 3)))
+    if len(differ):
+        for b, r in differ:
+            re = _oracle(cfg, {kk: vv[b:b + 1] for kk, vv in raw.items()}, [rows[r]],
+                         inject=gi[b:b + 1])
+            expect[b, r] = re["out"][0, 0]
+    err_b = maxabs(go[:, rows], expect)
+    assert err_b <= TOL[cfg.dtype], f"free-running output error {err_b}"
+
+    err_c = None
+    if check_c:
+        inj = gi.copy()
+        inj[:, rows] = orc["idx"]
+        out_c = nsa.prefill(q, k, v, g, top_k=cfg.top_k, window=cfg.window, out_dtype=torch.float32,
+                            idx=torch.from_numpy(inj).cuda(), inject=True)[0]
+        torch.cuda.synchronize()
+        err_c = maxabs(out_c.cpu().numpy()[:, rows], orc["out"])
+        assert err_c <= TOL[cfg.dtype], f"injected-index output error {err_c}"
+    print(f"  rows={len(rows)} exact={exact} excused={excused} errB={err_b:.3g} errC={err_c}", flush=True)
+    return {"gpu_idx": gi, "gpu_out": go, "rows": rows, "oracle": orc, "tensors": (q, k, v, g)}
+
+
+def assert_rows_well_formed(gi, block):
+    """Every row: ascending valid indices, -1 padding, own block present, range [0, own]."""
+    B, L, G, n = gi.shape
+    own = (np.arange(L) // block)[None, :, None]
+    valid = gi >= 0
+    cnt = valid.sum(-1)
+    assert np.all(cnt == np.minimum(n, own + 1))
+    assert np.all(valid[..., :-1] | ~valid[..., 1:])            # padding only at the end
+    big = np.where(valid, gi, np.iinfo(np.int32).max)
+    assert np.all(np.diff(big, axis=-1) > 0)                     # strictly ascending
+    assert np.all(gi <= own)
+    assert np.all(np.any(gi == own[..., None], axis=-1))
+
+
+# ------------------------------------------------------------------ full-row cases
+
+def test_tiny_fp32_config():
+    run_case(inputs.CONFIGS["tiny"])
+
+
+@pytest.mark.parametrize("cfg", [
+    inputs.PrefillConfig("bf16-ragged", 1, 1381, 32, 2, 128, "bf16", top_k=16, window=512),
+    inputs.PrefillConfig("bf16-d64-b2", 2, 777, 16, 2, 64, "bf16", top_k=5, window=100),
+    inputs.PrefillConfig("bf16-hg3", 1, 300, 6, 2, 128, "bf16", top_k=3, window=70),
+    inputs.PrefillConfig("f32-hg1", 1, 333, 2, 2, 64, "f32", top_k=4, window=33),
+    inputs.PrefillConfig("f32-d128", 1, 260, 8, 1, 128, "f32", top_k=2, window=64),
+], ids=lambda c: c.name)
+def test_prefill_full_rows(cfg):
+    run_case(cfg)
+
+
+@pytest.mark.parametrize("L", [1, 2, 63, 64, 65, 127, 128, 129])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_short_sequences(L, dtype):
+    run_case(inputs.PrefillConfig(f"short{L}", 1, L, 16, 1, 64, dtype, top_k=3, window=40))
+
+
+@pytest.mark.parametrize("top_k,window", [(1, 1), (64, 1), (2, 10000), (40, 3)])
+def test_prefill_parameter_extremes(top_k, window):
+    run_case(inputs.PrefillConfig(f"ext{top_k}-{window}", 1, 700, 16, 2, 64, "bf16", top_k=top_k,
+                                  window=window))
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _sample_rows(L, seed=0, n_random=36):
+    fixed = [0, 1, 62, 63, 64, 65, 127, 511, 512, 513, 4095, 4096, L // 2, L - 65, L - 64, L - 2, L - 1]
+    rnd = np.random.default_rng(seed).integers(0, L, n_random).tolist()
+    return fixed + rnd
+
+
+@pytest.mark.parametrize("name", ["p8k", "p32k", "p64k"])
+def test_full_size_prefill_sampled_rows(name):
+    cfg = inputs.CONFIGS[name]
+    rep = run_case(cfg, rows=_sample_rows(cfg.seqlen), check_c=True)
+    assert_rows_well_formed(rep["gpu_idx"], cfg.block)
+    assert np.all(np.isfinite(rep["gpu_out"]))
+
+
+# ------------------------------------------------------------------ properties
+
+def test_bf16_output_matches_fp32_output_to_rounding():
+    cfg = inputs.PrefillConfig("bf16out", 1, 900, 16, 1, 128, "bf16", top_k=6, window=128)
+    raw = inputs.make_prefill_inputs(cfg)
+    q, k, v, g = _upload(cfg, raw)
+    o32, i32 = nsa.prefill(q, k, v, g, top_k=6, window=128, out_dtype=torch.float32, return_idx=True)
+    o16, i16 = nsa.prefill(q, k, v, g, top_k=6, window=128, out_dtype=torch.bfloat16, return_idx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(i32, i16)
+    # at most two bf16 roundings (relative 2^-9 each) of terms bounded by |out| + 1
+    assert torch.all((o16.float() - o32).abs() <= 2 ** -8 * (o32.abs() + 1))
+
+
+def test_prefill_is_deterministic():
+    cfg = inputs.PrefillConfig("det", 1, 2000, 64, 4, 128, "bf16", top_k=16, window=512)
+    raw = inputs.make_prefill_inputs(cfg)
+    q, k, v, g = _upload(cfg, raw)
+    ref = nsa.prefill(q, k, v, g, top_k=16, window=512, return_idx=True)
+    for _ in range(3):
+        o, i = nsa.prefill(q, k, v, g, top_k=16, window=512, return_idx=True)
+        assert torch.equal(o.view(torch.int16), ref[0].view(torch.int16))
+        assert torch.equal(i, ref[1])
+
+
+def test_prefill_writes_only_its_outputs():
+    # out and idx are views inside larger buffers filled with a sentinel: the
+    # call must leave everything around them untouched
+    cfg = inputs.PrefillConfig("guard", 1, 333, 16, 2, 64, "bf16", top_k=4, window=50)
+    raw = inputs.make_prefill_inputs(cfg)
+    q, k, v, g = _upload(cfg, raw)
+    big = torch.full((3, 333, 16, 64), 7.25, dtype=torch.float32, device="cuda")
+    ibig = torch.full((3 * 333 * 2 * 4,), -77, dtype=torch.int32, device="cuda")
+    out = big[1:2]
+    idx = ibig[333 * 2 * 4: 2 * 333 * 2 * 4].view(1, 333, 2, 4)
+    nsa.prefill(q, k, v, g, top_k=4, window=50, out=out, idx=idx)
+    torch.cuda.synchronize()
+    assert torch.all(big[0] == 7.25) and torch.all(big[2] == 7.25)
+    assert torch.all(ibig[: 333 * 8] == -77) and torch.all(ibig[2 * 333 * 8:] == -77)
+    assert torch.all(torch.isfinite(out))
+
+
+def test_strided_inputs():
+    # q/k/v/gates/out as views of packed buffers (non-default strides)
+    cfg = inputs.PrefillConfig("strided", 1, 400, 16, 2, 64, "bf16", top_k=4, window=60)
+    raw = inputs.make_prefill_inputs(cfg)
+    q, k, v, g = _upload(cfg, raw)
+    ref, ridx = nsa.prefill(q, k, v, g, top_k=4, window=60, out_dtype=torch.float32, return_idx=True)
+    qkv = torch.zeros((1, 400, 16 + 2 + 2, 64), dtype=torch.bfloat16, device="cuda")
+    qkv[:, :, :16] = q
+    qkv[:, :, 16:18] = k
+    qkv[:, :, 18:20] = v
+    gb = torch.zeros((1, 400, 16, 5), dtype=torch.bfloat16, device="cuda")
+    gb[..., 1:4] = g
+    ob = torch.zeros((1, 400, 16, 72), dtype=torch.float32, device="cuda")
+    out, idx = nsa.prefill(qkv[:, :, :16], qkv[:, :, 16:18], qkv[:, :, 18:20], gb[..., 1:4], top_k=4,
+                           window=60, out=ob[..., :64], return_idx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, ridx)
+    assert torch.equal(out, ref)
+    assert torch.all(ob[..., 64:] == 0)
