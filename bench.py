@@ -171,8 +171,12 @@ def cpu_baseline(cfg, raw, seconds: float):
         return time.perf_counter() - t0
 
     L = cfg.seqlen
-    probe = run(np.linspace(0, L - 1, 4).astype(np.int64))
-    n_rows = int(max(8, min(4096, 4 * (seconds - probe) / max(probe, 1e-3))))
+    # per-row cost from two probes (the difference removes the fixed per-call cost)
+    t_small = run(np.linspace(0, L - 1, 8).astype(np.int64))
+    t_big = run(np.linspace(0, L - 1, 72).astype(np.int64))
+    per_row = max((t_big - t_small) / 64, 1e-5)
+    fixed = max(t_small - 8 * per_row, 0.0)
+    n_rows = int(max(16, min(20000, (seconds - fixed) / per_row)))
     rows = np.linspace(0, L - 1, n_rows).astype(np.int64)
     dt = run(rows)
     if limiter is not None:

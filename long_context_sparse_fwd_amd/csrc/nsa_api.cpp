@@ -102,7 +102,7 @@ nsa_status_t check_ptr(const char* name, const void* p, bool need16) {
 
 struct PrefillPlan {
   int Nb, Nc, NcT, cmp_waves, cmp_tiles, sw_tiles;
-  size_t off_kt, off_vt, off_kct, off_vct, off_idx, total;
+  size_t off_kt, off_vt, off_kct, off_kclt, off_vct, off_idx, total;
 };
 
 nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, PrefillPlan* pl) {
@@ -146,6 +146,8 @@ nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, Pr
   off = align_up(off + static_cast<size_t>(B * G) * pl->Nb * tile);
   pl->off_kct = off;
   off = align_up(off + static_cast<size_t>(B * G) * pl->NcT * tile);
+  pl->off_kclt = off;  // low parts of the bf16 block means of K
+  if (d->in_dtype == NSA_BF16) off = align_up(off + static_cast<size_t>(B * G) * pl->NcT * tile);
   pl->off_vct = off;
   off = align_up(off + static_cast<size_t>(B * G) * pl->NcT * tile);
   pl->off_idx = off;
@@ -305,6 +307,7 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
   a.kt = ws + pl.off_kt;
   a.vt = ws + pl.off_vt;
   a.kct = ws + pl.off_kct;
+  a.kclt = ws + pl.off_kclt;
   a.vct = ws + pl.off_vct;
   for (int i = 0; i < 3; ++i) {
     a.qs[i] = desc->q_stride[i];

@@ -33,8 +33,9 @@ struct PrefillArgs {
   int32_t* idx;
   void* kt;   // [B][G][Nb] 64-key K tiles (fragment-major)
   void* vt;   // [B][G][Nb] 64-key V^T tiles
-  void* kct;  // [B][G][NcT] 64-block tiles of block means of K
-  void* vct;  // same for V
+  void* kct;   // [B][G][NcT] 64-block tiles of block means of K (bf16: the high part)
+  void* kclt;  // bf16 input only: the low part, bf16(mean - high), same layout
+  void* vct;   // [B][G][NcT] 64-block V^T tiles of block means of V
   int64_t qs[3], ks[3], vs[3], gs[3], os[3];
 };
 

@@ -57,6 +57,15 @@ __device__ __forceinline__ f32x4 load4<F32>(const float* p) {
   return *reinterpret_cast<const f32x4*>(p);
 }
 
+// The block means of K enter the block scores, and the selection is judged
+// against exact means: with bf16 operands the mean is carried as a high part
+// plus a bf16 low part (hi + lo holds ~16 significant bits), and every
+// compressed-branch QK product is the sum of two MFMAs.
+template <class T>
+constexpr bool kSplitKc = false;
+template <>
+constexpr bool kSplitKc<BF16> = true;
+
 // ------------------------------------------------------------------ k_prep
 
 template <class T, int D>
@@ -111,6 +120,7 @@ __global__ __launch_bounds__(256) void k_prep(PrefillArgs a) {
     const int64_t tile = (static_cast<int64_t>(b * a.G + g) * a.NcT + c) * (64 * D);
     S* kc = static_cast<S*>(a.kct) + tile;
     S* vc = static_cast<S*>(a.vct) + tile;
+    S* kcl = kSplitKc<T> ? static_cast<S*>(a.kclt) + tile : nullptr;
     for (int d = tid; d < D; d += 256) {
       float sk = 0.f, sv = 0.f;
       if (j < a.Nc) {
@@ -121,7 +131,9 @@ __global__ __launch_bounds__(256) void k_prep(PrefillArgs a) {
         sk *= (1.0f / 64.0f);
         sv *= (1.0f / 64.0f);
       }
-      kc[ktile_off(r, d, D)] = from_f32<T>(sk);
+      const S hi = from_f32<T>(sk);
+      kc[ktile_off(r, d, D)] = hi;
+      if (kSplitKc<T>) kcl[ktile_off(r, d, D)] = from_f32<T>(sk - to_f32<T>(hi));
       vc[vtile_off(r, d)] = from_f32<T>(sv);
     }
   }
@@ -166,6 +178,7 @@ __global__ __launch_bounds__(256) void k_cmp(PrefillArgs a) {
   const int nch = (nvmax + 63) >> 6;
   const int64_t tbase = static_cast<int64_t>(b * a.G + g) * a.NcT * (64 * D);
   const S* KC = static_cast<const S*>(a.kct) + tbase;
+  const S* KCL = kSplitKc<T> ? static_cast<const S*>(a.kclt) + tbase : nullptr;
   const S* VC = static_cast<const S*>(a.vct) + tbase;
   const float sl2 = a.scale_log2;
 
@@ -177,18 +190,24 @@ __global__ __launch_bounds__(256) void k_cmp(PrefillArgs a) {
     ls[qt] = 0.f;
   }
   for (int c = 0; c < nch; ++c) {
-    const S* kc = KC + static_cast<int64_t>(c) * (64 * D);
+    const int64_t coff = static_cast<int64_t>(c) * (64 * D);
     f32x4 st[TPW][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      Frag<T> kf[KS];
+      Frag<T> kf[KS], kl[KS];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kf[s] = frag_load<T>(kc + ktile_frag(kt, s, lane, D));
+      for (int s = 0; s < KS; ++s) {
+        kf[s] = frag_load<T>(KC + coff + ktile_frag(kt, s, lane, D));
+        if (kSplitKc<T>) kl[s] = frag_load<T>(KCL + coff + ktile_frag(kt, s, lane, D));
+      }
 #pragma unroll
       for (int qt = 0; qt < TPW; ++qt) {
         st[qt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) mma(st[qt][kt], kf[s], qf[qt][s]);
+        for (int s = 0; s < KS; ++s) {
+          mma(st[qt][kt], kf[s], qf[qt][s]);
+          if (kSplitKc<T>) mma(st[qt][kt], kl[s], qf[qt][s]);
+        }
       }
     }
 #pragma unroll
@@ -231,21 +250,27 @@ __global__ __launch_bounds__(256) void k_cmp(PrefillArgs a) {
     for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int c = 0; c < nch; ++c) {
-    const S* kc = KC + static_cast<int64_t>(c) * (64 * D);
-    const S* vc = VC + static_cast<int64_t>(c) * (64 * D);
+    const int64_t coff = static_cast<int64_t>(c) * (64 * D);
+    const S* vc = VC + coff;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       f32x4 st[TPW][2];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        Frag<T> kf[KS];
+        Frag<T> kf[KS], kl[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kf[s] = frag_load<T>(kc + ktile_frag(2 * s2 + h2, s, lane, D));
+        for (int s = 0; s < KS; ++s) {
+          kf[s] = frag_load<T>(KC + coff + ktile_frag(2 * s2 + h2, s, lane, D));
+          if (kSplitKc<T>) kl[s] = frag_load<T>(KCL + coff + ktile_frag(2 * s2 + h2, s, lane, D));
+        }
 #pragma unroll
         for (int qt = 0; qt < TPW; ++qt) {
           st[qt][h2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < KS; ++s) mma(st[qt][h2], kf[s], qf[qt][s]);
+          for (int s = 0; s < KS; ++s) {
+            mma(st[qt][h2], kf[s], qf[qt][s]);
+            if (kSplitKc<T>) mma(st[qt][h2], kl[s], qf[qt][s]);
+          }
         }
       }
       Frag<T> vf[DT];

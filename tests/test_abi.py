@@ -76,7 +76,7 @@ def test_prefill_workspace_size_is_the_sum_of_its_parts(L):
     st, n = ws_prefill(L, pdesc(), nsa.make_params(16, 512))
     assert st == OK
     tiles = 2 * 4 * 1024 * 64 * 128 * 2          # K and V tiles
-    ctiles = 2 * 4 * 16 * 64 * 128 * 2           # block-mean tiles
+    ctiles = 3 * 4 * 16 * 64 * 128 * 2           # block-mean tiles (K high, K low, V)
     idx = 65536 * 4 * 16 * 4
     assert n == tiles + ctiles + idx
 

@@ -51,10 +51,10 @@ def run_decode(cfg, batches=None, check_c=True):
                          top_k=cfg.top_k, window=cfg.window)
     n = cfg.top_k
     own = np.broadcast_to(((raw["seqlens"][sel] - 1) // cfg.block)[:, None], orc["idx"].shape[:2])
+    sc = orc["scores"]
+    sc = sc.reshape(-1, sc.shape[-1]) if sc.shape[-1] else np.zeros((own.size, 1))
     exact, excused, bad = check_indices(gi[sel].reshape(-1, n), orc["idx"].reshape(-1, n),
-                                        orc["gap"].reshape(-1),
-                                        orc["scores"].reshape(-1, orc["scores"].shape[-1]),
-                                        own.reshape(-1), n)
+                                        orc["gap"].reshape(-1), sc, own.reshape(-1), n)
     assert not bad, f"index mismatches: {bad[:5]}"
     expect = orc["out"].copy()
     for r in np.argwhere(np.any(gi[sel] != orc["idx"], axis=2))[:, 0]:
