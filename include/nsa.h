@@ -192,9 +192,10 @@ nsa_status_t nsa_compress_kv(int32_t batch, int32_t n_kv_heads, int32_t n_tokens
  * (passed as void*) on the stream: before each of the call's kernels and
  * after the last one. Prefill runs 3 kernels (block compression + re-layout;
  * compressed branch + block selection; selected + window branches + gate
- * combination), so stage_events holds 4 events; decode runs 4 kernels
- * (compressed and window chunks; selection; selected chunks; combination),
- * so it holds 5. A NULL array or entry is NSA_ERR_INVALID_ARGUMENT.
+ * combination), so stage_events holds 4 events; decode runs 2 kernels
+ * (compressed and window chunks; merge + selection + selected blocks +
+ * combination), so it holds 3. A NULL array or entry is
+ * NSA_ERR_INVALID_ARGUMENT.
  */
 nsa_status_t nsa_fwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
                                    const void* q, const void* k, const void* v, const void* gates,

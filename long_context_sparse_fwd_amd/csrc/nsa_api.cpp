@@ -101,7 +101,7 @@ nsa_status_t check_ptr(const char* name, const void* p, bool need16) {
 // ------------------------------------------------------------------ prefill
 
 struct PrefillPlan {
-  int Nb, Nc, NcT, cmp_waves, cmp_tiles, sw_tiles;
+  int Nb, Nc, NcT, cmp_waves, cmp_tiles, sel_tiles;
   size_t off_kt, off_vt, off_kct, off_kclt, off_vct, off_idx, total;
 };
 
@@ -125,8 +125,9 @@ nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, Pr
   pl->Nc = static_cast<int>(L / 64);
   pl->NcT = (pl->Nc + 63) / 64;
   pl->cmp_waves = 0;
-  for (int w = 4; w >= 1; w /= 2)
-    if (nsa::cmp_lds_bytes(w, pl->NcT) <= static_cast<size_t>(nsa::kMaxLds)) {
+  for (int w = 8; w >= 1; w /= 2)
+    if (nsa::cmpwin_lds_bytes(w, pl->NcT, static_cast<int>(D), d->in_dtype == NSA_BF16) <=
+        static_cast<size_t>(nsa::kMaxLds)) {
       pl->cmp_waves = w;
       break;
     }
@@ -134,9 +135,9 @@ nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, Pr
     return fail(NSA_ERR_UNSUPPORTED, "seqlen %lld needs more LDS for block scores than a CU has",
                 static_cast<long long>(L));
   const int64_t tok_cmp = static_cast<int64_t>(pl->cmp_waves) * nsa::kCmpTPW;
-  const int64_t tok_sw = static_cast<int64_t>(nsa::kSwWaves) * nsa::kSwTPW;
+  const int64_t tok_sel = 4 * static_cast<int64_t>(nsa::kSelTPW);
   pl->cmp_tiles = static_cast<int>((L + tok_cmp - 1) / tok_cmp);
-  pl->sw_tiles = static_cast<int>((L + tok_sw - 1) / tok_sw);
+  pl->sel_tiles = static_cast<int>((L + tok_sel - 1) / tok_sel);
   const size_t elem = d->in_dtype == NSA_BF16 ? 2 : 4;
   const size_t tile = 64 * static_cast<size_t>(D) * elem;
   size_t off = 0;
@@ -159,7 +160,7 @@ nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, Pr
 // ------------------------------------------------------------------ decode
 
 struct DecodePlan {
-  int SC, SW, SS, NmaxPad, nslots;
+  int SC, SW, NmaxPad, nslots;
   size_t off_part, off_logits, off_idx, total;
 };
 
@@ -186,13 +187,12 @@ nsa_status_t plan_decode(const nsa_decode_desc_t* d, const nsa_params_t* p, Deco
   pl->SC = (nv + nsa::kDecSplitKeys - 1) / nsa::kDecSplitKeys;
   const int wv = p->sliding_window < d->max_seqlen ? p->sliding_window : d->max_seqlen;
   pl->SW = (wv + nsa::kDecSplitKeys - 1) / nsa::kDecSplitKeys;
-  pl->SS = (p->select_top_k + 3) / 4;
   pl->NmaxPad = pl->SC * nsa::kDecSplitKeys;
-  pl->nslots = 4 * (pl->SC + pl->SW + pl->SS) + 1;
+  pl->nslots = pl->SC + pl->SW;
   if (B * G > INT32_MAX / 16)
     return fail(NSA_ERR_UNSUPPORTED, "batch * n_kv_heads too large");
-  const size_t lds_sel = pl->NmaxPad * sizeof(float) + nsa::kSurvCap * 8 + 64 * 4 + 48 * 4;
-  if (lds_sel > static_cast<size_t>(nsa::kMaxLds))
+  if (nsa::dec_finish_lds_bytes(pl->NmaxPad, static_cast<int>(D), d->in_dtype == NSA_BF16) >
+      static_cast<size_t>(nsa::kMaxLds))
     return fail(NSA_ERR_UNSUPPORTED, "max_seqlen %d needs more LDS for block scores than a CU has",
                 d->max_seqlen);
   size_t off = 0;
@@ -294,7 +294,7 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
   a.NcT = pl.NcT;
   a.cmp_waves = pl.cmp_waves;
   a.cmp_tiles = pl.cmp_tiles;
-  a.sw_tiles = pl.sw_tiles;
+  a.sel_tiles = pl.sel_tiles;
   a.scale_log2 = scale_log2(params, a.D);
   a.inject = idx_mode == NSA_IDX_INJECT ? 1 : 0;
   a.q = q;
@@ -383,7 +383,6 @@ static nsa_status_t decode_impl(const nsa_decode_desc_t* desc, const nsa_params_
   a.w = params->sliding_window;
   a.SC = pl.SC;
   a.SW = pl.SW;
-  a.SS = pl.SS;
   a.NmaxPad = pl.NmaxPad;
   a.scale_log2 = scale_log2(params, a.D);
   a.inject = idx_mode == NSA_IDX_INJECT ? 1 : 0;

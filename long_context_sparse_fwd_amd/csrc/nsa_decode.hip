@@ -1,20 +1,24 @@
 // NSA decode on gfx950: one new query token per sequence against a K/V cache
 // and a block-mean cache, measured apart from prefill as the NSA how-to
-// (qwbw.cn/news/106443), section 5, advises. The work is HBM-bound (each key
-// is read once and used by the 16 heads of its group), so it is split into
-// many 64-key chunks, one per wave, each producing a partial softmax state:
+// (qwbw.cn/news/106443), section 5, advises. The work is HBM-bound: every key
+// is read once and serves the 16 query heads of its group, so the kernels
+// are organised around keeping many 32 KiB chunks in flight.
 //
-//  k_dec_scan     compressed chunks (64 blocks of the block cache) and window
-//                 chunks (64 cache tokens); also stores the compressed logits.
-//  k_dec_select   per (b, g): merge the compressed partials into the
-//                 log-sum-exp and gate_cmp * O_cmp, form the block scores
-//                 (probabilities summed over the group's heads) and select
-//                 the own block + top-(n-1) earlier blocks (nsa_topk.h).
-//  k_dec_sel      selected chunks: one selected 64-token block per wave.
-//  k_dec_combine  merge window and selected partials, add the gated branches.
+//  k_dec_scan    grid (sequence x group, compressed splits + window splits).
+//                Each wave loads one 64-key chunk (64 block means, or 64
+//                window tokens) into registers, attends the group's 16 heads
+//                over it, and the workgroup merges its 4 waves into one
+//                partial softmax state (max, sum, unnormalised output). The
+//                compressed splits also store their logits for the scores.
+//  k_dec_finish  one workgroup per (sequence, group): merges the compressed
+//                partials into the log-sum-exp and gate_cmp * O_cmp, forms
+//                the block scores (probabilities summed over the group's
+//                heads), selects the own block + top-(n-1) earlier blocks
+//                (nsa_topk.h), gathers the selected blocks across its waves,
+//                and adds the gated selected and window branches into out.
 //
 // K rows feed the S^T = K Q^T product straight from the cache; V rows go
-// through LDS into the permuted V^T tile order the P.V product expects.
+// through LDS into the permuted V^T tile order of the P.V product.
 #include "nsa_device.h"
 #include "nsa_internal.h"
 #include "nsa_topk.h"
@@ -24,63 +28,72 @@ namespace nsa {
 // floats per partial slot: m[16], l[16], O[16][D]
 __host__ __device__ constexpr int dec_slot_floats(int D) { return 32 + 16 * D; }
 
-__device__ __forceinline__ int dec_nslots(const DecodeArgs& a) { return 4 * (a.SC + a.SW + a.SS) + 1; }
-
 __device__ __forceinline__ int dec_seqlen(const DecodeArgs& a, int b) {
   const int s = a.seqlens[b];
   return (s >= 1 && s <= a.Lmax) ? s : 0;  // 0 marks an invalid sequence
 }
 
-// One wave: attention of the group's 16 query columns over the keys
-// [key0, key0 + 64) restricted to [klo, khi]; rows are read only inside that
-// range. Writes the partial state (max, sum, unnormalised output) to `slot`
-// and, if lrow != nullptr, the masked logits of the 64 keys to lrow[0..63].
+// One wave's registers for a 64-key chunk: the K rows as A operands and the V
+// rows as 8-element vectors (lane l holds rows l/(D/8) + 64 i/(D/8)).
 template <class T, int D>
-__device__ void dec_chunk(const typename T::storage* krows, int64_t kst,
-                          const typename T::storage* vrows, int64_t vst, int key0, int klo,
-                          int khi, const Frag<T> (&qf)[D / 32], float sl2,
-                          typename T::storage* lv, float* slot, float* lrow, int lane) {
-  using S = typename T::storage;
-  constexpr int KS = D / 32, DT = D / 16;
+struct Chunk {
+  Frag<T> k[4][D / 32];
+  Frag<T> v[D / 8];
+};
+
+// Loads keys [key0, key0 + 64) restricted to [klo, khi]; rows outside are
+// zero and never read.
+template <class T, int D>
+__device__ __forceinline__ void chunk_load(Chunk<T, D>& c, const typename T::storage* krows,
+                                           int64_t kst, const typename T::storage* vrows,
+                                           int64_t vst, int key0, int klo, int khi, int lane) {
   const int col = lane & 15, grp = lane >> 4;
-  const int first = max(key0, klo), last = min(key0 + 63, khi);
-  if (first > last) {
-    if (grp == 0) {
-      slot[col] = kNegBig;
-      slot[16 + col] = 0.f;
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<f32x4*>(slot + 32 + col * D + 16 * dt + 4 * grp) = f32x4{0.f, 0.f, 0.f, 0.f};
-    return;
-  }
-  f32x4 st[4];
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     const int key = key0 + 16 * kt + col;
     const bool ok = key >= klo && key <= khi;
-    Frag<T> kf[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      kf[s] = ok ? frag_load<T>(krows + static_cast<int64_t>(key) * kst + 32 * s + 8 * grp)
-                 : frag_zero<T>();
-    st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) mma(st[kt], kf[s], qf[s]);
+    for (int s = 0; s < D / 32; ++s)
+      c.k[kt][s] = ok ? frag_load<T>(krows + static_cast<int64_t>(key) * kst + 32 * s + 8 * grp)
+                      : frag_zero<T>();
   }
   constexpr int VPR = D / 8;
-  for (int e = lane; e < 64 * VPR; e += 64) {
-    const int r = e / VPR, c = (e % VPR) * 8;
-    const int key = key0 + r;
-    __align__(16) S tmp[8];
-    const Frag<T> vv = (key >= klo && key <= khi)
-                           ? frag_load<T>(vrows + static_cast<int64_t>(key) * vst + c)
-                           : frag_zero<T>();
-    frag_store<T>(tmp, vv);
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) lv[vtile_off(r, c + jj)] = tmp[jj];
+  for (int i = 0; i < VPR; ++i) {
+    const int e = lane + 64 * i;
+    const int key = key0 + e / VPR;
+    const bool ok = key >= klo && key <= khi;
+    c.v[i] = ok ? frag_load<T>(vrows + static_cast<int64_t>(key) * vst + (e % VPR) * 8) : frag_zero<T>();
   }
-  wave_lds_sync();
+}
+
+// Online-softmax update of (m, l, acc) with one loaded chunk. lv: this wave's
+// 64*D elements of LDS. lrow (optional): receives the masked log2-domain
+// logits of the chunk's 64 keys for this lane's query column.
+template <class T, int D>
+__device__ __forceinline__ void chunk_attend(const Chunk<T, D>& c, int key0, int klo, int khi,
+                                             const Frag<T> (&qf)[D / 32], float sl2,
+                                             typename T::storage* lv, float& m, float& l,
+                                             f32x4 (&acc)[D / 16], float* lrow, int lane) {
+  using S = typename T::storage;
+  constexpr int KS = D / 32, DT = D / 16, VPR = D / 8;
+  const int grp = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < VPR; ++i) {
+    const int e = lane + 64 * i;
+    const int r = e / VPR, cc = (e % VPR) * 8;
+    __align__(16) S tmp[8];
+    frag_store<T>(tmp, c.v[i]);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) lv[vtile_off(r, cc + jj)] = tmp[jj];
+  }
+  f32x4 st[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) mma(st[kt], c.k[kt][s], qf[s]);
+  }
   float mx = kNegBig;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
@@ -96,32 +109,28 @@ __device__ void dec_chunk(const typename T::storage* krows, int64_t kst,
     for (int kt = 0; kt < 4; ++kt) *reinterpret_cast<f32x4*>(lrow + 16 * kt + 4 * grp) = st[kt];
   }
   mx = col_max4(mx);
-  float l = 0.f;
+  const float mn = fmaxf(m, mx);
+  const float alpha = fast_exp2(m - mn);
+  float sum = 0.f;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float p = fast_exp2(st[kt][i] - mx);
+      const float p = fast_exp2(st[kt][i] - mn);
       st[kt][i] = p;
-      l += p;
+      sum += p;
     }
-  f32x4 o[DT];
+  l = l * alpha + sum;
+  m = mn;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+  wave_lds_sync();
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) {
     const Frag<T> pf = pack_p<T>(st[2 * s2], st[2 * s2 + 1]);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) mma(o[dt], frag_load<T>(lv + vtile_frag(dt, s2, lane)), pf);
+    for (int dt = 0; dt < DT; ++dt) mma(acc[dt], frag_load<T>(lv + vtile_frag(dt, s2, lane)), pf);
   }
-  l = col_sum4(l);
-  if (grp == 0) {
-    slot[col] = mx;
-    slot[16 + col] = l;
-  }
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-    *reinterpret_cast<f32x4*>(slot + 32 + col * D + 16 * dt + 4 * grp) = o[dt];
   wave_lds_sync();
 }
 
@@ -136,162 +145,226 @@ __device__ __forceinline__ void dec_load_q(const DecodeArgs& a, int b, int g, in
   for (int s = 0; s < D / 32; ++s) qf[s] = ok ? frag_load<T>(Q + 32 * s) : frag_zero<T>();
 }
 
+// Stores a wave's partial state (m per column, l summed over the column's
+// lanes, O^T accumulators) as m[16], l[16], O[16][D] at dst.
+template <int D>
+__device__ __forceinline__ void store_partial(float* dst, float m, float l, const f32x4 (&acc)[D / 16],
+                                              int lane) {
+  const int col = lane & 15, grp = lane >> 4;
+  if (grp == 0) {
+    dst[col] = m;
+    dst[16 + col] = l;
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+    *reinterpret_cast<f32x4*>(dst + 32 + col * D + 16 * dt + 4 * grp) = acc[dt];
+}
+
+// Merges `cnt` partial slots (stride SF floats) for head h: returns the
+// merged (max, sum); the output merge is done element-wise by the caller.
+__device__ __forceinline__ void merge_stats(const float* p, int cnt, int SF, int h, float& M, float& L) {
+  M = kNegBig;
+  for (int s = 0; s < cnt; ++s) M = fmaxf(M, p[s * SF + h]);
+  L = 0.f;
+  for (int s = 0; s < cnt; ++s) L += p[s * SF + 16 + h] * fast_exp2(p[s * SF + h] - M);
+}
+
 template <class T, int D>
 __global__ __launch_bounds__(256) void k_dec_scan(DecodeArgs a) {
   using S = typename T::storage;
+  constexpr int SF = dec_slot_floats(D), DT = D / 16;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int bg = blockIdx.x, b = bg / a.G, g = bg % a.G;
   const int sidx = blockIdx.y;
   const int seqlen = dec_seqlen(a, b);
   const int t = seqlen - 1;  // -1 for an invalid sequence: every chunk is empty
   S* lv = reinterpret_cast<S*>(smem) + wave * 64 * D;
-  float* slot = a.part + (static_cast<int64_t>(bg) * dec_nslots(a)) * dec_slot_floats(D);
   Frag<T> qf[D / 32];
   dec_load_q<T, D>(a, b, g, lane, qf);
+
+  int key0, klo, khi;
+  const S *kr, *vr;
+  int64_t kst, vst;
+  float* lrow = nullptr;
   if (sidx < a.SC) {
-    const int key0 = (4 * sidx + wave) * 64;
-    const int nvis = seqlen >> 6;
-    const S* kr = static_cast<const S*>(a.kccache) + b * a.kcs[0] + g * a.kcs[1];
-    const S* vr = static_cast<const S*>(a.vccache) + b * a.vcs[0] + g * a.vcs[1];
-    float* lrow = a.logits + (static_cast<int64_t>(bg) * 16 + (lane & 15)) * a.NmaxPad + key0;
-    dec_chunk<T, D>(kr, a.kcs[2], vr, a.vcs[2], key0, 0, nvis - 1, qf, a.scale_log2, lv,
-                    slot + (4 * sidx + wave) * dec_slot_floats(D), lrow, lane);
+    key0 = (4 * sidx + wave) * 64;
+    klo = 0;
+    khi = (seqlen >> 6) - 1;
+    kr = static_cast<const S*>(a.kccache) + b * a.kcs[0] + g * a.kcs[1];
+    vr = static_cast<const S*>(a.vccache) + b * a.vcs[0] + g * a.vcs[1];
+    kst = a.kcs[2];
+    vst = a.vcs[2];
+    lrow = a.logits + (static_cast<int64_t>(bg) * 16 + (lane & 15)) * a.NmaxPad + key0;
   } else {
-    const int ws = sidx - a.SC;
     const int wlo = max(0, seqlen - a.w);
-    const int key0 = wlo + (4 * ws + wave) * 64;
-    const S* kr = static_cast<const S*>(a.kcache) + b * a.ks[0] + g * a.ks[1];
-    const S* vr = static_cast<const S*>(a.vcache) + b * a.vs[0] + g * a.vs[1];
-    dec_chunk<T, D>(kr, a.ks[2], vr, a.vs[2], key0, wlo, t, qf, a.scale_log2, lv,
-                    slot + (4 * a.SC + 4 * ws + wave) * dec_slot_floats(D), nullptr, lane);
+    key0 = wlo + (4 * (sidx - a.SC) + wave) * 64;
+    klo = wlo;
+    khi = t;
+    kr = static_cast<const S*>(a.kcache) + b * a.ks[0] + g * a.ks[1];
+    vr = static_cast<const S*>(a.vcache) + b * a.vs[0] + g * a.vs[1];
+    kst = a.ks[2];
+    vst = a.vs[2];
+  }
+  float m = kNegBig, l = 0.f;
+  f32x4 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (max(key0, klo) <= min(key0 + 63, khi)) {
+    Chunk<T, D> c;
+    chunk_load<T, D>(c, kr, kst, vr, vst, key0, klo, khi, lane);
+    chunk_attend<T, D>(c, key0, klo, khi, qf, a.scale_log2, lv, m, l, acc, lrow, lane);
+  }
+  l = col_sum4(l);
+  // merge the 4 waves through LDS (reusing the V staging area)
+  __syncthreads();
+  float* mrg = reinterpret_cast<float*>(smem);
+  store_partial<D>(mrg + wave * SF, m, l, acc, lane);
+  __syncthreads();
+  float* slot = a.part + (static_cast<int64_t>(bg) * (a.SC + a.SW) + sidx) * SF;
+  if (tid < 16) {
+    float M, L;
+    merge_stats(mrg, 4, SF, tid, M, L);
+    slot[tid] = M;
+    slot[16 + tid] = L;
+  }
+  for (int e = tid; e < 16 * D; e += 256) {
+    const int h = e / D;
+    float M = kNegBig;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg[w * SF + h]);
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o += mrg[w * SF + 32 + e] * fast_exp2(mrg[w * SF + h] - M);
+    slot[32 + e] = o;
   }
 }
 
-template <class T, int D>
-__global__ __launch_bounds__(256) void k_dec_select(DecodeArgs a) {
+template <class T, class O, int D, int FW>
+__global__ __launch_bounds__(512) void k_dec_finish(DecodeArgs a) {
   using S = typename T::storage;
+  using SO = typename O::storage;
+  constexpr int SF = dec_slot_floats(D), DT = D / 16, NT = 64 * FW;
   extern __shared__ __align__(16) unsigned char smem[];
   float* sc = reinterpret_cast<float*>(smem);
-  uint64_t* surv = reinterpret_cast<uint64_t*>(smem + a.NmaxPad * sizeof(float));
+  uint64_t* surv = reinterpret_cast<uint64_t*>(sc + a.NmaxPad);
   int* selb = reinterpret_cast<int*>(surv + kSurvCap);
-  float* Ms = reinterpret_cast<float*>(selb + 64);
-  float* Ls = Ms + 16;
-  float* L2 = Ls + 16;
+  int* selo = selb + 64;
+  float* hs = reinterpret_cast<float*>(selo + 64);  // per head: M, L, lse2, g_cmp
+  float* ocmp = hs + 64;                            // [16][D]
+  unsigned char* big = reinterpret_cast<unsigned char*>(ocmp + 16 * D);
+
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int bg = blockIdx.x, b = bg / a.G, g = bg % a.G;
   const int seqlen = dec_seqlen(a, b);
-  constexpr int SF = dec_slot_floats(D);
-  const float* P = a.part + static_cast<int64_t>(bg) * dec_nslots(a) * SF;
-  float* cmp = a.part + (static_cast<int64_t>(bg) * dec_nslots(a) + dec_nslots(a) - 1) * SF + 32;
+  const int nslot = a.SC + a.SW;
+  const float* P = a.part + static_cast<int64_t>(bg) * nslot * SF;
   int32_t* idxo = a.idx + static_cast<int64_t>(bg) * a.n;
+  const S* GT = static_cast<const S*>(a.gates) + b * a.gs[0];
+  SO* OUT = static_cast<SO*>(a.out) + b * a.os[0];
   if (seqlen == 0) {
+    for (int e = tid; e < a.Hg * D; e += NT) OUT[(g * a.Hg + e / D) * a.os[1] + e % D] = from_f32<O>(0.f);
     if (!a.inject && tid < a.n) idxo[tid] = -1;
-    for (int e = tid; e < 16 * D; e += 256) cmp[e] = 0.f;
     return;
   }
   const int t = seqlen - 1, nvis = seqlen >> 6, own = t >> 6;
-  const int ncs = 4 * a.SC;
-  if (tid < 16) {
-    float M = kNegBig;
-    for (int s = 0; s < ncs; ++s) M = fmaxf(M, P[s * SF + tid]);
-    float L = 0.f;
-    for (int s = 0; s < ncs; ++s) L += P[s * SF + 16 + tid] * fast_exp2(P[s * SF + tid] - M);
-    Ms[tid] = M;
-    Ls[tid] = L;
-    L2[tid] = (nvis > 0 && tid < a.Hg) ? M + fast_log2(L) : INFINITY;
-  }
-  __syncthreads();
-  const S* GT = static_cast<const S*>(a.gates) + b * a.gs[0];
-  for (int e = tid; e < 16 * D; e += 256) {
-    const int hh = e / D, d = e % D;
-    float acc = 0.f;
-    for (int s = 0; s < ncs; ++s) acc += P[s * SF + 32 + e] * fast_exp2(P[s * SF + hh] - Ms[hh]);
-    const float gc = hh < a.Hg ? to_f32<T>(GT[(g * a.Hg + hh) * a.gs[1]]) : 0.f;
-    cmp[hh * D + d] = nvis > 0 ? acc / Ls[hh] * gc : 0.f;
-  }
-  if (a.inject) return;
-  for (int j = tid; j < own; j += 256) {
-    float s = 0.f;
-    for (int hh = 0; hh < a.Hg; ++hh)
-      s += fast_exp2(a.logits[(static_cast<int64_t>(bg) * 16 + hh) * a.NmaxPad + j] - L2[hh]);
-    sc[j] = s;
-  }
-  __syncthreads();
-  if (wave == 0) topk_wave(sc, own, a.n, idxo, surv, selb, lane);
-}
 
-template <class T, int D>
-__global__ __launch_bounds__(256) void k_dec_sel(DecodeArgs a) {
-  using S = typename T::storage;
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int bg = blockIdx.x, b = bg / a.G, g = bg % a.G;
-  const int e = 4 * blockIdx.y + wave;
-  const int seqlen = dec_seqlen(a, b);
-  const int t = seqlen - 1, own = t >> 6;
-  S* lv = reinterpret_cast<S*>(smem) + wave * 64 * D;
-  float* slot = a.part + (static_cast<int64_t>(bg) * dec_nslots(a) + 4 * (a.SC + a.SW) + e) *
-                             dec_slot_floats(D);
-  int j = -1;
-  if (seqlen > 0 && e < a.n) j = a.idx[static_cast<int64_t>(bg) * a.n + e];
-  const bool ok = j >= 0 && j <= own;
+  // ---- compressed branch: merge the partials, log-sum-exp, gated output
+  if (tid < 16) {
+    float M, L;
+    merge_stats(P, a.SC, SF, tid, M, L);
+    hs[4 * tid] = M;
+    hs[4 * tid + 1] = L;
+    hs[4 * tid + 2] = (nvis > 0 && tid < a.Hg) ? M + fast_log2(L) : INFINITY;
+    hs[4 * tid + 3] = tid < a.Hg ? to_f32<T>(GT[(g * a.Hg + tid) * a.gs[1]]) : 0.f;
+  }
+  __syncthreads();
+  for (int e = tid; e < 16 * D; e += NT) {
+    const int h = e / D;
+    float o = 0.f;
+    for (int s = 0; s < a.SC; ++s) o += P[s * SF + 32 + e] * fast_exp2(P[s * SF + h] - hs[4 * h]);
+    ocmp[e] = nvis > 0 ? o / hs[4 * h + 1] * hs[4 * h + 3] : 0.f;
+  }
+
+  // ---- block scores and selection
+  if (!a.inject) {
+    for (int j = tid; j < own; j += NT) {
+      float s = 0.f;
+      for (int h = 0; h < a.Hg; ++h)
+        s += fast_exp2(a.logits[(static_cast<int64_t>(bg) * 16 + h) * a.NmaxPad + j] - hs[4 * h + 2]);
+      sc[j] = s;
+    }
+    __syncthreads();
+    if (wave == 0) topk_wave(sc, own, a.n, selo, surv, selb, lane);
+    __syncthreads();
+    if (tid < a.n) idxo[tid] = selo[tid];
+  } else {
+    if (tid < a.n) selo[tid] = idxo[tid];
+    __syncthreads();
+  }
+
+  // ---- selected blocks, spread over the waves
   Frag<T> qf[D / 32];
   dec_load_q<T, D>(a, b, g, lane, qf);
   const S* kr = static_cast<const S*>(a.kcache) + b * a.ks[0] + g * a.ks[1];
   const S* vr = static_cast<const S*>(a.vcache) + b * a.vs[0] + g * a.vs[1];
-  // an unusable entry becomes an empty range (neutral partial)
-  dec_chunk<T, D>(kr, a.ks[2], vr, a.vs[2], ok ? 64 * j : 0, 0, ok ? t : -1, qf, a.scale_log2, lv,
-                  slot, nullptr, lane);
-}
-
-template <class T, class O, int D>
-__global__ __launch_bounds__(256) void k_dec_combine(DecodeArgs a) {
-  using S = typename T::storage;
-  using SO = typename O::storage;
-  __shared__ float Mw[16], Lw[16], Msl[16], Lsl[16];
-  const int tid = threadIdx.x;
-  const int bg = blockIdx.x, b = bg / a.G, g = bg % a.G;
-  const int seqlen = dec_seqlen(a, b);
-  constexpr int SF = dec_slot_floats(D);
-  SO* OUT = static_cast<SO*>(a.out) + b * a.os[0];
-  if (seqlen == 0) {
-    for (int e = tid; e < a.Hg * D; e += 256)
-      OUT[(g * a.Hg + e / D) * a.os[1] + e % D] = from_f32<O>(0.f);
-    return;
+  S* lv = reinterpret_cast<S*>(big) + wave * 64 * D;
+  float m = kNegBig, l = 0.f;
+  f32x4 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int e = wave; e < a.n; e += FW) {
+    const int j = selo[e];
+    if (j < 0 || j > own) continue;  // unusable injected entry
+    Chunk<T, D> c;
+    chunk_load<T, D>(c, kr, a.ks[2], vr, a.vs[2], 64 * j, 64 * j, t, lane);
+    chunk_attend<T, D>(c, 64 * j, 64 * j, t, qf, a.scale_log2, lv, m, l, acc, nullptr, lane);
   }
-  const float* P = a.part + static_cast<int64_t>(bg) * dec_nslots(a) * SF;
-  const float* W = P + 4 * a.SC * SF;
-  const float* SL = P + 4 * (a.SC + a.SW) * SF;
-  const float* cmp = P + (dec_nslots(a) - 1) * SF + 32;
-  const int nw = 4 * a.SW, ns = 4 * a.SS;
-  if (tid < 16) {
-    float M = kNegBig, L = 0.f;
-    for (int s = 0; s < nw; ++s) M = fmaxf(M, W[s * SF + tid]);
-    for (int s = 0; s < nw; ++s) L += W[s * SF + 16 + tid] * fast_exp2(W[s * SF + tid] - M);
-    Mw[tid] = M;
-    Lw[tid] = L;
-    M = kNegBig;
-    L = 0.f;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, SL[s * SF + tid]);
-    for (int s = 0; s < ns; ++s) L += SL[s * SF + 16 + tid] * fast_exp2(SL[s * SF + tid] - M);
-    Msl[tid] = M;
-    Lsl[tid] = L;
+  l = col_sum4(l);
+  __syncthreads();
+  float* wp = reinterpret_cast<float*>(big);  // per-wave partials, reusing the V staging
+  store_partial<D>(wp + wave * SF, m, l, acc, lane);
+  __syncthreads();
+
+  // ---- merge selected (in LDS) and window (from k_dec_scan) partials, combine
+  const float* W = P + a.SC * SF;
+  if (tid < 16) {  // per head: max and gate-scaled reciprocal sum of each branch
+    float Ms, Ls, Mw, Lw;
+    merge_stats(wp, FW, SF, tid, Ms, Ls);
+    merge_stats(W, a.SW, SF, tid, Mw, Lw);
+    const int hq = g * a.Hg + tid;
+    const float gsl = tid < a.Hg ? to_f32<T>(GT[hq * a.gs[1] + 1]) : 0.f;
+    const float gwn = tid < a.Hg ? to_f32<T>(GT[hq * a.gs[1] + 2]) : 0.f;
+    hs[4 * tid] = Ms;
+    hs[4 * tid + 1] = Ls > 0.f ? gsl / Ls : 0.f;
+    hs[4 * tid + 2] = Mw;
+    hs[4 * tid + 3] = Lw > 0.f ? gwn / Lw : 0.f;
   }
   __syncthreads();
-  const S* GT = static_cast<const S*>(a.gates) + b * a.gs[0];
-  for (int e = tid; e < a.Hg * D; e += 256) {
-    const int hh = e / D, d = e % D;
-    float ow = 0.f, osl = 0.f;
-    for (int s = 0; s < nw; ++s) ow += W[s * SF + 32 + hh * D + d] * fast_exp2(W[s * SF + hh] - Mw[hh]);
-    for (int s = 0; s < ns; ++s) osl += SL[s * SF + 32 + hh * D + d] * fast_exp2(SL[s * SF + hh] - Msl[hh]);
-    const int h = g * a.Hg + hh;
-    const float gsl = to_f32<T>(GT[h * a.gs[1] + 1]);
-    const float gwn = to_f32<T>(GT[h * a.gs[1] + 2]);
-    const float fs = Lsl[hh] > 0.f ? gsl / Lsl[hh] : 0.f;
-    const float v = cmp[hh * D + d] + osl * fs + ow * (gwn / Lw[hh]);
-    OUT[h * a.os[1] + d] = from_f32<O>(v);
+  for (int e = tid; e < a.Hg * D; e += NT) {
+    const int h = e / D;
+    float os = 0.f, ow = 0.f;
+#pragma unroll
+    for (int w = 0; w < FW; ++w) os += wp[w * SF + 32 + e] * fast_exp2(wp[w * SF + h] - hs[4 * h]);
+    for (int s = 0; s < a.SW; ++s) ow += W[s * SF + 32 + e] * fast_exp2(W[s * SF + h] - hs[4 * h + 2]);
+    const float v = ocmp[e] + os * hs[4 * h + 1] + ow * hs[4 * h + 3];
+    OUT[(g * a.Hg + h) * a.os[1] + e % D] = from_f32<O>(v);
   }
+}
+
+size_t dec_finish_lds_bytes(int NmaxPad, int D, bool bf16) {
+  const int FW = bf16 ? 8 : 4;
+  const size_t el = bf16 ? 2 : 4;
+  const size_t stage = static_cast<size_t>(FW) * 64 * D * el;
+  const size_t parts = static_cast<size_t>(FW) * dec_slot_floats(D) * sizeof(float);
+  return NmaxPad * sizeof(float) + kSurvCap * sizeof(uint64_t) + 128 * sizeof(int) +
+         64 * sizeof(float) + 16 * D * sizeof(float) + (stage > parts ? stage : parts);
+}
+
+size_t dec_scan_lds_bytes(int D, bool bf16) {
+  const size_t stage = 4 * 64 * static_cast<size_t>(D) * (bf16 ? 2 : 4);
+  const size_t parts = 4 * static_cast<size_t>(dec_slot_floats(D)) * sizeof(float);
+  return stage > parts ? stage : parts;
 }
 
 static hipError_t record(hipEvent_t* ev, int i, hipStream_t st) {
@@ -300,30 +373,23 @@ static hipError_t record(hipEvent_t* ev, int i, hipStream_t st) {
 
 template <class T, class O, int D>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st, hipEvent_t* ev) {
-  using S = typename T::storage;
-  const size_t lds_chunk = 4 * 64 * D * sizeof(S);
-  const size_t lds_sel = a.NmaxPad * sizeof(float) + kSurvCap * sizeof(uint64_t) + 64 * sizeof(int) +
-                         48 * sizeof(float);
+  constexpr bool kBf16 = sizeof(typename T::storage) == 2;
+  constexpr int FW = kBf16 ? 8 : 4;
+  const size_t lds_scan = dec_scan_lds_bytes(D, kBf16);
+  const size_t lds_fin = dec_finish_lds_bytes(a.NmaxPad, D, kBf16);
   hipError_t e;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec_scan<T, D>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_chunk));
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_scan));
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec_sel<T, D>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_chunk));
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec_select<T, D>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_sel));
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec_finish<T, O, D, FW>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_fin));
   if (e != hipSuccess) return e;
   const int BG = a.B * a.G;
   if ((e = record(ev, 0, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_dec_scan<T, D>), dim3(BG, a.SC + a.SW), dim3(256), lds_chunk, st, a);
+  hipLaunchKernelGGL((k_dec_scan<T, D>), dim3(BG, a.SC + a.SW), dim3(256), lds_scan, st, a);
   if ((e = record(ev, 1, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_dec_select<T, D>), dim3(BG), dim3(256), lds_sel, st, a);
+  hipLaunchKernelGGL((k_dec_finish<T, O, D, FW>), dim3(BG), dim3(64 * FW), lds_fin, st, a);
   if ((e = record(ev, 2, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_dec_sel<T, D>), dim3(BG, a.SS), dim3(256), lds_chunk, st, a);
-  if ((e = record(ev, 3, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_dec_combine<T, O, D>), dim3(BG), dim3(256), 0, st, a);
-  if ((e = record(ev, 4, st)) != hipSuccess) return e;
   return hipGetLastError();
 }
 

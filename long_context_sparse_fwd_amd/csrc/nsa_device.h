@@ -23,8 +23,10 @@
 namespace nsa {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
 constexpr float kLog2e = 1.4426950408889634f;
@@ -52,12 +54,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round-to-nearest-even float -> bf16 bits (inputs are finite).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two floats -> two bf16 (round to nearest even) packed low/high in 32 bits:
+// one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
+
+// Round-to-nearest-even float -> bf16 bits.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.f) & 0xFFFFu; }
 
 template <class T>
 __device__ __forceinline__ float to_f32(typename T::storage x);
@@ -149,10 +153,10 @@ __device__ __forceinline__ Frag<T> pack_p(const f32x4& a, const f32x4& b);
 template <>
 __device__ __forceinline__ Frag<BF16> pack_p<BF16>(const f32x4& a, const f32x4& b) {
   Frag<BF16> f;
-  f.v.x = f32_to_bf16_bits(a.x) | (f32_to_bf16_bits(a.y) << 16);
-  f.v.y = f32_to_bf16_bits(a.z) | (f32_to_bf16_bits(a.w) << 16);
-  f.v.z = f32_to_bf16_bits(b.x) | (f32_to_bf16_bits(b.y) << 16);
-  f.v.w = f32_to_bf16_bits(b.z) | (f32_to_bf16_bits(b.w) << 16);
+  f.v.x = pack_bf16x2(a.x, a.y);
+  f.v.y = pack_bf16x2(a.z, a.w);
+  f.v.z = pack_bf16x2(b.x, b.y);
+  f.v.w = pack_bf16x2(b.z, b.w);
   return f;
 }
 template <>
@@ -230,6 +234,14 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Lazy softmax rescaling: the running maximum (log2 units) is only raised
+// when a new logit exceeds it by more than this, so probabilities stay below
+// 2^kLazyMax and most steps need neither a cross-lane max nor a rescale.
+constexpr float kLazyMax = 8.0f;
+
+// True when any lane of the wave holds v != 0 (wave-uniform).
+__device__ __forceinline__ bool wave_any(bool v) { return __ballot(v) != 0; }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 }  // namespace nsa

@@ -10,9 +10,9 @@ namespace nsa {
 
 constexpr int kBlock = 64;         // compress / select block size supported
 constexpr int kSurvCap = 256;      // top-k survivor buffer per wave (entries)
-constexpr int kCmpTPW = 4;         // tokens per wave, compressed+selection kernel
-constexpr int kSwTPW = 2;          // tokens per wave, selected+window kernel
-constexpr int kSwWaves = 4;        // waves per workgroup, selected+window kernel
+constexpr int kCmpTPW = 2;         // tokens per wave, window+compressed+selection kernel
+constexpr int kSelTPW = 2;         // tokens per wave, selected-branch kernel (4 waves)
+constexpr int kSelRing = 2;        // half-block register buffers per wave in that kernel
 constexpr int kMaxLds = 160 * 1024;
 constexpr float kLog2eHost = 1.4426950408889634f;
 
@@ -22,7 +22,7 @@ struct PrefillArgs {
   int Nb;   // selectable blocks = ceil(L / 64)
   int Nc;   // complete (compressed) blocks = L / 64
   int NcT;  // 64-row chunks of the compressed tiles = ceil(Nc / 64)
-  int cmp_waves, cmp_tiles, sw_tiles;
+  int cmp_waves, cmp_tiles, sel_tiles;
   float scale_log2;  // softmax scale * log2(e)
   int inject;        // 1: idx holds the selection; 0: compute it into idx
   const void* q;
@@ -43,7 +43,6 @@ struct DecodeArgs {
   int B, Lmax, Nmax, Hq, G, Hg, D, n, w;
   int SC;  // compressed splits per (b, g), each kDecSplitKeys blocks
   int SW;  // window splits per (b, g), each kDecSplitKeys tokens
-  int SS;  // selected splits per (b, g), each 4 blocks
   int NmaxPad;
   float scale_log2;
   int inject;
@@ -56,7 +55,7 @@ struct DecodeArgs {
   const void* gates;
   void* out;
   int32_t* idx;
-  float* part;    // partial softmax states, [B*G][SC+SW+SS+1][Hg=16][2 + D]
+  float* part;    // partial softmax states, [B*G][SC+SW] x (m[16], l[16], O[16][D])
   float* logits;  // compressed logits (log2 domain), [B*G][16][NmaxPad]
   int64_t qs[2], ks[3], vs[3], kcs[3], vcs[3], gs[2], os[2];
 };
@@ -66,7 +65,7 @@ constexpr int kDecSplitKeys = 256;  // keys (or blocks) per decode workgroup: 4 
 // ev (nullable): kPrefillStages+1 / kDecodeStages+1 events recorded on st
 // before each kernel and after the last one.
 constexpr int kPrefillStages = 3;
-constexpr int kDecodeStages = 4;
+constexpr int kDecodeStages = 2;
 hipError_t launch_prefill(const PrefillArgs& a, bool in_bf16, bool out_bf16, hipStream_t st,
                           hipEvent_t* ev);
 hipError_t launch_decode(const DecodeArgs& a, bool in_bf16, bool out_bf16, hipStream_t st,
@@ -75,7 +74,12 @@ hipError_t launch_compress(int B, int G, int Nc, int D, bool bf16, const void* k
                            const void* v, const int64_t* vs, void* kc, const int64_t* kcs,
                            void* vc, const int64_t* vcs, hipStream_t st);
 
-// LDS bytes of the compressed+selection kernel for a given number of waves.
+size_t dec_finish_lds_bytes(int NmaxPad, int D, bool bf16);
+size_t dec_scan_lds_bytes(int D, bool bf16);
+
+size_t cmpwin_lds_bytes(int waves, int NcT, int D, bool bf16);
+
+// LDS bytes of the block scores and top-k scratch of the compressed kernel.
 inline size_t cmp_lds_bytes(int waves, int NcT) {
   return static_cast<size_t>(waves) *
          (static_cast<size_t>(kCmpTPW) * NcT * 64 * sizeof(float) + kSurvCap * sizeof(uint64_t) +

@@ -1,34 +1,38 @@
 // NSA prefill on gfx950: three kernels per call.
 //
-//  k_prep  block compression + re-layout. One workgroup per 64-token block
-//          (b, g, j): the block's K and V are staged in LDS, written back as a
-//          fragment-major K tile and a permuted V^T tile, and, for complete
-//          blocks, their fp32 means (the compressed keys/values) are written
-//          into the compressed tiles. Compression by block means, stride 64:
-//          compressed block representations, NSA factory write-up
-//          (chencunli.com), section "What dynamic sparsity actually
-//          sparsifies"; block size from the NSA how-to (qwbw.cn/news/106443),
-//          section 3.
-//  k_cmp   compressed branch + block scores + top-k selection. A wave owns 4
-//          query tokens of one KV group (16 query heads each). Pass 1 finds the
-//          log-sum-exp of the compressed logits; pass 2 recomputes them, forms
-//          normalised probabilities, accumulates the compressed output with
-//          MFMA and the per-block scores (probabilities summed over the
-//          group's heads, a DPP row reduction) into LDS; then the wave selects
-//          the blocks. Writes gate_cmp * O_cmp into out and the selection into
-//          idx. Workgroups run heaviest (latest tokens) first.
-//  k_sw    selected-block branch + sliding-window branch + gate combination.
-//          A wave owns 2 tokens: the window band is shared by both, the
-//          selected blocks are gathered per token straight from the K/V tiles
-//          in MFMA-fragment order. out += gate_slc * O_slc + gate_win * O_win.
-//          Work items are grouped by KV group per XCD so each XCD's L2 serves
-//          one group's K/V.
+//  k_prep     block compression + re-layout. One workgroup per 64-token block
+//             (b, g, j): the block's K and V are staged in LDS, written back as
+//             a fragment-major K tile and a permuted V^T tile, and, for
+//             complete blocks, their fp32 means (the compressed keys/values)
+//             are written into the compressed tiles. Compression by block
+//             means, stride 64: compressed block representations, NSA factory
+//             write-up (chencunli.com), section "What dynamic sparsity
+//             actually sparsifies"; block size from the NSA how-to
+//             (qwbw.cn/news/106443), section 3.
+//  k_cmpwin   sliding-window branch + compressed branch + block scores +
+//             top-k selection for 16 consecutive tokens of one KV group (8
+//             waves, two per SIMD, each owning 2 tokens x 16 query heads). Every 64-key tile the
+//             workgroup needs (window K/V blocks, block-mean tiles) is staged
+//             once in LDS, double-buffered, and shared by the 8 waves. The
+//             window output is normalised and gated first; the compressed
+//             branch then adds gate_cmp * P . Vc into the same accumulators
+//             (pass 1: log-sum-exp; pass 2: probabilities, output, and block
+//             scores = probabilities summed over the group's heads by a DPP
+//             row reduction, kept in LDS). The wave then selects each token's
+//             blocks. Writes gate_win * O_win + gate_cmp * O_cmp into out and
+//             the selection into idx. Workgroups run heaviest first.
+//  k_sel      selected-block branch: a wave walks each of its tokens' chosen
+//             blocks (32-key halves, the next one prefetched into registers
+//             while the current one is computed), straight from the K/V tiles
+//             in MFMA-fragment order; out += gate_slc * O_slc. One workgroup
+//             per CU and work grouped by KV group per XCD: the random block
+//             gathers are bound by L2-miss bandwidth, which fewer concurrent
+//             waves per XCD use better.
 #include "nsa_device.h"
 #include "nsa_internal.h"
 #include "nsa_topk.h"
 
 namespace nsa {
-
 // ------------------------------------------------------------------ stores
 
 template <class O>
@@ -36,8 +40,8 @@ __device__ __forceinline__ void store4(typename O::storage* p, const f32x4& v);
 template <>
 __device__ __forceinline__ void store4<BF16>(uint16_t* p, const f32x4& v) {
   uint2 w;
-  w.x = f32_to_bf16_bits(v.x) | (f32_to_bf16_bits(v.y) << 16);
-  w.y = f32_to_bf16_bits(v.z) | (f32_to_bf16_bits(v.w) << 16);
+  w.x = pack_bf16x2(v.x, v.y);
+  w.y = pack_bf16x2(v.z, v.w);
   *reinterpret_cast<uint2*>(p) = w;
 }
 template <>
@@ -139,99 +143,260 @@ __global__ __launch_bounds__(256) void k_prep(PrefillArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ k_cmp
+// ------------------------------------------------------------------ shared pieces
 
-template <class T, class O, int D, int TPW>
-__global__ __launch_bounds__(256) void k_cmp(PrefillArgs a) {
+// One 32-key step of an online-softmax attention for one 16-column query
+// tile: st holds the raw S^T of keys [kbase, kbase+32) in C layout; with MASK,
+// keys outside [klo, khi] are excluded. Updates (m, l, acc); m is raised
+// lazily (kLazyMax), the final output is acc / l whatever m is.
+template <class T, int DT, bool MASK>
+__device__ __forceinline__ void online_step(f32x4 (&st)[2], int kbase, int klo, int khi, int grp,
+                                            float sl2, float& m, float& l, f32x4 (&acc)[DT],
+                                            const Frag<T> (&vf)[DT]) {
+  float lmx = kNegBig;
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = st[h2][i] * sl2;
+      if (MASK) {
+        const int key = kbase + 16 * h2 + 4 * grp + i;
+        x = (key >= klo && key <= khi) ? x : -INFINITY;
+      }
+      st[h2][i] = x;
+      lmx = fmaxf(lmx, x);
+    }
+  if (wave_any(lmx > m + kLazyMax)) {
+    const float mn = fmaxf(m, col_max4(lmx));
+    const float alpha = fast_exp2(m - mn);
+    l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    m = mn;
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = fast_exp2(st[h2][i] - m);
+      st[h2][i] = p;
+      sum += p;
+    }
+  l += sum;
+  const Frag<T> pf = pack_p<T>(st[0], st[1]);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) mma(acc[dt], vf[dt], pf);
+}
+
+// Cooperative copy of one or two 64 x D tiles (fragment-major, contiguous)
+// from global memory into LDS through registers: issue() starts the loads of
+// the next tiles, commit() stores them once the current tiles are consumed.
+template <class T, int D, int NT>
+struct TileStager {
+  static constexpr int kVec = 64 * D * static_cast<int>(sizeof(typename T::storage)) / 16;
+  static constexpr int kPer = kVec / NT;
+  u32x4 r[2][kPer];
+  __device__ __forceinline__ void issue(const void* a, const void* b, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) r[0][i] = static_cast<const u32x4*>(a)[tid + NT * i];
+    if (b != nullptr) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) r[1][i] = static_cast<const u32x4*>(b)[tid + NT * i];
+    }
+  }
+  __device__ __forceinline__ void commit(void* a, void* b, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) static_cast<u32x4*>(a)[tid + NT * i] = r[0][i];
+    if (b != nullptr) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) static_cast<u32x4*>(b)[tid + NT * i] = r[1][i];
+    }
+  }
+};
+
+// ------------------------------------------------------------------ k_cmpwin
+
+template <class T, class O, int D, int NW>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_cmpwin(PrefillArgs a) {
   using S = typename T::storage;
   using SO = typename O::storage;
-  constexpr int KS = D / 32, DT = D / 16;
+  constexpr int TPW = kCmpTPW, KS = D / 32, DT = D / 16, NT = 64 * NW, TILE = 64 * D;
   extern __shared__ __align__(16) unsigned char smem[];
+  S* stage = reinterpret_cast<S*>(smem);  // [2 buffers][2 tiles][TILE]
+  const int NcPad = a.NcT * 64;
+  float* scb = reinterpret_cast<float*>(smem + 4 * TILE * sizeof(S));
+  uint64_t* survb = reinterpret_cast<uint64_t*>(scb + NW * TPW * NcPad);
+  int* selbb = reinterpret_cast<int*>(survb + NW * kSurvCap);
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int BG = a.B * a.G;
   const int tile = a.cmp_tiles - 1 - static_cast<int>(blockIdx.x) / BG;  // heaviest first
   const int bg = static_cast<int>(blockIdx.x) % BG, b = bg / a.G, g = bg % a.G;
-  const int t0 = (tile * nw + wave) * TPW;
-  if (t0 >= a.L) return;  // no workgroup barriers below
+  const int T0 = tile * TPW * NW;
+  if (T0 >= a.L) return;  // whole workgroup
   const int col = lane & 15, grp = lane >> 4;
   const bool colv = col < a.Hg;
   const int h = g * a.Hg + col;
-  const int NcPad = a.NcT * 64;
+  const int tw = T0 + TPW * wave;                     // this wave's first token
+  const int Tl = min(T0 + TPW * NW - 1, a.L - 1);     // the workgroup's last token
+  const float sl2 = a.scale_log2;
+  const int64_t bgoff = static_cast<int64_t>(b * a.G + g);
 
   const S* Q = static_cast<const S*>(a.q) + b * a.qs[0] + h * a.qs[2] + 8 * grp;
+  const S* GT = static_cast<const S*>(a.gates) + b * a.gs[0] + h * a.gs[2];
   Frag<T> qf[TPW][KS];
+  float gcmp[TPW], gwin[TPW];
   int nvis[TPW];
-  int nvmax = 0;
 #pragma unroll
   for (int qt = 0; qt < TPW; ++qt) {
-    const int t = t0 + qt;
-    const bool valid = t < a.L;
-    nvis[qt] = valid ? (t + 1) >> 6 : 0;
-    nvmax = max(nvmax, nvis[qt]);
+    const int t = tw + qt;
+    const bool valid = t < a.L && colv;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      qf[qt][s] = (valid && colv) ? frag_load<T>(Q + static_cast<int64_t>(t) * a.qs[1] + 32 * s)
-                                  : frag_zero<T>();
+      qf[qt][s] = valid ? frag_load<T>(Q + static_cast<int64_t>(t) * a.qs[1] + 32 * s) : frag_zero<T>();
+    gcmp[qt] = valid ? to_f32<T>(GT[static_cast<int64_t>(t) * a.gs[1]]) : 0.f;
+    gwin[qt] = valid ? to_f32<T>(GT[static_cast<int64_t>(t) * a.gs[1] + 2]) : 0.f;
+    nvis[qt] = t < a.L ? (t + 1) >> 6 : 0;
   }
-  const int nch = (nvmax + 63) >> 6;
-  const int64_t tbase = static_cast<int64_t>(b * a.G + g) * a.NcT * (64 * D);
-  const S* KC = static_cast<const S*>(a.kct) + tbase;
-  const S* KCL = kSplitKc<T> ? static_cast<const S*>(a.kclt) + tbase : nullptr;
-  const S* VC = static_cast<const S*>(a.vct) + tbase;
-  const float sl2 = a.scale_log2;
+  f32x4 oacc[TPW][DT];
+#pragma unroll
+  for (int qt = 0; qt < TPW; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  TileStager<T, D, NT> stg;
 
-  // ---- pass 1: log-sum-exp of the visible compressed logits (log2 domain)
+  // ---- sliding window over the workgroup's band of key blocks
+  {
+    const S* KT = static_cast<const S*>(a.kt) + bgoff * a.Nb * TILE;
+    const S* VT = static_cast<const S*>(a.vt) + bgoff * a.Nb * TILE;
+    const int b0 = max(0, T0 - a.w + 1) >> 6, b1 = Tl >> 6;
+    float mw[TPW], lw[TPW];
+#pragma unroll
+    for (int qt = 0; qt < TPW; ++qt) {
+      mw[qt] = kNegBig;
+      lw[qt] = 0.f;
+    }
+    stg.issue(KT + static_cast<int64_t>(b0) * TILE, VT + static_cast<int64_t>(b0) * TILE, tid);
+    stg.commit(stage, stage + TILE, tid);
+    __syncthreads();
+    for (int blk = b0; blk <= b1; ++blk) {
+      const int buf = (blk - b0) & 1;
+      const bool more = blk < b1;
+      if (more)
+        stg.issue(KT + static_cast<int64_t>(blk + 1) * TILE, VT + static_cast<int64_t>(blk + 1) * TILE, tid);
+      const S* kt = stage + buf * 2 * TILE;
+      const S* vt = kt + TILE;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int kb = 64 * blk + 32 * s2;
+        if (kb > tw + TPW - 1 || kb + 31 < tw - a.w + 1) continue;  // outside this wave's band
+        Frag<T> kf[2][KS];
+        Frag<T> vf[DT];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int s = 0; s < KS; ++s) kf[h2][s] = frag_load<T>(kt + ktile_frag(2 * s2 + h2, s, lane, D));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vf[dt] = frag_load<T>(vt + vtile_frag(dt, s2, lane));
+        // all 32 keys inside every token's window: no masks needed
+        const bool full = kb >= tw + TPW - a.w && kb + 31 <= tw && tw + TPW - 1 < a.L;
+#pragma unroll
+        for (int qt = 0; qt < TPW; ++qt) {
+          const int t = tw + qt;
+          f32x4 st[2];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            st[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) mma(st[h2], kf[h2][s], qf[qt][s]);
+          }
+          if (full)
+            online_step<T, DT, false>(st, kb, 0, 0, grp, sl2, mw[qt], lw[qt], oacc[qt], vf);
+          else
+            online_step<T, DT, true>(st, kb, t - a.w + 1, t < a.L ? t : -1, grp, sl2, mw[qt], lw[qt],
+                                     oacc[qt], vf);
+        }
+      }
+      if (more) stg.commit(stage + (buf ^ 1) * 2 * TILE, stage + (buf ^ 1) * 2 * TILE + TILE, tid);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int qt = 0; qt < TPW; ++qt) {
+      const float lt = col_sum4(lw[qt]);
+      const float f = lt > 0.f ? gwin[qt] / lt : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] *= f;
+    }
+  }
+
+  // ---- compressed branch
+  const int nch = (((Tl + 1) >> 6) + 63) >> 6;
+  const S* KC = static_cast<const S*>(a.kct) + bgoff * a.NcT * TILE;
+  const S* KCL = kSplitKc<T> ? static_cast<const S*>(a.kclt) + bgoff * a.NcT * TILE : nullptr;
+  const S* VC = static_cast<const S*>(a.vct) + bgoff * a.NcT * TILE;
+
+  // pass 1: log-sum-exp (log2 domain) from the high part of the block means.
+  // An error e_h in a head's log-sum-exp scales all of that head's
+  // probabilities by exp(-e_h); the differences between block scores, which
+  // the selection compares, move only in second order. Pass 2 uses the full
+  // precision logits.
   float m[TPW], ls[TPW];
 #pragma unroll
   for (int qt = 0; qt < TPW; ++qt) {
     m[qt] = kNegBig;
     ls[qt] = 0.f;
   }
+  if (nch > 0) {
+    stg.issue(KC, nullptr, tid);
+    stg.commit(stage, nullptr, tid);
+    __syncthreads();
+  }
   for (int c = 0; c < nch; ++c) {
-    const int64_t coff = static_cast<int64_t>(c) * (64 * D);
+    const int buf = c & 1;
+    const bool more = c + 1 < nch;
+    if (more) stg.issue(KC + static_cast<int64_t>(c + 1) * TILE, nullptr, tid);
+    const S* kc = stage + buf * 2 * TILE;
     f32x4 st[TPW][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      Frag<T> kf[KS], kl[KS];
+      Frag<T> kf[KS];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        kf[s] = frag_load<T>(KC + coff + ktile_frag(kt, s, lane, D));
-        if (kSplitKc<T>) kl[s] = frag_load<T>(KCL + coff + ktile_frag(kt, s, lane, D));
-      }
+      for (int s = 0; s < KS; ++s) kf[s] = frag_load<T>(kc + ktile_frag(kt, s, lane, D));
 #pragma unroll
       for (int qt = 0; qt < TPW; ++qt) {
         st[qt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          mma(st[qt][kt], kf[s], qf[qt][s]);
-          if (kSplitKc<T>) mma(st[qt][kt], kl[s], qf[qt][s]);
-        }
+        for (int s = 0; s < KS; ++s) mma(st[qt][kt], kf[s], qf[qt][s]);
       }
     }
+    const bool full = 64 * c + 63 < nvis[0];  // every key of the chunk visible to every token
 #pragma unroll
     for (int qt = 0; qt < TPW; ++qt) {
-      float mx = kNegBig;
+      float lmx = kNegBig;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = 64 * c + 16 * kt + 4 * grp + i;
-          const float x = key < nvis[qt] ? st[qt][kt][i] * sl2 : -INFINITY;
+          float x = st[qt][kt][i] * sl2;
+          if (!full) x = 64 * c + 16 * kt + 4 * grp + i < nvis[qt] ? x : -INFINITY;
           st[qt][kt][i] = x;
-          mx = fmaxf(mx, x);
+          lmx = fmaxf(lmx, x);
         }
-      mx = col_max4(mx);
-      const float mn = fmaxf(m[qt], mx);
+      if (wave_any(lmx > m[qt] + kLazyMax)) {
+        const float mn = fmaxf(m[qt], col_max4(lmx));
+        ls[qt] *= fast_exp2(m[qt] - mn);
+        m[qt] = mn;
+      }
       float sum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sum += fast_exp2(st[qt][kt][i] - mn);
-      ls[qt] = ls[qt] * fast_exp2(m[qt] - mn) + sum;
-      m[qt] = mn;
+        for (int i = 0; i < 4; ++i) sum += fast_exp2(st[qt][kt][i] - m[qt]);
+      ls[qt] += sum;
     }
+    if (more) stg.commit(stage + (buf ^ 1) * 2 * TILE, nullptr, tid);
+    __syncthreads();
   }
   float lse2[TPW];
 #pragma unroll
@@ -240,18 +405,21 @@ __global__ __launch_bounds__(256) void k_cmp(PrefillArgs a) {
     lse2[qt] = (nvis[qt] > 0 && colv) ? m[qt] + fast_log2(tot) : INFINITY;
   }
 
-  // ---- pass 2: probabilities, compressed output, block scores
+  // pass 2: probabilities, gate_cmp * P . Vc into the accumulators, block scores
   const bool select = !a.inject;
-  float* sc = reinterpret_cast<float*>(smem) + static_cast<size_t>(wave) * TPW * NcPad;
-  f32x4 oacc[TPW][DT];
-#pragma unroll
-  for (int qt = 0; qt < TPW; ++qt)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  float* sc = scb + static_cast<size_t>(wave) * TPW * NcPad;
+  if (nch > 0) {
+    stg.issue(KC, VC, tid);
+    stg.commit(stage, stage + TILE, tid);
+    __syncthreads();
+  }
   for (int c = 0; c < nch; ++c) {
-    const int64_t coff = static_cast<int64_t>(c) * (64 * D);
-    const S* vc = VC + coff;
+    const int buf = c & 1;
+    const bool more = c + 1 < nch;
+    if (more) stg.issue(KC + static_cast<int64_t>(c + 1) * TILE, VC + static_cast<int64_t>(c + 1) * TILE, tid);
+    const S* kc = stage + buf * 2 * TILE;
+    const S* vc = kc + TILE;
+    const S* kcl = kSplitKc<T> ? KCL + static_cast<int64_t>(c) * TILE : nullptr;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       f32x4 st[TPW][2];
@@ -260,8 +428,8 @@ __global__ __launch_bounds__(256) void k_cmp(PrefillArgs a) {
         Frag<T> kf[KS], kl[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          kf[s] = frag_load<T>(KC + coff + ktile_frag(2 * s2 + h2, s, lane, D));
-          if (kSplitKc<T>) kl[s] = frag_load<T>(KCL + coff + ktile_frag(2 * s2 + h2, s, lane, D));
+          kf[s] = frag_load<T>(kc + ktile_frag(2 * s2 + h2, s, lane, D));
+          if (kSplitKc<T>) kl[s] = frag_load<T>(kcl + ktile_frag(2 * s2 + h2, s, lane, D));
         }
 #pragma unroll
         for (int qt = 0; qt < TPW; ++qt) {
@@ -276,14 +444,15 @@ __global__ __launch_bounds__(256) void k_cmp(PrefillArgs a) {
       Frag<T> vf[DT];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) vf[dt] = frag_load<T>(vc + vtile_frag(dt, s2, lane));
+      const bool full = 64 * c + 32 * s2 + 31 < nvis[0];
 #pragma unroll
       for (int qt = 0; qt < TPW; ++qt) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = 64 * c + 32 * s2 + 16 * h2 + 4 * grp + i;
-            st[qt][h2][i] = key < nvis[qt] ? fast_exp2(st[qt][h2][i] * sl2 - lse2[qt]) : 0.f;
+            const float p = fast_exp2(st[qt][h2][i] * sl2 - lse2[qt]);
+            st[qt][h2][i] = (full || 64 * c + 32 * s2 + 16 * h2 + 4 * grp + i < nvis[qt]) ? p : 0.f;
           }
         if (select) {
 #pragma unroll
@@ -297,25 +466,25 @@ __global__ __launch_bounds__(256) void k_cmp(PrefillArgs a) {
               *reinterpret_cast<f32x4*>(sc + qt * NcPad + 64 * c + 32 * s2 + 16 * h2 + 4 * grp) = r;
           }
         }
-        const Frag<T> pf = pack_p<T>(st[qt][0], st[qt][1]);
+        const Frag<T> pf = pack_p<T>(st[qt][0] * gcmp[qt], st[qt][1] * gcmp[qt]);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) mma(oacc[qt][dt], vf[dt], pf);
       }
     }
+    if (more) stg.commit(stage + (buf ^ 1) * 2 * TILE, stage + (buf ^ 1) * 2 * TILE + TILE, tid);
+    __syncthreads();
   }
 
-  // ---- gate_cmp * O_cmp -> out (the other branches are added by k_sw)
+  // ---- gate_win * O_win + gate_cmp * O_cmp -> out (k_sel adds the selected branch)
   {
-    const S* GT = static_cast<const S*>(a.gates) + b * a.gs[0] + h * a.gs[2];
     SO* OUT = static_cast<SO*>(a.out) + b * a.os[0] + h * a.os[2] + 4 * grp;
 #pragma unroll
     for (int qt = 0; qt < TPW; ++qt) {
-      const int t = t0 + qt;
+      const int t = tw + qt;
       if (t < a.L && colv) {
-        const float gc = to_f32<T>(GT[static_cast<int64_t>(t) * a.gs[1]]);
         SO* o = OUT + static_cast<int64_t>(t) * a.os[1];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) store4<O>(o + 16 * dt, oacc[qt][dt] * gc);
+        for (int dt = 0; dt < DT; ++dt) store4<O>(o + 16 * dt, oacc[qt][dt]);
       }
     }
   }
@@ -323,13 +492,11 @@ __global__ __launch_bounds__(256) void k_cmp(PrefillArgs a) {
   // ---- selection
   if (select) {
     wave_lds_sync();
-    unsigned char* base = smem + static_cast<size_t>(nw) * TPW * NcPad * sizeof(float);
-    uint64_t* surv = reinterpret_cast<uint64_t*>(base) + static_cast<size_t>(wave) * kSurvCap;
-    int* selb = reinterpret_cast<int*>(base + static_cast<size_t>(nw) * kSurvCap * sizeof(uint64_t)) +
-                wave * 64;
+    uint64_t* surv = survb + static_cast<size_t>(wave) * kSurvCap;
+    int* selb = selbb + wave * 64;
 #pragma unroll 1
     for (int qt = 0; qt < TPW; ++qt) {
-      const int t = t0 + qt;
+      const int t = tw + qt;
       if (t >= a.L) break;
       int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.L + t) * a.G + g) * a.n;
       topk_wave(sc + qt * NcPad, t >> 6, a.n, row, surv, selb, lane);
@@ -337,177 +504,169 @@ __global__ __launch_bounds__(256) void k_cmp(PrefillArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ k_sw
+// ------------------------------------------------------------------ k_sel
 
-// One 32-key step of an online-softmax attention for one 16-column query
-// tile: st holds the raw S^T of keys [kbase, kbase+32) in C layout; keys
-// outside [klo, khi] are masked. Updates (m, l, acc) and returns nothing.
-template <class T, int DT>
-__device__ __forceinline__ void online_step(f32x4 (&st)[2], int kbase, int klo, int khi, int grp,
-                                            float sl2, float& m, float& l, f32x4 (&acc)[DT],
-                                            const Frag<T> (&vf)[DT]) {
-  float mx = kNegBig;
+// Registers of one 32-key half block: K fragments of its two key tiles and
+// the V^T fragments of its k-step.
+template <class T, int D>
+struct HalfBlock {
+  Frag<T> k[2][D / 32];
+  Frag<T> v[D / 16];
+};
+
+template <class T, int D>
+__device__ __forceinline__ void half_load(HalfBlock<T, D>& hb, const typename T::storage* KT,
+                                          const typename T::storage* VT, int j, int hh, int lane) {
+  const typename T::storage* kt = KT + static_cast<int64_t>(j) * (64 * D);
+  const typename T::storage* vt = VT + static_cast<int64_t>(j) * (64 * D);
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kbase + 16 * h2 + 4 * grp + i;
-      const float x = (key >= klo && key <= khi) ? st[h2][i] * sl2 : -INFINITY;
-      st[h2][i] = x;
-      mx = fmaxf(mx, x);
-    }
-  mx = col_max4(mx);
-  const float mn = fmaxf(m, mx);
-  const float alpha = fast_exp2(m - mn);
-  float sum = 0.f;
+    for (int s = 0; s < D / 32; ++s) hb.k[h2][s] = frag_load<T>(kt + ktile_frag(2 * hh + h2, s, lane, D));
 #pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = fast_exp2(st[h2][i] - mn);
-      st[h2][i] = p;
-      sum += p;
-    }
-  l = l * alpha + sum;
-  m = mn;
-  const Frag<T> pf = pack_p<T>(st[0], st[1]);
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    acc[dt] *= alpha;
-    mma(acc[dt], vf[dt], pf);
-  }
+  for (int dt = 0; dt < D / 16; ++dt) hb.v[dt] = frag_load<T>(vt + vtile_frag(dt, hh, lane));
 }
 
-template <class T, class O, int D, int TPW>
-__global__ __launch_bounds__(256) void k_sw(PrefillArgs a) {
+template <class T, int D, bool MASK>
+__device__ __forceinline__ void half_attend(const HalfBlock<T, D>& hb, const Frag<T> (&qf)[D / 32],
+                                            int kb, int t, int grp, float sl2, float& m, float& l,
+                                            f32x4 (&acc)[D / 16]) {
+  f32x4 st[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    st[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) mma(st[h2], hb.k[h2][s], qf[s]);
+  }
+  online_step<T, D / 16, MASK>(st, kb, 0, t, grp, sl2, m, l, acc, hb.v);
+}
+
+// A wave owns kSelTPW tokens. Their usable half blocks are flattened into one
+// step list (token, block, half) in LDS, and the tokens' query fragments are
+// kept in LDS too; a ring of kSelRing half-block register buffers keeps
+// kSelRing - 1 loads in flight while one is computed, across token
+// boundaries, with two waves per SIMD.
+template <class T, class O, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_sel(PrefillArgs a) {
   using S = typename T::storage;
   using SO = typename O::storage;
-  constexpr int KS = D / 32, DT = D / 16;
-
+  constexpr int TPW = kSelTPW, NB = kSelRing, KS = D / 32, DT = D / 16;
+  constexpr int FE = sizeof(Frag<T>) / 16;  // 16-byte words per fragment lane
+  __shared__ int steps_lds[4][TPW * 128];
+  __shared__ u32x4 q_lds[4][TPW][KS][FE][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nw = blockDim.x >> 6;
-  const int N = a.B * a.G * a.sw_tiles;
+  const int N = a.B * a.G * a.sel_tiles;
   const int per = (N + 7) >> 3;
   const int item = static_cast<int>(blockIdx.x & 7) * per + static_cast<int>(blockIdx.x >> 3);
-  if (item >= N) return;
-  const int g = item / (a.B * a.sw_tiles);
-  const int rem = item % (a.B * a.sw_tiles);
-  const int b = rem / a.sw_tiles, tile = rem % a.sw_tiles;
-  const int t0 = (tile * nw + wave) * TPW;
+  if (item >= N) return;  // no workgroup barriers in this kernel
+  const int g = item / (a.B * a.sel_tiles);
+  const int rem = item % (a.B * a.sel_tiles);
+  const int b = rem / a.sel_tiles, tile = rem % a.sel_tiles;
+  const int t0 = (tile * 4 + wave) * TPW;
   if (t0 >= a.L) return;
   const int col = lane & 15, grp = lane >> 4;
   const bool colv = col < a.Hg;
   const int h = g * a.Hg + col;
   const float sl2 = a.scale_log2;
-
-  const S* Q = static_cast<const S*>(a.q) + b * a.qs[0] + h * a.qs[2] + 8 * grp;
-  Frag<T> qf[TPW][KS];
-#pragma unroll
-  for (int qt = 0; qt < TPW; ++qt) {
-    const int t = t0 + qt;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qf[qt][s] = (t < a.L && colv) ? frag_load<T>(Q + static_cast<int64_t>(t) * a.qs[1] + 32 * s)
-                                    : frag_zero<T>();
-  }
   const int64_t tb = static_cast<int64_t>(b * a.G + g) * a.Nb * (64 * D);
   const S* KT = static_cast<const S*>(a.kt) + tb;
   const S* VT = static_cast<const S*>(a.vt) + tb;
+  const S* Q = static_cast<const S*>(a.q) + b * a.qs[0] + h * a.qs[2] + 8 * grp;
+  const int n = a.n;
 
-  // ---- sliding window, shared by the wave's tokens
-  const int tl = min(t0 + TPW - 1, a.L - 1);
-  const int lo = max(0, t0 - a.w + 1);
-  float mw[TPW], lw[TPW];
-  f32x4 ow[TPW][DT];
+  // ---- query fragments -> LDS; the step list: code = qt << 24 | half << 23 | block
+  int* steps = steps_lds[wave];
+  int nsteps = 0;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int qt = 0; qt < TPW; ++qt) {
-    mw[qt] = kNegBig;
-    lw[qt] = 0.f;
+    const int t = t0 + qt;
+    const bool tv = t < a.L;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) ow[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < KS; ++s) {
+      const Frag<T> f =
+          (tv && colv) ? frag_load<T>(Q + static_cast<int64_t>(t) * a.qs[1] + 32 * s) : frag_zero<T>();
+      const u32x4* w = reinterpret_cast<const u32x4*>(&f);
+#pragma unroll
+      for (int e = 0; e < FE; ++e) q_lds[wave][qt][s][e][lane] = w[e];
+    }
+    if (!tv) continue;
+    const int own = t >> 6;
+    const int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.L + t) * a.G + g) * n;
+    const int j = lane < n ? row[lane] : -1;
+    const bool v0 = j >= 0 && j <= own;            // padding / unusable injected entries drop out
+    const bool v1 = v0 && 64 * j + 32 <= t;
+    const uint64_t b0 = __ballot(v0), b1 = __ballot(v1);
+    const int pos = nsteps + __popcll(b0 & below) + __popcll(b1 & below);
+    if (v0) steps[pos] = (qt << 24) | j;
+    if (v1) steps[pos + 1] = (qt << 24) | (1 << 23) | j;
+    nsteps += __popcll(b0) + __popcll(b1);
   }
-  for (int kb = lo & ~31; kb <= tl; kb += 32) {
-    const int blk = kb >> 6, s2 = (kb >> 5) & 1;
-    const S* kt = KT + static_cast<int64_t>(blk) * (64 * D);
-    const S* vt = VT + static_cast<int64_t>(blk) * (64 * D);
-    Frag<T> kf[2][KS];
-    Frag<T> vf[DT];
+  wave_lds_sync();
+
+  float m[TPW], l[TPW];
+  f32x4 acc[TPW][DT];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+  for (int qt = 0; qt < TPW; ++qt) {
+    m[qt] = kNegBig;
+    l[qt] = 0.f;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kf[h2][s] = frag_load<T>(kt + ktile_frag(2 * s2 + h2, s, lane, D));
+    for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  HalfBlock<T, D> ring[NB];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vf[dt] = frag_load<T>(vt + vtile_frag(dt, s2, lane));
+  for (int k = 0; k < NB; ++k)
+    if (k < nsteps) {
+      const int code = steps[k];
+      half_load<T, D>(ring[k], KT, VT, code & 0x7FFFFF, (code >> 23) & 1, lane);
+    }
+#pragma unroll 1
+  for (int base = 0; base < nsteps; base += NB) {
 #pragma unroll
-    for (int qt = 0; qt < TPW; ++qt) {
+    for (int k = 0; k < NB; ++k) {
+      const int s = base + k;
+      if (s >= nsteps) break;
+      const int code = steps[s];
+      const int qt = code >> 24, j = code & 0x7FFFFF, hh = (code >> 23) & 1;
       const int t = t0 + qt;
-      f32x4 st[2];
+      const int kb = 64 * j + 32 * hh;
+      const bool full = kb + 31 <= t;
+      Frag<T> qf[KS];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        st[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ss = 0; ss < KS; ++ss) {
+        u32x4* w = reinterpret_cast<u32x4*>(&qf[ss]);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) mma(st[h2], kf[h2][s], qf[qt][s]);
+        for (int e = 0; e < FE; ++e) w[e] = q_lds[wave][qt][ss][e][lane];
       }
-      // tokens past the end of the sequence see an empty range
-      const int khi = t < a.L ? t : -1;
-      online_step<T, DT>(st, kb, t - a.w + 1, khi, grp, sl2, mw[qt], lw[qt], ow[qt], vf);
+#pragma unroll
+      for (int q = 0; q < TPW; ++q)
+        if (q == qt) {
+          if (full)
+            half_attend<T, D, false>(ring[k], qf, kb, t, grp, sl2, m[q], l[q], acc[q]);
+          else
+            half_attend<T, D, true>(ring[k], qf, kb, t, grp, sl2, m[q], l[q], acc[q]);
+        }
+      if (s + NB < nsteps) {
+        const int nc = steps[s + NB];
+        half_load<T, D>(ring[k], KT, VT, nc & 0x7FFFFF, (nc >> 23) & 1, lane);
+      }
     }
   }
 
-  // ---- selected blocks, one token at a time, then the gate combination
   const S* GT = static_cast<const S*>(a.gates) + b * a.gs[0] + h * a.gs[2];
   SO* OUT = static_cast<SO*>(a.out) + b * a.os[0] + h * a.os[2] + 4 * grp;
 #pragma unroll
   for (int qt = 0; qt < TPW; ++qt) {
     const int t = t0 + qt;
-    if (t >= a.L) break;
-    const int own = t >> 6;
-    const int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.L + t) * a.G + g) * a.n;
-    float ms = kNegBig, lsum = 0.f;
-    f32x4 os[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) os[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-    for (int e = 0; e < a.n; ++e) {
-      const int j = row[e];
-      if (j < 0 || j > own) continue;
-      const S* kt = KT + static_cast<int64_t>(j) * (64 * D);
-      const S* vt = VT + static_cast<int64_t>(j) * (64 * D);
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int kb = 64 * j + 32 * s2;
-        if (kb > t) break;
-        Frag<T> kf[2][KS];
-        Frag<T> vf[DT];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-          for (int s = 0; s < KS; ++s) kf[h2][s] = frag_load<T>(kt + ktile_frag(2 * s2 + h2, s, lane, D));
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vf[dt] = frag_load<T>(vt + vtile_frag(dt, s2, lane));
-        f32x4 st[2];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          st[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < KS; ++s) mma(st[h2], kf[h2][s], qf[qt][s]);
-        }
-        online_step<T, DT>(st, kb, 0, t, grp, sl2, ms, lsum, os, vf);
-      }
-    }
-    const float lst = col_sum4(lsum);
-    const float lwt = col_sum4(lw[qt]);
-    if (colv) {
-      const int64_t gt = static_cast<int64_t>(t) * a.gs[1];
-      const float gsl = to_f32<T>(GT[gt + 1]);
-      const float gwn = to_f32<T>(GT[gt + 2]);
-      const float fs = lst > 0.f ? gsl / lst : 0.f;
-      const float fw = gwn / lwt;
+    const float lt = col_sum4(l[qt]);
+    if (t < a.L && colv) {
+      const float gsl = to_f32<T>(GT[static_cast<int64_t>(t) * a.gs[1] + 1]);
+      const float f = lt > 0.f ? gsl / lt : 0.f;
       SO* o = OUT + static_cast<int64_t>(t) * a.os[1];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const f32x4 prev = load4<O>(o + 16 * dt);
-        store4<O>(o + 16 * dt, prev + os[dt] * fs + ow[qt][dt] * fw);
+        store4<O>(o + 16 * dt, prev + acc[qt][dt] * f);
       }
     }
   }
@@ -515,27 +674,40 @@ __global__ __launch_bounds__(256) void k_sw(PrefillArgs a) {
 
 // ------------------------------------------------------------------ launcher
 
+size_t cmpwin_lds_bytes(int waves, int NcT, int D, bool bf16) {
+  return 4 * 64 * static_cast<size_t>(D) * (bf16 ? 2 : 4) + cmp_lds_bytes(waves, NcT);
+}
+
 static hipError_t record(hipEvent_t* ev, int i, hipStream_t st) {
   return ev != nullptr ? hipEventRecord(ev[i], st) : hipSuccess;
 }
 
+template <class T, class O, int D, int NW>
+static hipError_t launch_cmpwin(const PrefillArgs& a, hipStream_t st) {
+  const size_t lds = cmpwin_lds_bytes(NW, a.NcT, D, sizeof(typename T::storage) == 2);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cmpwin<T, O, D, NW>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_cmpwin<T, O, D, NW>), dim3(a.B * a.G * a.cmp_tiles), dim3(64 * NW), lds, st, a);
+  return hipSuccess;
+}
+
 template <class T, class O, int D>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st, hipEvent_t* ev) {
-  const size_t lds = a.inject ? 0 : cmp_lds_bytes(a.cmp_waves, a.NcT);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cmp<T, O, D, kCmpTPW>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(lds));
-  if (e != hipSuccess) return e;
+  hipError_t e;
   const int nblk_prep = max(a.Nb, a.NcT * 64);
   if ((e = record(ev, 0, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((k_prep<T, D>), dim3(nblk_prep, a.G, a.B), dim3(256), 0, st, a);
   if ((e = record(ev, 1, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_cmp<T, O, D, kCmpTPW>), dim3(a.B * a.G * a.cmp_tiles), dim3(64 * a.cmp_waves),
-                     lds, st, a);
+  if (a.cmp_waves == 8) e = launch_cmpwin<T, O, D, 8>(a, st);
+  else if (a.cmp_waves == 4) e = launch_cmpwin<T, O, D, 4>(a, st);
+  else if (a.cmp_waves == 2) e = launch_cmpwin<T, O, D, 2>(a, st);
+  else e = launch_cmpwin<T, O, D, 1>(a, st);
+  if (e != hipSuccess) return e;
   if ((e = record(ev, 2, st)) != hipSuccess) return e;
-  const int N = a.B * a.G * a.sw_tiles;
+  const int N = a.B * a.G * a.sel_tiles;
   const int per = (N + 7) / 8;
-  hipLaunchKernelGGL((k_sw<T, O, D, kSwTPW>), dim3(per * 8), dim3(64 * kSwWaves), 0, st, a);
+  hipLaunchKernelGGL((k_sel<T, O, D>), dim3(per * 8), dim3(256), 0, st, a);
   if ((e = record(ev, 3, st)) != hipSuccess) return e;
   return hipGetLastError();
 }

@@ -150,8 +150,8 @@ def test_decode_workspace_and_validation(L):
     n = ctypes.c_size_t()
     d = ddesc()
     assert L.nsa_decode_workspace_bytes(ctypes.byref(d), ctypes.byref(p), ctypes.byref(n)) == OK
-    # partial states: 4 slots per split; splits: 4 compressed + 2 window + 4 selected, + 1 merged
-    nslots = 4 * (4 + 2 + 4) + 1
+    # one merged partial state per split: 4 compressed + 2 window splits
+    nslots = 4 + 2
     part = 64 * 4 * nslots * (32 + 16 * 128) * 4
     logits = 64 * 4 * 16 * 1024 * 4
     assert n.value == part + logits + 64 * 4 * 16 * 4
