@@ -33,7 +33,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 PREFILL_STAGES = ["k_prep", "k_cmpwin", "k_sel"]
-DECODE_STAGES = ["k_dec_scan", "k_dec_finish"]
+DECODE_STAGES = ["k_dec"]
 
 
 def log(msg):

@@ -192,9 +192,9 @@ nsa_status_t nsa_compress_kv(int32_t batch, int32_t n_kv_heads, int32_t n_tokens
  * (passed as void*) on the stream: before each of the call's kernels and
  * after the last one. Prefill runs 3 kernels (block compression + re-layout;
  * compressed branch + block selection; selected + window branches + gate
- * combination), so stage_events holds 4 events; decode runs 2 kernels
- * (compressed and window chunks; merge + selection + selected blocks +
- * combination), so it holds 3. A NULL array or entry is
+ * combination), so stage_events holds 4 events; decode runs 1 kernel
+ * (all three branches, selection and combination), so it holds 2. A NULL
+ * array or entry is
  * NSA_ERR_INVALID_ARGUMENT.
  */
 nsa_status_t nsa_fwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_params_t* params,

@@ -160,8 +160,8 @@ nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, Pr
 // ------------------------------------------------------------------ decode
 
 struct DecodePlan {
-  int SC, SW, NmaxPad, nslots;
-  size_t off_part, off_logits, off_idx, total;
+  int NmaxPad;
+  size_t off_logits, off_idx, total;
 };
 
 nsa_status_t plan_decode(const nsa_decode_desc_t* d, const nsa_params_t* p, DecodePlan* pl) {
@@ -184,20 +184,14 @@ nsa_status_t plan_decode(const nsa_decode_desc_t* d, const nsa_params_t* p, Deco
   NSA_TRY(check_strides("out", d->o_stride, 2, false));
   const int64_t B = d->batch, G = d->n_kv_heads, D = d->head_dim;
   const int nv = d->max_seqlen / 64;
-  pl->SC = (nv + nsa::kDecSplitKeys - 1) / nsa::kDecSplitKeys;
-  const int wv = p->sliding_window < d->max_seqlen ? p->sliding_window : d->max_seqlen;
-  pl->SW = (wv + nsa::kDecSplitKeys - 1) / nsa::kDecSplitKeys;
-  pl->NmaxPad = pl->SC * nsa::kDecSplitKeys;
-  pl->nslots = pl->SC + pl->SW;
+  pl->NmaxPad = (nv + 63) / 64 * 64;
   if (B * G > INT32_MAX / 16)
     return fail(NSA_ERR_UNSUPPORTED, "batch * n_kv_heads too large");
-  if (nsa::dec_finish_lds_bytes(pl->NmaxPad, static_cast<int>(D), d->in_dtype == NSA_BF16) >
+  if (nsa::dec_lds_bytes(pl->NmaxPad, static_cast<int>(D), d->in_dtype == NSA_BF16) >
       static_cast<size_t>(nsa::kMaxLds))
     return fail(NSA_ERR_UNSUPPORTED, "max_seqlen %d needs more LDS for block scores than a CU has",
                 d->max_seqlen);
   size_t off = 0;
-  pl->off_part = off;
-  off = align_up(off + static_cast<size_t>(B * G) * pl->nslots * (32 + 16 * D) * sizeof(float));
   pl->off_logits = off;
   off = align_up(off + static_cast<size_t>(B * G) * 16 * pl->NmaxPad * sizeof(float));
   pl->off_idx = off;
@@ -381,8 +375,6 @@ static nsa_status_t decode_impl(const nsa_decode_desc_t* desc, const nsa_params_
   a.D = desc->head_dim;
   a.n = params->select_top_k;
   a.w = params->sliding_window;
-  a.SC = pl.SC;
-  a.SW = pl.SW;
   a.NmaxPad = pl.NmaxPad;
   a.scale_log2 = scale_log2(params, a.D);
   a.inject = idx_mode == NSA_IDX_INJECT ? 1 : 0;
@@ -395,7 +387,6 @@ static nsa_status_t decode_impl(const nsa_decode_desc_t* desc, const nsa_params_
   a.gates = gates;
   a.out = out;
   char* ws = static_cast<char*>(workspace);
-  a.part = reinterpret_cast<float*>(ws + pl.off_part);
   a.logits = reinterpret_cast<float*>(ws + pl.off_logits);
   a.idx = idx != nullptr ? idx : reinterpret_cast<int32_t*>(ws + pl.off_idx);
   for (int i = 0; i < 2; ++i) {

@@ -1,148 +1,216 @@
 // NSA decode on gfx950: one new query token per sequence against a K/V cache
 // and a block-mean cache, measured apart from prefill as the NSA how-to
-// (qwbw.cn/news/106443), section 5, advises. The work is HBM-bound: every key
-// is read once and serves the 16 query heads of its group, so the kernels
-// are organised around keeping many 32 KiB chunks in flight.
+// (qwbw.cn/news/106443), section 5, advises.
 //
-//  k_dec_scan    grid (sequence x group, compressed splits + window splits).
-//                Each wave loads one 64-key chunk (64 block means, or 64
-//                window tokens) into registers, attends the group's 16 heads
-//                over it, and the workgroup merges its 4 waves into one
-//                partial softmax state (max, sum, unnormalised output). The
-//                compressed splits also store their logits for the scores.
-//  k_dec_finish  one workgroup per (sequence, group): merges the compressed
-//                partials into the log-sum-exp and gate_cmp * O_cmp, forms
-//                the block scores (probabilities summed over the group's
-//                heads), selects the own block + top-(n-1) earlier blocks
-//                (nsa_topk.h), gathers the selected blocks across its waves,
-//                and adds the gated selected and window branches into out.
-//
-// K rows feed the S^T = K Q^T product straight from the cache; V rows go
-// through LDS into the permuted V^T tile order of the P.V product.
+// k_dec: one workgroup per (sequence, KV group), 8 waves, one launch. The work
+// is HBM-bound -- every key is read once and serves the 16 query heads of its
+// group -- so the waves stream it in 32-key half chunks, each wave keeping the
+// next one in flight (a register ring) while it computes the current:
+//   A  compressed half chunks (block means), dealt round-robin to the waves;
+//      the logits go to the workspace for the block scores;
+//   B  the waves' compressed states are merged through LDS into the
+//      log-sum-exp and gate_cmp * O_cmp (kept in registers until the end);
+//   C  block scores (probabilities summed over the group's heads); wave 0
+//      selects the own block + top-(n-1) earlier blocks (nsa_topk.h) and
+//      lists their usable half blocks while the other waves stream the
+//      sliding window, whose states are then merged into gate_win * O_win;
+//   D  the selected half blocks, dealt round-robin to all waves, merged into
+//      gate_slc * O_slc;
+//   E  the sum of the three gated branches is written to out.
+// K rows feed the S^T = K Q^T product straight from the caches. V rows are
+// written to LDS row-major (padded so that reads do not conflict) and each
+// lane gathers the 8 keys of its V^T operand fragment from there.
 #include "nsa_device.h"
 #include "nsa_internal.h"
 #include "nsa_topk.h"
 
 namespace nsa {
 
-// floats per partial slot: m[16], l[16], O[16][D]
+// floats per partial state: m[16], l[16], O[16][D]
 __host__ __device__ constexpr int dec_slot_floats(int D) { return 32 + 16 * D; }
 
-__device__ __forceinline__ int dec_seqlen(const DecodeArgs& a, int b) {
-  const int s = a.seqlens[b];
-  return (s >= 1 && s <= a.Lmax) ? s : 0;  // 0 marks an invalid sequence
-}
-
-// One wave's registers for a 64-key chunk: the K rows as A operands and the V
-// rows as 8-element vectors (lane l holds rows l/(D/8) + 64 i/(D/8)).
+// One wave's registers for 32 keys: K rows as A operands of two key tiles,
+// V rows as 8-element vectors (which row and columns a lane holds: v_row,
+// v_col).
 template <class T, int D>
-struct Chunk {
-  Frag<T> k[4][D / 32];
-  Frag<T> v[D / 8];
+struct DHalf {
+  Frag<T> k[2][D / 32];
+  Frag<T> v[D / 16];
 };
 
-// Loads keys [key0, key0 + 64) restricted to [klo, khi]; rows outside are
-// zero and never read.
+// V vector i of lane l. bf16: rows come in pairs (2p, 2p + 1) held by the
+// same lane, so that the pair can be interleaved into dwords for LDS; fp32:
+// row-major order. Each load instruction covers whole rows.
 template <class T, int D>
-__device__ __forceinline__ void chunk_load(Chunk<T, D>& c, const typename T::storage* krows,
-                                           int64_t kst, const typename T::storage* vrows,
-                                           int64_t vst, int key0, int klo, int khi, int lane) {
+__device__ __forceinline__ int v_row(int lane, int i) {
+  constexpr int VPR = D / 8;
+  if constexpr (sizeof(typename T::storage) == 2)
+    return 2 * (lane / VPR + (64 / VPR) * (i >> 1)) + (i & 1);
+  else
+    return (lane + 64 * i) / VPR;
+}
+template <int D>
+__device__ __forceinline__ int v_col(int lane) { return (lane % (D / 8)) * 8; }
+
+// A half chunk: keys [key0, key0 + 32) of rows kr / vr, of which those in
+// [klo, khi] count (klo <= khi); lrow (or nullptr) receives this lane's logits.
+template <class T>
+struct DItem {
+  const typename T::storage* kr;
+  const typename T::storage* vr;
+  int64_t kst, vst;
+  int key0, klo, khi;
+  float* lrow;
+};
+
+// Rows outside [klo, khi] are loaded from the nearest row inside: their
+// logits are masked to -inf, so they get probability 0 and only have to be
+// finite.
+template <class T, int D>
+__device__ __forceinline__ void dhalf_load(DHalf<T, D>& c, const DItem<T>& it, int lane) {
   const int col = lane & 15, grp = lane >> 4;
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    const int key = key0 + 16 * kt + col;
-    const bool ok = key >= klo && key <= khi;
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = min(max(it.key0 + 16 * kt + col, it.klo), it.khi);
+    const typename T::storage* p = it.kr + static_cast<int64_t>(key) * it.kst + 8 * grp;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s)
-      c.k[kt][s] = ok ? frag_load<T>(krows + static_cast<int64_t>(key) * kst + 32 * s + 8 * grp)
-                      : frag_zero<T>();
+    for (int s = 0; s < D / 32; ++s) c.k[kt][s] = frag_load<T>(p + 32 * s);
   }
-  constexpr int VPR = D / 8;
 #pragma unroll
-  for (int i = 0; i < VPR; ++i) {
-    const int e = lane + 64 * i;
-    const int key = key0 + e / VPR;
-    const bool ok = key >= klo && key <= khi;
-    c.v[i] = ok ? frag_load<T>(vrows + static_cast<int64_t>(key) * vst + (e % VPR) * 8) : frag_zero<T>();
+  for (int i = 0; i < D / 16; ++i) {
+    const int key = min(max(it.key0 + v_row<T, D>(lane, i), it.klo), it.khi);
+    c.v[i] = frag_load<T>(it.vr + static_cast<int64_t>(key) * it.vst + v_col<D>(lane));
   }
 }
 
-// Online-softmax update of (m, l, acc) with one loaded chunk. lv: this wave's
-// 64*D elements of LDS. lrow (optional): receives the masked log2-domain
-// logits of the chunk's 64 keys for this lane's query column.
+// LDS staging of a wave's V half chunk, and the V^T operand fragments read
+// back from it. Fragment dt of lane l holds V[kappa(l/16, j)][16 dt + l%16],
+// kappa(a, j) = 4a + j (j < 4), 16 + 4a + j - 4 (j >= 4): the keys whose
+// probabilities the lane holds in the two S^T tiles (see pack_p). Rows are
+// padded by 16 bytes so that the four lane groups of a read hit distinct
+// banks.
 template <class T, int D>
-__device__ __forceinline__ void chunk_attend(const Chunk<T, D>& c, int key0, int klo, int khi,
-                                             const Frag<T> (&qf)[D / 32], float sl2,
-                                             typename T::storage* lv, float& m, float& l,
-                                             f32x4 (&acc)[D / 16], float* lrow, int lane) {
-  using S = typename T::storage;
-  constexpr int KS = D / 32, DT = D / 16, VPR = D / 8;
-  const int grp = lane >> 4;
+struct VStage;
+
+// bf16: dword (p, d) holds V[2p][d] (low half) and V[2p + 1][d] (high half),
+// so a fragment is four dword reads and needs no repacking.
+template <int D>
+struct VStage<BF16, D> {
+  static constexpr int kRow = D + 8;  // dwords per row pair
+  static constexpr size_t kBytes = 16 * kRow * 4;
+  __device__ static void put(void* lds, const DHalf<BF16, D>& c, int lane) {
+    uint32_t* base = static_cast<uint32_t*>(lds);
 #pragma unroll
-  for (int i = 0; i < VPR; ++i) {
-    const int e = lane + 64 * i;
-    const int r = e / VPR, cc = (e % VPR) * 8;
-    __align__(16) S tmp[8];
-    frag_store<T>(tmp, c.v[i]);
+    for (int q = 0; q < D / 32; ++q) {
+      const u32x4 r0 = c.v[2 * q].v, r1 = c.v[2 * q + 1].v;
+      u32x4 lo, hi;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) lv[vtile_off(r, cc + jj)] = tmp[jj];
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = r0[w], y = r1[w];
+        const uint32_t e = (x & 0xFFFFu) | (y << 16), o = (x >> 16) | (y & 0xFFFF0000u);
+        if (w < 2) {
+          lo[2 * w] = e;
+          lo[2 * w + 1] = o;
+        } else {
+          hi[2 * w - 4] = e;
+          hi[2 * w - 3] = o;
+        }
+      }
+      uint32_t* dst = base + (v_row<BF16, D>(lane, 2 * q) >> 1) * kRow + v_col<D>(lane);
+      *reinterpret_cast<u32x4*>(dst) = lo;
+      *reinterpret_cast<u32x4*>(dst + 4) = hi;
+    }
   }
-  f32x4 st[4];
+  __device__ static Frag<BF16> get(const void* lds, int dt, int lane) {
+    const uint32_t* p = static_cast<const uint32_t*>(lds) + 2 * (lane >> 4) * kRow + 16 * dt + (lane & 15);
+    Frag<BF16> f;
+    f.v = u32x4{p[0], p[kRow], p[8 * kRow], p[9 * kRow]};
+    return f;
+  }
+};
+
+// fp32: row-major.
+template <int D>
+struct VStage<F32, D> {
+  static constexpr int kRow = D + 4;  // floats per row
+  static constexpr size_t kBytes = 32 * kRow * 4;
+  __device__ static void put(void* lds, const DHalf<F32, D>& c, int lane) {
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
+    for (int i = 0; i < D / 16; ++i)
+      frag_store<F32>(static_cast<float*>(lds) + v_row<F32, D>(lane, i) * kRow + v_col<D>(lane), c.v[i]);
+  }
+  __device__ static Frag<F32> get(const void* lds, int dt, int lane) {
+    const float* p = static_cast<const float*>(lds) + 4 * (lane >> 4) * kRow + 16 * dt + (lane & 15);
+    Frag<F32> f;
+    f.lo = f32x4{p[0], p[kRow], p[2 * kRow], p[3 * kRow]};
+    f.hi = f32x4{p[16 * kRow], p[17 * kRow], p[18 * kRow], p[19 * kRow]};
+    return f;
+  }
+};
+
+// Online-softmax update of (m, l, acc) with one loaded half chunk; lv is this
+// wave's VStage<T, D>::kBytes of LDS.
+template <class T, int D>
+__device__ __forceinline__ void dhalf_attend(const DHalf<T, D>& c, const DItem<T>& it,
+                                             const Frag<T> (&qf)[D / 32], float sl2, void* lv,
+                                             float& m, float& l, f32x4 (&acc)[D / 16], int lane) {
+  constexpr int KS = D / 32, DT = D / 16;
+  const int grp = lane >> 4;
+  VStage<T, D>::put(lv, c, lane);
+  f32x4 st[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
     st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) mma(st[kt], c.k[kt][s], qf[s]);
   }
-  float mx = kNegBig;
+  if (it.lrow != nullptr) {
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x4 x;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = key0 + 16 * kt + 4 * grp + i;
-      const float x = (key >= klo && key <= khi) ? st[kt][i] * sl2 : -INFINITY;
-      st[kt][i] = x;
-      mx = fmaxf(mx, x);
+      for (int i = 0; i < 4; ++i) {
+        const int key = it.key0 + 16 * kt + 4 * grp + i;
+        x[i] = (key >= it.klo && key <= it.khi) ? st[kt][i] * sl2 : -INFINITY;
+      }
+      *reinterpret_cast<f32x4*>(it.lrow + 16 * kt + 4 * grp) = x;
     }
-  if (lrow != nullptr) {
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) *reinterpret_cast<f32x4*>(lrow + 16 * kt + 4 * grp) = st[kt];
   }
-  mx = col_max4(mx);
-  const float mn = fmaxf(m, mx);
-  const float alpha = fast_exp2(m - mn);
-  float sum = 0.f;
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = fast_exp2(st[kt][i] - mn);
-      st[kt][i] = p;
-      sum += p;
-    }
-  l = l * alpha + sum;
-  m = mn;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
   wave_lds_sync();
+  Frag<T> vf[DT];
 #pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2) {
-    const Frag<T> pf = pack_p<T>(st[2 * s2], st[2 * s2 + 1]);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) mma(acc[dt], frag_load<T>(lv + vtile_frag(dt, s2, lane)), pf);
-  }
+  for (int dt = 0; dt < DT; ++dt) vf[dt] = VStage<T, D>::get(lv, dt, lane);
+  const bool full = it.key0 >= it.klo && it.key0 + 31 <= it.khi;
+  if (full)
+    online_step<T, DT, false>(st, it.key0, 0, 0, grp, sl2, m, l, acc, vf);
+  else
+    online_step<T, DT, true>(st, it.key0, it.klo, it.khi, grp, sl2, m, l, acc, vf);
   wave_lds_sync();
 }
 
-template <class T, int D>
-__device__ __forceinline__ void dec_load_q(const DecodeArgs& a, int b, int g, int lane,
-                                           Frag<T> (&qf)[D / 32]) {
-  using S = typename T::storage;
-  const int col = lane & 15, grp = lane >> 4;
-  const bool ok = col < a.Hg;
-  const S* Q = static_cast<const S*>(a.q) + b * a.qs[0] + (g * a.Hg + col) * a.qs[1] + 8 * grp;
+// Streams `count` half chunks desc(0..count-1) through a ring of RING
+// register buffers (RING - 1 loads in flight while one is computed).
+// count must be wave-uniform.
+template <class T, int D, int RING, class Desc, class Body>
+__device__ __forceinline__ void dstream(int count, Desc desc, Body body, int lane) {
+  DHalf<T, D> ring[RING];
 #pragma unroll
-  for (int s = 0; s < D / 32; ++s) qf[s] = ok ? frag_load<T>(Q + 32 * s) : frag_zero<T>();
+  for (int r = 0; r < RING; ++r)
+    if (r < count) dhalf_load<T, D>(ring[r], desc(r), lane);
+#pragma unroll 1
+  for (int base = 0; base < count; base += RING) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      const int k = base + r;
+      if (k < count) {
+        body(ring[r], desc(k));
+        // keep the refill after the body: hoisted above it, the new loads
+        // would need a third set of registers
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + RING < count) dhalf_load<T, D>(ring[r], desc(k + RING), lane);
+      }
+    }
+  }
 }
 
 // Stores a wave's partial state (m per column, l summed over the column's
@@ -160,8 +228,7 @@ __device__ __forceinline__ void store_partial(float* dst, float m, float l, cons
     *reinterpret_cast<f32x4*>(dst + 32 + col * D + 16 * dt + 4 * grp) = acc[dt];
 }
 
-// Merges `cnt` partial slots (stride SF floats) for head h: returns the
-// merged (max, sum); the output merge is done element-wise by the caller.
+// Merged (max, sum) of head h over `cnt` partial states (stride SF floats).
 __device__ __forceinline__ void merge_stats(const float* p, int cnt, int SF, int h, float& M, float& L) {
   M = kNegBig;
   for (int s = 0; s < cnt; ++s) M = fmaxf(M, p[s * SF + h]);
@@ -169,202 +236,214 @@ __device__ __forceinline__ void merge_stats(const float* p, int cnt, int SF, int
   for (int s = 0; s < cnt; ++s) L += p[s * SF + 16 + h] * fast_exp2(p[s * SF + h] - M);
 }
 
-template <class T, int D>
-__global__ __launch_bounds__(256) void k_dec_scan(DecodeArgs a) {
-  using S = typename T::storage;
-  constexpr int SF = dec_slot_floats(D), DT = D / 16;
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int bg = blockIdx.x, b = bg / a.G, g = bg % a.G;
-  const int sidx = blockIdx.y;
-  const int seqlen = dec_seqlen(a, b);
-  const int t = seqlen - 1;  // -1 for an invalid sequence: every chunk is empty
-  S* lv = reinterpret_cast<S*>(smem) + wave * 64 * D;
-  Frag<T> qf[D / 32];
-  dec_load_q<T, D>(a, b, g, lane, qf);
-
-  int key0, klo, khi;
-  const S *kr, *vr;
-  int64_t kst, vst;
-  float* lrow = nullptr;
-  if (sidx < a.SC) {
-    key0 = (4 * sidx + wave) * 64;
-    klo = 0;
-    khi = (seqlen >> 6) - 1;
-    kr = static_cast<const S*>(a.kccache) + b * a.kcs[0] + g * a.kcs[1];
-    vr = static_cast<const S*>(a.vccache) + b * a.vcs[0] + g * a.vcs[1];
-    kst = a.kcs[2];
-    vst = a.vcs[2];
-    lrow = a.logits + (static_cast<int64_t>(bg) * 16 + (lane & 15)) * a.NmaxPad + key0;
-  } else {
-    const int wlo = max(0, seqlen - a.w);
-    key0 = wlo + (4 * (sidx - a.SC) + wave) * 64;
-    klo = wlo;
-    khi = t;
-    kr = static_cast<const S*>(a.kcache) + b * a.ks[0] + g * a.ks[1];
-    vr = static_cast<const S*>(a.vcache) + b * a.vs[0] + g * a.vs[1];
-    kst = a.ks[2];
-    vst = a.vs[2];
-  }
-  float m = kNegBig, l = 0.f;
-  f32x4 acc[DT];
+// Element e of the merged unnormalised output (relative to max M of its head).
+template <int NWV>
+__device__ __forceinline__ float merge_out(const float* p, int SF, int h, int e, float M) {
+  float o = 0.f;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (max(key0, klo) <= min(key0 + 63, khi)) {
-    Chunk<T, D> c;
-    chunk_load<T, D>(c, kr, kst, vr, vst, key0, klo, khi, lane);
-    chunk_attend<T, D>(c, key0, klo, khi, qf, a.scale_log2, lv, m, l, acc, lrow, lane);
-  }
-  l = col_sum4(l);
-  // merge the 4 waves through LDS (reusing the V staging area)
-  __syncthreads();
-  float* mrg = reinterpret_cast<float*>(smem);
-  store_partial<D>(mrg + wave * SF, m, l, acc, lane);
-  __syncthreads();
-  float* slot = a.part + (static_cast<int64_t>(bg) * (a.SC + a.SW) + sidx) * SF;
-  if (tid < 16) {
-    float M, L;
-    merge_stats(mrg, 4, SF, tid, M, L);
-    slot[tid] = M;
-    slot[16 + tid] = L;
-  }
-  for (int e = tid; e < 16 * D; e += 256) {
-    const int h = e / D;
-    float M = kNegBig;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg[w * SF + h]);
-    float o = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) o += mrg[w * SF + 32 + e] * fast_exp2(mrg[w * SF + h] - M);
-    slot[32 + e] = o;
-  }
+  for (int w = 0; w < NWV; ++w) o += p[w * SF + 32 + e] * fast_exp2(p[w * SF + h] - M);
+  return o;
 }
 
-template <class T, class O, int D, int FW>
-__global__ __launch_bounds__(512) void k_dec_finish(DecodeArgs a) {
+template <int D>
+__device__ __forceinline__ void reset_state(float& m, float& l, f32x4 (&acc)[D / 16]) {
+  m = kNegBig;
+  l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Merges the per-wave states (m, l, acc) of one branch through LDS and adds
+// gate * O of the branch to res (this thread's EPT output elements
+// tid + NT r); gates[goff + h * gstride] is head h's gate. Begins and ends
+// with a workgroup barrier, so parts may alias the V staging.
+template <class T, int D, int NWV>
+__device__ __forceinline__ void merge_into(float* parts, float m, float l, const f32x4 (&acc)[D / 16],
+                                           const typename T::storage* gates, int64_t goff,
+                                           int64_t gstride, int Hg, float* hs,
+                                           float (&res)[16 * D / (64 * NWV)], int tid, int lane) {
+  constexpr int SF = dec_slot_floats(D), NT = 64 * NWV, EPT = 16 * D / NT;
+  __syncthreads();
+  store_partial<D>(parts + (tid >> 6) * SF, m, l, acc, lane);
+  __syncthreads();
+  if (tid < 16) {
+    float M, L;
+    merge_stats(parts, NWV, SF, tid, M, L);
+    const float gt = tid < Hg ? to_f32<T>(gates[goff + tid * gstride]) : 0.f;
+    hs[4 * tid] = M;
+    hs[4 * tid + 1] = L > 0.f ? gt / L : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < EPT; ++r) {
+    const int e = tid + NT * r, h = e / D;
+    res[r] += merge_out<NWV>(parts, SF, h, e, hs[4 * h]) * hs[4 * h + 1];
+  }
+  __syncthreads();
+}
+
+constexpr int kDecWaves = 8;
+
+template <class T, int D>
+__host__ __device__ constexpr size_t dec_big_bytes() {
+  constexpr size_t stage = static_cast<size_t>(kDecWaves) * VStage<T, D>::kBytes;
+  constexpr size_t parts = static_cast<size_t>(kDecWaves) * dec_slot_floats(D) * sizeof(float);
+  return stage > parts ? stage : parts;
+}
+
+template <class T, class O, int D, int RING>
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_dec(DecodeArgs a) {
   using S = typename T::storage;
   using SO = typename O::storage;
-  constexpr int SF = dec_slot_floats(D), DT = D / 16, NT = 64 * FW;
+  constexpr int NWV = kDecWaves, NT = 64 * NWV, SF = dec_slot_floats(D), DT = D / 16;
+  constexpr int EPT = 16 * D / NT;
   extern __shared__ __align__(16) unsigned char smem[];
-  float* sc = reinterpret_cast<float*>(smem);
+  float* parts = reinterpret_cast<float*>(smem);  // aliases the V staging
+  float* sc = reinterpret_cast<float*>(smem + dec_big_bytes<T, D>());
   uint64_t* surv = reinterpret_cast<uint64_t*>(sc + a.NmaxPad);
   int* selb = reinterpret_cast<int*>(surv + kSurvCap);
   int* selo = selb + 64;
-  float* hs = reinterpret_cast<float*>(selo + 64);  // per head: M, L, lse2, g_cmp
-  float* ocmp = hs + 64;                            // [16][D]
-  unsigned char* big = reinterpret_cast<unsigned char*>(ocmp + 16 * D);
+  int* hl = selo + 64;              // usable selected half blocks: 2 j + half
+  int* nhl = hl + 128;              // their count
+  float* hs = reinterpret_cast<float*>(nhl + 4);  // per head: 4 floats
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15;
   const int bg = blockIdx.x, b = bg / a.G, g = bg % a.G;
-  const int seqlen = dec_seqlen(a, b);
-  const int nslot = a.SC + a.SW;
-  const float* P = a.part + static_cast<int64_t>(bg) * nslot * SF;
+  const int s_raw = a.seqlens[b];
   int32_t* idxo = a.idx + static_cast<int64_t>(bg) * a.n;
   const S* GT = static_cast<const S*>(a.gates) + b * a.gs[0];
   SO* OUT = static_cast<SO*>(a.out) + b * a.os[0];
-  if (seqlen == 0) {
+  if (s_raw < 1 || s_raw > a.Lmax) {  // invalid length: nothing of this sequence is read
     for (int e = tid; e < a.Hg * D; e += NT) OUT[(g * a.Hg + e / D) * a.os[1] + e % D] = from_f32<O>(0.f);
     if (!a.inject && tid < a.n) idxo[tid] = -1;
     return;
   }
-  const int t = seqlen - 1, nvis = seqlen >> 6, own = t >> 6;
+  const int t = s_raw - 1, nvis = s_raw >> 6, own = t >> 6;
+  const int wlo = max(0, s_raw - a.w);
+  const float sl2 = a.scale_log2;
+  void* lv = smem + wave * VStage<T, D>::kBytes;
 
-  // ---- compressed branch: merge the partials, log-sum-exp, gated output
+  Frag<T> qf[D / 32];
+  {
+    const S* Q = static_cast<const S*>(a.q) + b * a.qs[0] + (g * a.Hg + col) * a.qs[1] + 8 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) qf[s] = col < a.Hg ? frag_load<T>(Q + 32 * s) : frag_zero<T>();
+  }
+  const S* KCr = static_cast<const S*>(a.kccache) + b * a.kcs[0] + g * a.kcs[1];
+  const S* VCr = static_cast<const S*>(a.vccache) + b * a.vcs[0] + g * a.vcs[1];
+  const S* Kr = static_cast<const S*>(a.kcache) + b * a.ks[0] + g * a.ks[1];
+  const S* Vr = static_cast<const S*>(a.vcache) + b * a.vs[0] + g * a.vs[1];
+  float* lbase = a.inject ? nullptr : a.logits + (static_cast<int64_t>(bg) * 16 + col) * a.NmaxPad;
+
+  float m, l;
+  f32x4 acc[DT];
+  auto attend = [&](const DHalf<T, D>& c, const DItem<T>& it) {
+    dhalf_attend<T, D>(c, it, qf, sl2, lv, m, l, acc, lane);
+  };
+
+  // ---- A: compressed half chunks
+  {
+    const int ncmp = (nvis + 31) >> 5;
+    reset_state<D>(m, l, acc);
+    dstream<T, D, RING>((ncmp - wave + NWV - 1) / NWV, [&](int k) {
+      const int q = wave + NWV * k;
+      return DItem<T>{KCr, VCr, a.kcs[2], a.vcs[2], 32 * q, 0, nvis - 1,
+                      lbase != nullptr ? lbase + 32 * q : nullptr};
+    }, attend, lane);
+    l = col_sum4(l);
+  }
+
+  // ---- B: merge into the log-sum-exp and gate_cmp * O_cmp
+  __syncthreads();
+  store_partial<D>(parts + wave * SF, m, l, acc, lane);
+  __syncthreads();
   if (tid < 16) {
     float M, L;
-    merge_stats(P, a.SC, SF, tid, M, L);
+    merge_stats(parts, NWV, SF, tid, M, L);
     hs[4 * tid] = M;
     hs[4 * tid + 1] = L;
     hs[4 * tid + 2] = (nvis > 0 && tid < a.Hg) ? M + fast_log2(L) : INFINITY;
     hs[4 * tid + 3] = tid < a.Hg ? to_f32<T>(GT[(g * a.Hg + tid) * a.gs[1]]) : 0.f;
   }
   __syncthreads();
-  for (int e = tid; e < 16 * D; e += NT) {
-    const int h = e / D;
-    float o = 0.f;
-    for (int s = 0; s < a.SC; ++s) o += P[s * SF + 32 + e] * fast_exp2(P[s * SF + h] - hs[4 * h]);
-    ocmp[e] = nvis > 0 ? o / hs[4 * h + 1] * hs[4 * h + 3] : 0.f;
+  float res[EPT];
+#pragma unroll
+  for (int r = 0; r < EPT; ++r) {
+    const int e = tid + NT * r, h = e / D;
+    res[r] = nvis > 0 ? merge_out<NWV>(parts, SF, h, e, hs[4 * h]) / hs[4 * h + 1] * hs[4 * h + 3] : 0.f;
   }
 
-  // ---- block scores and selection
+  // ---- C: block scores (the logits were written by this workgroup)
   if (!a.inject) {
     for (int j = tid; j < own; j += NT) {
+      const float* lg = a.logits + static_cast<int64_t>(bg) * 16 * a.NmaxPad + j;
       float s = 0.f;
-      for (int h = 0; h < a.Hg; ++h)
-        s += fast_exp2(a.logits[(static_cast<int64_t>(bg) * 16 + h) * a.NmaxPad + j] - hs[4 * h + 2]);
+#pragma unroll
+      for (int h = 0; h < 16; ++h)
+        if (h < a.Hg) s += fast_exp2(lg[h * a.NmaxPad] - hs[4 * h + 2]);
       sc[j] = s;
     }
-    __syncthreads();
-    if (wave == 0) topk_wave(sc, own, a.n, selo, surv, selb, lane);
-    __syncthreads();
-    if (tid < a.n) idxo[tid] = selo[tid];
-  } else {
-    if (tid < a.n) selo[tid] = idxo[tid];
-    __syncthreads();
   }
+  __syncthreads();  // parts read, sc written: the staging area is free again
 
-  // ---- selected blocks, spread over the waves
-  Frag<T> qf[D / 32];
-  dec_load_q<T, D>(a, b, g, lane, qf);
-  const S* kr = static_cast<const S*>(a.kcache) + b * a.ks[0] + g * a.ks[1];
-  const S* vr = static_cast<const S*>(a.vcache) + b * a.vs[0] + g * a.vs[1];
-  S* lv = reinterpret_cast<S*>(big) + wave * 64 * D;
-  float m = kNegBig, l = 0.f;
-  f32x4 acc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int e = wave; e < a.n; e += FW) {
-    const int j = selo[e];
-    if (j < 0 || j > own) continue;  // unusable injected entry
-    Chunk<T, D> c;
-    chunk_load<T, D>(c, kr, a.ks[2], vr, a.vs[2], 64 * j, 64 * j, t, lane);
-    chunk_attend<T, D>(c, 64 * j, 64 * j, t, qf, a.scale_log2, lv, m, l, acc, nullptr, lane);
+  // ---- C': wave 0 selects, the other waves stream the window
+  if (wave == 0) {
+    if (!a.inject) {
+      topk_wave(sc, own, a.n, selo, surv, selb, lane);
+      wave_lds_sync();
+      if (lane < a.n) idxo[lane] = selo[lane];
+    } else if (lane < a.n) {
+      selo[lane] = idxo[lane];
+    }
+    wave_lds_sync();
+    const int j = lane < a.n ? selo[lane] : -1;
+    const bool h0 = j >= 0 && j <= own;
+    const bool h1 = h0 && 64 * j + 32 <= t;
+    const uint64_t b0 = __ballot(h0), b1 = __ballot(h1);
+    const uint64_t below = (uint64_t{1} << lane) - 1;
+    const int pos = __popcll(b0 & below) + __popcll(b1 & below);
+    if (h0) hl[pos] = 2 * j;
+    if (h1) hl[pos + 1] = 2 * j + 1;
+    if (lane == 0) *nhl = __popcll(b0) + __popcll(b1);
   }
-  l = col_sum4(l);
-  __syncthreads();
-  float* wp = reinterpret_cast<float*>(big);  // per-wave partials, reusing the V staging
-  store_partial<D>(wp + wave * SF, m, l, acc, lane);
-  __syncthreads();
+  {
+    const int w0 = a.inject ? 0 : 1, nww = NWV - w0;
+    const int nwin = (t - wlo + 32) >> 5;
+    reset_state<D>(m, l, acc);
+    if (wave >= w0)
+      dstream<T, D, RING>((nwin - (wave - w0) + nww - 1) / nww, [&](int k) {
+        return DItem<T>{Kr, Vr, a.ks[2], a.vs[2], wlo + 32 * ((wave - w0) + nww * k), wlo, t, nullptr};
+      }, attend, lane);
+    l = col_sum4(l);
+  }
+  // merge the window now, so that its state does not stay in registers
+  merge_into<T, D, NWV>(parts, m, l, acc, GT, (g * a.Hg) * a.gs[1] + 2, a.gs[1], a.Hg, hs, res, tid, lane);
 
-  // ---- merge selected (in LDS) and window (from k_dec_scan) partials, combine
-  const float* W = P + a.SC * SF;
-  if (tid < 16) {  // per head: max and gate-scaled reciprocal sum of each branch
-    float Ms, Ls, Mw, Lw;
-    merge_stats(wp, FW, SF, tid, Ms, Ls);
-    merge_stats(W, a.SW, SF, tid, Mw, Lw);
-    const int hq = g * a.Hg + tid;
-    const float gsl = tid < a.Hg ? to_f32<T>(GT[hq * a.gs[1] + 1]) : 0.f;
-    const float gwn = tid < a.Hg ? to_f32<T>(GT[hq * a.gs[1] + 2]) : 0.f;
-    hs[4 * tid] = Ms;
-    hs[4 * tid + 1] = Ls > 0.f ? gsl / Ls : 0.f;
-    hs[4 * tid + 2] = Mw;
-    hs[4 * tid + 3] = Lw > 0.f ? gwn / Lw : 0.f;
+  // ---- D: selected half blocks
+  {
+    const int nh = *nhl;
+    reset_state<D>(m, l, acc);
+    dstream<T, D, RING>((nh - wave + NWV - 1) / NWV, [&](int k) {
+      const int u = hl[wave + NWV * k], j = u >> 1;
+      return DItem<T>{Kr, Vr, a.ks[2], a.vs[2], 64 * j + 32 * (u & 1), 64 * j, t, nullptr};
+    }, attend, lane);
+    l = col_sum4(l);
   }
-  __syncthreads();
-  for (int e = tid; e < a.Hg * D; e += NT) {
-    const int h = e / D;
-    float os = 0.f, ow = 0.f;
+  merge_into<T, D, NWV>(parts, m, l, acc, GT, (g * a.Hg) * a.gs[1] + 1, a.gs[1], a.Hg, hs, res, tid, lane);
+
+  // ---- E: out = gate_cmp O_cmp + gate_slc O_slc + gate_win O_win
 #pragma unroll
-    for (int w = 0; w < FW; ++w) os += wp[w * SF + 32 + e] * fast_exp2(wp[w * SF + h] - hs[4 * h]);
-    for (int s = 0; s < a.SW; ++s) ow += W[s * SF + 32 + e] * fast_exp2(W[s * SF + h] - hs[4 * h + 2]);
-    const float v = ocmp[e] + os * hs[4 * h + 1] + ow * hs[4 * h + 3];
-    OUT[(g * a.Hg + h) * a.os[1] + e % D] = from_f32<O>(v);
+  for (int r = 0; r < EPT; ++r) {
+    const int e = tid + NT * r, h = e / D;
+    if (h < a.Hg) OUT[(g * a.Hg + h) * a.os[1] + e % D] = from_f32<O>(res[r]);
   }
 }
 
-size_t dec_finish_lds_bytes(int NmaxPad, int D, bool bf16) {
-  const int FW = bf16 ? 8 : 4;
-  const size_t el = bf16 ? 2 : 4;
-  const size_t stage = static_cast<size_t>(FW) * 64 * D * el;
-  const size_t parts = static_cast<size_t>(FW) * dec_slot_floats(D) * sizeof(float);
-  return NmaxPad * sizeof(float) + kSurvCap * sizeof(uint64_t) + 128 * sizeof(int) +
-         64 * sizeof(float) + 16 * D * sizeof(float) + (stage > parts ? stage : parts);
-}
-
-size_t dec_scan_lds_bytes(int D, bool bf16) {
-  const size_t stage = 4 * 64 * static_cast<size_t>(D) * (bf16 ? 2 : 4);
-  const size_t parts = 4 * static_cast<size_t>(dec_slot_floats(D)) * sizeof(float);
-  return stage > parts ? stage : parts;
+size_t dec_lds_bytes(int NmaxPad, int D, bool bf16) {
+  const size_t big = bf16 ? (D == 64 ? dec_big_bytes<BF16, 64>() : dec_big_bytes<BF16, 128>())
+                          : (D == 64 ? dec_big_bytes<F32, 64>() : dec_big_bytes<F32, 128>());
+  return big + NmaxPad * sizeof(float) + kSurvCap * sizeof(uint64_t) +
+         (64 + 64 + 128 + 4) * sizeof(int) + 64 * sizeof(float);
 }
 
 static hipError_t record(hipEvent_t* ev, int i, hipStream_t st) {
@@ -374,22 +453,14 @@ static hipError_t record(hipEvent_t* ev, int i, hipStream_t st) {
 template <class T, class O, int D>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st, hipEvent_t* ev) {
   constexpr bool kBf16 = sizeof(typename T::storage) == 2;
-  constexpr int FW = kBf16 ? 8 : 4;
-  const size_t lds_scan = dec_scan_lds_bytes(D, kBf16);
-  const size_t lds_fin = dec_finish_lds_bytes(a.NmaxPad, D, kBf16);
-  hipError_t e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec_scan<T, D>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_scan));
+  constexpr int RING = kBf16 ? 2 : 1;
+  const size_t lds = dec_lds_bytes(a.NmaxPad, D, kBf16);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec<T, O, D, RING>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec_finish<T, O, D, FW>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_fin));
-  if (e != hipSuccess) return e;
-  const int BG = a.B * a.G;
   if ((e = record(ev, 0, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_dec_scan<T, D>), dim3(BG, a.SC + a.SW), dim3(256), lds_scan, st, a);
+  hipLaunchKernelGGL((k_dec<T, O, D, RING>), dim3(a.B * a.G), dim3(64 * kDecWaves), lds, st, a);
   if ((e = record(ev, 1, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_dec_finish<T, O, D, FW>), dim3(BG), dim3(64 * FW), lds_fin, st, a);
-  if ((e = record(ev, 2, st)) != hipSuccess) return e;
   return hipGetLastError();
 }
 

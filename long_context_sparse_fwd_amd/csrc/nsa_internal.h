@@ -41,9 +41,7 @@ struct PrefillArgs {
 
 struct DecodeArgs {
   int B, Lmax, Nmax, Hq, G, Hg, D, n, w;
-  int SC;  // compressed splits per (b, g), each kDecSplitKeys blocks
-  int SW;  // window splits per (b, g), each kDecSplitKeys tokens
-  int NmaxPad;
+  int NmaxPad;  // row length of the logits workspace: ceil(Lmax / 64) rounded up to 64
   float scale_log2;
   int inject;
   const void* q;
@@ -55,17 +53,14 @@ struct DecodeArgs {
   const void* gates;
   void* out;
   int32_t* idx;
-  float* part;    // partial softmax states, [B*G][SC+SW] x (m[16], l[16], O[16][D])
   float* logits;  // compressed logits (log2 domain), [B*G][16][NmaxPad]
   int64_t qs[2], ks[3], vs[3], kcs[3], vcs[3], gs[2], os[2];
 };
 
-constexpr int kDecSplitKeys = 256;  // keys (or blocks) per decode workgroup: 4 waves x 64
-
 // ev (nullable): kPrefillStages+1 / kDecodeStages+1 events recorded on st
 // before each kernel and after the last one.
 constexpr int kPrefillStages = 3;
-constexpr int kDecodeStages = 2;
+constexpr int kDecodeStages = 1;
 hipError_t launch_prefill(const PrefillArgs& a, bool in_bf16, bool out_bf16, hipStream_t st,
                           hipEvent_t* ev);
 hipError_t launch_decode(const DecodeArgs& a, bool in_bf16, bool out_bf16, hipStream_t st,
@@ -74,8 +69,7 @@ hipError_t launch_compress(int B, int G, int Nc, int D, bool bf16, const void* k
                            const void* v, const int64_t* vs, void* kc, const int64_t* kcs,
                            void* vc, const int64_t* vcs, hipStream_t st);
 
-size_t dec_finish_lds_bytes(int NmaxPad, int D, bool bf16);
-size_t dec_scan_lds_bytes(int D, bool bf16);
+size_t dec_lds_bytes(int NmaxPad, int D, bool bf16);
 
 size_t cmpwin_lds_bytes(int waves, int NcT, int D, bool bf16);
 

@@ -145,50 +145,6 @@ __global__ __launch_bounds__(256) void k_prep(PrefillArgs a) {
 
 // ------------------------------------------------------------------ shared pieces
 
-// One 32-key step of an online-softmax attention for one 16-column query
-// tile: st holds the raw S^T of keys [kbase, kbase+32) in C layout; with MASK,
-// keys outside [klo, khi] are excluded. Updates (m, l, acc); m is raised
-// lazily (kLazyMax), the final output is acc / l whatever m is.
-template <class T, int DT, bool MASK>
-__device__ __forceinline__ void online_step(f32x4 (&st)[2], int kbase, int klo, int khi, int grp,
-                                            float sl2, float& m, float& l, f32x4 (&acc)[DT],
-                                            const Frag<T> (&vf)[DT]) {
-  float lmx = kNegBig;
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = st[h2][i] * sl2;
-      if (MASK) {
-        const int key = kbase + 16 * h2 + 4 * grp + i;
-        x = (key >= klo && key <= khi) ? x : -INFINITY;
-      }
-      st[h2][i] = x;
-      lmx = fmaxf(lmx, x);
-    }
-  if (wave_any(lmx > m + kLazyMax)) {
-    const float mn = fmaxf(m, col_max4(lmx));
-    const float alpha = fast_exp2(m - mn);
-    l *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-    m = mn;
-  }
-  float sum = 0.f;
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = fast_exp2(st[h2][i] - m);
-      st[h2][i] = p;
-      sum += p;
-    }
-  l += sum;
-  const Frag<T> pf = pack_p<T>(st[0], st[1]);
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) mma(acc[dt], vf[dt], pf);
-}
-
 // Cooperative copy of one or two 64 x D tiles (fragment-major, contiguous)
 // from global memory into LDS through registers: issue() starts the loads of
 // the next tiles, commit() stores them once the current tiles are consumed.

@@ -150,11 +150,9 @@ def test_decode_workspace_and_validation(L):
     n = ctypes.c_size_t()
     d = ddesc()
     assert L.nsa_decode_workspace_bytes(ctypes.byref(d), ctypes.byref(p), ctypes.byref(n)) == OK
-    # one merged partial state per split: 4 compressed + 2 window splits
-    nslots = 4 + 2
-    part = 64 * 4 * nslots * (32 + 16 * 128) * 4
+    # compressed logits of every (sequence, group, head) plus the selection
     logits = 64 * 4 * 16 * 1024 * 4
-    assert n.value == part + logits + 64 * 4 * 16 * 4
+    assert n.value == logits + 64 * 4 * 16 * 4
     bad = ddesc(nmax=1000)                       # block cache shorter than Lmax/64
     assert L.nsa_decode_workspace_bytes(ctypes.byref(bad), ctypes.byref(p), ctypes.byref(n)) == INV
     bad = ddesc()
