@@ -161,6 +161,7 @@ nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, Pr
 
 struct DecodePlan {
   int NmaxPad;
+  bool logits_lds;
   size_t off_logits, off_idx, total;
 };
 
@@ -187,13 +188,15 @@ nsa_status_t plan_decode(const nsa_decode_desc_t* d, const nsa_params_t* p, Deco
   pl->NmaxPad = (nv + 63) / 64 * 64;
   if (B * G > INT32_MAX / 16)
     return fail(NSA_ERR_UNSUPPORTED, "batch * n_kv_heads too large");
-  if (nsa::dec_lds_bytes(pl->NmaxPad, static_cast<int>(D), d->in_dtype == NSA_BF16) >
-      static_cast<size_t>(nsa::kMaxLds))
+  const bool bf16 = d->in_dtype == NSA_BF16;
+  if (nsa::dec_lds_bytes(pl->NmaxPad, static_cast<int>(D), bf16, false) > static_cast<size_t>(nsa::kMaxLds))
     return fail(NSA_ERR_UNSUPPORTED, "max_seqlen %d needs more LDS for block scores than a CU has",
                 d->max_seqlen);
+  pl->logits_lds =
+      nsa::dec_lds_bytes(pl->NmaxPad, static_cast<int>(D), bf16, true) <= static_cast<size_t>(nsa::kMaxLds);
   size_t off = 0;
   pl->off_logits = off;
-  off = align_up(off + static_cast<size_t>(B * G) * 16 * pl->NmaxPad * sizeof(float));
+  if (!pl->logits_lds) off = align_up(off + static_cast<size_t>(B * G) * 16 * pl->NmaxPad * sizeof(float));
   pl->off_idx = off;
   off = align_up(off + static_cast<size_t>(B * G) * p->select_top_k * sizeof(int32_t));
   pl->total = off;
@@ -387,6 +390,7 @@ static nsa_status_t decode_impl(const nsa_decode_desc_t* desc, const nsa_params_
   a.gates = gates;
   a.out = out;
   char* ws = static_cast<char*>(workspace);
+  a.logits_lds = pl.logits_lds ? 1 : 0;
   a.logits = reinterpret_cast<float*>(ws + pl.off_logits);
   a.idx = idx != nullptr ? idx : reinterpret_cast<int32_t*>(ws + pl.off_idx);
   for (int i = 0; i < 2; ++i) {

@@ -7,13 +7,13 @@
 // group -- so the waves stream it in 32-key half chunks, each wave keeping the
 // next one in flight (a register ring) while it computes the current:
 //   A  compressed half chunks (block means), dealt round-robin to the waves;
-//      the logits go to the workspace for the block scores;
-//   B  the waves' compressed states are merged through LDS into the
-//      log-sum-exp and gate_cmp * O_cmp (kept in registers until the end);
-//   C  block scores (probabilities summed over the group's heads); wave 0
-//      selects the own block + top-(n-1) earlier blocks (nsa_topk.h) and
-//      lists their usable half blocks while the other waves stream the
-//      sliding window, whose states are then merged into gate_win * O_win;
+//      the logits are kept (in LDS when they fit) for the block scores;
+//   B  the waves' states are merged through LDS into the log-sum-exp and
+//      gate_cmp * O_cmp;
+//   C  block scores (probabilities summed over the group's heads); then
+//      wave 0 selects the own block + top-(n-1) earlier blocks (nsa_topk.h)
+//      and lists their usable half blocks while the other waves stream the
+//      sliding window, merged into gate_win * O_win;
 //   D  the selected half blocks, dealt round-robin to all waves, merged into
 //      gate_slc * O_slc;
 //   E  the sum of the three gated branches is written to out.
@@ -53,7 +53,8 @@ template <int D>
 __device__ __forceinline__ int v_col(int lane) { return (lane % (D / 8)) * 8; }
 
 // A half chunk: keys [key0, key0 + 32) of rows kr / vr, of which those in
-// [klo, khi] count (klo <= khi); lrow (or nullptr) receives this lane's logits.
+// [klo, khi] count (klo <= khi); lrow (or nullptr) receives this lane's
+// logits.
 template <class T>
 struct DItem {
   const typename T::storage* kr;
@@ -149,14 +150,17 @@ struct VStage<F32, D> {
 };
 
 // Online-softmax update of (m, l, acc) with one loaded half chunk; lv is this
-// wave's VStage<T, D>::kBytes of LDS.
+// wave's VStage<T, D>::kBytes of LDS, qlds the query fragments (s, lane).
 template <class T, int D>
 __device__ __forceinline__ void dhalf_attend(const DHalf<T, D>& c, const DItem<T>& it,
-                                             const Frag<T> (&qf)[D / 32], float sl2, void* lv,
+                                             const Frag<T>* qlds, float sl2, void* lv,
                                              float& m, float& l, f32x4 (&acc)[D / 16], int lane) {
   constexpr int KS = D / 32, DT = D / 16;
   const int grp = lane >> 4;
   VStage<T, D>::put(lv, c, lane);
+  Frag<T> qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qf[s] = qlds[s * 64 + lane];
   f32x4 st[2];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
@@ -188,30 +192,37 @@ __device__ __forceinline__ void dhalf_attend(const DHalf<T, D>& c, const DItem<T
   wave_lds_sync();
 }
 
-// Streams `count` half chunks desc(0..count-1) through a ring of RING
-// register buffers (RING - 1 loads in flight while one is computed).
-// count must be wave-uniform.
-template <class T, int D, int RING, class Desc, class Body>
-__device__ __forceinline__ void dstream(int count, Desc desc, Body body, int lane) {
+// A wave's stream of `count` half chunks desc(0..count-1) through a ring of
+// RING register buffers: prime() issues the first RING loads, run() computes
+// them in order, refilling each buffer as soon as it is consumed. Work done
+// between the two overlaps the first loads. count must be wave-uniform.
+template <class T, int D, int RING>
+struct DStream {
   DHalf<T, D> ring[RING];
+  template <class Desc>
+  __device__ __forceinline__ void prime(int count, Desc desc, int lane) {
 #pragma unroll
-  for (int r = 0; r < RING; ++r)
-    if (r < count) dhalf_load<T, D>(ring[r], desc(r), lane);
+    for (int r = 0; r < RING; ++r)
+      if (r < count) dhalf_load<T, D>(ring[r], desc(r), lane);
+  }
+  template <class Desc, class Body>
+  __device__ __forceinline__ void run(int count, Desc desc, Body body, int lane) {
 #pragma unroll 1
-  for (int base = 0; base < count; base += RING) {
+    for (int base = 0; base < count; base += RING) {
 #pragma unroll
-    for (int r = 0; r < RING; ++r) {
-      const int k = base + r;
-      if (k < count) {
-        body(ring[r], desc(k));
-        // keep the refill after the body: hoisted above it, the new loads
-        // would need a third set of registers
-        __builtin_amdgcn_sched_barrier(0);
-        if (k + RING < count) dhalf_load<T, D>(ring[r], desc(k + RING), lane);
+      for (int r = 0; r < RING; ++r) {
+        const int k = base + r;
+        if (k < count) {
+          body(ring[r], desc(k));
+          // keep the refill after the body: hoisted above it, the new loads
+          // would need a third set of registers
+          __builtin_amdgcn_sched_barrier(0);
+          if (k + RING < count) dhalf_load<T, D>(ring[r], desc(k + RING), lane);
+        }
       }
     }
   }
-}
+};
 
 // Stores a wave's partial state (m per column, l summed over the column's
 // lanes, O^T accumulators) as m[16], l[16], O[16][D] at dst.
@@ -253,33 +264,51 @@ __device__ __forceinline__ void reset_state(float& m, float& l, f32x4 (&acc)[D /
   for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// Workgroup barrier that orders LDS accesses only: outstanding global loads
+// (a stream's first loads) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Block scores sc[j], j < own: the compressed-branch probabilities of block
+// j summed over the group's Hg heads, from the logits lg[h][j] (row stride
+// ld) and each head's log-sum-exp hs[4 h + 2].
+template <class P>
+__device__ __forceinline__ void block_scores(P lg, int ld, int own, int Hg, const float* hs, float* sc,
+                                             int tid, int nt) {
+  for (int j = tid; j < own; j += nt) {
+    float s = 0.f;
+#pragma unroll
+    for (int h = 0; h < 16; ++h)
+      if (h < Hg) s += fast_exp2(lg[h * ld + j] - hs[4 * h + 2]);
+    sc[j] = s;
+  }
+}
+
 // Merges the per-wave states (m, l, acc) of one branch through LDS and adds
-// gate * O of the branch to res (this thread's EPT output elements
-// tid + NT r); gates[goff + h * gstride] is head h's gate. Begins and ends
-// with a workgroup barrier, so parts may alias the V staging.
-template <class T, int D, int NWV>
+// gate[h] * O of the branch to res[16][D] (LDS). Begins and ends with a
+// workgroup barrier, so parts may alias the V staging.
+template <int D, int NWV>
 __device__ __forceinline__ void merge_into(float* parts, float m, float l, const f32x4 (&acc)[D / 16],
-                                           const typename T::storage* gates, int64_t goff,
-                                           int64_t gstride, int Hg, float* hs,
-                                           float (&res)[16 * D / (64 * NWV)], int tid, int lane) {
-  constexpr int SF = dec_slot_floats(D), NT = 64 * NWV, EPT = 16 * D / NT;
-  __syncthreads();
+                                           const float* gate, float* hs, float* res, int tid, int lane) {
+  constexpr int SF = dec_slot_floats(D), NT = 64 * NWV;
+  lds_barrier();
   store_partial<D>(parts + (tid >> 6) * SF, m, l, acc, lane);
-  __syncthreads();
+  lds_barrier();
   if (tid < 16) {
     float M, L;
     merge_stats(parts, NWV, SF, tid, M, L);
-    const float gt = tid < Hg ? to_f32<T>(gates[goff + tid * gstride]) : 0.f;
     hs[4 * tid] = M;
-    hs[4 * tid + 1] = L > 0.f ? gt / L : 0.f;
+    hs[4 * tid + 1] = L > 0.f ? gate[tid] / L : 0.f;
   }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < EPT; ++r) {
-    const int e = tid + NT * r, h = e / D;
-    res[r] += merge_out<NWV>(parts, SF, h, e, hs[4 * h]) * hs[4 * h + 1];
+  lds_barrier();
+  for (int e = tid; e < 16 * D; e += NT) {
+    const int h = e / D;
+    res[e] += merge_out<NWV>(parts, SF, h, e, hs[4 * h]) * hs[4 * h + 1];
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 constexpr int kDecWaves = 8;
@@ -296,22 +325,24 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   using S = typename T::storage;
   using SO = typename O::storage;
   constexpr int NWV = kDecWaves, NT = 64 * NWV, SF = dec_slot_floats(D), DT = D / 16;
-  constexpr int EPT = 16 * D / NT;
   extern __shared__ __align__(16) unsigned char smem[];
   float* parts = reinterpret_cast<float*>(smem);  // aliases the V staging
-  float* sc = reinterpret_cast<float*>(smem + dec_big_bytes<T, D>());
+  Frag<T>* qlds = reinterpret_cast<Frag<T>*>(smem + dec_big_bytes<T, D>());  // [D/32][64]
+  float* res = reinterpret_cast<float*>(qlds + D / 32 * 64);                  // [16][D] output
+  float* sc = res + 16 * D;
   uint64_t* surv = reinterpret_cast<uint64_t*>(sc + a.NmaxPad);
   int* selb = reinterpret_cast<int*>(surv + kSurvCap);
   int* selo = selb + 64;
-  int* hl = selo + 64;              // usable selected half blocks: 2 j + half
-  int* nhl = hl + 128;              // their count
+  int* hl = selo + 64;                            // usable selected half blocks: 2 j + half
+  int* nhl = hl + 128;                            // their count
   float* hs = reinterpret_cast<float*>(nhl + 4);  // per head: 4 floats
+  float* gts = hs + 64;                           // [3][16] gates
+  float* lg_lds = gts + 48;                       // [16][NmaxPad] logits, if a.logits_lds
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15;
   const int bg = blockIdx.x, b = bg / a.G, g = bg % a.G;
   const int s_raw = a.seqlens[b];
   int32_t* idxo = a.idx + static_cast<int64_t>(bg) * a.n;
-  const S* GT = static_cast<const S*>(a.gates) + b * a.gs[0];
   SO* OUT = static_cast<SO*>(a.out) + b * a.os[0];
   if (s_raw < 1 || s_raw > a.Lmax) {  // invalid length: nothing of this sequence is read
     for (int e = tid; e < a.Hg * D; e += NT) OUT[(g * a.Hg + e / D) * a.os[1] + e % D] = from_f32<O>(0.f);
@@ -323,70 +354,75 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   const float sl2 = a.scale_log2;
   void* lv = smem + wave * VStage<T, D>::kBytes;
 
-  Frag<T> qf[D / 32];
-  {
+  // query fragments (lane l: head l % 16) and gates of the group's heads
+  if (wave == 0) {
     const S* Q = static_cast<const S*>(a.q) + b * a.qs[0] + (g * a.Hg + col) * a.qs[1] + 8 * (lane >> 4);
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) qf[s] = col < a.Hg ? frag_load<T>(Q + 32 * s) : frag_zero<T>();
+    for (int s = 0; s < D / 32; ++s) qlds[s * 64 + lane] = col < a.Hg ? frag_load<T>(Q + 32 * s) : frag_zero<T>();
+    if (lane < 48) {
+      const int h = lane & 15, i = lane >> 4;
+      gts[16 * i + h] =
+          h < a.Hg ? to_f32<T>(static_cast<const S*>(a.gates)[b * a.gs[0] + (g * a.Hg + h) * a.gs[1] + i]) : 0.f;
+    }
   }
+  __syncthreads();
   const S* KCr = static_cast<const S*>(a.kccache) + b * a.kcs[0] + g * a.kcs[1];
   const S* VCr = static_cast<const S*>(a.vccache) + b * a.vcs[0] + g * a.vcs[1];
   const S* Kr = static_cast<const S*>(a.kcache) + b * a.ks[0] + g * a.ks[1];
   const S* Vr = static_cast<const S*>(a.vcache) + b * a.vs[0] + g * a.vs[1];
-  float* lbase = a.inject ? nullptr : a.logits + (static_cast<int64_t>(bg) * 16 + col) * a.NmaxPad;
+  // compressed logits, row h = head: in LDS when they fit, else in the workspace
+  float* lg = a.logits_lds ? lg_lds : a.logits + static_cast<int64_t>(bg) * 16 * a.NmaxPad;
 
   float m, l;
   f32x4 acc[DT];
   auto attend = [&](const DHalf<T, D>& c, const DItem<T>& it) {
-    dhalf_attend<T, D>(c, it, qf, sl2, lv, m, l, acc, lane);
+    dhalf_attend<T, D>(c, it, qlds, sl2, lv, m, l, acc, lane);
   };
 
   // ---- A: compressed half chunks
   {
-    const int ncmp = (nvis + 31) >> 5;
-    reset_state<D>(m, l, acc);
-    dstream<T, D, RING>((ncmp - wave + NWV - 1) / NWV, [&](int k) {
+    const int ncmp = (nvis + 31) >> 5, cnt = (ncmp - wave + NWV - 1) / NWV;
+    float* lrow = a.inject ? nullptr : lg + col * a.NmaxPad;
+    auto desc = [&](int k) {
       const int q = wave + NWV * k;
       return DItem<T>{KCr, VCr, a.kcs[2], a.vcs[2], 32 * q, 0, nvis - 1,
-                      lbase != nullptr ? lbase + 32 * q : nullptr};
-    }, attend, lane);
+                      lrow != nullptr ? lrow + 32 * q : nullptr};
+    };
+    DStream<T, D, RING> ds;
+    ds.prime(cnt, desc, lane);
+    reset_state<D>(m, l, acc);
+    ds.run(cnt, desc, attend, lane);
     l = col_sum4(l);
   }
 
   // ---- B: merge into the log-sum-exp and gate_cmp * O_cmp
-  __syncthreads();
+  __syncthreads();  // staging done; logits written (global memory when not in LDS)
   store_partial<D>(parts + wave * SF, m, l, acc, lane);
-  __syncthreads();
+  lds_barrier();
   if (tid < 16) {
     float M, L;
     merge_stats(parts, NWV, SF, tid, M, L);
     hs[4 * tid] = M;
-    hs[4 * tid + 1] = L;
+    hs[4 * tid + 1] = L > 0.f ? gts[tid] / L : 0.f;
     hs[4 * tid + 2] = (nvis > 0 && tid < a.Hg) ? M + fast_log2(L) : INFINITY;
-    hs[4 * tid + 3] = tid < a.Hg ? to_f32<T>(GT[(g * a.Hg + tid) * a.gs[1]]) : 0.f;
   }
-  __syncthreads();
-  float res[EPT];
-#pragma unroll
-  for (int r = 0; r < EPT; ++r) {
-    const int e = tid + NT * r, h = e / D;
-    res[r] = nvis > 0 ? merge_out<NWV>(parts, SF, h, e, hs[4 * h]) / hs[4 * h + 1] * hs[4 * h + 3] : 0.f;
+  lds_barrier();
+  for (int e = tid; e < 16 * D; e += NT) {
+    const int h = e / D;
+    res[e] = merge_out<NWV>(parts, SF, h, e, hs[4 * h]) * hs[4 * h + 1];
   }
 
-  // ---- C: block scores (the logits were written by this workgroup)
+  // ---- C: block scores
   if (!a.inject) {
-    for (int j = tid; j < own; j += NT) {
-      const float* lg = a.logits + static_cast<int64_t>(bg) * 16 * a.NmaxPad + j;
-      float s = 0.f;
-#pragma unroll
-      for (int h = 0; h < 16; ++h)
-        if (h < a.Hg) s += fast_exp2(lg[h * a.NmaxPad] - hs[4 * h + 2]);
-      sc[j] = s;
-    }
+    if (a.logits_lds)
+      block_scores(lg_lds, a.NmaxPad, own, a.Hg, hs, sc, tid, NT);
+    else
+      block_scores(lg, a.NmaxPad, own, a.Hg, hs, sc, tid, NT);
   }
-  __syncthreads();  // parts read, sc written: the staging area is free again
+  lds_barrier();  // sc written; parts read, so the V staging is free again
 
-  // ---- C': wave 0 selects, the other waves stream the window
+  // ---- C': wave 0 selects and lists the usable half blocks while the other
+  //      waves stream the sliding window (all waves when the selection is given)
   if (wave == 0) {
     if (!a.inject) {
       topk_wave(sc, own, a.n, selo, surv, selb, lane);
@@ -408,42 +444,45 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   }
   {
     const int w0 = a.inject ? 0 : 1, nww = NWV - w0;
-    const int nwin = (t - wlo + 32) >> 5;
+    const int wnum = ((t - wlo + 32) >> 5) - (wave - w0) + nww - 1;
+    const int cnt = wave >= w0 && wnum > 0 ? wnum / nww : 0;
+    auto desc = [&](int k) {
+      return DItem<T>{Kr, Vr, a.ks[2], a.vs[2], wlo + 32 * ((wave - w0) + nww * k), wlo, t, nullptr};
+    };
+    DStream<T, D, RING> ds;
+    ds.prime(cnt, desc, lane);
     reset_state<D>(m, l, acc);
-    if (wave >= w0)
-      dstream<T, D, RING>((nwin - (wave - w0) + nww - 1) / nww, [&](int k) {
-        return DItem<T>{Kr, Vr, a.ks[2], a.vs[2], wlo + 32 * ((wave - w0) + nww * k), wlo, t, nullptr};
-      }, attend, lane);
+    ds.run(cnt, desc, attend, lane);
     l = col_sum4(l);
   }
-  // merge the window now, so that its state does not stay in registers
-  merge_into<T, D, NWV>(parts, m, l, acc, GT, (g * a.Hg) * a.gs[1] + 2, a.gs[1], a.Hg, hs, res, tid, lane);
+  merge_into<D, NWV>(parts, m, l, acc, gts + 32, hs, res, tid, lane);
 
   // ---- D: selected half blocks
   {
-    const int nh = *nhl;
-    reset_state<D>(m, l, acc);
-    dstream<T, D, RING>((nh - wave + NWV - 1) / NWV, [&](int k) {
+    const int nh = *nhl, cnt = (nh - wave + NWV - 1) / NWV;
+    auto desc = [&](int k) {
       const int u = hl[wave + NWV * k], j = u >> 1;
       return DItem<T>{Kr, Vr, a.ks[2], a.vs[2], 64 * j + 32 * (u & 1), 64 * j, t, nullptr};
-    }, attend, lane);
+    };
+    DStream<T, D, RING> ds;
+    ds.prime(cnt, desc, lane);
+    reset_state<D>(m, l, acc);
+    ds.run(cnt, desc, attend, lane);
     l = col_sum4(l);
   }
-  merge_into<T, D, NWV>(parts, m, l, acc, GT, (g * a.Hg) * a.gs[1] + 1, a.gs[1], a.Hg, hs, res, tid, lane);
+  merge_into<D, NWV>(parts, m, l, acc, gts + 16, hs, res, tid, lane);
 
   // ---- E: out = gate_cmp O_cmp + gate_slc O_slc + gate_win O_win
-#pragma unroll
-  for (int r = 0; r < EPT; ++r) {
-    const int e = tid + NT * r, h = e / D;
-    if (h < a.Hg) OUT[(g * a.Hg + h) * a.os[1] + e % D] = from_f32<O>(res[r]);
-  }
+  for (int e = tid; e < a.Hg * D; e += NT) OUT[(g * a.Hg + e / D) * a.os[1] + e % D] = from_f32<O>(res[e]);
 }
 
-size_t dec_lds_bytes(int NmaxPad, int D, bool bf16) {
+size_t dec_lds_bytes(int NmaxPad, int D, bool bf16, bool logits_lds) {
   const size_t big = bf16 ? (D == 64 ? dec_big_bytes<BF16, 64>() : dec_big_bytes<BF16, 128>())
                           : (D == 64 ? dec_big_bytes<F32, 64>() : dec_big_bytes<F32, 128>());
-  return big + NmaxPad * sizeof(float) + kSurvCap * sizeof(uint64_t) +
-         (64 + 64 + 128 + 4) * sizeof(int) + 64 * sizeof(float);
+  const size_t qbytes = (bf16 ? 16 : 32) * static_cast<size_t>(D / 32) * 64;
+  return big + qbytes + 16 * static_cast<size_t>(D) * sizeof(float) + NmaxPad * sizeof(float) +
+         kSurvCap * sizeof(uint64_t) + (64 + 64 + 128 + 4) * sizeof(int) + (64 + 48) * sizeof(float) +
+         (logits_lds ? 16 * static_cast<size_t>(NmaxPad) * sizeof(float) : 0);
 }
 
 static hipError_t record(hipEvent_t* ev, int i, hipStream_t st) {
@@ -454,7 +493,7 @@ template <class T, class O, int D>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st, hipEvent_t* ev) {
   constexpr bool kBf16 = sizeof(typename T::storage) == 2;
   constexpr int RING = kBf16 ? 2 : 1;
-  const size_t lds = dec_lds_bytes(a.NmaxPad, D, kBf16);
+  const size_t lds = dec_lds_bytes(a.NmaxPad, D, kBf16, a.logits_lds != 0);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec<T, O, D, RING>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;

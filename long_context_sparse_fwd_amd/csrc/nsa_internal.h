@@ -53,7 +53,8 @@ struct DecodeArgs {
   const void* gates;
   void* out;
   int32_t* idx;
-  float* logits;  // compressed logits (log2 domain), [B*G][16][NmaxPad]
+  int logits_lds;  // 1: the compressed logits stay in LDS; 0: in `logits`
+  float* logits;   // compressed logits (log2 domain), [B*G][16][NmaxPad], if !logits_lds
   int64_t qs[2], ks[3], vs[3], kcs[3], vcs[3], gs[2], os[2];
 };
 
@@ -69,7 +70,8 @@ hipError_t launch_compress(int B, int G, int Nc, int D, bool bf16, const void* k
                            const void* v, const int64_t* vs, void* kc, const int64_t* kcs,
                            void* vc, const int64_t* vcs, hipStream_t st);
 
-size_t dec_lds_bytes(int NmaxPad, int D, bool bf16);
+// LDS bytes of the decode kernel, with or without room for the logits.
+size_t dec_lds_bytes(int NmaxPad, int D, bool bf16, bool logits_lds);
 
 size_t cmpwin_lds_bytes(int waves, int NcT, int D, bool bf16);
 

@@ -150,9 +150,13 @@ def test_decode_workspace_and_validation(L):
     n = ctypes.c_size_t()
     d = ddesc()
     assert L.nsa_decode_workspace_bytes(ctypes.byref(d), ctypes.byref(p), ctypes.byref(n)) == OK
-    # compressed logits of every (sequence, group, head) plus the selection
-    logits = 64 * 4 * 16 * 1024 * 4
-    assert n.value == logits + 64 * 4 * 16 * 4
+    # the compressed logits of 1024 blocks fit in LDS: only the selection
+    assert n.value == 64 * 4 * 16 * 4
+    f32 = ddesc()
+    f32.in_dtype = f32.out_dtype = nsa.NSA_F32
+    assert L.nsa_decode_workspace_bytes(ctypes.byref(f32), ctypes.byref(p), ctypes.byref(n)) == OK
+    # fp32 staging leaves no room for them: the logits go to the workspace
+    assert n.value == 64 * 4 * 16 * 1024 * 4 + 64 * 4 * 16 * 4
     bad = ddesc(nmax=1000)                       # block cache shorter than Lmax/64
     assert L.nsa_decode_workspace_bytes(ctypes.byref(bad), ctypes.byref(p), ctypes.byref(n)) == INV
     bad = ddesc()
