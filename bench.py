@@ -275,7 +275,7 @@ def bench_decode(cfg, steps, warmup, torch, inputs, nsa):
     return {"workload": cfg.name, "ms_per_step": ms, "step_ms_samples": step_ms,
             "sequences_per_s": cfg.batch / (ms * 1e-3), "unique_bytes_per_step": ubytes,
             "achieved_GBps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS, "kernels_ms": stage_ms,
-            "cache_flush": "1 GiB read between steps"}
+            "traffic": committed_traffic("k_dec", cfg.name), "cache_flush": "1 GiB read between steps"}
 
 
 def main():
@@ -288,6 +288,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run 3 plain fp32 copies of MIB MiB (a known HBM read + write "
+                         "volume for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -303,6 +306,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     nsa.lib()
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 18  # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 x (read {n * 4} B, write {n * 4} B)")
+        del src, dst
     cfg = inputs.CONFIGS[args.config]
     raw, wall_ms, stage_ms = bench_prefill(cfg, args.steps, args.warmup, torch, inputs, nsa)
     fl = prefill_flops(cfg)
