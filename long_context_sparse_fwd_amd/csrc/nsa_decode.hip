@@ -149,24 +149,24 @@ struct VStage<F32, D> {
   }
 };
 
-// Online-softmax update of (m, l, acc) with one loaded half chunk; lv is this
-// wave's VStage<T, D>::kBytes of LDS, qlds the query fragments (s, lane).
+// First half of a step: writes the loaded V rows to this wave's LDS staging
+// lv, computes S^T = K Q^T (query fragments qlds[s][lane]) into st and, if
+// it.lrow is set, stores this lane's logits. The register buffer c is free
+// afterwards.
 template <class T, int D>
-__device__ __forceinline__ void dhalf_attend(const DHalf<T, D>& c, const DItem<T>& it,
+__device__ __forceinline__ void dhalf_scores(const DHalf<T, D>& c, const DItem<T>& it,
                                              const Frag<T>* qlds, float sl2, void* lv,
-                                             float& m, float& l, f32x4 (&acc)[D / 16], int lane) {
-  constexpr int KS = D / 32, DT = D / 16;
+                                             f32x4 (&st)[2], int lane) {
+  constexpr int KS = D / 32;
   const int grp = lane >> 4;
   VStage<T, D>::put(lv, c, lane);
-  Frag<T> qf[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) qf[s] = qlds[s * 64 + lane];
-  f32x4 st[2];
+  for (int kt = 0; kt < 2; ++kt) st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < KS; ++s) {
+    const Frag<T> qf = qlds[s * 64 + lane];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) mma(st[kt], c.k[kt][s], qf[s]);
+    for (int kt = 0; kt < 2; ++kt) mma(st[kt], c.k[kt][s], qf);
   }
   if (it.lrow != nullptr) {
 #pragma unroll
@@ -180,45 +180,78 @@ __device__ __forceinline__ void dhalf_attend(const DHalf<T, D>& c, const DItem<T
       *reinterpret_cast<f32x4*>(it.lrow + 16 * kt + 4 * grp) = x;
     }
   }
+}
+
+// Second half: online-softmax update of (m, l, acc) from st, with the V^T
+// fragments read back from the staging one at a time.
+template <class T, int D>
+__device__ __forceinline__ void dhalf_update(f32x4 (&st)[2], const DItem<T>& it, float sl2, void* lv,
+                                             float& m, float& l, f32x4 (&acc)[D / 16], int lane) {
+  constexpr int DT = D / 16;
+  const int grp = lane >> 4;
   wave_lds_sync();
-  Frag<T> vf[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) vf[dt] = VStage<T, D>::get(lv, dt, lane);
   const bool full = it.key0 >= it.klo && it.key0 + 31 <= it.khi;
-  if (full)
-    online_step<T, DT, false>(st, it.key0, 0, 0, grp, sl2, m, l, acc, vf);
-  else
-    online_step<T, DT, true>(st, it.key0, it.klo, it.khi, grp, sl2, m, l, acc, vf);
+  const Frag<T> pf = full ? online_probs<T, DT, false>(st, it.key0, 0, 0, grp, sl2, m, l, acc)
+                          : online_probs<T, DT, true>(st, it.key0, it.klo, it.khi, grp, sl2, m, l, acc);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) mma(acc[dt], VStage<T, D>::get(lv, dt, lane), pf);
   wave_lds_sync();
 }
 
-// A wave's stream of `count` half chunks desc(0..count-1) through a ring of
-// RING register buffers: prime() issues the first RING loads, run() computes
-// them in order, refilling each buffer as soon as it is consumed. Work done
-// between the two overlaps the first loads. count must be wave-uniform.
+// A wave's share of a phase's `total` half chunks desc(0..total-1) -- items
+// first, first + stride, ... -- streamed through a ring of RING register
+// buffers: prime() fills the ring; run() computes the buffers in order,
+// refilling each as soon as it is consumed. Work done between the two
+// overlaps the first loads. (A shared work counter balancing the waves was
+// measured slower: the phases are bound by the memory system, not by the
+// slowest wave.)
 template <class T, int D, int RING>
 struct DStream {
   DHalf<T, D> ring[RING];
+  int q[RING];
+  int nxt, stride;
+  __device__ __forceinline__ DStream(int first, int step) : nxt(first), stride(step) {}
+  // Every buffer is (re)loaded unconditionally -- an index past the end
+  // reloads the last item, whose data is then never used -- so that the
+  // number of loads in flight is the same on every path through the loop
+  // and each use waits only for its own buffer. total must be >= 1.
   template <class Desc>
-  __device__ __forceinline__ void prime(int count, Desc desc, int lane) {
+  __device__ __forceinline__ void prime(int total, Desc desc, int lane) {
 #pragma unroll
-    for (int r = 0; r < RING; ++r)
-      if (r < count) dhalf_load<T, D>(ring[r], desc(r), lane);
+    for (int r = 0; r < RING; ++r) {
+      q[r] = nxt;
+      nxt += stride;
+      dhalf_load<T, D>(ring[r], desc(min(q[r], total - 1)), lane);
+      __builtin_amdgcn_sched_barrier(0);  // buffers in order
+    }
   }
-  template <class Desc, class Body>
-  __device__ __forceinline__ void run(int count, Desc desc, Body body, int lane) {
+  // scores(c, it, st) consumes buffer c into st; update(st, it) finishes
+  // the step. Each buffer is refilled between the two, so its next load is
+  // in flight during the softmax and the P.V product.
+  template <class Desc, class Scores, class Update>
+  __device__ __forceinline__ void run(int total, Desc desc, Scores scores, Update update, int lane) {
+    // The stream ends when buffer 0 is past the end; later buffers past the
+    // end are still stepped, as an empty key range that adds nothing: a loop
+    // whose only exit is at its top keeps the count of loads in flight the
+    // same on every path, which the compiler needs to wait for one buffer
+    // only.
 #pragma unroll 1
-    for (int base = 0; base < count; base += RING) {
+    while (q[0] < total) {
 #pragma unroll
       for (int r = 0; r < RING; ++r) {
-        const int k = base + r;
-        if (k < count) {
-          body(ring[r], desc(k));
-          // keep the refill after the body: hoisted above it, the new loads
-          // would need a third set of registers
-          __builtin_amdgcn_sched_barrier(0);
-          if (k + RING < count) dhalf_load<T, D>(ring[r], desc(k + RING), lane);
+        DItem<T> it = desc(min(q[r], total - 1));
+        if (q[r] >= total) {
+          it.klo = it.khi + 1;
+          it.lrow = nullptr;
         }
+        f32x4 st[2];
+        scores(ring[r], it, st);
+        __builtin_amdgcn_sched_barrier(0);
+        q[r] = nxt;
+        nxt += stride;
+        dhalf_load<T, D>(ring[r], desc(min(q[r], total - 1)), lane);
+        __builtin_amdgcn_sched_barrier(0);
+        update(st, it);
       }
     }
   }
@@ -320,7 +353,7 @@ __host__ __device__ constexpr size_t dec_big_bytes() {
   return stage > parts ? stage : parts;
 }
 
-template <class T, class O, int D, int RING>
+template <class T, class O, int D, int RING, bool LGL>
 __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_dec(DecodeArgs a) {
   using S = typename T::storage;
   using SO = typename O::storage;
@@ -337,7 +370,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   int* nhl = hl + 128;                            // their count
   float* hs = reinterpret_cast<float*>(nhl + 4);  // per head: 4 floats
   float* gts = hs + 64;                           // [3][16] gates
-  float* lg_lds = gts + 48;                       // [16][NmaxPad] logits, if a.logits_lds
+  float* lg_lds = gts + 48;                       // [16][NmaxPad] logits, if LGL
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15;
   const int bg = blockIdx.x, b = bg / a.G, g = bg % a.G;
@@ -371,27 +404,29 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   const S* Kr = static_cast<const S*>(a.kcache) + b * a.ks[0] + g * a.ks[1];
   const S* Vr = static_cast<const S*>(a.vcache) + b * a.vs[0] + g * a.vs[1];
   // compressed logits, row h = head: in LDS when they fit, else in the workspace
-  float* lg = a.logits_lds ? lg_lds : a.logits + static_cast<int64_t>(bg) * 16 * a.NmaxPad;
+  float* lg = LGL ? lg_lds : a.logits + static_cast<int64_t>(bg) * 16 * a.NmaxPad;
 
   float m, l;
   f32x4 acc[DT];
-  auto attend = [&](const DHalf<T, D>& c, const DItem<T>& it) {
-    dhalf_attend<T, D>(c, it, qlds, sl2, lv, m, l, acc, lane);
+  auto scores = [&](const DHalf<T, D>& c, const DItem<T>& it, f32x4 (&st)[2]) {
+    dhalf_scores<T, D>(c, it, qlds, sl2, lv, st, lane);
   };
+  auto update = [&](f32x4 (&st)[2], const DItem<T>& it) { dhalf_update<T, D>(st, it, sl2, lv, m, l, acc, lane); };
 
   // ---- A: compressed half chunks
   {
-    const int ncmp = (nvis + 31) >> 5, cnt = (ncmp - wave + NWV - 1) / NWV;
+    const int ncmp = (nvis + 31) >> 5;
     float* lrow = a.inject ? nullptr : lg + col * a.NmaxPad;
-    auto desc = [&](int k) {
-      const int q = wave + NWV * k;
+    auto desc = [&](int q) {
       return DItem<T>{KCr, VCr, a.kcs[2], a.vcs[2], 32 * q, 0, nvis - 1,
                       lrow != nullptr ? lrow + 32 * q : nullptr};
     };
-    DStream<T, D, RING> ds;
-    ds.prime(cnt, desc, lane);
     reset_state<D>(m, l, acc);
-    ds.run(cnt, desc, attend, lane);
+    if (ncmp > 0) {
+      DStream<T, D, RING> ds(wave, NWV);
+      ds.prime(ncmp, desc, lane);
+      ds.run(ncmp, desc, scores, update, lane);
+    }
     l = col_sum4(l);
   }
 
@@ -414,10 +449,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
 
   // ---- C: block scores
   if (!a.inject) {
-    if (a.logits_lds)
-      block_scores(lg_lds, a.NmaxPad, own, a.Hg, hs, sc, tid, NT);
-    else
-      block_scores(lg, a.NmaxPad, own, a.Hg, hs, sc, tid, NT);
+    block_scores(lg, a.NmaxPad, own, a.Hg, hs, sc, tid, NT);
   }
   lds_barrier();  // sc written; parts read, so the V staging is free again
 
@@ -443,31 +475,32 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     if (lane == 0) *nhl = __popcll(b0) + __popcll(b1);
   }
   {
-    const int w0 = a.inject ? 0 : 1, nww = NWV - w0;
-    const int wnum = ((t - wlo + 32) >> 5) - (wave - w0) + nww - 1;
-    const int cnt = wave >= w0 && wnum > 0 ? wnum / nww : 0;
-    auto desc = [&](int k) {
-      return DItem<T>{Kr, Vr, a.ks[2], a.vs[2], wlo + 32 * ((wave - w0) + nww * k), wlo, t, nullptr};
-    };
-    DStream<T, D, RING> ds;
-    ds.prime(cnt, desc, lane);
+    const int nwin = (t - wlo + 32) >> 5;
+    auto desc = [&](int q) { return DItem<T>{Kr, Vr, a.ks[2], a.vs[2], wlo + 32 * q, wlo, t, nullptr}; };
     reset_state<D>(m, l, acc);
-    ds.run(cnt, desc, attend, lane);
+    if (wave > 0 || a.inject) {
+      const int w0 = a.inject ? 0 : 1;
+      DStream<T, D, RING> ds(wave - w0, NWV - w0);
+      ds.prime(nwin, desc, lane);
+      ds.run(nwin, desc, scores, update, lane);
+    }
     l = col_sum4(l);
   }
   merge_into<D, NWV>(parts, m, l, acc, gts + 32, hs, res, tid, lane);
 
   // ---- D: selected half blocks
   {
-    const int nh = *nhl, cnt = (nh - wave + NWV - 1) / NWV;
-    auto desc = [&](int k) {
-      const int u = hl[wave + NWV * k], j = u >> 1;
+    const int nh = *nhl;
+    auto desc = [&](int q) {
+      const int u = hl[q], j = u >> 1;
       return DItem<T>{Kr, Vr, a.ks[2], a.vs[2], 64 * j + 32 * (u & 1), 64 * j, t, nullptr};
     };
-    DStream<T, D, RING> ds;
-    ds.prime(cnt, desc, lane);
     reset_state<D>(m, l, acc);
-    ds.run(cnt, desc, attend, lane);
+    if (nh > 0) {
+      DStream<T, D, RING> ds(wave, NWV);
+      ds.prime(nh, desc, lane);
+      ds.run(nh, desc, scores, update, lane);
+    }
     l = col_sum4(l);
   }
   merge_into<D, NWV>(parts, m, l, acc, gts + 16, hs, res, tid, lane);
@@ -489,30 +522,35 @@ static hipError_t record(hipEvent_t* ev, int i, hipStream_t st) {
   return ev != nullptr ? hipEventRecord(ev[i], st) : hipSuccess;
 }
 
-template <class T, class O, int D>
+template <class T, class O, int D, bool LGL>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st, hipEvent_t* ev) {
   constexpr bool kBf16 = sizeof(typename T::storage) == 2;
   constexpr int RING = kBf16 ? 2 : 1;
-  const size_t lds = dec_lds_bytes(a.NmaxPad, D, kBf16, a.logits_lds != 0);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec<T, O, D, RING>),
+  const size_t lds = dec_lds_bytes(a.NmaxPad, D, kBf16, LGL);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec<T, O, D, RING, LGL>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
   if ((e = record(ev, 0, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_dec<T, O, D, RING>), dim3(a.B * a.G), dim3(64 * kDecWaves), lds, st, a);
+  hipLaunchKernelGGL((k_dec<T, O, D, RING, LGL>), dim3(a.B * a.G), dim3(64 * kDecWaves), lds, st, a);
   if ((e = record(ev, 1, st)) != hipSuccess) return e;
   return hipGetLastError();
+}
+
+template <class T, class O, int D>
+static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t st, hipEvent_t* ev) {
+  return a.logits_lds ? launch_decode_t<T, O, D, true>(a, st, ev) : launch_decode_t<T, O, D, false>(a, st, ev);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool in_bf16, bool out_bf16, hipStream_t st,
                          hipEvent_t* ev) {
   if (in_bf16) {
     if (out_bf16)
-      return a.D == 64 ? launch_decode_t<BF16, BF16, 64>(a, st, ev)
-                       : launch_decode_t<BF16, BF16, 128>(a, st, ev);
-    return a.D == 64 ? launch_decode_t<BF16, F32, 64>(a, st, ev)
-                     : launch_decode_t<BF16, F32, 128>(a, st, ev);
+      return a.D == 64 ? launch_decode_d<BF16, BF16, 64>(a, st, ev)
+                       : launch_decode_d<BF16, BF16, 128>(a, st, ev);
+    return a.D == 64 ? launch_decode_d<BF16, F32, 64>(a, st, ev)
+                     : launch_decode_d<BF16, F32, 128>(a, st, ev);
   }
-  return a.D == 64 ? launch_decode_t<F32, F32, 64>(a, st, ev) : launch_decode_t<F32, F32, 128>(a, st, ev);
+  return a.D == 64 ? launch_decode_d<F32, F32, 64>(a, st, ev) : launch_decode_d<F32, F32, 128>(a, st, ev);
 }
 
 }  // namespace nsa

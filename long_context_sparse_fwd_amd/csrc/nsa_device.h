@@ -246,12 +246,12 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 // One 32-key step of an online-softmax attention for one 16-column query
 // tile: st holds the raw S^T of keys [kbase, kbase+32) in C layout; with MASK,
-// keys outside [klo, khi] are excluded. Updates (m, l, acc); m is raised
-// lazily (kLazyMax), the final output is acc / l whatever m is.
+// keys outside [klo, khi] are excluded. Updates m and l, rescales acc when m
+// moves, and returns the probabilities as the B operand of the P.V product.
+// m is raised lazily (kLazyMax); the final output is acc / l whatever m is.
 template <class T, int DT, bool MASK>
-__device__ __forceinline__ void online_step(f32x4 (&st)[2], int kbase, int klo, int khi, int grp,
-                                            float sl2, float& m, float& l, f32x4 (&acc)[DT],
-                                            const Frag<T> (&vf)[DT]) {
+__device__ __forceinline__ Frag<T> online_probs(f32x4 (&st)[2], int kbase, int klo, int khi, int grp,
+                                                float sl2, float& m, float& l, f32x4 (&acc)[DT]) {
   float lmx = kNegBig;
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
@@ -283,7 +283,15 @@ __device__ __forceinline__ void online_step(f32x4 (&st)[2], int kbase, int klo, 
       sum += p;
     }
   l += sum;
-  const Frag<T> pf = pack_p<T>(st[0], st[1]);
+  return pack_p<T>(st[0], st[1]);
+}
+
+// online_probs followed by acc += V^T . P^T with the V^T fragments vf.
+template <class T, int DT, bool MASK>
+__device__ __forceinline__ void online_step(f32x4 (&st)[2], int kbase, int klo, int khi, int grp,
+                                            float sl2, float& m, float& l, f32x4 (&acc)[DT],
+                                            const Frag<T> (&vf)[DT]) {
+  const Frag<T> pf = online_probs<T, DT, MASK>(st, kbase, klo, khi, grp, sl2, m, l, acc);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) mma(acc[dt], vf[dt], pf);
 }

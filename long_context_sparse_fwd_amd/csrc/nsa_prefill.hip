@@ -569,42 +569,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  HalfBlock<T, D> ring[NB];
-#pragma unroll
-  for (int k = 0; k < NB; ++k)
-    if (k < nsteps) {
-      const int code = steps[k];
-      half_load<T, D>(ring[k], KT, VT, code & 0x7FFFFF, (code >> 23) & 1, lane);
-    }
-#pragma unroll 1
-  for (int base = 0; base < nsteps; base += NB) {
+  // The ring is loaded unconditionally -- a step past the end reloads the
+  // last step's half block -- and the loop's only exit is at its top; a slot
+  // past the end is stepped as an empty key range. The count of loads in
+  // flight is then the same on every path, so each step waits only for its
+  // own slot's loads while the other slot's stay in flight.
+  if (nsteps > 0) {
+    HalfBlock<T, D> ring[NB];
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      const int s = base + k;
-      if (s >= nsteps) break;
-      const int code = steps[s];
-      const int qt = code >> 24, j = code & 0x7FFFFF, hh = (code >> 23) & 1;
-      const int t = t0 + qt;
-      const int kb = 64 * j + 32 * hh;
-      const bool full = kb + 31 <= t;
-      Frag<T> qf[KS];
+      const int code = steps[min(k, nsteps - 1)];
+      half_load<T, D>(ring[k], KT, VT, code & 0x7FFFFF, (code >> 23) & 1, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll 1
+    for (int base = 0; base < nsteps; base += NB) {
 #pragma unroll
-      for (int ss = 0; ss < KS; ++ss) {
-        u32x4* w = reinterpret_cast<u32x4*>(&qf[ss]);
+      for (int k = 0; k < NB; ++k) {
+        const int s = base + k;
+        const int code = steps[min(s, nsteps - 1)];
+        const int qt = code >> 24, j = code & 0x7FFFFF, hh = (code >> 23) & 1;
+        const int t = s < nsteps ? t0 + qt : -1;  // -1: every key masked
+        const int kb = 64 * j + 32 * hh;
+        const bool full = kb + 31 <= t;
+        Frag<T> qf[KS];
 #pragma unroll
-        for (int e = 0; e < FE; ++e) w[e] = q_lds[wave][qt][ss][e][lane];
-      }
+        for (int ss = 0; ss < KS; ++ss) {
+          u32x4* w = reinterpret_cast<u32x4*>(&qf[ss]);
 #pragma unroll
-      for (int q = 0; q < TPW; ++q)
-        if (q == qt) {
-          if (full)
-            half_attend<T, D, false>(ring[k], qf, kb, t, grp, sl2, m[q], l[q], acc[q]);
-          else
-            half_attend<T, D, true>(ring[k], qf, kb, t, grp, sl2, m[q], l[q], acc[q]);
+          for (int e = 0; e < FE; ++e) w[e] = q_lds[wave][qt][ss][e][lane];
         }
-      if (s + NB < nsteps) {
-        const int nc = steps[s + NB];
+#pragma unroll
+        for (int q = 0; q < TPW; ++q)
+          if (q == qt) {
+            if (full)
+              half_attend<T, D, false>(ring[k], qf, kb, t, grp, sl2, m[q], l[q], acc[q]);
+            else
+              half_attend<T, D, true>(ring[k], qf, kb, t, grp, sl2, m[q], l[q], acc[q]);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+        const int nc = steps[min(s + NB, nsteps - 1)];
         half_load<T, D>(ring[k], KT, VT, nc & 0x7FFFFF, (nc >> 23) & 1, lane);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
