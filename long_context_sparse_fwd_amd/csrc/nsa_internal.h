@@ -14,6 +14,7 @@ constexpr int kCmpTPW = 2;         // tokens per wave, window+compressed+selecti
 constexpr int kSelTPW = 2;         // tokens per wave, selected-branch kernel (4 waves)
 constexpr int kSelRing = 2;        // half-block register buffers per wave in that kernel
 constexpr int kMaxLds = 160 * 1024;
+constexpr size_t kSelLdsReserve = 82 * 1024;  // dynamic LDS of k_sel: one workgroup per CU
 constexpr float kLog2eHost = 1.4426950408889634f;
 
 // Everything a prefill launch needs; passed by value to every kernel.
