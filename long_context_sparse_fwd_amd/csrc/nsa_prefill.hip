@@ -326,19 +326,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int s = 0; s < KS; ++s) mma(st[qt][kt], kf[s], qf[qt][s]);
       }
     }
-    const bool full = 64 * c + 63 < nvis[0];  // every key of the chunk visible to every token
+    // every key of the chunk visible to every token (wave-uniform, so the
+    // masked variant below is a real branch, not per-lane selects)
+    const bool full = __builtin_amdgcn_readfirstlane(64 * c + 63 < nvis[0]);
 #pragma unroll
     for (int qt = 0; qt < TPW; ++qt) {
       float lmx = kNegBig;
+      if (full) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = st[qt][kt][i] * sl2;
-          if (!full) x = 64 * c + 16 * kt + 4 * grp + i < nvis[qt] ? x : -INFINITY;
-          st[qt][kt][i] = x;
-          lmx = fmaxf(lmx, x);
-        }
+          for (int i = 0; i < 4; ++i) {
+            st[qt][kt][i] *= sl2;
+            lmx = fmaxf(lmx, st[qt][kt][i]);
+          }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = 64 * c + 16 * kt + 4 * grp + i < nvis[qt] ? st[qt][kt][i] * sl2 : -INFINITY;
+            st[qt][kt][i] = x;
+            lmx = fmaxf(lmx, x);
+          }
+      }
       if (wave_any(lmx > m[qt] + kLazyMax)) {
         const float mn = fmaxf(m[qt], col_max4(lmx));
         ls[qt] *= fast_exp2(m[qt] - mn);
@@ -400,16 +411,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       Frag<T> vf[DT];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) vf[dt] = frag_load<T>(vc + vtile_frag(dt, s2, lane));
-      const bool full = 64 * c + 32 * s2 + 31 < nvis[0];
+      const bool full = __builtin_amdgcn_readfirstlane(64 * c + 32 * s2 + 31 < nvis[0]);
 #pragma unroll
       for (int qt = 0; qt < TPW; ++qt) {
+        if (full) {
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
+          for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = fast_exp2(st[qt][h2][i] * sl2 - lse2[qt]);
-            st[qt][h2][i] = (full || 64 * c + 32 * s2 + 16 * h2 + 4 * grp + i < nvis[qt]) ? p : 0.f;
-          }
+            for (int i = 0; i < 4; ++i) st[qt][h2][i] = fast_exp2(st[qt][h2][i] * sl2 - lse2[qt]);
+        } else {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float p = fast_exp2(st[qt][h2][i] * sl2 - lse2[qt]);
+              st[qt][h2][i] = 64 * c + 32 * s2 + 16 * h2 + 4 * grp + i < nvis[qt] ? p : 0.f;
+            }
+        }
         if (select) {
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
