@@ -134,6 +134,11 @@ nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, Pr
   if (pl->cmp_waves == 0)
     return fail(NSA_ERR_UNSUPPORTED, "seqlen %lld needs more LDS for block scores than a CU has",
                 static_cast<long long>(L));
+  if (nsa::sel_lds_bytes(pl->Nb, static_cast<int>(D), d->in_dtype == NSA_BF16) +
+          nsa::sel_static_lds_bytes(static_cast<int>(D), d->in_dtype == NSA_BF16) >
+      static_cast<size_t>(nsa::kMaxLds))
+    return fail(NSA_ERR_UNSUPPORTED, "seqlen %lld needs more LDS for the selection lists than a CU has",
+                static_cast<long long>(L));
   const int64_t tok_cmp = static_cast<int64_t>(pl->cmp_waves) * nsa::kCmpTPW;
   const int64_t tok_sel = 4 * static_cast<int64_t>(nsa::kSelTPW);
   pl->cmp_tiles = static_cast<int>((L + tok_cmp - 1) / tok_cmp);
@@ -292,6 +297,7 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
   a.cmp_waves = pl.cmp_waves;
   a.cmp_tiles = pl.cmp_tiles;
   a.sel_tiles = pl.sel_tiles;
+  a.sel_bm_words = nsa::sel_bm_words(pl.Nb);
   a.scale_log2 = scale_log2(params, a.D);
   a.inject = idx_mode == NSA_IDX_INJECT ? 1 : 0;
   a.q = q;

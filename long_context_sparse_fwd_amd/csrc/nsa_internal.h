@@ -11,10 +11,10 @@ namespace nsa {
 constexpr int kBlock = 64;         // compress / select block size supported
 constexpr int kSurvCap = 256;      // top-k survivor buffer per wave (entries)
 constexpr int kCmpTPW = 2;         // tokens per wave, window+compressed+selection kernel
-constexpr int kSelTPW = 2;         // tokens per wave, selected-branch kernel (4 waves)
+constexpr int kSelTPW = 4;         // tokens per wave, selected-branch kernel (4 waves)
 constexpr int kSelRing = 2;        // half-block register buffers per wave in that kernel
 constexpr int kMaxLds = 160 * 1024;
-constexpr size_t kSelLdsReserve = 82 * 1024;  // dynamic LDS of k_sel: one workgroup per CU
+constexpr size_t kSelLdsOneWg = 81 * 1024;  // k_sel LDS (static + dynamic) for one workgroup per CU
 constexpr float kLog2eHost = 1.4426950408889634f;
 
 // Everything a prefill launch needs; passed by value to every kernel.
@@ -24,6 +24,7 @@ struct PrefillArgs {
   int Nc;   // complete (compressed) blocks = L / 64
   int NcT;  // 64-row chunks of the compressed tiles = ceil(Nc / 64)
   int cmp_waves, cmp_tiles, sel_tiles;
+  int sel_bm_words;  // words of a k_sel wave's half-block bitmap (one byte per half block)
   float scale_log2;  // softmax scale * log2(e)
   int inject;        // 1: idx holds the selection; 0: compute it into idx
   const void* q;
@@ -75,6 +76,15 @@ hipError_t launch_compress(int B, int G, int Nc, int D, bool bf16, const void* k
 size_t dec_lds_bytes(int NmaxPad, int D, bool bf16, bool logits_lds);
 
 size_t cmpwin_lds_bytes(int waves, int NcT, int D, bool bf16);
+
+// k_sel: bitmap words per wave (one byte per half block of Nb blocks, padded
+// to 16 bytes) and the dynamic LDS of a launch.
+inline int sel_bm_words(int Nb) { return (2 * Nb + 15) / 16 * 4; }
+size_t sel_lds_bytes(int Nb, int D, bool bf16);
+// static LDS of k_sel (query fragments of 4 waves)
+inline size_t sel_static_lds_bytes(int D, bool bf16) {
+  return 4 * static_cast<size_t>(kSelTPW) * (D / 32) * (bf16 ? 16 : 32) * 64;
+}
 
 // LDS bytes of the block scores and top-k scratch of the compressed kernel.
 inline size_t cmp_lds_bytes(int waves, int NcT) {

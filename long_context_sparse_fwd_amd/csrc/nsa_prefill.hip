@@ -515,19 +515,23 @@ __device__ __forceinline__ void half_attend(const HalfBlock<T, D>& hb, const Fra
   online_step<T, D / 16, MASK>(st, kb, 0, t, grp, sl2, m, l, acc, hb.v);
 }
 
-// A wave owns kSelTPW tokens. Their usable half blocks are flattened into one
-// step list (token, block, half) in LDS, and the tokens' query fragments are
-// kept in LDS too; a ring of kSelRing half-block register buffers keeps
-// kSelRing - 1 loads in flight while one is computed, across token
-// boundaries, with two waves per SIMD.
+// A wave owns kSelTPW consecutive tokens of one KV group. The half blocks
+// they selected are marked in a per-wave LDS bitmap (one byte per half
+// block, bit qt = token qt uses it) and compacted into a step list in
+// ascending block order: a half block chosen by several of the wave's tokens
+// (always the own block, shared by neighbouring tokens) is loaded once, and
+// every wave sweeps the blocks in the same direction, so concurrent gathers
+// stay closer together in L2. The steps stream through a ring of kSelRing
+// half-block register buffers; each step runs the online-softmax update of
+// every token in its mask. Query fragments are kept in LDS.
 template <class T, class O, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_sel(PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_sel(PrefillArgs a) {
   using S = typename T::storage;
   using SO = typename O::storage;
   constexpr int TPW = kSelTPW, NB = kSelRing, KS = D / 32, DT = D / 16;
   constexpr int FE = sizeof(Frag<T>) / 16;  // 16-byte words per fragment lane
-  __shared__ int steps_lds[4][TPW * 128];
   __shared__ u32x4 q_lds[4][TPW][KS][FE][64];
+  extern __shared__ __align__(16) unsigned char sel_dyn[];  // per wave: bitmap words, then steps
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int N = a.B * a.G * a.sel_tiles;
   const int per = (N + 7) >> 3;
@@ -547,11 +551,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const S* VT = static_cast<const S*>(a.vt) + tb;
   const S* Q = static_cast<const S*>(a.q) + b * a.qs[0] + h * a.qs[2] + 8 * grp;
   const int n = a.n;
+  uint32_t* bm = reinterpret_cast<uint32_t*>(sel_dyn) + static_cast<size_t>(wave) * (a.sel_bm_words + TPW * 128);
+  int* steps = reinterpret_cast<int*>(bm + a.sel_bm_words);
 
-  // ---- query fragments -> LDS; the step list: code = qt << 24 | half << 23 | block
-  int* steps = steps_lds[wave];
-  int nsteps = 0;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // ---- query fragments -> LDS; the wave's half blocks -> bitmap -> step list
+  const int tl = min(t0 + TPW - 1, a.L - 1);
+  const int nwords = (2 * ((tl >> 6) + 1) + 3) >> 2;  // half blocks 0 .. 2 own(tl) + 1
+  for (int w = lane; w < nwords; w += 64) bm[w] = 0u;
 #pragma unroll
   for (int qt = 0; qt < TPW; ++qt) {
     const int t = t0 + qt;
@@ -564,17 +570,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int e = 0; e < FE; ++e) q_lds[wave][qt][s][e][lane] = w[e];
     }
-    if (!tv) continue;
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int qt = 0; qt < TPW; ++qt) {
+    const int t = t0 + qt;
+    if (t >= a.L) break;
     const int own = t >> 6;
     const int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.L + t) * a.G + g) * n;
     const int j = lane < n ? row[lane] : -1;
-    const bool v0 = j >= 0 && j <= own;            // padding / unusable injected entries drop out
-    const bool v1 = v0 && 64 * j + 32 <= t;
-    const uint64_t b0 = __ballot(v0), b1 = __ballot(v1);
-    const int pos = nsteps + __popcll(b0 & below) + __popcll(b1 & below);
-    if (v0) steps[pos] = (qt << 24) | j;
-    if (v1) steps[pos + 1] = (qt << 24) | (1 << 23) | j;
-    nsteps += __popcll(b0) + __popcll(b1);
+    if (j >= 0 && j <= own) {  // padding / unusable injected entries drop out
+      const uint32_t bit = 1u << qt;
+      atomicOr(&bm[j >> 1], bit << (16 * (j & 1)));
+      if (64 * j + 32 <= t) atomicOr(&bm[j >> 1], bit << (16 * (j & 1) + 8));
+    }
+  }
+  wave_lds_sync();
+  int nsteps = 0;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int w0 = 0; w0 < nwords; w0 += 64) {
+    const int w = w0 + lane;
+    const uint32_t word = w < nwords ? bm[w] : 0u;
+    int cnt = 0;
+#pragma unroll
+    for (int by = 0; by < 4; ++by) cnt += ((word >> (8 * by)) & 0xFFu) != 0u;
+    // prefix sum of the per-lane counts (0..4) over lower lanes, bit by bit
+    int pos = nsteps;
+    int tot = 0;
+#pragma unroll
+    for (int bit = 0; bit < 3; ++bit) {
+      const uint64_t bal = __ballot((cnt >> bit) & 1);
+      pos += __popcll(bal & below) << bit;
+      tot += __popcll(bal) << bit;
+    }
+#pragma unroll
+    for (int by = 0; by < 4; ++by) {
+      const uint32_t msk = (word >> (8 * by)) & 0xFFu;
+      if (msk != 0u) {
+        const int hb = 4 * w + by;  // half block: block hb / 2, half hb % 2
+        steps[pos++] = (hb >> 1) | ((hb & 1) << 23) | static_cast<int>(msk << 24);
+      }
+    }
+    nsteps += tot;
   }
   wave_lds_sync();
 
@@ -588,10 +625,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   // The ring is loaded unconditionally -- a step past the end reloads the
-  // last step's half block -- and the loop's only exit is at its top; a slot
-  // past the end is stepped as an empty key range. The count of loads in
-  // flight is then the same on every path, so each step waits only for its
-  // own slot's loads while the other slot's stay in flight.
+  // last step's half block and is run with no tokens -- and the loop's only
+  // exit is at its top, so the count of loads in flight is the same on every
+  // path and each step waits only for its own slot's loads while the other
+  // slots' stay in flight.
   if (nsteps > 0) {
     HalfBlock<T, D> ring[NB];
 #pragma unroll
@@ -606,25 +643,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int k = 0; k < NB; ++k) {
         const int s = base + k;
         const int code = steps[min(s, nsteps - 1)];
-        const int qt = code >> 24, j = code & 0x7FFFFF, hh = (code >> 23) & 1;
-        const int t = s < nsteps ? t0 + qt : -1;  // -1: every key masked
+        const int j = code & 0x7FFFFF, hh = (code >> 23) & 1;
+        const int msk = s < nsteps ? static_cast<int>(static_cast<uint32_t>(code) >> 24) : 0;
         const int kb = 64 * j + 32 * hh;
-        const bool full = kb + 31 <= t;
-        Frag<T> qf[KS];
 #pragma unroll
-        for (int ss = 0; ss < KS; ++ss) {
-          u32x4* w = reinterpret_cast<u32x4*>(&qf[ss]);
+        for (int qt = 0; qt < TPW; ++qt) {
+          if ((msk >> qt) & 1) {
+            const int t = t0 + qt;
+            Frag<T> qf[KS];
 #pragma unroll
-          for (int e = 0; e < FE; ++e) w[e] = q_lds[wave][qt][ss][e][lane];
-        }
+            for (int ss = 0; ss < KS; ++ss) {
+              u32x4* w = reinterpret_cast<u32x4*>(&qf[ss]);
 #pragma unroll
-        for (int q = 0; q < TPW; ++q)
-          if (q == qt) {
-            if (full)
-              half_attend<T, D, false>(ring[k], qf, kb, t, grp, sl2, m[q], l[q], acc[q]);
+              for (int e = 0; e < FE; ++e) w[e] = q_lds[wave][qt][ss][e][lane];
+            }
+            if (kb + 31 <= t)
+              half_attend<T, D, false>(ring[k], qf, kb, t, grp, sl2, m[qt], l[qt], acc[qt]);
             else
-              half_attend<T, D, true>(ring[k], qf, kb, t, grp, sl2, m[q], l[q], acc[q]);
+              half_attend<T, D, true>(ring[k], qf, kb, t, grp, sl2, m[qt], l[qt], acc[qt]);
           }
+        }
         __builtin_amdgcn_sched_barrier(0);
         const int nc = steps[min(s + NB, nsteps - 1)];
         half_load<T, D>(ring[k], KT, VT, nc & 0x7FFFFF, (nc >> 23) & 1, lane);
@@ -652,7 +690,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// ------------------------------------------------------------------ launcher
+size_t sel_lds_bytes(int Nb, int D, bool bf16) {
+  const size_t need = 4 * (static_cast<size_t>(sel_bm_words(Nb)) + kSelTPW * 128) * sizeof(uint32_t);
+  const size_t stat = sel_static_lds_bytes(D, bf16);
+  const size_t cap = kSelLdsOneWg > stat ? kSelLdsOneWg - stat : 0;  // total > half a CU's LDS
+  return need > cap ? need : cap;
+}
 
 size_t cmpwin_lds_bytes(int waves, int NcT, int D, bool bf16) {
   return 4 * 64 * static_cast<size_t>(D) * (bf16 ? 2 : 4) + cmp_lds_bytes(waves, NcT);
@@ -687,13 +730,14 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st, hipEven
   if ((e = record(ev, 2, st)) != hipSuccess) return e;
   const int N = a.B * a.G * a.sel_tiles;
   const int per = (N + 7) / 8;
-  // k_sel uses no dynamic LDS; reserving more than half a CU's LDS caps
-  // residency at one workgroup (4 waves) per CU, which was measured faster
-  // (~13 % at 64k) than two: the gathers then contend less for L2.
+  // Static + dynamic LDS above half a CU's caps residency at one workgroup
+  // (4 waves) per CU, which was measured faster (~13 % at 64k) than two: the
+  // gathers then contend less for L2.
+  const size_t sel_lds = sel_lds_bytes(a.Nb, D, sizeof(typename T::storage) == 2);
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sel<T, O, D>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kSelLdsReserve));
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sel_lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_sel<T, O, D>), dim3(per * 8), dim3(256), kSelLdsReserve, st, a);
+  hipLaunchKernelGGL((k_sel<T, O, D>), dim3(per * 8), dim3(256), sel_lds, st, a);
   if ((e = record(ev, 3, st)) != hipSuccess) return e;
   return hipGetLastError();
 }
