@@ -11,7 +11,7 @@ namespace nsa {
 constexpr int kBlock = 64;         // compress / select block size supported
 constexpr int kSurvCap = 256;      // top-k survivor buffer per wave (entries)
 constexpr int kCmpTPW = 2;         // tokens per wave, window+compressed+selection kernel
-constexpr int kSelTPW = 4;         // tokens per wave, selected-branch kernel (4 waves)
+constexpr int kSelTPW = 2;         // tokens per wave, selected-branch kernel (4 waves)
 constexpr int kSelRing = 2;        // half-block register buffers per wave in that kernel
 constexpr int kMaxLds = 160 * 1024;
 constexpr size_t kSelLdsOneWg = 81 * 1024;  // k_sel LDS (static + dynamic) for one workgroup per CU

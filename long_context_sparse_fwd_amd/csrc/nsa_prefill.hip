@@ -525,7 +525,7 @@ __device__ __forceinline__ void half_attend(const HalfBlock<T, D>& hb, const Fra
 // half-block register buffers; each step runs the online-softmax update of
 // every token in its mask. Query fragments are kept in LDS.
 template <class T, class O, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_sel(PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_sel(PrefillArgs a) {
   using S = typename T::storage;
   using SO = typename O::storage;
   constexpr int TPW = kSelTPW, NB = kSelRing, KS = D / 32, DT = D / 16;
