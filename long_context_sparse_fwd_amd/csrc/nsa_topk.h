@@ -13,11 +13,15 @@
 //  2. theta = the (n-1)-th largest of the 64 per-lane maxima (bitonic sort
 //     across lanes). At least n-1 candidates are >= theta, so every member of
 //     the answer is >= theta;
-//  3. the candidates >= theta (typically ~20) are compacted into LDS and each
-//     is ranked by counting larger keys; ranks < n-1 are the answer. If more
-//     than kSurvCap survive (heavy ties), n-1 rounds of wave-wide argmax over
-//     all candidates are used instead;
-//  4. the n chosen indices are sorted ascending by rank counting.
+//  3. the candidates >= theta (typically ~20) are compacted into LDS; up to
+//     64 of them are sorted across the lanes (one key per lane) and the first
+//     n-1 are the answer. With 65..kSurvCap survivors each is ranked by
+//     counting larger keys; with more (heavy ties), n-1 rounds of wave-wide
+//     argmax over all candidates are used instead;
+//  4. the n chosen indices are sorted ascending across the lanes.
+// The cross-lane sorts are bitonic networks whose exchanges inside 16-lane
+// rows are DPP moves; only the 16- and 32-lane distances go through the LDS
+// crossbar.
 #pragma once
 
 #include "nsa_device.h"
@@ -29,6 +33,47 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, 64);
   const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, 64);
   return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+// The value of lane (lane ^ m), m a power of two below 64 (a constant after
+// unrolling): DPP inside 16-lane rows (xor 4 as a half-row mirror followed by
+// a reversed quad permutation), ds_swizzle across the rows of a 32-lane half,
+// ds_bpermute across halves.
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int m) {
+  switch (m) {
+    case 1: return dpp_u<0xB1>(v);                // quad_perm [1,0,3,2]
+    case 2: return dpp_u<0x4E>(v);                // quad_perm [2,3,0,1]
+    case 4: return dpp_u<0x1B>(dpp_u<0x141>(v));  // row_half_mirror, quad_perm [3,2,1,0]
+    case 8: return dpp_u<0x128>(v);               // row_ror:8
+    case 16: return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x401F));
+    default: return static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), 32, 64));
+  }
+}
+__device__ __forceinline__ uint64_t lane_xor(uint64_t v, int m) {
+  const uint32_t lo = lane_xor(static_cast<uint32_t>(v), m);
+  const uint32_t hi = lane_xor(static_cast<uint32_t>(v >> 32), m);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Bitonic sort of one value per lane across the wave: descending (lane 0
+// holds the largest) or ascending.
+template <bool DESC, class K>
+__device__ __forceinline__ K wave_sort(K v, int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      const K o = lane_xor(v, jj);
+      const bool first = ((lane & jj) == 0) == ((lane & k) == 0);
+      v = (first == DESC) ? (v > o ? v : o) : (v < o ? v : o);
+    }
+  }
+  return v;
 }
 
 // sc: scores of blocks [0, own) in LDS (read by all lanes). out: n entries.
@@ -51,18 +96,8 @@ __device__ inline void topk_wave(const float* sc, int own, int n, int32_t* out, 
     const int j = lane + 64 * r;
     if (j < own) lmax = max(lmax, __float_as_uint(sc[j]) | 0x80000000u);
   }
-  // bitonic sort of the lane maxima, descending across lanes
-  uint32_t v = lmax;
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      const uint32_t o = __shfl_xor(v, jj, 64);
-      const bool keep_max = ((lane & jj) == 0) == ((lane & k) == 0);
-      v = keep_max ? max(v, o) : min(v, o);
-    }
-  }
-  const uint32_t theta = __shfl(v, n1 - 1, 64);
+  // theta: the (n-1)-th largest lane maximum
+  const uint32_t theta = __builtin_amdgcn_readlane(wave_sort<true>(lmax, lane), n1 - 1);
 
   int cnt = 0;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -77,43 +112,48 @@ __device__ inline void topk_wave(const float* sc, int own, int n, int32_t* out, 
     cnt += __popcll(bal);
   }
   wave_lds_sync();
-  if (cnt <= kSurvCap) {
-    for (int i = lane; i < cnt; i += 64) {
-      const uint64_t mine = surv[i];
-      int rank = 0;
-      for (int k = 0; k < cnt; ++k) rank += surv[k] > mine ? 1 : 0;
-      if (rank < n1) selb[rank] = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(mine));
-    }
+  uint32_t jsel;  // this lane's chosen block (lanes < n), 0xFFFFFFFF elsewhere
+  if (cnt <= 64) {
+    // one survivor per lane: sort the keys, the first n-1 lanes hold the answer
+    const uint64_t key = wave_sort<true>(lane < cnt ? surv[lane] : uint64_t{0}, lane);
+    jsel = lane < n1 ? 0xFFFFFFFFu - static_cast<uint32_t>(key) : 0xFFFFFFFFu;
   } else {
-    uint64_t prev = ~0ull;
-    for (int rr = 0; rr < n1; ++rr) {
-      uint64_t best = 0;
-      for (int r = 0; r < R; ++r) {
-        const int j = lane + 64 * r;
-        if (j < own) {
-          const uint64_t k64 =
-              (static_cast<uint64_t>(__float_as_uint(sc[j]) | 0x80000000u) << 32) |
-              static_cast<uint32_t>(0xFFFFFFFFu - j);
-          if (k64 < prev && k64 > best) best = k64;
+    if (cnt <= kSurvCap) {
+      for (int i = lane; i < cnt; i += 64) {
+        const uint64_t mine = surv[i];
+        int rank = 0;
+        for (int k = 0; k < cnt; ++k) rank += surv[k] > mine ? 1 : 0;
+        if (rank < n1) selb[rank] = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(mine));
+      }
+    } else {
+      uint64_t prev = ~0ull;
+      for (int rr = 0; rr < n1; ++rr) {
+        uint64_t best = 0;
+        for (int r = 0; r < R; ++r) {
+          const int j = lane + 64 * r;
+          if (j < own) {
+            const uint64_t k64 =
+                (static_cast<uint64_t>(__float_as_uint(sc[j]) | 0x80000000u) << 32) |
+                static_cast<uint32_t>(0xFFFFFFFFu - j);
+            if (k64 < prev && k64 > best) best = k64;
+          }
         }
-      }
 #pragma unroll
-      for (int m = 32; m > 0; m >>= 1) {
-        const uint64_t o = shfl_xor_u64(best, m);
-        best = o > best ? o : best;
+        for (int m = 32; m > 0; m >>= 1) {
+          const uint64_t o = shfl_xor_u64(best, m);
+          best = o > best ? o : best;
+        }
+        prev = best;
+        if (lane == 0) selb[rr] = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
       }
-      prev = best;
-      if (lane == 0) selb[rr] = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
     }
+    wave_lds_sync();
+    jsel = lane < n1 ? static_cast<uint32_t>(selb[lane]) : 0xFFFFFFFFu;
   }
-  if (lane == 0) selb[n1] = own;
-  wave_lds_sync();
-  if (lane < n) {
-    const int vj = selb[lane];
-    int pos = 0;
-    for (int k = 0; k < n; ++k) pos += selb[k] < vj ? 1 : 0;
-    out[pos] = vj;
-  }
+  if (lane == n1) jsel = static_cast<uint32_t>(own);
+  // the n chosen blocks in ascending order (the 0xFFFFFFFF fillers sort last)
+  jsel = wave_sort<false>(jsel, lane);
+  if (lane < n) out[lane] = static_cast<int32_t>(jsel);
   wave_lds_sync();
 }
 
