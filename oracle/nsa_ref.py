@@ -43,6 +43,9 @@ the design notes):
       post-sigmoid values, one per (token, head, branch), not renormalised.
 * R7  query head ``h`` belongs to KV group ``h // (Hq/G)``.
 * R8  ``select_block_size`` must equal ``compress_block_size``.
+* R12 an injected selection is a set of blocks: entries outside ``[0, t//l]``
+      and repeats add nothing; a row with no usable entry gives a selected
+      branch of 0.
 """
 
 from __future__ import annotations
@@ -142,12 +145,14 @@ def nsa_token(q_t, K, V, Kc, Vc, t: int, g_t, *, block: int, top_k: int, window:
             idx[g], gap[g] = select_blocks(scores, own, top_k)
         else:
             idx[g] = np.asarray(inject[g], dtype=np.int32)
-        # selected branch: tokens of the chosen blocks, causal (R5)
-        toks = [np.arange(j * block, min(j * block + block, t + 1))
-                for j in idx[g] if 0 <= j and j * block <= t]
-        toks = np.concatenate(toks)
-        o_slc[hs], _ = softmax_attend(qg, np.asarray(K[toks, g], dtype=np.float64),
-                                      np.asarray(V[toks, g], dtype=np.float64), scale)
+        # selected branch: tokens of the chosen blocks, causal (R5). The
+        # selection is a set of blocks: repeated or unusable injected entries
+        # add nothing, and no usable block leaves this branch at 0 (R12).
+        blocks = sorted({int(j) for j in idx[g] if 0 <= j and j * block <= t})
+        if blocks:
+            toks = np.concatenate([np.arange(j * block, min(j * block + block, t + 1)) for j in blocks])
+            o_slc[hs], _ = softmax_attend(qg, np.asarray(K[toks, g], dtype=np.float64),
+                                          np.asarray(V[toks, g], dtype=np.float64), scale)
         # sliding-window branch (R5)
         lo = max(0, t - window + 1)
         o_win[hs], _ = softmax_attend(qg, np.asarray(K[lo: t + 1, g], dtype=np.float64),

@@ -223,6 +223,58 @@ def test_top1_is_own_block_attention():
         assert np.all(r["idx"][0, lo:hi, 0, 0] == own)
 
 
+# ---------------------------------------------------------------- injected selections (R12)
+
+def _masked_attention(q, k, v, allowed):
+    """Attention of one query per head over the keys flagged in ``allowed`` [L],
+    with torch's SDPA in float64. q [Hq, D], k/v [L, G, D]."""
+    Hq, D = q.shape
+    G = k.shape[1]
+    Hg = Hq // G
+    kk = torch.from_numpy(np.repeat(k, Hg, axis=1).transpose(1, 0, 2).copy())[None]
+    vv = torch.from_numpy(np.repeat(v, Hg, axis=1).transpose(1, 0, 2).copy())[None]
+    qq = torch.from_numpy(q[:, None, :].copy())[None]
+    mask = torch.from_numpy(np.asarray(allowed, dtype=bool))[None, None, None, :]
+    o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask, scale=1.0 / np.sqrt(D))
+    return o[0, :, 0].numpy()
+
+
+def test_injected_selection_is_a_set_of_blocks():
+    # repeats and unusable entries (negative, or later than the own block) add
+    # nothing: the selected branch is attention over the union of the usable
+    # blocks' tokens at or before t
+    L, Hq, G, D, l, n = 50, 4, 2, 8, 8, 5
+    d = _data(L, Hq, G, D, seed=31)
+    rng = np.random.default_rng(5)
+    inj = rng.integers(-2, L // l + 2, size=(1, L, G, n)).astype(np.int32)
+    inj[0, :, :, 1] = inj[0, :, :, 0]            # a repeat in every row
+    r = nsa_ref.prefill(d["q"], d["k"], d["v"], d["gates"], block=l, top_k=n, window=4,
+                        inject_idx=inj, branches=True)
+    Hg = Hq // G
+    for t in range(L):
+        for g in range(G):
+            blocks = {int(j) for j in inj[0, t, g] if 0 <= j <= t // l}
+            hs = slice(g * Hg, (g + 1) * Hg)
+            if not blocks:
+                assert np.all(r["o_slc"][0, t, hs] == 0.0)
+                continue
+            allowed = np.array([(key // l) in blocks and key <= t for key in range(L)])
+            want = _masked_attention(d["q"][0, t, hs], d["k"][0][:, g:g + 1], d["v"][0][:, g:g + 1], allowed)
+            np.testing.assert_allclose(r["o_slc"][0, t, hs], want, atol=1e-12)
+
+
+def test_empty_injected_selection_drops_the_selected_branch():
+    L, Hq, G, D, l, n = 24, 2, 1, 8, 8, 3
+    d = _data(L, Hq, G, D, seed=37)
+    inj = np.full((1, L, G, n), -1, dtype=np.int32)
+    r = nsa_ref.prefill(d["q"], d["k"], d["v"], d["gates"], block=l, top_k=n, window=5,
+                        inject_idx=inj, branches=True)
+    assert np.all(r["o_slc"] == 0.0)
+    gates = d["gates"]
+    np.testing.assert_allclose(r["out"], gates[..., 0:1] * r["o_cmp"] + gates[..., 2:3] * r["o_win"],
+                               atol=1e-14)
+
+
 # ---------------------------------------------------------------- selection
 
 def test_selection_matches_brute_force_sort_and_score_mass():
