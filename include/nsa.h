@@ -150,8 +150,9 @@ nsa_status_t nsa_decode_workspace_bytes(const nsa_decode_desc_t* desc,
  * idx_mode NSA_IDX_COMPUTE: the selection is computed; if idx != NULL it is
  *   written there, each row ascending and padded with -1.
  * idx_mode NSA_IDX_INJECT: idx (required) supplies the selection. Entries
- *   outside [0, t/l] are skipped, duplicates count twice, and a row with no
- *   usable entry gives a selected-branch output of 0.
+ *   outside [0, t/l] are skipped and repeated entries count once (the
+ *   selection is a set of blocks); a row with no usable entry gives a
+ *   selected-branch output of 0.
  * `out` is also used as scratch while the call runs.
  */
 nsa_status_t nsa_fwd_prefill(const nsa_prefill_desc_t* desc, const nsa_params_t* params,

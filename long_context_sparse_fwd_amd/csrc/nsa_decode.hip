@@ -465,7 +465,10 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     }
     wave_lds_sync();
     const int j = lane < a.n ? selo[lane] : -1;
-    const bool h0 = j >= 0 && j <= own;
+    // the selection is a set of blocks: a repeated injected entry adds nothing
+    bool rep = false;
+    for (int k = 0; k < a.n; ++k) rep |= k < lane && __builtin_amdgcn_readlane(j, k) == j;
+    const bool h0 = j >= 0 && j <= own && !rep;
     const bool h1 = h0 && 64 * j + 32 <= t;
     const uint64_t b0 = __ballot(h0), b1 = __ballot(h1);
     const uint64_t below = (uint64_t{1} << lane) - 1;

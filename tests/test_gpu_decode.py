@@ -152,3 +152,29 @@ def test_decode_equals_prefill_last_rows_on_gpu():
         err = (dout[i] - pout[b, t]).abs().max().item()
         # identical block means and products; only summation orders differ
         assert err <= (1e-3 if same else 2e-1), (i, same, err)
+
+
+def test_decode_injected_selection_with_repeats_and_unusable_entries():
+    cfg = inputs.DecodeConfig("dec-inject", 4, 700, 8, 2, 64, "bf16", top_k=6, window=100,
+                              seqlens=(700, 65, 333, 1))
+    raw = inputs.make_decode_inputs(cfg)
+    print(f"[decode inject] {cfg.name}", flush=True)
+    q, kc_, vc_, g = (dev(raw[n], cfg.dtype) for n in ("q", "k_cache", "v_cache", "gates"))
+    kb = _stored(_block_cache_f64(Lazy(raw["k_cache"], cfg.dtype)[:], cfg.block), cfg.dtype)
+    vb = _stored(_block_cache_f64(Lazy(raw["v_cache"], cfg.dtype)[:], cfg.block), cfg.dtype)
+    kbd, vbd = dev(kb, cfg.dtype), dev(vb, cfg.dtype)
+    lens = torch.from_numpy(raw["seqlens"]).cuda()
+    rng = np.random.default_rng(13)
+    nb = cfg.max_seqlen // cfg.block
+    inj = rng.integers(-2, nb + 2, size=(cfg.batch, cfg.n_kv_heads, cfg.top_k)).astype(np.int32)
+    inj[..., 1] = inj[..., 0]
+    inj[2, 1] = -1                                          # one (sequence, group) selects nothing
+    out = nsa.decode(q, kc_, vc_, kbd, vbd, lens, g, top_k=cfg.top_k, window=cfg.window,
+                     out_dtype=torch.float32, idx=torch.from_numpy(inj).cuda(), inject=True)[0]
+    torch.cuda.synchronize()
+    lz = lambda n: Lazy(raw[n], cfg.dtype)
+    orc = nsa_ref.decode(lz("q")[:], lz("k_cache")[:], lz("v_cache")[:], Lazy(kb, cfg.dtype)[:],
+                         Lazy(vb, cfg.dtype)[:], raw["seqlens"], lz("gates")[:], block=cfg.block,
+                         top_k=cfg.top_k, window=cfg.window, inject_idx=inj)
+    err = maxabs(out.cpu().numpy().astype(np.float64), orc["out"])
+    assert err <= TOL[cfg.dtype], f"decode injected-selection error {err}"

@@ -195,3 +195,27 @@ def test_strided_inputs():
     assert torch.equal(idx, ridx)
     assert torch.equal(out, ref)
     assert torch.all(ob[..., 64:] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_injected_selection_with_repeats_and_unusable_entries(dtype):
+    # an injected selection is a set of blocks: repeats, negative entries and
+    # entries after the own block add nothing; rows with no usable entry get a
+    # selected branch of 0. Every row is compared with the oracle given the
+    # same injection.
+    cfg = inputs.PrefillConfig("inject", 2, 300, 8, 2, 64, dtype, top_k=6, window=40, seed=3)
+    raw = inputs.make_prefill_inputs(cfg)
+    q, k, v, g = _upload(cfg, raw)
+    rng = np.random.default_rng(11)
+    nb = -(-cfg.seqlen // cfg.block)
+    inj = rng.integers(-2, nb + 2, size=(cfg.batch, cfg.seqlen, cfg.n_kv_heads, cfg.top_k)).astype(np.int32)
+    inj[..., 1] = inj[..., 0]
+    inj[..., 3] = inj[..., 2]
+    inj[:, ::7] = -1                                        # some rows select nothing
+    print(f"[prefill inject] {cfg}", flush=True)
+    out = nsa.prefill(q, k, v, g, top_k=cfg.top_k, window=cfg.window, out_dtype=torch.float32,
+                      idx=torch.from_numpy(inj).cuda(), inject=True)[0]
+    torch.cuda.synchronize()
+    orc = _oracle(cfg, raw, np.arange(cfg.seqlen), inject=inj)
+    err = maxabs(out.cpu().numpy().astype(np.float64), orc["out"])
+    assert err <= TOL[dtype], f"injected-selection error {err}"
