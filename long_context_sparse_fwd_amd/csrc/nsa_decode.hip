@@ -368,6 +368,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   int* selo = selb + 64;
   int* hl = selo + 64;                            // usable selected half blocks: 2 j + half
   int* nhl = hl + 128;                            // their count
+  int* hl_ready = nhl + 1;                        // set by wave 0 once hl and nhl are written
   float* hs = reinterpret_cast<float*>(nhl + 4);  // per head: 4 floats
   float* gts = hs + 64;                           // [3][16] gates
   float* lg_lds = gts + 48;                       // [16][NmaxPad] logits, if LGL
@@ -387,6 +388,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   const float sl2 = a.scale_log2;
   void* lv = smem + wave * VStage<T, D>::kBytes;
 
+  if (tid == 0) *hl_ready = 0;
   // query fragments (lane l: head l % 16) and gates of the group's heads
   if (wave == 0) {
     const S* Q = static_cast<const S*>(a.q) + b * a.qs[0] + (g * a.Hg + col) * a.qs[1] + 8 * (lane >> 4);
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   lds_barrier();  // sc written; parts read, so the V staging is free again
 
   // ---- C': wave 0 selects and lists the usable half blocks while the other
-  //      waves stream the sliding window (all waves when the selection is given)
+  //      waves stream the sliding window
   if (wave == 0) {
     if (!a.inject) {
       topk_wave(sc, own, a.n, selo, surv, selb, lane);
@@ -476,20 +478,36 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     if (h0) hl[pos] = 2 * j;
     if (h1) hl[pos + 1] = 2 * j + 1;
     if (lane == 0) *nhl = __popcll(b0) + __popcll(b1);
+    if (lane == 0) __hip_atomic_store(hl_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
+  // The window is streamed by waves 1..7. When the logits region (free once
+  // the scores are done) can hold their 7 partial states, each wave parks its
+  // state there and moves on to the selected blocks as soon as wave 0 has
+  // published the list, without waiting for the other waves; the window is
+  // merged at the end. Otherwise the window is merged before the selected
+  // blocks.
+  const bool park = LGL && 16 * a.NmaxPad >= (NWV - 1) * SF;
   {
     const int nwin = (t - wlo + 32) >> 5;
     auto desc = [&](int q) { return DItem<T>{Kr, Vr, a.ks[2], a.vs[2], wlo + 32 * q, wlo, t, nullptr}; };
     reset_state<D>(m, l, acc);
-    if (wave > 0 || a.inject) {
-      const int w0 = a.inject ? 0 : 1;
-      DStream<T, D, RING> ds(wave - w0, NWV - w0);
+    if (wave > 0) {
+      DStream<T, D, RING> ds(wave - 1, NWV - 1);
       ds.prime(nwin, desc, lane);
       ds.run(nwin, desc, scores, update, lane);
     }
     l = col_sum4(l);
   }
-  merge_into<D, NWV>(parts, m, l, acc, gts + 32, hs, res, tid, lane);
+  if (park) {
+    if (wave > 0) {
+      store_partial<D>(lg_lds + (wave - 1) * SF, m, l, acc, lane);
+      // wait for wave 0's list (it always publishes it)
+      while (__hip_atomic_load(hl_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+        __builtin_amdgcn_s_sleep(1);
+    }
+  } else {
+    merge_into<D, NWV>(parts, m, l, acc, gts + 32, hs, res, tid, lane);
+  }
 
   // ---- D: selected half blocks
   {
@@ -507,6 +525,19 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     l = col_sum4(l);
   }
   merge_into<D, NWV>(parts, m, l, acc, gts + 16, hs, res, tid, lane);
+  if (park) {  // the parked window states
+    if (tid < 16) {
+      float M, L;
+      merge_stats(lg_lds, NWV - 1, SF, tid, M, L);
+      hs[4 * tid] = M;
+      hs[4 * tid + 1] = L > 0.f ? gts[32 + tid] / L : 0.f;
+    }
+    lds_barrier();
+    for (int e = tid; e < 16 * D; e += NT) {
+      const int h = e / D;
+      res[e] += merge_out<NWV - 1>(lg_lds, SF, h, e, hs[4 * h]) * hs[4 * h + 1];
+    }
+  }
 
   // ---- E: out = gate_cmp O_cmp + gate_slc O_slc + gate_win O_win
   for (int e = tid; e < a.Hg * D; e += NT) OUT[(g * a.Hg + e / D) * a.os[1] + e % D] = from_f32<O>(res[e]);
