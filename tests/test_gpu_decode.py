@@ -83,6 +83,8 @@ def run_decode(cfg, batches=None, check_c=True):
     inputs.DecodeConfig("dec-mixed", 6, 1000, 16, 2, 128, "bf16", top_k=7, window=130,
                         seqlens=(1, 63, 64, 700, 1000, 129)),
     inputs.DecodeConfig("dec-f32", 3, 700, 8, 2, 64, "f32", top_k=4, window=64, seqlens=(700, 65, 333)),
+    # fp32 with D 128 keeps the compressed logits in the workspace, not in LDS
+    inputs.DecodeConfig("dec-f32-d128", 2, 900, 8, 2, 128, "f32", top_k=5, window=200, seqlens=(900, 321)),
     inputs.DecodeConfig("dec-bf16-long", 2, 8192, 64, 4, 128, "bf16", top_k=16, window=512),
     inputs.DecodeConfig("dec-window-all", 2, 300, 4, 1, 64, "bf16", top_k=2, window=5000,
                         seqlens=(300, 190)),
