@@ -198,64 +198,71 @@ __device__ __forceinline__ void dhalf_update(f32x4 (&st)[2], const DItem<T>& it,
   wave_lds_sync();
 }
 
-// A wave's share of a phase's `total` half chunks desc(0..total-1) -- items
-// first, first + stride, ... -- streamed through a ring of RING register
-// buffers: prime() fills the ring; run() computes the buffers in order,
-// refilling each as soon as it is consumed. Work done between the two
-// overlaps the first loads. (A shared work counter balancing the waves was
-// measured slower: the phases are bound by the memory system, not by the
-// slowest wave.)
+// A wave's half chunks streamed through a ring of RING register buffers.
+// A phase is a count N of steps (a multiple of RING) and item(k), the k-th
+// step's half chunk; steps past the wave's real items are empty items (an
+// empty key range over rows the wave has just read, so the reload hits the
+// caches), which keeps every phase's loop free of conditional loads: the
+// number of loads in flight is the same on every path, so each step waits
+// only for its own buffer. Every buffer is refilled as soon as it is
+// consumed; the refills of a phase's last round load the first steps of the
+// next phase (next(k)), so the ring never drains between phases.
 template <class T, int D, int RING>
 struct DStream {
   DHalf<T, D> ring[RING];
-  int q[RING];
-  int nxt, stride;
-  __device__ __forceinline__ DStream(int first, int step) : nxt(first), stride(step) {}
-  // Every buffer is (re)loaded unconditionally -- an index past the end
-  // reloads the last item, whose data is then never used -- so that the
-  // number of loads in flight is the same on every path through the loop
-  // and each use waits only for its own buffer. total must be >= 1.
-  template <class Desc>
-  __device__ __forceinline__ void prime(int total, Desc desc, int lane) {
+  template <class Item>
+  __device__ __forceinline__ void prime(Item item, int lane) {
 #pragma unroll
     for (int r = 0; r < RING; ++r) {
-      q[r] = nxt;
-      nxt += stride;
-      dhalf_load<T, D>(ring[r], desc(min(q[r], total - 1)), lane);
+      dhalf_load<T, D>(ring[r], item(r), lane);
       __builtin_amdgcn_sched_barrier(0);  // buffers in order
     }
   }
-  // scores(c, it, st) consumes buffer c into st; update(st, it) finishes
-  // the step. Each buffer is refilled between the two, so its next load is
-  // in flight during the softmax and the P.V product.
-  template <class Desc, class Scores, class Update>
-  __device__ __forceinline__ void run(int total, Desc desc, Scores scores, Update update, int lane) {
-    // The stream ends when buffer 0 is past the end; later buffers past the
-    // end are still stepped, as an empty key range that adds nothing: a loop
-    // whose only exit is at its top keeps the count of loads in flight the
-    // same on every path, which the compiler needs to wait for one buffer
-    // only.
-#pragma unroll 1
-    while (q[0] < total) {
+  // One round: steps k0 .. k0 + RING - 1. scores(c, it, st) consumes buffer
+  // c into st; update(st, it) finishes the step. Each buffer is refilled
+  // with refill(r) between the two, so its loads are in flight during the
+  // softmax and the P.V product.
+  template <class Item, class Refill, class Scores, class Update>
+  __device__ __forceinline__ void round(int k0, Item item, Refill refill, Scores scores, Update update,
+                                        int lane) {
 #pragma unroll
-      for (int r = 0; r < RING; ++r) {
-        DItem<T> it = desc(min(q[r], total - 1));
-        if (q[r] >= total) {
-          it.klo = it.khi + 1;
-          it.lrow = nullptr;
-        }
-        f32x4 st[2];
-        scores(ring[r], it, st);
-        __builtin_amdgcn_sched_barrier(0);
-        q[r] = nxt;
-        nxt += stride;
-        dhalf_load<T, D>(ring[r], desc(min(q[r], total - 1)), lane);
-        __builtin_amdgcn_sched_barrier(0);
-        update(st, it);
-      }
+    for (int r = 0; r < RING; ++r) {
+      const DItem<T> it = item(k0 + r);
+      f32x4 st[2];
+      scores(ring[r], it, st);
+      __builtin_amdgcn_sched_barrier(0);
+      dhalf_load<T, D>(ring[r], refill(r), lane);
+      __builtin_amdgcn_sched_barrier(0);
+      update(st, it);
     }
   }
+  // A phase of N steps. All rounds but the last refill from this phase; the
+  // last round, after hook(), refills with the next phase's first steps.
+  template <class Item, class Next, class Hook, class Scores, class Update>
+  __device__ __forceinline__ void run(int N, Item item, Next next, Hook hook, Scores scores, Update update,
+                                      int lane) {
+#pragma unroll 1
+    for (int k0 = 0; k0 < N - RING; k0 += RING)
+      round(k0, item, [&](int r) { return item(k0 + r + RING); }, scores, update, lane);
+    hook();
+    round(N - RING, item, next, scores, update, lane);
+  }
 };
+
+// Steps of a phase whose wave holds n real items: n rounded up to a whole
+// number of rounds, at least one round.
+template <int RING>
+__device__ __forceinline__ int phase_steps(int n) {
+  return n > RING ? (n + RING - 1) / RING * RING : RING;
+}
+
+// The same rows, as an empty key range (nothing is added; no logits).
+template <class T>
+__device__ __forceinline__ DItem<T> empty_item(DItem<T> it) {
+  it.klo = it.khi + 1;
+  it.lrow = nullptr;
+  return it;
+}
 
 // Stores a wave's partial state (m per column, l summed over the column's
 // lanes, O^T accumulators) as m[16], l[16], O[16][D] at dst.
@@ -272,20 +279,37 @@ __device__ __forceinline__ void store_partial(float* dst, float m, float l, cons
     *reinterpret_cast<f32x4*>(dst + 32 + col * D + 16 * dt + 4 * grp) = acc[dt];
 }
 
-// Merged (max, sum) of head h over `cnt` partial states (stride SF floats).
-__device__ __forceinline__ void merge_stats(const float* p, int cnt, int SF, int h, float& M, float& L) {
+// Merge factors of head h over CNT partial states (stride SF floats, one
+// thread per head): M = max_w m_w, L = sum_w l_w 2^(m_w - M), and
+// fac[w][h] = 2^(m_w - M) gate / L (0 when L = 0), so that the merged, gated
+// output element e of head h is sum_w O_w[e] fac[w][h].
+template <int CNT>
+__device__ __forceinline__ void merge_factors(const float* p, int SF, int h, float gate, float* fac, float& M,
+                                              float& L) {
+  float mw[CNT];
   M = kNegBig;
-  for (int s = 0; s < cnt; ++s) M = fmaxf(M, p[s * SF + h]);
+#pragma unroll
+  for (int w = 0; w < CNT; ++w) {
+    mw[w] = p[w * SF + h];
+    M = fmaxf(M, mw[w]);
+  }
   L = 0.f;
-  for (int s = 0; s < cnt; ++s) L += p[s * SF + 16 + h] * fast_exp2(p[s * SF + h] - M);
+#pragma unroll
+  for (int w = 0; w < CNT; ++w) {
+    mw[w] = fast_exp2(mw[w] - M);
+    L += p[w * SF + 16 + h] * mw[w];
+  }
+  const float r = L > 0.f ? gate / L : 0.f;
+#pragma unroll
+  for (int w = 0; w < CNT; ++w) fac[w * 16 + h] = mw[w] * r;
 }
 
-// Element e of the merged unnormalised output (relative to max M of its head).
-template <int NWV>
-__device__ __forceinline__ float merge_out(const float* p, int SF, int h, int e, float M) {
+// Element e (head h) of the merged, gated output.
+template <int CNT>
+__device__ __forceinline__ float merge_out(const float* p, const float* fac, int SF, int h, int e) {
   float o = 0.f;
 #pragma unroll
-  for (int w = 0; w < NWV; ++w) o += p[w * SF + 32 + e] * fast_exp2(p[w * SF + h] - M);
+  for (int w = 0; w < CNT; ++w) o += p[w * SF + 32 + e] * fac[w * 16 + h];
   return o;
 }
 
@@ -306,16 +330,22 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Block scores sc[j], j < own: the compressed-branch probabilities of block
-// j summed over the group's Hg heads, from the logits lg[h][j] (row stride
-// ld) and each head's log-sum-exp hs[4 h + 2].
+// j summed over the group's heads, from the logits lg[h][j] (row stride ld)
+// and each head's log-sum-exp hs[4 h + 2]. Rows of heads h >= Hg hold finite
+// logits and have log-sum-exp +inf, so they add exact zeros.
 template <class P>
-__device__ __forceinline__ void block_scores(P lg, int ld, int own, int Hg, const float* hs, float* sc,
-                                             int tid, int nt) {
+__device__ __forceinline__ void block_scores(P lg, int ld, int own, const float* hs, float* sc, int tid,
+                                             int nt) {
+  float lse[16];
+#pragma unroll
+  for (int h = 0; h < 16; ++h) lse[h] = hs[4 * h + 2];
   for (int j = tid; j < own; j += nt) {
+    float x[16];
+#pragma unroll
+    for (int h = 0; h < 16; ++h) x[h] = lg[h * ld + j];
     float s = 0.f;
 #pragma unroll
-    for (int h = 0; h < 16; ++h)
-      if (h < Hg) s += fast_exp2(lg[h * ld + j] - hs[4 * h + 2]);
+    for (int h = 0; h < 16; ++h) s += fast_exp2(x[h] - lse[h]);
     sc[j] = s;
   }
 }
@@ -325,22 +355,17 @@ __device__ __forceinline__ void block_scores(P lg, int ld, int own, int Hg, cons
 // workgroup barrier, so parts may alias the V staging.
 template <int D, int NWV>
 __device__ __forceinline__ void merge_into(float* parts, float m, float l, const f32x4 (&acc)[D / 16],
-                                           const float* gate, float* hs, float* res, int tid, int lane) {
+                                           const float* gate, float* fac, float* res, int tid, int lane) {
   constexpr int SF = dec_slot_floats(D), NT = 64 * NWV;
   lds_barrier();
   store_partial<D>(parts + (tid >> 6) * SF, m, l, acc, lane);
   lds_barrier();
   if (tid < 16) {
     float M, L;
-    merge_stats(parts, NWV, SF, tid, M, L);
-    hs[4 * tid] = M;
-    hs[4 * tid + 1] = L > 0.f ? gate[tid] / L : 0.f;
+    merge_factors<NWV>(parts, SF, tid, gate[tid], fac, M, L);
   }
   lds_barrier();
-  for (int e = tid; e < 16 * D; e += NT) {
-    const int h = e / D;
-    res[e] += merge_out<NWV>(parts, SF, h, e, hs[4 * h]) * hs[4 * h + 1];
-  }
+  for (int e = tid; e < 16 * D; e += NT) res[e] += merge_out<NWV>(parts, fac, SF, e / D, e);
   lds_barrier();
 }
 
@@ -353,7 +378,9 @@ __host__ __device__ constexpr size_t dec_big_bytes() {
   return stage > parts ? stage : parts;
 }
 
-template <class T, class O, int D, int RING, bool LGL>
+// LGL: the compressed logits stay in LDS. PARK (requires LGL): the logits
+// region, free once the block scores are done, holds the 7 window states.
+template <class T, class O, int D, int RING, bool LGL, bool PARK>
 __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_dec(DecodeArgs a) {
   using S = typename T::storage;
   using SO = typename O::storage;
@@ -371,9 +398,11 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   int* hl_ready = nhl + 1;                        // set by wave 0 once hl and nhl are written
   float* hs = reinterpret_cast<float*>(nhl + 4);  // per head: 4 floats
   float* gts = hs + 64;                           // [3][16] gates
-  float* lg_lds = gts + 48;                       // [16][NmaxPad] logits, if LGL
+  float* fac = gts + 48;                          // [NWV][16] merge factors
+  float* lg_lds = fac + 16 * NWV;                 // [16][NmaxPad] logits, if LGL
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: phase counts and bases stay scalar
   const int bg = blockIdx.x, b = bg / a.G, g = bg % a.G;
   const int s_raw = a.seqlens[b];
   int32_t* idxo = a.idx + static_cast<int64_t>(bg) * a.n;
@@ -388,19 +417,6 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   const float sl2 = a.scale_log2;
   void* lv = smem + wave * VStage<T, D>::kBytes;
 
-  if (tid == 0) *hl_ready = 0;
-  // query fragments (lane l: head l % 16) and gates of the group's heads
-  if (wave == 0) {
-    const S* Q = static_cast<const S*>(a.q) + b * a.qs[0] + (g * a.Hg + col) * a.qs[1] + 8 * (lane >> 4);
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) qlds[s * 64 + lane] = col < a.Hg ? frag_load<T>(Q + 32 * s) : frag_zero<T>();
-    if (lane < 48) {
-      const int h = lane & 15, i = lane >> 4;
-      gts[16 * i + h] =
-          h < a.Hg ? to_f32<T>(static_cast<const S*>(a.gates)[b * a.gs[0] + (g * a.Hg + h) * a.gs[1] + i]) : 0.f;
-    }
-  }
-  __syncthreads();
   const S* KCr = static_cast<const S*>(a.kccache) + b * a.kcs[0] + g * a.kcs[1];
   const S* VCr = static_cast<const S*>(a.vccache) + b * a.vcs[0] + g * a.vcs[1];
   const S* Kr = static_cast<const S*>(a.kcache) + b * a.ks[0] + g * a.ks[1];
@@ -415,43 +431,89 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   };
   auto update = [&](f32x4 (&st)[2], const DItem<T>& it) { dhalf_update<T, D>(st, it, sl2, lv, m, l, acc, lane); };
 
-  // ---- A: compressed half chunks
-  {
-    const int ncmp = (nvis + 31) >> 5;
-    float* lrow = a.inject ? nullptr : lg + col * a.NmaxPad;
-    auto desc = [&](int q) {
-      return DItem<T>{KCr, VCr, a.kcs[2], a.vcs[2], 32 * q, 0, nvis - 1,
-                      lrow != nullptr ? lrow + 32 * q : nullptr};
-    };
-    reset_state<D>(m, l, acc);
-    if (ncmp > 0) {
-      DStream<T, D, RING> ds(wave, NWV);
-      ds.prime(ncmp, desc, lane);
-      ds.run(ncmp, desc, scores, update, lane);
+  // The three phases' items for this wave: the compressed half chunks
+  // wave, wave + 8, ...; the window's (wave - 1), (wave - 1) + 7, ... for
+  // waves 1..7; the selected half blocks wave, wave + 8, ... Past a wave's
+  // real items the steps are empty items; `none` (row 0 of the cache, always
+  // present) stands in when a wave has no real item in a phase.
+  const DItem<T> none{Kr, Vr, a.ks[2], a.vs[2], 0, 1, 0, nullptr};
+  const int ncmp = (nvis + 31) >> 5;
+  const int nA = wave < ncmp ? (ncmp - 1 - wave) / NWV + 1 : 0;
+  float* lrow = a.inject ? nullptr : lg + col * a.NmaxPad;
+  auto a_real = [&](int q) {
+    return DItem<T>{KCr, VCr, a.kcs[2], a.vcs[2], 32 * q, 0, nvis - 1, lrow != nullptr ? lrow + 32 * q : nullptr};
+  };
+  auto a_item = [&](int k) {
+    return k < nA ? a_real(wave + NWV * k) : (nA > 0 ? empty_item(a_real(wave + NWV * (nA - 1))) : none);
+  };
+  const int nwin = (t - wlo + 32) >> 5, wq = wave - 1;
+  const int nW = (wave > 0 && wq < nwin) ? (nwin - 1 - wq) / (NWV - 1) + 1 : 0;
+  auto w_real = [&](int q) { return DItem<T>{Kr, Vr, a.ks[2], a.vs[2], wlo + 32 * q, wlo, t, nullptr}; };
+  auto w_item = [&](int k) {
+    return k < nW ? w_real(wq + (NWV - 1) * k) : (nW > 0 ? empty_item(w_real(wq + (NWV - 1) * (nW - 1))) : none);
+  };
+  int nD = -1;  // known once wave 0 has published the selected half blocks
+  auto d_real = [&](int q) {
+    const int u = hl[q], j = u >> 1;
+    return DItem<T>{Kr, Vr, a.ks[2], a.vs[2], 64 * j + 32 * (u & 1), 64 * j, t, nullptr};
+  };
+  auto d_item = [&](int k) {
+    return k < nD ? d_real(wave + NWV * k) : (nD > 0 ? empty_item(d_real(wave + NWV * (nD - 1))) : none);
+  };
+  auto d_wait = [&]() {
+    if (nD < 0) {
+      // wave 0 always publishes the list
+      while (__hip_atomic_load(hl_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+        __builtin_amdgcn_s_sleep(1);
+      const int nh = *nhl;
+      nD = wave < nh ? (nh - 1 - wave) / NWV + 1 : 0;
     }
-    l = col_sum4(l);
-  }
+  };
+  auto no_next = [&](int) { return none; };
+  auto no_hook = [&]() {};
+  DStream<T, D, RING> ds;
 
-  // ---- B: merge into the log-sum-exp and gate_cmp * O_cmp
-  __syncthreads();  // staging done; logits written (global memory when not in LDS)
+  // ---- A: compressed half chunks. The first loads are issued before the
+  //      query is staged, so that their latency overlaps it; the last
+  //      refills of waves 1..7 load their first window half chunks.
+  ds.prime(a_item, lane);
+  // query fragments (lane l: head l % 16) and gates of the group's heads
+  if (tid == 0) *hl_ready = 0;
+  if (wave == 0) {
+    const S* Q = static_cast<const S*>(a.q) + b * a.qs[0] + (g * a.Hg + col) * a.qs[1] + 8 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) qlds[s * 64 + lane] = col < a.Hg ? frag_load<T>(Q + 32 * s) : frag_zero<T>();
+    if (lane < 48) {
+      const int h = lane & 15, i = lane >> 4;
+      gts[16 * i + h] =
+          h < a.Hg ? to_f32<T>(static_cast<const S*>(a.gates)[b * a.gs[0] + (g * a.Hg + h) * a.gs[1] + i]) : 0.f;
+    }
+  }
+  lds_barrier();
+  reset_state<D>(m, l, acc);
+  ds.run(phase_steps<RING>(nA), a_item, w_item, no_hook, scores, update, lane);
+  l = col_sum4(l);
+
+  // ---- B: merge into the log-sum-exp and gate_cmp * O_cmp (the window's
+  //      first loads stay in flight)
+  // staging done; logits written (to global memory when they are not in LDS)
+  if constexpr (LGL)
+    lds_barrier();
+  else
+    __syncthreads();
   store_partial<D>(parts + wave * SF, m, l, acc, lane);
   lds_barrier();
   if (tid < 16) {
     float M, L;
-    merge_stats(parts, NWV, SF, tid, M, L);
-    hs[4 * tid] = M;
-    hs[4 * tid + 1] = L > 0.f ? gts[tid] / L : 0.f;
+    merge_factors<NWV>(parts, SF, tid, gts[tid], fac, M, L);
     hs[4 * tid + 2] = (nvis > 0 && tid < a.Hg) ? M + fast_log2(L) : INFINITY;
   }
   lds_barrier();
-  for (int e = tid; e < 16 * D; e += NT) {
-    const int h = e / D;
-    res[e] = merge_out<NWV>(parts, SF, h, e, hs[4 * h]) * hs[4 * h + 1];
-  }
+  for (int e = tid; e < 16 * D; e += NT) res[e] = merge_out<NWV>(parts, fac, SF, e / D, e);
 
   // ---- C: block scores
   if (!a.inject) {
-    block_scores(lg, a.NmaxPad, own, a.Hg, hs, sc, tid, NT);
+    block_scores(lg, a.NmaxPad, own, hs, sc, tid, NT);
   }
   lds_barrier();  // sc written; parts read, so the V staging is free again
 
@@ -481,62 +543,33 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     if (lane == 0) __hip_atomic_store(hl_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   // The window is streamed by waves 1..7. When the logits region (free once
-  // the scores are done) can hold their 7 partial states, each wave parks its
-  // state there and moves on to the selected blocks as soon as wave 0 has
-  // published the list, without waiting for the other waves; the window is
-  // merged at the end. Otherwise the window is merged before the selected
-  // blocks.
-  const bool park = LGL && 16 * a.NmaxPad >= (NWV - 1) * SF;
-  {
-    const int nwin = (t - wlo + 32) >> 5;
-    auto desc = [&](int q) { return DItem<T>{Kr, Vr, a.ks[2], a.vs[2], wlo + 32 * q, wlo, t, nullptr}; };
-    reset_state<D>(m, l, acc);
-    if (wave > 0) {
-      DStream<T, D, RING> ds(wave - 1, NWV - 1);
-      ds.prime(nwin, desc, lane);
-      ds.run(nwin, desc, scores, update, lane);
-    }
-    l = col_sum4(l);
-  }
-  if (park) {
-    if (wave > 0) {
-      store_partial<D>(lg_lds + (wave - 1) * SF, m, l, acc, lane);
-      // wait for wave 0's list (it always publishes it)
-      while (__hip_atomic_load(hl_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
-        __builtin_amdgcn_s_sleep(1);
-    }
+  // the scores are done) can hold the 7 window states, each wave parks its
+  // state there and goes on to the selected blocks as soon as wave 0 has
+  // published them, and the window is merged at the end. Otherwise the
+  // window is merged before the selected blocks.
+  reset_state<D>(m, l, acc);
+  if (wave > 0) ds.run(phase_steps<RING>(nW), w_item, no_next, no_hook, scores, update, lane);
+  l = col_sum4(l);
+  if constexpr (PARK) {
+    if (wave > 0) store_partial<D>(lg_lds + (wave - 1) * SF, m, l, acc, lane);
   } else {
-    merge_into<D, NWV>(parts, m, l, acc, gts + 32, hs, res, tid, lane);
+    merge_into<D, NWV>(parts, m, l, acc, gts + 32, fac, res, tid, lane);
   }
 
   // ---- D: selected half blocks
-  {
-    const int nh = *nhl;
-    auto desc = [&](int q) {
-      const int u = hl[q], j = u >> 1;
-      return DItem<T>{Kr, Vr, a.ks[2], a.vs[2], 64 * j + 32 * (u & 1), 64 * j, t, nullptr};
-    };
-    reset_state<D>(m, l, acc);
-    if (nh > 0) {
-      DStream<T, D, RING> ds(wave, NWV);
-      ds.prime(nh, desc, lane);
-      ds.run(nh, desc, scores, update, lane);
-    }
-    l = col_sum4(l);
-  }
-  merge_into<D, NWV>(parts, m, l, acc, gts + 16, hs, res, tid, lane);
-  if (park) {  // the parked window states
+  d_wait();
+  ds.prime(d_item, lane);
+  reset_state<D>(m, l, acc);
+  ds.run(phase_steps<RING>(nD), d_item, no_next, no_hook, scores, update, lane);
+  l = col_sum4(l);
+  merge_into<D, NWV>(parts, m, l, acc, gts + 16, fac, res, tid, lane);
+  if constexpr (PARK) {  // the parked window states
     if (tid < 16) {
       float M, L;
-      merge_stats(lg_lds, NWV - 1, SF, tid, M, L);
-      hs[4 * tid] = M;
-      hs[4 * tid + 1] = L > 0.f ? gts[32 + tid] / L : 0.f;
+      merge_factors<NWV - 1>(lg_lds, SF, tid, gts[32 + tid], fac, M, L);
     }
     lds_barrier();
-    for (int e = tid; e < 16 * D; e += NT) {
-      const int h = e / D;
-      res[e] += merge_out<NWV - 1>(lg_lds, SF, h, e, hs[4 * h]) * hs[4 * h + 1];
-    }
+    for (int e = tid; e < 16 * D; e += NT) res[e] += merge_out<NWV - 1>(lg_lds, fac, SF, e / D, e);
   }
 
   // ---- E: out = gate_cmp O_cmp + gate_slc O_slc + gate_win O_win
@@ -548,7 +581,7 @@ size_t dec_lds_bytes(int NmaxPad, int D, bool bf16, bool logits_lds) {
                           : (D == 64 ? dec_big_bytes<F32, 64>() : dec_big_bytes<F32, 128>());
   const size_t qbytes = (bf16 ? 16 : 32) * static_cast<size_t>(D / 32) * 64;
   return big + qbytes + 16 * static_cast<size_t>(D) * sizeof(float) + NmaxPad * sizeof(float) +
-         kSurvCap * sizeof(uint64_t) + (64 + 64 + 128 + 4) * sizeof(int) + (64 + 48) * sizeof(float) +
+         kSurvCap * sizeof(uint64_t) + (64 + 64 + 128 + 4) * sizeof(int) + (64 + 48 + 16 * kDecWaves) * sizeof(float) +
          (logits_lds ? 16 * static_cast<size_t>(NmaxPad) * sizeof(float) : 0);
 }
 
@@ -556,23 +589,25 @@ static hipError_t record(hipEvent_t* ev, int i, hipStream_t st) {
   return ev != nullptr ? hipEventRecord(ev[i], st) : hipSuccess;
 }
 
-template <class T, class O, int D, bool LGL>
+template <class T, class O, int D, bool LGL, bool PARK>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st, hipEvent_t* ev) {
   constexpr bool kBf16 = sizeof(typename T::storage) == 2;
   constexpr int RING = kBf16 ? 2 : 1;
   const size_t lds = dec_lds_bytes(a.NmaxPad, D, kBf16, LGL);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec<T, O, D, RING, LGL>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec<T, O, D, RING, LGL, PARK>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
   if ((e = record(ev, 0, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_dec<T, O, D, RING, LGL>), dim3(a.B * a.G), dim3(64 * kDecWaves), lds, st, a);
+  hipLaunchKernelGGL((k_dec<T, O, D, RING, LGL, PARK>), dim3(a.B * a.G), dim3(64 * kDecWaves), lds, st, a);
   if ((e = record(ev, 1, st)) != hipSuccess) return e;
   return hipGetLastError();
 }
 
 template <class T, class O, int D>
 static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t st, hipEvent_t* ev) {
-  return a.logits_lds ? launch_decode_t<T, O, D, true>(a, st, ev) : launch_decode_t<T, O, D, false>(a, st, ev);
+  if (!a.logits_lds) return launch_decode_t<T, O, D, false, false>(a, st, ev);
+  const bool park = 16 * static_cast<size_t>(a.NmaxPad) >= (kDecWaves - 1) * static_cast<size_t>(dec_slot_floats(D));
+  return park ? launch_decode_t<T, O, D, true, true>(a, st, ev) : launch_decode_t<T, O, D, true, false>(a, st, ev);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool in_bf16, bool out_bf16, hipStream_t st,
