@@ -20,14 +20,17 @@
 // K rows feed the S^T = K Q^T product straight from the caches. V rows are
 // written to LDS row-major (padded so that reads do not conflict) and each
 // lane gathers the 8 keys of its V^T operand fragment from there.
+#include <type_traits>
+
 #include "nsa_device.h"
 #include "nsa_internal.h"
 #include "nsa_topk.h"
 
 namespace nsa {
 
-// floats per partial state: m[16], l[16], O[16][D]
-__host__ __device__ constexpr int dec_slot_floats(int D) { return 32 + 16 * D; }
+// floats per partial state: m[16], l[16], O[16][D + 4] (rows padded so that
+// the 16 heads' rows start in different LDS banks)
+__host__ __device__ constexpr int dec_slot_floats(int D) { return 32 + 16 * (D + 4); }
 
 // One wave's registers for 32 keys: K rows as A operands of two key tiles,
 // V rows as 8-element vectors (which row and columns a lane holds: v_row,
@@ -198,6 +201,12 @@ __device__ __forceinline__ void dhalf_update(f32x4 (&st)[2], const DItem<T>& it,
   wave_lds_sync();
 }
 
+// Passed as a phase's "next" when nothing follows it in the same ring.
+struct NoRefill {
+  template <class T>
+  __device__ DItem<T> operator()(int) const;  // never called
+};
+
 // A wave's half chunks streamed through a ring of RING register buffers.
 // A phase is a count N of steps (a multiple of RING) and item(k), the k-th
 // step's half chunk; steps past the wave's real items are empty items (an
@@ -219,10 +228,10 @@ struct DStream {
     }
   }
   // One round: steps k0 .. k0 + RING - 1. scores(c, it, st) consumes buffer
-  // c into st; update(st, it) finishes the step. Each buffer is refilled
-  // with refill(r) between the two, so its loads are in flight during the
-  // softmax and the P.V product.
-  template <class Item, class Refill, class Scores, class Update>
+  // c into st; update(st, it) finishes the step. With REFILL, each buffer is
+  // refilled with refill(r) between the two, so its loads are in flight
+  // during the softmax and the P.V product.
+  template <bool REFILL, class Item, class Refill, class Scores, class Update>
   __device__ __forceinline__ void round(int k0, Item item, Refill refill, Scores scores, Update update,
                                         int lane) {
 #pragma unroll
@@ -230,22 +239,26 @@ struct DStream {
       const DItem<T> it = item(k0 + r);
       f32x4 st[2];
       scores(ring[r], it, st);
-      __builtin_amdgcn_sched_barrier(0);
-      dhalf_load<T, D>(ring[r], refill(r), lane);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (REFILL) {
+        __builtin_amdgcn_sched_barrier(0);
+        dhalf_load<T, D>(ring[r], refill(r), lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       update(st, it);
     }
   }
   // A phase of N steps. All rounds but the last refill from this phase; the
-  // last round, after hook(), refills with the next phase's first steps.
+  // last round, after hook(), refills with the next phase's first steps
+  // (next(r)), or nothing when next is no_refill: then the phase ends with no
+  // loads in flight.
   template <class Item, class Next, class Hook, class Scores, class Update>
   __device__ __forceinline__ void run(int N, Item item, Next next, Hook hook, Scores scores, Update update,
                                       int lane) {
 #pragma unroll 1
     for (int k0 = 0; k0 < N - RING; k0 += RING)
-      round(k0, item, [&](int r) { return item(k0 + r + RING); }, scores, update, lane);
+      round<true>(k0, item, [&](int r) { return item(k0 + r + RING); }, scores, update, lane);
     hook();
-    round(N - RING, item, next, scores, update, lane);
+    round<!std::is_same<Next, NoRefill>::value>(N - RING, item, next, scores, update, lane);
   }
 };
 
@@ -265,7 +278,7 @@ __device__ __forceinline__ DItem<T> empty_item(DItem<T> it) {
 }
 
 // Stores a wave's partial state (m per column, l summed over the column's
-// lanes, O^T accumulators) as m[16], l[16], O[16][D] at dst.
+// lanes, O^T accumulators) as m[16], l[16], O[16][D + 4] at dst.
 template <int D>
 __device__ __forceinline__ void store_partial(float* dst, float m, float l, const f32x4 (&acc)[D / 16],
                                               int lane) {
@@ -276,7 +289,7 @@ __device__ __forceinline__ void store_partial(float* dst, float m, float l, cons
   }
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
-    *reinterpret_cast<f32x4*>(dst + 32 + col * D + 16 * dt + 4 * grp) = acc[dt];
+    *reinterpret_cast<f32x4*>(dst + 32 + col * (D + 4) + 16 * dt + 4 * grp) = acc[dt];
 }
 
 // Merge factors of head h over CNT partial states (stride SF floats, one
@@ -304,12 +317,13 @@ __device__ __forceinline__ void merge_factors(const float* p, int SF, int h, flo
   for (int w = 0; w < CNT; ++w) fac[w * 16 + h] = mw[w] * r;
 }
 
-// Element e (head h) of the merged, gated output.
-template <int CNT>
-__device__ __forceinline__ float merge_out(const float* p, const float* fac, int SF, int h, int e) {
+// Element e = h D + d (head h) of the merged, gated output.
+template <int CNT, int D>
+__device__ __forceinline__ float merge_out(const float* p, const float* fac, int SF, int e) {
+  const int h = e / D, off = 32 + e + 4 * h;  // O[h][d] of a partial state
   float o = 0.f;
 #pragma unroll
-  for (int w = 0; w < CNT; ++w) o += p[w * SF + 32 + e] * fac[w * 16 + h];
+  for (int w = 0; w < CNT; ++w) o += p[w * SF + off] * fac[w * 16 + h];
   return o;
 }
 
@@ -365,7 +379,7 @@ __device__ __forceinline__ void merge_into(float* parts, float m, float l, const
     merge_factors<NWV>(parts, SF, tid, gate[tid], fac, M, L);
   }
   lds_barrier();
-  for (int e = tid; e < 16 * D; e += NT) res[e] += merge_out<NWV>(parts, fac, SF, e / D, e);
+  for (int e = tid; e < 16 * D; e += NT) res[e] += merge_out<NWV, D>(parts, fac, SF, e);
   lds_barrier();
 }
 
@@ -469,7 +483,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
       nD = wave < nh ? (nh - 1 - wave) / NWV + 1 : 0;
     }
   };
-  auto no_next = [&](int) { return none; };
+  const NoRefill no_next;
   auto no_hook = [&]() {};
   DStream<T, D, RING> ds;
 
@@ -509,7 +523,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     hs[4 * tid + 2] = (nvis > 0 && tid < a.Hg) ? M + fast_log2(L) : INFINITY;
   }
   lds_barrier();
-  for (int e = tid; e < 16 * D; e += NT) res[e] = merge_out<NWV>(parts, fac, SF, e / D, e);
+  for (int e = tid; e < 16 * D; e += NT) res[e] = merge_out<NWV, D>(parts, fac, SF, e);
 
   // ---- C: block scores
   if (!a.inject) {
@@ -569,7 +583,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
       merge_factors<NWV - 1>(lg_lds, SF, tid, gts[32 + tid], fac, M, L);
     }
     lds_barrier();
-    for (int e = tid; e < 16 * D; e += NT) res[e] += merge_out<NWV - 1>(lg_lds, fac, SF, e / D, e);
+    for (int e = tid; e < 16 * D; e += NT) res[e] += merge_out<NWV - 1, D>(lg_lds, fac, SF, e);
   }
 
   // ---- E: out = gate_cmp O_cmp + gate_slc O_slc + gate_win O_win
