@@ -413,7 +413,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   float* hs = reinterpret_cast<float*>(nhl + 4);  // per head: 4 floats
   float* gts = hs + 64;                           // [3][16] gates
   float* fac = gts + 48;                          // [NWV][16] merge factors
-  float* lg_lds = fac + 16 * NWV;                 // [16][NmaxPad] logits, if LGL
+  float* lg_lds = fac + 16 * NWV;                 // [16][NmaxPad + 4] logits, if LGL
 
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: phase counts and bases stay scalar
@@ -437,6 +437,9 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   const S* Vr = static_cast<const S*>(a.vcache) + b * a.vs[0] + g * a.vs[1];
   // compressed logits, row h = head: in LDS when they fit, else in the workspace
   float* lg = LGL ? lg_lds : a.logits + static_cast<int64_t>(bg) * 16 * a.NmaxPad;
+  // row stride of the logits: in LDS padded so that the heads' rows start in
+  // different banks
+  const int ld = LGL ? a.NmaxPad + 4 : a.NmaxPad;
 
   float m, l;
   f32x4 acc[DT];
@@ -453,7 +456,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   const DItem<T> none{Kr, Vr, a.ks[2], a.vs[2], 0, 1, 0, nullptr};
   const int ncmp = (nvis + 31) >> 5;
   const int nA = wave < ncmp ? (ncmp - 1 - wave) / NWV + 1 : 0;
-  float* lrow = a.inject ? nullptr : lg + col * a.NmaxPad;
+  float* lrow = a.inject ? nullptr : lg + col * ld;
   auto a_real = [&](int q) {
     return DItem<T>{KCr, VCr, a.kcs[2], a.vcs[2], 32 * q, 0, nvis - 1, lrow != nullptr ? lrow + 32 * q : nullptr};
   };
@@ -527,7 +530,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
 
   // ---- C: block scores
   if (!a.inject) {
-    block_scores(lg, a.NmaxPad, own, hs, sc, tid, NT);
+    block_scores(lg, ld, own, hs, sc, tid, NT);
   }
   lds_barrier();  // sc written; parts read, so the V staging is free again
 
@@ -596,7 +599,7 @@ size_t dec_lds_bytes(int NmaxPad, int D, bool bf16, bool logits_lds) {
   const size_t qbytes = (bf16 ? 16 : 32) * static_cast<size_t>(D / 32) * 64;
   return big + qbytes + 16 * static_cast<size_t>(D) * sizeof(float) + NmaxPad * sizeof(float) +
          kSurvCap * sizeof(uint64_t) + (64 + 64 + 128 + 4) * sizeof(int) + (64 + 48 + 16 * kDecWaves) * sizeof(float) +
-         (logits_lds ? 16 * static_cast<size_t>(NmaxPad) * sizeof(float) : 0);
+         (logits_lds ? 16 * static_cast<size_t>(NmaxPad + 4) * sizeof(float) : 0);
 }
 
 static hipError_t record(hipEvent_t* ev, int i, hipStream_t st) {
@@ -620,7 +623,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st, hipEvent_
 template <class T, class O, int D>
 static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t st, hipEvent_t* ev) {
   if (!a.logits_lds) return launch_decode_t<T, O, D, false, false>(a, st, ev);
-  const bool park = 16 * static_cast<size_t>(a.NmaxPad) >= (kDecWaves - 1) * static_cast<size_t>(dec_slot_floats(D));
+  const bool park =
+      16 * static_cast<size_t>(a.NmaxPad + 4) >= (kDecWaves - 1) * static_cast<size_t>(dec_slot_floats(D));
   return park ? launch_decode_t<T, O, D, true, true>(a, st, ev) : launch_decode_t<T, O, D, true, false>(a, st, ev);
 }
 
