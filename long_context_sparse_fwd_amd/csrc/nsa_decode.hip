@@ -317,13 +317,14 @@ __device__ __forceinline__ void merge_factors(const float* p, int SF, int h, flo
   for (int w = 0; w < CNT; ++w) fac[w * 16 + h] = mw[w] * r;
 }
 
-// Element e = h D + d (head h) of the merged, gated output.
+// Elements e .. e + 3 (e = h D + d, d a multiple of 4; head h) of the
+// merged, gated output.
 template <int CNT, int D>
-__device__ __forceinline__ float merge_out(const float* p, const float* fac, int SF, int e) {
+__device__ __forceinline__ f32x4 merge_out4(const float* p, const float* fac, int SF, int e) {
   const int h = e / D, off = 32 + e + 4 * h;  // O[h][d] of a partial state
-  float o = 0.f;
+  f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int w = 0; w < CNT; ++w) o += p[w * SF + off] * fac[w * 16 + h];
+  for (int w = 0; w < CNT; ++w) o += *reinterpret_cast<const f32x4*>(p + w * SF + off) * fac[w * 16 + h];
   return o;
 }
 
@@ -364,22 +365,37 @@ __device__ __forceinline__ void block_scores(P lg, int ld, int own, const float*
   }
 }
 
+// Per-wave partial states live in the wave's own V staging (stride PS
+// floats), so a wave can store its state without waiting for the others.
+template <class T, int D>
+__host__ __device__ constexpr int dec_part_stride() {
+  return static_cast<int>(VStage<T, D>::kBytes / sizeof(float));
+}
+
+// Waits until the LDS counter *flag equals v (set by other waves of the
+// workgroup with release stores or adds).
+__device__ __forceinline__ void lds_wait_eq(int* flag, int v) {
+  while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != v) __builtin_amdgcn_s_sleep(1);
+}
+
 // Merges the per-wave states (m, l, acc) of one branch through LDS and adds
-// gate[h] * O of the branch to res[16][D] (LDS). Begins and ends with a
-// workgroup barrier, so parts may alias the V staging.
-template <int D, int NWV>
+// gate[h] * O of the branch to res[16][D] (LDS). Thread tid owns the
+// elements 4 tid .. 4 tid + 3 of res in every merge and in the output
+// store, so res needs no barrier of its own. Ends with a workgroup barrier, so the V staging may be
+// written again afterwards.
+template <class T, int D, int NWV>
 __device__ __forceinline__ void merge_into(float* parts, float m, float l, const f32x4 (&acc)[D / 16],
                                            const float* gate, float* fac, float* res, int tid, int lane) {
-  constexpr int SF = dec_slot_floats(D), NT = 64 * NWV;
-  lds_barrier();
-  store_partial<D>(parts + (tid >> 6) * SF, m, l, acc, lane);
+  constexpr int PS = dec_part_stride<T, D>();
+  store_partial<D>(parts + (tid >> 6) * PS, m, l, acc, lane);
   lds_barrier();
   if (tid < 16) {
     float M, L;
-    merge_factors<NWV>(parts, SF, tid, gate[tid], fac, M, L);
+    merge_factors<NWV>(parts, PS, tid, gate[tid], fac, M, L);
   }
   lds_barrier();
-  for (int e = tid; e < 16 * D; e += NT) res[e] += merge_out<NWV, D>(parts, fac, SF, e);
+  if (4 * tid < 16 * D)
+    *reinterpret_cast<f32x4*>(res + 4 * tid) += merge_out4<NWV, D>(parts, fac, PS, 4 * tid);
   lds_barrier();
 }
 
@@ -387,9 +403,8 @@ constexpr int kDecWaves = 8;
 
 template <class T, int D>
 __host__ __device__ constexpr size_t dec_big_bytes() {
-  constexpr size_t stage = static_cast<size_t>(kDecWaves) * VStage<T, D>::kBytes;
-  constexpr size_t parts = static_cast<size_t>(kDecWaves) * dec_slot_floats(D) * sizeof(float);
-  return stage > parts ? stage : parts;
+  static_assert(dec_part_stride<T, D>() >= dec_slot_floats(D), "a partial state must fit a wave's V staging");
+  return static_cast<size_t>(kDecWaves) * VStage<T, D>::kBytes;
 }
 
 // LGL: the compressed logits stay in LDS. PARK (requires LGL): the logits
@@ -399,8 +414,9 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   using S = typename T::storage;
   using SO = typename O::storage;
   constexpr int NWV = kDecWaves, NT = 64 * NWV, SF = dec_slot_floats(D), DT = D / 16;
+  constexpr int PS = dec_part_stride<T, D>();
   extern __shared__ __align__(16) unsigned char smem[];
-  float* parts = reinterpret_cast<float*>(smem);  // aliases the V staging
+  float* parts = reinterpret_cast<float*>(smem);  // wave w's state in its V staging, at w * PS
   Frag<T>* qlds = reinterpret_cast<Frag<T>*>(smem + dec_big_bytes<T, D>());  // [D/32][64]
   float* res = reinterpret_cast<float*>(qlds + D / 32 * 64);                  // [16][D] output
   float* sc = res + 16 * D;
@@ -410,10 +426,12 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   int* hl = selo + 64;                            // usable selected half blocks: 2 j + half
   int* nhl = hl + 128;                            // their count
   int* hl_ready = nhl + 1;                        // set by wave 0 once hl and nhl are written
+  int* parked = nhl + 2;                          // window states parked so far
   float* hs = reinterpret_cast<float*>(nhl + 4);  // per head: 4 floats
   float* gts = hs + 64;                           // [3][16] gates
   float* fac = gts + 48;                          // [NWV][16] merge factors
-  float* lg_lds = fac + 16 * NWV;                 // [16][NmaxPad + 4] logits, if LGL
+  float* facw = fac + 16 * NWV;                   // [NWV - 1][16] merge factors of the parked window states
+  float* lg_lds = facw + 16 * NWV;                // [16][NmaxPad + 4] logits, if LGL
 
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: phase counts and bases stay scalar
@@ -495,7 +513,10 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   //      refills of waves 1..7 load their first window half chunks.
   ds.prime(a_item, lane);
   // query fragments (lane l: head l % 16) and gates of the group's heads
-  if (tid == 0) *hl_ready = 0;
+  if (tid == 0) {
+    *hl_ready = 0;
+    *parked = 0;
+  }
   if (wave == 0) {
     const S* Q = static_cast<const S*>(a.q) + b * a.qs[0] + (g * a.Hg + col) * a.qs[1] + 8 * (lane >> 4);
 #pragma unroll
@@ -513,20 +534,20 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
 
   // ---- B: merge into the log-sum-exp and gate_cmp * O_cmp (the window's
   //      first loads stay in flight)
-  // staging done; logits written (to global memory when they are not in LDS)
+  store_partial<D>(parts + wave * PS, m, l, acc, lane);
+  // partial states and logits written (the logits to global memory when they
+  // are not in LDS)
   if constexpr (LGL)
     lds_barrier();
   else
     __syncthreads();
-  store_partial<D>(parts + wave * SF, m, l, acc, lane);
-  lds_barrier();
   if (tid < 16) {
     float M, L;
-    merge_factors<NWV>(parts, SF, tid, gts[tid], fac, M, L);
+    merge_factors<NWV>(parts, PS, tid, gts[tid], fac, M, L);
     hs[4 * tid + 2] = (nvis > 0 && tid < a.Hg) ? M + fast_log2(L) : INFINITY;
   }
   lds_barrier();
-  for (int e = tid; e < 16 * D; e += NT) res[e] = merge_out<NWV, D>(parts, fac, SF, e);
+  if (4 * tid < 16 * D) *reinterpret_cast<f32x4*>(res + 4 * tid) = merge_out4<NWV, D>(parts, fac, PS, 4 * tid);
 
   // ---- C: block scores
   if (!a.inject) {
@@ -568,9 +589,13 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   if (wave > 0) ds.run(phase_steps<RING>(nW), w_item, no_next, no_hook, scores, update, lane);
   l = col_sum4(l);
   if constexpr (PARK) {
-    if (wave > 0) store_partial<D>(lg_lds + (wave - 1) * SF, m, l, acc, lane);
+    if (wave > 0) {
+      store_partial<D>(lg_lds + (wave - 1) * SF, m, l, acc, lane);
+      wave_lds_sync();
+      if (lane == 0) __hip_atomic_fetch_add(parked, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
   } else {
-    merge_into<D, NWV>(parts, m, l, acc, gts + 32, fac, res, tid, lane);
+    merge_into<T, D, NWV>(parts, m, l, acc, gts + 32, fac, res, tid, lane);
   }
 
   // ---- D: selected half blocks
@@ -579,18 +604,38 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   reset_state<D>(m, l, acc);
   ds.run(phase_steps<RING>(nD), d_item, no_next, no_hook, scores, update, lane);
   l = col_sum4(l);
-  merge_into<D, NWV>(parts, m, l, acc, gts + 16, fac, res, tid, lane);
-  if constexpr (PARK) {  // the parked window states
-    if (tid < 16) {
-      float M, L;
-      merge_factors<NWV - 1>(lg_lds, SF, tid, gts[32 + tid], fac, M, L);
+  // The window states were parked before the selected blocks; wave 0, whose
+  // share of them ends first, takes their merge factors while the other
+  // waves finish.
+  if constexpr (PARK) {
+    if (wave == 0) {
+      lds_wait_eq(parked, NWV - 1);
+      if (lane < 16) {
+        float M, L;
+        merge_factors<NWV - 1>(lg_lds, SF, lane, gts[32 + lane], facw, M, L);
+      }
     }
-    lds_barrier();
-    for (int e = tid; e < 16 * D; e += NT) res[e] += merge_out<NWV - 1, D>(lg_lds, fac, SF, e);
+  }
+  // ---- merge of the selected-block states (and of the parked window states)
+  store_partial<D>(parts + wave * PS, m, l, acc, lane);
+  lds_barrier();
+  if (tid < 16) {
+    float M, L;
+    merge_factors<NWV>(parts, PS, tid, gts[16 + tid], fac, M, L);
+  }
+  lds_barrier();
+  f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (4 * tid < 16 * D) {
+    o = *reinterpret_cast<const f32x4*>(res + 4 * tid) + merge_out4<NWV, D>(parts, fac, PS, 4 * tid);
+    if constexpr (PARK) o += merge_out4<NWV - 1, D>(lg_lds, facw, SF, 4 * tid);
   }
 
   // ---- E: out = gate_cmp O_cmp + gate_slc O_slc + gate_win O_win
-  for (int e = tid; e < a.Hg * D; e += NT) OUT[(g * a.Hg + e / D) * a.os[1] + e % D] = from_f32<O>(res[e]);
+  if (4 * tid < a.Hg * D) {
+    SO* o4 = OUT + (g * a.Hg + 4 * tid / D) * a.os[1] + 4 * tid % D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o4[i] = from_f32<O>(o[i]);
+  }
 }
 
 size_t dec_lds_bytes(int NmaxPad, int D, bool bf16, bool logits_lds) {
@@ -598,7 +643,7 @@ size_t dec_lds_bytes(int NmaxPad, int D, bool bf16, bool logits_lds) {
                           : (D == 64 ? dec_big_bytes<F32, 64>() : dec_big_bytes<F32, 128>());
   const size_t qbytes = (bf16 ? 16 : 32) * static_cast<size_t>(D / 32) * 64;
   return big + qbytes + 16 * static_cast<size_t>(D) * sizeof(float) + NmaxPad * sizeof(float) +
-         kSurvCap * sizeof(uint64_t) + (64 + 64 + 128 + 4) * sizeof(int) + (64 + 48 + 16 * kDecWaves) * sizeof(float) +
+         kSurvCap * sizeof(uint64_t) + (64 + 64 + 128 + 4) * sizeof(int) + (64 + 48 + 32 * kDecWaves) * sizeof(float) +
          (logits_lds ? 16 * static_cast<size_t>(NmaxPad + 4) * sizeof(float) : 0);
 }
 

@@ -13,11 +13,13 @@
 //  2. theta = the (n-1)-th largest of the 64 per-lane maxima (bitonic sort
 //     across lanes). At least n-1 candidates are >= theta, so every member of
 //     the answer is >= theta;
-//  3. the candidates >= theta (typically ~20) are compacted into LDS; up to
-//     64 of them are sorted across the lanes (one key per lane) and the first
-//     n-1 are the answer. With 65..kSurvCap survivors each is ranked by
-//     counting larger keys; with more (heavy ties), n-1 rounds of wave-wide
-//     argmax over all candidates are used instead;
+//  3. the candidates >= theta (typically ~20) are compacted into LDS in
+//     ascending block order. Up to 64 of them sit one per lane and each is
+//     ranked by counting the larger keys; those of rank < n-1 are the
+//     answer, already ascending, and the own block (the largest index) goes
+//     last. With 65..kSurvCap survivors the ranks are counted the same way
+//     from LDS; with more (heavy ties), n-1 rounds of wave-wide argmax over
+//     all candidates are used instead; in both cases
 //  4. the n chosen indices are sorted ascending across the lanes.
 // The cross-lane sorts are bitonic networks whose exchanges inside 16-lane
 // rows are DPP moves; only the 16- and 32-lane distances go through the LDS
@@ -91,33 +93,61 @@ __device__ inline void topk_wave(const float* sc, int own, int n, int32_t* out, 
     return;
   }
   const int R = (own + 63) >> 6;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // Keys of blocks lane + 64 (r0 + i), i < 8; the reads are unconditional
+  // (indices clamped to own - 1) and independent, so they issue together.
+  auto keys8 = [&](int r0, uint32_t (&k)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = lane + 64 * (r0 + i);
+      const uint32_t bits = __float_as_uint(sc[min(j, own - 1)]);
+      k[i] = j < own ? (bits | 0x80000000u) : 0u;
+    }
+  };
   uint32_t lmax = 0;
-  for (int r = 0; r < R; ++r) {
-    const int j = lane + 64 * r;
-    if (j < own) lmax = max(lmax, __float_as_uint(sc[j]) | 0x80000000u);
+  for (int r0 = 0; r0 < R; r0 += 8) {
+    uint32_t k[8];
+    keys8(r0, k);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lmax = max(lmax, k[i]);
   }
   // theta: the (n-1)-th largest lane maximum
   const uint32_t theta = __builtin_amdgcn_readlane(wave_sort<true>(lmax, lane), n1 - 1);
 
+  // the candidates >= theta, compacted into surv in ascending block order
   int cnt = 0;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int r = 0; r < R; ++r) {
-    const int j = lane + 64 * r;
-    const uint32_t key = (j < own) ? (__float_as_uint(sc[j]) | 0x80000000u) : 0u;
-    const bool f = (j < own) && key >= theta;
-    const uint64_t bal = __ballot(f);
-    const int pos = cnt + __popcll(bal & below);
-    if (f && pos < kSurvCap)
-      surv[pos] = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - j);
-    cnt += __popcll(bal);
+  for (int r0 = 0; r0 < R; r0 += 8) {
+    uint32_t k[8];
+    keys8(r0, k);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool f = k[i] >= theta && k[i] != 0u;
+      const uint64_t bal = __ballot(f);
+      const int pos = cnt + __popcll(bal & below);
+      if (f && pos < kSurvCap)
+        surv[pos] = (static_cast<uint64_t>(k[i]) << 32) |
+                    static_cast<uint32_t>(0xFFFFFFFFu - (lane + 64 * (r0 + i)));
+      cnt += __popcll(bal);
+    }
   }
   wave_lds_sync();
-  uint32_t jsel;  // this lane's chosen block (lanes < n), 0xFFFFFFFF elsewhere
   if (cnt <= 64) {
-    // one survivor per lane: sort the keys, the first n-1 lanes hold the answer
-    const uint64_t key = wave_sort<true>(lane < cnt ? surv[lane] : uint64_t{0}, lane);
-    jsel = lane < n1 ? 0xFFFFFFFFu - static_cast<uint32_t>(key) : 0xFFFFFFFFu;
-  } else {
+    // one survivor per lane; its rank = the number of larger keys (keys are
+    // distinct). The n-1 of rank < n-1, taken in surv order, are already
+    // ascending; the own block, larger than all of them, comes last.
+    const uint64_t mine = lane < cnt ? surv[lane] : uint64_t{0};
+    int rank = 0;
+#pragma unroll 4
+    for (int k = 0; k < cnt; ++k) rank += surv[k] > mine ? 1 : 0;
+    const bool s = lane < cnt && rank < n1;
+    const int pos = __popcll(__ballot(s) & below);
+    if (s) out[pos] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(mine));
+    if (lane == 0) out[n1] = own;
+    wave_lds_sync();
+    return;
+  }
+  uint32_t jsel;  // this lane's chosen block (lanes < n), 0xFFFFFFFF elsewhere
+  {
     if (cnt <= kSurvCap) {
       for (int i = lane; i < cnt; i += 64) {
         const uint64_t mine = surv[i];
@@ -129,14 +159,11 @@ __device__ inline void topk_wave(const float* sc, int own, int n, int32_t* out, 
       uint64_t prev = ~0ull;
       for (int rr = 0; rr < n1; ++rr) {
         uint64_t best = 0;
-        for (int r = 0; r < R; ++r) {
-          const int j = lane + 64 * r;
-          if (j < own) {
-            const uint64_t k64 =
-                (static_cast<uint64_t>(__float_as_uint(sc[j]) | 0x80000000u) << 32) |
-                static_cast<uint32_t>(0xFFFFFFFFu - j);
-            if (k64 < prev && k64 > best) best = k64;
-          }
+        for (int j = lane; j < own; j += 64) {
+          const uint64_t k64 =
+              (static_cast<uint64_t>(__float_as_uint(sc[j]) | 0x80000000u) << 32) |
+              static_cast<uint32_t>(0xFFFFFFFFu - j);
+          if (k64 < prev && k64 > best) best = k64;
         }
 #pragma unroll
         for (int m = 32; m > 0; m >>= 1) {
