@@ -20,8 +20,6 @@
 // K rows feed the S^T = K Q^T product straight from the caches. V rows are
 // written to LDS row-major (padded so that reads do not conflict) and each
 // lane gathers the 8 keys of its V^T operand fragment from there.
-#include <type_traits>
-
 #include "nsa_device.h"
 #include "nsa_internal.h"
 #include "nsa_topk.h"
@@ -201,21 +199,15 @@ __device__ __forceinline__ void dhalf_update(f32x4 (&st)[2], const DItem<T>& it,
   wave_lds_sync();
 }
 
-// Passed as a phase's "next" when nothing follows it in the same ring.
-struct NoRefill {
-  template <class T>
-  __device__ DItem<T> operator()(int) const;  // never called
-};
-
 // A wave's half chunks streamed through a ring of RING register buffers.
-// A phase is a count N of steps (a multiple of RING) and item(k), the k-th
-// step's half chunk; steps past the wave's real items are empty items (an
-// empty key range over rows the wave has just read, so the reload hits the
-// caches), which keeps every phase's loop free of conditional loads: the
-// number of loads in flight is the same on every path, so each step waits
-// only for its own buffer. Every buffer is refilled as soon as it is
-// consumed; the refills of a phase's last round load the first steps of the
-// next phase (next(k)), so the ring never drains between phases.
+// A phase is a count N of steps (a multiple of RING, at least RING) and
+// item(k), the k-th step's half chunk; steps past the wave's real items are
+// empty items (an empty key range over rows the wave has just read, so the
+// reload hits the caches). All rounds but the last refill each buffer as
+// soon as it is consumed, unconditionally: the number of loads in flight is
+// then the same on every path, so each step waits only for its own buffer.
+// The last round refills nothing, so a phase ends with no loads in flight;
+// the next phase's ring is primed (prime()) where it can overlap other work.
 template <class T, int D, int RING>
 struct DStream {
   DHalf<T, D> ring[RING];
@@ -229,11 +221,10 @@ struct DStream {
   }
   // One round: steps k0 .. k0 + RING - 1. scores(c, it, st) consumes buffer
   // c into st; update(st, it) finishes the step. With REFILL, each buffer is
-  // refilled with refill(r) between the two, so its loads are in flight
-  // during the softmax and the P.V product.
-  template <bool REFILL, class Item, class Refill, class Scores, class Update>
-  __device__ __forceinline__ void round(int k0, Item item, Refill refill, Scores scores, Update update,
-                                        int lane) {
+  // refilled with step k0 + r + RING between the two, so its loads are in
+  // flight during the softmax and the P.V product.
+  template <bool REFILL, class Item, class Scores, class Update>
+  __device__ __forceinline__ void round(int k0, Item item, Scores scores, Update update, int lane) {
 #pragma unroll
     for (int r = 0; r < RING; ++r) {
       const DItem<T> it = item(k0 + r);
@@ -241,24 +232,17 @@ struct DStream {
       scores(ring[r], it, st);
       if constexpr (REFILL) {
         __builtin_amdgcn_sched_barrier(0);
-        dhalf_load<T, D>(ring[r], refill(r), lane);
+        dhalf_load<T, D>(ring[r], item(k0 + r + RING), lane);
         __builtin_amdgcn_sched_barrier(0);
       }
       update(st, it);
     }
   }
-  // A phase of N steps. All rounds but the last refill from this phase; the
-  // last round, after hook(), refills with the next phase's first steps
-  // (next(r)), or nothing when next is no_refill: then the phase ends with no
-  // loads in flight.
-  template <class Item, class Next, class Hook, class Scores, class Update>
-  __device__ __forceinline__ void run(int N, Item item, Next next, Hook hook, Scores scores, Update update,
-                                      int lane) {
+  template <class Item, class Scores, class Update>
+  __device__ __forceinline__ void run(int N, Item item, Scores scores, Update update, int lane) {
 #pragma unroll 1
-    for (int k0 = 0; k0 < N - RING; k0 += RING)
-      round<true>(k0, item, [&](int r) { return item(k0 + r + RING); }, scores, update, lane);
-    hook();
-    round<!std::is_same<Next, NoRefill>::value>(N - RING, item, next, scores, update, lane);
+    for (int k0 = 0; k0 < N - RING; k0 += RING) round<true>(k0, item, scores, update, lane);
+    round<false>(N - RING, item, scores, update, lane);
   }
 };
 
@@ -504,13 +488,10 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
       nD = wave < nh ? (nh - 1 - wave) / NWV + 1 : 0;
     }
   };
-  const NoRefill no_next;
-  auto no_hook = [&]() {};
   DStream<T, D, RING> ds;
 
   // ---- A: compressed half chunks. The first loads are issued before the
-  //      query is staged, so that their latency overlaps it; the last
-  //      refills of waves 1..7 load their first window half chunks.
+  //      query is staged, so that their latency overlaps it.
   ds.prime(a_item, lane);
   // query fragments (lane l: head l % 16) and gates of the group's heads
   if (tid == 0) {
@@ -529,11 +510,10 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   }
   lds_barrier();
   reset_state<D>(m, l, acc);
-  ds.run(phase_steps<RING>(nA), a_item, w_item, no_hook, scores, update, lane);
+  ds.run(phase_steps<RING>(nA), a_item, scores, update, lane);
   l = col_sum4(l);
 
-  // ---- B: merge into the log-sum-exp and gate_cmp * O_cmp (the window's
-  //      first loads stay in flight)
+  // ---- B: merge into the log-sum-exp and gate_cmp * O_cmp
   store_partial<D>(parts + wave * PS, m, l, acc, lane);
   // partial states and logits written (the logits to global memory when they
   // are not in LDS)
@@ -554,6 +534,8 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     block_scores(lg, ld, own, hs, sc, tid, NT);
   }
   lds_barrier();  // sc written; parts read, so the V staging is free again
+  // waves 1..7 issue their first window loads; their streams cover the top-k
+  if (wave > 0) ds.prime(w_item, lane);
 
   // ---- C': wave 0 selects and lists the usable half blocks while the other
   //      waves stream the sliding window
@@ -586,7 +568,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   // published them, and the window is merged at the end. Otherwise the
   // window is merged before the selected blocks.
   reset_state<D>(m, l, acc);
-  if (wave > 0) ds.run(phase_steps<RING>(nW), w_item, no_next, no_hook, scores, update, lane);
+  if (wave > 0) ds.run(phase_steps<RING>(nW), w_item, scores, update, lane);
   l = col_sum4(l);
   if constexpr (PARK) {
     if (wave > 0) {
@@ -602,7 +584,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   d_wait();
   ds.prime(d_item, lane);
   reset_state<D>(m, l, acc);
-  ds.run(phase_steps<RING>(nD), d_item, no_next, no_hook, scores, update, lane);
+  ds.run(phase_steps<RING>(nD), d_item, scores, update, lane);
   l = col_sum4(l);
   // The window states were parked before the selected blocks; wave 0, whose
   // share of them ends first, takes their merge factors while the other
