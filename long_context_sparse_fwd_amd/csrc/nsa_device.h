@@ -214,16 +214,26 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
-__device__ __forceinline__ float xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+// The value of lane l ^ 16 / l ^ 32, from the gfx950 lane swaps (no LDS):
+// swapping a value with itself leaves r[0] holding the even rows (resp. the
+// low half) twice and r[1] the odd rows (the high half) twice.
+__device__ __forceinline__ float xor16_f(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((__lane_id() & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32_f(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((__lane_id() & 32) ? r[0] : r[1]);
+}
 
 // Reductions over the four lanes l, l^16, l^32, l^48 (same column, all keys).
 __device__ __forceinline__ float col_max4(float v) {
-  v = fmaxf(v, xor_f(v, 16));
-  return fmaxf(v, xor_f(v, 32));
+  v = fmaxf(v, xor16_f(v));
+  return fmaxf(v, xor32_f(v));
 }
 __device__ __forceinline__ float col_sum4(float v) {
-  v += xor_f(v, 16);
-  return v + xor_f(v, 32);
+  v += xor16_f(v);
+  return v + xor32_f(v);
 }
 
 // Orders this wave's LDS accesses before the following ones.
@@ -252,12 +262,14 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 template <class T, int DT, bool MASK>
 __device__ __forceinline__ Frag<T> online_probs(f32x4 (&st)[2], int kbase, int klo, int khi, int grp,
                                                 float sl2, float& m, float& l, f32x4 (&acc)[DT]) {
-  float lmx = kNegBig;
+  // The maximum is taken over the raw scores (sl2 > 0), and the scaling is
+  // folded into the exponent: p = 2^(s sl2 - m).
+  float lmx = -INFINITY;
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float x = st[h2][i] * sl2;
+      float x = st[h2][i];
       if (MASK) {
         const int key = kbase + 16 * h2 + 4 * grp + i;
         x = (key >= klo && key <= khi) ? x : -INFINITY;
@@ -265,6 +277,7 @@ __device__ __forceinline__ Frag<T> online_probs(f32x4 (&st)[2], int kbase, int k
       st[h2][i] = x;
       lmx = fmaxf(lmx, x);
     }
+  lmx = fmaxf(lmx * sl2, kNegBig);
   if (wave_any(lmx > m + kLazyMax)) {
     const float mn = fmaxf(m, col_max4(lmx));
     const float alpha = fast_exp2(m - mn);
@@ -278,7 +291,7 @@ __device__ __forceinline__ Frag<T> online_probs(f32x4 (&st)[2], int kbase, int k
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float p = fast_exp2(st[h2][i] - m);
+      const float p = fast_exp2(fmaf(st[h2][i], sl2, -m));
       st[h2][i] = p;
       sum += p;
     }

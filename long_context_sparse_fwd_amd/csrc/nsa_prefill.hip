@@ -331,25 +331,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool full = __builtin_amdgcn_readfirstlane(64 * c + 63 < nvis[0]);
 #pragma unroll
     for (int qt = 0; qt < TPW; ++qt) {
-      float lmx = kNegBig;
+      // maximum over the raw scores (sl2 > 0); the scaling goes into the exponent
+      float lmx = -INFINITY;
       if (full) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            st[qt][kt][i] *= sl2;
-            lmx = fmaxf(lmx, st[qt][kt][i]);
-          }
+          for (int i = 0; i < 4; ++i) lmx = fmaxf(lmx, st[qt][kt][i]);
       } else {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float x = 64 * c + 16 * kt + 4 * grp + i < nvis[qt] ? st[qt][kt][i] * sl2 : -INFINITY;
+            const float x = 64 * c + 16 * kt + 4 * grp + i < nvis[qt] ? st[qt][kt][i] : -INFINITY;
             st[qt][kt][i] = x;
             lmx = fmaxf(lmx, x);
           }
       }
+      lmx = fmaxf(lmx * sl2, kNegBig);
       if (wave_any(lmx > m[qt] + kLazyMax)) {
         const float mn = fmaxf(m[qt], col_max4(lmx));
         ls[qt] *= fast_exp2(m[qt] - mn);
@@ -359,7 +358,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sum += fast_exp2(st[qt][kt][i] - m[qt]);
+        for (int i = 0; i < 4; ++i) sum += fast_exp2(fmaf(st[qt][kt][i], sl2, -m[qt]));
       ls[qt] += sum;
     }
     if (more) stg.commit(stage + (buf ^ 1) * 2 * TILE, nullptr, tid);
