@@ -83,9 +83,15 @@ def run_decode(cfg, batches=None, check_c=True):
     inputs.DecodeConfig("dec-mixed", 6, 1000, 16, 2, 128, "bf16", top_k=7, window=130,
                         seqlens=(1, 63, 64, 700, 1000, 129)),
     inputs.DecodeConfig("dec-f32", 3, 700, 8, 2, 64, "f32", top_k=4, window=64, seqlens=(700, 65, 333)),
-    # fp32 with D 128 keeps the compressed logits in the workspace, not in LDS
+    # fp32 with D 128: logits in LDS, no room to park the window states
     inputs.DecodeConfig("dec-f32-d128", 2, 900, 8, 2, 128, "f32", top_k=5, window=200, seqlens=(900, 321)),
+    # fp32 with D 128 and 128 blocks: the compressed logits go to the workspace
+    inputs.DecodeConfig("dec-f32-d128-long", 2, 8192, 8, 1, 128, "f32", top_k=6, window=300,
+                        seqlens=(8192, 5000)),
     inputs.DecodeConfig("dec-bf16-long", 2, 8192, 64, 4, 128, "bf16", top_k=16, window=512),
+    # bf16 with D 64 and 512 blocks: the window states are parked in the logits region
+    inputs.DecodeConfig("dec-bf16-d64-park", 2, 32768, 16, 1, 64, "bf16", top_k=8, window=256,
+                        seqlens=(32768, 30001)),
     inputs.DecodeConfig("dec-window-all", 2, 300, 4, 1, 64, "bf16", top_k=2, window=5000,
                         seqlens=(300, 190)),
 ], ids=lambda c: c.name)
@@ -180,3 +186,19 @@ def test_decode_injected_selection_with_repeats_and_unusable_entries():
                          top_k=cfg.top_k, window=cfg.window, inject_idx=inj)
     err = maxabs(out.cpu().numpy().astype(np.float64), orc["out"])
     assert err <= TOL[cfg.dtype], f"decode injected-selection error {err}"
+
+
+def test_decode_is_deterministic():
+    """The merges combine the waves' states in a fixed order: repeated calls agree bit for bit."""
+    cfg = inputs.DecodeConfig("dec-det", 4, 4096, 32, 2, 128, "bf16", top_k=16, window=512,
+                              seqlens=(4096, 4000, 2049, 777))
+    raw = inputs.make_decode_inputs(cfg)
+    q, kc_, vc_, g = (dev(raw[n], cfg.dtype) for n in ("q", "k_cache", "v_cache", "gates"))
+    kb, vb = nsa.compress_kv(kc_, vc_)
+    lens = torch.from_numpy(raw["seqlens"]).cuda()
+    runs = [nsa.decode(q, kc_, vc_, kb, vb, lens, g, top_k=cfg.top_k, window=cfg.window, return_idx=True)
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, i in runs[1:]:
+        assert torch.equal(o.view(torch.int16), runs[0][0].view(torch.int16))
+        assert torch.equal(i, runs[0][1])
