@@ -481,9 +481,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   };
   auto d_wait = [&]() {
     if (nD < 0) {
-      // wave 0 always publishes the list
-      while (__hip_atomic_load(hl_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
-        __builtin_amdgcn_s_sleep(1);
+      lds_wait_eq(hl_ready, 1);  // wave 0 always publishes the list
       const int nh = *nhl;
       nD = wave < nh ? (nh - 1 - wave) / NWV + 1 : 0;
     }
@@ -550,8 +548,10 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     wave_lds_sync();
     const int j = lane < a.n ? selo[lane] : -1;
     // the selection is a set of blocks: a repeated injected entry adds nothing
+    // (a computed selection has no repeats)
     bool rep = false;
-    for (int k = 0; k < a.n; ++k) rep |= k < lane && __builtin_amdgcn_readlane(j, k) == j;
+    if (a.inject)
+      for (int k = 0; k < a.n; ++k) rep |= k < lane && __builtin_amdgcn_readlane(j, k) == j;
     const bool h0 = j >= 0 && j <= own && !rep;
     const bool h1 = h0 && 64 * j + 32 <= t;
     const uint64_t b0 = __ballot(h0), b1 = __ballot(h1);
@@ -560,6 +560,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     if (h0) hl[pos] = 2 * j;
     if (h1) hl[pos + 1] = 2 * j + 1;
     if (lane == 0) *nhl = __popcll(b0) + __popcll(b1);
+    wave_lds_sync();  // every lane's hl entries before the flag
     if (lane == 0) __hip_atomic_store(hl_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   // The window is streamed by waves 1..7. When the logits region (free once
