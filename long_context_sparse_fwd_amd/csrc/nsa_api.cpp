@@ -101,7 +101,7 @@ nsa_status_t check_ptr(const char* name, const void* p, bool need16) {
 // ------------------------------------------------------------------ prefill
 
 struct PrefillPlan {
-  int Nb, Nc, NcT, cmp_waves, cmp_tiles, sel_tiles;
+  int Nb, Nc, NcT, cmp_waves, cmp_lo_lds, cmp_tiles, sel_tiles;
   size_t off_kt, off_vt, off_kct, off_kclt, off_vct, off_idx, total;
 };
 
@@ -124,13 +124,19 @@ nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, Pr
   pl->Nb = static_cast<int>((L + 63) / 64);
   pl->Nc = static_cast<int>(L / 64);
   pl->NcT = (pl->Nc + 63) / 64;
+  // the widest compressed-kernel workgroup whose LDS fits; at 8 waves the
+  // low parts of the K means go through LDS as well when that still fits
   pl->cmp_waves = 0;
-  for (int w = 8; w >= 1; w /= 2)
-    if (nsa::cmpwin_lds_bytes(w, pl->NcT, static_cast<int>(D), d->in_dtype == NSA_BF16) <=
-        static_cast<size_t>(nsa::kMaxLds)) {
-      pl->cmp_waves = w;
-      break;
-    }
+  pl->cmp_lo_lds = 0;
+  const bool bf16 = d->in_dtype == NSA_BF16;
+  for (int w = 8; w >= 1 && pl->cmp_waves == 0; w /= 2)
+    for (int lol = (w == 8 && bf16) ? 1 : 0; lol >= 0; --lol)
+      if (nsa::cmpwin_lds_bytes(w, pl->NcT, static_cast<int>(D), bf16, lol != 0) <=
+          static_cast<size_t>(nsa::kMaxLds)) {
+        pl->cmp_waves = w;
+        pl->cmp_lo_lds = lol;
+        break;
+      }
   if (pl->cmp_waves == 0)
     return fail(NSA_ERR_UNSUPPORTED, "seqlen %lld needs more LDS for block scores than a CU has",
                 static_cast<long long>(L));
@@ -295,6 +301,7 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
   a.Nc = pl.Nc;
   a.NcT = pl.NcT;
   a.cmp_waves = pl.cmp_waves;
+  a.cmp_lo_lds = pl.cmp_lo_lds;
   a.cmp_tiles = pl.cmp_tiles;
   a.sel_tiles = pl.sel_tiles;
   a.sel_bm_words = nsa::sel_bm_words(pl.Nb);

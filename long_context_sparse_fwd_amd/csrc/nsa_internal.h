@@ -24,6 +24,7 @@ struct PrefillArgs {
   int Nc;   // complete (compressed) blocks = L / 64
   int NcT;  // 64-row chunks of the compressed tiles = ceil(Nc / 64)
   int cmp_waves, cmp_tiles, sel_tiles;
+  int cmp_lo_lds;  // compressed kernel stages the low parts of the K means in LDS (8 waves only)
   int sel_bm_words;  // words of a k_sel wave's half-block bitmap (one byte per half block)
   float scale_log2;  // softmax scale * log2(e)
   int inject;        // 1: idx holds the selection; 0: compute it into idx
@@ -75,7 +76,7 @@ hipError_t launch_compress(int B, int G, int Nc, int D, bool bf16, const void* k
 // LDS bytes of the decode kernel, with or without room for the logits.
 size_t dec_lds_bytes(int NmaxPad, int D, bool bf16, bool logits_lds);
 
-size_t cmpwin_lds_bytes(int waves, int NcT, int D, bool bf16);
+size_t cmpwin_lds_bytes(int waves, int NcT, int D, bool bf16, bool lo_lds);
 
 // k_sel: bitmap words per wave (one byte per half block of Nb blocks, padded
 // to 16 bytes) and the dynamic LDS of a launch.
@@ -86,11 +87,11 @@ inline size_t sel_static_lds_bytes(int D, bool bf16) {
   return 4 * static_cast<size_t>(kSelTPW) * (D / 32) * (bf16 ? 16 : 32) * 64;
 }
 
-// LDS bytes of the block scores and top-k scratch of the compressed kernel.
+// LDS bytes of the block scores of the compressed kernel, and its per-wave
+// top-k scratch (which reuses the tile stage once the compressed passes end).
 inline size_t cmp_lds_bytes(int waves, int NcT) {
-  return static_cast<size_t>(waves) *
-         (static_cast<size_t>(kCmpTPW) * NcT * 64 * sizeof(float) + kSurvCap * sizeof(uint64_t) +
-          64 * sizeof(int));
+  return static_cast<size_t>(waves) * kCmpTPW * NcT * 64 * sizeof(float);
 }
+inline size_t cmp_topk_scratch_bytes() { return kSurvCap * sizeof(uint64_t) + 64 * sizeof(int); }
 
 }  // namespace nsa

@@ -70,6 +70,14 @@ constexpr bool kSplitKc = false;
 template <>
 constexpr bool kSplitKc<BF16> = true;
 
+// Tiles in the compressed kernel's LDS stage: two buffers of K and V, plus
+// the low part of K when the means are split and LOL (low part through LDS)
+// is chosen; otherwise each wave reads the low part from L2 itself.
+template <class T, bool LOL>
+constexpr int cmp_stage_tiles() {
+  return kSplitKc<T> && LOL ? 6 : 4;
+}
+
 // ------------------------------------------------------------------ k_prep
 
 template <class T, int D>
@@ -152,37 +160,49 @@ template <class T, int D, int NT>
 struct TileStager {
   static constexpr int kVec = 64 * D * static_cast<int>(sizeof(typename T::storage)) / 16;
   static constexpr int kPer = kVec / NT;
-  u32x4 r[2][kPer];
-  __device__ __forceinline__ void issue(const void* a, const void* b, int tid) {
+  u32x4 r[3][kPer];
+  __device__ __forceinline__ void issue(const void* a, const void* b, const void* c, int tid) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) r[0][i] = static_cast<const u32x4*>(a)[tid + NT * i];
     if (b != nullptr) {
 #pragma unroll
       for (int i = 0; i < kPer; ++i) r[1][i] = static_cast<const u32x4*>(b)[tid + NT * i];
     }
+    if (c != nullptr) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) r[2][i] = static_cast<const u32x4*>(c)[tid + NT * i];
+    }
   }
-  __device__ __forceinline__ void commit(void* a, void* b, int tid) const {
+  __device__ __forceinline__ void commit(void* a, void* b, void* c, int tid) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) static_cast<u32x4*>(a)[tid + NT * i] = r[0][i];
     if (b != nullptr) {
 #pragma unroll
       for (int i = 0; i < kPer; ++i) static_cast<u32x4*>(b)[tid + NT * i] = r[1][i];
     }
+    if (c != nullptr) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) static_cast<u32x4*>(c)[tid + NT * i] = r[2][i];
+    }
   }
 };
 
 // ------------------------------------------------------------------ k_cmpwin
 
-template <class T, class O, int D, int NW>
+template <class T, class O, int D, int NW, bool LOL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_cmpwin(PrefillArgs a) {
   using S = typename T::storage;
   using SO = typename O::storage;
   constexpr int TPW = kCmpTPW, KS = D / 32, DT = D / 16, NT = 64 * NW, TILE = 64 * D;
+  constexpr bool LOLDS = kSplitKc<T> && LOL;
+  constexpr int BUF = cmp_stage_tiles<T, LOL>() / 2 * TILE;  // elements of one stage buffer
   extern __shared__ __align__(16) unsigned char smem[];
-  S* stage = reinterpret_cast<S*>(smem);  // [2 buffers][2 tiles][TILE]
+  // [2 buffers][K, V (, K low part)][TILE], then the block scores; the top-k
+  // scratch reuses the stage once the compressed passes are done
+  S* stage = reinterpret_cast<S*>(smem);
   const int NcPad = a.NcT * 64;
-  float* scb = reinterpret_cast<float*>(smem + 4 * TILE * sizeof(S));
-  uint64_t* survb = reinterpret_cast<uint64_t*>(scb + NW * TPW * NcPad);
+  float* scb = reinterpret_cast<float*>(smem + 2 * BUF * sizeof(S));
+  uint64_t* survb = reinterpret_cast<uint64_t*>(smem);
   int* selbb = reinterpret_cast<int*>(survb + NW * kSurvCap);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -233,15 +253,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       mw[qt] = kNegBig;
       lw[qt] = 0.f;
     }
-    stg.issue(KT + static_cast<int64_t>(b0) * TILE, VT + static_cast<int64_t>(b0) * TILE, tid);
-    stg.commit(stage, stage + TILE, tid);
+    stg.issue(KT + static_cast<int64_t>(b0) * TILE, VT + static_cast<int64_t>(b0) * TILE, nullptr, tid);
+    stg.commit(stage, stage + TILE, nullptr, tid);
     __syncthreads();
     for (int blk = b0; blk <= b1; ++blk) {
       const int buf = (blk - b0) & 1;
       const bool more = blk < b1;
       if (more)
-        stg.issue(KT + static_cast<int64_t>(blk + 1) * TILE, VT + static_cast<int64_t>(blk + 1) * TILE, tid);
-      const S* kt = stage + buf * 2 * TILE;
+        stg.issue(KT + static_cast<int64_t>(blk + 1) * TILE, VT + static_cast<int64_t>(blk + 1) * TILE, nullptr,
+                  tid);
+      const S* kt = stage + buf * BUF;
       const S* vt = kt + TILE;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -274,7 +295,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                      oacc[qt], vf);
         }
       }
-      if (more) stg.commit(stage + (buf ^ 1) * 2 * TILE, stage + (buf ^ 1) * 2 * TILE + TILE, tid);
+      if (more) stg.commit(stage + (buf ^ 1) * BUF, stage + (buf ^ 1) * BUF + TILE, nullptr, tid);
       __syncthreads();
     }
 #pragma unroll
@@ -304,15 +325,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     ls[qt] = 0.f;
   }
   if (nch > 0) {
-    stg.issue(KC, nullptr, tid);
-    stg.commit(stage, nullptr, tid);
+    stg.issue(KC, nullptr, nullptr, tid);
+    stg.commit(stage, nullptr, nullptr, tid);
     __syncthreads();
   }
   for (int c = 0; c < nch; ++c) {
     const int buf = c & 1;
     const bool more = c + 1 < nch;
-    if (more) stg.issue(KC + static_cast<int64_t>(c + 1) * TILE, nullptr, tid);
-    const S* kc = stage + buf * 2 * TILE;
+    if (more) stg.issue(KC + static_cast<int64_t>(c + 1) * TILE, nullptr, nullptr, tid);
+    const S* kc = stage + buf * BUF;
     f32x4 st[TPW][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -361,7 +382,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int i = 0; i < 4; ++i) sum += fast_exp2(fmaf(st[qt][kt][i], sl2, -m[qt]));
       ls[qt] += sum;
     }
-    if (more) stg.commit(stage + (buf ^ 1) * 2 * TILE, nullptr, tid);
+    if (more) stg.commit(stage + (buf ^ 1) * BUF, nullptr, nullptr, tid);
     __syncthreads();
   }
   float lse2[TPW];
@@ -375,17 +396,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool select = !a.inject;
   float* sc = scb + static_cast<size_t>(wave) * TPW * NcPad;
   if (nch > 0) {
-    stg.issue(KC, VC, tid);
-    stg.commit(stage, stage + TILE, tid);
+    stg.issue(KC, VC, LOLDS ? KCL : nullptr, tid);
+    stg.commit(stage, stage + TILE, LOLDS ? stage + 2 * TILE : nullptr, tid);
     __syncthreads();
   }
   for (int c = 0; c < nch; ++c) {
     const int buf = c & 1;
     const bool more = c + 1 < nch;
-    if (more) stg.issue(KC + static_cast<int64_t>(c + 1) * TILE, VC + static_cast<int64_t>(c + 1) * TILE, tid);
-    const S* kc = stage + buf * 2 * TILE;
+    if (more)
+      stg.issue(KC + static_cast<int64_t>(c + 1) * TILE, VC + static_cast<int64_t>(c + 1) * TILE,
+                LOLDS ? KCL + static_cast<int64_t>(c + 1) * TILE : nullptr, tid);
+    const S* kc = stage + buf * BUF;
     const S* vc = kc + TILE;
-    const S* kcl = kSplitKc<T> ? KCL + static_cast<int64_t>(c) * TILE : nullptr;
+    // low parts (bf16 inputs only): staged after V, or read from L2
+    const S* kcl = LOLDS ? vc + TILE : kSplitKc<T> ? KCL + static_cast<int64_t>(c) * TILE : nullptr;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       f32x4 st[TPW][2];
@@ -444,7 +468,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int dt = 0; dt < DT; ++dt) mma(oacc[qt][dt], vf[dt], pf);
       }
     }
-    if (more) stg.commit(stage + (buf ^ 1) * 2 * TILE, stage + (buf ^ 1) * 2 * TILE + TILE, tid);
+    if (more)
+      stg.commit(stage + (buf ^ 1) * BUF, stage + (buf ^ 1) * BUF + TILE,
+                 LOLDS ? stage + (buf ^ 1) * BUF + 2 * TILE : nullptr, tid);
     __syncthreads();
   }
 
@@ -696,21 +722,25 @@ size_t sel_lds_bytes(int Nb, int D, bool bf16) {
   return need > cap ? need : cap;
 }
 
-size_t cmpwin_lds_bytes(int waves, int NcT, int D, bool bf16) {
-  return 4 * 64 * static_cast<size_t>(D) * (bf16 ? 2 : 4) + cmp_lds_bytes(waves, NcT);
+size_t cmpwin_lds_bytes(int waves, int NcT, int D, bool bf16, bool lo_lds) {
+  const int tiles = bf16 ? (lo_lds ? cmp_stage_tiles<BF16, true>() : cmp_stage_tiles<BF16, false>())
+                         : cmp_stage_tiles<F32, false>();
+  const size_t stage = tiles * 64 * static_cast<size_t>(D) * (bf16 ? 2 : 4);
+  const size_t topk = static_cast<size_t>(waves) * cmp_topk_scratch_bytes();
+  return (stage > topk ? stage : topk) + cmp_lds_bytes(waves, NcT);
 }
 
 static hipError_t record(hipEvent_t* ev, int i, hipStream_t st) {
   return ev != nullptr ? hipEventRecord(ev[i], st) : hipSuccess;
 }
 
-template <class T, class O, int D, int NW>
+template <class T, class O, int D, int NW, bool LOL>
 static hipError_t launch_cmpwin(const PrefillArgs& a, hipStream_t st) {
-  const size_t lds = cmpwin_lds_bytes(NW, a.NcT, D, sizeof(typename T::storage) == 2);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cmpwin<T, O, D, NW>),
+  const size_t lds = cmpwin_lds_bytes(NW, a.NcT, D, sizeof(typename T::storage) == 2, LOL);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cmpwin<T, O, D, NW, LOL>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_cmpwin<T, O, D, NW>), dim3(a.B * a.G * a.cmp_tiles), dim3(64 * NW), lds, st, a);
+  hipLaunchKernelGGL((k_cmpwin<T, O, D, NW, LOL>), dim3(a.B * a.G * a.cmp_tiles), dim3(64 * NW), lds, st, a);
   return hipSuccess;
 }
 
@@ -721,10 +751,16 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st, hipEven
   if ((e = record(ev, 0, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((k_prep<T, D>), dim3(nblk_prep, a.G, a.B), dim3(256), 0, st, a);
   if ((e = record(ev, 1, st)) != hipSuccess) return e;
-  if (a.cmp_waves == 8) e = launch_cmpwin<T, O, D, 8>(a, st);
-  else if (a.cmp_waves == 4) e = launch_cmpwin<T, O, D, 4>(a, st);
-  else if (a.cmp_waves == 2) e = launch_cmpwin<T, O, D, 2>(a, st);
-  else e = launch_cmpwin<T, O, D, 1>(a, st);
+  if (a.cmp_waves == 8) {
+    if (a.cmp_lo_lds) e = launch_cmpwin<T, O, D, 8, true>(a, st);
+    else e = launch_cmpwin<T, O, D, 8, false>(a, st);
+  } else if (a.cmp_waves == 4) {
+    e = launch_cmpwin<T, O, D, 4, false>(a, st);
+  } else if (a.cmp_waves == 2) {
+    e = launch_cmpwin<T, O, D, 2, false>(a, st);
+  } else {
+    e = launch_cmpwin<T, O, D, 1, false>(a, st);
+  }
   if (e != hipSuccess) return e;
   if ((e = record(ev, 2, st)) != hipSuccess) return e;
   const int N = a.B * a.G * a.sel_tiles;
