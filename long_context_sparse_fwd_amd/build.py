@@ -3,7 +3,9 @@
     python -m long_context_sparse_fwd_amd.build [-v]
 
 Every source is compiled on each call; objects go to csrc/_build/ and the
-shared library to the package directory, where the binding loads it.
+shared library to the package directory, where the binding loads it. The
+gather-bandwidth probe (csrc/probe_gather.hip, a measurement program, not part
+of the library) is built next to it as probe_gather.
 """
 
 from __future__ import annotations
@@ -18,6 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(PKG, "libnsa.so")
+PROBE = os.path.join(PKG, "probe_gather")
 SOURCES = ["nsa_api.cpp", "nsa_prefill.hip", "nsa_decode.hip", "nsa_compress.hip"]
 ARCH = "gfx950"
 
@@ -66,6 +69,13 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    cmd = [hipcc, *common_flags(), os.path.join(CSRC, "probe_gather.hip"), "-o", PROBE + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for probe_gather.hip:\n{r.stdout}\n{r.stderr}")
+    os.replace(PROBE + ".tmp", PROBE)
     return LIB
 
 
