@@ -188,11 +188,12 @@ def cpu_baseline(cfg, raw, seconds: float):
 
 # ---------------------------------------------------------------- benchmark legs
 
-def bench_prefill(cfg, steps, warmup, torch, inputs, nsa):
+def bench_prefill(cfg, steps, warmup, torch, inputs, nsa, raw=None):
     dev = torch.device("cuda:0")
-    t0 = time.perf_counter()
-    raw = inputs.make_prefill_inputs(cfg)
-    log(f"[bench] inputs {cfg.name} generated in {time.perf_counter() - t0:.1f} s")
+    if raw is None:
+        t0 = time.perf_counter()
+        raw = inputs.make_prefill_inputs(cfg)
+        log(f"[bench] inputs {cfg.name} generated in {time.perf_counter() - t0:.1f} s")
     up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
     q, k, v, g = (up(raw[n]) for n in ("q", "k", "v", "gates"))
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
@@ -284,6 +285,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="p64k", choices=["p8k", "p32k", "p64k"])
+    ap.add_argument("--also", default="p8k,p32k",
+                    help="shorter prefill configs also reported (their inputs are prefixes of the "
+                         "main config's); empty for none")
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -359,6 +363,20 @@ def main():
                     "mfma_frac": total_fl / (wall_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                     "algorithmic_flops": fl, "kernels_ms": stage_ms},
     }
+    others = {}
+    for name in [x for x in args.also.split(",") if x]:
+        oc = inputs.CONFIGS[name]
+        if oc.seqlen >= cfg.seqlen or oc.batch != cfg.batch:
+            continue
+        # the keyed generator makes the shorter config's inputs a prefix of these
+        sub = {n: np.ascontiguousarray(raw[n][:, :oc.seqlen]) for n in ("q", "k", "v", "gates")}
+        _, o_ms, o_stage = bench_prefill(oc, args.steps, args.warmup, torch, inputs, nsa, raw=sub)
+        o_fl = sum(prefill_flops(oc).values())
+        others[name] = {"ms_per_step": o_ms, "tokens_per_s": oc.batch * oc.seqlen / (o_ms * 1e-3),
+                        "tflops": o_fl / (o_ms * 1e-3) / 1e12,
+                        "mfma_frac": o_fl / (o_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "kernels_ms": o_stage}
+    if others:
+        result["other_prefill"] = others
     if not args.no_decode:
         result["decode"] = bench_decode(inputs.CONFIGS["d64k"], args.decode_steps, 3, torch, inputs, nsa)
     if not args.no_cpu_baseline:

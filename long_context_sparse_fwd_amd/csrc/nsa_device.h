@@ -214,6 +214,34 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
+// Sums over the 16 lanes of each DPP row of eight values per lane, with the
+// totals spread back over the row (reduce-scatter by halving, no branches):
+// v[h][i] is the lane's term of item 4h + i. A lane whose position in its
+// row is c receives the total of item 4·c₃ + 2·c₀ + c₁ (cₖ = bit k of c);
+// lanes c and c ^ 4 receive the same item. 23 VALU operations against 32 for
+// eight full row sums.
+__device__ __forceinline__ float row_scatter_sum8(const f32x4 (&v)[2], int c) {
+  const bool b3 = (c & 8) != 0, b0 = (c & 1) != 0, b1 = (c & 2) != 0;
+  float a[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // partner c ^ 8 keeps the other half
+    const float send = b3 ? v[0][i] : v[1][i];
+    const float keep = b3 ? v[1][i] : v[0][i];
+    a[i] = keep + dpp_f<0x128>(send);  // row_ror:8
+  }
+  float b[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {  // partner c ^ 1
+    const float send = b0 ? a[k] : a[k + 2];
+    const float keep = b0 ? a[k + 2] : a[k];
+    b[k] = keep + dpp_f<0xB1>(send);  // quad_perm [1,0,3,2]
+  }
+  const float send = b1 ? b[0] : b[1];  // partner c ^ 2
+  const float keep = b1 ? b[1] : b[0];
+  const float d = keep + dpp_f<0x4E>(send);  // quad_perm [2,3,0,1]
+  return d + dpp_f<0x1B>(dpp_f<0x141>(d));  // + lane c ^ 4: row_half_mirror, quad_perm [3,2,1,0]
+}
+
 // The value of lane l ^ 16 / l ^ 32, from the gfx950 lane swaps (no LDS):
 // swapping a value with itself leaves r[0] holding the even rows (resp. the
 // low half) twice and r[1] the odd rows (the high half) twice.

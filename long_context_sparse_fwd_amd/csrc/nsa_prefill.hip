@@ -28,6 +28,8 @@
 //             per CU and work grouped by KV group per XCD: the random block
 //             gathers are bound by L2-miss bandwidth, which fewer concurrent
 //             waves per XCD use better.
+#include <type_traits>
+
 #include "nsa_device.h"
 #include "nsa_internal.h"
 #include "nsa_topk.h"
@@ -393,23 +395,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   // pass 2: probabilities, gate_cmp * P . Vc into the accumulators, block scores
-  const bool select = !a.inject;
   float* sc = scb + static_cast<size_t>(wave) * TPW * NcPad;
   if (nch > 0) {
     stg.issue(KC, VC, LOLDS ? KCL : nullptr, tid);
     stg.commit(stage, stage + TILE, LOLDS ? stage + 2 * TILE : nullptr, tid);
     __syncthreads();
   }
-  for (int c = 0; c < nch; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nch;
-    if (more)
-      stg.issue(KC + static_cast<int64_t>(c + 1) * TILE, VC + static_cast<int64_t>(c + 1) * TILE,
-                LOLDS ? KCL + static_cast<int64_t>(c + 1) * TILE : nullptr, tid);
-    const S* kc = stage + buf * BUF;
-    const S* vc = kc + TILE;
-    // low parts (bf16 inputs only): staged after V, or read from L2
-    const S* kcl = LOLDS ? vc + TILE : kSplitKc<T> ? KCL + static_cast<int64_t>(c) * TILE : nullptr;
+  // One 64-key chunk; FULL: every key visible to both tokens (no masks).
+  // The full chunks come first and run as one loop, the partial ones as a
+  // second: each loop body is straight-line code (no branch between the QK
+  // products, the softmax and the PV products) that the compiler schedules
+  // as one region. The block scores are computed even when the caller
+  // injects the selection (they are then unused).
+  auto chunk2 = [&](auto full_c, int c, const S* kc, const S* vc, const S* kcl) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       f32x4 st[TPW][2];
@@ -434,45 +433,47 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       Frag<T> vf[DT];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) vf[dt] = frag_load<T>(vc + vtile_frag(dt, s2, lane));
-      const bool full = __builtin_amdgcn_readfirstlane(64 * c + 32 * s2 + 31 < nvis[0]);
 #pragma unroll
       for (int qt = 0; qt < TPW; ++qt) {
-        if (full) {
 #pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2)
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) st[qt][h2][i] = fast_exp2(st[qt][h2][i] * sl2 - lse2[qt]);
-        } else {
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float p = fast_exp2(st[qt][h2][i] * sl2 - lse2[qt]);
-              st[qt][h2][i] = 64 * c + 32 * s2 + 16 * h2 + 4 * grp + i < nvis[qt] ? p : 0.f;
-            }
-        }
-        if (select) {
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            f32x4 r;
-            r.x = row_sum16(st[qt][h2].x);
-            r.y = row_sum16(st[qt][h2].y);
-            r.z = row_sum16(st[qt][h2].z);
-            r.w = row_sum16(st[qt][h2].w);
-            if (col == 0)
-              *reinterpret_cast<f32x4*>(sc + qt * NcPad + 64 * c + 32 * s2 + 16 * h2 + 4 * grp) = r;
+          for (int i = 0; i < 4; ++i) {
+            const float p = fast_exp2(st[qt][h2][i] * sl2 - lse2[qt]);
+            st[qt][h2][i] = (FULL || 64 * c + 32 * s2 + 16 * h2 + 4 * grp + i < nvis[qt]) ? p : 0.f;
           }
+        {
+          // the head sum of key 16·c₃ + 4·grp + 2·c₀ + c₁ of this half (c = col)
+          const float r = row_scatter_sum8(st[qt], col);
+          sc[qt * NcPad + 64 * c + 32 * s2 + 16 * ((col >> 3) & 1) + 4 * grp + 2 * (col & 1) + ((col >> 1) & 1)] = r;
         }
         const Frag<T> pf = pack_p<T>(st[qt][0] * gcmp[qt], st[qt][1] * gcmp[qt]);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) mma(oacc[qt][dt], vf[dt], pf);
       }
     }
+  };
+  // chunks [0, nfull) are visible to both tokens in full
+  const int nfull = __builtin_amdgcn_readfirstlane(min(nch, nvis[0] >> 6));
+  auto step2 = [&](auto full_c, int c) __attribute__((always_inline)) {
+    const int buf = c & 1;
+    const bool more = c + 1 < nch;
+    if (more)
+      stg.issue(KC + static_cast<int64_t>(c + 1) * TILE, VC + static_cast<int64_t>(c + 1) * TILE,
+                LOLDS ? KCL + static_cast<int64_t>(c + 1) * TILE : nullptr, tid);
+    const S* kc = stage + buf * BUF;
+    const S* vc = kc + TILE;
+    // low parts (bf16 inputs only): staged after V, or read from L2
+    const S* kcl = LOLDS ? vc + TILE : kSplitKc<T> ? KCL + static_cast<int64_t>(c) * TILE : nullptr;
+    chunk2(full_c, c, kc, vc, kcl);
     if (more)
       stg.commit(stage + (buf ^ 1) * BUF, stage + (buf ^ 1) * BUF + TILE,
                  LOLDS ? stage + (buf ^ 1) * BUF + 2 * TILE : nullptr, tid);
     __syncthreads();
-  }
+  };
+  int c = 0;
+  for (; c < nfull; ++c) step2(std::integral_constant<bool, true>{}, c);
+  for (; c < nch; ++c) step2(std::integral_constant<bool, false>{}, c);
 
   // ---- gate_win * O_win + gate_cmp * O_cmp -> out (k_sel adds the selected branch)
   {
@@ -489,7 +490,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   // ---- selection
-  if (select) {
+  if (!a.inject) {
     wave_lds_sync();
     uint64_t* surv = survb + static_cast<size_t>(wave) * kSurvCap;
     int* selb = selbb + wave * 64;
