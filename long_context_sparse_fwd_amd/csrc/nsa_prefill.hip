@@ -258,7 +258,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     stg.issue(KT + static_cast<int64_t>(b0) * TILE, VT + static_cast<int64_t>(b0) * TILE, nullptr, tid);
     stg.commit(stage, stage + TILE, nullptr, tid);
     __syncthreads();
-    for (int blk = b0; blk <= b1; ++blk) {
+    // INNER: both halves of the block lie inside the window of every token of
+    // the workgroup (no band test, no masks); the band's edge blocks take
+    // the general body. Three loops, so each body is straight-line code.
+    auto stepw = [&](auto inner_c, int blk) __attribute__((always_inline)) {
+      constexpr bool INNER = decltype(inner_c)::value;
       const int buf = (blk - b0) & 1;
       const bool more = blk < b1;
       if (more)
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const int kb = 64 * blk + 32 * s2;
-        if (kb > tw + TPW - 1 || kb + 31 < tw - a.w + 1) continue;  // outside this wave's band
+        if (!INNER && (kb > tw + TPW - 1 || kb + 31 < tw - a.w + 1)) continue;  // outside this wave's band
         Frag<T> kf[2][KS];
         Frag<T> vf[DT];
 #pragma unroll
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) vf[dt] = frag_load<T>(vt + vtile_frag(dt, s2, lane));
         // all 32 keys inside every token's window: no masks needed
-        const bool full = kb >= tw + TPW - a.w && kb + 31 <= tw && tw + TPW - 1 < a.L;
+        const bool full = INNER || (kb >= tw + TPW - a.w && kb + 31 <= tw && tw + TPW - 1 < a.L);
 #pragma unroll
         for (int qt = 0; qt < TPW; ++qt) {
           const int t = tw + qt;
@@ -299,7 +303,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       if (more) stg.commit(stage + (buf ^ 1) * BUF, stage + (buf ^ 1) * BUF + TILE, nullptr, tid);
       __syncthreads();
+    };
+    // inner blocks: 64 blk >= (last token + 1) - w and 64 blk + 63 <= first token
+    int lo = b1 + 1, hi = b1;
+    if (T0 + TPW * NW - 1 < a.L) {
+      const int x = T0 + TPW * NW - a.w;  // lowest first key of an inner block
+      lo = x <= 0 ? b0 : max(b0, (x + 63) >> 6);
+      hi = T0 >= 63 ? min(b1, (T0 - 63) >> 6) : -1;
+      if (lo > hi) lo = hi + 1;
     }
+    int blk = b0;
+    for (; blk < lo && blk <= b1; ++blk) stepw(std::integral_constant<bool, false>{}, blk);
+    for (; blk <= hi; ++blk) stepw(std::integral_constant<bool, true>{}, blk);
+    for (; blk <= b1; ++blk) stepw(std::integral_constant<bool, false>{}, blk);
 #pragma unroll
     for (int qt = 0; qt < TPW; ++qt) {
       const float lt = col_sum4(lw[qt]);
@@ -331,7 +347,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     stg.commit(stage, nullptr, nullptr, tid);
     __syncthreads();
   }
-  for (int c = 0; c < nch; ++c) {
+  // Fully visible chunks first, then the partial ones, each loop one
+  // straight-line body (FULL drops the masks).
+  auto step1 = [&](auto full_c, int c) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_c)::value;
     const int buf = c & 1;
     const bool more = c + 1 < nch;
     if (more) stg.issue(KC + static_cast<int64_t>(c + 1) * TILE, nullptr, nullptr, tid);
@@ -349,28 +368,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int s = 0; s < KS; ++s) mma(st[qt][kt], kf[s], qf[qt][s]);
       }
     }
-    // every key of the chunk visible to every token (wave-uniform, so the
-    // masked variant below is a real branch, not per-lane selects)
-    const bool full = __builtin_amdgcn_readfirstlane(64 * c + 63 < nvis[0]);
 #pragma unroll
     for (int qt = 0; qt < TPW; ++qt) {
       // maximum over the raw scores (sl2 > 0); the scaling goes into the exponent
       float lmx = -INFINITY;
-      if (full) {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) lmx = fmaxf(lmx, st[qt][kt][i]);
-      } else {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = 64 * c + 16 * kt + 4 * grp + i < nvis[qt] ? st[qt][kt][i] : -INFINITY;
-            st[qt][kt][i] = x;
-            lmx = fmaxf(lmx, x);
-          }
-      }
+        for (int i = 0; i < 4; ++i) {
+          const float x = (FULL || 64 * c + 16 * kt + 4 * grp + i < nvis[qt]) ? st[qt][kt][i] : -INFINITY;
+          st[qt][kt][i] = x;
+          lmx = fmaxf(lmx, x);
+        }
       lmx = fmaxf(lmx * sl2, kNegBig);
       if (wave_any(lmx > m[qt] + kLazyMax)) {
         const float mn = fmaxf(m[qt], col_max4(lmx));
@@ -386,6 +395,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     if (more) stg.commit(stage + (buf ^ 1) * BUF, nullptr, nullptr, tid);
     __syncthreads();
+  };
+  // chunks [0, nfull) are visible to both tokens in full
+  const int nfull = __builtin_amdgcn_readfirstlane(min(nch, nvis[0] >> 6));
+  {
+    int c = 0;
+    for (; c < nfull; ++c) step1(std::integral_constant<bool, true>{}, c);
+    for (; c < nch; ++c) step1(std::integral_constant<bool, false>{}, c);
   }
   float lse2[TPW];
 #pragma unroll
@@ -453,8 +469,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   };
-  // chunks [0, nfull) are visible to both tokens in full
-  const int nfull = __builtin_amdgcn_readfirstlane(min(nch, nvis[0] >> 6));
   auto step2 = [&](auto full_c, int c) __attribute__((always_inline)) {
     const int buf = c & 1;
     const bool more = c + 1 < nch;
