@@ -62,6 +62,12 @@ __device__ __forceinline__ uint64_t lane_xor(uint64_t v, int m) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// base + the number of set bits of m in the lanes below this one
+__device__ __forceinline__ int mbcnt(uint64_t m, int base) {
+  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+      static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), static_cast<uint32_t>(base))));
+}
+
 // Bitonic sort of one value per lane across the wave: descending (lane 0
 // holds the largest) or ascending.
 template <bool DESC, class K>
@@ -79,7 +85,7 @@ __device__ __forceinline__ K wave_sort(K v, int lane) {
 }
 
 // sc: scores of blocks [0, own) in LDS (read by all lanes). out: n entries.
-// surv: kSurvCap u64 of LDS scratch; selb: 64 ints of LDS scratch.
+// surv: kSurvSlots u64 of LDS scratch; selb: 64 ints of LDS scratch.
 // Must be called by a whole wave with uniform arguments.
 __device__ inline void topk_wave(const float* sc, int own, int n, int32_t* out, uint64_t* surv,
                                  int* selb, int lane) {
@@ -93,7 +99,6 @@ __device__ inline void topk_wave(const float* sc, int own, int n, int32_t* out, 
     return;
   }
   const int R = (own + 63) >> 6;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   // Keys of blocks lane + 64 (r0 + i), i < 8; the reads are unconditional
   // (indices clamped to own - 1) and independent, so they issue together.
   auto keys8 = [&](int r0, uint32_t (&k)[8]) {
@@ -114,20 +119,28 @@ __device__ inline void topk_wave(const float* sc, int own, int n, int32_t* out, 
   // theta: the (n-1)-th largest lane maximum
   const uint32_t theta = __builtin_amdgcn_readlane(wave_sort<true>(lmax, lane), n1 - 1);
 
-  // the candidates >= theta, compacted into surv in ascending block order
+  // the candidates >= theta, compacted into surv in ascending block order:
+  // the eight rows' ballots first, their counts summed in scalar registers,
+  // then one unconditional store per row (a lane that does not survive, or
+  // whose place is past kSurvCap, writes its own discard slot)
   int cnt = 0;
   for (int r0 = 0; r0 < R; r0 += 8) {
     uint32_t k[8];
     keys8(r0, k);
+    bool f[8];
+    uint64_t bal[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const bool f = k[i] >= theta && k[i] != 0u;
-      const uint64_t bal = __ballot(f);
-      const int pos = cnt + __popcll(bal & below);
-      if (f && pos < kSurvCap)
-        surv[pos] = (static_cast<uint64_t>(k[i]) << 32) |
-                    static_cast<uint32_t>(0xFFFFFFFFu - (lane + 64 * (r0 + i)));
-      cnt += __popcll(bal);
+      f[i] = k[i] >= theta && k[i] != 0u;
+      bal[i] = __ballot(f[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pos = mbcnt(bal[i], cnt);  // cnt + survivors in lower lanes
+      const bool keep = f[i] && pos < kSurvCap;
+      surv[keep ? pos : kSurvCap + lane] = (static_cast<uint64_t>(k[i]) << 32) |
+                                           static_cast<uint32_t>(0xFFFFFFFFu - (lane + 64 * (r0 + i)));
+      cnt += __popcll(bal[i]);
     }
   }
   wave_lds_sync();
@@ -140,7 +153,7 @@ __device__ inline void topk_wave(const float* sc, int own, int n, int32_t* out, 
 #pragma unroll 4
     for (int k = 0; k < cnt; ++k) rank += surv[k] > mine ? 1 : 0;
     const bool s = lane < cnt && rank < n1;
-    const int pos = __popcll(__ballot(s) & below);
+    const int pos = mbcnt(__ballot(s), 0);
     if (s) out[pos] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(mine));
     if (lane == 0) out[n1] = own;
     wave_lds_sync();
