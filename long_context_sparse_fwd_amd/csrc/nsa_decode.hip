@@ -405,7 +405,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   float* res = reinterpret_cast<float*>(qlds + D / 32 * 64);                  // [16][D] output
   float* sc = res + 16 * D;
   uint64_t* surv = reinterpret_cast<uint64_t*>(sc + a.NmaxPad);
-  int* selb = reinterpret_cast<int*>(surv + kSurvSlots);
+  int* selb = reinterpret_cast<int*>(surv + kSurvCap);
   int* selo = selb + 64;
   int* hl = selo + 64;                            // usable selected half blocks: 2 j + half
   int* nhl = hl + 128;                            // their count
@@ -626,7 +626,7 @@ size_t dec_lds_bytes(int NmaxPad, int D, bool bf16, bool logits_lds) {
                           : (D == 64 ? dec_big_bytes<F32, 64>() : dec_big_bytes<F32, 128>());
   const size_t qbytes = (bf16 ? 16 : 32) * static_cast<size_t>(D / 32) * 64;
   return big + qbytes + 16 * static_cast<size_t>(D) * sizeof(float) + NmaxPad * sizeof(float) +
-         kSurvSlots * sizeof(uint64_t) + (64 + 64 + 128 + 4) * sizeof(int) + (64 + 48 + 32 * kDecWaves) * sizeof(float) +
+         kSurvCap * sizeof(uint64_t) + (64 + 64 + 128 + 4) * sizeof(int) + (64 + 48 + 32 * kDecWaves) * sizeof(float) +
          (logits_lds ? 16 * static_cast<size_t>(NmaxPad + 4) * sizeof(float) : 0);
 }
 

@@ -10,7 +10,6 @@ namespace nsa {
 
 constexpr int kBlock = 64;         // compress / select block size supported
 constexpr int kSurvCap = 256;      // top-k survivor buffer per wave (entries)
-constexpr int kSurvSlots = kSurvCap + 64;  // plus one discard slot per lane
 constexpr int kCmpTPW = 2;         // tokens per wave, window+compressed+selection kernel
 constexpr int kSelTPW = 2;         // tokens per wave, selected-branch kernel (4 waves)
 constexpr int kSelRing = 2;        // half-block register buffers per wave in that kernel
@@ -93,6 +92,6 @@ inline size_t sel_static_lds_bytes(int D, bool bf16) {
 inline size_t cmp_lds_bytes(int waves, int NcT) {
   return static_cast<size_t>(waves) * kCmpTPW * NcT * 64 * sizeof(float);
 }
-inline size_t cmp_topk_scratch_bytes() { return kSurvSlots * sizeof(uint64_t) + 64 * sizeof(int); }
+inline size_t cmp_topk_scratch_bytes() { return kSurvCap * sizeof(uint64_t) + 64 * sizeof(int); }
 
 }  // namespace nsa

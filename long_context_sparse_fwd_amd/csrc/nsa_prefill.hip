@@ -205,7 +205,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int NcPad = a.NcT * 64;
   float* scb = reinterpret_cast<float*>(smem + 2 * BUF * sizeof(S));
   uint64_t* survb = reinterpret_cast<uint64_t*>(smem);
-  int* selbb = reinterpret_cast<int*>(survb + NW * kSurvSlots);
+  int* selbb = reinterpret_cast<int*>(survb + NW * kSurvCap);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int BG = a.B * a.G;
@@ -506,7 +506,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // ---- selection
   if (!a.inject) {
     wave_lds_sync();
-    uint64_t* surv = survb + static_cast<size_t>(wave) * kSurvSlots;
+    uint64_t* surv = survb + static_cast<size_t>(wave) * kSurvCap;
     int* selb = selbb + wave * 64;
 #pragma unroll 1
     for (int qt = 0; qt < TPW; ++qt) {

@@ -85,7 +85,7 @@ __device__ __forceinline__ K wave_sort(K v, int lane) {
 }
 
 // sc: scores of blocks [0, own) in LDS (read by all lanes). out: n entries.
-// surv: kSurvSlots u64 of LDS scratch; selb: 64 ints of LDS scratch.
+// surv: kSurvCap u64 of LDS scratch; selb: 64 ints of LDS scratch.
 // Must be called by a whole wave with uniform arguments.
 __device__ inline void topk_wave(const float* sc, int own, int n, int32_t* out, uint64_t* surv,
                                  int* selb, int lane) {
@@ -120,9 +120,8 @@ __device__ inline void topk_wave(const float* sc, int own, int n, int32_t* out, 
   const uint32_t theta = __builtin_amdgcn_readlane(wave_sort<true>(lmax, lane), n1 - 1);
 
   // the candidates >= theta, compacted into surv in ascending block order:
-  // the eight rows' ballots first, their counts summed in scalar registers,
-  // then one unconditional store per row (a lane that does not survive, or
-  // whose place is past kSurvCap, writes its own discard slot)
+  // the eight rows' ballots first, then each survivor's place from v_mbcnt
+  // and its store (the rows no longer wait on each other)
   int cnt = 0;
   for (int r0 = 0; r0 < R; r0 += 8) {
     uint32_t k[8];
@@ -137,9 +136,8 @@ __device__ inline void topk_wave(const float* sc, int own, int n, int32_t* out, 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int pos = mbcnt(bal[i], cnt);  // cnt + survivors in lower lanes
-      const bool keep = f[i] && pos < kSurvCap;
-      surv[keep ? pos : kSurvCap + lane] = (static_cast<uint64_t>(k[i]) << 32) |
-                                           static_cast<uint32_t>(0xFFFFFFFFu - (lane + 64 * (r0 + i)));
+      if (f[i] && pos < kSurvCap)
+        surv[pos] = (static_cast<uint64_t>(k[i]) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - (lane + 64 * (r0 + i)));
       cnt += __popcll(bal[i]);
     }
   }

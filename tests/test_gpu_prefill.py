@@ -153,7 +153,7 @@ def test_prefill_is_deterministic():
     raw = inputs.make_prefill_inputs(cfg)
     q, k, v, g = _upload(cfg, raw)
     ref = nsa.prefill(q, k, v, g, top_k=16, window=512, return_idx=True)
-    for _ in range(3):
+    for _ in range(10):
         o, i = nsa.prefill(q, k, v, g, top_k=16, window=512, return_idx=True)
         assert torch.equal(o.view(torch.int16), ref[0].view(torch.int16))
         assert torch.equal(i, ref[1])
