@@ -204,16 +204,6 @@ __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the 16 lanes of each DPP row (row_ror butterfly); every lane of the
-// row receives the row total.
-__device__ __forceinline__ float row_sum16(float v) {
-  v += dpp_f<0x128>(v);  // row_ror:8
-  v += dpp_f<0x124>(v);  // row_ror:4
-  v += dpp_f<0x122>(v);  // row_ror:2
-  v += dpp_f<0x121>(v);  // row_ror:1
-  return v;
-}
-
 // Sums over the 16 lanes of each DPP row of eight values per lane, with the
 // totals spread back over the row (reduce-scatter by halving, no branches):
 // v[h][i] is the lane's term of item 4h + i. A lane whose position in its

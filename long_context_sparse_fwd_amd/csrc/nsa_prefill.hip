@@ -11,16 +11,19 @@
 //             (qwbw.cn/news/106443), section 3.
 //  k_cmpwin   sliding-window branch + compressed branch + block scores +
 //             top-k selection for 16 consecutive tokens of one KV group (8
-//             waves, two per SIMD, each owning 2 tokens x 16 query heads). Every 64-key tile the
-//             workgroup needs (window K/V blocks, block-mean tiles) is staged
-//             once in LDS, double-buffered, and shared by the 8 waves. The
-//             window output is normalised and gated first; the compressed
-//             branch then adds gate_cmp * P . Vc into the same accumulators
-//             (pass 1: log-sum-exp; pass 2: probabilities, output, and block
-//             scores = probabilities summed over the group's heads by a DPP
-//             row reduction, kept in LDS). The wave then selects each token's
-//             blocks. Writes gate_win * O_win + gate_cmp * O_cmp into out and
-//             the selection into idx. Workgroups run heaviest first.
+//             waves, two per SIMD, each owning 2 tokens x 16 query heads).
+//             Every 64-key tile the workgroup needs (window K/V blocks,
+//             block-mean tiles, and at 8 waves the low parts of the K means)
+//             is staged once in LDS, double-buffered, and shared by the 8
+//             waves. The window output is normalised and gated first; the
+//             compressed branch then adds gate_cmp * P . Vc into the same
+//             accumulators (pass 1: log-sum-exp; pass 2: probabilities,
+//             output, and block scores = probabilities summed over the
+//             group's heads by a DPP reduce-scatter, kept in LDS). Each phase
+//             runs its unmasked tiles and its masked edge tiles as separate
+//             straight-line loops. The wave then selects each token's blocks.
+//             Writes gate_win * O_win + gate_cmp * O_cmp into out and the
+//             selection into idx. Workgroups run heaviest first.
 //  k_sel      selected-block branch: a wave walks each of its tokens' chosen
 //             blocks (32-key halves, the next one prefetched into registers
 //             while the current one is computed), straight from the K/V tiles
