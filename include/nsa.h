@@ -51,7 +51,7 @@ extern "C" {
 typedef enum {
   NSA_OK = 0,
   NSA_ERR_INVALID_ARGUMENT = 1,    /* null pointer, bad size, bad stride, ... */
-  NSA_ERR_UNSUPPORTED = 2,         /* valid NSA geometry this build does not run */
+  NSA_ERR_UNSUPPORTED = 2,         /* valid NSA geometry this library does not run */
   NSA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the required size */
   NSA_ERR_HIP = 4                  /* a HIP launch reported an error */
 } nsa_status_t;
