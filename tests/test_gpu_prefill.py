@@ -134,6 +134,19 @@ def test_full_size_prefill_sampled_rows(name):
     assert np.all(np.isfinite(rep["gpu_out"]))
 
 
+@pytest.mark.parametrize("L", [70000, 110000, 200000])
+def test_long_prefill_other_compressed_layouts(L):
+    """Past 64k tokens (D 128, bf16) the block scores leave less LDS for the
+    compressed kernel's stage: 70000 runs it with 8 waves and the low parts
+    of the K means read from L2, 110000 with 4 waves per workgroup, 200000
+    with 2. Sixteen query heads in one group keep the host side small;
+    compared on sampled rows."""
+    cfg = inputs.PrefillConfig(f"long{L}", 1, L, 16, 1, 128, "bf16", top_k=16, window=512)
+    rep = run_case(cfg, rows=_sample_rows(L, n_random=12), check_c=True)
+    assert_rows_well_formed(rep["gpu_idx"], cfg.block)
+    assert np.all(np.isfinite(rep["gpu_out"]))
+
+
 # ------------------------------------------------------------------ properties
 
 def test_bf16_output_matches_fp32_output_to_rounding():
