@@ -161,6 +161,26 @@ nsa_status_t nsa_fwd_prefill(const nsa_prefill_desc_t* desc, const nsa_params_t*
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Chunked prefill: the NSA forward of query positions [q_offset, seqlen)
+ * only, each against the whole context [0, its position] - the prefill half
+ * of serving long prompts in pieces, as with the continuous batching switch
+ * of the NSA how-to's config (qwbw.cn/news/106443, section 3). desc->seqlen
+ * is the context length: k and v hold all seqlen positions as for
+ * nsa_fwd_prefill, while q, gates, out and idx hold only the
+ * seqlen - q_offset query rows (their strides in desc; idx shaped
+ * [B, seqlen - q_offset, G, n]). Every row equals the same row of an
+ * nsa_fwd_prefill over the whole context. 0 <= q_offset <= seqlen, else
+ * NSA_ERR_INVALID_ARGUMENT; q_offset == seqlen does nothing. The workspace
+ * is sized by nsa_prefill_workspace_bytes for the same desc (the context
+ * length decides it). The K/V re-layout covers the whole context on every
+ * call.
+ */
+nsa_status_t nsa_fwd_prefill_chunk(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                                   int32_t q_offset, const void* q, const void* k, const void* v,
+                                   const void* gates, void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * NSA forward for one new token per sequence over a KV cache and a block
  * cache (the decode phase, measured apart from prefill as the NSA how-to
  * advises, section 5). Same arithmetic as one prefill row at t = seqlens[b]-1;

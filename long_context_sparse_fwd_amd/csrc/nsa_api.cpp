@@ -105,7 +105,10 @@ struct PrefillPlan {
   size_t off_kt, off_vt, off_kct, off_kclt, off_vct, off_idx, total;
 };
 
-nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, PrefillPlan* pl) {
+// q_offset: the queries are positions [q_offset, seqlen) (0 for a whole
+// prefill); only the tile counts depend on it, not the workspace.
+nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, PrefillPlan* pl,
+                          int64_t q_offset = 0) {
   if (d == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "desc is NULL");
   if (d->batch < 0 || d->seqlen < 0)
     return fail(NSA_ERR_INVALID_ARGUMENT, "batch and seqlen must be >= 0");
@@ -147,8 +150,9 @@ nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, Pr
                 static_cast<long long>(L));
   const int64_t tok_cmp = static_cast<int64_t>(pl->cmp_waves) * nsa::kCmpTPW;
   const int64_t tok_sel = 4 * static_cast<int64_t>(nsa::kSelTPW);
-  pl->cmp_tiles = static_cast<int>((L + tok_cmp - 1) / tok_cmp);
-  pl->sel_tiles = static_cast<int>((L + tok_sel - 1) / tok_sel);
+  const int64_t Lq = L - q_offset;
+  pl->cmp_tiles = static_cast<int>((Lq + tok_cmp - 1) / tok_cmp);
+  pl->sel_tiles = static_cast<int>((Lq + tok_sel - 1) / tok_sel);
   const size_t elem = d->in_dtype == NSA_BF16 ? 2 : 4;
   const size_t tile = 64 * static_cast<size_t>(D) * elem;
   size_t off = 0;
@@ -262,14 +266,20 @@ nsa_status_t nsa_decode_workspace_bytes(const nsa_decode_desc_t* desc, const nsa
 }
 
 static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
-                                 const void* q, const void* k, const void* v, const void* gates,
-                                 void* out, int32_t* idx, nsa_idx_mode_t idx_mode, void* workspace,
-                                 size_t workspace_bytes, void* stream, void* const* events) {
+                                 int64_t q_offset, const void* q, const void* k, const void* v,
+                                 const void* gates, void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* events) {
+  if (desc == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (q_offset < 0 || q_offset > desc->seqlen)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "q_offset %lld outside [0, seqlen %d]",
+                static_cast<long long>(q_offset), desc->seqlen);
   PrefillPlan pl;
-  NSA_TRY(plan_prefill(desc, params, &pl));
+  NSA_TRY(plan_prefill(desc, params, &pl, q_offset));
   if (idx_mode != NSA_IDX_COMPUTE && idx_mode != NSA_IDX_INJECT)
     return fail(NSA_ERR_INVALID_ARGUMENT, "unknown idx_mode %d", static_cast<int>(idx_mode));
-  if (desc->batch == 0 || desc->seqlen == 0) return ok();  // empty input: nothing to do
+  // empty input or no query rows: nothing to do
+  if (desc->batch == 0 || desc->seqlen == 0 || q_offset == desc->seqlen) return ok();
   NSA_TRY(check_ptr("q", q, true));
   NSA_TRY(check_ptr("k", k, true));
   NSA_TRY(check_ptr("v", v, true));
@@ -291,6 +301,8 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
   std::memset(&a, 0, sizeof(a));
   a.B = desc->batch;
   a.L = desc->seqlen;
+  a.t0 = static_cast<int>(q_offset);
+  a.Lq = desc->seqlen - a.t0;
   a.Hq = desc->n_q_heads;
   a.G = desc->n_kv_heads;
   a.Hg = a.Hq / a.G;
@@ -337,8 +349,16 @@ nsa_status_t nsa_fwd_prefill(const nsa_prefill_desc_t* desc, const nsa_params_t*
                              const void* q, const void* k, const void* v, const void* gates,
                              void* out, int32_t* idx, nsa_idx_mode_t idx_mode, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  return prefill_impl(desc, params, q, k, v, gates, out, idx, idx_mode, workspace, workspace_bytes,
+  return prefill_impl(desc, params, 0, q, k, v, gates, out, idx, idx_mode, workspace, workspace_bytes,
                       stream, nullptr);
+}
+
+nsa_status_t nsa_fwd_prefill_chunk(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                                   int32_t q_offset, const void* q, const void* k, const void* v,
+                                   const void* gates, void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(desc, params, q_offset, q, k, v, gates, out, idx, idx_mode, workspace,
+                      workspace_bytes, stream, nullptr);
 }
 
 nsa_status_t nsa_fwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
@@ -349,7 +369,7 @@ nsa_status_t nsa_fwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_par
   if (stage_events == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "stage_events is NULL");
   for (int i = 0; i <= nsa::kPrefillStages; ++i)
     if (stage_events[i] == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "stage_events[%d] is NULL", i);
-  return prefill_impl(desc, params, q, k, v, gates, out, idx, idx_mode, workspace, workspace_bytes,
+  return prefill_impl(desc, params, 0, q, k, v, gates, out, idx, idx_mode, workspace, workspace_bytes,
                       stream, stage_events);
 }
 

@@ -20,6 +20,7 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 // Everything a prefill launch needs; passed by value to every kernel.
 struct PrefillArgs {
   int B, L, Hq, G, Hg, D, n, w;
+  int t0, Lq;  // the queries are positions [t0, t0 + Lq) = [t0, L) of the L-token context
   int Nb;   // selectable blocks = ceil(L / 64)
   int Nc;   // complete (compressed) blocks = L / 64
   int NcT;  // 64-row chunks of the compressed tiles = ceil(Nc / 64)

@@ -214,8 +214,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int BG = a.B * a.G;
   const int tile = a.cmp_tiles - 1 - static_cast<int>(blockIdx.x) / BG;  // heaviest first
   const int bg = static_cast<int>(blockIdx.x) % BG, b = bg / a.G, g = bg % a.G;
-  const int T0 = tile * TPW * NW;
-  if (T0 >= a.L) return;  // whole workgroup
+  const int T0 = a.t0 + tile * TPW * NW;  // absolute position; query row = position - t0
+  if (T0 >= a.L) return;                   // whole workgroup
   const int col = lane & 15, grp = lane >> 4;
   const bool colv = col < a.Hg;
   const int h = g * a.Hg + col;
@@ -235,9 +235,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool valid = t < a.L && colv;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      qf[qt][s] = valid ? frag_load<T>(Q + static_cast<int64_t>(t) * a.qs[1] + 32 * s) : frag_zero<T>();
-    gcmp[qt] = valid ? to_f32<T>(GT[static_cast<int64_t>(t) * a.gs[1]]) : 0.f;
-    gwin[qt] = valid ? to_f32<T>(GT[static_cast<int64_t>(t) * a.gs[1] + 2]) : 0.f;
+      qf[qt][s] = valid ? frag_load<T>(Q + static_cast<int64_t>(t - a.t0) * a.qs[1] + 32 * s) : frag_zero<T>();
+    gcmp[qt] = valid ? to_f32<T>(GT[static_cast<int64_t>(t - a.t0) * a.gs[1]]) : 0.f;
+    gwin[qt] = valid ? to_f32<T>(GT[static_cast<int64_t>(t - a.t0) * a.gs[1] + 2]) : 0.f;
     nvis[qt] = t < a.L ? (t + 1) >> 6 : 0;
   }
   f32x4 oacc[TPW][DT];
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int qt = 0; qt < TPW; ++qt) {
       const int t = tw + qt;
       if (t < a.L && colv) {
-        SO* o = OUT + static_cast<int64_t>(t) * a.os[1];
+        SO* o = OUT + static_cast<int64_t>(t - a.t0) * a.os[1];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) store4<O>(o + 16 * dt, oacc[qt][dt]);
       }
@@ -515,7 +515,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int qt = 0; qt < TPW; ++qt) {
       const int t = tw + qt;
       if (t >= a.L) break;
-      int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.L + t) * a.G + g) * a.n;
+      int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.Lq + (t - a.t0)) * a.G + g) * a.n;
       topk_wave(sc + qt * NcPad, t >> 6, a.n, row, surv, selb, lane);
     }
   }
@@ -583,7 +583,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int g = item / (a.B * a.sel_tiles);
   const int rem = item % (a.B * a.sel_tiles);
   const int b = rem / a.sel_tiles, tile = rem % a.sel_tiles;
-  const int t0 = (tile * 4 + wave) * TPW;
+  const int t0 = a.t0 + (tile * 4 + wave) * TPW;  // absolute position; query row = position - a.t0
   if (t0 >= a.L) return;
   const int col = lane & 15, grp = lane >> 4;
   const bool colv = col < a.Hg;
@@ -608,7 +608,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const Frag<T> f =
-          (tv && colv) ? frag_load<T>(Q + static_cast<int64_t>(t) * a.qs[1] + 32 * s) : frag_zero<T>();
+          (tv && colv) ? frag_load<T>(Q + static_cast<int64_t>(t - a.t0) * a.qs[1] + 32 * s) : frag_zero<T>();
       const u32x4* w = reinterpret_cast<const u32x4*>(&f);
 #pragma unroll
       for (int e = 0; e < FE; ++e) q_lds[wave][qt][s][e][lane] = w[e];
@@ -620,7 +620,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int t = t0 + qt;
     if (t >= a.L) break;
     const int own = t >> 6;
-    const int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.L + t) * a.G + g) * n;
+    const int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.Lq + (t - a.t0)) * a.G + g) * n;
     const int j = lane < n ? row[lane] : -1;
     if (j >= 0 && j <= own) {  // padding / unusable injected entries drop out
       const uint32_t bit = 1u << qt;
@@ -721,9 +721,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int t = t0 + qt;
     const float lt = col_sum4(l[qt]);
     if (t < a.L && colv) {
-      const float gsl = to_f32<T>(GT[static_cast<int64_t>(t) * a.gs[1] + 1]);
+      const float gsl = to_f32<T>(GT[static_cast<int64_t>(t - a.t0) * a.gs[1] + 1]);
       const float f = lt > 0.f ? gsl / lt : 0.f;
-      SO* o = OUT + static_cast<int64_t>(t) * a.os[1];
+      SO* o = OUT + static_cast<int64_t>(t - a.t0) * a.os[1];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const f32x4 prev = load4<O>(o + 16 * dt);

@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
     L.nsa_fwd_prefill.restype = ctypes.c_int
     L.nsa_fwd_prefill.argtypes = [P(PrefillDesc), P(NsaParams), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                   ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
+    L.nsa_fwd_prefill_chunk.restype = ctypes.c_int
+    L.nsa_fwd_prefill_chunk.argtypes = [P(PrefillDesc), P(NsaParams), c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                        c_vp, ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
     L.nsa_fwd_decode.restype = ctypes.c_int
     L.nsa_fwd_decode.argtypes = [P(DecodeDesc), P(NsaParams), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                  c_vp, c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
@@ -178,6 +181,46 @@ def prefill(q, k, v, gates, *, top_k: int, window: int, block: int = 64, select_
                              _ptr(gates), _ptr(out), _ptr(idx),
                              NSA_IDX_INJECT if inject else NSA_IDX_COMPUTE, _ptr(workspace),
                              workspace.numel(), _stream_of(q)))
+    if idx is not None:
+        return out, idx
+    return out
+
+
+def prefill_chunk(q, k, v, gates, q_offset: int, *, top_k: int, window: int, block: int = 64,
+                  select_block=None, scale: float = 0.0, out=None, out_dtype=None, idx=None,
+                  inject: bool = False, return_idx: bool = False, workspace=None):
+    """Chunked NSA prefill: query positions [q_offset, L) against the L-token
+    context. q [B,Lq,Hq,D] and gates [B,Lq,Hq,3] hold the Lq = L - q_offset
+    query rows, k/v [B,L,G,D] the whole context; out (and idx [B,Lq,G,top_k])
+    have the query rows."""
+    _require_gpu(q, k, v, gates)
+    B, Lq, Hq, D = q.shape
+    _, L, G, _ = k.shape
+    if L - q_offset != Lq or k.shape != (B, L, G, D) or v.shape != k.shape or gates.shape != (B, Lq, Hq, 3):
+        raise ValueError("shape mismatch among q, k, v, gates and q_offset")
+    if not (q.dtype == k.dtype == v.dtype == gates.dtype):
+        raise TypeError("q, k, v and gates must share one dtype")
+    if out is None:
+        out = torch.empty((B, Lq, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if inject and idx is None:
+        raise ValueError("inject=True needs idx")
+    if idx is None and return_idx:
+        idx = torch.empty((B, Lq, G, top_k), dtype=torch.int32, device=q.device)
+    if idx is not None and (idx.dtype != torch.int32 or not idx.is_contiguous()
+                            or tuple(idx.shape) != (B, Lq, G, top_k)):
+        raise ValueError("idx must be a contiguous int32 [B, Lq, G, top_k] tensor")
+    desc = prefill_desc(q, k, v, gates, out)
+    desc.seqlen = L
+    params = make_params(top_k, window, block, select_block, scale)
+    L_ = lib()
+    nbytes = ctypes.c_size_t()
+    check(L_.nsa_prefill_workspace_bytes(ctypes.byref(desc), ctypes.byref(params), ctypes.byref(nbytes)))
+    if workspace is None or workspace.numel() < nbytes.value:
+        workspace = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=q.device)
+    check(L_.nsa_fwd_prefill_chunk(ctypes.byref(desc), ctypes.byref(params), q_offset, _ptr(q), _ptr(k),
+                                   _ptr(v), _ptr(gates), _ptr(out), _ptr(idx),
+                                   NSA_IDX_INJECT if inject else NSA_IDX_COMPUTE, _ptr(workspace),
+                                   workspace.numel(), _stream_of(q)))
     if idx is not None:
         return out, idx
     return out

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function(L):
     names = nsa.header_functions()
     assert {"nsa_fwd_prefill", "nsa_fwd_decode", "nsa_compress_kv", "nsa_prefill_workspace_bytes",
             "nsa_decode_workspace_bytes", "nsa_status_string", "nsa_last_error", "nsa_version",
-            "nsa_fwd_prefill_timed", "nsa_fwd_decode_timed"} <= set(names)
+            "nsa_fwd_prefill_timed", "nsa_fwd_decode_timed", "nsa_fwd_prefill_chunk"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert L.nsa_version() >= 100
@@ -131,6 +131,24 @@ def test_prefill_empty_problem_is_ok_without_launch(L):
     for d in (pdesc(B=0), pdesc(Lq=0)):
         assert L.nsa_fwd_prefill(ctypes.byref(d), ctypes.byref(p), None, None, None, None, None, None,
                                  0, None, 0, None) == OK
+
+
+def test_prefill_chunk_offset_checks(L):
+    """The chunked prefill rejects a query offset outside [0, seqlen] before
+    anything else, and an empty chunk (offset == seqlen) returns without a
+    launch."""
+    d, p = pdesc(Lq=4096), nsa.make_params(16, 512)
+    _, need = ws_prefill(L, d, p)
+    call = lambda off, q=FAKE: L.nsa_fwd_prefill_chunk(ctypes.byref(d), ctypes.byref(p), off, q, FAKE, FAKE,
+                                                      FAKE, FAKE, None, 0, FAKE, need, None)
+    assert call(-1) == INV
+    assert "q_offset" in L.nsa_last_error().decode()
+    assert call(4097) == INV
+    assert call(4096, q=None) == OK           # no query rows: nothing is read
+    assert call(1000, q=None) == INV          # rows to compute, but no q
+    bad = pdesc(Lq=4096, D=96)
+    assert L.nsa_fwd_prefill_chunk(ctypes.byref(bad), ctypes.byref(p), 10, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                   0, FAKE, need, None) == UNS
 
 
 def test_timed_variants_need_events(L):

@@ -147,6 +147,28 @@ def test_long_prefill_other_compressed_layouts(L):
     assert np.all(np.isfinite(rep["gpu_out"]))
 
 
+def test_chunked_prefill_equals_whole_prefill_rows():
+    """nsa_fwd_prefill_chunk over consecutive chunks at unaligned offsets, each
+    seeing the context only up to its end, reproduces the whole prefill's
+    rows bit for bit (output and selection, computed and injected); the whole
+    prefill of the same inputs is checked against the oracle first."""
+    cfg = inputs.PrefillConfig("chunks", 2, 3001, 32, 2, 128, "bf16", top_k=8, window=300)
+    rep = run_case(cfg, rows=_sample_rows(cfg.seqlen, n_random=12), check_c=False)
+    q, k, v, g = rep["tensors"]
+    fo, fi = nsa.prefill(q, k, v, g, top_k=8, window=300, out_dtype=torch.float32, return_idx=True)
+    bounds = [0, 1, 700, 1029, 2048, 2999, 3001]
+    for t0, t1 in zip(bounds[:-1], bounds[1:]):
+        args = (q[:, t0:t1], k[:, :t1], v[:, :t1], g[:, t0:t1], t0)
+        o, i = nsa.prefill_chunk(*args, top_k=8, window=300, out_dtype=torch.float32, return_idx=True)
+        oi = nsa.prefill_chunk(*args, top_k=8, window=300, out_dtype=torch.float32,
+                               idx=fi[:, t0:t1].contiguous(), inject=True)[0]
+        torch.cuda.synchronize()
+        print(f"  chunk [{t0}, {t1}) max |diff| {(o - fo[:, t0:t1]).abs().max().item():.3g}", flush=True)
+        assert torch.equal(i, fi[:, t0:t1]), (t0, t1)
+        assert torch.equal(o, fo[:, t0:t1]), (t0, t1)
+        assert torch.equal(oi, fo[:, t0:t1]), (t0, t1)
+
+
 # ------------------------------------------------------------------ properties
 
 def test_bf16_output_matches_fp32_output_to_rounding():
