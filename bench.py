@@ -229,6 +229,37 @@ def bench_prefill(cfg, steps, warmup, torch, inputs, nsa, raw=None):
     return raw, wall_ms, stage_ms
 
 
+def bench_chunked(cfg, raw, chunk, steps, warmup, torch, nsa):
+    """The same prefill as a sequence of nsa_fwd_prefill_chunk calls over
+    query chunks of `chunk` positions, each against the context up to its
+    end (one step = all chunks); outputs land in one [B, L, Hq, D] tensor."""
+    dev = torch.device("cuda:0")
+    up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v, g = (up(raw[n]) for n in ("q", "k", "v", "gates"))
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(nsa.prefill_workspace_bytes(q, k, v, g, out, top_k=cfg.top_k, window=cfg.window),
+                     dtype=torch.uint8, device=dev)
+    L = cfg.seqlen
+    bounds = list(range(0, L, chunk)) + [L]
+
+    def step():
+        for t0, t1 in zip(bounds[:-1], bounds[1:]):
+            nsa.prefill_chunk(q[:, t0:t1], k[:, :t1], v[:, :t1], g[:, t0:t1], t0, top_k=cfg.top_k,
+                              window=cfg.window, out=out[:, t0:t1], workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    log(f"[bench] chunked prefill {cfg.name} in chunks of {chunk}: {ms:.3f} ms per pass")
+    return {"chunk": chunk, "calls": len(bounds) - 1, "ms_per_pass": ms,
+            "tokens_per_s": cfg.batch * L / (ms * 1e-3)}
+
+
 def bench_decode(cfg, steps, warmup, torch, inputs, nsa):
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
@@ -285,6 +316,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="p64k", choices=["p8k", "p32k", "p64k"])
+    ap.add_argument("--chunk", type=int, default=8192,
+                    help="also time the main config as chunked prefill calls of this many query "
+                         "positions (0: skip)")
     ap.add_argument("--also", default="p8k,p32k",
                     help="shorter prefill configs also reported (their inputs are prefixes of the "
                          "main config's); empty for none")
@@ -377,6 +411,8 @@ def main():
                         "mfma_frac": o_fl / (o_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "kernels_ms": o_stage}
     if others:
         result["other_prefill"] = others
+    if args.chunk > 0:
+        result["chunked_prefill"] = bench_chunked(cfg, raw, args.chunk, args.steps, args.warmup, torch, nsa)
     if not args.no_decode:
         result["decode"] = bench_decode(inputs.CONFIGS["d64k"], args.decode_steps, 3, torch, inputs, nsa)
     if not args.no_cpu_baseline:
