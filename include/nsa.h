@@ -181,6 +181,29 @@ nsa_status_t nsa_fwd_prefill_chunk(const nsa_prefill_desc_t* desc, const nsa_par
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Varlen prefill: sequences of different lengths in one call, each with its
+ * own query range - batching prompts of mixed lengths, and chunks of them,
+ * as the continuous batching switch of the NSA how-to's config (section 3)
+ * asks. desc->seqlen is the row capacity of k and v ([B, seqlen, G, D]);
+ * seq_lens[b] (device, required) is sequence b's context length and
+ * q_offsets[b] (device; NULL means 0) its first query position. Its queries
+ * are positions [q_offsets[b], min(seq_lens[b], q_offsets[b] + query_rows)),
+ * held in rows 0, 1, ... of q, gates, out and idx, which have query_rows
+ * rows per sequence (their strides in desc; idx [B, query_rows, G, n]).
+ * Rows past a sequence's queries are not written, and a sequence with
+ * seq_lens[b] outside [0, seqlen] or q_offsets[b] outside [0, seq_lens[b]]
+ * gets no rows (nothing is written for it). Every row equals the same row of
+ * an nsa_fwd_prefill of that sequence alone. 0 <= query_rows <= seqlen, else
+ * NSA_ERR_INVALID_ARGUMENT; the workspace is sized by
+ * nsa_prefill_workspace_bytes for the same desc.
+ */
+nsa_status_t nsa_fwd_prefill_varlen(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                                    const int32_t* seq_lens, const int32_t* q_offsets,
+                                    int32_t query_rows, const void* q, const void* k, const void* v,
+                                    const void* gates, void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * NSA forward for one new token per sequence over a KV cache and a block
  * cache (the decode phase, measured apart from prefill as the NSA how-to
  * advises, section 5). Same arithmetic as one prefill row at t = seqlens[b]-1;

@@ -265,11 +265,14 @@ nsa_status_t nsa_decode_workspace_bytes(const nsa_decode_desc_t* desc, const nsa
   return ok();
 }
 
+// Sequences: either one query range [q_offset, seqlen) for every sequence
+// (seq_lens == nullptr), or per-sequence device arrays seq_lens / q_offsets
+// with q_offset = seqlen - (rows of the query arrays).
 static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
-                                 int64_t q_offset, const void* q, const void* k, const void* v,
-                                 const void* gates, void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
-                                 void* workspace, size_t workspace_bytes, void* stream,
-                                 void* const* events) {
+                                 int64_t q_offset, const int32_t* seq_lens, const int32_t* q_offsets,
+                                 const void* q, const void* k, const void* v, const void* gates,
+                                 void* out, int32_t* idx, nsa_idx_mode_t idx_mode, void* workspace,
+                                 size_t workspace_bytes, void* stream, void* const* events) {
   if (desc == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "desc is NULL");
   if (q_offset < 0 || q_offset > desc->seqlen)
     return fail(NSA_ERR_INVALID_ARGUMENT, "q_offset %lld outside [0, seqlen %d]",
@@ -280,6 +283,12 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
     return fail(NSA_ERR_INVALID_ARGUMENT, "unknown idx_mode %d", static_cast<int>(idx_mode));
   // empty input or no query rows: nothing to do
   if (desc->batch == 0 || desc->seqlen == 0 || q_offset == desc->seqlen) return ok();
+  if (seq_lens != nullptr) {
+    NSA_TRY(check_ptr("seq_lens", seq_lens, false));
+    if ((reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(q_offsets) & 3u) != 0)
+      return fail(NSA_ERR_INVALID_ARGUMENT, "seq_lens / q_offsets are not 4-byte aligned");
+  }
   NSA_TRY(check_ptr("q", q, true));
   NSA_TRY(check_ptr("k", k, true));
   NSA_TRY(check_ptr("v", v, true));
@@ -301,8 +310,10 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
   std::memset(&a, 0, sizeof(a));
   a.B = desc->batch;
   a.L = desc->seqlen;
-  a.t0 = static_cast<int>(q_offset);
-  a.Lq = desc->seqlen - a.t0;
+  a.t0 = seq_lens != nullptr ? 0 : static_cast<int>(q_offset);
+  a.Lq = desc->seqlen - static_cast<int>(q_offset);
+  a.seq_lens = seq_lens;
+  a.q_offs = seq_lens != nullptr ? q_offsets : nullptr;
   a.Hq = desc->n_q_heads;
   a.G = desc->n_kv_heads;
   a.Hg = a.Hq / a.G;
@@ -349,16 +360,29 @@ nsa_status_t nsa_fwd_prefill(const nsa_prefill_desc_t* desc, const nsa_params_t*
                              const void* q, const void* k, const void* v, const void* gates,
                              void* out, int32_t* idx, nsa_idx_mode_t idx_mode, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  return prefill_impl(desc, params, 0, q, k, v, gates, out, idx, idx_mode, workspace, workspace_bytes,
-                      stream, nullptr);
+  return prefill_impl(desc, params, 0, nullptr, nullptr, q, k, v, gates, out, idx, idx_mode, workspace,
+                      workspace_bytes, stream, nullptr);
 }
 
 nsa_status_t nsa_fwd_prefill_chunk(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
                                    int32_t q_offset, const void* q, const void* k, const void* v,
                                    const void* gates, void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
                                    void* workspace, size_t workspace_bytes, void* stream) {
-  return prefill_impl(desc, params, q_offset, q, k, v, gates, out, idx, idx_mode, workspace,
-                      workspace_bytes, stream, nullptr);
+  return prefill_impl(desc, params, q_offset, nullptr, nullptr, q, k, v, gates, out, idx, idx_mode,
+                      workspace, workspace_bytes, stream, nullptr);
+}
+
+nsa_status_t nsa_fwd_prefill_varlen(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                                    const int32_t* seq_lens, const int32_t* q_offsets,
+                                    int32_t query_rows, const void* q, const void* k, const void* v,
+                                    const void* gates, void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (desc == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (seq_lens == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "seq_lens is NULL");
+  if (query_rows < 0 || query_rows > desc->seqlen)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "query_rows %d outside [0, seqlen %d]", query_rows, desc->seqlen);
+  return prefill_impl(desc, params, static_cast<int64_t>(desc->seqlen) - query_rows, seq_lens, q_offsets, q, k,
+                      v, gates, out, idx, idx_mode, workspace, workspace_bytes, stream, nullptr);
 }
 
 nsa_status_t nsa_fwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
@@ -369,8 +393,8 @@ nsa_status_t nsa_fwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_par
   if (stage_events == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "stage_events is NULL");
   for (int i = 0; i <= nsa::kPrefillStages; ++i)
     if (stage_events[i] == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "stage_events[%d] is NULL", i);
-  return prefill_impl(desc, params, 0, q, k, v, gates, out, idx, idx_mode, workspace, workspace_bytes,
-                      stream, stage_events);
+  return prefill_impl(desc, params, 0, nullptr, nullptr, q, k, v, gates, out, idx, idx_mode, workspace,
+                      workspace_bytes, stream, stage_events);
 }
 
 static nsa_status_t decode_impl(const nsa_decode_desc_t* desc, const nsa_params_t* params,

@@ -21,6 +21,12 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 struct PrefillArgs {
   int B, L, Hq, G, Hg, D, n, w;
   int t0, Lq;  // the queries are positions [t0, t0 + Lq) = [t0, L) of the L-token context
+  // Per-sequence lengths and first query positions (device arrays, or null
+  // for L and t0 above). Sequence b then has a seq_lens[b]-token context and
+  // query positions [q_offs[b], min(seq_lens[b], q_offs[b] + Lq)); Lq is the
+  // number of query rows the q / gates / out / idx arrays hold.
+  const int32_t* seq_lens;
+  const int32_t* q_offs;
   int Nb;   // selectable blocks = ceil(L / 64)
   int Nc;   // complete (compressed) blocks = L / 64
   int NcT;  // 64-row chunks of the compressed tiles = ceil(Nc / 64)

@@ -83,6 +83,19 @@ constexpr int cmp_stage_tiles() {
   return kSplitKc<T> && LOL ? 6 : 4;
 }
 
+// Sequence b's context length and first query position (the uniform L and
+// t0 unless per-sequence arrays are given). A pair outside 0 <= t0 <= L <=
+// a.L gives an empty sequence: no query rows, no key rows.
+struct SeqSpan {
+  int L, t0;
+};
+__device__ __forceinline__ SeqSpan seq_span(const PrefillArgs& a, int b) {
+  if (a.seq_lens == nullptr) return SeqSpan{a.L, a.t0};
+  const int L = a.seq_lens[b], t0 = a.q_offs != nullptr ? a.q_offs[b] : 0;
+  if (L < 0 || L > a.L || t0 < 0 || t0 > L) return SeqSpan{0, 0};
+  return SeqSpan{L, t0};
+}
+
 // ------------------------------------------------------------------ k_prep
 
 template <class T, int D>
@@ -92,6 +105,7 @@ __global__ __launch_bounds__(256) void k_prep(PrefillArgs a) {
   __shared__ __align__(16) S vbuf[64 * D];
   const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
+  const int Lb = __builtin_amdgcn_readfirstlane(seq_span(a, b).L);  // key rows past it are zero-filled
   const bool have = j < a.Nb;
   if (have) {
     const S* K = static_cast<const S*>(a.k) + b * a.ks[0] + g * a.ks[2];
@@ -101,7 +115,7 @@ __global__ __launch_bounds__(256) void k_prep(PrefillArgs a) {
       const int r = e / VPR, c = (e % VPR) * 8;
       const int t = j * 64 + r;
       Frag<T> kf = frag_zero<T>(), vf = frag_zero<T>();
-      if (t < a.L) {
+      if (t < Lb) {
         kf = frag_load<T>(K + static_cast<int64_t>(t) * a.ks[1] + c);
         vf = frag_load<T>(V + static_cast<int64_t>(t) * a.vs[1] + c);
       }
@@ -214,13 +228,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int BG = a.B * a.G;
   const int tile = a.cmp_tiles - 1 - static_cast<int>(blockIdx.x) / BG;  // heaviest first
   const int bg = static_cast<int>(blockIdx.x) % BG, b = bg / a.G, g = bg % a.G;
-  const int T0 = a.t0 + tile * TPW * NW;  // absolute position; query row = position - t0
-  if (T0 >= a.L) return;                   // whole workgroup
+  const SeqSpan sp = seq_span(a, b);
+  const int t0q = __builtin_amdgcn_readfirstlane(sp.t0);  // first query position; query row = position - t0q
+  const int Le = __builtin_amdgcn_readfirstlane(min(sp.L, sp.t0 + a.Lq));  // end of the query positions
+  const int T0 = t0q + tile * TPW * NW;   // absolute position of the workgroup's first token
+  if (T0 >= Le) return;                   // whole workgroup
   const int col = lane & 15, grp = lane >> 4;
   const bool colv = col < a.Hg;
   const int h = g * a.Hg + col;
   const int tw = T0 + TPW * wave;                     // this wave's first token
-  const int Tl = min(T0 + TPW * NW - 1, a.L - 1);     // the workgroup's last token
+  const int Tl = min(T0 + TPW * NW - 1, Le - 1);     // the workgroup's last token
   const float sl2 = a.scale_log2;
   const int64_t bgoff = static_cast<int64_t>(b * a.G + g);
 
@@ -232,13 +249,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int qt = 0; qt < TPW; ++qt) {
     const int t = tw + qt;
-    const bool valid = t < a.L && colv;
+    const bool valid = t < Le && colv;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      qf[qt][s] = valid ? frag_load<T>(Q + static_cast<int64_t>(t - a.t0) * a.qs[1] + 32 * s) : frag_zero<T>();
-    gcmp[qt] = valid ? to_f32<T>(GT[static_cast<int64_t>(t - a.t0) * a.gs[1]]) : 0.f;
-    gwin[qt] = valid ? to_f32<T>(GT[static_cast<int64_t>(t - a.t0) * a.gs[1] + 2]) : 0.f;
-    nvis[qt] = t < a.L ? (t + 1) >> 6 : 0;
+      qf[qt][s] = valid ? frag_load<T>(Q + static_cast<int64_t>(t - t0q) * a.qs[1] + 32 * s) : frag_zero<T>();
+    gcmp[qt] = valid ? to_f32<T>(GT[static_cast<int64_t>(t - t0q) * a.gs[1]]) : 0.f;
+    gwin[qt] = valid ? to_f32<T>(GT[static_cast<int64_t>(t - t0q) * a.gs[1] + 2]) : 0.f;
+    nvis[qt] = t < Le ? (t + 1) >> 6 : 0;
   }
   f32x4 oacc[TPW][DT];
 #pragma unroll
@@ -286,7 +303,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) vf[dt] = frag_load<T>(vt + vtile_frag(dt, s2, lane));
         // all 32 keys inside every token's window: no masks needed
-        const bool full = INNER || (kb >= tw + TPW - a.w && kb + 31 <= tw && tw + TPW - 1 < a.L);
+        const bool full = INNER || (kb >= tw + TPW - a.w && kb + 31 <= tw && tw + TPW - 1 < Le);
 #pragma unroll
         for (int qt = 0; qt < TPW; ++qt) {
           const int t = tw + qt;
@@ -300,7 +317,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           if (full)
             online_step<T, DT, false>(st, kb, 0, 0, grp, sl2, mw[qt], lw[qt], oacc[qt], vf);
           else
-            online_step<T, DT, true>(st, kb, t - a.w + 1, t < a.L ? t : -1, grp, sl2, mw[qt], lw[qt],
+            online_step<T, DT, true>(st, kb, t - a.w + 1, t < Le ? t : -1, grp, sl2, mw[qt], lw[qt],
                                      oacc[qt], vf);
         }
       }
@@ -309,7 +326,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
     // inner blocks: 64 blk >= (last token + 1) - w and 64 blk + 63 <= first token
     int lo = b1 + 1, hi = b1;
-    if (T0 + TPW * NW - 1 < a.L) {
+    if (T0 + TPW * NW - 1 < Le) {
       const int x = T0 + TPW * NW - a.w;  // lowest first key of an inner block
       lo = x <= 0 ? b0 : max(b0, (x + 63) >> 6);
       hi = T0 >= 63 ? min(b1, (T0 - 63) >> 6) : -1;
@@ -498,8 +515,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int qt = 0; qt < TPW; ++qt) {
       const int t = tw + qt;
-      if (t < a.L && colv) {
-        SO* o = OUT + static_cast<int64_t>(t - a.t0) * a.os[1];
+      if (t < Le && colv) {
+        SO* o = OUT + static_cast<int64_t>(t - t0q) * a.os[1];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) store4<O>(o + 16 * dt, oacc[qt][dt]);
       }
@@ -514,8 +531,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll 1
     for (int qt = 0; qt < TPW; ++qt) {
       const int t = tw + qt;
-      if (t >= a.L) break;
-      int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.Lq + (t - a.t0)) * a.G + g) * a.n;
+      if (t >= Le) break;
+      int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.Lq + (t - t0q)) * a.G + g) * a.n;
       topk_wave(sc + qt * NcPad, t >> 6, a.n, row, surv, selb, lane);
     }
   }
@@ -583,8 +600,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int g = item / (a.B * a.sel_tiles);
   const int rem = item % (a.B * a.sel_tiles);
   const int b = rem / a.sel_tiles, tile = rem % a.sel_tiles;
-  const int t0 = a.t0 + (tile * 4 + wave) * TPW;  // absolute position; query row = position - a.t0
-  if (t0 >= a.L) return;
+  const SeqSpan sp = seq_span(a, b);
+  const int t0q = __builtin_amdgcn_readfirstlane(sp.t0);  // first query position; query row = position - t0q
+  const int Le = __builtin_amdgcn_readfirstlane(min(sp.L, sp.t0 + a.Lq));  // end of the query positions
+  const int t0 = t0q + (tile * 4 + wave) * TPW;  // absolute position of the wave's first token
+  if (t0 >= Le) return;
   const int col = lane & 15, grp = lane >> 4;
   const bool colv = col < a.Hg;
   const int h = g * a.Hg + col;
@@ -598,17 +618,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int* steps = reinterpret_cast<int*>(bm + a.sel_bm_words);
 
   // ---- query fragments -> LDS; the wave's half blocks -> bitmap -> step list
-  const int tl = min(t0 + TPW - 1, a.L - 1);
+  const int tl = min(t0 + TPW - 1, Le - 1);
   const int nwords = (2 * ((tl >> 6) + 1) + 3) >> 2;  // half blocks 0 .. 2 own(tl) + 1
   for (int w = lane; w < nwords; w += 64) bm[w] = 0u;
 #pragma unroll
   for (int qt = 0; qt < TPW; ++qt) {
     const int t = t0 + qt;
-    const bool tv = t < a.L;
+    const bool tv = t < Le;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const Frag<T> f =
-          (tv && colv) ? frag_load<T>(Q + static_cast<int64_t>(t - a.t0) * a.qs[1] + 32 * s) : frag_zero<T>();
+          (tv && colv) ? frag_load<T>(Q + static_cast<int64_t>(t - t0q) * a.qs[1] + 32 * s) : frag_zero<T>();
       const u32x4* w = reinterpret_cast<const u32x4*>(&f);
 #pragma unroll
       for (int e = 0; e < FE; ++e) q_lds[wave][qt][s][e][lane] = w[e];
@@ -618,9 +638,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int qt = 0; qt < TPW; ++qt) {
     const int t = t0 + qt;
-    if (t >= a.L) break;
+    if (t >= Le) break;
     const int own = t >> 6;
-    const int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.Lq + (t - a.t0)) * a.G + g) * n;
+    const int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.Lq + (t - t0q)) * a.G + g) * n;
     const int j = lane < n ? row[lane] : -1;
     if (j >= 0 && j <= own) {  // padding / unusable injected entries drop out
       const uint32_t bit = 1u << qt;
@@ -720,10 +740,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int qt = 0; qt < TPW; ++qt) {
     const int t = t0 + qt;
     const float lt = col_sum4(l[qt]);
-    if (t < a.L && colv) {
-      const float gsl = to_f32<T>(GT[static_cast<int64_t>(t - a.t0) * a.gs[1] + 1]);
+    if (t < Le && colv) {
+      const float gsl = to_f32<T>(GT[static_cast<int64_t>(t - t0q) * a.gs[1] + 1]);
       const float f = lt > 0.f ? gsl / lt : 0.f;
-      SO* o = OUT + static_cast<int64_t>(t - a.t0) * a.os[1];
+      SO* o = OUT + static_cast<int64_t>(t - t0q) * a.os[1];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const f32x4 prev = load4<O>(o + 16 * dt);

@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
     L.nsa_fwd_prefill_chunk.restype = ctypes.c_int
     L.nsa_fwd_prefill_chunk.argtypes = [P(PrefillDesc), P(NsaParams), c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
                                         c_vp, ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
+    L.nsa_fwd_prefill_varlen.restype = ctypes.c_int
+    L.nsa_fwd_prefill_varlen.argtypes = [P(PrefillDesc), P(NsaParams), c_vp, c_vp, c_i32, c_vp, c_vp, c_vp,
+                                         c_vp, c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
     L.nsa_fwd_decode.restype = ctypes.c_int
     L.nsa_fwd_decode.argtypes = [P(DecodeDesc), P(NsaParams), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                  c_vp, c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
@@ -221,6 +224,51 @@ def prefill_chunk(q, k, v, gates, q_offset: int, *, top_k: int, window: int, blo
                                    _ptr(v), _ptr(gates), _ptr(out), _ptr(idx),
                                    NSA_IDX_INJECT if inject else NSA_IDX_COMPUTE, _ptr(workspace),
                                    workspace.numel(), _stream_of(q)))
+    if idx is not None:
+        return out, idx
+    return out
+
+
+def prefill_varlen(q, k, v, gates, seq_lens, q_offsets=None, *, top_k: int, window: int, block: int = 64,
+                   select_block=None, scale: float = 0.0, out=None, out_dtype=None, idx=None,
+                   inject: bool = False, return_idx: bool = False, workspace=None):
+    """Varlen NSA prefill. k/v [B,L,G,D] hold up to L context rows per
+    sequence; seq_lens [B] and q_offsets [B] (int32 device tensors) give each
+    sequence's context length and first query position; q [B,R,Hq,D] and
+    gates [B,R,Hq,3] hold R query rows per sequence (row i = position
+    q_offsets[b] + i). out (and idx [B,R,G,top_k]) get those rows; rows past a
+    sequence's queries are left as they are."""
+    _require_gpu(q, k, v, gates, seq_lens)
+    B, R, Hq, D = q.shape
+    _, L, G, _ = k.shape
+    if R > L or k.shape != (B, L, G, D) or v.shape != k.shape or gates.shape != (B, R, Hq, 3):
+        raise ValueError("shape mismatch among q, k, v and gates")
+    for t in (seq_lens,) + ((q_offsets,) if q_offsets is not None else ()):
+        if t.dtype != torch.int32 or tuple(t.shape) != (B,) or not t.is_contiguous():
+            raise ValueError("seq_lens / q_offsets must be contiguous int32 [B] tensors")
+    if not (q.dtype == k.dtype == v.dtype == gates.dtype):
+        raise TypeError("q, k, v and gates must share one dtype")
+    if out is None:
+        out = torch.zeros((B, R, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if inject and idx is None:
+        raise ValueError("inject=True needs idx")
+    if idx is None and return_idx:
+        idx = torch.full((B, R, G, top_k), -1, dtype=torch.int32, device=q.device)
+    if idx is not None and (idx.dtype != torch.int32 or not idx.is_contiguous()
+                            or tuple(idx.shape) != (B, R, G, top_k)):
+        raise ValueError("idx must be a contiguous int32 [B, R, G, top_k] tensor")
+    desc = prefill_desc(q, k, v, gates, out)
+    desc.seqlen = L
+    params = make_params(top_k, window, block, select_block, scale)
+    L_ = lib()
+    nbytes = ctypes.c_size_t()
+    check(L_.nsa_prefill_workspace_bytes(ctypes.byref(desc), ctypes.byref(params), ctypes.byref(nbytes)))
+    if workspace is None or workspace.numel() < nbytes.value:
+        workspace = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=q.device)
+    check(L_.nsa_fwd_prefill_varlen(ctypes.byref(desc), ctypes.byref(params), _ptr(seq_lens), _ptr(q_offsets),
+                                    R, _ptr(q), _ptr(k), _ptr(v), _ptr(gates), _ptr(out), _ptr(idx),
+                                    NSA_IDX_INJECT if inject else NSA_IDX_COMPUTE, _ptr(workspace),
+                                    workspace.numel(), _stream_of(q)))
     if idx is not None:
         return out, idx
     return out

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function(L):
     names = nsa.header_functions()
     assert {"nsa_fwd_prefill", "nsa_fwd_decode", "nsa_compress_kv", "nsa_prefill_workspace_bytes",
             "nsa_decode_workspace_bytes", "nsa_status_string", "nsa_last_error", "nsa_version",
-            "nsa_fwd_prefill_timed", "nsa_fwd_decode_timed", "nsa_fwd_prefill_chunk"} <= set(names)
+            "nsa_fwd_prefill_timed", "nsa_fwd_decode_timed", "nsa_fwd_prefill_chunk", "nsa_fwd_prefill_varlen"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert L.nsa_version() >= 100
@@ -149,6 +149,22 @@ def test_prefill_chunk_offset_checks(L):
     bad = pdesc(Lq=4096, D=96)
     assert L.nsa_fwd_prefill_chunk(ctypes.byref(bad), ctypes.byref(p), 10, FAKE, FAKE, FAKE, FAKE, FAKE, None,
                                    0, FAKE, need, None) == UNS
+
+
+def test_prefill_varlen_checks(L):
+    """The varlen prefill needs seq_lens and a row count in [0, seqlen]; with
+    zero query rows it returns without a launch."""
+    d, p = pdesc(Lq=4096), nsa.make_params(16, 512)
+    _, need = ws_prefill(L, d, p)
+    call = lambda lens, rows, q=FAKE: L.nsa_fwd_prefill_varlen(
+        ctypes.byref(d), ctypes.byref(p), lens, None, rows, q, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, need, None)
+    assert call(None, 100) == INV
+    assert "seq_lens" in L.nsa_last_error().decode()
+    assert call(FAKE, -1) == INV
+    assert call(FAKE, 4097) == INV
+    assert call(FAKE, 0, q=None) == OK      # no query rows: nothing is read
+    assert call(FAKE + 2, 100) == INV       # misaligned lengths
+    assert call(FAKE, 100, q=None) == INV
 
 
 def test_timed_variants_need_events(L):

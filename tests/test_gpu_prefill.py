@@ -169,6 +169,41 @@ def test_chunked_prefill_equals_whole_prefill_rows():
         assert torch.equal(oi, fo[:, t0:t1]), (t0, t1)
 
 
+def test_varlen_prefill_equals_per_sequence_chunks():
+    """nsa_fwd_prefill_varlen with mixed context lengths and query offsets in
+    one call (including a query range cut by the row count and an invalid
+    length) gives, per sequence, the chunked prefill of that sequence alone
+    bit for bit, and leaves every other row untouched."""
+    cfg = inputs.PrefillConfig("varlen", 4, 2100, 16, 2, 128, "bf16", top_k=8, window=300)
+    raw = inputs.make_prefill_inputs(cfg)
+    q, k, v, g = _upload(cfg, raw)
+    B, L, Hq, D = q.shape
+    lens, offs, R = [2100, 1500, 777, 3000], [0, 1000, 700, 0], 1400
+    qv = torch.zeros((B, R, Hq, D), dtype=q.dtype, device=q.device)
+    gv = torch.zeros((B, R, Hq, 3), dtype=g.dtype, device=g.device)
+    rows = [min(ln, o + R) - o if ln <= L else 0 for ln, o in zip(lens, offs)]
+    for b in range(B):
+        if rows[b]:
+            qv[b, :rows[b]] = q[b, offs[b]:offs[b] + rows[b]]
+            gv[b, :rows[b]] = g[b, offs[b]:offs[b] + rows[b]]
+    sl = torch.tensor(lens, dtype=torch.int32, device=q.device)
+    so = torch.tensor(offs, dtype=torch.int32, device=q.device)
+    out, idx = nsa.prefill_varlen(qv, k, v, gv, sl, so, top_k=8, window=300, out_dtype=torch.float32,
+                                  return_idx=True)
+    torch.cuda.synchronize()
+    assert rows == [1400, 500, 77, 0]
+    for b in range(B):
+        n, t0 = rows[b], offs[b]
+        if n:
+            ro, ri = nsa.prefill_chunk(q[b:b + 1, t0:t0 + n], k[b:b + 1, :t0 + n], v[b:b + 1, :t0 + n],
+                                       g[b:b + 1, t0:t0 + n], t0, top_k=8, window=300, out_dtype=torch.float32,
+                                       return_idx=True)
+            torch.cuda.synchronize()
+            assert torch.equal(out[b, :n], ro[0]), b
+            assert torch.equal(idx[b, :n], ri[0]), b
+        assert torch.all(out[b, n:] == 0) and torch.all(idx[b, n:] == -1), b
+
+
 # ------------------------------------------------------------------ properties
 
 def test_bf16_output_matches_fp32_output_to_rounding():
