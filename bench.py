@@ -260,6 +260,35 @@ def bench_chunked(cfg, raw, chunk, steps, warmup, torch, nsa):
             "tokens_per_s": cfg.batch * L / (ms * 1e-3)}
 
 
+def bench_varlen(cfg, raw, steps, warmup, torch, nsa):
+    """One nsa_fwd_prefill_varlen call over four sequences of 1, 3/4, 1/2 and
+    1/4 of the main config's length (all views of its inputs, batch stride 0);
+    each sequence's queries are its whole length."""
+    dev = torch.device("cuda:0")
+    up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v, g = (up(raw[n]) for n in ("q", "k", "v", "gates"))
+    L = cfg.seqlen
+    lens = [L, 3 * L // 4, L // 2, L // 4]
+    nb = len(lens)
+    q4, k4, v4, g4 = (t.expand(nb, *t.shape[1:]) for t in (q, k, v, g))
+    out = torch.empty((nb,) + tuple(q.shape[1:]), dtype=torch.bfloat16, device=dev)
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    ws = torch.empty(nsa.prefill_workspace_bytes(q4, k4, v4, g4, out, top_k=cfg.top_k, window=cfg.window),
+                     dtype=torch.uint8, device=dev)
+    call = lambda: nsa.prefill_varlen(q4, k4, v4, g4, sl, None, top_k=cfg.top_k, window=cfg.window, out=out,
+                                      workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    log(f"[bench] varlen prefill {lens}: {ms:.3f} ms per call")
+    return {"seq_lens": lens, "ms_per_call": ms, "tokens_per_s": sum(lens) / (ms * 1e-3)}
+
+
 def bench_decode(cfg, steps, warmup, torch, inputs, nsa):
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
@@ -319,6 +348,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=8192,
                     help="also time the main config as chunked prefill calls of this many query "
                          "positions (0: skip)")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the varlen prefill of four sequences of mixed lengths")
     ap.add_argument("--also", default="p8k,p32k",
                     help="shorter prefill configs also reported (their inputs are prefixes of the "
                          "main config's); empty for none")
@@ -413,6 +444,8 @@ def main():
         result["other_prefill"] = others
     if args.chunk > 0:
         result["chunked_prefill"] = bench_chunked(cfg, raw, args.chunk, args.steps, args.warmup, torch, nsa)
+    if not args.no_varlen:
+        result["varlen_prefill"] = bench_varlen(cfg, raw, args.steps, args.warmup, torch, nsa)
     if not args.no_decode:
         result["decode"] = bench_decode(inputs.CONFIGS["d64k"], args.decode_steps, 3, torch, inputs, nsa)
     if not args.no_cpu_baseline:
