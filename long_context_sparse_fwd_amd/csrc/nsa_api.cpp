@@ -314,6 +314,9 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
   a.Lq = desc->seqlen - static_cast<int>(q_offset);
   a.seq_lens = seq_lens;
   a.q_offs = seq_lens != nullptr ? q_offsets : nullptr;
+  // k_sel's XCD mapping: contiguous for a whole prefill, interleaved for
+  // chunks and varlen batches (and only where the groups divide the XCDs)
+  a.sel_interleave = (seq_lens != nullptr || q_offset > 0) && 8 % desc->n_kv_heads == 0 ? 1 : 0;
   a.Hq = desc->n_q_heads;
   a.G = desc->n_kv_heads;
   a.Hg = a.Hq / a.G;

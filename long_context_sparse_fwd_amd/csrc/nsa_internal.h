@@ -27,6 +27,7 @@ struct PrefillArgs {
   // number of query rows the q / gates / out / idx arrays hold.
   const int32_t* seq_lens;
   const int32_t* q_offs;
+  int sel_interleave;  // k_sel's XCD mapping: 1 = a group's XCDs take its tiles in turn, 0 = contiguous
   int Nb;   // selectable blocks = ceil(L / 64)
   int Nc;   // complete (compressed) blocks = L / 64
   int NcT;  // 64-row chunks of the compressed tiles = ceil(Nc / 64)

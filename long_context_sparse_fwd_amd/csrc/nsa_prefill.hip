@@ -593,13 +593,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ u32x4 q_lds[4][TPW][KS][FE][64];
   extern __shared__ __align__(16) unsigned char sel_dyn[];  // per wave: bitmap words, then steps
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int N = a.B * a.G * a.sel_tiles;
-  const int per = (N + 7) >> 3;
-  const int item = static_cast<int>(blockIdx.x & 7) * per + static_cast<int>(blockIdx.x >> 3);
-  if (item >= N) return;  // no workgroup barriers in this kernel
-  const int g = item / (a.B * a.sel_tiles);
-  const int rem = item % (a.B * a.sel_tiles);
-  const int b = rem / a.sel_tiles, tile = rem % a.sel_tiles;
+  // This workgroup's (group, sequence, tile); workgroup i runs on XCD i % 8.
+  // Contiguous: each XCD takes an eighth of the (group, sequence, tile)
+  // items in order, so an XCD serves one group, and for a whole prefill the
+  // XCD with the early tokens works from a small set of blocks (the best L2
+  // hit rate, measured). Interleaved (when G divides 8): each group is served
+  // by 8 / G XCDs that take its tiles in turn (k, k + 8/G, ...), sequence
+  // after sequence, so those XCDs get equal shares of every sequence whatever
+  // the lengths (for varlen batches and chunks, measured faster). There are
+  // no workgroup barriers in this kernel, so workgroups without an item exit.
+  int g, b, tile;
+  {
+    const int xcd = static_cast<int>(blockIdx.x & 7), slot = static_cast<int>(blockIdx.x >> 3);
+    if (a.sel_interleave) {
+      const int pg = 8 / a.G, k = xcd / a.G;
+      const int tk = (a.sel_tiles - k + pg - 1) / pg;  // this XCD's tiles of one sequence
+      if (slot >= a.B * tk) return;
+      g = xcd % a.G;
+      b = slot / tk;
+      tile = k + pg * (slot % tk);
+    } else {
+      const int N = a.B * a.G * a.sel_tiles;
+      const int item = xcd * ((N + 7) >> 3) + slot;
+      if (item >= N) return;
+      g = item / (a.B * a.sel_tiles);
+      const int rem = item % (a.B * a.sel_tiles);
+      b = rem / a.sel_tiles;
+      tile = rem % a.sel_tiles;
+    }
+  }
   const SeqSpan sp = seq_span(a, b);
   const int t0q = __builtin_amdgcn_readfirstlane(sp.t0);  // first query position; query row = position - t0q
   const int Le = __builtin_amdgcn_readfirstlane(min(sp.L, sp.t0 + a.Lq));  // end of the query positions
@@ -801,8 +823,8 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st, hipEven
   }
   if (e != hipSuccess) return e;
   if ((e = record(ev, 2, st)) != hipSuccess) return e;
-  const int N = a.B * a.G * a.sel_tiles;
-  const int per = (N + 7) / 8;
+  // workgroups per XCD (see the item mapping in k_sel)
+  const int per = a.sel_interleave ? a.B * ((a.sel_tiles + 8 / a.G - 1) / (8 / a.G)) : (a.B * a.G * a.sel_tiles + 7) / 8;
   // Static + dynamic LDS above half a CU's caps residency at one workgroup
   // (4 waves) per CU, which was measured faster (~13 % at 64k) than two: the
   // gathers then contend less for L2.
