@@ -265,6 +265,24 @@ nsa_status_t nsa_decode_workspace_bytes(const nsa_decode_desc_t* desc, const nsa
   return ok();
 }
 
+// Splits of a KV group's (sequence, tile) items of the selected-block kernel
+// over the group's 8 / G XCDs, for a whole prefill: equal contiguous shares,
+// except for one sequence longer than 32768 tokens shared by two XCDs, where
+// the first XCD (the earlier tokens, whose blocks come from a shorter
+// context) takes 57 % of the tiles. Measured at 64k (k_sel, ms, one box):
+// 50 % 7.72, 55 % 7.48-7.69, 56 % 7.82-7.86, 57 % 7.29-7.30, 57.5 % 7.50-7.55,
+// 58 % 7.90, 60 % 7.79; 57 % was 5-7 % faster than 50 % on every box
+// tried. The dependence is not smooth, so no model is fitted; at 32k the
+// best split measured (55 %) gained ~3 % and is not used.
+static void sel_split(int B, int G, int T, int L, bool interleave, int* bounds) {
+  bounds[0] = -1;
+  if (interleave || G <= 0 || 8 % G != 0 || T <= 0) return;
+  const int pg = 8 / G;
+  const int64_t n_items = static_cast<int64_t>(B) * T;
+  for (int k = 0; k <= pg; ++k) bounds[k] = static_cast<int>(n_items * k / pg);
+  if (pg == 2 && B == 1 && L > 32768) bounds[1] = static_cast<int>((static_cast<int64_t>(T) * 57 + 99) / 100);
+}
+
 // Sequences: either one query range [q_offset, seqlen) for every sequence
 // (seq_lens == nullptr), or per-sequence device arrays seq_lens / q_offsets
 // with q_offset = seqlen - (rows of the query arrays).
@@ -317,6 +335,7 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
   // k_sel's XCD mapping: contiguous for a whole prefill, interleaved for
   // chunks and varlen batches (and only where the groups divide the XCDs)
   a.sel_interleave = (seq_lens != nullptr || q_offset > 0) && 8 % desc->n_kv_heads == 0 ? 1 : 0;
+  sel_split(desc->batch, desc->n_kv_heads, pl.sel_tiles, desc->seqlen, a.sel_interleave != 0, a.sel_bounds);
   a.Hq = desc->n_q_heads;
   a.G = desc->n_kv_heads;
   a.Hg = a.Hq / a.G;

@@ -28,6 +28,10 @@ struct PrefillArgs {
   const int32_t* seq_lens;
   const int32_t* q_offs;
   int sel_interleave;  // k_sel's XCD mapping: 1 = a group's XCDs take its tiles in turn, 0 = contiguous
+  // Contiguous mapping with G dividing 8: the XCDs of a group (8 / G of
+  // them) take the (sequence, tile) items [sel_bounds[k], sel_bounds[k+1])
+  // of the group; sel_bounds[0] = -1 selects the plain eighths instead.
+  int sel_bounds[9];
   int Nb;   // selectable blocks = ceil(L / 64)
   int Nc;   // complete (compressed) blocks = L / 64
   int NcT;  // 64-row chunks of the compressed tiles = ceil(Nc / 64)

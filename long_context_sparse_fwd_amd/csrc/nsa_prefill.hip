@@ -606,12 +606,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   {
     const int xcd = static_cast<int>(blockIdx.x & 7), slot = static_cast<int>(blockIdx.x >> 3);
     if (a.sel_interleave) {
-      const int pg = 8 / a.G, k = xcd / a.G;
+      const int pg = 8 / a.G, k = xcd % pg;  // a group's XCDs are neighbours: xcd / pg = g
       const int tk = (a.sel_tiles - k + pg - 1) / pg;  // this XCD's tiles of one sequence
       if (slot >= a.B * tk) return;
-      g = xcd % a.G;
+      g = xcd / pg;
       b = slot / tk;
       tile = k + pg * (slot % tk);
+    } else if (a.sel_bounds[0] >= 0) {
+      const int pg = 8 / a.G, k = xcd % pg;
+      const int item = a.sel_bounds[k] + slot;
+      if (item >= a.sel_bounds[k + 1]) return;
+      g = xcd / pg;
+      b = item / a.sel_tiles;
+      tile = item % a.sel_tiles;
     } else {
       const int N = a.B * a.G * a.sel_tiles;
       const int item = xcd * ((N + 7) >> 3) + slot;
@@ -824,7 +831,11 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st, hipEven
   if (e != hipSuccess) return e;
   if ((e = record(ev, 2, st)) != hipSuccess) return e;
   // workgroups per XCD (see the item mapping in k_sel)
-  const int per = a.sel_interleave ? a.B * ((a.sel_tiles + 8 / a.G - 1) / (8 / a.G)) : (a.B * a.G * a.sel_tiles + 7) / 8;
+  int per = a.sel_interleave ? a.B * ((a.sel_tiles + 8 / a.G - 1) / (8 / a.G)) : (a.B * a.G * a.sel_tiles + 7) / 8;
+  if (!a.sel_interleave && a.sel_bounds[0] >= 0) {
+    per = 0;
+    for (int k = 0; k < 8 / a.G; ++k) per = max(per, a.sel_bounds[k + 1] - a.sel_bounds[k]);
+  }
   // Static + dynamic LDS above half a CU's caps residency at one workgroup
   // (4 waves) per CU, which was measured faster (~13 % at 64k) than two: the
   // gathers then contend less for L2.
