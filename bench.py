@@ -125,6 +125,20 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def probe_gather_ceiling():
+    """TB/s of random 16 KiB half-block reads from a 32 MiB per-XCD working
+    set (the selected branch's pattern at 64k), as committed from the
+    gather probe (best of its in-flight depths); None if absent."""
+    path = os.path.join(ROOT, "profiles", "gather_ceiling_random_halfblocks.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^\| 32 MiB[^|]*\|([^\n]*)$", open(path).read(), re.M)
+    if not m:
+        return None
+    vals = [float(x) for x in re.findall(r"([0-9]+\.[0-9]+)", m.group(1))]
+    return max(vals) if vals else None
+
+
 def committed_traffic(kernel: str, workload: str):
     """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
     if taken on the current kernel sources; else None."""
@@ -406,6 +420,19 @@ def main():
                 "traffic": committed_traffic(dominant, cfg.name),
                 "work_per_launch": prep_bytes, "avg_launch_ms": stage_ms[dominant]}
 
+    # the selected branch is bound by gathering K/V, not by its MFMA work: its
+    # gathered bytes (D bf16 of K and of V per selected (query token, KV group,
+    # key)), their rate, the rate of its L2 misses (committed counters), and the
+    # gather probe's ceiling for the same pattern
+    slc_keys = pair_counts(cfg.seqlen, cfg.block, cfg.top_k, cfg.window)[1] * cfg.batch * cfg.n_kv_heads
+    gathered = slc_keys * cfg.head_dim * 2 * 2
+    sel_s = stage_ms["k_sel"] * 1e-3
+    sel_traffic = committed_traffic("k_sel", cfg.name)
+    gather = {"kernel": "k_sel", "gathered_bytes_per_launch": gathered,
+              "gathered_TBps": gathered / sel_s / 1e12,
+              "l2_miss_TBps": sel_traffic / sel_s / 1e12 if sel_traffic else None,
+              "probe_random_gather_32MiB_TBps": probe_gather_ceiling()}
+
     result = {
         "metric": "NSA fwd prefill tokens/s & MFMA % peak at 64k; decode HBM GB/s % peak",
         "value": tokens_per_s,
@@ -424,6 +451,7 @@ def main():
                    "compress_block_size": cfg.block, "select_block_size": cfg.block,
                    "select_top_k": cfg.top_k, "sliding_window": cfg.window},
         "roofline": roof,
+        "gather": gather,
         "prefill": {"tflops": total_fl / (wall_ms * 1e-3) / 1e12,
                     "mfma_frac": total_fl / (wall_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                     "algorithmic_flops": fl, "kernels_ms": stage_ms},
