@@ -303,6 +303,51 @@ def bench_varlen(cfg, raw, steps, warmup, torch, nsa):
     return {"seq_lens": lens, "ms_per_call": ms, "tokens_per_s": sum(lens) / (ms * 1e-3)}
 
 
+def bench_shared_selection(cfg, raw, steps, torch, nsa):
+    """The main config with an injected selection in which the 64 query
+    tokens of each block share one random set of earlier blocks per KV group
+    (plus their own block): a stand-in for the locality of real text, where
+    neighbouring tokens read the same passages. A separate, clearly labelled
+    run; per-kernel times as in the main run."""
+    dev = torch.device("cuda:0")
+    up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v, g = (up(raw[n]) for n in ("q", "k", "v", "gates"))
+    B, L, G, n = cfg.batch, cfg.seqlen, cfg.n_kv_heads, cfg.top_k
+    rng = np.random.default_rng(1)
+    nqb = (L + 63) // 64
+    rows = np.full((B, nqb, G, n), -1, dtype=np.int32)
+    for b in range(B):
+        for qb in range(nqb):
+            m = min(n - 1, qb)
+            for gg in range(G):
+                rows[b, qb, gg, :m + 1] = np.sort(np.append(rng.choice(qb, m, replace=False), qb))
+    idx = torch.from_numpy(np.ascontiguousarray(np.repeat(rows, 64, axis=1)[:, :L])).to(dev)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(nsa.prefill_workspace_bytes(q, k, v, g, out, top_k=n, window=cfg.window), dtype=torch.uint8,
+                     device=dev)
+    ns = len(PREFILL_STAGES) + 1
+    ev = HipEvents(ns * steps)
+    desc = nsa.prefill_desc(q, k, v, g, out)
+    params = nsa.make_params(n, cfg.window)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    call = lambda evs: nsa.check(nsa.lib().nsa_fwd_prefill_timed(
+        ctypes.byref(desc), ctypes.byref(params), ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+        ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(g.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+        ctypes.c_void_p(idx.data_ptr()), nsa.NSA_IDX_INJECT, ctypes.c_void_p(ws.data_ptr()), ws.numel(), stream,
+        evs))
+    call(ev.array(0, ns))  # warm-up
+    torch.cuda.synchronize()
+    for i in range(steps):
+        call(ev.array(i * ns, ns))
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([ev.elapsed_ms(i * ns + s_, i * ns + s_ + 1) for i in range(steps)]))
+                for s_, name in enumerate(PREFILL_STAGES)}
+    ev.close()
+    log(f"[bench] shared-selection prefill {cfg.name}: kernels {stage_ms}")
+    return {"selection": "injected; the 64 query tokens of a block share one random block set per KV group",
+            "kernels_ms": stage_ms, "note": "not the headline workload (its selection is computed)"}
+
+
 def bench_decode(cfg, steps, warmup, torch, inputs, nsa):
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
@@ -364,6 +409,8 @@ def main():
                          "positions (0: skip)")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the varlen prefill of four sequences of mixed lengths")
+    ap.add_argument("--no-shared-selection", action="store_true",
+                    help="skip the run with an injected selection shared by neighbouring tokens")
     ap.add_argument("--also", default="p8k,p32k",
                     help="shorter prefill configs also reported (their inputs are prefixes of the "
                          "main config's); empty for none")
@@ -474,6 +521,8 @@ def main():
         result["chunked_prefill"] = bench_chunked(cfg, raw, args.chunk, args.steps, args.warmup, torch, nsa)
     if not args.no_varlen:
         result["varlen_prefill"] = bench_varlen(cfg, raw, args.steps, args.warmup, torch, nsa)
+    if not args.no_shared_selection:
+        result["shared_selection_prefill"] = bench_shared_selection(cfg, raw, args.steps, torch, nsa)
     if not args.no_decode:
         result["decode"] = bench_decode(inputs.CONFIGS["d64k"], args.decode_steps, 3, torch, inputs, nsa)
     if not args.no_cpu_baseline:

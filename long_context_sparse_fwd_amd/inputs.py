@@ -9,8 +9,9 @@ Recipe (stated once, used everywhere):
 * Every tensor is built from 64-token chunks. Chunk ``(tensor_id, b, blk)`` is
   ``numpy.random.Generator(PCG64(SeedSequence([seed, tensor_id, b, blk])))
   .standard_normal(shape, dtype=float32)``. Tensor ids: 0 = Q, 1 = K, 2 = V,
-  3 = gate logits. Chunk shapes are ``(64, Hq, D)``, ``(64, G, D)``,
-  ``(64, G, D)`` and ``(64, Hq, 3)``.
+  3 = gate logits, 4 = the upstream gradient of the output (backward pass).
+  Chunk shapes are ``(64, Hq, D)``, ``(64, G, D)``, ``(64, G, D)``,
+  ``(64, Hq, 3)`` and ``(64, Hq, D)``.
 * Because the key never contains the sequence length, a shorter workload is an
   exact prefix of a longer one with the same seed and heads.
 * bf16 values are the float32 draw rounded to nearest-even (stored as uint16
@@ -37,7 +38,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-TID_Q, TID_K, TID_V, TID_GATE = 0, 1, 2, 3
+TID_Q, TID_K, TID_V, TID_GATE, TID_DOUT = 0, 1, 2, 3, 4
 CHUNK = 64
 
 
@@ -184,6 +185,19 @@ def make_prefill_inputs(cfg: PrefillConfig, threads: int | None = None) -> dict:
     else:
         with ThreadPoolExecutor(nw) as ex:
             list(ex.map(work, items))
+    return out
+
+
+def make_dout(cfg: PrefillConfig, dtype: str | None = None) -> np.ndarray:
+    """Upstream gradient dout [B,L,Hq,D] in stored form (tensor id 4), in the
+    output's dtype (the input dtype unless given)."""
+    B, L, Hq, D = cfg.batch, cfg.seqlen, cfg.n_q_heads, cfg.head_dim
+    dt = dtype or cfg.dtype
+    out = np.empty((B, L, Hq, D), storage_dtype(dt))
+    for b in range(B):
+        for blk in range((L + CHUNK - 1) // CHUNK):
+            t0, t1 = blk * CHUNK, min(L, (blk + 1) * CHUNK)
+            out[b, t0:t1] = encode(chunk_normal(cfg.seed, TID_DOUT, b, blk, (CHUNK, Hq, D))[: t1 - t0], dt)
     return out
 
 
