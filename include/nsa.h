@@ -253,6 +253,47 @@ nsa_status_t nsa_fwd_decode_timed(const nsa_decode_desc_t* desc, const nsa_param
                                   int32_t* idx, nsa_idx_mode_t idx_mode, void* workspace,
                                   size_t workspace_bytes, void* stream, void* const* stage_events);
 
+/*
+ * Backward pass of the prefill: the gradients of sum(out * dout) with respect
+ * to q, k, v and gates, for the block selection `idx` held fixed (the top-k
+ * choice is piecewise constant, so it carries no gradient). NSA is trained end
+ * to end, with the backward pass claimed to gain from the same sparsity as the
+ * forward (NSA how-to, qwbw.cn/news/106443, section 1); each branch is
+ * softmax attention over its key set, and the compressed branch's keys and
+ * values are block means, so their gradients are spread evenly over the 64
+ * tokens of each complete block.
+ *
+ * desc, params, q, k, v, gates: as for nsa_fwd_prefill (same layouts, dtypes,
+ *   strides and limits). dout [B, L, Hq, D] is the upstream gradient, in
+ *   desc->out_dtype with the strides desc->o_stride (element size aligned).
+ * idx [B, L, G, top_k] int32, contiguous, required: the selection the
+ *   forward used (its NSA_IDX_COMPUTE output, or the injected one), read with
+ *   the injected-selection rule (entries outside [0, t/64] and repeats add
+ *   nothing).
+ * dq [B, L, Hq, D], dk / dv [B, L, G, D], dgates [B, L, Hq, 3]: contiguous
+ *   float32 outputs, written in full (dq 16-byte aligned, the rest 4-byte).
+ *   dgates[..., x] = dout . o_x, the gradient of gate x of branch x in the
+ *   order (compressed, selected, window).
+ * workspace: device memory of at least nsa_bwd_prefill_workspace_bytes()
+ *   bytes (16-byte aligned), caller-owned, contents not preserved. The call
+ *   is asynchronous on `stream`; inputs must stay valid until it completes.
+ * dk and dv are sums accumulated with floating-point atomics, so their last
+ * bits may differ from call to call. Errors are reported as for the forward
+ * entry points; a failing call launches nothing.
+ */
+nsa_status_t nsa_bwd_prefill_workspace_bytes(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                                             size_t* bytes);
+nsa_status_t nsa_bwd_prefill(const nsa_prefill_desc_t* desc, const nsa_params_t* params, const void* q,
+                             const void* k, const void* v, const void* gates, const void* dout,
+                             const int32_t* idx, float* dq, float* dk, float* dv, float* dgates,
+                             void* workspace, size_t workspace_bytes, void* stream);
+/* nsa_bwd_prefill with 4 stage events (prep; query side; key side). */
+nsa_status_t nsa_bwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_params_t* params, const void* q,
+                                   const void* k, const void* v, const void* gates, const void* dout,
+                                   const int32_t* idx, float* dq, float* dk, float* dv, float* dgates,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   void* const* stage_events);
+
 /* Static name of a status code. */
 const char* nsa_status_string(nsa_status_t status);
 

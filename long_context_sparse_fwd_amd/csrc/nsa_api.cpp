@@ -3,6 +3,7 @@
 // enqueued; a failing call launches nothing and writes nothing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -168,6 +169,77 @@ nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, Pr
   off = align_up(off + static_cast<size_t>(B * G) * pl->NcT * tile);
   pl->off_idx = off;
   off = align_up(off + static_cast<size_t>(B * L * G) * p->select_top_k * sizeof(int32_t));
+  pl->total = off;
+  return NSA_OK;
+}
+
+// ------------------------------------------------------------------ backward
+
+struct BwdPlan {
+  int Nb, Nc, NcT, units[3];
+  size_t off_ka, off_kv, off_va, off_vv, off_kcm, off_vcm, off_kca, off_kcv, off_vca, off_vcv;
+  size_t off_qT, off_dT, off_dN, off_stat, off_dkc, off_dvc, off_cnt, off_offs, off_pofs, off_list, total;
+};
+
+nsa_status_t plan_backward(const nsa_prefill_desc_t* d, const nsa_params_t* p, BwdPlan* pl) {
+  if (d == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->batch < 0 || d->seqlen < 0)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "batch and seqlen must be >= 0");
+  NSA_TRY(check_heads(d->n_q_heads, d->n_kv_heads, d->head_dim));
+  NSA_TRY(check_dtypes(d->in_dtype, d->out_dtype));
+  NSA_TRY(check_params(p, d->head_dim));
+  NSA_TRY(check_strides("q", d->q_stride, 3, true));
+  NSA_TRY(check_strides("k", d->k_stride, 3, true));
+  NSA_TRY(check_strides("v", d->v_stride, 3, true));
+  NSA_TRY(check_strides("gates", d->g_stride, 3, false));
+  NSA_TRY(check_strides("dout", d->o_stride, 3, false));
+  const int64_t B = d->batch, L = d->seqlen, G = d->n_kv_heads, D = d->head_dim, Hq = d->n_q_heads;
+  if (B * L * Hq * D > INT32_MAX * 4LL || B * L * G * p->select_top_k > INT32_MAX ||
+      B * G * ((L + 63) / 64) * 64 > INT32_MAX || B * L * G > INT32_MAX / 16)
+    return fail(NSA_ERR_UNSUPPORTED, "problem too large for 32-bit work indexing");
+  pl->Nb = static_cast<int>((L + 63) / 64);
+  pl->Nc = static_cast<int>(L / 64);
+  pl->NcT = (pl->Nc + 63) / 64;
+  // key-side workgroups per (sequence, group): compressed, pieces of
+  // kBwdCmpPiece tokens of [64*64c + 63, L) per 64-mean chunk; selected, at
+  // most one piece per block plus one per kBwdSelPiece list entries; window,
+  // one per 64-key chunk (its 63 + w tokens)
+  const int64_t cmp_pieces = std::max<int64_t>(1, (L + nsa::kBwdCmpPiece - 1) / nsa::kBwdCmpPiece);
+  pl->units[0] = static_cast<int>(pl->NcT * cmp_pieces);
+  pl->units[1] = static_cast<int>(pl->Nb + (L * p->select_top_k + nsa::kBwdSelPiece - 1) / nsa::kBwdSelPiece);
+  pl->units[2] = pl->Nb;
+  if (B * G * std::max<int64_t>(pl->units[0], pl->units[1]) > INT32_MAX)
+    return fail(NSA_ERR_UNSUPPORTED, "problem too large for 32-bit work indexing");
+  const size_t elem = d->in_dtype == NSA_BF16 ? 2 : 4;
+  const size_t tiles = static_cast<size_t>(B * G) * pl->Nb * 64 * D * elem;
+  const size_t ctiles = static_cast<size_t>(B * G) * pl->NcT * 64 * D * elem;
+  const size_t means = static_cast<size_t>(B) * pl->Nc * G * D * elem;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  pl->off_ka = take(tiles);
+  pl->off_kv = take(tiles);
+  pl->off_va = take(tiles);
+  pl->off_vv = take(tiles);
+  pl->off_kcm = take(means);
+  pl->off_vcm = take(means);
+  pl->off_kca = take(ctiles);
+  pl->off_kcv = take(ctiles);
+  pl->off_vca = take(ctiles);
+  pl->off_vcv = take(ctiles);
+  pl->off_qT = take(static_cast<size_t>(B * L * G) * D * 16 * elem);
+  pl->off_dT = take(static_cast<size_t>(B * L * G) * D * 16 * elem);
+  pl->off_dN = take(static_cast<size_t>(B * L * Hq) * D * elem);
+  pl->off_stat = take(static_cast<size_t>(B * L * Hq) * 3 * 2 * sizeof(float));
+  pl->off_dkc = take(static_cast<size_t>(B) * pl->Nc * G * D * sizeof(float));
+  pl->off_dvc = take(static_cast<size_t>(B) * pl->Nc * G * D * sizeof(float));
+  pl->off_cnt = take(static_cast<size_t>(B * G) * pl->Nb * sizeof(int32_t));
+  pl->off_offs = take(static_cast<size_t>(B * G) * (pl->Nb + 1) * sizeof(int32_t));
+  pl->off_pofs = take(static_cast<size_t>(B * G) * (pl->Nb + 1) * sizeof(int32_t));
+  pl->off_list = take(static_cast<size_t>(B * G * L) * p->select_top_k * sizeof(int32_t));
   pl->total = off;
   return NSA_OK;
 }
@@ -405,6 +477,124 @@ nsa_status_t nsa_fwd_prefill_varlen(const nsa_prefill_desc_t* desc, const nsa_pa
     return fail(NSA_ERR_INVALID_ARGUMENT, "query_rows %d outside [0, seqlen %d]", query_rows, desc->seqlen);
   return prefill_impl(desc, params, static_cast<int64_t>(desc->seqlen) - query_rows, seq_lens, q_offsets, q, k,
                       v, gates, out, idx, idx_mode, workspace, workspace_bytes, stream, nullptr);
+}
+
+static nsa_status_t backward_impl(const nsa_prefill_desc_t* desc, const nsa_params_t* params, const void* q,
+                                  const void* k, const void* v, const void* gates, const void* dout,
+                                  const int32_t* idx, float* dq, float* dk, float* dv, float* dgates,
+                                  void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+  BwdPlan pl;
+  NSA_TRY(plan_backward(desc, params, &pl));
+  if (desc->batch == 0 || desc->seqlen == 0) return ok();
+  NSA_TRY(check_ptr("q", q, true));
+  NSA_TRY(check_ptr("k", k, true));
+  NSA_TRY(check_ptr("v", v, true));
+  NSA_TRY(check_ptr("gates", gates, false));
+  NSA_TRY(check_ptr("dout", dout, false));
+  NSA_TRY(check_ptr("idx", idx, false));
+  NSA_TRY(check_ptr("dq", dq, true));
+  NSA_TRY(check_ptr("dk", dk, false));
+  NSA_TRY(check_ptr("dv", dv, false));
+  NSA_TRY(check_ptr("dgates", dgates, false));
+  NSA_TRY(check_ptr("workspace", workspace, true));
+  const size_t gal = desc->in_dtype == NSA_BF16 ? 2 : 4, oal = desc->out_dtype == NSA_BF16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(gates) % gal) != 0)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "gates is not aligned to its element size");
+  if ((reinterpret_cast<uintptr_t>(dout) % oal) != 0)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "dout is not aligned to its element size");
+  if ((reinterpret_cast<uintptr_t>(idx) & 3u) != 0 || (reinterpret_cast<uintptr_t>(dk) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(dv) & 3u) != 0 || (reinterpret_cast<uintptr_t>(dgates) & 3u) != 0)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "idx / dk / dv / dgates are not 4-byte aligned");
+  if (workspace_bytes < pl.total)
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", pl.total, workspace_bytes);
+  nsa::BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = desc->batch;
+  a.L = desc->seqlen;
+  a.Hq = desc->n_q_heads;
+  a.G = desc->n_kv_heads;
+  a.Hg = a.Hq / a.G;
+  a.D = desc->head_dim;
+  a.n = params->select_top_k;
+  a.w = params->sliding_window;
+  a.Nb = pl.Nb;
+  a.Nc = pl.Nc;
+  a.NcT = pl.NcT;
+  for (int i = 0; i < 3; ++i) a.bkv_units[i] = pl.units[i];
+  a.scale_log2 = scale_log2(params, a.D);
+  a.scale = a.scale_log2 / nsa::kLog2eHost;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.gates = gates;
+  a.dout = dout;
+  a.idx = idx;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dgates = dgates;
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = desc->q_stride[i];
+    a.ks[i] = desc->k_stride[i];
+    a.vs[i] = desc->v_stride[i];
+    a.gs[i] = desc->g_stride[i];
+    a.os[i] = desc->o_stride[i];
+  }
+  char* ws = static_cast<char*>(workspace);
+  a.ka = ws + pl.off_ka;
+  a.kv = ws + pl.off_kv;
+  a.va = ws + pl.off_va;
+  a.vv = ws + pl.off_vv;
+  a.kcm = ws + pl.off_kcm;
+  a.vcm = ws + pl.off_vcm;
+  a.kca = ws + pl.off_kca;
+  a.kcv = ws + pl.off_kcv;
+  a.vca = ws + pl.off_vca;
+  a.vcv = ws + pl.off_vcv;
+  a.qT = ws + pl.off_qT;
+  a.dT = ws + pl.off_dT;
+  a.dN = ws + pl.off_dN;
+  a.stat = reinterpret_cast<float2*>(ws + pl.off_stat);
+  a.dkc = reinterpret_cast<float*>(ws + pl.off_dkc);
+  a.dvc = reinterpret_cast<float*>(ws + pl.off_dvc);
+  a.cnt = reinterpret_cast<int32_t*>(ws + pl.off_cnt);
+  a.offs = reinterpret_cast<int32_t*>(ws + pl.off_offs);
+  a.pofs = reinterpret_cast<int32_t*>(ws + pl.off_pofs);
+  a.list = reinterpret_cast<int32_t*>(ws + pl.off_list);
+  hipError_t e = nsa::launch_backward(a, desc->in_dtype == NSA_BF16, desc->out_dtype == NSA_BF16,
+                                      static_cast<hipStream_t>(stream),
+                                      reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)));
+  if (e != hipSuccess) return fail(NSA_ERR_HIP, "HIP error in backward launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+nsa_status_t nsa_bwd_prefill_workspace_bytes(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                                             size_t* bytes) {
+  if (bytes == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  BwdPlan pl;
+  NSA_TRY(plan_backward(desc, params, &pl));
+  *bytes = pl.total;
+  return ok();
+}
+
+nsa_status_t nsa_bwd_prefill(const nsa_prefill_desc_t* desc, const nsa_params_t* params, const void* q,
+                             const void* k, const void* v, const void* gates, const void* dout,
+                             const int32_t* idx, float* dq, float* dk, float* dv, float* dgates,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(desc, params, q, k, v, gates, dout, idx, dq, dk, dv, dgates, workspace, workspace_bytes,
+                       stream, nullptr);
+}
+
+nsa_status_t nsa_bwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_params_t* params, const void* q,
+                                   const void* k, const void* v, const void* gates, const void* dout,
+                                   const int32_t* idx, float* dq, float* dk, float* dv, float* dgates,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   void* const* stage_events) {
+  if (stage_events == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "stage_events is NULL");
+  for (int i = 0; i <= nsa::kBwdStages; ++i)
+    if (stage_events[i] == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "stage_events[%d] is NULL", i);
+  return backward_impl(desc, params, q, k, v, gates, dout, idx, dq, dk, dv, dgates, workspace, workspace_bytes,
+                       stream, stage_events);
 }
 
 nsa_status_t nsa_fwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_params_t* params,

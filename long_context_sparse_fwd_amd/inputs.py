@@ -201,6 +201,29 @@ def make_dout(cfg: PrefillConfig, dtype: str | None = None) -> np.ndarray:
     return out
 
 
+def make_selection(cfg: PrefillConfig, share: int = 8) -> np.ndarray:
+    """A seeded block selection idx [B,L,G,top_k] int32 in the forward's
+    output form: each row holds the token's own block t // 64 and top_k - 1
+    distinct earlier blocks drawn uniformly (all of them when there are fewer),
+    ascending, padded with -1. The ``share`` consecutive tokens of an aligned
+    group draw one set (their own block is the same). A stand-in selection for
+    the backward pass, whose gradients take the selection as given."""
+    B, L, G, n = cfg.batch, cfg.seqlen, cfg.n_kv_heads, cfg.top_k
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, 5])))
+    idx = np.full((B, L, G, n), -1, dtype=np.int32)
+    for t0 in range(0, L, share):
+        own = t0 // CHUNK
+        m = min(n - 1, own)
+        if m < own:
+            pick = np.argpartition(rng.random((B, G, own)), m - 1, axis=2)[..., :m] if m > 0 else \
+                np.zeros((B, G, 0), np.int64)
+        else:
+            pick = np.broadcast_to(np.arange(own), (B, G, own))
+        rows = np.sort(np.concatenate([pick, np.full((B, G, 1), own)], axis=2), axis=2).astype(np.int32)
+        idx[:, t0: t0 + share, :, : m + 1] = rows[:, None]
+    return idx
+
+
 def make_decode_inputs(cfg: DecodeConfig, threads: int | None = None) -> dict:
     """q [B,Hq,D], k/v cache [B,G,Lmax,D], gates [B,Hq,3], seqlens [B] int32."""
     B, Lm, Hq, G, D = cfg.batch, cfg.max_seqlen, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim

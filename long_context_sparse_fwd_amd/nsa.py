@@ -86,6 +86,13 @@ def lib() -> ctypes.CDLL:
     L.nsa_fwd_decode.restype = ctypes.c_int
     L.nsa_fwd_decode.argtypes = [P(DecodeDesc), P(NsaParams), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                  c_vp, c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
+    L.nsa_bwd_prefill_workspace_bytes.restype = ctypes.c_int
+    L.nsa_bwd_prefill_workspace_bytes.argtypes = [P(PrefillDesc), P(NsaParams), P(ctypes.c_size_t)]
+    L.nsa_bwd_prefill.restype = ctypes.c_int
+    L.nsa_bwd_prefill.argtypes = [P(PrefillDesc), P(NsaParams), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                  c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]
+    L.nsa_bwd_prefill_timed.restype = ctypes.c_int
+    L.nsa_bwd_prefill_timed.argtypes = L.nsa_bwd_prefill.argtypes + [c_vp]
     L.nsa_compress_kv.restype = ctypes.c_int
     L.nsa_compress_kv.argtypes = [c_i32, c_i32, c_i32, c_i32, ctypes.c_int, c_i32, c_vp, P(c_i64),
                                   c_vp, P(c_i64), c_vp, P(c_i64), c_vp, P(c_i64), c_vp]
@@ -280,6 +287,48 @@ def prefill_workspace_bytes(q, k, v, gates, out, *, top_k, window, block=64) -> 
     nbytes = ctypes.c_size_t()
     check(lib().nsa_prefill_workspace_bytes(ctypes.byref(desc), ctypes.byref(params), ctypes.byref(nbytes)))
     return nbytes.value
+
+
+def prefill_backward_workspace_bytes(q, k, v, gates, dout, *, top_k, window, block=64) -> int:
+    desc = prefill_desc(q, k, v, gates, dout)
+    params = make_params(top_k, window, block)
+    nbytes = ctypes.c_size_t()
+    check(lib().nsa_bwd_prefill_workspace_bytes(ctypes.byref(desc), ctypes.byref(params), ctypes.byref(nbytes)))
+    return nbytes.value
+
+
+def prefill_backward(q, k, v, gates, dout, idx, *, top_k: int, window: int, block: int = 64,
+                     scale: float = 0.0, grads=None, workspace=None):
+    """Gradients of sum(out * dout) of the NSA prefill for the fixed selection idx.
+
+    q, k, v, gates as for prefill(); dout [B,L,Hq,D] in the output dtype;
+    idx [B,L,G,top_k] int32 (the forward's selection). Returns float32
+    (dq, dk, dv, dgates); `grads` may supply those four contiguous tensors.
+    """
+    _require_gpu(q, k, v, gates, dout, idx)
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 tensor")
+    B, L, Hq, D = q.shape
+    G = k.shape[2]
+    if tuple(idx.shape) != (B, L, G, top_k):
+        raise ValueError(f"idx shape {tuple(idx.shape)} != {(B, L, G, top_k)}")
+    if grads is None:
+        f32 = dict(dtype=torch.float32, device=q.device)
+        grads = (torch.empty((B, L, Hq, D), **f32), torch.empty((B, L, G, D), **f32),
+                 torch.empty((B, L, G, D), **f32), torch.empty((B, L, Hq, 3), **f32))
+    for gtn in grads:
+        if gtn.dtype != torch.float32 or not gtn.is_contiguous():
+            raise ValueError("gradient outputs must be contiguous float32 tensors")
+    desc = prefill_desc(q, k, v, gates, dout)
+    params = make_params(top_k, window, block, scale=scale)
+    if workspace is None:
+        workspace = torch.empty(prefill_backward_workspace_bytes(q, k, v, gates, dout, top_k=top_k,
+                                                                 window=window, block=block),
+                                dtype=torch.uint8, device=q.device)
+    check(lib().nsa_bwd_prefill(ctypes.byref(desc), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(gates),
+                                _ptr(dout), _ptr(idx), *(_ptr(x) for x in grads), _ptr(workspace),
+                                workspace.numel(), _stream_of(q)))
+    return grads
 
 
 def decode_desc(q, k_cache, v_cache, kc_cache, vc_cache, gates, out) -> DecodeDesc:

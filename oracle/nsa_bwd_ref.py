@@ -53,13 +53,16 @@ def _attend_backward(qg, keys, vals, dout_g, gate, scale):
 
 
 def prefill_backward(q, k, v, gates, dout, idx, *, block: int = 64, select_block=None,
-                     top_k: int, window: int, scale=None) -> dict:
+                     top_k: int, window: int, scale=None, rows=None) -> dict:
     """Gradients of the NSA prefill for a fixed selection ``idx`` [B, L, G, top_k].
 
     q [B, L, Hq, D]; k, v [B, L, G, D]; gates [B, L, Hq, 3]; dout [B, L, Hq, D].
     ``idx`` follows the injected-selection rule R12 (a set of blocks; entries
     outside [0, t // block] and repeats add nothing). Returns float64 dq, dk,
-    dv and dgates of the input shapes.
+    dv and dgates of the input shapes. ``rows`` restricts the query positions
+    taken into account (all by default): dq and dgates are then filled for
+    those rows only, and dk / dv hold the sums over those rows' terms, which is
+    the whole gradient for keys seen by no other row.
     """
     _check_blocks(block, select_block)
     B, L, Hq, D = q.shape
@@ -78,7 +81,8 @@ def prefill_backward(q, k, v, gates, dout, idx, *, block: int = 64, select_block
         Vc = compress(V[None], block)[0]
         dKc = np.zeros_like(Kc)
         dVc = np.zeros_like(Vc)
-        for t in range(L):
+        for t in (range(L) if rows is None else rows):
+            t = int(t)
             qt = np.asarray(q[b, t], dtype=np.float64)
             gt = np.asarray(gates[b, t], dtype=np.float64)
             dt = np.asarray(dout[b, t], dtype=np.float64)

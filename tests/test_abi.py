@@ -26,7 +26,8 @@ def test_library_exports_every_declared_function(L):
     names = nsa.header_functions()
     assert {"nsa_fwd_prefill", "nsa_fwd_decode", "nsa_compress_kv", "nsa_prefill_workspace_bytes",
             "nsa_decode_workspace_bytes", "nsa_status_string", "nsa_last_error", "nsa_version",
-            "nsa_fwd_prefill_timed", "nsa_fwd_decode_timed", "nsa_fwd_prefill_chunk", "nsa_fwd_prefill_varlen"} <= set(names)
+            "nsa_fwd_prefill_timed", "nsa_fwd_decode_timed", "nsa_fwd_prefill_chunk", "nsa_fwd_prefill_varlen",
+            "nsa_bwd_prefill", "nsa_bwd_prefill_timed", "nsa_bwd_prefill_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert L.nsa_version() >= 100
@@ -177,6 +178,47 @@ def test_timed_variants_need_events(L):
     dd = ddesc(B=2, Lm=512)
     assert L.nsa_fwd_decode_timed(ctypes.byref(dd), ctypes.byref(p), *([FAKE] * 8), None, 0, FAKE,
                                   1 << 40, None, None) == INV
+
+
+def test_backward_workspace_size_is_the_sum_of_its_parts(L):
+    d, p = pdesc(), nsa.make_params(16, 512)
+    n = ctypes.c_size_t(0)
+    assert L.nsa_bwd_prefill_workspace_bytes(ctypes.byref(d), ctypes.byref(p), ctypes.byref(n)) == OK
+    T, B, G, Hq, D, Nb, Nc = 65536, 1, 4, 64, 128, 1024, 1024
+    tiles = 4 * B * G * Nb * 64 * D * 2          # K, K^T, V, V^T layouts
+    means = 2 * B * Nc * G * D * 2               # block means of K and V
+    ctiles = 4 * B * G * 16 * 64 * D * 2         # their four tile layouts
+    heads = 2 * B * T * G * D * 16 * 2 + B * T * Hq * D * 2   # head-minor q, dout; dout copy
+    stat = B * T * Hq * 3 * 8
+    dmeans = 2 * B * Nc * G * D * 4
+    lists = 3 * B * G * (Nb + 1) * 4 + B * G * T * 16 * 4
+    assert abs(n.value - (tiles + means + ctiles + heads + stat + dmeans + lists)) <= 21 * 256
+
+
+def test_backward_validation_and_empty_problem(L):
+    d, p = pdesc(Lq=4096), nsa.make_params(16, 512)
+    n = ctypes.c_size_t(0)
+    assert L.nsa_bwd_prefill_workspace_bytes(ctypes.byref(d), ctypes.byref(p), ctypes.byref(n)) == OK
+    need = n.value
+
+    def call(q=FAKE, dout=FAKE, idx=FAKE, dq=FAKE, ws=FAKE, nb=need, desc=d, params=p):
+        return L.nsa_bwd_prefill(ctypes.byref(desc), ctypes.byref(params), q, FAKE, FAKE, FAKE, dout, idx, dq,
+                                 FAKE, FAKE, FAKE, ws, nb, None)
+    assert call(q=None) == INV
+    assert call(dout=None) == INV
+    assert call(idx=None) == INV
+    assert "idx" in L.nsa_last_error().decode()
+    assert call(idx=FAKE + 2) == INV
+    assert call(dq=FAKE + 4) == INV            # dq needs 16-byte alignment
+    assert call(ws=None) == INV
+    assert call(nb=need - 1) == WS
+    assert call(desc=pdesc(Lq=4096, D=96)) == UNS
+    assert call(params=nsa.make_params(16, 512, block=32)) == UNS
+    for empty in (pdesc(B=0), pdesc(Lq=0)):
+        assert L.nsa_bwd_prefill(ctypes.byref(empty), ctypes.byref(p), None, None, None, None, None, None, None,
+                                 None, None, None, None, 0, None) == OK
+    ev = (ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)
+    assert L.nsa_bwd_prefill_timed(ctypes.byref(d), ctypes.byref(p), *([FAKE] * 11), need, None, ev) == INV
 
 
 def test_decode_workspace_and_validation(L):
