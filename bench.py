@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 PREFILL_STAGES = ["k_prep", "k_cmpwin", "k_sel"]
+BACKWARD_STAGES = ["prep", "query_side", "key_side"]
 DECODE_STAGES = ["k_dec"]
 
 
@@ -117,10 +118,13 @@ class HipEvents:
 # ---------------------------------------------------------------- traffic from committed counters
 
 def kernel_source_digest() -> str:
+    """Digest of the sources the forward kernels and their launches are built
+    from (everything in csrc/ but the gather probe and the backward pass's own
+    kernel file and header)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "long_context_sparse_fwd_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")) and not name.startswith("probe_"):
+        if name.endswith((".hip", ".h", ".cpp")) and not name.startswith(("probe_", "nsa_backward")):
             h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
@@ -348,6 +352,57 @@ def bench_shared_selection(cfg, raw, steps, torch, nsa):
             "kernels_ms": stage_ms, "note": "not the headline workload (its selection is computed)"}
 
 
+def bench_backward(cfg, raw, steps, torch, nsa):
+    """nsa_bwd_prefill on the main config: the selection is the forward's own
+    (computed by nsa_fwd_prefill on the same inputs), dout a seeded bf16
+    normal draw made on the GPU. Algorithmic work: the five products of
+    attention's backward (S, dP, dq, dK, dV) over every (query, key, head)
+    the forward visits, 2.5 times the forward's flops; the query-side kernel
+    also recomputes each branch's forward (S and P.V once more)."""
+    dev = torch.device("cuda:0")
+    up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v, g = (up(raw[n]) for n in ("q", "k", "v", "gates"))
+    B, L, Hq, D = q.shape
+    G = k.shape[2]
+    out, idx = nsa.prefill(q, k, v, g, top_k=cfg.top_k, window=cfg.window, return_idx=True)
+    del out
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    dout = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    f32 = dict(dtype=torch.float32, device=dev)
+    grads = (torch.empty((B, L, Hq, D), **f32), torch.empty((B, L, G, D), **f32),
+             torch.empty((B, L, G, D), **f32), torch.empty((B, L, Hq, 3), **f32))
+    ws = torch.empty(nsa.prefill_backward_workspace_bytes(q, k, v, g, dout, top_k=cfg.top_k, window=cfg.window),
+                     dtype=torch.uint8, device=dev)
+    desc = nsa.prefill_desc(q, k, v, g, dout)
+    params = nsa.make_params(cfg.top_k, cfg.window)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    ns = len(BACKWARD_STAGES) + 1
+    ev = HipEvents(ns * steps)
+    call = lambda evs: nsa.check(nsa.lib().nsa_bwd_prefill_timed(
+        ctypes.byref(desc), ctypes.byref(params), P(q), P(k), P(v), P(g), P(dout), P(idx), *(P(x) for x in grads),
+        P(ws), ws.numel(), stream, evs))
+    call(ev.array(0, ns))  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(ev.array(i * ns, ns))
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    stage_ms = {name: float(np.mean([ev.elapsed_ms(i * ns + s_, i * ns + s_ + 1) for i in range(steps)]))
+                for s_, name in enumerate(BACKWARD_STAGES)}
+    ev.close()
+    fl = 2.5 * sum(prefill_flops(cfg).values())
+    log(f"[bench] backward {cfg.name}: {wall_ms:.3f} ms/step over {steps} steps, kernels {stage_ms}")
+    return {"workload": f"nsa_prefill_backward_{cfg.name}", "ms_per_step": wall_ms,
+            "tokens_per_s": cfg.batch * cfg.seqlen / (wall_ms * 1e-3), "kernels_ms": stage_ms,
+            "algorithmic_flops": fl, "tflops": fl / (wall_ms * 1e-3) / 1e12,
+            "mfma_frac": fl / (wall_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "selection": "the forward's computed selection", "dout": "seeded bf16 normal draw",
+            "outputs": "fp32 dq, dk, dv, dgates"}
+
+
 def bench_decode(cfg, steps, warmup, torch, inputs, nsa):
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
@@ -409,6 +464,7 @@ def main():
                          "positions (0: skip)")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the varlen prefill of four sequences of mixed lengths")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward pass of the main config")
     ap.add_argument("--no-shared-selection", action="store_true",
                     help="skip the run with an injected selection shared by neighbouring tokens")
     ap.add_argument("--also", default="p8k,p32k",
@@ -523,6 +579,8 @@ def main():
         result["varlen_prefill"] = bench_varlen(cfg, raw, args.steps, args.warmup, torch, nsa)
     if not args.no_shared_selection:
         result["shared_selection_prefill"] = bench_shared_selection(cfg, raw, args.steps, torch, nsa)
+    if not args.no_backward:
+        result["backward"] = bench_backward(cfg, raw, max(1, min(args.steps, 5)), torch, nsa)
     if not args.no_decode:
         result["decode"] = bench_decode(inputs.CONFIGS["d64k"], args.decode_steps, 3, torch, inputs, nsa)
     if not args.no_cpu_baseline:

@@ -12,6 +12,7 @@
 
 #include "nsa.h"
 #include "nsa_internal.h"
+#include "nsa_backward.h"
 
 namespace {
 

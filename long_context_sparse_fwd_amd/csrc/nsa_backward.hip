@@ -27,13 +27,14 @@
 //             the gate gradient), then dq;
 //   k_bkv     key side, one workgroup per (branch, group, 64-key block,
 //             piece of its token set), each wave a 16-key tile: dK and dV
-//             accumulated over the tokens that see the block, then added to
-//             the fp32 outputs with atomics;
+//             accumulated over the tokens that see the block (staged through
+//             LDS a few at a time for the four waves), then added to the fp32
+//             outputs with atomics;
 //   k_bfin    adds the block-mean gradients / 64 to the tokens of each block.
 #include <algorithm>
 
 #include "nsa_device.h"
-#include "nsa_internal.h"
+#include "nsa_backward.h"
 
 namespace nsa {
 
@@ -377,11 +378,29 @@ __device__ __forceinline__ Frag<F32> pair_rows<F32>(const float* xa, const float
 
 // Key side of branch X: one workgroup per (sequence, group, 64-key chunk,
 // piece of the tokens that see it); wave w owns keys [16 w, 16 w + 16) of the
-// chunk. Tokens are taken two at a time (32 rows of the dK / dV products).
+// chunk. The tokens go through LDS kBwdStage at a time, loaded once by the
+// whole workgroup (q and dout in both operand layouts, each head's
+// log-sum-exp, dout.o and gate), and each wave takes them two at a time (32
+// rows of the dK / dV products).
+template <class T, int D>
+struct BkvStage {
+  using S = typename T::storage;
+  static constexpr int RS = D + 8;  // padded row of a natural-layout head (16-byte multiple)
+  S qn[kBwdStage][16][RS];          // q, [token][head][d]
+  S dn[kBwdStage][16][RS];          // dout in the input type
+  S qt[kBwdStage][D * 16];          // q, [token][d][head]
+  S dt[kBwdStage][D * 16];          // dout, [token][d][head]
+  float2 st[kBwdStage][16];         // (log2-domain log-sum-exp, dout . o) of this branch
+  float gt[kBwdStage][16];          // this branch's gate
+  int tok[kBwdStage];               // token position, -1 past the piece
+};
+
 template <class T, int D, int X>
 __global__ __launch_bounds__(256) void k_bkv(BwdArgs a) {
   using S = typename T::storage;
-  constexpr int KS = D / 32, DT = D / 16;
+  constexpr int KS = D / 32, DT = D / 16, TT = kBwdStage;
+  extern __shared__ __align__(16) unsigned char bkv_smem[];
+  BkvStage<T, D>& sm = *reinterpret_cast<BkvStage<T, D>*>(bkv_smem);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
   const int nchunk = X == 0 ? a.NcT : a.Nb;
   const int units = a.bkv_units[X];  // units per (sequence, group)
@@ -415,7 +434,7 @@ __global__ __launch_bounds__(256) void k_bkv(BwdArgs a) {
     i0 = tstart + piece * max(span, 0);
     i1 = min(tend, i0 + max(span, 0));
   }
-  if (i0 >= i1) return;
+  if (i0 >= i1) return;  // uniform over the workgroup: no barrier is skipped by part of it
   const float sl2 = a.scale_log2;
   const size_t tile_off = (static_cast<size_t>(bg) * nchunk + c) * 64 * D;
   const S* KA = static_cast<const S*>(X == 0 ? a.kca : a.ka) + tile_off;
@@ -433,60 +452,84 @@ __global__ __launch_bounds__(256) void k_bkv(BwdArgs a) {
     dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const bool colv = col < a.Hg;
-  for (int i = i0; i < i1; i += 2) {
-    const int ta = X == 1 ? list[i] : i;
-    const int tb = i + 1 < i1 ? (X == 1 ? list[i + 1] : i + 1) : -1;
-    f32x4 P[2], dS[2];
+  const int tid = threadIdx.x;
+  for (int ib = i0; ib < i1; ib += TT) {
+    __syncthreads();  // the previous stage has been read
+    // stage tokens ib .. ib + TT - 1: 256 threads x 8 elements cover one
+    // token's 16 x D of each array
 #pragma unroll
-    for (int uu = 0; uu < 2; ++uu) {
-      const int t = uu == 0 ? ta : tb;
-      P[uu] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dS[uu] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (t < 0) continue;
-      const size_t row = static_cast<size_t>(b) * a.L + t;
-      const int h = g * a.Hg + (colv ? col : 0);
-      const S* qp = static_cast<const S*>(a.q) + b * a.qs[0] + t * a.qs[1] + h * a.qs[2];
-      const S* dnp = static_cast<const S*>(a.dN) + (row * a.Hq + h) * D;
-      f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f}, dp4 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const Frag<T> qa = colv ? frag_load<T>(qp + 32 * s + 8 * grp) : frag_zero<T>();
-        const Frag<T> da = colv ? frag_load<T>(dnp + 32 * s + 8 * grp) : frag_zero<T>();
-        mma(s4, qa, kb[s]);
-        mma(dp4, da, vb[s]);
+    for (int uu = 0; uu < TT; ++uu) {
+      const int i = ib + uu;
+      const int t = i < i1 ? (X == 1 ? list[i] : i) : -1;
+      const int e = tid * 8, hh = e / D, d = e % D;
+      if (e < 16 * D) {  // 16 x D elements per array and token: all threads at D = 128, half at 64
+        Frag<T> xq = frag_zero<T>(), xd = frag_zero<T>(), xqt = frag_zero<T>(), xdt = frag_zero<T>();
+        if (t >= 0) {
+          const size_t row = static_cast<size_t>(b) * a.L + t;
+          if (hh < a.Hg) {
+            const int h = g * a.Hg + hh;
+            xq = frag_load<T>(static_cast<const S*>(a.q) + b * a.qs[0] + t * a.qs[1] + h * a.qs[2] + d);
+            xd = frag_load<T>(static_cast<const S*>(a.dN) + (row * a.Hq + h) * D + d);
+          }
+          xqt = frag_load<T>(static_cast<const S*>(a.qT) + (row * a.G + g) * D * 16 + e);
+          xdt = frag_load<T>(static_cast<const S*>(a.dT) + (row * a.G + g) * D * 16 + e);
+        }
+        frag_store<T>(&sm.qn[uu][hh][d], xq);
+        frag_store<T>(&sm.dn[uu][hh][d], xd);
+        frag_store<T>(&sm.qt[uu][e], xqt);
+        frag_store<T>(&sm.dt[uu][e], xdt);
       }
-      // lane holds rows (heads) 4 grp + i2 of column `key`
-      bool vis;
-      if (X == 0) vis = key < a.Nc && 64 * key + 63 <= t;
-      else if (X == 1) vis = key <= t;
-      else vis = key <= t && key >= t - a.w + 1;
-#pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        const int hh = 4 * grp + i2;
-        if (!vis || hh >= a.Hg) continue;
-        const int hq = g * a.Hg + hh;
-        const float2 st = a.stat[(row * a.Hq + hq) * 3 + X];
-        const float gate =
-            to_f32<T>(static_cast<const S*>(a.gates)[b * a.gs[0] + t * a.gs[1] + hq * a.gs[2] + X]);
-        const float p = gate * fast_exp2(fmaf(s4[i2], sl2, -st.x));
-        P[uu][i2] = p;
-        dS[uu][i2] = p * (dp4[i2] - st.y);
+      if (tid < 16) {
+        float2 stv = make_float2(0.f, 0.f);
+        float gv = 0.f;
+        if (t >= 0 && tid < a.Hg) {
+          const int hq = g * a.Hg + tid;
+          stv = a.stat[((static_cast<size_t>(b) * a.L + t) * a.Hq + hq) * 3 + X];
+          gv = to_f32<T>(static_cast<const S*>(a.gates)[b * a.gs[0] + t * a.gs[1] + hq * a.gs[2] + X]);
+        }
+        sm.st[uu][tid] = stv;
+        sm.gt[uu][tid] = gv;
+        if (tid == 0) sm.tok[uu] = t;
       }
     }
-    const Frag<T> pf = pack_p<T>(P[0], P[1]);
-    const Frag<T> sf = pack_p<T>(dS[0], dS[1]);
-    const size_t ra = ((static_cast<size_t>(b) * a.L + ta) * a.G + g) * D;
-    const size_t rb = tb >= 0 ? ((static_cast<size_t>(b) * a.L + tb) * a.G + g) * D : 0;
+    __syncthreads();
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 16 * dt + col;
-      const S* qT = static_cast<const S*>(a.qT);
-      const S* dT = static_cast<const S*>(a.dT);
-      const Frag<T> qbf = pair_rows<T>(qT + (ra + d) * 16 + 4 * grp, tb >= 0 ? qT + (rb + d) * 16 + 4 * grp : nullptr);
-      const Frag<T> dbf = pair_rows<T>(dT + (ra + d) * 16 + 4 * grp, tb >= 0 ? dT + (rb + d) * 16 + 4 * grp : nullptr);
-      mma(dv[dt], pf, dbf);
-      mma(dk[dt], sf, qbf);
+    for (int pp = 0; pp < TT; pp += 2) {
+      f32x4 P[2], dS[2];
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const int t = sm.tok[pp + uu];
+        P[uu] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dS[uu] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (t < 0) continue;
+        f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f}, dp4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          mma(s4, frag_load<T>(&sm.qn[pp + uu][col][32 * s + 8 * grp]), kb[s]);
+          mma(dp4, frag_load<T>(&sm.dn[pp + uu][col][32 * s + 8 * grp]), vb[s]);
+        }
+        // lane holds rows (heads) 4 grp + i2 of column `key`
+        bool vis;
+        if (X == 0) vis = key < a.Nc && 64 * key + 63 <= t;
+        else if (X == 1) vis = key <= t;
+        else vis = key <= t && key >= t - a.w + 1;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          const int hh = 4 * grp + i2;
+          const float2 stv = sm.st[pp + uu][hh];
+          const float p = (vis && hh < a.Hg) ? sm.gt[pp + uu][hh] * fast_exp2(fmaf(s4[i2], sl2, -stv.x)) : 0.f;
+          P[uu][i2] = p;
+          dS[uu][i2] = p * (dp4[i2] - stv.y);
+        }
+      }
+      const Frag<T> pf = pack_p<T>(P[0], P[1]);
+      const Frag<T> sf = pack_p<T>(dS[0], dS[1]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int o = (16 * dt + col) * 16 + 4 * grp;
+        mma(dv[dt], pf, pair_rows<T>(&sm.dt[pp][o], &sm.dt[pp + 1][o]));
+        mma(dk[dt], sf, pair_rows<T>(&sm.qt[pp][o], &sm.qt[pp + 1][o]));
+      }
     }
   }
   // lane holds dK / dV of keys 64 c + 16 wave + 4 grp + i2, column 16 dt + col
@@ -577,10 +620,18 @@ hipError_t launch_backward_t(const BwdArgs& a, hipStream_t st, hipEvent_t* ev) {
   if ((e = rec(1)) != hipSuccess) return e;
   hipLaunchKernelGGL((k_bq<T, O, D>), dim3(a.B * a.G * ((a.L + 3) / 4)), dim3(256), 0, st, a);
   if ((e = rec(2)) != hipSuccess) return e;
+  const int lds = static_cast<int>(sizeof(BkvStage<T, D>));
+  if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bkv<T, D, 0>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess ||
+      (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bkv<T, D, 1>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess ||
+      (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bkv<T, D, 2>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess)
+    return e;
   if (a.NcT > 0)
-    hipLaunchKernelGGL((k_bkv<T, D, 0>), dim3(a.B * a.G * a.bkv_units[0]), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((k_bkv<T, D, 1>), dim3(a.B * a.G * a.bkv_units[1]), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((k_bkv<T, D, 2>), dim3(a.B * a.G * a.bkv_units[2]), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_bkv<T, D, 0>), dim3(a.B * a.G * a.bkv_units[0]), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((k_bkv<T, D, 1>), dim3(a.B * a.G * a.bkv_units[1]), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((k_bkv<T, D, 2>), dim3(a.B * a.G * a.bkv_units[2]), dim3(256), lds, st, a);
   if (a.Nc > 0) {
     const size_t n = static_cast<size_t>(a.B) * a.Nc * 64 * a.G * D;
     hipLaunchKernelGGL(k_bfin, dim3(static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 16384))), dim3(256),
