@@ -395,12 +395,42 @@ def bench_backward(cfg, raw, steps, torch, nsa):
     ev.close()
     fl = 2.5 * sum(prefill_flops(cfg).values())
     log(f"[bench] backward {cfg.name}: {wall_ms:.3f} ms/step over {steps} steps, kernels {stage_ms}")
+
+    # the training path: nsa_fwd_prefill_save keeps the selected branch's
+    # output and log-sum-exp, and nsa_bwd_prefill_saved uses them
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        _, idx_s, saved = nsa.prefill_save(q, k, v, g, top_k=cfg.top_k, window=cfg.window)
+    torch.cuda.synchronize()
+    save_ms = (time.perf_counter() - t0) * 1e3 / steps
+    o_slc, lse_slc = saved
+    ev = HipEvents(ns * steps)
+    call_s = lambda evs: nsa.check(nsa.lib().nsa_bwd_prefill_saved_timed(
+        ctypes.byref(desc), ctypes.byref(params), P(q), P(k), P(v), P(g), P(dout), P(idx_s), P(o_slc), P(lse_slc),
+        *(P(x) for x in grads), P(ws), ws.numel(), stream, evs))
+    call_s(ev.array(0, ns))  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call_s(ev.array(i * ns, ns))
+    torch.cuda.synchronize()
+    saved_ms = (time.perf_counter() - t0) * 1e3 / steps
+    saved_stage = {name: float(np.mean([ev.elapsed_ms(i * ns + s_, i * ns + s_ + 1) for i in range(steps)]))
+                   for s_, name in enumerate(BACKWARD_STAGES)}
+    ev.close()
+    log(f"[bench] backward {cfg.name} from the saved selected branch: {saved_ms:.3f} ms/step, kernels "
+        f"{saved_stage}; the saving forward {save_ms:.3f} ms/step")
     return {"workload": f"nsa_prefill_backward_{cfg.name}", "ms_per_step": wall_ms,
             "tokens_per_s": cfg.batch * cfg.seqlen / (wall_ms * 1e-3), "kernels_ms": stage_ms,
             "algorithmic_flops": fl, "tflops": fl / (wall_ms * 1e-3) / 1e12,
             "mfma_frac": fl / (wall_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "selection": "the forward's computed selection", "dout": "seeded bf16 normal draw",
-            "outputs": "fp32 dq, dk, dv, dgates"}
+            "outputs": "fp32 dq, dk, dv, dgates",
+            "saved": {"entry": "nsa_bwd_prefill_saved after nsa_fwd_prefill_save", "ms_per_step": saved_ms,
+                      "kernels_ms": saved_stage, "tflops": fl / (saved_ms * 1e-3) / 1e12,
+                      "mfma_frac": fl / (saved_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                      "forward_save_ms_per_step": save_ms}}
 
 
 def bench_decode(cfg, steps, warmup, torch, inputs, nsa):

@@ -161,6 +161,22 @@ nsa_status_t nsa_fwd_prefill(const nsa_prefill_desc_t* desc, const nsa_params_t*
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nsa_fwd_prefill that also keeps what the backward pass needs of the
+ * selected branch (the branch whose keys are gathered per token): its own
+ * output o_slc [B, L, Hq, D] (before the gate, contiguous, out_dtype,
+ * 16-byte aligned) and the natural-log log-sum-exp of its scaled logits
+ * lse_slc [B, L, Hq] (float32, contiguous; -inf where the token has no
+ * usable block, whose output is then 0). Both caller-owned and fully
+ * written; out and idx are exactly those of nsa_fwd_prefill. Pass them to
+ * nsa_bwd_prefill_saved. Errors as for nsa_fwd_prefill, plus
+ * NSA_ERR_INVALID_ARGUMENT for a NULL or misaligned o_slc / lse_slc.
+ */
+nsa_status_t nsa_fwd_prefill_save(const nsa_prefill_desc_t* desc, const nsa_params_t* params, const void* q,
+                                  const void* k, const void* v, const void* gates, void* out, int32_t* idx,
+                                  nsa_idx_mode_t idx_mode, void* o_slc, float* lse_slc, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * Chunked prefill: the NSA forward of query positions [q_offset, seqlen)
  * only, each against the whole context [0, its position] - the prefill half
  * of serving long prompts in pieces, as with the continuous batching switch
@@ -287,6 +303,25 @@ nsa_status_t nsa_bwd_prefill(const nsa_prefill_desc_t* desc, const nsa_params_t*
                              const void* k, const void* v, const void* gates, const void* dout,
                              const int32_t* idx, float* dq, float* dk, float* dv, float* dgates,
                              void* workspace, size_t workspace_bytes, void* stream);
+/*
+ * nsa_bwd_prefill given the selected branch's output and log-sum-exp kept by
+ * nsa_fwd_prefill_save for the same inputs and selection (o_slc: out_dtype,
+ * 16-byte aligned; lse_slc: float32): the query side then skips that
+ * branch's forward recomputation (its blocks are gathered once instead of
+ * twice). Same results up to rounding; same errors, plus
+ * NSA_ERR_INVALID_ARGUMENT for a NULL or misaligned o_slc / lse_slc.
+ */
+nsa_status_t nsa_bwd_prefill_saved(const nsa_prefill_desc_t* desc, const nsa_params_t* params, const void* q,
+                                   const void* k, const void* v, const void* gates, const void* dout,
+                                   const int32_t* idx, const void* o_slc, const float* lse_slc, float* dq,
+                                   float* dk, float* dv, float* dgates, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+nsa_status_t nsa_bwd_prefill_saved_timed(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                                         const void* q, const void* k, const void* v, const void* gates,
+                                         const void* dout, const int32_t* idx, const void* o_slc,
+                                         const float* lse_slc, float* dq, float* dk, float* dv, float* dgates,
+                                         void* workspace, size_t workspace_bytes, void* stream,
+                                         void* const* stage_events);
 /* nsa_bwd_prefill with 4 stage events (prep; query side; key side). */
 nsa_status_t nsa_bwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_params_t* params, const void* q,
                                    const void* k, const void* v, const void* gates, const void* dout,

@@ -363,7 +363,8 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
                                  int64_t q_offset, const int32_t* seq_lens, const int32_t* q_offsets,
                                  const void* q, const void* k, const void* v, const void* gates,
                                  void* out, int32_t* idx, nsa_idx_mode_t idx_mode, void* workspace,
-                                 size_t workspace_bytes, void* stream, void* const* events) {
+                                 size_t workspace_bytes, void* stream, void* const* events,
+                                 void* save_o = nullptr, float* save_lse = nullptr) {
   if (desc == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "desc is NULL");
   if (q_offset < 0 || q_offset > desc->seqlen)
     return fail(NSA_ERR_INVALID_ARGUMENT, "q_offset %lld outside [0, seqlen %d]",
@@ -434,6 +435,8 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
   a.idx = idx != nullptr ? idx : reinterpret_cast<int32_t*>(ws + pl.off_idx);
   a.kt = ws + pl.off_kt;
   a.vt = ws + pl.off_vt;
+  a.save_o = save_o;
+  a.save_lse = save_lse;
   a.kct = ws + pl.off_kct;
   a.kclt = ws + pl.off_kclt;
   a.vct = ws + pl.off_vct;
@@ -457,6 +460,20 @@ nsa_status_t nsa_fwd_prefill(const nsa_prefill_desc_t* desc, const nsa_params_t*
                              size_t workspace_bytes, void* stream) {
   return prefill_impl(desc, params, 0, nullptr, nullptr, q, k, v, gates, out, idx, idx_mode, workspace,
                       workspace_bytes, stream, nullptr);
+}
+
+nsa_status_t nsa_fwd_prefill_save(const nsa_prefill_desc_t* desc, const nsa_params_t* params, const void* q,
+                                  const void* k, const void* v, const void* gates, void* out, int32_t* idx,
+                                  nsa_idx_mode_t idx_mode, void* o_slc, float* lse_slc, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (desc != nullptr && desc->batch > 0 && desc->seqlen > 0) {
+    NSA_TRY(check_ptr("o_slc", o_slc, true));
+    NSA_TRY(check_ptr("lse_slc", lse_slc, false));
+    if ((reinterpret_cast<uintptr_t>(lse_slc) & 3u) != 0)
+      return fail(NSA_ERR_INVALID_ARGUMENT, "lse_slc is not 4-byte aligned");
+  }
+  return prefill_impl(desc, params, 0, nullptr, nullptr, q, k, v, gates, out, idx, idx_mode, workspace,
+                      workspace_bytes, stream, nullptr, o_slc, lse_slc);
 }
 
 nsa_status_t nsa_fwd_prefill_chunk(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
@@ -483,7 +500,8 @@ nsa_status_t nsa_fwd_prefill_varlen(const nsa_prefill_desc_t* desc, const nsa_pa
 static nsa_status_t backward_impl(const nsa_prefill_desc_t* desc, const nsa_params_t* params, const void* q,
                                   const void* k, const void* v, const void* gates, const void* dout,
                                   const int32_t* idx, float* dq, float* dk, float* dv, float* dgates,
-                                  void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+                                  void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                                  const void* o_slc = nullptr, const float* lse_slc = nullptr) {
   BwdPlan pl;
   NSA_TRY(plan_backward(desc, params, &pl));
   if (desc->batch == 0 || desc->seqlen == 0) return ok();
@@ -530,6 +548,8 @@ static nsa_status_t backward_impl(const nsa_prefill_desc_t* desc, const nsa_para
   a.gates = gates;
   a.dout = dout;
   a.idx = idx;
+  a.o_slc = o_slc;
+  a.lse_slc = lse_slc;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -584,6 +604,38 @@ nsa_status_t nsa_bwd_prefill(const nsa_prefill_desc_t* desc, const nsa_params_t*
                              void* workspace, size_t workspace_bytes, void* stream) {
   return backward_impl(desc, params, q, k, v, gates, dout, idx, dq, dk, dv, dgates, workspace, workspace_bytes,
                        stream, nullptr);
+}
+
+nsa_status_t nsa_bwd_prefill_saved(const nsa_prefill_desc_t* desc, const nsa_params_t* params, const void* q,
+                                   const void* k, const void* v, const void* gates, const void* dout,
+                                   const int32_t* idx, const void* o_slc, const float* lse_slc, float* dq,
+                                   float* dk, float* dv, float* dgates, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (desc != nullptr && desc->batch > 0 && desc->seqlen > 0) {
+    NSA_TRY(check_ptr("o_slc", o_slc, true));
+    NSA_TRY(check_ptr("lse_slc", lse_slc, false));
+    if ((reinterpret_cast<uintptr_t>(lse_slc) & 3u) != 0)
+      return fail(NSA_ERR_INVALID_ARGUMENT, "lse_slc is not 4-byte aligned");
+  }
+  return backward_impl(desc, params, q, k, v, gates, dout, idx, dq, dk, dv, dgates, workspace, workspace_bytes,
+                       stream, nullptr, o_slc, lse_slc);
+}
+
+nsa_status_t nsa_bwd_prefill_saved_timed(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                                         const void* q, const void* k, const void* v, const void* gates,
+                                         const void* dout, const int32_t* idx, const void* o_slc,
+                                         const float* lse_slc, float* dq, float* dk, float* dv, float* dgates,
+                                         void* workspace, size_t workspace_bytes, void* stream,
+                                         void* const* stage_events) {
+  if (stage_events == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "stage_events is NULL");
+  for (int i = 0; i <= nsa::kBwdStages; ++i)
+    if (stage_events[i] == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "stage_events[%d] is NULL", i);
+  if (desc != nullptr && desc->batch > 0 && desc->seqlen > 0) {
+    NSA_TRY(check_ptr("o_slc", o_slc, true));
+    NSA_TRY(check_ptr("lse_slc", lse_slc, false));
+  }
+  return backward_impl(desc, params, q, k, v, gates, dout, idx, dq, dk, dv, dgates, workspace, workspace_bytes,
+                       stream, stage_events, o_slc, lse_slc);
 }
 
 nsa_status_t nsa_bwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_params_t* params, const void* q,

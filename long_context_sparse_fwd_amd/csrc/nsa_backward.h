@@ -24,6 +24,11 @@ struct BwdArgs {
   const void* gates;
   const void* dout;  // [B, L, Hq, D] in the output type
   const int32_t* idx;
+  // Optional: the selected branch's output [B, L, Hq, D] (output type) and
+  // natural-log log-sum-exp [B, L, Hq] saved by the forward; when given, the
+  // query side takes them instead of recomputing that branch's forward.
+  const void* o_slc;
+  const float* lse_slc;
   float* dq;      // [B, L, Hq, D]
   float* dk;      // [B, L, G, D]
   float* dv;      // [B, L, G, D]

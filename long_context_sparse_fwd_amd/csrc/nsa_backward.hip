@@ -220,7 +220,9 @@ __device__ __forceinline__ Chunk chunk_at(const BwdArgs& a, int t, const int32_t
 
 // Query side of branch X for one token (one wave, 16 head columns): the
 // forward over the key set (log-sum-exp, o, dout.o), then dq += scale dS K.
-template <class T, class O, int D, int X>
+// SAVED (selected branch only): the branch's output and log-sum-exp come
+// from the forward (BwdArgs::o_slc / lse_slc) instead of a forward pass here.
+template <class T, class O, int D, int X, bool SAVED = false>
 __device__ __forceinline__ void bq_branch(const BwdArgs& a, int b, int g, int t, int lane,
                                           const Frag<T> (&qf)[D / 32], const Frag<T> (&df)[D / 32],
                                           float gate, const typename O::storage* dout_row,
@@ -237,12 +239,27 @@ __device__ __forceinline__ void bq_branch(const BwdArgs& a, int b, int g, int t,
   const int32_t* row = a.idx + ((static_cast<size_t>(b) * a.L + t) * a.G + g) * a.n;
   const int nch = n_chunks<X>(a, t);
 
+  float lse2 = 0.f, dsum = 0.f;
+  bool any = false;
+  if (SAVED) {
+    for (int i = 0; i < nch && !any; ++i) any = chunk_at<X>(a, t, row, i).ok;
+    if (any) {
+      const size_t r = (static_cast<size_t>(b) * a.L + t) * a.Hq + g * a.Hg + (col < a.Hg ? col : 0);
+      lse2 = a.lse_slc[r] * kLog2e;
+      const typename O::storage* op = static_cast<const typename O::storage*>(a.o_slc) + r * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dsum += to_f32<O>(dout_row[16 * dt + 4 * grp + i]) * to_f32<O>(op[16 * dt + 4 * grp + i]);
+      dsum = col_sum4(dsum);
+    }
+  } else {
   // forward over the key set
   float m = kNegBig, l = 0.f;
   f32x4 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bool any = false;
   for (int i = 0; i < nch; ++i) {
     const Chunk c = chunk_at<X>(a, t, row, i);
     if (!c.ok || c.khi < c.klo) continue;
@@ -262,7 +279,6 @@ __device__ __forceinline__ void bq_branch(const BwdArgs& a, int b, int g, int t,
       online_step<T, DT, true>(st, c.base + 32 * s2, c.klo, c.khi, grp, sl2, m, l, acc, vf);
     }
   }
-  float lse2 = 0.f, dsum = 0.f;
   if (any) {
     const float lt = col_sum4(l);
     lse2 = m + fast_log2(lt);
@@ -272,6 +288,7 @@ __device__ __forceinline__ void bq_branch(const BwdArgs& a, int b, int g, int t,
 #pragma unroll
       for (int i = 0; i < 4; ++i) dsum += to_f32<O>(dout_row[16 * dt + 4 * grp + i]) * acc[dt][i] * inv;
     dsum = col_sum4(dsum);
+  }
   }
   if (grp == 0 && stat != nullptr) {
     stat[X] = make_float2(lse2, dsum);
@@ -317,7 +334,7 @@ __device__ __forceinline__ void bq_branch(const BwdArgs& a, int b, int g, int t,
 // faster than the unconstrained two: each wave spends most of its time
 // waiting for one gathered tile, so more waves hide more of that latency;
 // four (128 registers) spilled too much and was 40 % slower.
-template <class T, class O, int D>
+template <class T, class O, int D, bool SAVED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_bq(BwdArgs a) {
   using S = typename T::storage;
   using SO = typename O::storage;
@@ -349,7 +366,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   bq_branch<T, O, D, 0>(a, b, g, t, lane, qf, df, g0, dout_row, dq, stat, dgate);
-  bq_branch<T, O, D, 1>(a, b, g, t, lane, qf, df, g1, dout_row, dq, stat, dgate);
+  bq_branch<T, O, D, 1, SAVED>(a, b, g, t, lane, qf, df, g1, dout_row, dq, stat, dgate);
   bq_branch<T, O, D, 2>(a, b, g, t, lane, qf, df, g2, dout_row, dq, stat, dgate);
   if (!colv) return;
   float* dqp = a.dq + (row * a.Hq + h) * D;
@@ -622,7 +639,10 @@ hipError_t launch_backward_t(const BwdArgs& a, hipStream_t st, hipEvent_t* ev) {
   hipLaunchKernelGGL(k_bsel_scan, dim3(a.B * a.G), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_bsel_fill, dim3(rgrid), dim3(256), 0, st, a);
   if ((e = rec(1)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_bq<T, O, D>), dim3(a.B * a.G * ((a.L + 3) / 4)), dim3(256), 0, st, a);
+  if (a.lse_slc != nullptr)
+    hipLaunchKernelGGL((k_bq<T, O, D, true>), dim3(a.B * a.G * ((a.L + 3) / 4)), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_bq<T, O, D, false>), dim3(a.B * a.G * ((a.L + 3) / 4)), dim3(256), 0, st, a);
   if ((e = rec(2)) != hipSuccess) return e;
   const int lds = static_cast<int>(sizeof(BkvStage<T, D>));
   if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bkv<T, D, 0>),

@@ -30,6 +30,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 // Element type tags.
 struct BF16 {

@@ -52,6 +52,11 @@ struct PrefillArgs {
   void* kclt;  // bf16 input only: the low part, bf16(mean - high), same layout
   void* vct;   // [B][G][NcT] 64-block V^T tiles of block means of V
   int64_t qs[3], ks[3], vs[3], gs[3], os[3];
+  // Optional (null: not written): the selected branch's own output
+  // [B][Lq][Hq][D] in the output type and its natural-log log-sum-exp
+  // [B][Lq][Hq] (-inf for no usable block), for the backward pass.
+  void* save_o;
+  float* save_lse;
 };
 
 struct DecodeArgs {

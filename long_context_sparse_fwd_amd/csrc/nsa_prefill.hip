@@ -584,7 +584,7 @@ __device__ __forceinline__ void half_attend(const HalfBlock<T, D>& hb, const Fra
 // stay closer together in L2. The steps stream through a ring of kSelRing
 // half-block register buffers; each step runs the online-softmax update of
 // every token in its mask. Query fragments are kept in LDS.
-template <class T, class O, int D>
+template <class T, class O, int D, bool SAVE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_sel(PrefillArgs a) {
   using S = typename T::storage;
   using SO = typename O::storage;
@@ -778,6 +778,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const f32x4 prev = load4<O>(o + 16 * dt);
         store4<O>(o + 16 * dt, prev + acc[qt][dt] * f);
       }
+      if (SAVE) {  // the branch's own output and log-sum-exp, kept for the backward pass
+        const int64_t r = (static_cast<int64_t>(b) * a.Lq + (t - t0q)) * a.Hq + h;
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        SO* so = static_cast<SO*>(a.save_o) + r * D + 4 * grp;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) store4<O>(so + 16 * dt, acc[qt][dt] * inv);
+        if (grp == 0) a.save_lse[r] = lt > 0.f ? (m[qt] + fast_log2(lt)) * kLn2 : -INFINITY;
+      }
     }
   }
 }
@@ -840,10 +848,17 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st, hipEven
   // (4 waves) per CU, which was measured faster (~13 % at 64k) than two: the
   // gathers then contend less for L2.
   const size_t sel_lds = sel_lds_bytes(a.Nb, D, sizeof(typename T::storage) == 2);
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sel<T, O, D>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sel_lds));
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_sel<T, O, D>), dim3(per * 8), dim3(256), sel_lds, st, a);
+  if (a.save_o != nullptr) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sel<T, O, D, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sel_lds));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_sel<T, O, D, true>), dim3(per * 8), dim3(256), sel_lds, st, a);
+  } else {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sel<T, O, D, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sel_lds));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_sel<T, O, D, false>), dim3(per * 8), dim3(256), sel_lds, st, a);
+  }
   if ((e = record(ev, 3, st)) != hipSuccess) return e;
   return hipGetLastError();
 }

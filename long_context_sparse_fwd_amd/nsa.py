@@ -93,6 +93,14 @@ def lib() -> ctypes.CDLL:
                                   c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]
     L.nsa_bwd_prefill_timed.restype = ctypes.c_int
     L.nsa_bwd_prefill_timed.argtypes = L.nsa_bwd_prefill.argtypes + [c_vp]
+    L.nsa_bwd_prefill_saved.restype = ctypes.c_int
+    L.nsa_bwd_prefill_saved.argtypes = [P(PrefillDesc), P(NsaParams), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                        c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]
+    L.nsa_bwd_prefill_saved_timed.restype = ctypes.c_int
+    L.nsa_bwd_prefill_saved_timed.argtypes = L.nsa_bwd_prefill_saved.argtypes + [c_vp]
+    L.nsa_fwd_prefill_save.restype = ctypes.c_int
+    L.nsa_fwd_prefill_save.argtypes = [P(PrefillDesc), P(NsaParams), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                       ctypes.c_int, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]
     L.nsa_compress_kv.restype = ctypes.c_int
     L.nsa_compress_kv.argtypes = [c_i32, c_i32, c_i32, c_i32, ctypes.c_int, c_i32, c_vp, P(c_i64),
                                   c_vp, P(c_i64), c_vp, P(c_i64), c_vp, P(c_i64), c_vp]
@@ -297,13 +305,41 @@ def prefill_backward_workspace_bytes(q, k, v, gates, dout, *, top_k, window, blo
     return nbytes.value
 
 
+def prefill_save(q, k, v, gates, *, top_k: int, window: int, block: int = 64, scale: float = 0.0,
+                 out_dtype=None, idx=None, inject: bool = False, workspace=None):
+    """nsa_fwd_prefill_save: the prefill plus what the backward keeps of the
+    selected branch. Returns (out, idx, (o_slc, lse_slc)); with inject=True,
+    idx supplies the selection."""
+    _require_gpu(q, k, v, gates)
+    B, L, Hq, D = q.shape
+    G = k.shape[2]
+    out = torch.empty((B, L, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if idx is None:
+        if inject:
+            raise ValueError("inject=True needs idx")
+        idx = torch.empty((B, L, G, top_k), dtype=torch.int32, device=q.device)
+    o_slc = torch.empty_like(out)
+    lse_slc = torch.empty((B, L, Hq), dtype=torch.float32, device=q.device)
+    desc = prefill_desc(q, k, v, gates, out)
+    params = make_params(top_k, window, block, scale=scale)
+    if workspace is None:
+        workspace = torch.empty(prefill_workspace_bytes(q, k, v, gates, out, top_k=top_k, window=window,
+                                                        block=block), dtype=torch.uint8, device=q.device)
+    check(lib().nsa_fwd_prefill_save(ctypes.byref(desc), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(gates), _ptr(out), _ptr(idx),
+                                     NSA_IDX_INJECT if inject else NSA_IDX_COMPUTE, _ptr(o_slc),
+                                     _ptr(lse_slc), _ptr(workspace), workspace.numel(), _stream_of(q)))
+    return out, idx, (o_slc, lse_slc)
+
+
 def prefill_backward(q, k, v, gates, dout, idx, *, top_k: int, window: int, block: int = 64,
-                     scale: float = 0.0, grads=None, workspace=None):
+                     scale: float = 0.0, grads=None, workspace=None, saved=None):
     """Gradients of sum(out * dout) of the NSA prefill for the fixed selection idx.
 
     q, k, v, gates as for prefill(); dout [B,L,Hq,D] in the output dtype;
     idx [B,L,G,top_k] int32 (the forward's selection). Returns float32
     (dq, dk, dv, dgates); `grads` may supply those four contiguous tensors.
+    `saved` = (o_slc, lse_slc) from prefill_save() selects nsa_bwd_prefill_saved.
     """
     _require_gpu(q, k, v, gates, dout, idx)
     if idx.dtype != torch.int32 or not idx.is_contiguous():
@@ -325,6 +361,13 @@ def prefill_backward(q, k, v, gates, dout, idx, *, top_k: int, window: int, bloc
         workspace = torch.empty(prefill_backward_workspace_bytes(q, k, v, gates, dout, top_k=top_k,
                                                                  window=window, block=block),
                                 dtype=torch.uint8, device=q.device)
+    if saved is not None:
+        o_slc, lse_slc = saved
+        check(lib().nsa_bwd_prefill_saved(ctypes.byref(desc), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(gates), _ptr(dout), _ptr(idx), _ptr(o_slc), _ptr(lse_slc),
+                                          *(_ptr(x) for x in grads), _ptr(workspace), workspace.numel(),
+                                          _stream_of(q)))
+        return grads
     check(lib().nsa_bwd_prefill(ctypes.byref(desc), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(gates),
                                 _ptr(dout), _ptr(idx), *(_ptr(x) for x in grads), _ptr(workspace),
                                 workspace.numel(), _stream_of(q)))

@@ -123,6 +123,7 @@ def nsa_token(q_t, K, V, Kc, Vc, t: int, g_t, *, block: int, top_k: int, window:
     o_slc = np.zeros((Hq, D))
     o_win = np.zeros((Hq, D))
     lse = np.full(Hq, -np.inf)
+    lse_slc = np.full(Hq, -np.inf)
     idx = np.full((G, top_k), -1, dtype=np.int32)
     gap = np.full(G, np.inf)
     group_scores = []
@@ -151,15 +152,15 @@ def nsa_token(q_t, K, V, Kc, Vc, t: int, g_t, *, block: int, top_k: int, window:
         blocks = sorted({int(j) for j in idx[g] if 0 <= j and j * block <= t})
         if blocks:
             toks = np.concatenate([np.arange(j * block, min(j * block + block, t + 1)) for j in blocks])
-            o_slc[hs], _ = softmax_attend(qg, np.asarray(K[toks, g], dtype=np.float64),
-                                          np.asarray(V[toks, g], dtype=np.float64), scale)
+            o_slc[hs], lse_slc[hs] = softmax_attend(qg, np.asarray(K[toks, g], dtype=np.float64),
+                                                    np.asarray(V[toks, g], dtype=np.float64), scale)
         # sliding-window branch (R5)
         lo = max(0, t - window + 1)
         o_win[hs], _ = softmax_attend(qg, np.asarray(K[lo: t + 1, g], dtype=np.float64),
                                       np.asarray(V[lo: t + 1, g], dtype=np.float64), scale)
 
     out = g_t[:, 0:1] * o_cmp + g_t[:, 1:2] * o_slc + g_t[:, 2:3] * o_win   # R6
-    return {"out": out, "idx": idx, "lse": lse, "gap": gap,
+    return {"out": out, "idx": idx, "lse": lse, "gap": gap, "lse_slc": lse_slc,
             "o_cmp": o_cmp, "o_slc": o_slc, "o_win": o_win, "scores": group_scores}
 
 
@@ -178,7 +179,8 @@ def prefill(q, k, v, gates, *, block: int = 64, select_block=None, top_k: int, w
     query positions (all positions by default); K/V always span the full
     sequence. ``inject_idx`` [B, L, G, top_k] replaces the selection.
     Returns out [B, R, Hq, D], idx [B, R, G, top_k], lse [B, R, Hq] and
-    gap [B, R, G] (plus the three branch outputs when ``branches``, and the
+    gap [B, R, G] (plus the three branch outputs and the selected branch's own
+    log-sum-exp ``lse_slc`` [B, R, Hq] when ``branches``, and the
     block scores [B, R, G, L // block] when ``scores``, NaN where undefined).
     """
     _check_blocks(block, select_block)
@@ -195,6 +197,7 @@ def prefill(q, k, v, gates, *, block: int = 64, select_block=None, top_k: int, w
     if branches:
         for name in ("o_cmp", "o_slc", "o_win"):
             res[name] = np.zeros((B, R, Hq, D))
+        res["lse_slc"] = np.zeros((B, R, Hq))
     fixed = list(res)
     if scores:
         res["scores"] = np.full((B, R, G, L // block), np.nan)

@@ -27,7 +27,8 @@ def test_library_exports_every_declared_function(L):
     assert {"nsa_fwd_prefill", "nsa_fwd_decode", "nsa_compress_kv", "nsa_prefill_workspace_bytes",
             "nsa_decode_workspace_bytes", "nsa_status_string", "nsa_last_error", "nsa_version",
             "nsa_fwd_prefill_timed", "nsa_fwd_decode_timed", "nsa_fwd_prefill_chunk", "nsa_fwd_prefill_varlen",
-            "nsa_bwd_prefill", "nsa_bwd_prefill_timed", "nsa_bwd_prefill_workspace_bytes"} <= set(names)
+            "nsa_bwd_prefill", "nsa_bwd_prefill_timed", "nsa_bwd_prefill_workspace_bytes",
+            "nsa_fwd_prefill_save", "nsa_bwd_prefill_saved", "nsa_bwd_prefill_saved_timed"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert L.nsa_version() >= 100
@@ -217,6 +218,20 @@ def test_backward_validation_and_empty_problem(L):
     for empty in (pdesc(B=0), pdesc(Lq=0)):
         assert L.nsa_bwd_prefill(ctypes.byref(empty), ctypes.byref(p), None, None, None, None, None, None, None,
                                  None, None, None, None, 0, None) == OK
+    # the saved variants need both kept arrays
+    # (q, k, v, gates, dout, idx), o_slc, lse_slc, (dq, dk, dv, dgates), workspace
+    assert L.nsa_bwd_prefill_saved(ctypes.byref(d), ctypes.byref(p), *([FAKE] * 6), None, FAKE, *([FAKE] * 4),
+                                   FAKE, need, None) == INV
+    assert "o_slc" in L.nsa_last_error().decode()
+    assert L.nsa_bwd_prefill_saved(ctypes.byref(d), ctypes.byref(p), *([FAKE] * 6), FAKE + 4, FAKE, *([FAKE] * 4),
+                                   FAKE, need, None) == INV
+    assert L.nsa_bwd_prefill_saved(ctypes.byref(d), ctypes.byref(p), *([FAKE] * 6), FAKE, None, *([FAKE] * 4),
+                                   FAKE, need, None) == INV
+    assert "lse_slc" in L.nsa_last_error().decode()
+    st, fneed = ws_prefill(L, d, p)
+    assert L.nsa_fwd_prefill_save(ctypes.byref(d), ctypes.byref(p), *([FAKE] * 5), None, 0, FAKE, None, FAKE,
+                                  fneed, None) == INV
+    assert "lse_slc" in L.nsa_last_error().decode()
     ev = (ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)
     assert L.nsa_bwd_prefill_timed(ctypes.byref(d), ctypes.byref(p), *([FAKE] * 11), need, None, ev) == INV
 

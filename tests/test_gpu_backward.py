@@ -107,6 +107,47 @@ def test_backward_edge_cases(case):
         assert e <= TOL[dtype], f"{nm} error {e}"
 
 
+@pytest.mark.parametrize("case", [CASES[0], CASES[1]], ids=["f32", "bf16"])
+def test_forward_save_and_saved_backward(case):
+    # nsa_fwd_prefill_save: out and idx bit for bit those of nsa_fwd_prefill,
+    # the kept selected-branch output and log-sum-exp equal to the oracle's;
+    # nsa_bwd_prefill_saved from them (the oracle's selection injected)
+    # matches the backward oracle like the plain backward does.
+    name, B, L, Hq, G, D, dtype, n, w, _ = case
+    cfg = inputs.PrefillConfig(name, B, L, Hq, G, D, dtype, top_k=n, window=w, seed=14)
+    print(f"[bwd saved] {cfg}", flush=True)
+    raw = inputs.make_prefill_inputs(cfg)
+    q, k, v, g = (_up(raw[nm], dtype) for nm in ("q", "k", "v", "gates"))
+    out0, idx0 = nsa.prefill(q, k, v, g, top_k=n, window=w, return_idx=True)
+    out1, idx1, _ = nsa.prefill_save(q, k, v, g, top_k=n, window=w)
+    torch.cuda.synchronize()
+    assert torch.equal(idx0, idx1)
+    assert torch.equal(out0.view(torch.int16) if dtype == "bf16" else out0,
+                       out1.view(torch.int16) if dtype == "bf16" else out1)
+    x = _f64(raw, dtype)
+    orc = nsa_ref.prefill(x["q"], x["k"], x["v"], x["gates"], top_k=n, window=w, branches=True)
+    _, _, (o_slc, lse_slc) = nsa.prefill_save(q, k, v, g, top_k=n, window=w,
+                                              idx=torch.from_numpy(orc["idx"]).cuda(), inject=True)
+    torch.cuda.synchronize()
+    e_o = float(np.abs(o_slc.float().cpu().numpy() - orc["o_slc"]).max())
+    lg, lr = lse_slc.cpu().numpy().astype(np.float64), orc["lse_slc"]
+    assert np.array_equal(np.isinf(lg), np.isinf(lr))
+    fin = np.isfinite(lr)
+    e_l = float(np.abs(lg[fin] - lr[fin]).max())
+    print(f"[bwd saved] {name} o_slc err {e_o:.2e} lse_slc err {e_l:.2e}", flush=True)
+    assert e_o <= (2e-2 if dtype == "bf16" else 1e-4) and e_l <= 1e-4
+    dout_raw = inputs.make_dout(cfg)
+    ref = nsa_bwd_ref.prefill_backward(x["q"], x["k"], x["v"], x["gates"], inputs.to_f64(dout_raw, dtype),
+                                       orc["idx"], top_k=n, window=w)
+    grads = nsa.prefill_backward(q, k, v, g, _up(dout_raw, dtype), torch.from_numpy(orc["idx"]).cuda(), top_k=n,
+                                 window=w, saved=(o_slc, lse_slc))
+    torch.cuda.synchronize()
+    for nm, gt in zip(("dq", "dk", "dv", "dgates"), grads):
+        e = _err(gt.cpu().numpy().astype(np.float64), ref[nm])
+        print(f"[bwd saved] {name} {nm} err {e:.2e}", flush=True)
+        assert e <= TOL[dtype], f"{nm} error {e}"
+
+
 def test_backward_with_fp32_upstream_gradient_and_odd_selection():
     # bf16 inputs with an fp32 output (so an fp32 dout), and an injected
     # selection with repeats, entries past the own block and negative entries
