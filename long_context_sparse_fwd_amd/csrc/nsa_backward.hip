@@ -24,7 +24,9 @@
 //             tokens that chose it;
 //   k_bq      query side, one wave per (token, group): for each branch, the
 //             forward over its key set (log-sum-exp and dout.o, which is also
-//             the gate gradient), then dq;
+//             the gate gradient), then dq; with the selected branch's output
+//             and log-sum-exp kept by the forward (nsa_fwd_prefill_save),
+//             that branch skips its forward and gathers its blocks once;
 //   k_bkv     key side, one workgroup per (branch, group, 64-key block,
 //             piece of its token set), each wave a 16-key tile: dK and dV
 //             accumulated over the tokens that see the block (staged through
