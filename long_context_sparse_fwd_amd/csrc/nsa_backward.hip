@@ -67,32 +67,50 @@ __global__ __launch_bounds__(256) void k_btile(const typename T::storage* src, i
 }
 
 // Per token: qT / dT [b][t][g][d][16] (head within the group fastest, zero
-// past Hg) and dN [b][t][h][d], dout converted to the input type.
+// past Hg) and dN [b][t][h][d], dout converted to the input type. One group
+// at a time goes through LDS: 16-byte coalesced reads of its heads' rows,
+// then the head-minor rows written in order.
 template <class T, class O, int D>
 __global__ __launch_bounds__(256) void k_btrans(BwdArgs a) {
   using S = typename T::storage;
   using SO = typename O::storage;
-  const int t = blockIdx.x, b = blockIdx.y;
+  __shared__ S qs[16][D], ds[16][D];
+  const int t = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const S* q = static_cast<const S*>(a.q) + b * a.qs[0] + t * a.qs[1];
   const SO* dout = static_cast<const SO*>(a.dout) + b * a.os[0] + t * a.os[1];
   const size_t row = static_cast<size_t>(b) * a.L + t;
-  S* qT = static_cast<S*>(a.qT) + row * a.G * D * 16;
-  S* dT = static_cast<S*>(a.dT) + row * a.G * D * 16;
-  S* dN = static_cast<S*>(a.dN) + row * a.Hq * D;
-  for (int e = threadIdx.x; e < a.G * D * 16; e += 256) {
-    const int hh = e & 15, d = (e >> 4) % D, g = (e >> 4) / D;
-    S xq{}, xd{};
-    if (hh < a.Hg) {
-      const int h = g * a.Hg + hh;
-      xq = q[h * a.qs[2] + d];
-      xd = from_f32<T>(to_f32<O>(dout[h * a.os[2] + d]));
+  for (int g = 0; g < a.G; ++g) {
+    __syncthreads();  // the previous group's rows have been read
+    for (int e = tid * 8; e < 16 * D; e += 256 * 8) {
+      const int hh = e / D, d = e % D;
+      Frag<T> xq = frag_zero<T>(), xd = frag_zero<T>();
+      if (hh < a.Hg) {
+        const int h = g * a.Hg + hh;
+        xq = frag_load<T>(q + h * a.qs[2] + d);
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = to_f32<O>(dout[h * a.os[2] + d + j]);
+        S* dn = static_cast<S*>(a.dN) + (row * a.Hq + h) * D + d;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const S x = from_f32<T>(f[j]);
+          ds[hh][d + j] = x;
+          dn[j] = x;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ds[hh][d + j] = S{};
+      }
+      frag_store<T>(&qs[hh][d], xq);
     }
-    qT[e] = xq;
-    dT[e] = xd;
-  }
-  for (int e = threadIdx.x; e < a.Hq * D; e += 256) {
-    const int h = e / D, d = e % D;
-    dN[e] = from_f32<T>(to_f32<O>(dout[h * a.os[2] + d]));
+    __syncthreads();
+    S* qT = static_cast<S*>(a.qT) + (row * a.G + g) * D * 16;
+    S* dT = static_cast<S*>(a.dT) + (row * a.G + g) * D * 16;
+    for (int e = tid; e < 16 * D; e += 256) {
+      const int hh = e & 15, d = e >> 4;
+      qT[e] = qs[hh][d];
+      dT[e] = ds[hh][d];
+    }
   }
 }
 
