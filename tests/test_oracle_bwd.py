@@ -147,3 +147,21 @@ def test_closed_form_sums_of_key_and_value_gradients():
     w = d["gates"][..., 1] + d["gates"][..., 2] + d["gates"][..., 0] * has_cmp[None, :, None]
     want = (w[..., None] * d["dout"]).reshape(B, L, 2, Hq // 2, D).sum(axis=(1, 3))
     np.testing.assert_allclose(g["dv"].sum(axis=1), want, atol=1e-11)
+
+
+def test_rows_option_gives_the_whole_gradient_of_keys_only_those_rows_see():
+    # The 64k GPU check compares dk / dv of the last block's keys with the
+    # oracle run on the last 64 rows only: no earlier row sees those keys
+    # (causal window, own-or-earlier blocks, complete block means), so the
+    # restricted run must equal the full one there, and dq / dgates of the
+    # given rows must equal the full run's.
+    block, top_k, window = 16, 3, 20
+    d = _data(80, 4, 2, 8, seed=9, top_k=top_k, window=window, block=block)
+    idx = nsa_ref.prefill(d["q"], d["k"], d["v"], d["gates"], block=block, top_k=top_k, window=window)["idx"]
+    full = nsa_bwd_ref.prefill_backward(d["q"], d["k"], d["v"], d["gates"], d["dout"], idx, block=block,
+                                        top_k=top_k, window=window)
+    last = np.arange(80 - block, 80)
+    part = nsa_bwd_ref.prefill_backward(d["q"], d["k"], d["v"], d["gates"], d["dout"], idx, block=block,
+                                        top_k=top_k, window=window, rows=last)
+    for name in ("dk", "dv", "dq", "dgates"):
+        np.testing.assert_allclose(part[name][:, last], full[name][:, last], rtol=0, atol=1e-12)
