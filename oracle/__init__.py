@@ -3,6 +3,8 @@
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
 this package; the GPU library never does.
 """
-from .nsa_ref import compress, decode, nsa_token, prefill, select_blocks, softmax_attend
+from .nsa_ref import (compress, decode, gates_from_query, n_compressed, nsa_token, prefill, select_blocks,
+                      selection_scores, softmax_attend)
 
-__all__ = ["compress", "decode", "nsa_token", "prefill", "select_blocks", "softmax_attend"]
+__all__ = ["compress", "decode", "gates_from_query", "n_compressed", "nsa_token", "prefill", "select_blocks",
+           "selection_scores", "softmax_attend"]

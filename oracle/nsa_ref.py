@@ -42,10 +42,30 @@ the design notes):
 * R6  softmax scale ``1/sqrt(D)`` in all three branches; gates are given
       post-sigmoid values, one per (token, head, branch), not renormalised.
 * R7  query head ``h`` belongs to KV group ``h // (Hq/G)``.
-* R8  ``select_block_size`` must equal ``compress_block_size``.
 * R12 an injected selection is a set of blocks: entries outside ``[0, t//l]``
       and repeats add nothing; a row with no usable entry gives a selected
       branch of 0.
+
+General geometry (the ``[model.nsa]`` table lists ``compress_block_size`` and
+``select_block_size`` as separate fields; the factory write-up's sketch
+compresses each block with a learned linear map of the flattened block):
+
+* R14 compressed block ``i`` summarises tokens ``[i*d, i*d + l)`` for a
+      compression stride ``1 <= d <= l`` (``d < l``: overlapping blocks); it
+      exists when the whole block lies inside the sequence and is visible to
+      query ``t`` when ``i*d + l - 1 <= t``. The summary is the block mean, or
+      a linear map ``W[o, p, i]`` (output dim, position in the block, input
+      dim) of the flattened block plus a bias ``b[o]``.
+* R15 selection blocks hold ``l' >= l`` tokens: block ``j`` is
+      ``[j*l', j*l' + l')``, the own block is ``t // l'``. A selection
+      block's score is the compressed-attention mass on its tokens, each
+      compressed block's probability spread evenly over the ``l`` tokens it
+      summarises (with ``d = l = l'`` each compressed block is exactly one
+      selection block and this is R3).
+* R16 gates may come from a gate layer: ``gate[t, h, c] = sigmoid(q[t, h] .
+      Wg[h, :, c] + bg[h, c])`` for the branches ``c`` in the order
+      (compressed, selected, window); a one-layer MLP on the query, with
+      synthetic weights here.
 """
 
 from __future__ import annotations
@@ -53,15 +73,64 @@ from __future__ import annotations
 import numpy as np
 
 
-def compress(x, block: int) -> np.ndarray:
-    """Block means (R1): x [B, L, G, D] -> [B, L // block, G, D], float64.
+def n_compressed(L: int, block: int, stride: int) -> int:
+    """Compressed blocks of an L-token sequence (R14): those wholly inside it."""
+    return (L - block) // stride + 1 if L >= block else 0
 
-    Only complete blocks get an entry; a trailing partial block has none.
+
+def compress(x, block: int, stride=None, weight=None, bias=None) -> np.ndarray:
+    """Compressed block representations: x [B, L, G, D] -> [B, Nc, G, D], float64.
+
+    Stride ``block`` and no weight: the block means of R1 (a trailing partial
+    block has no entry). Otherwise R14: block i covers tokens
+    [i*stride, i*stride + block); its representation is the mean, or
+    ``weight`` [D, block, D] (output dim, position, input dim) applied to the
+    flattened block plus ``bias`` [D].
     """
     x = np.asarray(x, dtype=np.float64)
     B, L, G, D = x.shape
-    nc = L // block
-    return x[:, : nc * block].reshape(B, nc, block, G, D).mean(axis=2)
+    if (stride is None or stride == block) and weight is None:
+        nc = L // block
+        return x[:, : nc * block].reshape(B, nc, block, G, D).mean(axis=2)
+    stride = block if stride is None else stride
+    nc = n_compressed(L, block, stride)
+    out = np.zeros((B, nc, G, D))
+    for i in range(nc):
+        blk = x[:, i * stride: i * stride + block]          # [B, block, G, D]
+        if weight is None:
+            out[:, i] = blk.mean(axis=1)
+        else:
+            w = np.asarray(weight, dtype=np.float64)
+            out[:, i] = np.einsum("opc,bpgc->bgo", w, blk) + np.asarray(bias, dtype=np.float64)
+    return out
+
+
+def selection_scores(cmp_scores: np.ndarray, block: int, stride: int, select_block: int, own: int) -> np.ndarray:
+    """Selection-block scores from compressed-block scores (R15).
+
+    ``cmp_scores`` [nvis] holds the scores of the visible compressed blocks.
+    With stride == block == select_block they are the selection scores
+    themselves; otherwise the result [own + 1] gives, for selection block j,
+    the sum over compressed blocks i of score_i times the fraction of block
+    i's tokens that lie in selection block j.
+    """
+    if stride == block == select_block:
+        return cmp_scores
+    out = np.zeros(own + 1)
+    for i, si in enumerate(cmp_scores):
+        lo, hi = i * stride, i * stride + block
+        for j in range(lo // select_block, (hi - 1) // select_block + 1):
+            overlap = min(hi, (j + 1) * select_block) - max(lo, j * select_block)
+            out[j] += si * overlap / block
+    return out
+
+
+def gates_from_query(q, weight, bias) -> np.ndarray:
+    """Gate layer (R16): q [B, L, Hq, D], weight [Hq, D, 3], bias [Hq, 3] ->
+    gates [B, L, Hq, 3] = sigmoid(q . weight + bias), float64."""
+    q = np.asarray(q, dtype=np.float64)
+    z = np.einsum("blhd,hdc->blhc", q, np.asarray(weight, dtype=np.float64)) + np.asarray(bias, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-z))
 
 
 def softmax_attend(qh: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: float):
@@ -85,7 +154,9 @@ def select_blocks(scores: np.ndarray, own: int, top_k: int):
     ``scores`` holds the block scores of every visible block; candidates are the
     blocks before the own block. Returns (idx [top_k] int32 ascending, padded
     with -1; gap) where gap is the (top_k-1)-th largest candidate score minus
-    the top_k-th largest (inf when every candidate is taken).
+    the top_k-th largest: the last chosen candidate against the first one
+    left out. gap is inf when no score decides the set: every candidate is
+    taken, or top_k == 1 (the own block alone, no candidate is chosen).
     """
     if own <= top_k - 1:
         chosen = list(range(own + 1))
@@ -97,27 +168,31 @@ def select_blocks(scores: np.ndarray, own: int, top_k: int):
         chosen = sorted(int(j) for j in order[: top_k - 1]) + [own]
         chosen.sort()
         ranked = cand[order]
-        gap = float(ranked[top_k - 2] - ranked[top_k - 1])
+        gap = float(ranked[top_k - 2] - ranked[top_k - 1]) if top_k >= 2 else np.inf
     idx = np.full(top_k, -1, dtype=np.int32)
     idx[: len(chosen)] = chosen
     return idx, gap
 
 
 def nsa_token(q_t, K, V, Kc, Vc, t: int, g_t, *, block: int, top_k: int, window: int,
-              scale: float, inject=None) -> dict:
+              scale: float, inject=None, select_block=None, stride=None) -> dict:
     """NSA forward for one query position ``t`` of one sequence.
 
     q_t [Hq, D]; K, V [T, G, D] with T > t (rows after t are never read);
-    Kc, Vc [nc, G, D] with nc >= (t+1)//block; g_t [Hq, 3] gates in the order
-    (compressed, selected, window); inject [G, top_k] replaces the selection.
+    Kc, Vc [nc, G, D] holding at least the compressed blocks visible at t;
+    g_t [Hq, 3] gates in the order (compressed, selected, window); inject
+    [G, top_k] replaces the selection. ``select_block`` (l') and ``stride``
+    (d) default to ``block`` (l).
     """
     q_t = np.asarray(q_t, dtype=np.float64)
     g_t = np.asarray(g_t, dtype=np.float64)
     Hq, D = q_t.shape
     G = K.shape[1]
     Hg = Hq // G
-    nvis = (t + 1) // block          # R2
-    own = t // block                 # R4
+    d = block if stride is None else stride
+    ls = block if select_block is None else select_block
+    nvis = (t - block + 1) // d + 1 if t >= block - 1 else 0   # R2, R14
+    own = t // ls                                           # R4, R15
 
     o_cmp = np.zeros((Hq, D))
     o_slc = np.zeros((Hq, D))
@@ -140,6 +215,7 @@ def nsa_token(q_t, K, V, Kc, Vc, t: int, g_t, *, block: int, top_k: int, window:
             scores = probs.sum(axis=0)        # R3
         else:
             scores = np.zeros(0)
+        scores = selection_scores(scores, block, d, ls, own)   # R15
         group_scores.append(scores)
         # block selection shared by the group
         if inject is None:
@@ -149,9 +225,9 @@ def nsa_token(q_t, K, V, Kc, Vc, t: int, g_t, *, block: int, top_k: int, window:
         # selected branch: tokens of the chosen blocks, causal (R5). The
         # selection is a set of blocks: repeated or unusable injected entries
         # add nothing, and no usable block leaves this branch at 0 (R12).
-        blocks = sorted({int(j) for j in idx[g] if 0 <= j and j * block <= t})
+        blocks = sorted({int(j) for j in idx[g] if 0 <= j and j * ls <= t})
         if blocks:
-            toks = np.concatenate([np.arange(j * block, min(j * block + block, t + 1)) for j in blocks])
+            toks = np.concatenate([np.arange(j * ls, min(j * ls + ls, t + 1)) for j in blocks])
             o_slc[hs], lse_slc[hs] = softmax_attend(qg, np.asarray(K[toks, g], dtype=np.float64),
                                                     np.asarray(V[toks, g], dtype=np.float64), scale)
         # sliding-window branch (R5)
@@ -164,26 +240,33 @@ def nsa_token(q_t, K, V, Kc, Vc, t: int, g_t, *, block: int, top_k: int, window:
             "o_cmp": o_cmp, "o_slc": o_slc, "o_win": o_win, "scores": group_scores}
 
 
-def _check_blocks(block: int, select_block):
-    if select_block is not None and select_block != block:
-        raise NotImplementedError("select_block_size must equal compress_block_size (R8)")
+def _geometry(block: int, select_block, stride):
+    """(l', d) with the defaults l' = d = l; 1 <= d <= l <= l' (R14, R15)."""
+    ls = block if select_block is None else int(select_block)
+    d = block if stride is None else int(stride)
+    if not (1 <= d <= block <= ls):
+        raise ValueError(f"need 1 <= stride ({d}) <= block ({block}) <= select_block ({ls})")
+    return ls, d
 
 
 def prefill(q, k, v, gates, *, block: int = 64, select_block=None, top_k: int, window: int,
             scale=None, inject_idx=None, rows=None, branches: bool = False,
-            scores: bool = False) -> dict:
+            scores: bool = False, stride=None, cmp_weights=None) -> dict:
     """NSA prefill: every query position attends causally within its sequence.
 
     q [B, L, Hq, D]; k, v [B, L, G, D]; gates [B, L, Hq, 3]; any float dtype
     holding the exact stored values. ``rows`` restricts the output to the given
     query positions (all positions by default); K/V always span the full
     sequence. ``inject_idx`` [B, L, G, top_k] replaces the selection.
-    Returns out [B, R, Hq, D], idx [B, R, G, top_k], lse [B, R, Hq] and
-    gap [B, R, G] (plus the three branch outputs and the selected branch's own
-    log-sum-exp ``lse_slc`` [B, R, Hq] when ``branches``, and the
-    block scores [B, R, G, L // block] when ``scores``, NaN where undefined).
+    ``select_block`` (l'), ``stride`` (d) and ``cmp_weights`` (wk, bk, wv, bv:
+    the learned compressor of R14; None = block means) give the general
+    geometry. Returns out [B, R, Hq, D], idx [B, R, G, top_k], lse [B, R, Hq]
+    and gap [B, R, G] (plus the three branch outputs and the selected
+    branch's own log-sum-exp ``lse_slc`` [B, R, Hq] when ``branches``, and
+    the selection-block scores [B, R, G, ceil(L / l')] when ``scores``, NaN
+    where undefined).
     """
-    _check_blocks(block, select_block)
+    ls, d = _geometry(block, select_block, stride)
     B, L, Hq, D = q.shape
     G = k.shape[2]
     if Hq % G:
@@ -200,17 +283,18 @@ def prefill(q, k, v, gates, *, block: int = 64, select_block=None, top_k: int, w
         res["lse_slc"] = np.zeros((B, R, Hq))
     fixed = list(res)
     if scores:
-        res["scores"] = np.full((B, R, G, L // block), np.nan)
+        res["scores"] = np.full((B, R, G, -(-L // ls)), np.nan)
+    wk, bk, wv, bv = (None,) * 4 if cmp_weights is None else cmp_weights
     for b in range(B):
         K = np.asarray(k[b], dtype=np.float64)
         V = np.asarray(v[b], dtype=np.float64)
-        Kc = compress(K[None], block)[0]
-        Vc = compress(V[None], block)[0]
+        Kc = compress(K[None], block, d, wk, bk)[0]
+        Vc = compress(V[None], block, d, wv, bv)[0]
         for r, t in enumerate(rows):
             t = int(t)
             inj = None if inject_idx is None else inject_idx[b, t]
             one = nsa_token(q[b, t], K, V, Kc, Vc, t, gates[b, t], block=block, top_k=top_k,
-                            window=window, scale=scale, inject=inj)
+                            window=window, scale=scale, inject=inj, select_block=ls, stride=d)
             for name in fixed:
                 res[name][b, r] = one[name]
             if scores:
@@ -221,16 +305,17 @@ def prefill(q, k, v, gates, *, block: int = 64, select_block=None, top_k: int, w
 
 def decode(q, k_cache, v_cache, kc_cache, vc_cache, seqlens, gates, *, block: int = 64,
            select_block=None, top_k: int, window: int, scale=None, inject_idx=None,
-           branches: bool = False) -> dict:
+           branches: bool = False, stride=None) -> dict:
     """NSA decode: one new query per sequence at position ``seqlens[b] - 1``.
 
     q [B, Hq, D]; k_cache, v_cache [B, G, Lmax, D] already holding the new
-    token; kc_cache, vc_cache [B, G, Nmax, D] holding the block means of the
-    complete blocks (used as given); seqlens [B]; gates [B, Hq, 3].
-    Returns out [B, Hq, D], idx [B, G, top_k], lse [B, Hq], gap [B, G] and the
-    block scores [B, G, Nmax] (NaN where undefined).
+    token; kc_cache, vc_cache [B, G, Nmax, D] holding the representations of
+    the compressed blocks that lie wholly in the sequence (used as given);
+    seqlens [B]; gates [B, Hq, 3]. Returns out [B, Hq, D], idx [B, G, top_k],
+    lse [B, Hq], gap [B, G] and the selection-block scores
+    [B, G, max(Nmax, ceil(Lmax / l'))] (NaN where undefined).
     """
-    _check_blocks(block, select_block)
+    ls, d = _geometry(block, select_block, stride)
     B, Hq, D = q.shape
     G = k_cache.shape[1]
     if scale is None:
@@ -241,17 +326,17 @@ def decode(q, k_cache, v_cache, kc_cache, vc_cache, seqlens, gates, *, block: in
         for name in ("o_cmp", "o_slc", "o_win"):
             res[name] = np.zeros((B, Hq, D))
     fixed = list(res)
-    res["scores"] = np.full((B, G, kc_cache.shape[2]), np.nan)
+    res["scores"] = np.full((B, G, max(kc_cache.shape[2], -(-k_cache.shape[2] // ls))), np.nan)
     for b in range(B):
         t = int(seqlens[b]) - 1
-        nvis = (t + 1) // block
+        nvis = n_compressed(t + 1, block, d)
         K = np.asarray(k_cache[b, :, : t + 1], dtype=np.float64).transpose(1, 0, 2)
         V = np.asarray(v_cache[b, :, : t + 1], dtype=np.float64).transpose(1, 0, 2)
         Kc = np.asarray(kc_cache[b, :, :nvis], dtype=np.float64).transpose(1, 0, 2)
         Vc = np.asarray(vc_cache[b, :, :nvis], dtype=np.float64).transpose(1, 0, 2)
         inj = None if inject_idx is None else inject_idx[b]
         one = nsa_token(q[b], K, V, Kc, Vc, t, gates[b], block=block, top_k=top_k,
-                        window=window, scale=scale, inject=inj)
+                        window=window, scale=scale, inject=inj, select_block=ls, stride=d)
         for name in fixed:
             res[name][b] = one[name]
         for g, sg in enumerate(one["scores"]):

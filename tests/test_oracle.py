@@ -371,9 +371,11 @@ def test_edge_shapes():
     r2 = nsa_ref.prefill(d["q"], d["k"], d["v"], d["gates"], block=8, top_k=4, window=3,
                          inject_idx=inj)
     np.testing.assert_allclose(r2["out"], r["out"], atol=1e-15)
-    with pytest.raises(NotImplementedError):
-        nsa_ref.prefill(d["q"], d["k"], d["v"], d["gates"], block=8, select_block=16, top_k=2,
-                        window=3)
+    # selection blocks smaller than the compressed blocks, or a stride past the block: rejected
+    with pytest.raises(ValueError):
+        nsa_ref.prefill(d["q"], d["k"], d["v"], d["gates"], block=8, select_block=4, top_k=2, window=3)
+    with pytest.raises(ValueError):
+        nsa_ref.prefill(d["q"], d["k"], d["v"], d["gates"], block=8, stride=9, top_k=2, window=3)
 
 
 # ---------------------------------------------------------------- generator
@@ -399,3 +401,62 @@ def test_generator_is_deterministic_and_prefix_stable():
     np.testing.assert_array_equal(d["gates"][0], b["gates"][0, 149])
     g = inputs.to_f64(b["gates"], "bf16")
     assert np.all((g > 0) & (g < 1))
+
+
+# ---------------------------------------------------------------- selection gap
+
+@pytest.mark.parametrize("top_k,idx,gap", [
+    # candidates 0..4 score 0.5, 0.1, 0.9, 0.35, 0.62; the own block is 5
+    (1, [5], np.inf),                      # own block alone: no score decides anything
+    (2, [2, 5], 0.9 - 0.62),               # last chosen 0.9, first left out 0.62
+    (3, [2, 4, 5], 0.62 - 0.5),
+    (4, [0, 2, 4, 5], 0.5 - 0.35),
+    (5, [0, 2, 3, 4, 5], 0.35 - 0.1),      # own == top_k: one candidate left out
+    (6, [0, 1, 2, 3, 4, 5], np.inf),       # own == top_k - 1: every candidate taken
+    (8, [0, 1, 2, 3, 4, 5, -1, -1], np.inf),
+])
+def test_selection_gap_on_hand_built_scores(top_k, idx, gap):
+    # Check A's excuse rule reads this gap: the score of the last candidate the
+    # rule keeps minus the score of the first one it leaves out.
+    scores = np.array([0.5, 0.1, 0.9, 0.35, 0.62, 0.01])   # the last entry is the own block's
+    got_idx, got_gap = nsa_ref.select_blocks(scores, 5, top_k)
+    assert list(got_idx) == idx
+    if np.isinf(gap):
+        assert np.isinf(got_gap) and got_gap > 0
+    else:
+        assert abs(got_gap - gap) < 1e-15
+
+
+def test_selection_gap_at_a_near_tie_and_an_exact_tie():
+    # a 1e-9 lead decides the boundary: the gap is that lead
+    idx, gap = nsa_ref.select_blocks(np.array([0.3, 0.3 + 1e-9, 0.1, 0.2]), 4, 2)
+    assert list(idx) == [1, 4] and abs(gap - 1e-9) < 1e-15
+    idx, gap = nsa_ref.select_blocks(np.array([0.3, 0.3 + 1e-9, 0.1, 0.2]), 4, 3)
+    assert list(idx) == [0, 1, 4] and abs(gap - 0.1) < 1e-15
+    # an exact tie at the boundary: the lower index wins and the gap is 0
+    idx, gap = nsa_ref.select_blocks(np.array([0.2, 0.3, 0.3, 0.1]), 4, 2)
+    assert list(idx) == [1, 4] and gap == 0.0
+
+
+def test_prefill_gap_is_the_boundary_of_a_full_sort_of_its_scores():
+    # through the whole prefill: for rows with own == top_k - 1 (all taken),
+    # own == top_k (one left out) and own > top_k, the reported gap is the
+    # difference between ranks top_k - 1 and top_k of a plain descending sort
+    # of the row's candidate scores, and the chosen set is the top of that sort
+    L, Hq, G, D, l, n = 120, 6, 2, 8, 8, 4
+    d = _data(L, Hq, G, D, seed=43)
+    rows = [3 * l, 3 * l + 5, 4 * l, 4 * l + 7, 10 * l, L - 1]
+    r = nsa_ref.prefill(d["q"], d["k"], d["v"], d["gates"], block=l, top_k=n, window=6, rows=rows,
+                        scores=True)
+    for i, t in enumerate(rows):
+        own = t // l
+        for g in range(G):
+            cand = [(float(r["scores"][0, i, g, j]), j) for j in range(own)]
+            if own <= n - 1:
+                assert np.isinf(r["gap"][0, i, g])
+                continue
+            desc = sorted(cand, key=lambda sj: (-sj[0], sj[1]))
+            want = desc[n - 2][0] - desc[n - 1][0]
+            assert abs(r["gap"][0, i, g] - want) < 1e-15
+            assert r["gap"][0, i, g] > 0                       # distinct random scores
+            assert sorted(j for _, j in desc[: n - 1]) + [own] == list(r["idx"][0, i, g])
