@@ -168,6 +168,34 @@ class _LazyBf16:
         return inputs.bf16_bits_to_f32(self.arr[key])
 
 
+def host_description():
+    """CPU model (from /proc/cpuinfo) and the BLAS library numpy calls."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer')})"
+                for i in threadpool_info() if i.get("user_api") == "blas"]
+        blas = "; ".join(libs) or None
+    except Exception:
+        pass
+    if blas is None:
+        try:
+            cfg = np.show_config(mode="dicts")
+            b = cfg.get("Build Dependencies", {}).get("blas", {})
+            blas = f"{b.get('name')} {b.get('version')}"
+        except Exception:
+            blas = "unknown"
+    return model or "unknown", blas
+
+
 def cpu_baseline(cfg, raw, seconds: float):
     """The float64 oracle on evenly spaced query rows of the same workload."""
     from oracle import nsa_ref
@@ -175,6 +203,7 @@ def cpu_baseline(cfg, raw, seconds: float):
         ncores = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         ncores = os.cpu_count() or 1
+    cpu_model, blas = host_description()
     try:
         from threadpoolctl import threadpool_limits
         limiter = threadpool_limits(limits=ncores)
@@ -200,6 +229,7 @@ def cpu_baseline(cfg, raw, seconds: float):
     if limiter is not None:
         limiter.unregister() if hasattr(limiter, "unregister") else None
     return {"value": n_rows * cfg.batch / dt, "unit": "tokens/s", "cores": ncores, "kind": "oracle",
+            "cpu_model": cpu_model, "blas": blas,
             "sample": f"{n_rows} evenly spaced query rows of the {cfg.name} workload (full "
                       f"{L}-token context, all {cfg.n_q_heads} heads), float64 numpy, {dt:.1f} s"}
 

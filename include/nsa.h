@@ -20,20 +20,29 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Calls enqueue their kernels on it and return; results are ready when the
  *    stream reaches that point.
- *  - Arguments are validated on the host before anything is enqueued. On any
- *    error nothing is launched, nothing is written, and a status code is
- *    returned; nsa_last_error() then holds a message (per calling thread).
- *    There is no silent fallback (no dense path, no clamping).
+ *  - Arguments are validated on the host before anything is enqueued. On an
+ *    argument error (NSA_ERR_INVALID_ARGUMENT, NSA_ERR_UNSUPPORTED,
+ *    NSA_ERR_WORKSPACE_TOO_SMALL) nothing is launched and nothing is
+ *    written. Kernel attributes are set before the first launch, so a HIP
+ *    failure there also launches nothing; NSA_ERR_HIP from a later launch or
+ *    event record means the kernels before it are already enqueued and may
+ *    have written their outputs or the workspace. nsa_last_error() holds a
+ *    message for any failing call (per calling thread). There is no silent
+ *    fallback (no dense path, no clamping).
  *  - Strides are in ELEMENTS; the head dimension is always contiguous.
  *  - Element types: in_dtype applies to q, k, v, caches and gates; out_dtype
  *    to out. Supported: (bf16 in, bf16 out), (bf16 in, f32 out),
  *    (f32 in, f32 out). Block summaries and matrix products use the input
  *    type as operands with fp32 accumulation; softmax, block scores, top-k and
  *    the gate combination run in fp32.
- *  - Supported geometry: compress_block_size == select_block_size == 64;
- *    head_dim in {64, 128}; n_q_heads a multiple of n_kv_heads with at most 16
- *    query heads per KV head; 1 <= select_top_k <= 64; sliding_window >= 1;
- *    any seqlen >= 1 (a trailing partial block is allowed).
+ *  - Supported geometry: head_dim in {64, 128}; n_q_heads a multiple of
+ *    n_kv_heads with at most 16 query heads per KV head; 1 <= select_top_k
+ *    <= 64; sliding_window >= 1; any seqlen >= 1 (a trailing partial block is
+ *    allowed). Block sizes: the forward prefill entry points take any
+ *    compress_block_size l <= select_block_size l' with l' a multiple of 32
+ *    and select_top_k * l' <= 4096 (see nsa_fwd_prefill_general for the
+ *    compressed-to-selection mapping); decode, the backward pass and the
+ *    prefill that keeps the selected branch need l == l' == 64.
  *  - Query head h reads KV head h / (n_q_heads / n_kv_heads).
  *  - Calls are reentrant; two calls that share a workspace or an output
  *    buffer must be ordered by the caller.
@@ -65,8 +74,8 @@ typedef enum {
 
 /* The [model.nsa] parameters of the NSA how-to (qwbw.cn/news/106443), section 3. */
 typedef struct {
-  int32_t compress_block_size; /* l: tokens per compressed block; stride l, no overlap */
-  int32_t select_block_size;   /* l': tokens per selectable block; must equal l */
+  int32_t compress_block_size; /* l: tokens per compressed block; stride l unless nsa_general_t says otherwise */
+  int32_t select_block_size;   /* l': tokens per selectable block, l' >= l */
   int32_t select_top_k;        /* n: blocks each query attends to, its own block included */
   int32_t sliding_window;      /* w: window length in tokens, the query itself included */
   float softmax_scale;         /* <= 0 selects 1/sqrt(head_dim); used by all three branches */
@@ -153,12 +162,66 @@ nsa_status_t nsa_decode_workspace_bytes(const nsa_decode_desc_t* desc,
  *   outside [0, t/l] are skipped and repeated entries count once (the
  *   selection is a set of blocks); a row with no usable entry gives a
  *   selected-branch output of 0.
- * `out` is also used as scratch while the call runs.
+ * With a float32 output, `out` also holds the window + compressed part of
+ * each row while the call runs; with a bf16 output that part is kept in
+ * float32 in the workspace, so every output element is rounded to bf16
+ * once, from the float32 sum of the three gated branches.
  */
 nsa_status_t nsa_fwd_prefill(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
                              const void* q, const void* k, const void* v, const void* gates,
                              void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * General geometry of the prefill (the [model.nsa] fields of the NSA how-to,
+ * qwbw.cn/news/106443, section 3, list compress_block_size and
+ * select_block_size separately; the NSA factory write-up, chencunli.com,
+ * section "What dynamic sparsity actually sparsifies", compresses each block
+ * into one representation with a learned linear map of the flattened block,
+ * and the how-to's gate_type is "learned"):
+ *   compress_stride d, 1 <= d <= l: compressed block i covers tokens
+ *       [i*d, i*d + l) (d < l: overlapping blocks); the blocks that lie wholly
+ *       inside the sequence exist, and block i is visible to query t when
+ *       i*d + l - 1 <= t;
+ *   wk, bk, wv, bv (all or none; NULL: block means): the learned compressor,
+ *       kc_i[o] = sum_{p < l, c < D} wk[o][p][c] * k[i*d + p][c] + bk[o] (and
+ *       the same for v). wk, wv: [D][l][D] contiguous, 16-byte aligned; bk,
+ *       bv: [D]; all in in_dtype;
+ *   gate_w, gate_b (both or none; NULL: the gates argument is used): the gate
+ *       layer gate[t][h][c] = sigmoid(q[t][h] . gate_w[h][:, c] +
+ *       gate_b[h][c]) for the branches c = (compressed, selected, window),
+ *       gate_w [Hq][D][3], gate_b [Hq][3] contiguous in in_dtype; the gates
+ *       are computed in float32 into the workspace and the gates argument may
+ *       be NULL.
+ * Selection blocks hold l' = select_block_size tokens; the own block is
+ * t / l'. A selection block's score is the compressed-attention mass on its
+ * tokens, each compressed block's probability spread evenly over its l tokens
+ * (sum over compressed blocks i of p_i * |tokens of i in the block| / l);
+ * with d = l = l' this is the plain block score. All else as nsa_fwd_prefill
+ * (idx rows hold selection-block indices). The caller owns the weights; they
+ * must stay valid until the call completes on the stream.
+ */
+typedef struct {
+  int32_t compress_stride;
+  const void* wk;
+  const void* bk;
+  const void* wv;
+  const void* bv;
+  const void* gate_w;
+  const void* gate_b;
+} nsa_general_t;
+
+/* Workspace bytes of nsa_fwd_prefill_general (general may be NULL: the plain
+ * stride and block means, gates given). */
+nsa_status_t nsa_prefill_general_workspace_bytes(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                                                 const nsa_general_t* general, size_t* bytes);
+/* nsa_fwd_prefill with the general geometry above; errors as for
+ * nsa_fwd_prefill, plus NSA_ERR_INVALID_ARGUMENT for a stride outside [1, l],
+ * an incomplete weight set or a misaligned weight. */
+nsa_status_t nsa_fwd_prefill_general(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                                     const nsa_general_t* general, const void* q, const void* k, const void* v,
+                                     const void* gates, void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * nsa_fwd_prefill that also keeps what the backward pass needs of the
@@ -232,7 +295,13 @@ nsa_status_t nsa_fwd_decode(const nsa_decode_desc_t* desc, const nsa_params_t* p
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Block compression used by both phases: kc[b, g, j] = mean of k[b, g, t] over
+ * Block compression, the step that turns each key/value block into one
+ * compressed representation (NSA factory write-up, chencunli.com, "DeepSeek
+ * NSA on the Siemens 840D manual", section "What dynamic sparsity actually
+ * sparsifies"; block size: compress_block_size of the NSA how-to,
+ * qwbw.cn/news/106443, section 3). The pages call that step learnable; here,
+ * as in the prefill, it is the plain mean of the block.
+ * Used by both phases: kc[b, g, j] = mean of k[b, g, t] over
  * t in [j*block_size, (j+1)*block_size), for j < n_tokens / block_size (only
  * complete blocks), and the same for v -> vc. Summation in fp32, one rounding
  * to dtype. k, v are [B, G, n_tokens, D] with strides (b, kv head, t); kc, vc
@@ -295,7 +364,7 @@ nsa_status_t nsa_fwd_decode_timed(const nsa_decode_desc_t* desc, const nsa_param
  *   is asynchronous on `stream`; inputs must stay valid until it completes.
  * dk and dv are sums accumulated with floating-point atomics, so their last
  * bits may differ from call to call. Errors are reported as for the forward
- * entry points; a failing call launches nothing.
+ * entry points.
  */
 nsa_status_t nsa_bwd_prefill_workspace_bytes(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
                                              size_t* bytes);

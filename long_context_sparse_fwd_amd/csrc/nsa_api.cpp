@@ -39,7 +39,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool dtype_ok(nsa_dtype_t d) { return d == NSA_F32 || d == NSA_BF16; }
 
-nsa_status_t check_params(const nsa_params_t* p, int head_dim) {
+// general: the prefill's block sizes (l <= l', l' a multiple of 32);
+// otherwise (decode, backward) both must be 64.
+nsa_status_t check_params(const nsa_params_t* p, int head_dim, bool general = false) {
   if (p == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "params is NULL");
   if (p->compress_block_size < 1 || p->select_block_size < 1)
     return fail(NSA_ERR_INVALID_ARGUMENT, "block sizes must be >= 1 (got %d, %d)",
@@ -50,12 +52,54 @@ nsa_status_t check_params(const nsa_params_t* p, int head_dim) {
     return fail(NSA_ERR_INVALID_ARGUMENT, "sliding_window must be >= 1 (got %d)", p->sliding_window);
   if (!std::isfinite(p->softmax_scale))
     return fail(NSA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
-  if (p->compress_block_size != nsa::kBlock || p->select_block_size != nsa::kBlock)
-    return fail(NSA_ERR_UNSUPPORTED, "only compress_block_size == select_block_size == 64 is supported "
-                                     "(got %d, %d)", p->compress_block_size, p->select_block_size);
   if (p->select_top_k > 64)
     return fail(NSA_ERR_UNSUPPORTED, "select_top_k > 64 is not supported (got %d)", p->select_top_k);
+  const int l = p->compress_block_size, ls = p->select_block_size;
+  if (!general) {
+    if (l != nsa::kBlock || ls != nsa::kBlock)
+      return fail(NSA_ERR_UNSUPPORTED, "this entry point needs compress_block_size == select_block_size == 64 "
+                                       "(got %d, %d)", l, ls);
+  } else {
+    if (ls < l)
+      return fail(NSA_ERR_UNSUPPORTED, "select_block_size (%d) below compress_block_size (%d) is not supported",
+                  ls, l);
+    if (ls % 32 != 0)
+      return fail(NSA_ERR_UNSUPPORTED, "select_block_size must be a multiple of 32 (got %d)", ls);
+    if (static_cast<int64_t>(ls) * p->select_top_k > nsa::kMaxSelTokens)
+      return fail(NSA_ERR_UNSUPPORTED, "select_top_k * select_block_size above %d is not supported (got %d * %d)",
+                  nsa::kMaxSelTokens, p->select_top_k, ls);
+    if (l > 4096) return fail(NSA_ERR_UNSUPPORTED, "compress_block_size above 4096 is not supported (got %d)", l);
+  }
   (void)head_dim;
+  return NSA_OK;
+}
+
+// Geometry of a prefill call beyond nsa_params_t: the compression stride and
+// the optional learned compressor / gate layer (all null: block means, gates
+// given).
+struct Geometry {
+  int stride;  // d (the compress block size when not given)
+  const nsa_general_t* gen;
+  bool learned() const { return gen != nullptr && (gen->wk != nullptr || gen->wv != nullptr); }
+  bool gate_layer() const { return gen != nullptr && gen->gate_w != nullptr; }
+};
+
+nsa_status_t check_general(const nsa_params_t* p, const nsa_general_t* gen, Geometry* geo) {
+  geo->gen = gen;
+  geo->stride = p->compress_block_size;
+  if (gen == nullptr) return NSA_OK;
+  if (gen->compress_stride < 1 || gen->compress_stride > p->compress_block_size)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "compress_stride must lie in [1, compress_block_size %d] (got %d)",
+                p->compress_block_size, gen->compress_stride);
+  geo->stride = gen->compress_stride;
+  if ((gen->wk == nullptr) != (gen->bk == nullptr) || (gen->wv == nullptr) != (gen->bv == nullptr) ||
+      (gen->wk == nullptr) != (gen->wv == nullptr))
+    return fail(NSA_ERR_INVALID_ARGUMENT, "the learned compressor needs all of wk, bk, wv, bv (or none)");
+  if ((gen->gate_w == nullptr) != (gen->gate_b == nullptr))
+    return fail(NSA_ERR_INVALID_ARGUMENT, "the gate layer needs both gate_w and gate_b (or neither)");
+  if ((gen->wk != nullptr && (!aligned16(gen->wk) || !aligned16(gen->wv))) ||
+      (gen->gate_w != nullptr && (reinterpret_cast<uintptr_t>(gen->gate_w) & 1u)))
+    return fail(NSA_ERR_INVALID_ARGUMENT, "wk / wv must be 16-byte aligned and gate_w element aligned");
   return NSA_OK;
 }
 
@@ -104,19 +148,22 @@ nsa_status_t check_ptr(const char* name, const void* p, bool need16) {
 
 struct PrefillPlan {
   int Nb, Nc, NcT, cmp_waves, cmp_lo_lds, cmp_tiles, sel_tiles;
-  size_t off_kt, off_vt, off_kct, off_kclt, off_vct, off_idx, total;
+  size_t off_kt, off_vt, off_kct, off_kclt, off_vct, off_idx, off_part, off_gates, total;
 };
 
 // q_offset: the queries are positions [q_offset, seqlen) (0 for a whole
 // prefill); only the tile counts depend on it, not the workspace.
 nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, PrefillPlan* pl,
-                          int64_t q_offset = 0) {
+                          int64_t q_offset = 0, const nsa_general_t* gen = nullptr, Geometry* geo_out = nullptr) {
   if (d == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "desc is NULL");
   if (d->batch < 0 || d->seqlen < 0)
     return fail(NSA_ERR_INVALID_ARGUMENT, "batch and seqlen must be >= 0");
   NSA_TRY(check_heads(d->n_q_heads, d->n_kv_heads, d->head_dim));
   NSA_TRY(check_dtypes(d->in_dtype, d->out_dtype));
-  NSA_TRY(check_params(p, d->head_dim));
+  NSA_TRY(check_params(p, d->head_dim, true));
+  Geometry geo;
+  NSA_TRY(check_general(p, gen, &geo));
+  if (geo_out != nullptr) *geo_out = geo;
   NSA_TRY(check_strides("q", d->q_stride, 3, true));
   NSA_TRY(check_strides("k", d->k_stride, 3, true));
   NSA_TRY(check_strides("v", d->v_stride, 3, true));
@@ -127,8 +174,11 @@ nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, Pr
       B * G * ((L + 63) / 64) * 64 > INT32_MAX)
     return fail(NSA_ERR_UNSUPPORTED, "problem too large for 32-bit work indexing");
   pl->Nb = static_cast<int>((L + 63) / 64);
-  pl->Nc = static_cast<int>(L / 64);
+  const int64_t cl = p->compress_block_size;
+  pl->Nc = static_cast<int>(L >= cl ? (L - cl) / geo.stride + 1 : 0);
   pl->NcT = (pl->Nc + 63) / 64;
+  if (B * G * static_cast<int64_t>(pl->NcT) * 64 > INT32_MAX)
+    return fail(NSA_ERR_UNSUPPORTED, "problem too large for 32-bit work indexing");
   // the widest compressed-kernel workgroup whose LDS fits; at 8 waves the
   // low parts of the K means go through LDS as well when that still fits
   pl->cmp_waves = 0;
@@ -170,6 +220,13 @@ nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, Pr
   off = align_up(off + static_cast<size_t>(B * G) * pl->NcT * tile);
   pl->off_idx = off;
   off = align_up(off + static_cast<size_t>(B * L * G) * p->select_top_k * sizeof(int32_t));
+  // bf16 output: fp32 rows of the window + compressed part, so that the
+  // output is rounded once (the query rows never exceed the context length)
+  pl->off_part = off;
+  if (d->out_dtype == NSA_BF16) off = align_up(off + static_cast<size_t>(B * L * d->n_q_heads) * D * sizeof(float));
+  // gate layer: its fp32 gates of every query row
+  pl->off_gates = off;
+  if (geo.gate_layer()) off = align_up(off + static_cast<size_t>(B * L * d->n_q_heads) * 3 * sizeof(float));
   pl->total = off;
   return NSA_OK;
 }
@@ -364,13 +421,20 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
                                  const void* q, const void* k, const void* v, const void* gates,
                                  void* out, int32_t* idx, nsa_idx_mode_t idx_mode, void* workspace,
                                  size_t workspace_bytes, void* stream, void* const* events,
-                                 void* save_o = nullptr, float* save_lse = nullptr) {
+                                 void* save_o = nullptr, float* save_lse = nullptr,
+                                 const nsa_general_t* gen = nullptr) {
   if (desc == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "desc is NULL");
   if (q_offset < 0 || q_offset > desc->seqlen)
     return fail(NSA_ERR_INVALID_ARGUMENT, "q_offset %lld outside [0, seqlen %d]",
                 static_cast<long long>(q_offset), desc->seqlen);
   PrefillPlan pl;
-  NSA_TRY(plan_prefill(desc, params, &pl, q_offset));
+  Geometry geo;
+  NSA_TRY(plan_prefill(desc, params, &pl, q_offset, gen, &geo));
+  if (save_o != nullptr &&
+      (params->compress_block_size != nsa::kBlock || params->select_block_size != nsa::kBlock ||
+       geo.stride != nsa::kBlock || geo.learned() || geo.gate_layer()))
+    return fail(NSA_ERR_UNSUPPORTED, "keeping the selected branch for the backward needs the plain geometry "
+                                     "(blocks of 64, stride 64, block means, given gates)");
   if (idx_mode != NSA_IDX_COMPUTE && idx_mode != NSA_IDX_INJECT)
     return fail(NSA_ERR_INVALID_ARGUMENT, "unknown idx_mode %d", static_cast<int>(idx_mode));
   // empty input or no query rows: nothing to do
@@ -384,7 +448,7 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
   NSA_TRY(check_ptr("q", q, true));
   NSA_TRY(check_ptr("k", k, true));
   NSA_TRY(check_ptr("v", v, true));
-  NSA_TRY(check_ptr("gates", gates, false));
+  if (!geo.gate_layer()) NSA_TRY(check_ptr("gates", gates, false));
   NSA_TRY(check_ptr("out", out, true));
   NSA_TRY(check_ptr("workspace", workspace, true));
   if (idx_mode == NSA_IDX_INJECT && idx == nullptr)
@@ -392,7 +456,7 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
   if (idx != nullptr && (reinterpret_cast<uintptr_t>(idx) & 3u) != 0)
     return fail(NSA_ERR_INVALID_ARGUMENT, "idx is not 4-byte aligned");
   const size_t gal = desc->in_dtype == NSA_BF16 ? 2 : 4;
-  if ((reinterpret_cast<uintptr_t>(gates) % gal) != 0)
+  if (!geo.gate_layer() && (reinterpret_cast<uintptr_t>(gates) % gal) != 0)
     return fail(NSA_ERR_INVALID_ARGUMENT, "gates is not aligned to its element size");
   if (workspace_bytes < pl.total)
     return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", pl.total,
@@ -437,6 +501,24 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
   a.vt = ws + pl.off_vt;
   a.save_o = save_o;
   a.save_lse = save_lse;
+  a.part = desc->out_dtype == NSA_BF16 ? reinterpret_cast<float*>(ws + pl.off_part) : nullptr;
+  a.cl = params->compress_block_size;
+  a.cd = geo.stride;
+  a.ls = params->select_block_size;
+  a.inv_cl = 1.0f / static_cast<float>(a.cl);
+  a.sel_map = !(a.cl == a.cd && a.cd == a.ls) ? 1 : 0;
+  a.cmp_in_prep = (a.cl == nsa::kBlock && a.cd == nsa::kBlock && !geo.learned()) ? 1 : 0;
+  if (geo.learned()) {
+    a.wk = gen->wk;
+    a.bk = gen->bk;
+    a.wv = gen->wv;
+    a.bv = gen->bv;
+  }
+  if (geo.gate_layer()) {
+    a.gate_w = gen->gate_w;
+    a.gate_b = gen->gate_b;
+    a.gates32 = reinterpret_cast<float*>(ws + pl.off_gates);
+  }
   a.kct = ws + pl.off_kct;
   a.kclt = ws + pl.off_kclt;
   a.vct = ws + pl.off_vct;
@@ -460,6 +542,23 @@ nsa_status_t nsa_fwd_prefill(const nsa_prefill_desc_t* desc, const nsa_params_t*
                              size_t workspace_bytes, void* stream) {
   return prefill_impl(desc, params, 0, nullptr, nullptr, q, k, v, gates, out, idx, idx_mode, workspace,
                       workspace_bytes, stream, nullptr);
+}
+
+nsa_status_t nsa_prefill_general_workspace_bytes(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                                                 const nsa_general_t* general, size_t* bytes) {
+  if (bytes == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  PrefillPlan pl;
+  NSA_TRY(plan_prefill(desc, params, &pl, 0, general));
+  *bytes = pl.total;
+  return ok();
+}
+
+nsa_status_t nsa_fwd_prefill_general(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
+                                     const nsa_general_t* general, const void* q, const void* k, const void* v,
+                                     const void* gates, void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(desc, params, 0, nullptr, nullptr, q, k, v, gates, out, idx, idx_mode, workspace,
+                      workspace_bytes, stream, nullptr, nullptr, nullptr, general);
 }
 
 nsa_status_t nsa_fwd_prefill_save(const nsa_prefill_desc_t* desc, const nsa_params_t* params, const void* q,
@@ -633,6 +732,8 @@ nsa_status_t nsa_bwd_prefill_saved_timed(const nsa_prefill_desc_t* desc, const n
   if (desc != nullptr && desc->batch > 0 && desc->seqlen > 0) {
     NSA_TRY(check_ptr("o_slc", o_slc, true));
     NSA_TRY(check_ptr("lse_slc", lse_slc, false));
+    if ((reinterpret_cast<uintptr_t>(lse_slc) & 3u) != 0)
+      return fail(NSA_ERR_INVALID_ARGUMENT, "lse_slc is not 4-byte aligned");
   }
   return backward_impl(desc, params, q, k, v, gates, dout, idx, dq, dk, dv, dgates, workspace, workspace_bytes,
                        stream, stage_events, o_slc, lse_slc);

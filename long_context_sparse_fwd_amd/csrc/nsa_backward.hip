@@ -625,6 +625,15 @@ hipError_t launch_backward_t(const BwdArgs& a, hipStream_t st, hipEvent_t* ev) {
   using S = typename T::storage;
   hipError_t e;
   auto rec = [&](int i) { return ev != nullptr ? hipEventRecord(ev[i], st) : hipSuccess; };
+  // the key-side kernels' attributes are set before the first launch
+  const int lds = static_cast<int>(sizeof(BkvStage<T, D>));
+  if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bkv<T, D, 0>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess ||
+      (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bkv<T, D, 1>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess ||
+      (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bkv<T, D, 2>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess)
+    return e;
   if ((e = rec(0)) != hipSuccess) return e;
   const size_t kv_bytes = static_cast<size_t>(a.B) * a.L * a.G * a.D * sizeof(float);
   const size_t kc_bytes = static_cast<size_t>(a.B) * a.Nc * a.G * a.D * sizeof(float);
@@ -664,14 +673,6 @@ hipError_t launch_backward_t(const BwdArgs& a, hipStream_t st, hipEvent_t* ev) {
   else
     hipLaunchKernelGGL((k_bq<T, O, D, false>), dim3(a.B * a.G * ((a.L + 3) / 4)), dim3(256), 0, st, a);
   if ((e = rec(2)) != hipSuccess) return e;
-  const int lds = static_cast<int>(sizeof(BkvStage<T, D>));
-  if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bkv<T, D, 0>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess ||
-      (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bkv<T, D, 1>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess ||
-      (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bkv<T, D, 2>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess)
-    return e;
   if (a.NcT > 0)
     hipLaunchKernelGGL((k_bkv<T, D, 0>), dim3(a.B * a.G * a.bkv_units[0]), dim3(256), lds, st, a);
   hipLaunchKernelGGL((k_bkv<T, D, 1>), dim3(a.B * a.G * a.bkv_units[1]), dim3(256), lds, st, a);

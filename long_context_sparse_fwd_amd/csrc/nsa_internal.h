@@ -32,9 +32,28 @@ struct PrefillArgs {
   // them) take the (sequence, tile) items [sel_bounds[k], sel_bounds[k+1])
   // of the group; sel_bounds[0] = -1 selects the plain eighths instead.
   int sel_bounds[9];
-  int Nb;   // selectable blocks = ceil(L / 64)
-  int Nc;   // complete (compressed) blocks = L / 64
+  int Nb;   // 64-token key tiles = ceil(L / 64)
+  int Nc;   // compressed blocks (wholly inside the context) = (L - cl) / cd + 1, or 0
   int NcT;  // 64-row chunks of the compressed tiles = ceil(Nc / 64)
+  // Geometry: compressed block i covers tokens [i*cd, i*cd + cl); selection
+  // blocks hold ls tokens (a multiple of 32). The plain geometry is
+  // cl = cd = ls = 64 with block means.
+  int cl, cd, ls;
+  float inv_cl;   // 1 / cl
+  int sel_map;    // 1: selection-block scores from the compressed scores by token overlap
+  int cmp_in_prep;  // 1: k_prep writes the compressed tiles (means of its 64-token blocks)
+  // Learned compressor (null: block means): w [D][cl][D] (output dim,
+  // position in the block, input dim) and bias [D], in the input type.
+  const void* wk;
+  const void* bk;
+  const void* wv;
+  const void* bv;
+  // Gate layer (null: the gates are given): gates = sigmoid(q . gate_w[h] +
+  // gate_b[h]), gate_w [Hq][D][3], gate_b [Hq][3] in the input type, written
+  // by k_gate as fp32 [B][Lq][Hq][3] into gates32, which the branches read.
+  const void* gate_w;
+  const void* gate_b;
+  float* gates32;
   int cmp_waves, cmp_tiles, sel_tiles;
   int cmp_lo_lds;  // compressed kernel stages the low parts of the K means in LDS (8 waves only)
   int sel_bm_words;  // words of a k_sel wave's half-block bitmap (one byte per half block)
@@ -48,6 +67,10 @@ struct PrefillArgs {
   int32_t* idx;
   void* kt;   // [B][G][Nb] 64-key K tiles (fragment-major)
   void* vt;   // [B][G][Nb] 64-key V^T tiles
+  // bf16 output: the window + compressed part of each output row in fp32,
+  // [B][Lq][Hq][D], which k_sel completes and rounds to bf16 once; null for
+  // fp32 output (out itself holds that part until k_sel adds to it).
+  float* part;
   void* kct;   // [B][G][NcT] 64-block tiles of block means of K (bf16: the high part)
   void* kclt;  // bf16 input only: the low part, bf16(mean - high), same layout
   void* vct;   // [B][G][NcT] 64-block V^T tiles of block means of V
@@ -94,6 +117,10 @@ hipError_t launch_compress(int B, int G, int Nc, int D, bool bf16, const void* k
 size_t dec_lds_bytes(int NmaxPad, int D, bool bf16, bool logits_lds);
 
 size_t cmpwin_lds_bytes(int waves, int NcT, int D, bool bf16, bool lo_lds);
+
+// Largest select_top_k * select_block_size: a k_sel wave's step list holds
+// kSelTPW * 128 half blocks.
+constexpr int kMaxSelTokens = 64 * 64;
 
 // k_sel: bitmap words per wave (one byte per half block of Nb blocks, padded
 // to 16 bytes) and the dynamic LDS of a launch.

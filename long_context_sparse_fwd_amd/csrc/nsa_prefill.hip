@@ -31,6 +31,7 @@
 //             per CU and work grouped by KV group per XCD: the random block
 //             gathers are bound by L2-miss bandwidth, which fewer concurrent
 //             waves per XCD use better.
+#include <algorithm>
 #include <type_traits>
 
 #include "nsa_device.h"
@@ -96,6 +97,34 @@ __device__ __forceinline__ SeqSpan seq_span(const PrefillArgs& a, int b) {
   return SeqSpan{L, t0};
 }
 
+// Compressed blocks visible to query t: those whose last token i*cd + cl - 1
+// is at or before t.
+__device__ __forceinline__ int nvis_of(const PrefillArgs& a, int t) {
+  return t + 1 >= a.cl ? (t + 1 - a.cl) / a.cd + 1 : 0;
+}
+
+// Gate c (compressed, selected, window) of query row `row` and head h: the
+// gate layer's fp32 output when there is one, else the given gates.
+template <class T>
+__device__ __forceinline__ float gate_of(const PrefillArgs& a, int b, int row, int h, int c) {
+  if (a.gates32 != nullptr) return a.gates32[((static_cast<int64_t>(b) * a.Lq + row) * a.Hq + h) * 3 + c];
+  const typename T::storage* GT = static_cast<const typename T::storage*>(a.gates);
+  return to_f32<T>(GT[b * a.gs[0] + static_cast<int64_t>(row) * a.gs[1] + h * a.gs[2] + c]);
+}
+
+// Element j (0..7) of a fragment.
+template <class T>
+__device__ __forceinline__ float frag_elem(const Frag<T>& f, int j);
+template <>
+__device__ __forceinline__ float frag_elem<BF16>(const Frag<BF16>& f, int j) {
+  const uint32_t w = f.v[j >> 1];
+  return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+template <>
+__device__ __forceinline__ float frag_elem<F32>(const Frag<F32>& f, int j) {
+  return j < 4 ? f.lo[j] : f.hi[j - 4];
+}
+
 // ------------------------------------------------------------------ k_prep
 
 template <class T, int D>
@@ -146,7 +175,7 @@ __global__ __launch_bounds__(256) void k_prep(PrefillArgs a) {
       frag_store<T>(vt + f * 8, frag_load<T>(tmp));
     }
   }
-  if (j < a.NcT * 64) {
+  if (a.cmp_in_prep && j < a.NcT * 64) {
     const int c = j >> 6, r = j & 63;
     const int64_t tile = (static_cast<int64_t>(b * a.G + g) * a.NcT + c) * (64 * D);
     S* kc = static_cast<S*>(a.kct) + tile;
@@ -167,6 +196,152 @@ __global__ __launch_bounds__(256) void k_prep(PrefillArgs a) {
       if (kSplitKc<T>) kcl[ktile_off(r, d, D)] = from_f32<T>(sk - to_f32<T>(hi));
       vc[vtile_off(r, d)] = from_f32<T>(sv);
     }
+  }
+}
+
+// ------------------------------------------------------------------ k_ctile
+
+// Compressed tiles for the general geometry: compressed block i of (b, g)
+// summarises tokens [i*cd, i*cd + cl) -- their mean, or the learned linear map
+// w[o][p][c] of the flattened block plus bias[o] (each block compressed into
+// one representation by a learned projection: NSA factory write-up,
+// chencunli.com, section "What dynamic sparsity actually sparsifies").
+// Workgroup (x, g, b): 64 compressed blocks, of K for even x and of V for odd
+// x. The learned map is a [64 x cl*D] by [cl*D x D] product on MFMA: wave w
+// takes rows 16w..16w+15 and all D outputs, the reduction running over
+// (position, input dim) in steps of 32. Rows past Nc are written as zeros.
+template <class T, int D>
+__global__ __launch_bounds__(256) void k_ctile(PrefillArgs a) {
+  using S = typename T::storage;
+  const int c = blockIdx.x >> 1, is_v = blockIdx.x & 1, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int Lb = __builtin_amdgcn_readfirstlane(seq_span(a, b).L);  // key rows past it read as zero
+  const S* X = static_cast<const S*>(is_v ? a.v : a.k) + b * (is_v ? a.vs[0] : a.ks[0]) +
+               g * (is_v ? a.vs[2] : a.ks[2]);
+  const int64_t xs = is_v ? a.vs[1] : a.ks[1];
+  const int64_t tile = (static_cast<int64_t>(b * a.G + g) * a.NcT + c) * (64 * D);
+  S* hi_t = static_cast<S*>(is_v ? a.vct : a.kct) + tile;
+  S* lo_t = (kSplitKc<T> && !is_v) ? static_cast<S*>(a.kclt) + tile : nullptr;
+  auto put = [&](int r, int d, float x) {
+    if (is_v) {
+      hi_t[vtile_off(r, d)] = from_f32<T>(x);
+    } else {
+      const S h = from_f32<T>(x);
+      hi_t[ktile_off(r, d, D)] = h;
+      if (kSplitKc<T>) lo_t[ktile_off(r, d, D)] = from_f32<T>(x - to_f32<T>(h));
+    }
+  };
+  const void* wp = is_v ? a.wv : a.wk;
+  if (wp == nullptr) {
+    for (int e = tid; e < 64 * D; e += 256) {
+      const int r = e / D, d = e % D, i = 64 * c + r;
+      float sum = 0.f;
+      if (i < a.Nc) {
+        const int t0 = i * a.cd, t1 = min(t0 + a.cl, Lb);
+        for (int t = t0; t < t1; ++t) sum += to_f32<T>(X[static_cast<int64_t>(t) * xs + d]);
+        sum *= a.inv_cl;
+      }
+      put(r, d, sum);
+    }
+    return;
+  }
+  const S* W = static_cast<const S*>(wp);
+  const S* bias = static_cast<const S*>(is_v ? a.bv : a.bk);
+  constexpr int DT = D / 16, KS = D / 32;
+  const int i = 64 * c + 16 * wave + (lane & 15);  // this lane's row of the A operand
+  const bool row_ok = i < a.Nc;
+  const int t0 = i * a.cd;
+  f32x4 acc[DT];
+#pragma unroll
+  for (int nt = 0; nt < DT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < a.cl; ++p) {
+    const int t = t0 + p;
+    const bool tok = row_ok && t < Lb;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c0 = 32 * ks + 8 * (lane >> 4);
+      const Frag<T> af = tok ? frag_load<T>(X + static_cast<int64_t>(t) * xs + c0) : frag_zero<T>();
+#pragma unroll
+      for (int nt = 0; nt < DT; ++nt) {
+        const int o = 16 * nt + (lane & 15);
+        mma(acc[nt], af, frag_load<T>(W + (static_cast<int64_t>(o) * a.cl + p) * D + c0));
+      }
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < DT; ++nt) {
+    const int o = 16 * nt + (lane & 15);
+    const float bo = to_f32<T>(bias[o]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 16 * wave + 4 * (lane >> 4) + k;
+      put(r, o, 64 * c + r < a.Nc ? acc[nt][k] + bo : 0.f);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ k_gate
+
+// Gate layer: gates32[b][row][h][c] = sigmoid(q[b][row][h] . gate_w[h][:, c] +
+// gate_b[h][c]) in fp32, one thread per (b, row, head). The gates of the
+// three branches are learned (NSA how-to, qwbw.cn/news/106443, section 3,
+// gate_type learned); here a one-layer map of the head's query.
+template <class T, int D>
+__global__ __launch_bounds__(256) void k_gate(PrefillArgs a) {
+  using S = typename T::storage;
+  const S* W = static_cast<const S*>(a.gate_w);
+  const S* Bg = static_cast<const S*>(a.gate_b);
+  const int64_t n = static_cast<int64_t>(a.B) * a.Lq * a.Hq;
+  for (int64_t e = blockIdx.x * static_cast<int64_t>(256) + threadIdx.x; e < n;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    const int h = static_cast<int>(e % a.Hq);
+    const int64_t br = e / a.Hq;
+    const int row = static_cast<int>(br % a.Lq), b = static_cast<int>(br / a.Lq);
+    const S* q = static_cast<const S*>(a.q) + b * a.qs[0] + static_cast<int64_t>(row) * a.qs[1] + h * a.qs[2];
+    const S* w = W + static_cast<int64_t>(h) * D * 3;
+    float z0 = to_f32<T>(Bg[3 * h]), z1 = to_f32<T>(Bg[3 * h + 1]), z2 = to_f32<T>(Bg[3 * h + 2]);
+    for (int d0 = 0; d0 < D; d0 += 8) {
+      const Frag<T> f = frag_load<T>(q + d0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = frag_elem<T>(f, j);
+        const S* wr = w + 3 * (d0 + j);
+        z0 = fmaf(x, to_f32<T>(wr[0]), z0);
+        z1 = fmaf(x, to_f32<T>(wr[1]), z1);
+        z2 = fmaf(x, to_f32<T>(wr[2]), z2);
+      }
+    }
+    float* o = a.gates32 + e * 3;
+    o[0] = 1.0f / (1.0f + fast_exp2(-z0 * kLog2e));
+    o[1] = 1.0f / (1.0f + fast_exp2(-z1 * kLog2e));
+    o[2] = 1.0f / (1.0f + fast_exp2(-z2 * kLog2e));
+  }
+}
+
+// Selection-block scores from the compressed-block scores of one token, in
+// place (sc[0 .. own) on return): the compressed-attention mass on each
+// selection block's tokens, every compressed block's probability spread evenly
+// over its cl tokens. Selection block j reads compressed blocks i >= j only
+// (cl <= ls, cd <= cl), so rounds of 64 blocks can overwrite the scores they
+// have consumed. Whole wave, uniform arguments.
+__device__ inline void map_selection_scores(const PrefillArgs& a, float* sc, int own, int nv, int lane) {
+  for (int r0 = 0; r0 < own; r0 += 64) {
+    const int j = r0 + lane;
+    float sum = 0.f;
+    if (j < own) {
+      const int lo = j * a.ls, hi = lo + a.ls;
+      const int x = lo - a.cl + 1;
+      const int i0 = x <= 0 ? 0 : (x + a.cd - 1) / a.cd;
+      const int i1 = min(nv - 1, (hi - 1) / a.cd);
+      for (int i = i0; i <= i1; ++i) {
+        const int blo = i * a.cd;
+        sum = fmaf(sc[i], static_cast<float>(min(blo + a.cl, hi) - max(blo, lo)), sum);
+      }
+      sum *= a.inv_cl;
+    }
+    wave_lds_sync();
+    if (j < own) sc[j] = sum;
+    wave_lds_sync();
   }
 }
 
@@ -242,7 +417,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t bgoff = static_cast<int64_t>(b * a.G + g);
 
   const S* Q = static_cast<const S*>(a.q) + b * a.qs[0] + h * a.qs[2] + 8 * grp;
-  const S* GT = static_cast<const S*>(a.gates) + b * a.gs[0] + h * a.gs[2];
   Frag<T> qf[TPW][KS];
   float gcmp[TPW], gwin[TPW];
   int nvis[TPW];
@@ -253,9 +427,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       qf[qt][s] = valid ? frag_load<T>(Q + static_cast<int64_t>(t - t0q) * a.qs[1] + 32 * s) : frag_zero<T>();
-    gcmp[qt] = valid ? to_f32<T>(GT[static_cast<int64_t>(t - t0q) * a.gs[1]]) : 0.f;
-    gwin[qt] = valid ? to_f32<T>(GT[static_cast<int64_t>(t - t0q) * a.gs[1] + 2]) : 0.f;
-    nvis[qt] = t < Le ? (t + 1) >> 6 : 0;
+    gcmp[qt] = valid ? gate_of<T>(a, b, t - t0q, h, 0) : 0.f;
+    gwin[qt] = valid ? gate_of<T>(a, b, t - t0q, h, 2) : 0.f;
+    nvis[qt] = t < Le ? nvis_of(a, t) : 0;
   }
   f32x4 oacc[TPW][DT];
 #pragma unroll
@@ -346,7 +520,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   // ---- compressed branch
-  const int nch = (((Tl + 1) >> 6) + 63) >> 6;
+  const int nch = (nvis_of(a, Tl) + 63) >> 6;
   const S* KC = static_cast<const S*>(a.kct) + bgoff * a.NcT * TILE;
   const S* KCL = kSplitKc<T> ? static_cast<const S*>(a.kclt) + bgoff * a.NcT * TILE : nullptr;
   const S* VC = static_cast<const S*>(a.vct) + bgoff * a.NcT * TILE;
@@ -509,8 +683,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (; c < nfull; ++c) step2(std::integral_constant<bool, true>{}, c);
   for (; c < nch; ++c) step2(std::integral_constant<bool, false>{}, c);
 
-  // ---- gate_win * O_win + gate_cmp * O_cmp -> out (k_sel adds the selected branch)
-  {
+  // ---- gate_win * O_win + gate_cmp * O_cmp -> out (fp32 output) or the fp32
+  // partial rows (bf16 output); k_sel adds the selected branch, so a bf16
+  // output is rounded once, from the fp32 sum of all three branches
+  if constexpr (std::is_same<O, BF16>::value) {
+    float* P = a.part + (static_cast<int64_t>(b) * a.Lq * a.Hq + h) * D + 4 * grp;
+#pragma unroll
+    for (int qt = 0; qt < TPW; ++qt) {
+      const int t = tw + qt;
+      if (t < Le && colv) {
+        float* o = P + static_cast<int64_t>(t - t0q) * a.Hq * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = oacc[qt][dt];
+      }
+    }
+  } else {
     SO* OUT = static_cast<SO*>(a.out) + b * a.os[0] + h * a.os[2] + 4 * grp;
 #pragma unroll
     for (int qt = 0; qt < TPW; ++qt) {
@@ -533,7 +720,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int t = tw + qt;
       if (t >= Le) break;
       int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.Lq + (t - t0q)) * a.G + g) * a.n;
-      topk_wave(sc + qt * NcPad, t >> 6, a.n, row, surv, selb, lane);
+      const int own = t / a.ls;
+      if (a.sel_map) map_selection_scores(a, sc + qt * NcPad, own, nvis[qt], lane);
+      topk_wave(sc + qt * NcPad, own, a.n, row, surv, selb, lane);
     }
   }
 }
@@ -648,7 +837,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---- query fragments -> LDS; the wave's half blocks -> bitmap -> step list
   const int tl = min(t0 + TPW - 1, Le - 1);
-  const int nwords = (2 * ((tl >> 6) + 1) + 3) >> 2;  // half blocks 0 .. 2 own(tl) + 1
+  const int nwords = ((tl >> 5) + 4) >> 2;  // half blocks 0 .. tl / 32
   for (int w = lane; w < nwords; w += 64) bm[w] = 0u;
 #pragma unroll
   for (int qt = 0; qt < TPW; ++qt) {
@@ -668,13 +857,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int qt = 0; qt < TPW; ++qt) {
     const int t = t0 + qt;
     if (t >= Le) break;
-    const int own = t >> 6;
+    const int own = t / a.ls;
     const int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.Lq + (t - t0q)) * a.G + g) * n;
     const int j = lane < n ? row[lane] : -1;
     if (j >= 0 && j <= own) {  // padding / unusable injected entries drop out
+      // the selection block's half blocks that start at or before t
       const uint32_t bit = 1u << qt;
-      atomicOr(&bm[j >> 1], bit << (16 * (j & 1)));
-      if (64 * j + 32 <= t) atomicOr(&bm[j >> 1], bit << (16 * (j & 1) + 8));
+      const int hpb = a.ls >> 5, hb0 = j * hpb, hb1 = min(hb0 + hpb, (t >> 5) + 1);
+      for (int hb = hb0; hb < hb1; ++hb) atomicOr(&bm[hb >> 2], bit << (8 * (hb & 3)));
     }
   }
   wave_lds_sync();
@@ -763,19 +953,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
-  const S* GT = static_cast<const S*>(a.gates) + b * a.gs[0] + h * a.gs[2];
   SO* OUT = static_cast<SO*>(a.out) + b * a.os[0] + h * a.os[2] + 4 * grp;
 #pragma unroll
   for (int qt = 0; qt < TPW; ++qt) {
     const int t = t0 + qt;
     const float lt = col_sum4(l[qt]);
     if (t < Le && colv) {
-      const float gsl = to_f32<T>(GT[static_cast<int64_t>(t - t0q) * a.gs[1] + 1]);
+      const float gsl = gate_of<T>(a, b, t - t0q, h, 1);
       const float f = lt > 0.f ? gsl / lt : 0.f;
       SO* o = OUT + static_cast<int64_t>(t - t0q) * a.os[1];
+      // the window + compressed part: fp32 partial rows for a bf16 output, out itself for fp32
+      const float* pp = std::is_same<O, BF16>::value
+                            ? a.part + ((static_cast<int64_t>(b) * a.Lq + (t - t0q)) * a.Hq + h) * D + 4 * grp
+                            : nullptr;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const f32x4 prev = load4<O>(o + 16 * dt);
+        const f32x4 prev = std::is_same<O, BF16>::value ? *reinterpret_cast<const f32x4*>(pp + 16 * dt)
+                                                        : load4<O>(o + 16 * dt);
         store4<O>(o + 16 * dt, prev + acc[qt][dt] * f);
       }
       if (SAVE) {  // the branch's own output and log-sum-exp, kept for the backward pass
@@ -809,56 +1003,67 @@ static hipError_t record(hipEvent_t* ev, int i, hipStream_t st) {
   return ev != nullptr ? hipEventRecord(ev[i], st) : hipSuccess;
 }
 
-template <class T, class O, int D, int NW, bool LOL>
-static hipError_t launch_cmpwin(const PrefillArgs& a, hipStream_t st) {
-  const size_t lds = cmpwin_lds_bytes(NW, a.NcT, D, sizeof(typename T::storage) == 2, LOL);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cmpwin<T, O, D, NW, LOL>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_cmpwin<T, O, D, NW, LOL>), dim3(a.B * a.G * a.cmp_tiles), dim3(64 * NW), lds, st, a);
-  return hipSuccess;
+template <class T, class O, int D>
+static const void* cmpwin_kernel(const PrefillArgs& a) {
+  if (a.cmp_waves == 8)
+    return a.cmp_lo_lds ? reinterpret_cast<const void*>(&k_cmpwin<T, O, D, 8, true>)
+                        : reinterpret_cast<const void*>(&k_cmpwin<T, O, D, 8, false>);
+  if (a.cmp_waves == 4) return reinterpret_cast<const void*>(&k_cmpwin<T, O, D, 4, false>);
+  if (a.cmp_waves == 2) return reinterpret_cast<const void*>(&k_cmpwin<T, O, D, 2, false>);
+  return reinterpret_cast<const void*>(&k_cmpwin<T, O, D, 1, false>);
+}
+
+static hipError_t launch_one(const void* fn, dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                             const PrefillArgs& a) {
+  void* args[] = {const_cast<PrefillArgs*>(&a)};
+  return hipLaunchKernel(fn, grid, block, args, lds, st);
 }
 
 template <class T, class O, int D>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st, hipEvent_t* ev) {
+  constexpr bool kBf16 = sizeof(typename T::storage) == 2;
+  // every kernel attribute is set before the first launch
+  const void* cmp_fn = cmpwin_kernel<T, O, D>(a);
+  const size_t cmp_lds = cmpwin_lds_bytes(a.cmp_waves, a.NcT, D, kBf16, a.cmp_lo_lds != 0);
+  const void* sel_fn = a.save_o != nullptr ? reinterpret_cast<const void*>(&k_sel<T, O, D, true>)
+                                           : reinterpret_cast<const void*>(&k_sel<T, O, D, false>);
+  // Static + dynamic LDS above half a CU's caps residency at one workgroup
+  // (4 waves) per CU, which was measured faster (~13 % at 64k) than two: the
+  // gathers then contend less for L2.
+  const size_t sel_lds = sel_lds_bytes(a.Nb, D, kBf16);
   hipError_t e;
-  const int nblk_prep = max(a.Nb, a.NcT * 64);
-  if ((e = record(ev, 0, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_prep<T, D>), dim3(nblk_prep, a.G, a.B), dim3(256), 0, st, a);
-  if ((e = record(ev, 1, st)) != hipSuccess) return e;
-  if (a.cmp_waves == 8) {
-    if (a.cmp_lo_lds) e = launch_cmpwin<T, O, D, 8, true>(a, st);
-    else e = launch_cmpwin<T, O, D, 8, false>(a, st);
-  } else if (a.cmp_waves == 4) {
-    e = launch_cmpwin<T, O, D, 4, false>(a, st);
-  } else if (a.cmp_waves == 2) {
-    e = launch_cmpwin<T, O, D, 2, false>(a, st);
-  } else {
-    e = launch_cmpwin<T, O, D, 1, false>(a, st);
-  }
-  if (e != hipSuccess) return e;
-  if ((e = record(ev, 2, st)) != hipSuccess) return e;
+  if ((e = hipFuncSetAttribute(cmp_fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(cmp_lds))) !=
+          hipSuccess ||
+      (e = hipFuncSetAttribute(sel_fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sel_lds))) !=
+          hipSuccess)
+    return e;
   // workgroups per XCD (see the item mapping in k_sel)
   int per = a.sel_interleave ? a.B * ((a.sel_tiles + 8 / a.G - 1) / (8 / a.G)) : (a.B * a.G * a.sel_tiles + 7) / 8;
   if (!a.sel_interleave && a.sel_bounds[0] >= 0) {
     per = 0;
     for (int k = 0; k < 8 / a.G; ++k) per = max(per, a.sel_bounds[k + 1] - a.sel_bounds[k]);
   }
-  // Static + dynamic LDS above half a CU's caps residency at one workgroup
-  // (4 waves) per CU, which was measured faster (~13 % at 64k) than two: the
-  // gathers then contend less for L2.
-  const size_t sel_lds = sel_lds_bytes(a.Nb, D, sizeof(typename T::storage) == 2);
-  if (a.save_o != nullptr) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sel<T, O, D, true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sel_lds));
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_sel<T, O, D, true>), dim3(per * 8), dim3(256), sel_lds, st, a);
-  } else {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sel<T, O, D, false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sel_lds));
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_sel<T, O, D, false>), dim3(per * 8), dim3(256), sel_lds, st, a);
+  const int nblk_prep = a.cmp_in_prep ? max(a.Nb, a.NcT * 64) : a.Nb;
+  if ((e = record(ev, 0, st)) != hipSuccess) return e;
+  if (a.gate_w != nullptr) {
+    const int64_t rows = static_cast<int64_t>(a.B) * a.Lq * a.Hq;
+    const unsigned grid = static_cast<unsigned>(std::min<int64_t>((rows + 255) / 256, 65536));
+    if ((e = launch_one(reinterpret_cast<const void*>(&k_gate<T, D>), dim3(grid), dim3(256), 0, st, a)) !=
+        hipSuccess)
+      return e;
   }
+  if ((e = launch_one(reinterpret_cast<const void*>(&k_prep<T, D>), dim3(nblk_prep, a.G, a.B), dim3(256), 0, st,
+                      a)) != hipSuccess)
+    return e;
+  if (!a.cmp_in_prep && a.NcT > 0 &&
+      (e = launch_one(reinterpret_cast<const void*>(&k_ctile<T, D>), dim3(2 * a.NcT, a.G, a.B), dim3(256), 0, st,
+                      a)) != hipSuccess)
+    return e;
+  if ((e = record(ev, 1, st)) != hipSuccess) return e;
+  if ((e = launch_one(cmp_fn, dim3(a.B * a.G * a.cmp_tiles), dim3(64 * a.cmp_waves), cmp_lds, st, a)) != hipSuccess)
+    return e;
+  if ((e = record(ev, 2, st)) != hipSuccess) return e;
+  if ((e = launch_one(sel_fn, dim3(per * 8), dim3(256), sel_lds, st, a)) != hipSuccess) return e;
   if ((e = record(ev, 3, st)) != hipSuccess) return e;
   return hipGetLastError();
 }

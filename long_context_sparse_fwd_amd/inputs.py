@@ -18,6 +18,13 @@ Recipe (stated once, used everywhere):
   bit patterns); fp32 values are the draw itself.
 * Gates are ``sigmoid(logit)`` evaluated in float64, rounded to float32
   (nearest-even) and then, for bf16 workloads, to bf16 (nearest-even).
+* Synthetic weights of the general geometry (no trained weights exist): the
+  learned compressor ``wk``/``wv`` [D, block, D] is N(0,1) / (block *
+  sqrt(D)) (so a compressed key has the spread of a block mean, 1/sqrt(block)
+  per dimension) and ``bk``/``bv`` [D] is 0.1 N(0,1); the gate layer
+  ``gate_w`` [Hq, D, 3] is N(0,1) / sqrt(D) and ``gate_b`` [Hq, 3] is N(0,1).
+  Each tensor is one keyed draw ``(seed, tensor_id)``, ids 10..15, scaled in
+  float32 and stored like the other inputs.
 * Decode sequence ``b`` with length ``s`` is the prefill-shaped batch row ``b``
   read at position ``s - 1``: its query is row ``(s-1) % 64`` of Q chunk
   ``(0, b, (s-1)//64)``, its gates the same row of chunk ``(3, b, ...)``, and its
@@ -39,6 +46,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 TID_Q, TID_K, TID_V, TID_GATE, TID_DOUT = 0, 1, 2, 3, 4
+# synthetic weights of the general geometry (one draw per tensor, not chunked)
+TID_WK, TID_BK, TID_WV, TID_BV, TID_GW, TID_GB = 10, 11, 12, 13, 14, 15
 CHUNK = 64
 
 
@@ -199,6 +208,29 @@ def make_dout(cfg: PrefillConfig, dtype: str | None = None) -> np.ndarray:
             t0, t1 = blk * CHUNK, min(L, (blk + 1) * CHUNK)
             out[b, t0:t1] = encode(chunk_normal(cfg.seed, TID_DOUT, b, blk, (CHUNK, Hq, D))[: t1 - t0], dt)
     return out
+
+
+def _weight(seed: int, tensor_id: int, shape, scale: float, dtype: str) -> np.ndarray:
+    ss = np.random.SeedSequence([seed, tensor_id])
+    x = np.random.Generator(np.random.PCG64(ss)).standard_normal(shape, dtype=np.float32)
+    return encode(x * np.float32(scale), dtype)
+
+
+def make_compressor_weights(cfg: PrefillConfig, block: int) -> dict:
+    """Synthetic learned compressor: wk, wv [D, block, D]; bk, bv [D] (stored form)."""
+    D = cfg.head_dim
+    ws = 1.0 / (block * np.sqrt(D))
+    return {"wk": _weight(cfg.seed, TID_WK, (D, block, D), ws, cfg.dtype),
+            "bk": _weight(cfg.seed, TID_BK, (D,), 0.1, cfg.dtype),
+            "wv": _weight(cfg.seed, TID_WV, (D, block, D), ws, cfg.dtype),
+            "bv": _weight(cfg.seed, TID_BV, (D,), 0.1, cfg.dtype)}
+
+
+def make_gate_weights(cfg: PrefillConfig) -> dict:
+    """Synthetic gate layer: gate_w [Hq, D, 3], gate_b [Hq, 3] (stored form)."""
+    Hq, D = cfg.n_q_heads, cfg.head_dim
+    return {"gate_w": _weight(cfg.seed, TID_GW, (Hq, D, 3), 1.0 / np.sqrt(D), cfg.dtype),
+            "gate_b": _weight(cfg.seed, TID_GB, (Hq, 3), 1.0, cfg.dtype)}
 
 
 def make_selection(cfg: PrefillConfig, share: int = 8) -> np.ndarray:

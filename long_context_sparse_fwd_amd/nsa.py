@@ -46,6 +46,11 @@ class DecodeDesc(ctypes.Structure):
                 ("o_stride", c_i64 * 2)]
 
 
+class NsaGeneral(ctypes.Structure):
+    _fields_ = [("compress_stride", c_i32), ("wk", c_vp), ("bk", c_vp), ("wv", c_vp), ("bv", c_vp),
+                ("gate_w", c_vp), ("gate_b", c_vp)]
+
+
 class NsaError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(message)
@@ -77,6 +82,12 @@ def lib() -> ctypes.CDLL:
     L.nsa_fwd_prefill.restype = ctypes.c_int
     L.nsa_fwd_prefill.argtypes = [P(PrefillDesc), P(NsaParams), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                   ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
+    L.nsa_prefill_general_workspace_bytes.restype = ctypes.c_int
+    L.nsa_prefill_general_workspace_bytes.argtypes = [P(PrefillDesc), P(NsaParams), P(NsaGeneral),
+                                                      P(ctypes.c_size_t)]
+    L.nsa_fwd_prefill_general.restype = ctypes.c_int
+    L.nsa_fwd_prefill_general.argtypes = [P(PrefillDesc), P(NsaParams), P(NsaGeneral), c_vp, c_vp, c_vp, c_vp,
+                                          c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
     L.nsa_fwd_prefill_chunk.restype = ctypes.c_int
     L.nsa_fwd_prefill_chunk.argtypes = [P(PrefillDesc), P(NsaParams), c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
                                         c_vp, ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
@@ -199,6 +210,69 @@ def prefill(q, k, v, gates, *, top_k: int, window: int, block: int = 64, select_
                              _ptr(gates), _ptr(out), _ptr(idx),
                              NSA_IDX_INJECT if inject else NSA_IDX_COMPUTE, _ptr(workspace),
                              workspace.numel(), _stream_of(q)))
+    if idx is not None:
+        return out, idx
+    return out
+
+
+def make_general(stride: int, compressor=None, gate_layer=None) -> NsaGeneral:
+    """compressor: (wk, bk, wv, bv) device tensors or None; gate_layer:
+    (gate_w, gate_b) or None. The tensors must outlive the call."""
+    g = NsaGeneral()
+    g.compress_stride = stride
+    if compressor is not None:
+        for name, t in zip(("wk", "bk", "wv", "bv"), compressor):
+            if not (t.is_cuda and t.is_contiguous()):
+                raise ValueError("compressor weights must be contiguous device tensors")
+            setattr(g, name, t.data_ptr())
+    if gate_layer is not None:
+        for name, t in zip(("gate_w", "gate_b"), gate_layer):
+            if not (t.is_cuda and t.is_contiguous()):
+                raise ValueError("gate layer weights must be contiguous device tensors")
+            setattr(g, name, t.data_ptr())
+    return g
+
+
+def prefill_general(q, k, v, gates, *, top_k: int, window: int, block: int = 64, select_block=None,
+                    stride=None, compressor=None, gate_layer=None, scale: float = 0.0, out=None, out_dtype=None,
+                    idx=None, inject: bool = False, return_idx: bool = False, workspace=None):
+    """NSA prefill with the general geometry (nsa_fwd_prefill_general):
+    compression stride, selection blocks of select_block tokens, a learned
+    compressor (wk [D,block,D], bk [D], wv, bv) and a gate layer (gate_w
+    [Hq,D,3], gate_b [Hq,3]); with a gate layer, gates may be None."""
+    tensors = [q, k, v] + ([gates] if gates is not None else [])
+    _require_gpu(*tensors)
+    B, L, Hq, D = q.shape
+    G = k.shape[2]
+    if k.shape != (B, L, G, D) or v.shape != k.shape or (gates is not None and gates.shape != (B, L, Hq, 3)):
+        raise ValueError("shape mismatch among q, k, v, gates")
+    if gates is None and gate_layer is None:
+        raise ValueError("gates are needed unless a gate layer computes them")
+    for t in tensors + list(compressor or ()) + list(gate_layer or ()):
+        if t.dtype != q.dtype:
+            raise TypeError("inputs and weights must share one dtype")
+    if out is None:
+        out = torch.empty((B, L, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if inject and idx is None:
+        raise ValueError("inject=True needs idx")
+    if idx is None and return_idx:
+        idx = torch.empty((B, L, G, top_k), dtype=torch.int32, device=q.device)
+    if idx is not None and (idx.dtype != torch.int32 or not idx.is_contiguous()
+                            or tuple(idx.shape) != (B, L, G, top_k)):
+        raise ValueError("idx must be a contiguous int32 [B, L, G, top_k] tensor")
+    desc = prefill_desc(q, k, v, gates if gates is not None else q[..., :3], out)
+    params = make_params(top_k, window, block, select_block, scale)
+    gen = make_general(block if stride is None else stride, compressor, gate_layer)
+    L_ = lib()
+    nbytes = ctypes.c_size_t()
+    check(L_.nsa_prefill_general_workspace_bytes(ctypes.byref(desc), ctypes.byref(params), ctypes.byref(gen),
+                                                 ctypes.byref(nbytes)))
+    if workspace is None or workspace.numel() < nbytes.value:
+        workspace = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=q.device)
+    check(L_.nsa_fwd_prefill_general(ctypes.byref(desc), ctypes.byref(params), ctypes.byref(gen), _ptr(q), _ptr(k),
+                                     _ptr(v), _ptr(gates), _ptr(out), _ptr(idx),
+                                     NSA_IDX_INJECT if inject else NSA_IDX_COMPUTE, _ptr(workspace),
+                                     workspace.numel(), _stream_of(q)))
     if idx is not None:
         return out, idx
     return out

@@ -31,7 +31,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .nsa_ref import compress, _check_blocks
+from .nsa_ref import compress
 
 
 def _attend_backward(qg, keys, vals, dout_g, gate, scale):
@@ -64,7 +64,8 @@ def prefill_backward(q, k, v, gates, dout, idx, *, block: int = 64, select_block
     those rows only, and dk / dv hold the sums over those rows' terms, which is
     the whole gradient for keys seen by no other row.
     """
-    _check_blocks(block, select_block)
+    if select_block is not None and select_block != block:
+        raise NotImplementedError("the backward oracle covers selection blocks equal to the compressed blocks")
     B, L, Hq, D = q.shape
     G = k.shape[2]
     Hg = Hq // G

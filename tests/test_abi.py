@@ -80,7 +80,12 @@ def test_prefill_workspace_size_is_the_sum_of_its_parts(L):
     tiles = 2 * 4 * 1024 * 64 * 128 * 2          # K and V tiles
     ctiles = 3 * 4 * 16 * 64 * 128 * 2           # block-mean tiles (K high, K low, V)
     idx = 65536 * 4 * 16 * 4
-    assert n == tiles + ctiles + idx
+    part = 65536 * 64 * 128 * 4                  # fp32 window + compressed rows (bf16 output)
+    assert n == tiles + ctiles + idx + part
+    d = pdesc()
+    d.out_dtype = nsa.NSA_F32                    # an fp32 output holds that part itself
+    st, n32 = ws_prefill(L, d, nsa.make_params(16, 512))
+    assert st == OK and n32 == tiles + ctiles + idx
 
 
 @pytest.mark.parametrize("mut,code", [
@@ -93,8 +98,9 @@ def test_prefill_workspace_size_is_the_sum_of_its_parts(L):
     (lambda d, p: setattr(d, "in_dtype", nsa.NSA_F32), UNS),  # f32 in, bf16 out
     (lambda d, p: d.q_stride.__setitem__(1, 8 * 1000 + 4), INV),
     (lambda d, p: d.k_stride.__setitem__(0, -8), INV),
-    (lambda d, p: setattr(p, "compress_block_size", 32), UNS),
-    (lambda d, p: setattr(p, "select_block_size", 128), UNS),
+    (lambda d, p: setattr(p, "compress_block_size", 128), UNS),     # above the selection block
+    (lambda d, p: setattr(p, "select_block_size", 48), UNS),        # not a multiple of 32
+    (lambda d, p: (setattr(p, "select_block_size", 128), setattr(p, "select_top_k", 33)), UNS),  # > 4096 tokens
     (lambda d, p: setattr(p, "select_block_size", 0), INV),
     (lambda d, p: setattr(p, "select_top_k", 0), INV),
     (lambda d, p: setattr(p, "select_top_k", 65), UNS),
@@ -110,6 +116,53 @@ def test_prefill_validation(L, mut, code):
                            FAKE, 1 << 40, None)
     assert st == code
     assert L.nsa_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("block,select_block,top_k", [(32, 64, 16), (64, 128, 16), (16, 32, 64), (64, 256, 16)])
+def test_prefill_accepts_general_block_sizes(L, block, select_block, top_k):
+    d, p = pdesc(Lq=4096), nsa.make_params(top_k, 512, block=block, select_block=select_block)
+    st, n = ws_prefill(L, d, p)
+    assert st == OK, L.nsa_last_error()
+    # the compressed tiles follow the number of compressed blocks
+    _, n64 = ws_prefill(L, d, nsa.make_params(top_k, 512))
+    assert (n > n64) == (block < 64)
+
+
+def test_general_entry_checks(L):
+    d, p = pdesc(Lq=4096), nsa.make_params(16, 512, block=32, select_block=64)
+    n = ctypes.c_size_t()
+    ws = lambda g: L.nsa_prefill_general_workspace_bytes(ctypes.byref(d), ctypes.byref(p), g, ctypes.byref(n))
+    assert ws(None) == OK
+    plain = n.value
+    g = nsa.NsaGeneral()
+    g.compress_stride = 16
+    assert ws(ctypes.byref(g)) == OK
+    assert n.value > plain                       # twice the compressed blocks
+    for bad in (0, 33):                          # stride outside [1, compress_block_size]
+        g.compress_stride = bad
+        assert ws(ctypes.byref(g)) == INV
+    g.compress_stride = 32
+    g.wk = FAKE                                   # an incomplete compressor
+    assert ws(ctypes.byref(g)) == INV
+    g.bk, g.wv, g.bv = FAKE, FAKE, FAKE
+    assert ws(ctypes.byref(g)) == OK
+    g.wv = FAKE + 8                               # misaligned
+    assert ws(ctypes.byref(g)) == INV
+    g.wv = FAKE
+    g.gate_w = FAKE                               # gate layer without its bias
+    assert ws(ctypes.byref(g)) == INV
+    g.gate_b = FAKE
+    assert ws(ctypes.byref(g)) == OK
+    assert n.value == plain + 4096 * 64 * 3 * 4   # + the fp32 gates
+    # with a gate layer the gates argument may be NULL; the workspace must cover the gates
+    call = lambda gates, nb: L.nsa_fwd_prefill_general(ctypes.byref(d), ctypes.byref(p), ctypes.byref(g), FAKE,
+                                                       FAKE, FAKE, gates, FAKE, None, 0, FAKE, nb, None)
+    assert call(None, n.value - 1) == WS
+    g.gate_w = g.gate_b = None
+    assert call(None, n.value) == INV             # no gate layer: gates are required
+    # the selected branch is kept for the backward only in the plain geometry
+    assert L.nsa_fwd_prefill_save(ctypes.byref(d), ctypes.byref(p), *([FAKE] * 5), None, 0, FAKE, FAKE, FAKE,
+                                  n.value, None) == UNS
 
 
 def test_prefill_pointer_and_workspace_checks(L):
@@ -215,6 +268,7 @@ def test_backward_validation_and_empty_problem(L):
     assert call(nb=need - 1) == WS
     assert call(desc=pdesc(Lq=4096, D=96)) == UNS
     assert call(params=nsa.make_params(16, 512, block=32)) == UNS
+    assert call(params=nsa.make_params(16, 512, select_block=128)) == UNS
     for empty in (pdesc(B=0), pdesc(Lq=0)):
         assert L.nsa_bwd_prefill(ctypes.byref(empty), ctypes.byref(p), None, None, None, None, None, None, None,
                                  None, None, None, None, 0, None) == OK
@@ -262,6 +316,9 @@ def test_decode_workspace_and_validation(L):
         assert call(d, ptrs) == INV, i
     assert call(d, good, nb=10) == WS
     assert call(ddesc(B=0), [None] * 8) == OK
+    # decode needs blocks of 64
+    for pb in (nsa.make_params(16, 512, block=32), nsa.make_params(16, 512, select_block=128)):
+        assert L.nsa_decode_workspace_bytes(ctypes.byref(d), ctypes.byref(pb), ctypes.byref(n)) == UNS
 
 
 def test_compress_validation(L):

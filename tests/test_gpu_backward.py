@@ -3,10 +3,14 @@
 Every gradient is compared element by element with the oracle on the same
 seeded inputs and the same selection (the oracle's own forward selection, or a
 seeded synthetic one: no oracle input comes from the GPU). The error measure
-is max |gpu - oracle| / max(max |oracle|, 1) per tensor, bounded by 2e-2 for bf16
-inputs (probabilities and score gradients enter the matrix products rounded to
-bf16, relative step 2^-8, and the sums run over thousands of terms) and 1e-4
-for fp32 inputs.
+is max |gpu - oracle| / max |oracle| per tensor (relative to the tensor's own
+largest gradient), bounded by 2e-2 for bf16 inputs (probabilities and score
+gradients enter the matrix products rounded to bf16, relative step 2^-8, and
+the sums run over thousands of terms) and 1e-4 for fp32 inputs. Where the
+exact gradient vanishes (a softmax over a single key has zero derivative, so
+dq and dk of a one-token sequence are 0), the GPU's value is a cancellation
+residue of products of the size of dout . o; it is bounded by the same
+tolerance times the largest |dout . o| (the gate gradient).
 
 At the 64k bench shape the oracle checks sampled query rows (dq, dgates), the
 keys of the last block (dk, dv: only the last 64 rows see them), and the
@@ -27,9 +31,24 @@ TOL = {"bf16": 2e-2, "f32": 1e-4}
 
 
 def _err(got, want):
-    # relative to the largest gradient, or to 1 where a gradient vanishes
-    # (a single key: every softmax derivative is 0 up to rounding)
-    return float(np.abs(got - want).max() / max(np.abs(want).max(), 1.0))
+    """Largest deviation relative to the tensor's largest gradient."""
+    return float(np.abs(got - want).max() / max(np.abs(want).max(), 1e-300))
+
+
+VANISH = 1e-12  # an oracle gradient this small is zero up to float64 rounding
+
+
+def _check_grads(tag, names, got, ref, dtype):
+    scale = float(np.abs(ref["dgates"]).max())   # |dout . o|: the size of the products
+    for nm, gv in zip(names, got):
+        want = ref[nm]
+        if np.abs(want).max() <= VANISH * max(scale, 1.0):
+            e = float(np.abs(gv).max()) / max(scale, 1e-300)
+            print(f"[bwd] {tag} {nm} vanishes: max |gpu| / max |dout . o| = {e:.2e}", flush=True)
+        else:
+            e = _err(gv, want)
+            print(f"[bwd] {tag} {nm} relative err {e:.2e}", flush=True)
+        assert e <= TOL[dtype], f"{tag} {nm} error {e}"
 
 
 def _run(cfg, raw, dout_raw, idx, out_dtype=None):
@@ -69,10 +88,7 @@ def test_backward_matches_oracle(case):
         idx = inputs.make_selection(cfg)
     ref = nsa_bwd_ref.prefill_backward(x["q"], x["k"], x["v"], x["gates"], dout, idx, top_k=n, window=w)
     got = _run(cfg, raw, dout_raw, idx)
-    for nm, gv in zip(("dq", "dk", "dv", "dgates"), got):
-        e = _err(gv, ref[nm])
-        print(f"[bwd] {name} {nm} err {e:.2e}", flush=True)
-        assert e <= TOL[dtype], f"{nm} error {e}"
+    _check_grads(name, ("dq", "dk", "dv", "dgates"), got, ref, dtype)
 
 
 EDGE = [
@@ -101,10 +117,7 @@ def test_backward_edge_cases(case):
     idx = nsa_ref.prefill(x["q"], x["k"], x["v"], x["gates"], top_k=n, window=w)["idx"]
     ref = nsa_bwd_ref.prefill_backward(x["q"], x["k"], x["v"], x["gates"], dout, idx, top_k=n, window=w)
     got = _run(cfg, raw, dout_raw, idx)
-    for nm, gv in zip(("dq", "dk", "dv", "dgates"), got):
-        e = _err(gv, ref[nm])
-        print(f"[bwd] {name} {nm} err {e:.2e}", flush=True)
-        assert e <= TOL[dtype], f"{nm} error {e}"
+    _check_grads(name, ("dq", "dk", "dv", "dgates"), got, ref, dtype)
 
 
 @pytest.mark.parametrize("case", [CASES[0], CASES[1]], ids=["f32", "bf16"])
@@ -142,10 +155,8 @@ def test_forward_save_and_saved_backward(case):
     grads = nsa.prefill_backward(q, k, v, g, _up(dout_raw, dtype), torch.from_numpy(orc["idx"]).cuda(), top_k=n,
                                  window=w, saved=(o_slc, lse_slc))
     torch.cuda.synchronize()
-    for nm, gt in zip(("dq", "dk", "dv", "dgates"), grads):
-        e = _err(gt.cpu().numpy().astype(np.float64), ref[nm])
-        print(f"[bwd saved] {name} {nm} err {e:.2e}", flush=True)
-        assert e <= TOL[dtype], f"{nm} error {e}"
+    _check_grads(f"saved {name}", ("dq", "dk", "dv", "dgates"),
+                 [gt.cpu().numpy().astype(np.float64) for gt in grads], ref, dtype)
 
 
 def test_backward_with_fp32_upstream_gradient_and_odd_selection():
@@ -164,10 +175,7 @@ def test_backward_with_fp32_upstream_gradient_and_odd_selection():
     ref = nsa_bwd_ref.prefill_backward(x["q"], x["k"], x["v"], x["gates"], inputs.to_f64(dout_raw, "f32"), idx,
                                        top_k=4, window=50)
     got = _run(cfg, raw, dout_raw, idx, out_dtype="f32")
-    for nm, gv in zip(("dq", "dk", "dv", "dgates"), got):
-        e = _err(gv, ref[nm])
-        print(f"[bwd] odd {nm} err {e:.2e}", flush=True)
-        assert e <= TOL["bf16"], f"{nm} error {e}"
+    _check_grads('odd', ("dq", "dk", "dv", "dgates"), got, ref, "bf16")
 
 
 def test_backward_at_64k_sampled_rows_last_block_and_value_sum():
