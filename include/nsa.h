@@ -295,6 +295,25 @@ nsa_status_t nsa_fwd_decode(const nsa_decode_desc_t* desc, const nsa_params_t* p
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nsa_fwd_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * no workspace argument; the scratch the decode kernel needs (the selection
+ * when idx is NULL, and the compressed logits when they do not fit in LDS) is
+ * a 40 MiB device array inside the library, one per GPU, held until the
+ * process ends (enough for 64 sequences x 4 KV heads of up to 131072 tokens
+ * in bf16). A call whose nsa_decode_workspace_bytes exceeds 40 MiB
+ * returns NSA_ERR_WORKSPACE_TOO_SMALL and launches nothing. Nothing in the
+ * scratch needs to start at zero and no call allocates. Every call on one GPU
+ * shares that GPU's scratch, so two calls that may run at the same time on
+ * one GPU (different streams, or one stream and graph replays) race: order
+ * them. Otherwise as nsa_fwd_decode, with the same results.
+ */
+nsa_status_t nsa_fwd_decode_noalloc(const nsa_decode_desc_t* desc, const nsa_params_t* params, const void* q,
+                                    const void* k_cache, const void* v_cache, const void* kc_cache,
+                                    const void* vc_cache, const int32_t* seqlens, const void* gates, void* out,
+                                    int32_t* idx, nsa_idx_mode_t idx_mode, void* stream);
+
+/*
  * Block compression, the step that turns each key/value block into one
  * compressed representation (NSA factory write-up, chencunli.com, "DeepSeek
  * NSA on the Siemens 840D manual", section "What dynamic sparsity actually

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "nsa.h"
@@ -832,6 +833,65 @@ static nsa_status_t decode_impl(const nsa_decode_desc_t* desc, const nsa_params_
                                     reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)));
   if (e != hipSuccess) return fail(NSA_ERR_HIP, "HIP error in decode launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ allocation-free decode
+
+// Scratch of nsa_fwd_decode_noalloc: a file-scope device array, so that the
+// call allocates nothing. Each GPU the library runs on holds its own copy
+// (at its own address) until the process ends. In host code the array's name
+// is only a stand-in; its device address is looked up per device with
+// hipGetSymbolAddress and that address is what the kernels receive.
+constexpr size_t kNoAllocScratchBytes = size_t{40} << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once looked up
+
+// The current device's address of `scratch` (looked up on its first use on
+// that device, with that device current).
+nsa_status_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(NSA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(NSA_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch table holds", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(NSA_ERR_HIP, "hipGetSymbolAddress of the decode scratch failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return NSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+nsa_status_t nsa_fwd_decode_noalloc(const nsa_decode_desc_t* desc, const nsa_params_t* params, const void* q,
+                                    const void* k_cache, const void* v_cache, const void* kc_cache,
+                                    const void* vc_cache, const int32_t* seqlens, const void* gates, void* out,
+                                    int32_t* idx, nsa_idx_mode_t idx_mode, void* stream) {
+  DecodePlan pl;
+  NSA_TRY(plan_decode(desc, params, &pl));
+  if (pl.total > kNoAllocScratchBytes)
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL,
+                "this decode needs %zu bytes of scratch; the allocation-free decode holds %zu "
+                "(use nsa_fwd_decode with a workspace)", pl.total, kNoAllocScratchBytes);
+  if (desc->batch == 0)
+    return decode_impl(desc, params, q, k_cache, v_cache, kc_cache, vc_cache, seqlens, gates, out, idx, idx_mode,
+                       nullptr, 0, stream, nullptr);
+  void* ws = nullptr;
+  NSA_TRY(noalloc_scratch(&ws));
+  return decode_impl(desc, params, q, k_cache, v_cache, kc_cache, vc_cache, seqlens, gates, out, idx, idx_mode, ws,
+                     kNoAllocScratchBytes, stream, nullptr);
 }
 
 nsa_status_t nsa_fwd_decode(const nsa_decode_desc_t* desc, const nsa_params_t* params,

@@ -97,6 +97,9 @@ def lib() -> ctypes.CDLL:
     L.nsa_fwd_decode.restype = ctypes.c_int
     L.nsa_fwd_decode.argtypes = [P(DecodeDesc), P(NsaParams), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                  c_vp, c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
+    L.nsa_fwd_decode_noalloc.restype = ctypes.c_int
+    L.nsa_fwd_decode_noalloc.argtypes = [P(DecodeDesc), P(NsaParams), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                         c_vp, c_vp, c_vp, ctypes.c_int, c_vp]
     L.nsa_bwd_prefill_workspace_bytes.restype = ctypes.c_int
     L.nsa_bwd_prefill_workspace_bytes.argtypes = [P(PrefillDesc), P(NsaParams), P(ctypes.c_size_t)]
     L.nsa_bwd_prefill.restype = ctypes.c_int
@@ -499,6 +502,30 @@ def decode(q, k_cache, v_cache, kc_cache, vc_cache, seqlens, gates, *, top_k: in
     if idx is not None:
         return out, idx
     return out
+
+
+def decode_noalloc(q, k_cache, v_cache, kc_cache, vc_cache, seqlens, gates, *, top_k: int, window: int,
+                   out, idx=None, inject: bool = False, block: int = 64, select_block=None, scale: float = 0.0):
+    """nsa_fwd_decode_noalloc: the decode with the library's own device
+    scratch (no workspace). out (and idx) must be given, so that nothing is
+    allocated on this path either."""
+    _require_gpu(q, k_cache, v_cache, kc_cache, vc_cache, gates, out)
+    B, Hq, D = q.shape
+    G = k_cache.shape[1]
+    if seqlens.dtype != torch.int32 or not seqlens.is_cuda or seqlens.shape != (B,):
+        raise ValueError("seqlens must be an int32 device tensor of shape [B]")
+    if inject and idx is None:
+        raise ValueError("inject=True needs idx")
+    if idx is not None and (idx.dtype != torch.int32 or not idx.is_contiguous()
+                            or tuple(idx.shape) != (B, G, top_k)):
+        raise ValueError("idx must be a contiguous int32 [B, G, top_k] tensor")
+    desc = decode_desc(q, k_cache, v_cache, kc_cache, vc_cache, gates, out)
+    params = make_params(top_k, window, block, select_block, scale)
+    check(lib().nsa_fwd_decode_noalloc(ctypes.byref(desc), ctypes.byref(params), _ptr(q), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(kc_cache), _ptr(vc_cache), _ptr(seqlens), _ptr(gates),
+                                       _ptr(out), _ptr(idx), NSA_IDX_INJECT if inject else NSA_IDX_COMPUTE,
+                                       _stream_of(q)))
+    return (out, idx) if idx is not None else out
 
 
 def compress_kv(k, v, kc=None, vc=None, *, block: int = 64):

@@ -332,3 +332,23 @@ def test_compress_validation(L):
     assert f(k=None) == INV
     assert f(T=63) == OK          # no complete block: nothing to do
     assert f(B=0) == OK
+
+
+def test_noalloc_decode_rejects_work_beyond_its_scratch(L):
+    # bf16 caches of 262144 tokens: the compressed logits of 64 x 4 (sequence,
+    # group) pairs need 64 MiB of scratch, more than the 40 MiB the
+    # allocation-free decode holds; the call fails before any HIP call.
+    # 131072 tokens (32 MiB + the selection) fit.
+    p = nsa.make_params(16, 512)
+    n = ctypes.c_size_t()
+    d = ddesc(Lm=131072)
+    assert L.nsa_decode_workspace_bytes(ctypes.byref(d), ctypes.byref(p), ctypes.byref(n)) == OK
+    assert (32 << 20) < n.value <= (40 << 20)
+    d = ddesc(Lm=262144)
+    assert L.nsa_decode_workspace_bytes(ctypes.byref(d), ctypes.byref(p), ctypes.byref(n)) == OK
+    assert n.value > 40 << 20
+    st = L.nsa_fwd_decode_noalloc(ctypes.byref(d), ctypes.byref(p), *([FAKE] * 8), None, 0, None)
+    assert st == WS
+    assert "scratch" in L.nsa_last_error().decode()
+    # an empty batch needs no scratch and no device
+    assert L.nsa_fwd_decode_noalloc(ctypes.byref(ddesc(B=0)), ctypes.byref(p), *([None] * 9), 0, None) == OK
