@@ -25,6 +25,11 @@ Recipe (stated once, used everywhere):
   ``gate_w`` [Hq, D, 3] is N(0,1) / sqrt(D) and ``gate_b`` [Hq, 3] is N(0,1).
   Each tensor is one keyed draw ``(seed, tensor_id)``, ids 10..15, scaled in
   float32 and stored like the other inputs.
+* Token-level sparse attention (DSA) adds, per 64-token chunk, the indexer
+  queries ``qi`` (64, Hi, Di) drawn N(0,1) / sqrt(Di), the indexer keys ``ki``
+  (64, Di) drawn N(0,1) and the indexer head weights ``w`` (64, Hi) drawn
+  N(0,1) / sqrt(Hi) (tensor ids 20, 21, 22), so that a head's dot product is
+  N(0,1) and a score has spread ~0.7; q, k, v follow the recipe above.
 * Decode sequence ``b`` with length ``s`` is the prefill-shaped batch row ``b``
   read at position ``s - 1``: its query is row ``(s-1) % 64`` of Q chunk
   ``(0, b, (s-1)//64)``, its gates the same row of chunk ``(3, b, ...)``, and its
@@ -48,6 +53,8 @@ import numpy as np
 TID_Q, TID_K, TID_V, TID_GATE, TID_DOUT = 0, 1, 2, 3, 4
 # synthetic weights of the general geometry (one draw per tensor, not chunked)
 TID_WK, TID_BK, TID_WV, TID_BV, TID_GW, TID_GB = 10, 11, 12, 13, 14, 15
+# token-level sparse attention: indexer queries, indexer keys, indexer head weights
+TID_QI, TID_KI, TID_WI = 20, 21, 22
 CHUNK = 64
 
 
@@ -105,6 +112,36 @@ CONFIGS = {
     "p32k": PrefillConfig("p32k", 1, 32768, 64, 4, 128, "bf16", top_k=16, window=512),
     "p64k": PrefillConfig("p64k", 1, 65536, 64, 4, 128, "bf16", top_k=16, window=512),
     "d64k": DecodeConfig("d64k", 64, 65536, 64, 4, 128, "bf16", top_k=16, window=512),
+}
+
+
+@dataclass(frozen=True)
+class DsaConfig:
+    """Token-level sparse attention: indexer with idx_heads heads of idx_dim
+    dimensions, top_k tokens per query; attention heads as in the prefill."""
+    name: str
+    batch: int
+    seqlen: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    idx_heads: int
+    idx_dim: int
+    dtype: str
+    top_k: int
+    seed: int = 0
+
+    @property
+    def kind(self) -> str:
+        return "dsa"
+
+
+# The DSA how-to's prefill example: one 64K sequence, a 16-head indexer,
+# top-k 2048, attention in the absorbed MLA form (one key/value head shared by
+# all query heads); and a short case.
+DSA_CONFIGS = {
+    "dsa64k": DsaConfig("dsa64k", 1, 65536, 64, 1, 128, 16, 128, "bf16", top_k=2048),
+    "dsa8k": DsaConfig("dsa8k", 1, 8192, 64, 1, 128, 16, 128, "bf16", top_k=2048),
 }
 
 
@@ -285,6 +322,44 @@ def make_decode_inputs(cfg: DecodeConfig, threads: int | None = None) -> dict:
         vv = chunk_normal(cfg.seed, TID_V, b, blk, (CHUNK, G, D))[:n]
         out["k_cache"][b, :, t0:t1] = encode(kk, cfg.dtype).transpose(1, 0, 2)
         out["v_cache"][b, :, t0:t1] = encode(vv, cfg.dtype).transpose(1, 0, 2)
+
+    items = [(b, blk) for b in range(B) for blk in range(nblk)]
+    nw = threads or _workers()
+    if nw == 1 or len(items) < 4:
+        for it in items:
+            work(it)
+    else:
+        with ThreadPoolExecutor(nw) as ex:
+            list(ex.map(work, items))
+    return out
+
+
+def make_dsa_inputs(cfg: DsaConfig, threads: int | None = None) -> dict:
+    """q [B,L,Hq,D], k/v [B,L,G,D], qi [B,L,Hi,Di], ki [B,L,Di], w [B,L,Hi] in stored form."""
+    B, L, Hq, G, D, Hi, Di = (cfg.batch, cfg.seqlen, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.idx_heads,
+                              cfg.idx_dim)
+    sd = storage_dtype(cfg.dtype)
+    out = {
+        "q": np.empty((B, L, Hq, D), sd),
+        "k": np.empty((B, L, G, D), sd),
+        "v": np.empty((B, L, G, D), sd),
+        "qi": np.empty((B, L, Hi, Di), sd),
+        "ki": np.empty((B, L, Di), sd),
+        "w": np.empty((B, L, Hi), sd),
+    }
+    nblk = (L + CHUNK - 1) // CHUNK
+    sq, sw = np.float32(1.0 / np.sqrt(Di)), np.float32(1.0 / np.sqrt(Hi))
+
+    def work(item):
+        b, blk = item
+        t0, t1 = blk * CHUNK, min(L, (blk + 1) * CHUNK)
+        n = t1 - t0
+        out["q"][b, t0:t1] = encode(chunk_normal(cfg.seed, TID_Q, b, blk, (CHUNK, Hq, D))[:n], cfg.dtype)
+        out["k"][b, t0:t1] = encode(chunk_normal(cfg.seed, TID_K, b, blk, (CHUNK, G, D))[:n], cfg.dtype)
+        out["v"][b, t0:t1] = encode(chunk_normal(cfg.seed, TID_V, b, blk, (CHUNK, G, D))[:n], cfg.dtype)
+        out["qi"][b, t0:t1] = encode(chunk_normal(cfg.seed, TID_QI, b, blk, (CHUNK, Hi, Di))[:n] * sq, cfg.dtype)
+        out["ki"][b, t0:t1] = encode(chunk_normal(cfg.seed, TID_KI, b, blk, (CHUNK, Di))[:n], cfg.dtype)
+        out["w"][b, t0:t1] = encode(chunk_normal(cfg.seed, TID_WI, b, blk, (CHUNK, Hi))[:n] * sw, cfg.dtype)
 
     items = [(b, blk) for b in range(B) for blk in range(nblk)]
     nw = threads or _workers()

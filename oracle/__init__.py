@@ -1,4 +1,5 @@
-"""Float64 CPU oracle of the NSA forward pass (test infrastructure only).
+"""Float64 CPU oracles of the NSA forward pass and of token-level sparse
+attention (test infrastructure only).
 
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
 this package; the GPU library never does.
@@ -8,3 +9,4 @@ from .nsa_ref import (compress, decode, gates_from_query, n_compressed, nsa_toke
 
 __all__ = ["compress", "decode", "gates_from_query", "n_compressed", "nsa_token", "prefill", "select_blocks",
            "selection_scores", "softmax_attend"]
+from . import dsa_ref  # noqa: E402,F401

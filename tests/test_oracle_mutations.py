@@ -2,9 +2,10 @@
 
 Each case plants one plausible mistake into a copy of the oracle's source
 (a dropped term, a wrong sign or index, an off-by-one, a transposed map),
-loads the copy as a separate module, points the pin tests of
-tests/test_oracle.py and tests/test_oracle_general.py at it and runs them:
-at least one pin must fail. A
+loads the copy as a separate module, points the pin tests at it
+(tests/test_oracle.py and tests/test_oracle_general.py for the NSA oracle,
+tests/test_oracle_dsa.py for the token-level sparse attention oracle) and
+runs them: at least one pin must fail. A
 mutant that every pin passes marks a part of the oracle that nothing
 independent checks. The mistakes are planted in the oracle's source text only,
 on the CPU; the oracle module itself is never modified.
@@ -17,11 +18,13 @@ import types
 
 import pytest
 
-from tests import test_oracle, test_oracle_general
+from tests import test_oracle, test_oracle_dsa, test_oracle_general
 
 PIN_MODULES = (test_oracle, test_oracle_general)
 
-ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "nsa_ref.py")
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+ORACLE_SRC = os.path.join(ORACLE_DIR, "nsa_ref.py")
+DSA_SRC = os.path.join(ORACLE_DIR, "dsa_ref.py")
 
 # (name, original text, planted text): the original must occur exactly once.
 MUTANTS = [
@@ -112,11 +115,31 @@ def _module_pins(module):
     return calls
 
 
-def _mutant_module(original: str, planted: str) -> types.ModuleType:
-    src = open(ORACLE_SRC).read()
+# mistakes planted in the token-level sparse attention oracle
+DSA_MUTANTS = [
+    ("indexer without its ReLU", "np.maximum(qi_t @ ki.T, 0.0)", "(qi_t @ ki.T)"),
+    ("indexer head weights ignored", "(w_t[:, None] * np.maximum(qi_t @ ki.T, 0.0)).sum(axis=0)",
+     "np.maximum(qi_t @ ki.T, 0.0).sum(axis=0)"),
+    ("ties to the higher token", "np.lexsort((np.arange(n), -cand))", "np.lexsort((-np.arange(n), -cand))"),
+    ("one candidate past the query", "n = t + 1\n    if n <= top_k:", "n = t + 2\n    if n <= top_k:"),
+    ("gap one rank late", "gap = float(ranked[top_k - 1] - ranked[top_k])",
+     "gap = float(ranked[top_k] - ranked[min(top_k + 1, n - 1)])"),
+    ("attention scale missing", "s = scale * (qh @ keys.T)", "s = qh @ keys.T"),
+    ("heads grouped by stride", "hs = slice(g * Hg, (g + 1) * Hg)", "hs = slice(g, Hq, G)"),
+    ("injected tokens after the query kept", "toks = sorted({int(j) for j in idx if 0 <= j <= t})",
+     "toks = sorted({int(j) for j in idx if 0 <= j})"),
+    ("injected repeats counted twice", "toks = sorted({int(j) for j in idx if 0 <= j <= t})",
+     "toks = sorted(int(j) for j in idx if 0 <= j <= t)"),
+    ("scores of the next query", "sc = indexer_scores(qi[b, t], KI[: t + 1], w[b, t])",
+     "sc = indexer_scores(qi[b, min(t + 1, L - 1)], KI[: t + 1], w[b, t])"),
+]
+
+
+def _mutant_module(original: str, planted: str, path: str = ORACLE_SRC) -> types.ModuleType:
+    src = open(path).read()
     assert src.count(original) == 1, f"the original text must occur once in the oracle: {original!r}"
     mod = types.ModuleType("nsa_ref_mutant")
-    mod.__file__ = ORACLE_SRC + " (mutant)"
+    mod.__file__ = path + " (mutant)"
     exec(compile(src.replace(original, planted), mod.__file__, "exec"), mod.__dict__)
     return mod
 
@@ -140,5 +163,22 @@ def test_some_pin_kills_the_mutant(name, original, planted, monkeypatch):
         try:
             fn(**kw)
         except Exception:  # an assertion, or a crash the mistake causes
+            return
+    pytest.fail(f"no pin detects the planted mistake '{name}'")
+
+
+def test_dsa_pins_pass_on_the_unmodified_oracle_text(monkeypatch):
+    monkeypatch.setattr(test_oracle_dsa, "dsa_ref", _mutant_module("import numpy as np", "import numpy as np", DSA_SRC))
+    for name, fn, kw in _module_pins(test_oracle_dsa):
+        fn(**kw)
+
+
+@pytest.mark.parametrize("name,original,planted", DSA_MUTANTS, ids=[m[0] for m in DSA_MUTANTS])
+def test_some_dsa_pin_kills_the_mutant(name, original, planted, monkeypatch):
+    monkeypatch.setattr(test_oracle_dsa, "dsa_ref", _mutant_module(original, planted, DSA_SRC))
+    for pin, fn, kw in _module_pins(test_oracle_dsa):
+        try:
+            fn(**kw)
+        except Exception:
             return
     pytest.fail(f"no pin detects the planted mistake '{name}'")
