@@ -463,6 +463,76 @@ def bench_backward(cfg, raw, steps, torch, nsa):
                       "forward_save_ms_per_step": save_ms}}
 
 
+def dsa_flops(cfg):
+    """Algorithmic work of token-level sparse attention: the indexer's dot
+    products (2 Di per (query, earlier token, indexer head)) and the attention
+    over the chosen tokens (4 D per (query, chosen token, query head))."""
+    L, k = cfg.seqlen, cfg.top_k
+    t = np.arange(L, dtype=np.int64)
+    pairs = int((t + 1).sum())
+    chosen = int(np.minimum(t + 1, k).sum())
+    return {"indexer": cfg.batch * pairs * cfg.idx_heads * 2 * cfg.idx_dim,
+            "attention": cfg.batch * chosen * cfg.n_q_heads * 4 * cfg.head_dim,
+            "score_bytes": cfg.batch * pairs * 4, "chosen": cfg.batch * chosen}
+
+
+def bench_dsa(cfg, steps, warmup, torch, inputs, nsa):
+    """nsa_dsa_prefill (indexer, top-k, attention over the chosen tokens) on
+    the token-level sparse workload, timed per stage with HIP events."""
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    raw = inputs.make_dsa_inputs(cfg)
+    log(f"[bench] inputs {cfg.name} generated in {time.perf_counter() - t0:.1f} s")
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    ts = [up(raw[n]) for n in ("q", "k", "v", "qi", "ki", "w")]
+    del raw
+    out = torch.empty(ts[0].shape, dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((cfg.batch, cfg.seqlen, cfg.top_k), dtype=torch.int32, device=dev)
+    ws = torch.empty(nsa.dsa_workspace_bytes(*ts, out, top_k=cfg.top_k), dtype=torch.uint8, device=dev)
+    desc = nsa.dsa_desc(*ts, out)
+    params = nsa.DsaParams(cfg.top_k, 0.0)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    call = lambda: nsa.dsa_prefill(*ts, top_k=cfg.top_k, out=out, idx=idx, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    stages = ["indexer", "topk", "attention"]
+    ns = len(stages) + 1
+    ev = HipEvents(ns * steps)
+    for i in range(steps):
+        nsa.check(nsa.lib().nsa_dsa_prefill_timed(ctypes.byref(desc), ctypes.byref(params), *(P(x) for x in ts), P(out),
+                                                  P(idx), nsa.NSA_IDX_COMPUTE, P(ws), ws.numel(), stream,
+                                                  ev.array(i * ns, ns)))
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([ev.elapsed_ms(i * ns + s, i * ns + s + 1) for i in range(steps)]))
+                for s, name in enumerate(stages)}
+    ev.close()
+    fl = dsa_flops(cfg)
+    gathered = fl["chosen"] * cfg.n_kv_heads * cfg.head_dim * 2 * 2
+    log(f"[bench] dsa {cfg.name}: {wall_ms:.3f} ms/step, kernels {stage_ms}")
+    return {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen, "top_k": cfg.top_k,
+            "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
+            "idx_heads": cfg.idx_heads, "idx_dim": cfg.idx_dim, "ms_per_step": wall_ms,
+            "tokens_per_s": cfg.batch * cfg.seqlen / (wall_ms * 1e-3), "kernels_ms": stage_ms,
+            "indexer": {"flops": fl["indexer"], "tflops": fl["indexer"] / (stage_ms["indexer"] * 1e-3) / 1e12,
+                        "mfma_frac": fl["indexer"] / (stage_ms["indexer"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                        "score_bytes_written": fl["score_bytes"]},
+            "topk": {"score_bytes_read": fl["score_bytes"],
+                     "GBps": fl["score_bytes"] / (stage_ms["topk"] * 1e-3) / 1e9},
+            "attention": {"flops": fl["attention"],
+                          "tflops": fl["attention"] / (stage_ms["attention"] * 1e-3) / 1e12,
+                          "mfma_frac": fl["attention"] / (stage_ms["attention"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                          "gathered_bytes": gathered,
+                          "gathered_TBps": gathered / (stage_ms["attention"] * 1e-3) / 1e12},
+            "dtype": "bf16 (indexer and attention operands), fp32 scores and accumulation"}
+
+
 def bench_decode(cfg, steps, warmup, torch, inputs, nsa):
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
@@ -530,6 +600,7 @@ def main():
     ap.add_argument("--also", default="p8k,p32k",
                     help="shorter prefill configs also reported (their inputs are prefixes of the "
                          "main config's); empty for none")
+    ap.add_argument("--dsa", default="dsa64k", help="token-level sparse attention workload also timed ('' to skip)")
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -641,6 +712,8 @@ def main():
         result["shared_selection_prefill"] = bench_shared_selection(cfg, raw, args.steps, torch, nsa)
     if not args.no_backward:
         result["backward"] = bench_backward(cfg, raw, max(1, min(args.steps, 5)), torch, nsa)
+    if args.dsa:
+        result["dsa"] = bench_dsa(inputs.DSA_CONFIGS[args.dsa], max(1, min(args.steps, 5)), 1, torch, inputs, nsa)
     if not args.no_decode:
         result["decode"] = bench_decode(inputs.CONFIGS["d64k"], args.decode_steps, 3, torch, inputs, nsa)
     if not args.no_cpu_baseline:

@@ -417,6 +417,65 @@ nsa_status_t nsa_bwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_par
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    void* const* stage_events);
 
+/*
+ * Token-level sparse attention with a ReLU indexer (DeepSeek Sparse
+ * Attention, DSA; DSA how-to, bjdmk.com.cn/news/5181035): each query token
+ * attends only to the top_k tokens (2048 on that page) that a lightweight
+ * multi-head indexer ranks highest, which takes the core attention from
+ * O(L^2) to O(L * top_k) (section 1); the indexer is a linear layer, a dot
+ * product and ReLU with 8 or 16 heads and one cached indexer key per token
+ * (section 3); a top_k at or above the sequence length is dense attention
+ * (section 5). Computes, for each (b, t):
+ *   scores:    I(t, s) = sum_j w[t][j] * max(qi[t][j] . ki[s], 0) for s <= t;
+ *   selection: the top_k tokens s <= t by score, ties to the lower token, all
+ *              of them when t + 1 <= top_k; shared by all query heads;
+ *   attention: out[t][h] = softmax attention of q[t][h] (scale softmax_scale,
+ *              <= 0 -> 1/sqrt(head_dim)) over k, v of the chosen tokens in
+ *              KV head h / (n_q_heads / n_kv_heads).
+ *   q [B, L, Hq, D], k/v [B, L, G, D], out [B, L, Hq, D] with (b, t, head)
+ *   strides; qi [B, L, Hi, Di] with (b, t, indexer head) strides; ki [B, L, Di]
+ *   and w [B, L, Hi] with (b, t) strides (last dimension contiguous).
+ *   idx [B, L, top_k] int32 dense: NSA_IDX_COMPUTE writes the chosen tokens
+ *   ascending, padded with -1 (when idx != NULL); NSA_IDX_INJECT reads them
+ *   (a set of tokens: entries outside [0, t] and repeats add nothing; no
+ *   usable entry gives out = 0) and runs no indexer.
+ * Supported: head_dim and idx_dim in {64, 128}; 1 <= idx_heads <= 16;
+ * 1 <= top_k <= 2048; n_q_heads <= 64 with n_q_heads / n_kv_heads at most 16
+ * or a multiple of 16; bf16 in / {bf16, f32} out, f32 in / f32 out; strides
+ * multiples of 8 elements. The workspace (nsa_dsa_workspace_bytes) holds the
+ * float32 indexer scores of every (query, earlier token) pair,
+ * B * L * (L + 1) / 2 floats (8 GiB for one 64k sequence), and the
+ * selection when idx is NULL. Errors as for the other entry points.
+ */
+typedef struct {
+  int32_t batch, seqlen, n_q_heads, n_kv_heads, head_dim, idx_heads, idx_dim;
+  nsa_dtype_t in_dtype, out_dtype;
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+  int64_t qi_stride[3];
+  int64_t ki_stride[2];
+  int64_t w_stride[2];
+} nsa_dsa_desc_t;
+
+typedef struct {
+  int32_t top_k;
+  float softmax_scale; /* <= 0 selects 1/sqrt(head_dim) */
+} nsa_dsa_params_t;
+
+nsa_status_t nsa_dsa_workspace_bytes(const nsa_dsa_desc_t* desc, const nsa_dsa_params_t* params, size_t* bytes);
+nsa_status_t nsa_dsa_prefill(const nsa_dsa_desc_t* desc, const nsa_dsa_params_t* params, const void* q,
+                             const void* k, const void* v, const void* qi, const void* ki, const void* w, void* out,
+                             int32_t* idx, nsa_idx_mode_t idx_mode, void* workspace, size_t workspace_bytes,
+                             void* stream);
+/* nsa_dsa_prefill recording 4 caller-created hipEvents (indexer; top-k;
+ * attention); with NSA_IDX_INJECT the first two stages are empty. */
+nsa_status_t nsa_dsa_prefill_timed(const nsa_dsa_desc_t* desc, const nsa_dsa_params_t* params, const void* q,
+                                   const void* k, const void* v, const void* qi, const void* ki, const void* w,
+                                   void* out, int32_t* idx, nsa_idx_mode_t idx_mode, void* workspace,
+                                   size_t workspace_bytes, void* stream, void* const* stage_events);
+
 /* Static name of a status code. */
 const char* nsa_status_string(nsa_status_t status);
 

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(PKG, "libnsa.so")
-SOURCES = ["nsa_api.cpp", "nsa_prefill.hip", "nsa_decode.hip", "nsa_compress.hip", "nsa_backward.hip"]
+SOURCES = ["nsa_api.cpp", "nsa_prefill.hip", "nsa_decode.hip", "nsa_compress.hip", "nsa_backward.hip",
+           "nsa_dsa.hip"]
 ARCH = "gfx950"
 
 

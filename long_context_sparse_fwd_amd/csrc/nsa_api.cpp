@@ -752,6 +752,169 @@ nsa_status_t nsa_bwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_par
                        stream, stage_events);
 }
 
+}  // extern "C"
+
+// ------------------------------------------------------------------ token-level sparse attention (DSA)
+
+namespace {
+
+struct DsaPlan {
+  int waves, heads_per_wave, topk_cache;
+  size_t off_scores, off_idx, total;
+};
+
+nsa_status_t plan_dsa(const nsa_dsa_desc_t* d, const nsa_dsa_params_t* p, DsaPlan* pl) {
+  if (d == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (p == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "params is NULL");
+  if (d->batch < 0 || d->seqlen < 0) return fail(NSA_ERR_INVALID_ARGUMENT, "batch and seqlen must be >= 0");
+  const int Hq = d->n_q_heads, G = d->n_kv_heads, D = d->head_dim;
+  if (Hq < 1 || G < 1 || D < 1 || d->idx_heads < 1 || d->idx_dim < 1)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "head counts and dimensions must be >= 1");
+  if (Hq % G != 0)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", Hq, G);
+  NSA_TRY(check_dtypes(d->in_dtype, d->out_dtype));
+  if (p->top_k < 1) return fail(NSA_ERR_INVALID_ARGUMENT, "top_k must be >= 1 (got %d)", p->top_k);
+  if (!std::isfinite(p->softmax_scale)) return fail(NSA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
+  if (D != 64 && D != 128) return fail(NSA_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", D);
+  if (d->idx_dim != 64 && d->idx_dim != 128)
+    return fail(NSA_ERR_UNSUPPORTED, "idx_dim %d is not supported (64 or 128)", d->idx_dim);
+  if (d->idx_heads > 16) return fail(NSA_ERR_UNSUPPORTED, "more than 16 indexer heads (%d)", d->idx_heads);
+  if (p->top_k > nsa::kDsaMaxTopK)
+    return fail(NSA_ERR_UNSUPPORTED, "top_k above %d is not supported (got %d)", nsa::kDsaMaxTopK, p->top_k);
+  const int Hg = Hq / G;
+  if (Hq > 64 || (Hg > 16 && Hg % 16 != 0))
+    return fail(NSA_ERR_UNSUPPORTED, "needs n_q_heads <= 64 with at most 16 or a multiple of 16 query heads per "
+                                     "KV head (got %d, %d)", Hq, Hg);
+  NSA_TRY(check_strides("q", d->q_stride, 3, true));
+  NSA_TRY(check_strides("k", d->k_stride, 3, true));
+  NSA_TRY(check_strides("v", d->v_stride, 3, true));
+  NSA_TRY(check_strides("out", d->o_stride, 3, true));
+  NSA_TRY(check_strides("qi", d->qi_stride, 3, true));
+  NSA_TRY(check_strides("ki", d->ki_stride, 2, true));
+  NSA_TRY(check_strides("w", d->w_stride, 2, false));
+  pl->waves = Hg >= 16 ? Hq / 16 : G;
+  pl->heads_per_wave = Hg >= 16 ? 16 : Hg;
+  const bool bf16 = d->in_dtype == NSA_BF16;
+  const int gpw = Hg >= 16 ? 1 : G;   // KV heads staged per workgroup
+  if (nsa::dsa_attn_lds_bytes(gpw, D, bf16, p->top_k) > static_cast<size_t>(nsa::kMaxLds))
+    return fail(NSA_ERR_UNSUPPORTED, "the attention stage of %d KV heads does not fit a CU's LDS", gpw);
+  pl->topk_cache = 32768;
+  const int64_t B = d->batch, L = d->seqlen;
+  if (B * L > INT32_MAX) return fail(NSA_ERR_UNSUPPORTED, "batch * seqlen too large");
+  size_t off = 0;
+  pl->off_scores = off;
+  off = align_up(off + static_cast<size_t>(B) * static_cast<size_t>(L) * static_cast<size_t>(L + 1) / 2 *
+                           sizeof(float));
+  pl->off_idx = off;
+  off = align_up(off + static_cast<size_t>(B * L) * p->top_k * sizeof(int32_t));
+  pl->total = off;
+  return NSA_OK;
+}
+
+nsa_status_t dsa_impl(const nsa_dsa_desc_t* desc, const nsa_dsa_params_t* params, const void* q, const void* k,
+                      const void* v, const void* qi, const void* ki, const void* w, void* out, int32_t* idx,
+                      nsa_idx_mode_t idx_mode, void* workspace, size_t workspace_bytes, void* stream,
+                      void* const* events) {
+  DsaPlan pl;
+  NSA_TRY(plan_dsa(desc, params, &pl));
+  if (idx_mode != NSA_IDX_COMPUTE && idx_mode != NSA_IDX_INJECT)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "unknown idx_mode %d", static_cast<int>(idx_mode));
+  if (desc->batch == 0 || desc->seqlen == 0) return ok();
+  const bool inject = idx_mode == NSA_IDX_INJECT;
+  NSA_TRY(check_ptr("q", q, true));
+  NSA_TRY(check_ptr("k", k, true));
+  NSA_TRY(check_ptr("v", v, true));
+  NSA_TRY(check_ptr("out", out, true));
+  if (!inject) {
+    NSA_TRY(check_ptr("qi", qi, true));
+    NSA_TRY(check_ptr("ki", ki, true));
+    NSA_TRY(check_ptr("w", w, false));
+    const size_t el = desc->in_dtype == NSA_BF16 ? 2 : 4;
+    if ((reinterpret_cast<uintptr_t>(w) % el) != 0)
+      return fail(NSA_ERR_INVALID_ARGUMENT, "w is not aligned to its element size");
+  }
+  NSA_TRY(check_ptr("workspace", workspace, true));
+  if (inject && idx == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "NSA_IDX_INJECT needs idx");
+  if (idx != nullptr && (reinterpret_cast<uintptr_t>(idx) & 3u) != 0)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "idx is not 4-byte aligned");
+  if (workspace_bytes < pl.total)
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", pl.total, workspace_bytes);
+  nsa::DsaArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = desc->batch;
+  a.L = desc->seqlen;
+  a.Hq = desc->n_q_heads;
+  a.G = desc->n_kv_heads;
+  a.Hg = a.Hq / a.G;
+  a.D = desc->head_dim;
+  a.Hi = desc->idx_heads;
+  a.Di = desc->idx_dim;
+  a.topk = params->top_k;
+  a.waves = pl.waves;
+  a.heads_per_wave = pl.heads_per_wave;
+  a.idx_tiles = (a.L + 15) / 16;
+  a.topk_cache = pl.topk_cache;
+  const float sc = params->softmax_scale > 0.f ? params->softmax_scale : 1.0f / std::sqrt(static_cast<float>(a.D));
+  a.scale_log2 = sc * nsa::kLog2eHost;
+  a.inject = inject ? 1 : 0;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.qi = qi;
+  a.ki = ki;
+  a.w = w;
+  a.out = out;
+  char* ws = static_cast<char*>(workspace);
+  a.scores = reinterpret_cast<float*>(ws + pl.off_scores);
+  a.idx = idx != nullptr ? idx : reinterpret_cast<int32_t*>(ws + pl.off_idx);
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = desc->q_stride[i];
+    a.ks[i] = desc->k_stride[i];
+    a.vs[i] = desc->v_stride[i];
+    a.os[i] = desc->o_stride[i];
+    a.qis[i] = desc->qi_stride[i];
+  }
+  for (int i = 0; i < 2; ++i) {
+    a.kis[i] = desc->ki_stride[i];
+    a.wis[i] = desc->w_stride[i];
+  }
+  hipError_t e = nsa::launch_dsa(a, desc->in_dtype == NSA_BF16, desc->out_dtype == NSA_BF16,
+                                 static_cast<hipStream_t>(stream),
+                                 reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)));
+  if (e != hipSuccess) return fail(NSA_ERR_HIP, "HIP error in the sparse attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+nsa_status_t nsa_dsa_workspace_bytes(const nsa_dsa_desc_t* desc, const nsa_dsa_params_t* params, size_t* bytes) {
+  if (bytes == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  DsaPlan pl;
+  NSA_TRY(plan_dsa(desc, params, &pl));
+  *bytes = pl.total;
+  return ok();
+}
+
+nsa_status_t nsa_dsa_prefill(const nsa_dsa_desc_t* desc, const nsa_dsa_params_t* params, const void* q,
+                             const void* k, const void* v, const void* qi, const void* ki, const void* w, void* out,
+                             int32_t* idx, nsa_idx_mode_t idx_mode, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return dsa_impl(desc, params, q, k, v, qi, ki, w, out, idx, idx_mode, workspace, workspace_bytes, stream, nullptr);
+}
+
+nsa_status_t nsa_dsa_prefill_timed(const nsa_dsa_desc_t* desc, const nsa_dsa_params_t* params, const void* q,
+                                   const void* k, const void* v, const void* qi, const void* ki, const void* w,
+                                   void* out, int32_t* idx, nsa_idx_mode_t idx_mode, void* workspace,
+                                   size_t workspace_bytes, void* stream, void* const* stage_events) {
+  if (stage_events == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "stage_events is NULL");
+  for (int i = 0; i <= nsa::kDsaStages; ++i)
+    if (stage_events[i] == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "stage_events[%d] is NULL", i);
+  return dsa_impl(desc, params, q, k, v, qi, ki, w, out, idx, idx_mode, workspace, workspace_bytes, stream,
+                  stage_events);
+}
+
 nsa_status_t nsa_fwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_params_t* params,
                                    const void* q, const void* k, const void* v, const void* gates,
                                    void* out, int32_t* idx, nsa_idx_mode_t idx_mode,

@@ -139,3 +139,34 @@ inline size_t cmp_lds_bytes(int waves, int NcT) {
 inline size_t cmp_topk_scratch_bytes() { return kSurvCap * sizeof(uint64_t) + 64 * sizeof(int); }
 
 }  // namespace nsa
+
+namespace nsa {
+
+// Token-level sparse attention with a ReLU indexer (DSA): the arguments of
+// its three kernels.
+struct DsaArgs {
+  int B, L, Hq, G, Hg, D, Hi, Di, topk;
+  int waves;        // attention waves per workgroup: 16 query heads each
+  int heads_per_wave;  // min(Hg, 16)
+  int idx_tiles;    // indexer workgroups per sequence (16 query tokens each)
+  int topk_cache;   // orderable keys of a row kept in LDS by the top-k kernel
+  float scale_log2; // softmax scale * log2(e)
+  int inject;       // 1: idx holds the selection (a set of tokens)
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* qi;
+  const void* ki;
+  const void* w;
+  void* out;
+  int32_t* idx;     // [B][L][topk], ascending, -1 padded
+  float* scores;    // indexer scores, row t of sequence b at b*L(L+1)/2 + t(t+1)/2
+  int64_t qs[3], ks[3], vs[3], os[3], qis[3], kis[2], wis[2];
+};
+constexpr int kDsaStages = 3;
+constexpr int kDsaMaxTopK = 2048;
+hipError_t launch_dsa(const DsaArgs& a, bool in_bf16, bool out_bf16, hipStream_t st, hipEvent_t* ev);
+size_t dsa_topk_lds_bytes(int cache);
+size_t dsa_attn_lds_bytes(int groups_per_wg, int D, bool bf16, int k);
+
+}  // namespace nsa

@@ -51,6 +51,18 @@ class NsaGeneral(ctypes.Structure):
                 ("gate_w", c_vp), ("gate_b", c_vp)]
 
 
+class DsaDesc(ctypes.Structure):
+    _fields_ = [("batch", c_i32), ("seqlen", c_i32), ("n_q_heads", c_i32), ("n_kv_heads", c_i32),
+                ("head_dim", c_i32), ("idx_heads", c_i32), ("idx_dim", c_i32), ("in_dtype", ctypes.c_int),
+                ("out_dtype", ctypes.c_int), ("q_stride", c_i64 * 3), ("k_stride", c_i64 * 3),
+                ("v_stride", c_i64 * 3), ("o_stride", c_i64 * 3), ("qi_stride", c_i64 * 3),
+                ("ki_stride", c_i64 * 2), ("w_stride", c_i64 * 2)]
+
+
+class DsaParams(ctypes.Structure):
+    _fields_ = [("top_k", c_i32), ("softmax_scale", c_f32)]
+
+
 class NsaError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(message)
@@ -100,6 +112,13 @@ def lib() -> ctypes.CDLL:
     L.nsa_fwd_decode_noalloc.restype = ctypes.c_int
     L.nsa_fwd_decode_noalloc.argtypes = [P(DecodeDesc), P(NsaParams), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                          c_vp, c_vp, c_vp, ctypes.c_int, c_vp]
+    L.nsa_dsa_workspace_bytes.restype = ctypes.c_int
+    L.nsa_dsa_workspace_bytes.argtypes = [P(DsaDesc), P(DsaParams), P(ctypes.c_size_t)]
+    L.nsa_dsa_prefill.restype = ctypes.c_int
+    L.nsa_dsa_prefill.argtypes = [P(DsaDesc), P(DsaParams), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                  ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
+    L.nsa_dsa_prefill_timed.restype = ctypes.c_int
+    L.nsa_dsa_prefill_timed.argtypes = L.nsa_dsa_prefill.argtypes + [c_vp]
     L.nsa_bwd_prefill_workspace_bytes.restype = ctypes.c_int
     L.nsa_bwd_prefill_workspace_bytes.argtypes = [P(PrefillDesc), P(NsaParams), P(ctypes.c_size_t)]
     L.nsa_bwd_prefill.restype = ctypes.c_int
@@ -541,3 +560,64 @@ def compress_kv(k, v, kc=None, vc=None, *, block: int = 64):
     check(lib().nsa_compress_kv(B, G, L, D, _dtype_code(k.dtype), block, _ptr(k), arr(k), _ptr(v),
                                 arr(v), _ptr(kc), arr(kc), _ptr(vc), arr(vc), _stream_of(k)))
     return kc, vc
+
+
+def dsa_desc(q, k, v, qi, ki, w, out) -> DsaDesc:
+    B, L, Hq, D = q.shape
+    d = DsaDesc()
+    d.batch, d.seqlen, d.n_q_heads, d.n_kv_heads, d.head_dim = B, L, Hq, k.shape[2], D
+    d.idx_heads, d.idx_dim = qi.shape[2], qi.shape[3]
+    d.in_dtype, d.out_dtype = _dtype_code(q.dtype), _dtype_code(out.dtype)
+    d.q_stride[:] = q.stride()[:3]
+    d.k_stride[:] = k.stride()[:3]
+    d.v_stride[:] = v.stride()[:3]
+    d.o_stride[:] = out.stride()[:3]
+    d.qi_stride[:] = qi.stride()[:3]
+    d.ki_stride[:] = ki.stride()[:2]
+    d.w_stride[:] = w.stride()[:2]
+    return d
+
+
+def dsa_workspace_bytes(q, k, v, qi, ki, w, out, *, top_k: int) -> int:
+    n = ctypes.c_size_t()
+    check(lib().nsa_dsa_workspace_bytes(ctypes.byref(dsa_desc(q, k, v, qi, ki, w, out)),
+                                        ctypes.byref(DsaParams(top_k, 0.0)), ctypes.byref(n)))
+    return n.value
+
+
+def dsa_prefill(q, k, v, qi, ki, w, *, top_k: int, scale: float = 0.0, out=None, out_dtype=None, idx=None,
+                inject: bool = False, return_idx: bool = False, workspace=None):
+    """Token-level sparse attention with a ReLU indexer (nsa_dsa_prefill).
+    q [B,L,Hq,D], k/v [B,L,G,D], qi [B,L,Hi,Di], ki [B,L,Di], w [B,L,Hi].
+    Returns out (and idx [B,L,top_k] int32 when return_idx or idx is given)."""
+    _require_gpu(q, k, v, qi, ki, w)
+    B, L, Hq, D = q.shape
+    G = k.shape[2]
+    Hi, Di = qi.shape[2], qi.shape[3]
+    if (k.shape != (B, L, G, D) or v.shape != k.shape or qi.shape[:2] != (B, L) or ki.shape != (B, L, Di)
+            or w.shape != (B, L, Hi)):
+        raise ValueError("shape mismatch among q, k, v, qi, ki, w")
+    if not (q.dtype == k.dtype == v.dtype == qi.dtype == ki.dtype == w.dtype):
+        raise TypeError("all inputs must share one dtype")
+    if out is None:
+        out = torch.empty((B, L, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if inject and idx is None:
+        raise ValueError("inject=True needs idx")
+    if idx is None and return_idx:
+        idx = torch.empty((B, L, top_k), dtype=torch.int32, device=q.device)
+    if idx is not None and (idx.dtype != torch.int32 or not idx.is_contiguous()
+                            or tuple(idx.shape) != (B, L, top_k)):
+        raise ValueError("idx must be a contiguous int32 [B, L, top_k] tensor")
+    desc = dsa_desc(q, k, v, qi, ki, w, out)
+    params = DsaParams(top_k, scale)
+    L_ = lib()
+    nbytes = ctypes.c_size_t()
+    check(L_.nsa_dsa_workspace_bytes(ctypes.byref(desc), ctypes.byref(params), ctypes.byref(nbytes)))
+    if workspace is None or workspace.numel() < nbytes.value:
+        workspace = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=q.device)
+    check(L_.nsa_dsa_prefill(ctypes.byref(desc), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(qi), _ptr(ki),
+                             _ptr(w), _ptr(out), _ptr(idx), NSA_IDX_INJECT if inject else NSA_IDX_COMPUTE,
+                             _ptr(workspace), workspace.numel(), _stream_of(q)))
+    if idx is not None:
+        return out, idx
+    return out
