@@ -440,7 +440,8 @@ nsa_status_t nsa_bwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_par
  *   (a set of tokens: entries outside [0, t] and repeats add nothing; no
  *   usable entry gives out = 0) and runs no indexer.
  * Supported: head_dim and idx_dim in {64, 128}; 1 <= idx_heads <= 16;
- * 1 <= top_k <= 2048; n_q_heads <= 64 with n_q_heads / n_kv_heads at most 16
+ * 1 <= top_k <= 2048; seqlen <= 131072 (the page's 128K maximum context);
+ * n_q_heads <= 64 with n_q_heads / n_kv_heads at most 16
  * or a multiple of 16; bf16 in / {bf16, f32} out, f32 in / f32 out; strides
  * multiples of 8 elements. The workspace (nsa_dsa_workspace_bytes) holds the
  * float32 indexer scores of every (query, earlier token) pair,

@@ -759,7 +759,7 @@ nsa_status_t nsa_bwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_par
 namespace {
 
 struct DsaPlan {
-  int waves, heads_per_wave, topk_cache;
+  int waves, heads_per_wave, topk_cache, parts, gpw, wg_waves;
   size_t off_scores, off_idx, total;
 };
 
@@ -795,10 +795,23 @@ nsa_status_t plan_dsa(const nsa_dsa_desc_t* d, const nsa_dsa_params_t* p, DsaPla
   pl->waves = Hg >= 16 ? Hq / 16 : G;
   pl->heads_per_wave = Hg >= 16 ? 16 : Hg;
   const bool bf16 = d->in_dtype == NSA_BF16;
-  const int gpw = Hg >= 16 ? 1 : G;   // KV heads staged per workgroup
-  if (nsa::dsa_attn_lds_bytes(gpw, D, bf16, p->top_k) > static_cast<size_t>(nsa::kMaxLds))
-    return fail(NSA_ERR_UNSUPPORTED, "the attention stage of %d KV heads does not fit a CU's LDS", gpw);
-  pl->topk_cache = 32768;
+  // a query token's KV heads over as few attention workgroups as the LDS
+  // allows: the most KV heads (a divisor of G) whose staging fits
+  const int wpg = Hg >= 16 ? Hg / 16 : 1;
+  const size_t lds_cap = static_cast<size_t>(nsa::kMaxLds) - 1024;   // room for the static LDS
+  pl->gpw = 0;
+  for (int gpw = G; gpw >= 1; --gpw)
+    if (G % gpw == 0 && nsa::dsa_attn_lds_bytes(gpw, D, bf16, p->top_k) <= lds_cap) {
+      pl->gpw = gpw;
+      break;
+    }
+  if (pl->gpw == 0) return fail(NSA_ERR_UNSUPPORTED, "the attention stage of one KV head does not fit a CU's LDS");
+  pl->parts = G / pl->gpw;
+  pl->wg_waves = pl->gpw * wpg;
+  pl->topk_cache = 65536;   // top 16 bits of a row's keys in LDS (128 KiB)
+  if (d->seqlen > 131072)
+    return fail(NSA_ERR_UNSUPPORTED, "seqlen above 131072 (the 128K context of the DSA how-to) is not supported "
+                                     "(got %d)", d->seqlen);
   const int64_t B = d->batch, L = d->seqlen;
   if (B * L > INT32_MAX) return fail(NSA_ERR_UNSUPPORTED, "batch * seqlen too large");
   size_t off = 0;
@@ -852,6 +865,9 @@ nsa_status_t dsa_impl(const nsa_dsa_desc_t* desc, const nsa_dsa_params_t* params
   a.topk = params->top_k;
   a.waves = pl.waves;
   a.heads_per_wave = pl.heads_per_wave;
+  a.parts = pl.parts;
+  a.gpw = pl.gpw;
+  a.wg_waves = pl.wg_waves;
   a.idx_tiles = (a.L + 15) / 16;
   a.topk_cache = pl.topk_cache;
   const float sc = params->softmax_scale > 0.f ? params->softmax_scale : 1.0f / std::sqrt(static_cast<float>(a.D));

@@ -168,25 +168,26 @@ __global__ __launch_bounds__(512) void k_dsa_index(DsaArgs a) {
 
 // ------------------------------------------------------------------ k_dsa_topk
 
-constexpr int kTopkThreads = 512;
+constexpr int kTopkThreads = 512, kTopkWaves = kTopkThreads / 64;
+constexpr int kTopkCand = 1024;   // exact keys kept for the candidates sharing the boundary's top 16 bits
 
 // The bin holding the `need`-th largest element (1-based) of a histogram of
 // nb bins, and that element's rank inside the bin. Wave 0 computes it; the
 // caller synchronises afterwards.
 __device__ void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* lane_tot, uint32_t* result, int tid) {
   if (tid < 64) {
-    const int per = nb / 64, lo = tid * per;
+    const int per = nb >= 64 ? nb / 64 : 1, lo = tid * per, hi = min(nb, lo + per);
     uint32_t sum = 0;
-    for (int i = 0; i < per; ++i) sum += hist[lo + i];
+    for (int i = lo; i < hi; ++i) sum += hist[i];
     lane_tot[tid] = sum;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     __builtin_amdgcn_wave_barrier();
     uint32_t above = 0;  // elements in the bins of higher lanes
     for (int j = tid + 1; j < 64; ++j) above += lane_tot[j];
-    for (int i = per - 1; i >= 0; --i) {
-      const uint32_t c = hist[lo + i];
+    for (int i = hi - 1; i >= lo; --i) {
+      const uint32_t c = hist[i];
       if (above < need && need <= above + c) {
-        result[0] = static_cast<uint32_t>(lo + i);
+        result[0] = static_cast<uint32_t>(i);
         result[1] = need - above;
       }
       above += c;
@@ -194,13 +195,47 @@ __device__ void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* 
   }
 }
 
+// Exclusive prefix sum of v over the workgroup (thread order) and its total.
+// wsum: kTopkWaves words of LDS; synchronises once, and the caller must
+// synchronise again before wsum is reused.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total, int lane, int wave) {
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    if (w < wave) before += wsum[w];
+    tot += wsum[w];
+  }
+  *total = tot;
+  return before + x - v;
+}
+
+// Exact top-k of one row of indexer scores: the chosen tokens are the k
+// largest 64-bit keys (orderable score, complement of the token), so equal
+// scores go to the lower token. The top 16 bits of every key are kept in LDS
+// (the row is read from memory once, up to 65536 candidates); a 12-bit and a
+// 4-bit digit find the top-16-bit value P of the k-th key; the candidates
+// whose top 16 bits equal P (few, on these inputs) are re-read, ranked by a
+// sort of their exact keys and the chosen ones marked in a bitmap. With more
+// than kTopkCand such candidates (heavy ties), the remaining 48 key bits are
+// resolved by 8-bit digits instead. Then an ordered compaction writes the
+// chosen tokens ascending.
 __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
-  extern __shared__ __align__(16) uint32_t tk_lds[];
-  uint32_t* hist = tk_lds;           // 4096 bins
-  uint32_t* cache = tk_lds + 4096;   // orderable keys of the row's first topk_cache candidates
+  extern __shared__ __align__(16) unsigned char tk_lds[];
+  uint32_t* hist = reinterpret_cast<uint32_t*>(tk_lds);                 // 4096 bins; later the bitmap
+  uint64_t* cand = reinterpret_cast<uint64_t*>(tk_lds + 4096 * 4);     // kTopkCand exact keys
+  uint16_t* c16 = reinterpret_cast<uint16_t*>(tk_lds + 4096 * 4 + kTopkCand * 8);  // top 16 bits of each key
   __shared__ uint32_t lane_tot[64];
   __shared__ uint32_t res[2];
-  __shared__ uint32_t wcnt[2][2][kTopkThreads / 64];  // [round parity][greater, equal][wave]
+  __shared__ uint32_t wsum[kTopkWaves];
+  __shared__ uint32_t ncand;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x;
   const int b = static_cast<int>(row / a.L), t = static_cast<int>(row % a.L);
@@ -211,78 +246,166 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
     return;
   }
   const float* S = a.scores + score_row(a, b, t);
-  const int nc = min(n, a.topk_cache);
-  auto key_at = [&](int i) -> uint32_t { return i < nc ? cache[i] : orderable(S[i]); };
+  const int cap = a.topk_cache;   // c16 holds candidates [0, min(n, cap))
+  auto top16 = [&](int i) -> uint32_t { return i < cap ? c16[i] : (orderable(S[i]) >> 16); };
+  auto key64 = [&](int i) -> uint64_t {
+    return (static_cast<uint64_t>(orderable(S[i])) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(i));
+  };
 
-  // digit 1: bits 31..20
+  // digit 1 (bits 31..20): one read of the row, eight loads in flight per thread
   for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0u;
+  if (tid == 0) ncand = 0u;
   __syncthreads();
-  for (int i = tid; i < n; i += kTopkThreads) {
-    const uint32_t u = orderable(S[i]);
-    if (i < nc) cache[i] = u;
+  auto take = [&](int i, float x) {
+    const uint32_t u = orderable(x);
+    if (i < cap) c16[i] = static_cast<uint16_t>(u >> 16);
     atomicAdd(&hist[u >> 20], 1u);
+  };
+  // the row starts at an arbitrary float: a scalar head up to 16-byte
+  // alignment, then 16-byte loads (eight in flight per thread), a scalar tail
+  const int head = min(n, static_cast<int>((4 - ((reinterpret_cast<uintptr_t>(S) >> 2) & 3)) & 3));
+  if (tid < head) take(tid, S[tid]);
+  const int nv = (n - head) >> 2;   // whole float4s after the head
+  const f32x4* S4 = reinterpret_cast<const f32x4*>(S + head);
+  constexpr int UNR = 8;
+  for (int base = 0; base < nv; base += kTopkThreads * UNR) {
+    f32x4 v[UNR];
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int q4 = base + tid + kTopkThreads * j;
+      v[j] = q4 < nv ? S4[q4] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int q4 = base + tid + kTopkThreads * j;
+      if (q4 < nv) {
+        const int i = head + 4 * q4;
+        take(i, v[j].x);
+        take(i + 1, v[j].y);
+        take(i + 2, v[j].z);
+        take(i + 3, v[j].w);
+      }
+    }
   }
+  for (int i = head + 4 * nv + tid; i < n; i += kTopkThreads) take(i, S[i]);
   __syncthreads();
   find_bin(hist, 4096, static_cast<uint32_t>(k), lane_tot, res, tid);
   __syncthreads();
   const uint32_t d1 = res[0], need1 = res[1];
-  // digit 2: bits 19..8 of the keys in bin d1
-  for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0u;
+  // digit 2 (bits 19..16) among the keys of bin d1
+  if (tid < 16) hist[tid] = 0u;
   __syncthreads();
   for (int i = tid; i < n; i += kTopkThreads) {
-    const uint32_t u = key_at(i);
-    if ((u >> 20) == d1) atomicAdd(&hist[(u >> 8) & 0xFFFu], 1u);
+    const uint32_t c = top16(i);
+    if ((c >> 4) == d1) atomicAdd(&hist[c & 15u], 1u);
   }
   __syncthreads();
-  find_bin(hist, 4096, need1, lane_tot, res, tid);
+  find_bin(hist, 16, need1, lane_tot, res, tid);
   __syncthreads();
-  const uint32_t pre = (d1 << 12) | res[0], need2 = res[1];
-  // digit 3: bits 7..0 of the keys sharing the first 24 bits
-  for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0u;
-  __syncthreads();
-  for (int i = tid; i < n; i += kTopkThreads) {
-    const uint32_t u = key_at(i);
-    if ((u >> 8) == pre) atomicAdd(&hist[u & 0xFFu], 1u);
-  }
-  __syncthreads();
-  find_bin(hist, 256, need2, lane_tot, res, tid);
-  __syncthreads();
-  // the k-th largest key, and how many of the keys equal to it are taken
-  // (those of the lowest tokens: ties go to the lower token)
-  const uint32_t ustar = (pre << 8) | res[0], quota0 = res[1];
-
-  // ordered compaction in rounds of kTopkThreads candidates
-  uint32_t written = 0, ties_seen = 0;
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  for (int r0 = 0, par = 0; r0 < n; r0 += kTopkThreads, par ^= 1) {
-    const int i = r0 + tid;
-    const uint32_t u = i < n ? key_at(i) : 0u;
-    const bool gt = i < n && u > ustar, eq = i < n && u == ustar;
-    const uint64_t bg = __ballot(gt), be = __ballot(eq);
-    if (lane == 0) {
-      wcnt[par][0][wave] = static_cast<uint32_t>(__popcll(bg));
-      wcnt[par][1][wave] = static_cast<uint32_t>(__popcll(be));
+  const uint32_t P = (d1 << 4) | res[0];
+  uint32_t need = res[1];   // rank of the k-th key among the keys whose top 16 bits are P
+  // the candidates sharing P: their exact keys
+  for (int i = tid; i < n; i += kTopkThreads)
+    if (top16(i) == P) {
+      const uint32_t pos = atomicAdd(&ncand, 1u);
+      if (pos < static_cast<uint32_t>(kTopkCand)) cand[pos] = key64(i);
     }
+  __syncthreads();
+  const uint32_t nc = ncand;
+  uint64_t kth;   // the k-th largest key of the row
+  if (nc <= static_cast<uint32_t>(kTopkCand)) {
+    // bitonic sort of the candidates, descending (zero keys pad to a power of two)
+    int Pn = 1;
+    while (Pn < static_cast<int>(nc)) Pn <<= 1;
+    for (int i = static_cast<int>(nc) + tid; i < Pn; i += kTopkThreads) cand[i] = 0ull;
     __syncthreads();
-    uint32_t gt_before = static_cast<uint32_t>(__popcll(bg & below)), eq_before = static_cast<uint32_t>(__popcll(be & below));
-    uint32_t gt_tot = 0, eq_tot = 0;
-    for (int w = 0; w < kTopkThreads / 64; ++w) {
-      if (w < wave) {
-        gt_before += wcnt[par][0][w];
-        eq_before += wcnt[par][1][w];
+    for (int size = 2; size <= Pn; size <<= 1)
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < Pn / 2; i += kTopkThreads) {
+          const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
+          const bool desc = (lo & size) == 0;
+          const uint64_t x = cand[lo], y = cand[hi];
+          if ((x < y) == desc) {
+            cand[lo] = y;
+            cand[hi] = x;
+          }
+        }
+        __syncthreads();
       }
-      gt_tot += wcnt[par][0][w];
-      eq_tot += wcnt[par][1][w];
+    kth = cand[need - 1];
+  } else {
+    // heavy ties: resolve the remaining 48 bits of the key by 8-bit digits
+    uint64_t pre = P;   // the known high bits of the k-th key
+    for (int shift = 40; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0u;
+      __syncthreads();
+      for (int i = tid; i < n; i += kTopkThreads)
+        if (top16(i) == P) {
+          const uint64_t kk = key64(i);
+          if ((kk >> (shift + 8)) == pre) atomicAdd(&hist[(kk >> shift) & 0xFFu], 1u);
+        }
+      __syncthreads();
+      find_bin(hist, 256, need, lane_tot, res, tid);
+      __syncthreads();
+      pre = (pre << 8) | res[0];
+      need = res[1];
+      __syncthreads();
     }
-    const uint32_t quota = quota0 > ties_seen ? quota0 - ties_seen : 0u;  // ties still to take
-    const bool take = gt || (eq && eq_before < quota);
-    if (take) out[written + gt_before + min(eq_before, quota)] = i;
-    written += gt_tot + min(eq_tot, quota);
-    ties_seen += eq_tot;
+    kth = pre;
+  }
+  __syncthreads();
+  // bitmap (over the histogram) of the chosen candidates sharing P
+  uint32_t* bits = hist;
+  const int nwords = (n + 31) >> 5;
+  for (int i = tid; i < nwords; i += kTopkThreads) bits[i] = 0u;
+  __syncthreads();
+  if (nc <= static_cast<uint32_t>(kTopkCand)) {
+    for (int i = tid; i < static_cast<int>(nc); i += kTopkThreads) {
+      const uint64_t kk = cand[i];
+      if (kk >= kth) {
+        const uint32_t tok = 0xFFFFFFFFu - static_cast<uint32_t>(kk);
+        atomicOr(&bits[tok >> 5], 1u << (tok & 31));
+      }
+    }
+  } else {
+    for (int i = tid; i < n; i += kTopkThreads)
+      if (top16(i) == P && key64(i) >= kth) atomicOr(&bits[i >> 5], 1u << (i & 31));
+  }
+  __syncthreads();
+  // ordered compaction: chunks of 8 consecutive candidates per thread
+  uint32_t written = 0;
+  for (int c0 = 0; c0 < n; c0 += kTopkThreads * 8) {
+    const int i0 = c0 + 8 * tid;
+    uint32_t sel = 0;   // bit j: candidate i0 + j is chosen
+    if (i0 < n) {
+      uint16_t cc[8];
+      if (i0 + 8 <= min(n, cap)) {
+        const uint4 w4 = *reinterpret_cast<const uint4*>(c16 + i0);
+        const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cc[j] = static_cast<uint16_t>(ww[j >> 1] >> (16 * (j & 1)));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cc[j] = i0 + j < n ? static_cast<uint16_t>(top16(i0 + j)) : 0;
+      }
+      const uint32_t mb = (bits[i0 >> 5] >> (i0 & 31)) & 0xFFu;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (i0 + j < n && (cc[j] > P || (cc[j] == P && ((mb >> j) & 1u)))) sel |= 1u << j;
+    }
+    uint32_t tot;
+    uint32_t pos = written + block_excl_scan(static_cast<uint32_t>(__popc(sel)), wsum, &tot, lane, wave);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if ((sel >> j) & 1u) out[pos++] = i0 + j;
+    written += tot;
+    __syncthreads();
   }
 }
 
 // ------------------------------------------------------------------ k_dsa_attn
+
+constexpr int kAttnBufs = 3;   // LDS buffers of 32 K rows + 32 V rows per KV head
 
 template <class T, class O, int D, int WPG>
 __global__ __launch_bounds__(256) void k_dsa_attn(DsaArgs a) {
@@ -295,17 +418,19 @@ __global__ __launch_bounds__(256) void k_dsa_attn(DsaArgs a) {
   __shared__ int cnt_sh;
   __shared__ uint32_t wtot[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int NTH = 64 * a.waves;
-  const int64_t row = blockIdx.x;
+  const int NTH = 64 * a.wg_waves;
+  // workgroup (row, part): query token `row`, KV heads [part * gpw, part * gpw + gpw)
+  const int64_t row = blockIdx.x / a.parts;
+  const int part = static_cast<int>(blockIdx.x % a.parts);
   const int b = static_cast<int>(row / a.L), t = static_cast<int>(row % a.L);
   constexpr int wpg = WPG;                      // waves sharing one KV head (Hg / 16, or 1)
-  const int ngw = a.waves / wpg;                 // KV heads in the workgroup (= G)
-  const int gw = wave / wpg;
-  const int h0 = a.Hg >= 16 ? 16 * wave : gw * a.Hg;
+  const int gl = wave / wpg;                     // KV head of this wave within the workgroup
+  const int gw = part * a.gpw + gl;              // ... and in the layer
+  const int h0 = a.Hg >= 16 ? 16 * (part * a.wg_waves + wave) : gw * a.Hg;
   const int col = lane & 15, grp = lane >> 4;
   const bool colv = col < a.heads_per_wave;
-  S* gbuf = reinterpret_cast<S*>(at_lds) + static_cast<size_t>(gw) * 4 * HALF;   // [2 buffers][K, V^T]
-  int* list = reinterpret_cast<int*>(at_lds + static_cast<size_t>(ngw) * 4 * HALF * sizeof(S));
+  S* gbuf = reinterpret_cast<S*>(at_lds) + static_cast<size_t>(gl) * kAttnBufs * 2 * HALF;   // [buffers][K, V^T]
+  int* list = reinterpret_cast<int*>(at_lds + static_cast<size_t>(a.gpw) * kAttnBufs * 2 * HALF * sizeof(S));
   int P = 1;
   while (P < a.topk) P <<= 1;
   int* tmp = list + P;
@@ -355,7 +480,7 @@ __global__ __launch_bounds__(256) void k_dsa_attn(DsaArgs a) {
       if (lane == 0) wtot[wave] = static_cast<uint32_t>(__popcll(bal));
       __syncthreads();
       int before = __popcll(bal & below), tot = 0;
-      for (int w = 0; w < a.waves; ++w) {
+      for (int w = 0; w < a.wg_waves; ++w) {
         if (w < wave) before += static_cast<int>(wtot[w]);
         tot += static_cast<int>(wtot[w]);
       }
@@ -380,23 +505,27 @@ __global__ __launch_bounds__(256) void k_dsa_attn(DsaArgs a) {
   const S* K = static_cast<const S*>(a.k) + b * a.ks[0] + gw * a.ks[2];
   const S* V = static_cast<const S*>(a.v) + b * a.vs[0] + gw * a.vs[2];
   constexpr int MAXPER = (CH + 64 * WPG - 1) / (64 * WPG);   // chunks per staging thread
-  u32x4 rk[MAXPER], rv[MAXPER];
-  auto issue = [&](int step) {
+  // two register sets: the rows of step j travel in set j & 1, issued two
+  // steps before they are computed
+  u32x4 rk[2][MAXPER], rv[2][MAXPER];
+  auto issue = [&](int step, auto set_c) {
+    constexpr int set = decltype(set_c)::value;
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
       const int e = gt + gthreads * i;
-      rk[i] = rv[i] = u32x4{0u, 0u, 0u, 0u};
+      rk[set][i] = rv[set][i] = u32x4{0u, 0u, 0u, 0u};
       if (e < CH) {
         const int r = (e * EPC) / D, d = (e * EPC) % D, pos = 32 * step + r;
         if (pos < cnt) {
           const int64_t tok = list[pos];
-          rk[i] = *reinterpret_cast<const u32x4*>(K + tok * a.ks[1] + d);
-          rv[i] = *reinterpret_cast<const u32x4*>(V + tok * a.vs[1] + d);
+          rk[set][i] = *reinterpret_cast<const u32x4*>(K + tok * a.ks[1] + d);
+          rv[set][i] = *reinterpret_cast<const u32x4*>(V + tok * a.vs[1] + d);
         }
       }
     }
   };
-  auto commit = [&](int buf) {
+  auto commit = [&](int buf, auto set_c) {
+    constexpr int set = decltype(set_c)::value;
     S* kp = gbuf + buf * 2 * HALF;
     S* vp = kp + HALF;
 #pragma unroll
@@ -404,8 +533,8 @@ __global__ __launch_bounds__(256) void k_dsa_attn(DsaArgs a) {
       const int e = gt + gthreads * i;
       if (e < CH) {
         const int r = (e * EPC) / D, d = (e * EPC) % D;
-        *reinterpret_cast<u32x4*>(kp + ktile_off(r, d, D)) = rk[i];
-        const S* src = reinterpret_cast<const S*>(&rv[i]);
+        *reinterpret_cast<u32x4*>(kp + ktile_off(r, d, D)) = rk[set][i];
+        const S* src = reinterpret_cast<const S*>(&rv[set][i]);
 #pragma unroll
         for (int j = 0; j < EPC; ++j) vp[vhalf_off(r, d + j)] = src[j];
       }
@@ -418,15 +547,18 @@ __global__ __launch_bounds__(256) void k_dsa_attn(DsaArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nsteps = (cnt + 31) >> 5;
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
   if (nsteps > 0) {
-    issue(0);
-    commit(0);
+    issue(0, Set0{});
+    commit(0, Set0{});
+    if (nsteps > 1) issue(1, Set1{});
+    if (nsteps > 2) issue(2, Set0{});
     __syncthreads();
   }
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) issue(step + 1);
+  // one step; `next_c` is the register set of step + 1 (a constant: the loop runs steps in pairs)
+  auto run_step = [&](int step, auto next_c) __attribute__((always_inline)) {
+    const int buf = step % kAttnBufs;
     const S* kp = gbuf + buf * 2 * HALF;
     const S* vp = kp + HALF;
     f32x4 st[2];
@@ -444,8 +576,16 @@ __global__ __launch_bounds__(256) void k_dsa_attn(DsaArgs a) {
       online_step<T, DT, false>(st, 32 * step, 0, 0, grp, sl2, m, l, acc, vf);
     else
       online_step<T, DT, true>(st, 32 * step, 0, cnt - 1, grp, sl2, m, l, acc, vf);
-    if (more) commit(buf ^ 1);
+    // step + 1's rows into the buffer last read at step - 2; then step + 3's loads
+    if (step + 1 < nsteps) {
+      commit((step + 1) % kAttnBufs, next_c);
+      if (step + 3 < nsteps) issue(step + 3, next_c);
+    }
     __syncthreads();
+  };
+  for (int step = 0; step < nsteps; step += 2) {
+    run_step(step, Set1{});
+    if (step + 1 < nsteps) run_step(step + 1, Set0{});
   }
 
   const float lt = col_sum4(l);
@@ -475,7 +615,7 @@ hipError_t launch_dsa_t(const DsaArgs& a, hipStream_t st, hipEvent_t* ev) {
                      : wpg == 3 ? reinterpret_cast<const void*>(&k_dsa_attn<T, O, D, 3>)
                                 : reinterpret_cast<const void*>(&k_dsa_attn<T, O, D, 4>);
   const void* topk = reinterpret_cast<const void*>(&k_dsa_topk);
-  const size_t attn_lds = dsa_attn_lds_bytes(a.waves / wpg, D, kBf16, a.topk);
+  const size_t attn_lds = dsa_attn_lds_bytes(a.gpw, D, kBf16, a.topk);
   const size_t topk_lds = dsa_topk_lds_bytes(a.topk_cache);
   hipError_t e;
   if ((e = hipFuncSetAttribute(attn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(attn_lds))) !=
@@ -492,7 +632,7 @@ hipError_t launch_dsa_t(const DsaArgs& a, hipStream_t st, hipEvent_t* ev) {
   if ((e = record(ev, 1, st)) != hipSuccess) return e;
   if (!a.inject && (e = launch_one(topk, dim3(rows), dim3(kTopkThreads), topk_lds, st, a)) != hipSuccess) return e;
   if ((e = record(ev, 2, st)) != hipSuccess) return e;
-  if ((e = launch_one(attn, dim3(rows), dim3(64 * a.waves), attn_lds, st, a)) != hipSuccess) return e;
+  if ((e = launch_one(attn, dim3(rows * a.parts), dim3(64 * a.wg_waves), attn_lds, st, a)) != hipSuccess) return e;
   if ((e = record(ev, 3, st)) != hipSuccess) return e;
   return hipGetLastError();
 }
@@ -505,12 +645,15 @@ hipError_t launch_dsa_o(const DsaArgs& a, hipStream_t st, hipEvent_t* ev) {
 
 }  // namespace
 
-size_t dsa_topk_lds_bytes(int cache) { return (4096 + static_cast<size_t>(cache)) * sizeof(uint32_t); }
+size_t dsa_topk_lds_bytes(int cache) {
+  return 4096 * sizeof(uint32_t) + kTopkCand * sizeof(uint64_t) + static_cast<size_t>(cache) * sizeof(uint16_t);
+}
 
 size_t dsa_attn_lds_bytes(int groups_per_wg, int D, bool bf16, int k) {
   int P = 1;
   while (P < k) P <<= 1;
-  return static_cast<size_t>(groups_per_wg) * 4 * 32 * D * (bf16 ? 2 : 4) + 2 * static_cast<size_t>(P) * sizeof(int);
+  return static_cast<size_t>(groups_per_wg) * kAttnBufs * 2 * 32 * D * (bf16 ? 2 : 4) +
+         2 * static_cast<size_t>(P) * sizeof(int);
 }
 
 hipError_t launch_dsa(const DsaArgs& a, bool in_bf16, bool out_bf16, hipStream_t st, hipEvent_t* ev) {

@@ -146,8 +146,11 @@ namespace nsa {
 // its three kernels.
 struct DsaArgs {
   int B, L, Hq, G, Hg, D, Hi, Di, topk;
-  int waves;        // attention waves per workgroup: 16 query heads each
+  int waves;        // attention waves per query token: 16 query heads each
   int heads_per_wave;  // min(Hg, 16)
+  int parts;        // attention workgroups per query token (each takes gpw KV heads)
+  int gpw;          // KV heads staged per attention workgroup
+  int wg_waves;     // waves per attention workgroup
   int idx_tiles;    // indexer workgroups per sequence (16 query tokens each)
   int topk_cache;   // orderable keys of a row kept in LDS by the top-k kernel
   float scale_log2; // softmax scale * log2(e)
