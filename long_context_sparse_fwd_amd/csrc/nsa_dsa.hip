@@ -53,15 +53,95 @@ __device__ __forceinline__ int64_t score_row(const DsaArgs& a, int b, int t) {
 }
 
 // A 32-key piece of V^T in the A-operand order of the P.V product: the
-// fragment of d-tile dt for lane l is 8 contiguous elements at (dt*64 + l)*8
-// holding V[kappa(l/16, j)][16 dt + l%16] (kappa as for the 64-key V^T tiles:
-// the keys whose probabilities lane l holds after the S^T product).
+// fragment of d-tile dt for lane l is 8 contiguous elements holding
+// V[kappa(l/16, j)][16 dt + l%16] (kappa as for the 64-key V^T tiles: the keys
+// whose probabilities lane l holds after the S^T product), in 16-byte slot
+// dt*64 + 16 (l/16) + ((l%16) ^ (dt%8)): the XOR spreads a staging write of
+// 16 lanes (one dim octet pair over eight d-tiles) over 16 bank groups.
+__device__ __forceinline__ int vhalf_frag(int dt, int lane) {
+  return (dt * 64 + 16 * (lane >> 4) + ((lane & 15) ^ (dt & 7))) * 8;
+}
 __device__ __forceinline__ int vhalf_off(int r, int d) {
   const int half = r >> 4, a = (r & 15) >> 2, i = r & 3;
-  const int lane = (d & 15) + 16 * a;
-  return ((d >> 4) * 64 + lane) * 8 + 4 * half + i;
+  return vhalf_frag(d >> 4, (d & 15) + 16 * a) + 4 * half + i;
 }
-__device__ __forceinline__ int vhalf_frag(int dt, int lane) { return (dt * 64 + lane) * 8; }
+
+// K tiles of the bf16 kernels: the fragment-major layout of ktile_off with
+// the 16-byte slots of each fragment XOR-swizzled, slot (r & 15) ^ m + 16 (m & 3)
+// for key r and dim octet m = d / 8. A staging write of 16 lanes (one key,
+// octets 0..15) then covers 16 distinct bank groups, and a fragment read of
+// 16 lanes a permutation of 16 consecutive slots.
+template <class T>
+__device__ __forceinline__ int kchunk_off(int r, int d, int D) {
+  if constexpr (sizeof(typename T::storage) == 2) {
+    const int m = (d >> 3) & 15;
+    return (((r >> 4) * (D >> 5) + (d >> 5)) * 64 + (((r & 15) ^ m) + 16 * (m & 3))) * 8;
+  } else {
+    return ktile_off(r, d, D);
+  }
+}
+template <class T>
+__device__ __forceinline__ int kfrag_off(int kt, int s, int lane, int D) {
+  if constexpr (sizeof(typename T::storage) == 2) {
+    const int m = (4 * s + (lane >> 4)) & 15;
+    return ((kt * (D >> 5) + s) * 64 + (((lane & 15) ^ m) + 16 * (lane >> 4))) * 8;
+  } else {
+    return ktile_frag(kt, s, lane, D);
+  }
+}
+
+// Staging position of 16-byte chunk e (8 elements of one key row) of a
+// 32-key bf16 piece in the transposing order, D = 8 * NM with NM in {8, 16}:
+// bits 0-3 of e (mlo) and 4-5 (i) come from the lane, the rest from the wave
+// and slot; the chunk holds key 16h + 4a + i, dims 8m .. 8m + 7, with
+// m = mlo % NM and (h, a) from the remaining bits. So the four lanes l, l^16,
+// l^32, l^48 hold keys 4a + {0..3} of one dim octet and, in the chunk CH/2
+// later, keys 16 + 4a + {0..3}: the eight keys of one V^T fragment.
+template <int D>
+__device__ __forceinline__ void stage_pos(int e, int& r, int& d) {
+  constexpr int NM = D / 8;
+  static_assert(NM == 8 || NM == 16, "head dims 64 and 128");
+  const int mlo = e & 15, i = (e >> 4) & 3, rest = e >> 6;
+  int a, h;
+  if constexpr (NM == 16) {
+    a = rest & 3;
+    h = rest >> 2;
+  } else {
+    a = 2 * (rest & 1) + (mlo >> 3);
+    h = rest >> 1;
+  }
+  r = 16 * h + 4 * a + i;
+  d = 8 * (mlo % NM);
+}
+
+// v_permlane32_swap / v_permlane16_swap on a pair of registers: the upper
+// 32 lanes of p trade with the lower 32 of q; odd 16-lane rows of p with even
+// rows of q.
+__device__ __forceinline__ void swap32(uint32_t& p, uint32_t& q) {
+  const auto r = __builtin_amdgcn_permlane32_swap(p, q, false, false);
+  p = r[0];
+  q = r[1];
+}
+__device__ __forceinline__ void swap16(uint32_t& p, uint32_t& q) {
+  const auto r = __builtin_amdgcn_permlane16_swap(p, q, false, false);
+  p = r[0];
+  q = r[1];
+}
+
+// Four lanes l + 16 i (i = 0..3) each hold dwords D[0..3] of one key row
+// (keys 4a + i, dims 8m .. 8m + 7); afterwards lane i holds in F[j] dword i of
+// lane j's row, i.e. dims 8m + 2i and 8m + 2i + 1 of key 4a + j.
+__device__ __forceinline__ void transpose4x4(const u32x4& x, uint32_t F[4]) {
+  uint32_t p0 = x[0], p1 = x[1], q0 = x[2], q1 = x[3];
+  swap32(p0, q0);  // p: rows of lanes with i < 2, q: of lanes with i >= 2; dwords 2 (i >> 1) + {0, 1}
+  swap32(p1, q1);
+  swap16(p0, p1);  // p0 from i = 0, p1 from i = 1, dword i of the source
+  swap16(q0, q1);
+  F[0] = p0;
+  F[1] = p1;
+  F[2] = q0;
+  F[3] = q1;
+}
 
 // Unsigned key that orders like the float (larger float -> larger key).
 __device__ __forceinline__ uint32_t orderable(float f) {
@@ -126,7 +206,7 @@ __global__ __launch_bounds__(512) void k_dsa_index(DsaArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = tid + NT * i, r = (e * EPC) / DI, d = (e * EPC) % DI;
-      *reinterpret_cast<u32x4*>(&stage[buf][ktile_off(r, d, DI)]) = reg[i];
+      *reinterpret_cast<u32x4*>(&stage[buf][kchunk_off<T>(r, d, DI)]) = reg[i];
     }
   };
   const int nch = (Tl >> 6) + 1;
@@ -145,7 +225,7 @@ __global__ __launch_bounds__(512) void k_dsa_index(DsaArgs a) {
     for (int kt = 0; kt < 4; ++kt) {
       Frag<T> kf[KS];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kf[s] = frag_load<T>(&stage[buf][ktile_frag(kt, s, lane, DI)]);
+      for (int s = 0; s < KS; ++s) kf[s] = frag_load<T>(&stage[buf][kfrag_off<T>(kt, s, lane, DI)]);
       const int key = 64 * c + 16 * kt + col;
 #pragma unroll
       for (int qt = 0; qt < kIdxTPW; ++qt) {
@@ -171,30 +251,6 @@ __global__ __launch_bounds__(512) void k_dsa_index(DsaArgs a) {
 constexpr int kTopkThreads = 512, kTopkWaves = kTopkThreads / 64;
 constexpr int kTopkCand = 1024;   // exact keys kept for the candidates sharing the boundary's top 16 bits
 
-// The bin holding the `need`-th largest element (1-based) of a histogram of
-// nb bins, and that element's rank inside the bin. Wave 0 computes it; the
-// caller synchronises afterwards.
-__device__ void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* lane_tot, uint32_t* result, int tid) {
-  if (tid < 64) {
-    const int per = nb >= 64 ? nb / 64 : 1, lo = tid * per, hi = min(nb, lo + per);
-    uint32_t sum = 0;
-    for (int i = lo; i < hi; ++i) sum += hist[i];
-    lane_tot[tid] = sum;
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    uint32_t above = 0;  // elements in the bins of higher lanes
-    for (int j = tid + 1; j < 64; ++j) above += lane_tot[j];
-    for (int i = hi - 1; i >= lo; --i) {
-      const uint32_t c = hist[i];
-      if (above < need && need <= above + c) {
-        result[0] = static_cast<uint32_t>(i);
-        result[1] = need - above;
-      }
-      above += c;
-    }
-  }
-}
-
 // Exclusive prefix sum of v over the workgroup (thread order) and its total.
 // wsum: kTopkWaves words of LDS; synchronises once, and the caller must
 // synchronise again before wsum is reused.
@@ -217,6 +273,40 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
   return before + x - v;
 }
 
+// The bin holding the `need`-th largest element (1-based) of a histogram of
+// nb bins (nb <= 8 * kTopkThreads, a multiple of 8 when above kTopkThreads),
+// and that element's rank inside the bin, found by the whole workgroup:
+// thread i sums the bins of slice kTopkThreads - 1 - i (thread 0 the highest
+// bins), an exclusive scan gives the count above each slice, and the thread
+// whose slice holds the element writes result[0..1]. The caller synchronises
+// before reading result or reusing wsum.
+__device__ void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* wsum, uint32_t* result, int tid,
+                         int lane, int wave) {
+  const int per = nb > kTopkThreads ? nb / kTopkThreads : 1;
+  const int lo = (kTopkThreads - 1 - tid) * per, hi = min(nb, lo + per);
+  uint32_t c[8];
+  uint32_t sum = 0;
+  if (per == 8) {
+    const uint4 x = *reinterpret_cast<const uint4*>(hist + lo), y = *reinterpret_cast<const uint4*>(hist + lo + 4);
+    c[0] = x.x, c[1] = x.y, c[2] = x.z, c[3] = x.w, c[4] = y.x, c[5] = y.y, c[6] = y.z, c[7] = y.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = lo + j < hi ? hist[lo + j] : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sum += c[j];
+  uint32_t tot;
+  uint32_t above = block_excl_scan(sum, wsum, &tot, lane, wave);
+#pragma unroll
+  for (int j = 7; j >= 0; --j) {
+    if (lo + j < hi && above < need && need <= above + c[j]) {
+      result[0] = static_cast<uint32_t>(lo + j);
+      result[1] = need - above;
+    }
+    above += c[j];
+  }
+}
+
 // Exact top-k of one row of indexer scores: the chosen tokens are the k
 // largest 64-bit keys (orderable score, complement of the token), so equal
 // scores go to the lower token. The top 16 bits of every key are kept in LDS
@@ -232,7 +322,6 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
   uint32_t* hist = reinterpret_cast<uint32_t*>(tk_lds);                 // 4096 bins; later the bitmap
   uint64_t* cand = reinterpret_cast<uint64_t*>(tk_lds + 4096 * 4);     // kTopkCand exact keys
   uint16_t* c16 = reinterpret_cast<uint16_t*>(tk_lds + 4096 * 4 + kTopkCand * 8);  // top 16 bits of each key
-  __shared__ uint32_t lane_tot[64];
   __shared__ uint32_t res[2];
   __shared__ uint32_t wsum[kTopkWaves];
   __shared__ uint32_t ncand;
@@ -289,27 +378,38 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
   }
   for (int i = head + 4 * nv + tid; i < n; i += kTopkThreads) take(i, S[i]);
   __syncthreads();
-  find_bin(hist, 4096, static_cast<uint32_t>(k), lane_tot, res, tid);
+  find_bin(hist, 4096, static_cast<uint32_t>(k), wsum, res, tid, lane, wave);
   __syncthreads();
   const uint32_t d1 = res[0], need1 = res[1];
+  // passes over the cached top 16 bits, eight keys (one 16-byte word) at a time
+  const int nq = min(n, cap) >> 3;   // whole words in the cache
+  auto for_top16 = [&](auto&& f) {
+    for (int q = tid; q < nq; q += kTopkThreads) {
+      const uint4 w4 = *reinterpret_cast<const uint4*>(c16 + 8 * q);
+      const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f(8 * q + j, (ww[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+    }
+    for (int i = 8 * nq + tid; i < n; i += kTopkThreads) f(i, top16(i));
+  };
   // digit 2 (bits 19..16) among the keys of bin d1
   if (tid < 16) hist[tid] = 0u;
   __syncthreads();
-  for (int i = tid; i < n; i += kTopkThreads) {
-    const uint32_t c = top16(i);
+  for_top16([&](int, uint32_t c) {
     if ((c >> 4) == d1) atomicAdd(&hist[c & 15u], 1u);
-  }
+  });
   __syncthreads();
-  find_bin(hist, 16, need1, lane_tot, res, tid);
+  find_bin(hist, 16, need1, wsum, res, tid, lane, wave);
   __syncthreads();
   const uint32_t P = (d1 << 4) | res[0];
   uint32_t need = res[1];   // rank of the k-th key among the keys whose top 16 bits are P
   // the candidates sharing P: their exact keys
-  for (int i = tid; i < n; i += kTopkThreads)
-    if (top16(i) == P) {
+  for_top16([&](int i, uint32_t c) {
+    if (c == P) {
       const uint32_t pos = atomicAdd(&ncand, 1u);
       if (pos < static_cast<uint32_t>(kTopkCand)) cand[pos] = key64(i);
     }
+  });
   __syncthreads();
   const uint32_t nc = ncand;
   uint64_t kth;   // the k-th largest key of the row
@@ -345,7 +445,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
           if ((kk >> (shift + 8)) == pre) atomicAdd(&hist[(kk >> shift) & 0xFFu], 1u);
         }
       __syncthreads();
-      find_bin(hist, 256, need, lane_tot, res, tid);
+      find_bin(hist, 256, need, wsum, res, tid, lane, wave);
       __syncthreads();
       pre = (pre << 8) | res[0];
       need = res[1];
@@ -372,11 +472,12 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
       if (top16(i) == P && key64(i) >= kth) atomicOr(&bits[i >> 5], 1u << (i & 31));
   }
   __syncthreads();
-  // ordered compaction: chunks of 8 consecutive candidates per thread
-  uint32_t written = 0;
-  for (int c0 = 0; c0 < n; c0 += kTopkThreads * 8) {
-    const int i0 = c0 + 8 * tid;
-    uint32_t sel = 0;   // bit j: candidate i0 + j is chosen
+  // ordered compaction: wave w takes the candidates [w * span, (w + 1) * span),
+  // eight consecutive ones per lane and round; one workgroup scan of the wave
+  // counts, then wave-level prefix sums
+  const int span = ((n + 8 * kTopkThreads - 1) / (8 * kTopkThreads)) * 512;
+  auto chosen8 = [&](int i0) -> uint32_t {   // bit j: candidate i0 + j is chosen
+    uint32_t sel = 0;
     if (i0 < n) {
       uint16_t cc[8];
       if (i0 + 8 <= min(n, cap)) {
@@ -393,13 +494,33 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
       for (int j = 0; j < 8; ++j)
         if (i0 + j < n && (cc[j] > P || (cc[j] == P && ((mb >> j) & 1u)))) sel |= 1u << j;
     }
-    uint32_t tot;
-    uint32_t pos = written + block_excl_scan(static_cast<uint32_t>(__popc(sel)), wsum, &tot, lane, wave);
+    return sel;
+  };
+  const int w0 = wave * span, w1 = min(n, w0 + span);
+  uint32_t cnt = 0;
+  for (int i0 = w0 + 8 * lane; i0 < w1; i0 += 512) cnt += static_cast<uint32_t>(__popc(chosen8(i0)));
+  uint32_t tot;
+  // the scan at lane 0 of a wave counts the chosen candidates of the lower waves
+  uint32_t pos = __shfl(block_excl_scan(cnt, wsum, &tot, lane, wave), 0, 64);
+  for (int r0 = w0; r0 < w1; r0 += 512) {
+    const int i0 = r0 + 8 * lane;
+    const uint32_t sel = i0 < w1 ? chosen8(i0) : 0u;
+    const uint32_t c = static_cast<uint32_t>(__popc(sel));
+    // inclusive prefix over the lanes of this round
+    uint32_t x = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    uint32_t p = pos + x - c;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if ((sel >> j) & 1u) out[pos++] = i0 + j;
-    written += tot;
-    __syncthreads();
+      if ((sel >> j) & 1u) {
+        if (p < static_cast<uint32_t>(k)) out[p] = i0 + j;   // exactly k are chosen; the test only bounds the store
+        ++p;
+      }
+    pos += __shfl(x, 63, 64);
   }
 }
 
@@ -408,7 +529,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
 constexpr int kAttnBufs = 3;   // LDS buffers of 32 K rows + 32 V rows per KV head
 
 template <class T, class O, int D, int WPG>
-__global__ __launch_bounds__(256) void k_dsa_attn(DsaArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(typename T::storage) == 2 ? 2 : 1))) void
+k_dsa_attn(DsaArgs a) {
   using S = typename T::storage;
   using SO = typename O::storage;
   constexpr int KS = D / 32, DT = D / 16, HALF = 32 * D;   // elements of a 32-key K piece or V^T piece
@@ -505,6 +627,19 @@ __global__ __launch_bounds__(256) void k_dsa_attn(DsaArgs a) {
   const S* K = static_cast<const S*>(a.k) + b * a.ks[0] + gw * a.ks[2];
   const S* V = static_cast<const S*>(a.v) + b * a.vs[0] + gw * a.vs[2];
   constexpr int MAXPER = (CH + 64 * WPG - 1) / (64 * WPG);   // chunks per staging thread
+  // bf16 with an even number of chunks per thread: V^T fragments are made in
+  // registers (a 4 x 4 dword transpose over lanes l + 16 i, then half-word
+  // packing) and stored with one 16-byte write each; otherwise V is written
+  // element by element
+  constexpr bool TR = EPC == 8 && CH % (128 * WPG) == 0;
+  auto pos_of = [&](int e, int& r, int& d) {
+    if constexpr (TR) {
+      stage_pos<D>(e, r, d);
+    } else {
+      r = (e * EPC) / D;
+      d = (e * EPC) % D;
+    }
+  };
   // two register sets: the rows of step j travel in set j & 1, issued two
   // steps before they are computed
   u32x4 rk[2][MAXPER], rv[2][MAXPER];
@@ -515,7 +650,9 @@ __global__ __launch_bounds__(256) void k_dsa_attn(DsaArgs a) {
       const int e = gt + gthreads * i;
       rk[set][i] = rv[set][i] = u32x4{0u, 0u, 0u, 0u};
       if (e < CH) {
-        const int r = (e * EPC) / D, d = (e * EPC) % D, pos = 32 * step + r;
+        int r, d;
+        pos_of(e, r, d);
+        const int pos = 32 * step + r;
         if (pos < cnt) {
           const int64_t tok = list[pos];
           rk[set][i] = *reinterpret_cast<const u32x4*>(K + tok * a.ks[1] + d);
@@ -532,11 +669,39 @@ __global__ __launch_bounds__(256) void k_dsa_attn(DsaArgs a) {
     for (int i = 0; i < MAXPER; ++i) {
       const int e = gt + gthreads * i;
       if (e < CH) {
-        const int r = (e * EPC) / D, d = (e * EPC) % D;
-        *reinterpret_cast<u32x4*>(kp + ktile_off(r, d, D)) = rk[set][i];
-        const S* src = reinterpret_cast<const S*>(&rv[set][i]);
+        int r, d;
+        pos_of(e, r, d);
+        *reinterpret_cast<u32x4*>(kp + kchunk_off<T>(r, d, D)) = rk[set][i];
+        if constexpr (!TR) {
+          const S* src = reinterpret_cast<const S*>(&rv[set][i]);
 #pragma unroll
-        for (int j = 0; j < EPC; ++j) vp[vhalf_off(r, d + j)] = src[j];
+          for (int j = 0; j < EPC; ++j) vp[vhalf_off(r, d + j)] = src[j];
+        }
+      }
+    }
+    if constexpr (TR) {
+      // slot i holds key 4a + i' (i' = lane / 16) and slot i + MAXPER / 2 key
+      // 16 + 4a + i', dims 8m .. 8m + 7; lane i' ends with the fragments of
+      // dims 8m + 2i' and 8m + 2i' + 1 (keys 4a + {0..3}, 16 + 4a + {0..3})
+#pragma unroll
+      for (int i = 0; i < MAXPER / 2; ++i) {
+        const int e = gt + gthreads * i;
+        int r, d;
+        pos_of(e, r, d);
+        uint32_t F0[4], F1[4];
+        transpose4x4(rv[set][i], F0);
+        transpose4x4(rv[set][i + MAXPER / 2], F1);
+        const int ag = (r & 15) >> 2, dim = d + 2 * (lane >> 4);
+        u32x4 lo, hi;   // fragments of dims `dim` (low halves) and `dim + 1` (high halves)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          lo[q] = (F0[2 * q] & 0xFFFFu) | (F0[2 * q + 1] << 16);
+          hi[q] = (F0[2 * q] >> 16) | (F0[2 * q + 1] & 0xFFFF0000u);
+          lo[2 + q] = (F1[2 * q] & 0xFFFFu) | (F1[2 * q + 1] << 16);
+          hi[2 + q] = (F1[2 * q] >> 16) | (F1[2 * q + 1] & 0xFFFF0000u);
+        }
+        *reinterpret_cast<u32x4*>(vp + vhalf_frag(dim >> 4, (dim & 15) + 16 * ag)) = lo;
+        *reinterpret_cast<u32x4*>(vp + vhalf_frag(dim >> 4, ((dim + 1) & 15) + 16 * ag)) = hi;
       }
     }
   };
@@ -566,7 +731,7 @@ __global__ __launch_bounds__(256) void k_dsa_attn(DsaArgs a) {
     for (int h2 = 0; h2 < 2; ++h2) {
       st[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) mma(st[h2], frag_load<T>(kp + ktile_frag(h2, s, lane, D)), qf[s]);
+      for (int s = 0; s < KS; ++s) mma(st[h2], frag_load<T>(kp + kfrag_off<T>(h2, s, lane, D)), qf[s]);
     }
     Frag<T> vf[DT];
 #pragma unroll
