@@ -148,7 +148,7 @@ nsa_status_t check_ptr(const char* name, const void* p, bool need16) {
 // ------------------------------------------------------------------ prefill
 
 struct PrefillPlan {
-  int Nb, Nc, NcT, cmp_waves, cmp_lo_lds, cmp_tiles, sel_tiles;
+  int Nb, Nc, NcT, cmp_waves, cmp_lo_lds, cmp_tiles, sel_tiles, sel_pf;
   size_t off_kt, off_vt, off_kct, off_kclt, off_vct, off_idx, off_part, off_gates, total;
 };
 
@@ -196,8 +196,12 @@ nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, Pr
   if (pl->cmp_waves == 0)
     return fail(NSA_ERR_UNSUPPORTED, "seqlen %lld needs more LDS for block scores than a CU has",
                 static_cast<long long>(L));
-  if (nsa::sel_lds_bytes(pl->Nb, static_cast<int>(D), d->in_dtype == NSA_BF16) +
-          nsa::sel_static_lds_bytes(static_cast<int>(D), d->in_dtype == NSA_BF16) >
+  const size_t sel_stat = nsa::sel_static_lds_bytes(static_cast<int>(D), d->in_dtype == NSA_BF16);
+  pl->sel_pf = nsa::sel_lds_bytes(pl->Nb, static_cast<int>(D), d->in_dtype == NSA_BF16, true) + sel_stat <=
+                       static_cast<size_t>(nsa::kMaxLds)
+                   ? 1
+                   : 0;
+  if (nsa::sel_lds_bytes(pl->Nb, static_cast<int>(D), d->in_dtype == NSA_BF16, false) + sel_stat >
       static_cast<size_t>(nsa::kMaxLds))
     return fail(NSA_ERR_UNSUPPORTED, "seqlen %lld needs more LDS for the selection lists than a CU has",
                 static_cast<long long>(L));
@@ -489,6 +493,7 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
   a.cmp_tiles = pl.cmp_tiles;
   a.sel_tiles = pl.sel_tiles;
   a.sel_bm_words = nsa::sel_bm_words(pl.Nb);
+  a.sel_pf = pl.sel_pf;
   a.scale_log2 = scale_log2(params, a.D);
   a.inject = idx_mode == NSA_IDX_INJECT ? 1 : 0;
   a.q = q;

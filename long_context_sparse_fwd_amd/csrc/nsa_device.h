@@ -255,6 +255,14 @@ __device__ __forceinline__ float col_sum4(float v) {
   return v + xor32_f(v);
 }
 
+// Direct global-to-LDS copy, 16 bytes per active lane: lane l's bytes land
+// at lds + 16 l (lds must be the same in every lane). Tracked by vmcnt like a
+// load; the compiler waits for it before the wave's next LDS read unless an
+// explicit wait covers it first.
+__device__ __forceinline__ void lds_copy16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
 // Orders this wave's LDS accesses before the following ones.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");

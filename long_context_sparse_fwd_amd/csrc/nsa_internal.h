@@ -57,6 +57,7 @@ struct PrefillArgs {
   int cmp_waves, cmp_tiles, sel_tiles;
   int cmp_lo_lds;  // compressed kernel stages the low parts of the K means in LDS (8 waves only)
   int sel_bm_words;  // words of a k_sel wave's half-block bitmap (one byte per half block)
+  int sel_pf;        // k_sel prefetches the rows its epilogue adds to into LDS (1) or reads them at the end (0)
   float scale_log2;  // softmax scale * log2(e)
   int inject;        // 1: idx holds the selection; 0: compute it into idx
   const void* q;
@@ -125,7 +126,10 @@ constexpr int kMaxSelTokens = 64 * 64;
 // k_sel: bitmap words per wave (one byte per half block of Nb blocks, padded
 // to 16 bytes) and the dynamic LDS of a launch.
 inline int sel_bm_words(int Nb) { return (2 * Nb + 15) / 16 * 4; }
-size_t sel_lds_bytes(int Nb, int D, bool bf16);
+// k_sel's prefetch region: per wave the fp32 rows (kSelTPW tokens x 16 heads
+// x D) that its epilogue adds the selected branch to
+inline size_t sel_pf_bytes(int D) { return 4 * static_cast<size_t>(kSelTPW) * 16 * D * sizeof(float); }
+size_t sel_lds_bytes(int Nb, int D, bool bf16, bool prefetch);
 // static LDS of k_sel (query fragments of 4 waves)
 inline size_t sel_static_lds_bytes(int D, bool bf16) {
   return 4 * static_cast<size_t>(kSelTPW) * (D / 32) * (bf16 ? 16 : 32) * 64;

@@ -112,6 +112,16 @@ __device__ __forceinline__ float gate_of(const PrefillArgs& a, int b, int row, i
   return to_f32<T>(GT[b * a.gs[0] + static_cast<int64_t>(row) * a.gs[1] + h * a.gs[2] + c]);
 }
 
+// A fragment read from p where ok, zeros elsewhere. p must be readable in
+// every lane (callers clamp the indices), so the read is unconditional: the
+// reads of a loop then stay in flight together instead of each sitting in a
+// branch of its own that the compiler waits on.
+template <class T>
+__device__ __forceinline__ Frag<T> frag_load_if(const typename T::storage* p, bool ok) {
+  const Frag<T> f = frag_load<T>(p);
+  return ok ? f : frag_zero<T>();
+}
+
 // Element j (0..7) of a fragment.
 template <class T>
 __device__ __forceinline__ float frag_elem(const Frag<T>& f, int j);
@@ -420,15 +430,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   Frag<T> qf[TPW][KS];
   float gcmp[TPW], gwin[TPW];
   int nvis[TPW];
+  // reads at clamped (token, head) indices, zeroed where not valid
+  const S* Qc = static_cast<const S*>(a.q) + b * a.qs[0] + (colv ? h : g * a.Hg) * a.qs[2] + 8 * grp;
 #pragma unroll
   for (int qt = 0; qt < TPW; ++qt) {
-    const int t = tw + qt;
+    const int t = tw + qt, tc = min(t, Le - 1);
     const bool valid = t < Le && colv;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      qf[qt][s] = valid ? frag_load<T>(Q + static_cast<int64_t>(t - t0q) * a.qs[1] + 32 * s) : frag_zero<T>();
-    gcmp[qt] = valid ? gate_of<T>(a, b, t - t0q, h, 0) : 0.f;
-    gwin[qt] = valid ? gate_of<T>(a, b, t - t0q, h, 2) : 0.f;
+      qf[qt][s] = frag_load_if<T>(Qc + static_cast<int64_t>(tc - t0q) * a.qs[1] + 32 * s, valid);
+  }
+#pragma unroll
+  for (int qt = 0; qt < TPW; ++qt) {
+    const int t = tw + qt, tc = min(t, Le - 1);
+    const bool valid = t < Le && colv;
+    const float gc = gate_of<T>(a, b, tc - t0q, colv ? h : g * a.Hg, 0);
+    const float gw = gate_of<T>(a, b, tc - t0q, colv ? h : g * a.Hg, 2);
+    gcmp[qt] = valid ? gc : 0.f;
+    gwin[qt] = valid ? gw : 0.f;
     nvis[qt] = t < Le ? nvis_of(a, t) : 0;
   }
   f32x4 oacc[TPW][DT];
@@ -773,7 +792,7 @@ __device__ __forceinline__ void half_attend(const HalfBlock<T, D>& hb, const Fra
 // stay closer together in L2. The steps stream through a ring of kSelRing
 // half-block register buffers; each step runs the online-softmax update of
 // every token in its mask. Query fragments are kept in LDS.
-template <class T, class O, int D, bool SAVE>
+template <class T, class O, int D, bool SAVE, bool PF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_sel(PrefillArgs a) {
   using S = typename T::storage;
   using SO = typename O::storage;
@@ -839,18 +858,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tl = min(t0 + TPW - 1, Le - 1);
   const int nwords = ((tl >> 5) + 4) >> 2;  // half blocks 0 .. tl / 32
   for (int w = lane; w < nwords; w += 64) bm[w] = 0u;
+  // reads at clamped (token, head) indices, all issued before the first LDS
+  // store, zeroed where not valid; the selected branch's gates are read now
+  // rather than after the loop
+  const S* Qc = static_cast<const S*>(a.q) + b * a.qs[0] + (colv ? h : g * a.Hg) * a.qs[2] + 8 * grp;
+  Frag<T> qv[TPW][KS];
+  float gsl[TPW];
 #pragma unroll
   for (int qt = 0; qt < TPW; ++qt) {
-    const int t = t0 + qt;
-    const bool tv = t < Le;
+    const int t = t0 + qt, tc = min(t, Le - 1);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qv[qt][s] = frag_load_if<T>(Qc + static_cast<int64_t>(tc - t0q) * a.qs[1] + 32 * s, t < Le && colv);
+  }
+#pragma unroll
+  for (int qt = 0; qt < TPW; ++qt) {
+    const int t = t0 + qt, tc = min(t, Le - 1);
+    const float gv = gate_of<T>(a, b, tc - t0q, colv ? h : g * a.Hg, 1);
+    gsl[qt] = t < Le && colv ? gv : 0.f;
+  }
+#pragma unroll
+  for (int qt = 0; qt < TPW; ++qt)
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const Frag<T> f =
-          (tv && colv) ? frag_load<T>(Q + static_cast<int64_t>(t - t0q) * a.qs[1] + 32 * s) : frag_zero<T>();
-      const u32x4* w = reinterpret_cast<const u32x4*>(&f);
+      const u32x4* w = reinterpret_cast<const u32x4*>(&qv[qt][s]);
 #pragma unroll
       for (int e = 0; e < FE; ++e) q_lds[wave][qt][s][e][lane] = w[e];
     }
+  // the tokens' selection rows, both read before either is used
+  int jv[TPW];
+#pragma unroll
+  for (int qt = 0; qt < TPW; ++qt) {
+    const int tc = min(t0 + qt, Le - 1);
+    const int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.Lq + (tc - t0q)) * a.G + g) * n;
+    const int v = row[min(lane, n - 1)];
+    jv[qt] = lane < n ? v : -1;
   }
   wave_lds_sync();
 #pragma unroll
@@ -858,8 +900,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int t = t0 + qt;
     if (t >= Le) break;
     const int own = t / a.ls;
-    const int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.Lq + (t - t0q)) * a.G + g) * n;
-    const int j = lane < n ? row[lane] : -1;
+    const int j = jv[qt];
     if (j >= 0 && j <= own) {  // padding / unusable injected entries drop out
       // the selection block's half blocks that start at or before t
       const uint32_t bit = 1u << qt;
@@ -897,6 +938,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   wave_lds_sync();
 
+  // The fp32 rows the epilogue adds to (the window + compressed part: partial
+  // rows for a bf16 output, the output itself for fp32), copied to LDS by
+  // direct global-to-LDS loads (lane l's 16 bytes land at slot l) issued just
+  // before the ring's first loads, so the epilogue does not wait on memory.
+  constexpr bool kPart = std::is_same<O, BF16>::value;
+  float* pf = reinterpret_cast<float*>(sel_dyn + 4 * (static_cast<size_t>(a.sel_bm_words) + TPW * 128) * 4) +
+              static_cast<size_t>(wave) * TPW * 16 * D;
+  auto row_src = [&](int t, int hh) -> const float* {   // head g*Hg + hh of position t
+    return kPart ? a.part + ((static_cast<int64_t>(b) * a.Lq + (t - t0q)) * a.Hq + g * a.Hg + hh) * D
+                 : reinterpret_cast<const float*>(a.out) + b * a.os[0] + static_cast<int64_t>(t - t0q) * a.os[1] +
+                       (g * a.Hg + hh) * a.os[2];
+  };
+  auto prefetch_rows = [&]() {
+    if (!PF) return;
+    const int nch = a.Hg * (D / 4);   // 16-byte chunks of one position's rows
+#pragma unroll
+    for (int qt = 0; qt < TPW; ++qt) {
+      const int t = t0 + qt;
+      if (t >= Le) break;
+      for (int c0 = 0; c0 < nch; c0 += 64) {
+        const int c = c0 + lane;
+        if (c < nch)
+          lds_copy16(row_src(t, c / (D / 4)) + 4 * (c % (D / 4)), pf + qt * 16 * D + 4 * c0);
+      }
+    }
+  };
+
   float m[TPW], l[TPW];
   f32x4 acc[TPW][DT];
 #pragma unroll
@@ -911,13 +979,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // exit is at its top, so the count of loads in flight is the same on every
   // path and each step waits only for its own slot's loads while the other
   // slots' stay in flight.
+  int code0[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) code0[k] = steps[max(0, min(k, nsteps - 1))];
+  prefetch_rows();
+  __builtin_amdgcn_sched_barrier(0);
   if (nsteps > 0) {
     HalfBlock<T, D> ring[NB];
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      const int code = steps[min(k, nsteps - 1)];
-      half_load<T, D>(ring[k], KT, VT, code & 0x7FFFFF, (code >> 23) & 1, lane);
+      half_load<T, D>(ring[k], KT, VT, code0[k] & 0x7FFFFF, (code0[k] >> 23) & 1, lane);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    {
+      // loads return in order: once no more than the ring's loads are
+      // outstanding, the prefetched rows are in LDS (and the compiler, seeing
+      // this wait on every path, adds none of its own for them in the loop)
+      constexpr int kRingLoads = NB * (2 * (D / 32) + D / 16) * FE;
+      constexpr int kVm = kRingLoads < 63 ? kRingLoads : 63;
+      __builtin_amdgcn_s_waitcnt((kVm & 15) | ((kVm >> 4) << 14) | (7 << 4) | (15 << 8));
     }
 #pragma unroll 1
     for (int base = 0; base < nsteps; base += NB) {
@@ -959,19 +1039,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int t = t0 + qt;
     const float lt = col_sum4(l[qt]);
     if (t < Le && colv) {
-      const float gsl = gate_of<T>(a, b, t - t0q, h, 1);
-      const float f = lt > 0.f ? gsl / lt : 0.f;
+      const float f = lt > 0.f ? gsl[qt] / lt : 0.f;
       SO* o = OUT + static_cast<int64_t>(t - t0q) * a.os[1];
-      // the window + compressed part: fp32 partial rows for a bf16 output, out itself for fp32
-      const float* pp = std::is_same<O, BF16>::value
-                            ? a.part + ((static_cast<int64_t>(b) * a.Lq + (t - t0q)) * a.Hq + h) * D + 4 * grp
-                            : nullptr;
+      // the window + compressed part (prefetched, or fp32 partial rows for a
+      // bf16 output, out itself for fp32), all read before the first store:
+      // the compiler cannot tell that the stores do not alias them, and would
+      // otherwise wait for each read after the previous store
+      f32x4 prev[DT];
+      if (PF) {
+        const float* pl = pf + qt * 16 * D + col * D + 4 * grp;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const f32x4 prev = std::is_same<O, BF16>::value ? *reinterpret_cast<const f32x4*>(pp + 16 * dt)
-                                                        : load4<O>(o + 16 * dt);
-        store4<O>(o + 16 * dt, prev + acc[qt][dt] * f);
+        for (int dt = 0; dt < DT; ++dt) prev[dt] = *reinterpret_cast<const f32x4*>(pl + 16 * dt);
+      } else if (kPart) {
+        const float* pg = row_src(t, col) + 4 * grp;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) prev[dt] = *reinterpret_cast<const f32x4*>(pg + 16 * dt);
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) prev[dt] = load4<O>(o + 16 * dt);
       }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) store4<O>(o + 16 * dt, prev[dt] + acc[qt][dt] * f);
       if (SAVE) {  // the branch's own output and log-sum-exp, kept for the backward pass
         const int64_t r = (static_cast<int64_t>(b) * a.Lq + (t - t0q)) * a.Hq + h;
         const float inv = lt > 0.f ? 1.0f / lt : 0.f;
@@ -984,8 +1072,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-size_t sel_lds_bytes(int Nb, int D, bool bf16) {
-  const size_t need = 4 * (static_cast<size_t>(sel_bm_words(Nb)) + kSelTPW * 128) * sizeof(uint32_t);
+size_t sel_lds_bytes(int Nb, int D, bool bf16, bool prefetch) {
+  const size_t need = 4 * (static_cast<size_t>(sel_bm_words(Nb)) + kSelTPW * 128) * sizeof(uint32_t) +
+                      (prefetch ? sel_pf_bytes(D) : 0);
   const size_t stat = sel_static_lds_bytes(D, bf16);
   const size_t cap = kSelLdsOneWg > stat ? kSelLdsOneWg - stat : 0;  // total > half a CU's LDS
   return need > cap ? need : cap;
@@ -1025,12 +1114,16 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st, hipEven
   // every kernel attribute is set before the first launch
   const void* cmp_fn = cmpwin_kernel<T, O, D>(a);
   const size_t cmp_lds = cmpwin_lds_bytes(a.cmp_waves, a.NcT, D, kBf16, a.cmp_lo_lds != 0);
-  const void* sel_fn = a.save_o != nullptr ? reinterpret_cast<const void*>(&k_sel<T, O, D, true>)
-                                           : reinterpret_cast<const void*>(&k_sel<T, O, D, false>);
+  const void* sel_fn =
+      a.save_o != nullptr
+          ? (a.sel_pf ? reinterpret_cast<const void*>(&k_sel<T, O, D, true, true>)
+                      : reinterpret_cast<const void*>(&k_sel<T, O, D, true, false>))
+          : (a.sel_pf ? reinterpret_cast<const void*>(&k_sel<T, O, D, false, true>)
+                      : reinterpret_cast<const void*>(&k_sel<T, O, D, false, false>));
   // Static + dynamic LDS above half a CU's caps residency at one workgroup
   // (4 waves) per CU, which was measured faster (~13 % at 64k) than two: the
   // gathers then contend less for L2.
-  const size_t sel_lds = sel_lds_bytes(a.Nb, D, kBf16);
+  const size_t sel_lds = sel_lds_bytes(a.Nb, D, kBf16, a.sel_pf != 0);
   hipError_t e;
   if ((e = hipFuncSetAttribute(cmp_fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(cmp_lds))) !=
           hipSuccess ||
