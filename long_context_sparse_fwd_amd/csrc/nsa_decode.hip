@@ -488,23 +488,32 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   };
   DStream<T, D, RING> ds;
 
-  // ---- A: compressed half chunks. The first loads are issued before the
-  //      query is staged, so that their latency overlaps it.
+  // ---- A: compressed half chunks. Every wave reads the query fragments
+  //      (lane l: head l % 16) and the gates of the group's heads first, at
+  //      clamped indices and outside any branch, so nothing waits for them
+  //      here; then it issues its first loads, whose latency overlaps the
+  //      staging of the query by wave 0 (loads return in order, so waiting
+  //      for the query does not wait for them).
+  Frag<T> qv[D / 32];
+  float gv;
+  {
+    const int hq = col < a.Hg ? col : 0;
+    const S* Q = static_cast<const S*>(a.q) + b * a.qs[0] + (g * a.Hg + hq) * a.qs[1] + 8 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) qv[s] = frag_load_if<T>(Q + 32 * s, col < a.Hg);
+    const int h = lane & 15, i = min(lane >> 4, 2);
+    const float gg = to_f32<T>(static_cast<const S*>(a.gates)[b * a.gs[0] + (g * a.Hg + min(h, a.Hg - 1)) * a.gs[1] + i]);
+    gv = lane < 48 && h < a.Hg ? gg : 0.f;
+  }
   ds.prime(a_item, lane);
-  // query fragments (lane l: head l % 16) and gates of the group's heads
   if (tid == 0) {
     *hl_ready = 0;
     *parked = 0;
   }
   if (wave == 0) {
-    const S* Q = static_cast<const S*>(a.q) + b * a.qs[0] + (g * a.Hg + col) * a.qs[1] + 8 * (lane >> 4);
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) qlds[s * 64 + lane] = col < a.Hg ? frag_load<T>(Q + 32 * s) : frag_zero<T>();
-    if (lane < 48) {
-      const int h = lane & 15, i = lane >> 4;
-      gts[16 * i + h] =
-          h < a.Hg ? to_f32<T>(static_cast<const S*>(a.gates)[b * a.gs[0] + (g * a.Hg + h) * a.gs[1] + i]) : 0.f;
-    }
+    for (int s = 0; s < D / 32; ++s) qlds[s * 64 + lane] = qv[s];
+    if (lane < 48) gts[16 * (lane >> 4) + (lane & 15)] = gv;
   }
   lds_barrier();
   reset_state<D>(m, l, acc);

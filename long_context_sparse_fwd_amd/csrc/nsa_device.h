@@ -255,6 +255,16 @@ __device__ __forceinline__ float col_sum4(float v) {
   return v + xor32_f(v);
 }
 
+// A fragment read from p where ok, zeros elsewhere. p must be readable in
+// every lane (callers clamp the indices), so the read is unconditional: the
+// reads of a loop then stay in flight together instead of each sitting in a
+// branch of its own that the compiler waits on.
+template <class T>
+__device__ __forceinline__ Frag<T> frag_load_if(const typename T::storage* p, bool ok) {
+  const Frag<T> f = frag_load<T>(p);
+  return ok ? f : frag_zero<T>();
+}
+
 // Direct global-to-LDS copy, 16 bytes per active lane: lane l's bytes land
 // at lds + 16 l (lds must be the same in every lane). Tracked by vmcnt like a
 // load; the compiler waits for it before the wave's next LDS read unless an

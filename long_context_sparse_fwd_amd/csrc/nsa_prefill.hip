@@ -112,14 +112,25 @@ __device__ __forceinline__ float gate_of(const PrefillArgs& a, int b, int row, i
   return to_f32<T>(GT[b * a.gs[0] + static_cast<int64_t>(row) * a.gs[1] + h * a.gs[2] + c]);
 }
 
-// A fragment read from p where ok, zeros elsewhere. p must be readable in
-// every lane (callers clamp the indices), so the read is unconditional: the
-// reads of a loop then stay in flight together instead of each sitting in a
-// branch of its own that the compiler waits on.
-template <class T>
-__device__ __forceinline__ Frag<T> frag_load_if(const typename T::storage* p, bool ok) {
-  const Frag<T> f = frag_load<T>(p);
-  return ok ? f : frag_zero<T>();
+// Gate components c[0..NC) of query rows row[0..N) of head h, all read
+// before any is used (one wait, not one per read): the branch on where the
+// gates live sits outside the reads.
+template <class T, int N, int NC>
+__device__ __forceinline__ void gates_of(const PrefillArgs& a, int b, const int (&row)[N], int h, const int (&c)[NC],
+                                         float (&g)[N][NC]) {
+  if (a.gates32 != nullptr) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+      for (int j = 0; j < NC; ++j) g[i][j] = a.gates32[((static_cast<int64_t>(b) * a.Lq + row[i]) * a.Hq + h) * 3 + c[j]];
+  } else {
+    const typename T::storage* GT = static_cast<const typename T::storage*>(a.gates);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+      for (int j = 0; j < NC; ++j)
+        g[i][j] = to_f32<T>(GT[b * a.gs[0] + static_cast<int64_t>(row[i]) * a.gs[1] + h * a.gs[2] + c[j]]);
+  }
 }
 
 // Element j (0..7) of a fragment.
@@ -440,15 +451,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int s = 0; s < KS; ++s)
       qf[qt][s] = frag_load_if<T>(Qc + static_cast<int64_t>(tc - t0q) * a.qs[1] + 32 * s, valid);
   }
+  {
+    int rows[TPW];
+    float gv[TPW][2];
 #pragma unroll
-  for (int qt = 0; qt < TPW; ++qt) {
-    const int t = tw + qt, tc = min(t, Le - 1);
-    const bool valid = t < Le && colv;
-    const float gc = gate_of<T>(a, b, tc - t0q, colv ? h : g * a.Hg, 0);
-    const float gw = gate_of<T>(a, b, tc - t0q, colv ? h : g * a.Hg, 2);
-    gcmp[qt] = valid ? gc : 0.f;
-    gwin[qt] = valid ? gw : 0.f;
-    nvis[qt] = t < Le ? nvis_of(a, t) : 0;
+    for (int qt = 0; qt < TPW; ++qt) rows[qt] = min(tw + qt, Le - 1) - t0q;
+    gates_of<T>(a, b, rows, colv ? h : g * a.Hg, {0, 2}, gv);
+#pragma unroll
+    for (int qt = 0; qt < TPW; ++qt) {
+      const int t = tw + qt;
+      const bool valid = t < Le && colv;
+      gcmp[qt] = valid ? gv[qt][0] : 0.f;
+      gwin[qt] = valid ? gv[qt][1] : 0.f;
+      nvis[qt] = t < Le ? nvis_of(a, t) : 0;
+    }
   }
   f32x4 oacc[TPW][DT];
 #pragma unroll
@@ -871,11 +887,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int s = 0; s < KS; ++s)
       qv[qt][s] = frag_load_if<T>(Qc + static_cast<int64_t>(tc - t0q) * a.qs[1] + 32 * s, t < Le && colv);
   }
+  {
+    int rows[TPW];
+    float gv[TPW][1];
 #pragma unroll
-  for (int qt = 0; qt < TPW; ++qt) {
-    const int t = t0 + qt, tc = min(t, Le - 1);
-    const float gv = gate_of<T>(a, b, tc - t0q, colv ? h : g * a.Hg, 1);
-    gsl[qt] = t < Le && colv ? gv : 0.f;
+    for (int qt = 0; qt < TPW; ++qt) rows[qt] = min(t0 + qt, Le - 1) - t0q;
+    gates_of<T>(a, b, rows, colv ? h : g * a.Hg, {1}, gv);
+#pragma unroll
+    for (int qt = 0; qt < TPW; ++qt) gsl[qt] = t0 + qt < Le && colv ? gv[qt][0] : 0.f;
   }
 #pragma unroll
   for (int qt = 0; qt < TPW; ++qt)
