@@ -445,8 +445,9 @@ nsa_status_t nsa_bwd_prefill_timed(const nsa_prefill_desc_t* desc, const nsa_par
  * or a multiple of 16; bf16 in / {bf16, f32} out, f32 in / f32 out; strides
  * multiples of 8 elements. The workspace (nsa_dsa_workspace_bytes) holds the
  * float32 indexer scores of every (query, earlier token) pair,
- * B * L * (L + 1) / 2 floats (8 GiB for one 64k sequence), and the
- * selection when idx is NULL. Errors as for the other entry points.
+ * B * L * (L + 1) / 2 floats (8 GiB for one 64k sequence) and 256 bytes
+ * after them, and the selection when idx is NULL. Errors as for the other
+ * entry points.
  */
 typedef struct {
   int32_t batch, seqlen, n_q_heads, n_kv_heads, head_dim, idx_heads, idx_dim;

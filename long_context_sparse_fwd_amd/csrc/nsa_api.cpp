@@ -821,8 +821,11 @@ nsa_status_t plan_dsa(const nsa_dsa_desc_t* d, const nsa_dsa_params_t* p, DsaPla
   if (B * L > INT32_MAX) return fail(NSA_ERR_UNSUPPORTED, "batch * seqlen too large");
   size_t off = 0;
   pl->off_scores = off;
+  // the scores, then 64 floats where the indexer's lanes without a score to
+  // write store (so its stores need no branch)
   off = align_up(off + static_cast<size_t>(B) * static_cast<size_t>(L) * static_cast<size_t>(L + 1) / 2 *
-                           sizeof(float));
+                           sizeof(float) +
+                 64 * sizeof(float));
   pl->off_idx = off;
   off = align_up(off + static_cast<size_t>(B * L) * p->top_k * sizeof(int32_t));
   pl->total = off;
@@ -873,7 +876,7 @@ nsa_status_t dsa_impl(const nsa_dsa_desc_t* desc, const nsa_dsa_params_t* params
   a.parts = pl.parts;
   a.gpw = pl.gpw;
   a.wg_waves = pl.wg_waves;
-  a.idx_tiles = (a.L + 15) / 16;
+  a.idx_tiles = (a.L + nsa::kIdxWaves * nsa::kIdxTPW - 1) / (nsa::kIdxWaves * nsa::kIdxTPW);
   a.topk_cache = pl.topk_cache;
   const float sc = params->softmax_scale > 0.f ? params->softmax_scale : 1.0f / std::sqrt(static_cast<float>(a.D));
   a.scale_log2 = sc * nsa::kLog2eHost;

@@ -320,13 +320,6 @@ __device__ __forceinline__ void reset_state(float& m, float& l, f32x4 (&acc)[D /
   for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// Workgroup barrier that orders LDS accesses only: outstanding global loads
-// (a stream's first loads) stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // Block scores sc[j], j < own: the compressed-branch probabilities of block
 // j summed over the group's heads, from the logits lg[h][j] (row stride ld)

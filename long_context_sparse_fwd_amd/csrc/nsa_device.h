@@ -273,6 +273,25 @@ __device__ __forceinline__ void lds_copy16(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
+// col_sum4 without the lane selects: a lane swap with the value as both
+// operands returns the lane's own value in one half and its partner's in the
+// other, so their sum is the pair's sum in every lane. Floating-point
+// addition is commutative, so the result equals col_sum4's bit for bit.
+__device__ __forceinline__ float col_sum4_fast(float v) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
+// Workgroup barrier that orders LDS accesses only: outstanding global loads
+// and stores stay in flight across it (__syncthreads waits for all of them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Orders this wave's LDS accesses before the following ones.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");

@@ -151,7 +151,6 @@ __device__ __forceinline__ uint32_t orderable(float f) {
 
 // ------------------------------------------------------------------ k_dsa_index
 
-constexpr int kIdxWaves = 8, kIdxTPW = 2;
 
 template <class T, int DI>
 __global__ __launch_bounds__(512) void k_dsa_index(DsaArgs a) {
@@ -177,56 +176,68 @@ __global__ __launch_bounds__(512) void k_dsa_index(DsaArgs a) {
   // are heads 4 grp + i, whose weights it keeps
   Frag<T> qf[kIdxTPW][KS];
   float wv[kIdxTPW][4];
+  // reads at clamped (token, head) indices, all in flight together, zeroed where not valid
 #pragma unroll
   for (int qt = 0; qt < kIdxTPW; ++qt) {
-    const int t = tw + qt;
+    const int t = tw + qt, tc = min(t, a.L - 1);
     const bool ok = t < a.L && col < a.Hi;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      qf[qt][s] = ok ? frag_load<T>(QI + static_cast<int64_t>(t) * a.qis[1] + col * a.qis[2] + 32 * s + 8 * grp)
-                     : frag_zero<T>();
+      qf[qt][s] = frag_load_if<T>(
+          QI + static_cast<int64_t>(tc) * a.qis[1] + min(col, a.Hi - 1) * a.qis[2] + 32 * s + 8 * grp, ok);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * grp + i;
-      wv[qt][i] = (t < a.L && h < a.Hi) ? to_f32<T>(W[static_cast<int64_t>(t) * a.wis[1] + h]) : 0.f;
+      const float x = to_f32<T>(W[static_cast<int64_t>(tc) * a.wis[1] + min(h, a.Hi - 1)]);
+      wv[qt][i] = (t < a.L && h < a.Hi) ? x : 0.f;
     }
   }
 
-  // 16-byte chunk e of chunk c: key row r, dims d .. d + EPC - 1 -> its place in the fragment-major tile
-  u32x4 reg[PER];
-  auto issue = [&](int c) {
+  // 16-byte chunk e of chunk c: key row r, dims d .. d + EPC - 1 -> its place
+  // in the fragment-major tile. Two register sets: chunk j travels in set
+  // j & 1, issued two chunks before it is computed; keys past the sequence
+  // read its last key instead (their scores are never stored).
+  u32x4 reg[2][PER];
+  auto issue = [&](int c, auto set_c) {
+    constexpr int set = decltype(set_c)::value;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int e = tid + NT * i, r = (e * EPC) / DI, d = (e * EPC) % DI, key = 64 * c + r;
-      reg[i] = key < a.L ? *reinterpret_cast<const u32x4*>(KI + static_cast<int64_t>(key) * a.kis[1] + d)
-                         : u32x4{0u, 0u, 0u, 0u};
+      const int e = tid + NT * i, r = (e * EPC) / DI, d = (e * EPC) % DI, key = min(64 * c + r, a.L - 1);
+      reg[set][i] = *reinterpret_cast<const u32x4*>(KI + static_cast<int64_t>(key) * a.kis[1] + d);
     }
   };
-  auto commit = [&](int buf) {
+  auto commit = [&](int buf, auto set_c) {
+    constexpr int set = decltype(set_c)::value;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = tid + NT * i, r = (e * EPC) / DI, d = (e * EPC) % DI;
-      *reinterpret_cast<u32x4*>(&stage[buf][kchunk_off<T>(r, d, DI)]) = reg[i];
+      *reinterpret_cast<u32x4*>(&stage[buf][kchunk_off<T>(r, d, DI)]) = reg[set][i];
     }
   };
-  const int nch = (Tl >> 6) + 1;
-  issue(0);
-  commit(0);
-  __syncthreads();
   float* SC = a.scores;
+  float* sink = a.scores + static_cast<int64_t>(a.B) * a.L * (static_cast<int64_t>(a.L) + 1) / 2;
   int64_t rows[kIdxTPW];
+  // w * ReLU(x) is computed as (w / 2) * (x + |x|): the same product (x + |x|
+  // is 2x or +0, and halving w is exact for normal w), in two instructions
+  // where fmaxf needs three (it quiets NaN inputs first)
+  float hw[kIdxTPW][4];
 #pragma unroll
-  for (int qt = 0; qt < kIdxTPW; ++qt) rows[qt] = score_row(a, b, min(tw + qt, a.L - 1));
-  for (int c = 0; c < nch; ++c) {
+  for (int qt = 0; qt < kIdxTPW; ++qt) {
+    rows[qt] = score_row(a, b, min(tw + qt, a.L - 1));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hw[qt][i] = 0.5f * wv[qt][i];
+  }
+  auto compute = [&](int c) {
     const int buf = c & 1;
-    const bool more = c + 1 < nch;
-    if (more) issue(c + 1);
+    // after the column sum every lane of a column holds the key's score; lane
+    // (col, grp) keeps the one of 16-key tile kt = grp, so that one store per
+    // token writes the chunk's 64 scores (key 64 c + lane)
+    float mine[kIdxTPW] = {};
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       Frag<T> kf[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) kf[s] = frag_load<T>(&stage[buf][kfrag_off<T>(kt, s, lane, DI)]);
-      const int key = 64 * c + 16 * kt + col;
 #pragma unroll
       for (int qt = 0; qt < kIdxTPW; ++qt) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -234,15 +245,49 @@ __global__ __launch_bounds__(512) void k_dsa_index(DsaArgs a) {
         for (int s = 0; s < KS; ++s) mma(acc, qf[qt][s], kf[s]);
         float v = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v = fmaf(wv[qt][i], fmaxf(acc[i], 0.f), v);
-        // heads 4 grp .. 4 grp + 3 of the four lanes of this column; + 0 turns -0 into +0
-        v = col_sum4(v) + 0.f;
-        const int t = tw + qt;
-        if (grp == 0 && t < a.L && key <= t) SC[rows[qt] + key] = v;
+        for (int i = 0; i < 4; ++i) v = fmaf(hw[qt][i], acc[i] + fabsf(acc[i]), v);
+        // heads 4 grp .. 4 grp + 3 of the four lanes of this column
+        v = col_sum4_fast(v);
+        mine[qt] = grp == kt ? v : mine[qt];
       }
     }
-    if (more) commit(buf ^ 1);
-    __syncthreads();
+    // lanes without a score to write (keys after the token) store to the
+    // sink after the scores instead: no branch around the stores, so the
+    // compiler's count of stores in flight is the same on every path
+    const int key = 64 * c + lane;
+#pragma unroll
+    for (int qt = 0; qt < kIdxTPW; ++qt) {
+      const int t = tw + qt;
+      float* dst = (t < a.L && key <= t) ? SC + rows[qt] + key : sink + lane;
+      *dst = mine[qt] + 0.f;   // + 0 turns -0 into +0
+    }
+  };
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
+  const int nch = (Tl >> 6) + 1;
+  issue(0, Set0{});
+  issue(min(1, nch - 1), Set1{});
+  commit(0, Set0{});
+  lds_barrier();
+  // chunk c: issue c + 2 into the set chunk c came in (committed a step ago),
+  // compute c, commit c + 1 (from `next_c`) into the buffer read at c - 1.
+  // Every step issues and commits, chunks past the last one clamped to it,
+  // and steps run in pairs (an odd count computes one chunk past the last,
+  // whose keys follow every token, so nothing is stored): the loads in
+  // flight are then the same on every path, and the compiler's waits cover
+  // only the chunk being committed, not the one just issued.
+  auto step = [&](int c, auto next_c) __attribute__((always_inline)) {
+    constexpr int nxt = decltype(next_c)::value;
+    issue(min(c + 2, nch - 1), std::integral_constant<int, 1 - nxt>{});
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the chunk's work
+    compute(c);
+    __builtin_amdgcn_sched_barrier(0);   // and the commit after it
+    commit((c + 1) & 1, next_c);
+    lds_barrier();
+  };
+  for (int c = 0; c < nch; c += 2) {
+    step(c, Set1{});
+    step(c + 1, Set0{});
   }
 }
 
@@ -262,7 +307,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
     if (lane >= o) x += y;
   }
   if (lane == 63) wsum[wave] = x;
-  __syncthreads();
+  lds_barrier();
   uint32_t before = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < kTopkWaves; ++w) {
@@ -344,7 +389,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
   // digit 1 (bits 31..20): one read of the row, eight loads in flight per thread
   for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0u;
   if (tid == 0) ncand = 0u;
-  __syncthreads();
+  lds_barrier();
   auto take = [&](int i, float x) {
     const uint32_t u = orderable(x);
     if (i < cap) c16[i] = static_cast<uint16_t>(u >> 16);
@@ -377,9 +422,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
     }
   }
   for (int i = head + 4 * nv + tid; i < n; i += kTopkThreads) take(i, S[i]);
-  __syncthreads();
+  lds_barrier();
   find_bin(hist, 4096, static_cast<uint32_t>(k), wsum, res, tid, lane, wave);
-  __syncthreads();
+  lds_barrier();
   const uint32_t d1 = res[0], need1 = res[1];
   // passes over the cached top 16 bits, eight keys (one 16-byte word) at a time
   const int nq = min(n, cap) >> 3;   // whole words in the cache
@@ -394,13 +439,13 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
   };
   // digit 2 (bits 19..16) among the keys of bin d1
   if (tid < 16) hist[tid] = 0u;
-  __syncthreads();
+  lds_barrier();
   for_top16([&](int, uint32_t c) {
     if ((c >> 4) == d1) atomicAdd(&hist[c & 15u], 1u);
   });
-  __syncthreads();
+  lds_barrier();
   find_bin(hist, 16, need1, wsum, res, tid, lane, wave);
-  __syncthreads();
+  lds_barrier();
   const uint32_t P = (d1 << 4) | res[0];
   uint32_t need = res[1];   // rank of the k-th key among the keys whose top 16 bits are P
   // the candidates sharing P: their exact keys
@@ -410,7 +455,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
       if (pos < static_cast<uint32_t>(kTopkCand)) cand[pos] = key64(i);
     }
   });
-  __syncthreads();
+  lds_barrier();
   const uint32_t nc = ncand;
   uint64_t kth;   // the k-th largest key of the row
   if (nc <= static_cast<uint32_t>(kTopkCand)) {
@@ -418,7 +463,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
     int Pn = 1;
     while (Pn < static_cast<int>(nc)) Pn <<= 1;
     for (int i = static_cast<int>(nc) + tid; i < Pn; i += kTopkThreads) cand[i] = 0ull;
-    __syncthreads();
+    lds_barrier();
     for (int size = 2; size <= Pn; size <<= 1)
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
         for (int i = tid; i < Pn / 2; i += kTopkThreads) {
@@ -430,7 +475,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
             cand[hi] = x;
           }
         }
-        __syncthreads();
+        lds_barrier();
       }
     kth = cand[need - 1];
   } else {
@@ -438,27 +483,27 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
     uint64_t pre = P;   // the known high bits of the k-th key
     for (int shift = 40; shift >= 0; shift -= 8) {
       for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0u;
-      __syncthreads();
+      lds_barrier();
       for (int i = tid; i < n; i += kTopkThreads)
         if (top16(i) == P) {
           const uint64_t kk = key64(i);
           if ((kk >> (shift + 8)) == pre) atomicAdd(&hist[(kk >> shift) & 0xFFu], 1u);
         }
-      __syncthreads();
+      lds_barrier();
       find_bin(hist, 256, need, wsum, res, tid, lane, wave);
-      __syncthreads();
+      lds_barrier();
       pre = (pre << 8) | res[0];
       need = res[1];
-      __syncthreads();
+      lds_barrier();
     }
     kth = pre;
   }
-  __syncthreads();
+  lds_barrier();
   // bitmap (over the histogram) of the chosen candidates sharing P
   uint32_t* bits = hist;
   const int nwords = (n + 31) >> 5;
   for (int i = tid; i < nwords; i += kTopkThreads) bits[i] = 0u;
-  __syncthreads();
+  lds_barrier();
   if (nc <= static_cast<uint32_t>(kTopkCand)) {
     for (int i = tid; i < static_cast<int>(nc); i += kTopkThreads) {
       const uint64_t kk = cand[i];
@@ -471,7 +516,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
     for (int i = tid; i < n; i += kTopkThreads)
       if (top16(i) == P && key64(i) >= kth) atomicOr(&bits[i >> 5], 1u << (i & 31));
   }
-  __syncthreads();
+  lds_barrier();
   // ordered compaction: wave w takes the candidates [w * span, (w + 1) * span),
   // eight consecutive ones per lane and round; one workgroup scan of the wave
   // counts, then wave-level prefix sums
@@ -560,7 +605,7 @@ k_dsa_attn(DsaArgs a) {
   // ---- this token's keys: ascending, distinct, each at or before t
   const int32_t* irow = a.idx + row * a.topk;
   if (tid == 0) cnt_sh = 0;
-  __syncthreads();
+  lds_barrier();
   if (!a.inject) {
     // a computed row is ascending with -1 padding
     int c = 0;
@@ -570,14 +615,14 @@ k_dsa_attn(DsaArgs a) {
       c += j >= 0 ? 1 : 0;
     }
     if (c) atomicAdd(&cnt_sh, c);
-    __syncthreads();
+    lds_barrier();
   } else {
     // an injected row is a set of tokens: drop entries outside [0, t], sort, drop repeats
     for (int i = tid; i < P; i += NTH) {
       const int j = i < a.topk ? irow[i] : -1;
       tmp[i] = (j >= 0 && j <= t) ? j : INT_MAX;
     }
-    __syncthreads();
+    lds_barrier();
     for (int size = 2; size <= P; size <<= 1)
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
         for (int i = tid; i < P / 2; i += NTH) {
@@ -589,7 +634,7 @@ k_dsa_attn(DsaArgs a) {
             tmp[hi] = x;
           }
         }
-        __syncthreads();
+        lds_barrier();
       }
     // ordered compaction of the first occurrences
     const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -600,7 +645,7 @@ k_dsa_attn(DsaArgs a) {
       const bool keep = x != INT_MAX && (i == 0 || tmp[i - 1] != x);
       const uint64_t bal = __ballot(keep);
       if (lane == 0) wtot[wave] = static_cast<uint32_t>(__popcll(bal));
-      __syncthreads();
+      lds_barrier();
       int before = __popcll(bal & below), tot = 0;
       for (int w = 0; w < a.wg_waves; ++w) {
         if (w < wave) before += static_cast<int>(wtot[w]);
@@ -608,10 +653,10 @@ k_dsa_attn(DsaArgs a) {
       }
       if (keep) list[written + before] = x;
       written += tot;
-      __syncthreads();
+      lds_barrier();
     }
     if (tid == 0) cnt_sh = written;
-    __syncthreads();
+    lds_barrier();
   }
   const int cnt = cnt_sh;
 
@@ -643,21 +688,20 @@ k_dsa_attn(DsaArgs a) {
   // two register sets: the rows of step j travel in set j & 1, issued two
   // steps before they are computed
   u32x4 rk[2][MAXPER], rv[2][MAXPER];
+  // positions past the list read its last token's rows (masked out of the
+  // softmax), so every load is unconditional and the loads in flight are the
+  // same on every path (the compiler then waits only for the step committed)
   auto issue = [&](int step, auto set_c) {
     constexpr int set = decltype(set_c)::value;
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
       const int e = gt + gthreads * i;
-      rk[set][i] = rv[set][i] = u32x4{0u, 0u, 0u, 0u};
-      if (e < CH) {
+      if (TR || e < CH) {
         int r, d;
         pos_of(e, r, d);
-        const int pos = 32 * step + r;
-        if (pos < cnt) {
-          const int64_t tok = list[pos];
-          rk[set][i] = *reinterpret_cast<const u32x4*>(K + tok * a.ks[1] + d);
-          rv[set][i] = *reinterpret_cast<const u32x4*>(V + tok * a.vs[1] + d);
-        }
+        const int64_t tok = list[min(32 * step + r, cnt - 1)];
+        rk[set][i] = *reinterpret_cast<const u32x4*>(K + tok * a.ks[1] + d);
+        rv[set][i] = *reinterpret_cast<const u32x4*>(V + tok * a.vs[1] + d);
       }
     }
   };
@@ -668,7 +712,7 @@ k_dsa_attn(DsaArgs a) {
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
       const int e = gt + gthreads * i;
-      if (e < CH) {
+      if (TR || e < CH) {
         int r, d;
         pos_of(e, r, d);
         *reinterpret_cast<u32x4*>(kp + kchunk_off<T>(r, d, D)) = rk[set][i];
@@ -717,9 +761,9 @@ k_dsa_attn(DsaArgs a) {
   if (nsteps > 0) {
     issue(0, Set0{});
     commit(0, Set0{});
-    if (nsteps > 1) issue(1, Set1{});
-    if (nsteps > 2) issue(2, Set0{});
-    __syncthreads();
+    issue(min(1, nsteps - 1), Set1{});
+    issue(min(2, nsteps - 1), Set0{});
+    lds_barrier();
   }
   // one step; `next_c` is the register set of step + 1 (a constant: the loop runs steps in pairs)
   auto run_step = [&](int step, auto next_c) __attribute__((always_inline)) {
@@ -736,21 +780,23 @@ k_dsa_attn(DsaArgs a) {
     Frag<T> vf[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vf[dt] = frag_load<T>(vp + vhalf_frag(dt, lane));
-    // positions past the list hold zero rows: masked out of the softmax
+    // positions past the list are masked out of the softmax (a step past
+    // the last one is masked entirely)
     if (32 * step + 31 < cnt)
       online_step<T, DT, false>(st, 32 * step, 0, 0, grp, sl2, m, l, acc, vf);
     else
       online_step<T, DT, true>(st, 32 * step, 0, cnt - 1, grp, sl2, m, l, acc, vf);
-    // step + 1's rows into the buffer last read at step - 2; then step + 3's loads
-    if (step + 1 < nsteps) {
-      commit((step + 1) % kAttnBufs, next_c);
-      if (step + 3 < nsteps) issue(step + 3, next_c);
-    }
-    __syncthreads();
+    // step + 1's rows into the buffer last read at step - 2; then step + 3's
+    // loads (clamped to the last step, as every step commits and issues)
+    __builtin_amdgcn_sched_barrier(0);
+    commit((step + 1) % kAttnBufs, next_c);
+    issue(min(step + 3, nsteps - 1), next_c);
+    lds_barrier();
   };
+  // steps in pairs; with an odd count the last pair's second step is masked
   for (int step = 0; step < nsteps; step += 2) {
     run_step(step, Set1{});
-    if (step + 1 < nsteps) run_step(step + 1, Set0{});
+    run_step(step + 1, Set0{});
   }
 
   const float lt = col_sum4(l);

@@ -155,7 +155,7 @@ struct DsaArgs {
   int parts;        // attention workgroups per query token (each takes gpw KV heads)
   int gpw;          // KV heads staged per attention workgroup
   int wg_waves;     // waves per attention workgroup
-  int idx_tiles;    // indexer workgroups per sequence (16 query tokens each)
+  int idx_tiles;    // indexer workgroups per sequence (kIdxWaves * kIdxTPW query tokens each)
   int topk_cache;   // orderable keys of a row kept in LDS by the top-k kernel
   float scale_log2; // softmax scale * log2(e)
   int inject;       // 1: idx holds the selection (a set of tokens)
@@ -170,6 +170,7 @@ struct DsaArgs {
   float* scores;    // indexer scores, row t of sequence b at b*L(L+1)/2 + t(t+1)/2
   int64_t qs[3], ks[3], vs[3], os[3], qis[3], kis[2], wis[2];
 };
+constexpr int kIdxWaves = 8, kIdxTPW = 2;   // indexer: waves per workgroup, query tokens per wave
 constexpr int kDsaStages = 3;
 constexpr int kDsaMaxTopK = 2048;
 hipError_t launch_dsa(const DsaArgs& a, bool in_bf16, bool out_bf16, hipStream_t st, hipEvent_t* ev);
