@@ -370,6 +370,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
   __shared__ uint32_t res[2];
   __shared__ uint32_t wsum[kTopkWaves];
   __shared__ uint32_t ncand;
+  __shared__ uint64_t kth_sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x;
   const int b = static_cast<int>(row / a.L), t = static_cast<int>(row % a.L);
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
     return (static_cast<uint64_t>(orderable(S[i])) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(i));
   };
 
-  // digit 1 (bits 31..20): one read of the row, eight loads in flight per thread
+  // digit 1 (bits 31..20): one read of the row, sixteen loads in flight per thread
   for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0u;
   if (tid == 0) ncand = 0u;
   lds_barrier();
@@ -396,12 +397,12 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
     atomicAdd(&hist[u >> 20], 1u);
   };
   // the row starts at an arbitrary float: a scalar head up to 16-byte
-  // alignment, then 16-byte loads (eight in flight per thread), a scalar tail
+  // alignment, then 16-byte loads (sixteen in flight per thread), a scalar tail
   const int head = min(n, static_cast<int>((4 - ((reinterpret_cast<uintptr_t>(S) >> 2) & 3)) & 3));
   if (tid < head) take(tid, S[tid]);
   const int nv = (n - head) >> 2;   // whole float4s after the head
   const f32x4* S4 = reinterpret_cast<const f32x4*>(S + head);
-  constexpr int UNR = 8;
+  constexpr int UNR = 16;
   for (int base = 0; base < nv; base += kTopkThreads * UNR) {
     f32x4 v[UNR];
 #pragma unroll
@@ -458,7 +459,18 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
   lds_barrier();
   const uint32_t nc = ncand;
   uint64_t kth;   // the k-th largest key of the row
-  if (nc <= static_cast<uint32_t>(kTopkCand)) {
+  if (nc <= 256u) {
+    // few candidates (the usual case): the k-th key is the one with exactly
+    // need - 1 larger candidates (keys are distinct: they hold the token)
+    for (int i = tid; i < static_cast<int>(nc); i += kTopkThreads) {
+      const uint64_t x = cand[i];
+      uint32_t above = 0;
+      for (int j = 0; j < static_cast<int>(nc); ++j) above += cand[j] > x ? 1u : 0u;
+      if (above == need - 1) kth_sh = x;
+    }
+    lds_barrier();
+    kth = kth_sh;
+  } else if (nc <= static_cast<uint32_t>(kTopkCand)) {
     // bitonic sort of the candidates, descending (zero keys pad to a power of two)
     int Pn = 1;
     while (Pn < static_cast<int>(nc)) Pn <<= 1;
