@@ -117,15 +117,22 @@ class HipEvents:
 
 # ---------------------------------------------------------------- traffic from committed counters
 
-def kernel_source_digest() -> str:
-    """Digest of the sources the forward kernels and their launches are built
-    from (everything in csrc/ but the gather probe and the backward pass's own
-    kernel file and header)."""
+# the sources each family of forward kernels (and their launches) is built from
+DIGEST_SOURCES = {
+    "nsa": ("nsa_api.cpp", "nsa_compress.hip", "nsa_decode.hip", "nsa_device.h", "nsa_internal.h",
+            "nsa_prefill.hip", "nsa_topk.h"),
+    "dsa": ("nsa_api.cpp", "nsa_device.h", "nsa_dsa.hip", "nsa_internal.h"),
+}
+
+
+def kernel_source_digest(family: str = "nsa") -> str:
+    """Digest of the sources a family of forward kernels is built from
+    (DIGEST_SOURCES); a committed counter record applies while it matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "long_context_sparse_fwd_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")) and not name.startswith(("probe_", "nsa_backward")):
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in DIGEST_SOURCES[family]:
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -143,7 +150,7 @@ def probe_gather_ceiling():
     return max(vals) if vals else None
 
 
-def committed_traffic(kernel: str, workload: str):
+def committed_traffic(kernel: str, workload: str, family: str = "nsa"):
     """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
     if taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", f"pmc_{workload}.md")
@@ -151,7 +158,7 @@ def committed_traffic(kernel: str, workload: str):
         return None
     text = open(path).read()
     m = re.search(r"kernel_source_digest:\s*(\w+)", text)
-    if not m or m.group(1) != kernel_source_digest():
+    if not m or m.group(1) != kernel_source_digest(family):
         return None
     m = re.search(rf"traffic_bytes_per_launch\s+{kernel}:\s*([0-9.eE+]+)", text)
     return float(m.group(1)) if m else None
@@ -196,8 +203,14 @@ def host_description():
     return model or "unknown", blas
 
 
-def cpu_baseline(cfg, raw, seconds: float):
-    """The float64 oracle on evenly spaced query rows of the same workload."""
+def cpu_baseline(cfg, raw, seconds: float, gpu=None):
+    """The float64 oracle on evenly spaced query rows of the same workload.
+
+    With gpu = (out, idx) from the library on the same input (bf16 output,
+    as timed), the oracle rows just computed also give the parity of that
+    output: the selection compared row by row, and the largest absolute
+    output error against the oracle run with the library's own selection
+    where the two differ (the tests' Check B)."""
     from oracle import nsa_ref
     try:
         ncores = len(os.sched_getaffinity(0))
@@ -211,10 +224,12 @@ def cpu_baseline(cfg, raw, seconds: float):
         limiter = None
     lz = {n: _LazyBf16(raw[n]) for n in raw}
 
+    last = {}
+
     def run(rows):
         t0 = time.perf_counter()
-        nsa_ref.prefill(lz["q"], lz["k"], lz["v"], lz["gates"], block=cfg.block, top_k=cfg.top_k,
-                        window=cfg.window, rows=rows)
+        last["res"] = nsa_ref.prefill(lz["q"], lz["k"], lz["v"], lz["gates"], block=cfg.block, top_k=cfg.top_k,
+                                      window=cfg.window, rows=rows)
         return time.perf_counter() - t0
 
     L = cfg.seqlen
@@ -226,12 +241,33 @@ def cpu_baseline(cfg, raw, seconds: float):
     n_rows = int(max(16, min(20000, (seconds - fixed) / per_row)))
     rows = np.linspace(0, L - 1, n_rows).astype(np.int64)
     dt = run(rows)
+    parity = None
+    if gpu is not None:
+        res = last["res"]
+        g_out, g_idx = gpu
+        import torch
+        rsel = torch.as_tensor(rows, device=g_out.device)
+        go = g_out[:, rsel].float().cpu().numpy().astype(np.float64)
+        gi = g_idx[:, rsel].cpu().numpy()
+        expect = res["out"].copy()
+        differ = np.argwhere(np.any(gi != res["idx"], axis=(2, 3)))
+        for b, r in differ:
+            inj = np.zeros((1, L, cfg.n_kv_heads, cfg.top_k), np.int32)
+            inj[0, rows[r]] = gi[b, r]
+            lb = {n: _LazyBf16(raw[n][b:b + 1]) for n in ("q", "k", "v", "gates")}
+            expect[b, r] = nsa_ref.prefill(lb["q"], lb["k"], lb["v"], lb["gates"], block=cfg.block,
+                                           top_k=cfg.top_k, window=cfg.window, rows=[rows[r]],
+                                           inject_idx=inj)["out"][0, 0]
+        parity = {"rows": int(n_rows * cfg.batch), "rows_with_the_oracle_selection": int(n_rows * cfg.batch - len(differ)),
+                  "out_dtype": "bf16", "max_abs_err": float(np.max(np.abs(go - expect))), "tol": 2e-2,
+                  "note": "rows whose selection differs are compared with the oracle given the library's selection"}
     if limiter is not None:
         limiter.unregister() if hasattr(limiter, "unregister") else None
     return {"value": n_rows * cfg.batch / dt, "unit": "tokens/s", "cores": ncores, "kind": "oracle",
             "cpu_model": cpu_model, "blas": blas,
             "sample": f"{n_rows} evenly spaced query rows of the {cfg.name} workload (full "
-                      f"{L}-token context, all {cfg.n_q_heads} heads), float64 numpy, {dt:.1f} s"}
+                      f"{L}-token context, all {cfg.n_q_heads} heads), float64 numpy, {dt:.1f} s",
+            "parity_of_timed_output": parity}
 
 
 # ---------------------------------------------------------------- benchmark legs
@@ -530,7 +566,8 @@ def bench_dsa(cfg, steps, warmup, torch, inputs, nsa):
                           "mfma_frac": fl["attention"] / (stage_ms["attention"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                           "gathered_bytes": gathered,
                           "gathered_TBps": gathered / (stage_ms["attention"] * 1e-3) / 1e12},
-            "dtype": "bf16 (indexer and attention operands), fp32 scores and accumulation"}
+            "dtype": "bf16 (indexer and attention operands), fp32 scores and accumulation",
+            "traffic": {kn: committed_traffic(kn, cfg.name, "dsa") for kn in ("k_dsa_index", "k_dsa_topk", "k_dsa_attn")}}
 
 
 def bench_decode(cfg, steps, warmup, torch, inputs, nsa):
@@ -718,7 +755,12 @@ def main():
         result["decode"] = bench_decode(inputs.CONFIGS["d64k"], args.decode_steps, 3, torch, inputs, nsa)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(cfg, raw, args.cpu_seconds)
+        up = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        q, k, v, g = (up(raw[n]) for n in ("q", "k", "v", "gates"))
+        gpu = nsa.prefill(q, k, v, g, top_k=cfg.top_k, window=cfg.window, out_dtype=torch.bfloat16, return_idx=True)
+        torch.cuda.synchronize()
+        del q, k, v, g
+        result["cpu_baseline"] = cpu_baseline(cfg, raw, args.cpu_seconds, gpu=gpu)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

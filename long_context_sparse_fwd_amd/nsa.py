@@ -393,6 +393,26 @@ def prefill_workspace_bytes(q, k, v, gates, out, *, top_k, window, block=64) -> 
     return nbytes.value
 
 
+def prefill_general_workspace_bytes(q, k, v, gates, out, *, top_k, window, block=64, select_block=None,
+                                     stride=None, compressor=None, gate_layer=None, scale: float = 0.0) -> int:
+    desc = prefill_desc(q, k, v, gates if gates is not None else q[..., :3], out)
+    params = make_params(top_k, window, block, select_block, scale)
+    gen = make_general(block if stride is None else stride, compressor, gate_layer)
+    nbytes = ctypes.c_size_t()
+    check(lib().nsa_prefill_general_workspace_bytes(ctypes.byref(desc), ctypes.byref(params), ctypes.byref(gen),
+                                                    ctypes.byref(nbytes)))
+    return nbytes.value
+
+
+def decode_workspace_bytes(q, k_cache, v_cache, kc_cache, vc_cache, gates, out, *, top_k, window, block=64,
+                           select_block=None) -> int:
+    desc = decode_desc(q, k_cache, v_cache, kc_cache, vc_cache, gates, out)
+    params = make_params(top_k, window, block, select_block)
+    nbytes = ctypes.c_size_t()
+    check(lib().nsa_decode_workspace_bytes(ctypes.byref(desc), ctypes.byref(params), ctypes.byref(nbytes)))
+    return nbytes.value
+
+
 def prefill_backward_workspace_bytes(q, k, v, gates, dout, *, top_k, window, block=64) -> int:
     desc = prefill_desc(q, k, v, gates, dout)
     params = make_params(top_k, window, block)
