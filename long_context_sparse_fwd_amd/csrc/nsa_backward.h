@@ -10,7 +10,7 @@ namespace nsa {
 // Backward pass of the prefill (gradients for a fixed selection).
 constexpr int kBwdSelPiece = 256;  // tokens per workgroup of the selected branch's key side
 constexpr int kBwdCmpPiece = 512;  // tokens per workgroup of the compressed branch's key side
-constexpr int kBwdStage = 4;      // tokens staged in LDS at a time by the key-side kernel (even)
+constexpr int kBwdStage = 2;      // tokens staged in LDS at a time by the key-side kernel (even)
 struct BwdArgs {
   int B, L, Hq, G, Hg, D, n, w;
   int Nb, Nc, NcT;

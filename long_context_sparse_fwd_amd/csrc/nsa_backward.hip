@@ -437,7 +437,8 @@ struct BkvStage {
 };
 
 template <class T, int D, int X>
-__global__ __launch_bounds__(256) void k_bkv(BwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(typename T::storage) == 2 ? 2 : 1))) void
+k_bkv(BwdArgs a) {
   using S = typename T::storage;
   constexpr int KS = D / 32, DT = D / 16, TT = kBwdStage;
   extern __shared__ __align__(16) unsigned char bkv_smem[];
@@ -494,46 +495,79 @@ __global__ __launch_bounds__(256) void k_bkv(BwdArgs a) {
     dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const int tid = threadIdx.x;
-  for (int ib = i0; ib < i1; ib += TT) {
-    __syncthreads();  // the previous stage has been read
-    // stage tokens ib .. ib + TT - 1: 256 threads x 8 elements cover one
-    // token's 16 x D of each array
+  // Staging, software-pipelined: the next stage's rows are read into
+  // registers while this stage is computed, and written to LDS after it. All
+  // reads are unconditional, at clamped (token, head) indices, zeroed where
+  // not valid, so the loads in flight are the same on every path and the
+  // compiler waits only for the stage being written. A stage's tokens come
+  // from the selection list (branch 1) one stage ahead of its rows.
+  const int e = tid * 8, hh = e / D, d = e % D;
+  const bool estage = e < 16 * D;   // 16 x D elements per array and token: all threads at D = 128, half at 64
+  const int hc = g * a.Hg + min(hh, a.Hg - 1), hs = g * a.Hg + min(tid & 15, a.Hg - 1);
+  auto token_of = [&](int i) -> int {
+    if (X == 1) {
+      const int v = list[min(i, i1 - 1)];
+      return i < i1 ? v : -1;
+    }
+    return i < i1 ? i : -1;
+  };
+  Frag<T> rq[TT], rd[TT], rqt[TT], rdt[TT];
+  float2 rst[TT];
+  float rgt[TT];
+  int rtok[TT], ntok[TT];
+  auto load_stage = [&](const int (&tok)[TT]) {
 #pragma unroll
     for (int uu = 0; uu < TT; ++uu) {
-      const int i = ib + uu;
-      const int t = i < i1 ? (X == 1 ? list[i] : i) : -1;
-      const int e = tid * 8, hh = e / D, d = e % D;
-      if (e < 16 * D) {  // 16 x D elements per array and token: all threads at D = 128, half at 64
-        Frag<T> xq = frag_zero<T>(), xd = frag_zero<T>(), xqt = frag_zero<T>(), xdt = frag_zero<T>();
-        if (t >= 0) {
-          const size_t row = static_cast<size_t>(b) * a.L + t;
-          if (hh < a.Hg) {
-            const int h = g * a.Hg + hh;
-            xq = frag_load<T>(static_cast<const S*>(a.q) + b * a.qs[0] + t * a.qs[1] + h * a.qs[2] + d);
-            xd = frag_load<T>(static_cast<const S*>(a.dN) + (row * a.Hq + h) * D + d);
-          }
-          xqt = frag_load<T>(static_cast<const S*>(a.qT) + (row * a.G + g) * D * 16 + e);
-          xdt = frag_load<T>(static_cast<const S*>(a.dT) + (row * a.G + g) * D * 16 + e);
-        }
-        frag_store<T>(&sm.qn[uu][hh][d], xq);
-        frag_store<T>(&sm.dn[uu][hh][d], xd);
-        frag_store<T>(&sm.qt[uu][e], xqt);
-        frag_store<T>(&sm.dt[uu][e], xdt);
+      const int t = tok[uu], tcl = t < 0 ? 0 : t;
+      const size_t row = static_cast<size_t>(b) * a.L + tcl;
+      const bool tv = t >= 0;
+      rq[uu] = frag_load_if<T>(static_cast<const S*>(a.q) + b * a.qs[0] + tcl * a.qs[1] + hc * a.qs[2] + d,
+                               estage && tv && hh < a.Hg);
+      rd[uu] = frag_load_if<T>(static_cast<const S*>(a.dN) + (row * a.Hq + hc) * D + d, estage && tv && hh < a.Hg);
+      rqt[uu] = frag_load_if<T>(static_cast<const S*>(a.qT) + (row * a.G + g) * D * 16 + (estage ? e : 0), estage && tv);
+      rdt[uu] = frag_load_if<T>(static_cast<const S*>(a.dT) + (row * a.G + g) * D * 16 + (estage ? e : 0), estage && tv);
+      const float2 sv = a.stat[(row * a.Hq + hs) * 3 + X];
+      const float gv = to_f32<T>(static_cast<const S*>(a.gates)[b * a.gs[0] + tcl * a.gs[1] + hs * a.gs[2] + X]);
+      const bool sok = tv && (tid & 15) < a.Hg;
+      rst[uu] = sok ? sv : make_float2(0.f, 0.f);
+      rgt[uu] = sok ? gv : 0.f;
+      rtok[uu] = t;
+    }
+  };
+  auto store_stage = [&]() {
+#pragma unroll
+    for (int uu = 0; uu < TT; ++uu) {
+      if (estage) {
+        frag_store<T>(&sm.qn[uu][hh][d], rq[uu]);
+        frag_store<T>(&sm.dn[uu][hh][d], rd[uu]);
+        frag_store<T>(&sm.qt[uu][e], rqt[uu]);
+        frag_store<T>(&sm.dt[uu][e], rdt[uu]);
       }
       if (tid < 16) {
-        float2 stv = make_float2(0.f, 0.f);
-        float gv = 0.f;
-        if (t >= 0 && tid < a.Hg) {
-          const int hq = g * a.Hg + tid;
-          stv = a.stat[((static_cast<size_t>(b) * a.L + t) * a.Hq + hq) * 3 + X];
-          gv = to_f32<T>(static_cast<const S*>(a.gates)[b * a.gs[0] + t * a.gs[1] + hq * a.gs[2] + X]);
-        }
-        sm.st[uu][tid] = stv;
-        sm.gt[uu][tid] = gv;
-        if (tid == 0) sm.tok[uu] = t;
+        sm.st[uu][tid] = rst[uu];
+        sm.gt[uu][tid] = rgt[uu];
+        if (tid == 0) sm.tok[uu] = rtok[uu];
       }
     }
-    __syncthreads();
+  };
+  {
+    int tok[TT];
+#pragma unroll
+    for (int uu = 0; uu < TT; ++uu) tok[uu] = token_of(i0 + uu);
+    load_stage(tok);
+#pragma unroll
+    for (int uu = 0; uu < TT; ++uu) ntok[uu] = token_of(i0 + TT + uu);
+  }
+  for (int ib = i0; ib < i1; ib += TT) {
+    lds_barrier();  // the previous stage has been read
+    store_stage();
+    lds_barrier();
+    // the next stage's rows (its tokens were read a stage ago), then the
+    // tokens of the stage after it
+    load_stage(ntok);
+#pragma unroll
+    for (int uu = 0; uu < TT; ++uu) ntok[uu] = token_of(ib + 2 * TT + uu);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int pp = 0; pp < TT; pp += 2) {
       f32x4 P[2], dS[2];
