@@ -86,6 +86,23 @@ __device__ __forceinline__ float from_f32<F32>(float x) {
   return x;
 }
 
+// A fragment of ones (every one of the 8 elements is 1.0).
+template <class T>
+__device__ __forceinline__ Frag<T> frag_ones();
+template <>
+__device__ __forceinline__ Frag<BF16> frag_ones<BF16>() {
+  Frag<BF16> f;
+  f.v = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<F32> frag_ones<F32>() {
+  Frag<F32> f;
+  f.lo = f32x4{1.f, 1.f, 1.f, 1.f};
+  f.hi = f.lo;
+  return f;
+}
+
 template <class T>
 __device__ __forceinline__ Frag<T> frag_zero();
 template <>

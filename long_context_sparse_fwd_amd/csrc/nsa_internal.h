@@ -72,7 +72,7 @@ struct PrefillArgs {
   // [B][Lq][Hq][D], which k_sel completes and rounds to bf16 once; null for
   // fp32 output (out itself holds that part until k_sel adds to it).
   float* part;
-  void* kct;   // [B][G][NcT] 64-block tiles of block means of K (bf16: the high part)
+  void* kct;   // [B][G][NcT] 64-block tiles of block means of K times scale_log2 (bf16: the high part)
   void* kclt;  // bf16 input only: the low part, bf16(mean - high), same layout
   void* vct;   // [B][G][NcT] 64-block V^T tiles of block means of V
   int64_t qs[3], ks[3], vs[3], gs[3], os[3];

@@ -69,12 +69,22 @@ __device__ __forceinline__ f32x4 load4<F32>(const float* p) {
 
 // The block means of K enter the block scores, and the selection is judged
 // against exact means: with bf16 operands the mean is carried as a high part
-// plus a bf16 low part (hi + lo holds ~16 significant bits), and every
-// compressed-branch QK product is the sum of two MFMAs.
+// plus a bf16 low part (hi + lo holds ~16 significant bits), and the
+// compressed-branch QK products of the scoring pass add the low part with a
+// second MFMA where it matters (kLoMinBlocks).
 template <class T>
 constexpr bool kSplitKc = false;
 template <>
 constexpr bool kSplitKc<BF16> = true;
+
+// Queries that see at least this many block means score them from the high
+// parts alone (plain geometry). A block score is a head sum of probabilities
+// of about 1/n each among n visible blocks, so the relative logit error of
+// the bf16 high part (~2^-9 per element) moves a score by O(1/n): measured
+// over random i.i.d. N(0,1) rows at 512 blocks, at most 7.6e-6 (median
+// 5.5e-6), against 1e-4 gaps the selection has to resolve exactly; at 64
+// blocks the same error reaches 6.9e-5, hence the low parts below the bound.
+constexpr int kLoMinBlocks = 512;
 
 // Tiles in the compressed kernel's LDS stage: two buffers of K and V, plus
 // the low part of K when the means are split and LOL (low part through LDS)
@@ -212,6 +222,7 @@ __global__ __launch_bounds__(256) void k_prep(PrefillArgs a) {
         sk *= (1.0f / 64.0f);
         sv *= (1.0f / 64.0f);
       }
+      sk *= a.scale_log2;  // K means are kept as log2-domain logit factors
       const S hi = from_f32<T>(sk);
       kc[ktile_off(r, d, D)] = hi;
       if (kSplitKc<T>) kcl[ktile_off(r, d, D)] = from_f32<T>(sk - to_f32<T>(hi));
@@ -247,6 +258,7 @@ __global__ __launch_bounds__(256) void k_ctile(PrefillArgs a) {
     if (is_v) {
       hi_t[vtile_off(r, d)] = from_f32<T>(x);
     } else {
+      x *= a.scale_log2;  // K representations are kept as log2-domain logit factors
       const S h = from_f32<T>(x);
       hi_t[ktile_off(r, d, D)] = h;
       if (kSplitKc<T>) lo_t[ktile_off(r, d, D)] = from_f32<T>(x - to_f32<T>(h));
@@ -473,67 +485,162 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   TileStager<T, D, NT> stg;
 
+  // The three phases below (window, compressed pass 1, compressed pass 2)
+  // step over 64-key chunks x = 0 .. n-1 in two segments each, separated by
+  // LDS barriers: segment 1 is the softmax arithmetic of chunk x (VALU),
+  // segment 2 the P.V products of chunk x and the Q.K products of chunk
+  // x + 1 (MFMA). Waves w and w + 4 share a SIMD; waves 4..7 run one segment
+  // behind waves 0..3, so between two barriers one wave of every SIMD does
+  // vector work while the other keeps the matrix unit busy.
+  // Staging: stage buffer y & 1 holds K (and the low part of K) and V of
+  // chunk y. D(y) = {K(y), V(y - 1)} (indices clamped to the last chunk)
+  // replaces K(y - 2) and V(y - 3); each wave loads and stores its share of
+  // D(y) within one segment 1 (so the loaded registers are not live across
+  // the products): the trailing waves in segment 1 of chunk y - 2, the
+  // leading ones in segment 1 of chunk y - 1, one period later. Both periods
+  // come after the last reads of K(y - 2) and V(y - 3) (the trailing waves'
+  // segment 2 of chunk y - 3) and before the first read of D(y) (the leading
+  // waves' segment 2 of chunk y - 1), and in neither does the other group
+  // read the slots being written.
+  const bool trail = NW == 8 && wave >= 4;
+  // Masks compare the lane's key offset g4 = 4 grp with wave-uniform bounds,
+  // so no per-key lane offsets stay live.
+  const int g4 = 4 * grp;
+
+  static_assert(TPW == 2, "the low-part products below are written for two tokens per wave");
+  // S^T of one 64-key chunk for the wave's tokens, accumulated onto init[qt]:
+  // st[qt][kt][i] holds key 16 kt + 4 grp + i of the chunk, head col. Token
+  // qt adds the products with the low parts kl when lo[qt] (wave-uniform).
+  // The k-steps are the outer loop: the eight accumulators (4 key tiles x 2
+  // tokens) each take one product per k-step, so consecutive products do not
+  // depend on each other (an MFMA that accumulates onto the previous one's
+  // result waits for it to finish).
+  auto qk_chunk = [&](const S* kb, const S* kl, const bool (&lo)[TPW], const f32x4 (&init)[TPW],
+                      f32x4 (&st)[TPW][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < TPW; ++qt) st[qt][kt] = init[qt];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      Frag<T> kf[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) kf[kt] = frag_load<T>(kb + ktile_frag(kt, s, lane, D));
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < TPW; ++qt) mma(st[qt][kt], kf[kt], qf[qt][s]);
+    }
+    if (kSplitKc<T> && lo[0]) {  // the low parts after the high ones (lo[1] implies lo[0])
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        Frag<T> kf[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) kf[kt] = frag_load<T>(kl + ktile_frag(kt, s, lane, D));
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) mma(st[0][kt], kf[kt], qf[0][s]);
+        if (lo[1]) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) mma(st[1][kt], kf[kt], qf[1][s]);
+        }
+      }
+    }
+  };
+  // acc[qt] += V^T . P^T over one 64-key chunk; pf[qt][s2] holds the
+  // probabilities of keys [32 s2, 32 s2 + 32) (pack_p order). With lacc, the
+  // softmax denominators too, on the matrix unit: a product with an all-ones
+  // A operand sums the packed probabilities over the keys, and every lane of
+  // a column receives its head's sum (the two products of an accumulator
+  // are sixteen products apart).
+  const Frag<T> ones = frag_ones<T>();
+  auto pv_chunk = [&](const S* vb, const Frag<T> (&pf)[TPW][2], f32x4 (*lacc)[TPW]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      Frag<T> vf[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vf[dt] = frag_load<T>(vb + vtile_frag(dt, s2, lane));
+#pragma unroll
+      for (int qt = 0; qt < TPW; ++qt)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) mma(oacc[qt][dt], vf[dt], pf[qt][s2]);
+      if (lacc != nullptr) {
+#pragma unroll
+        for (int qt = 0; qt < TPW; ++qt) mma((*lacc)[qt], ones, pf[qt][s2]);
+      }
+    }
+  };
+  auto sum_chunk = [&](const Frag<T> (&pf)[TPW][2], f32x4 (&lacc)[TPW]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int qt = 0; qt < TPW; ++qt) mma(lacc[qt], ones, pf[qt][s2]);
+  };
+  // an LDS barrier that no instruction is scheduled across
+  auto seg_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The pipeline of one phase over n chunks. stage_(y, commit): issue the
+  // loads of D(y) (commit = false) or store them into their slots (true);
+  // qk_(x): Q.K products of chunk x into st; seg1_(x): softmax arithmetic of
+  // chunk x into pf; seg2_(x): the products of chunk x that use pf.
+  auto run_phase = [&](int n, auto&& stage_, auto&& qk_, auto&& seg1_, auto&& seg2_) __attribute__((always_inline)) {
+    stage_(0, false);
+    stage_(0, true);
+    stage_(1, false);
+    stage_(1, true);
+    seg_barrier();
+    qk_(0);
+    if (trail) seg_barrier();
+#pragma unroll 1
+    for (int x = 0; x < n; ++x) {
+      const int y = trail ? x + 2 : x + 1;
+      const bool stg_y = y >= 2 && y <= n;
+      if (stg_y) stage_(y, false);
+      seg1_(x);
+      if (stg_y) stage_(y, true);
+      seg_barrier();
+      // the wave feeding the matrix unit goes first; its partner's vector
+      // work fills the issue slots between the products
+      __builtin_amdgcn_s_setprio(2);
+      seg2_(x);
+      if (x + 1 < n) qk_(x + 1);
+      __builtin_amdgcn_s_setprio(0);
+      seg_barrier();
+    }
+    if (!trail) seg_barrier();
+  };
+  const std::integral_constant<bool, true> kT{};
+  const std::integral_constant<bool, false> kF{};
+  bool nolo[TPW];
+#pragma unroll
+  for (int qt = 0; qt < TPW; ++qt) nolo[qt] = false;
+  f32x4 st[TPW][4], zero4[TPW];
+  Frag<T> pf[TPW][2];
+#pragma unroll
+  for (int qt = 0; qt < TPW; ++qt) zero4[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the compressed gate is applied once at the end: the accumulators carry
+  // gate_win O_win / gc + P . Vc, then are scaled by gc (gc > 0 stands in for
+  // a zero gate, whose branch then contributes 2^-30 of its output)
+  float gc[TPW];
+#pragma unroll
+  for (int qt = 0; qt < TPW; ++qt) gc[qt] = fmaxf(gcmp[qt], 0x1p-30f);
+
   // ---- sliding window over the workgroup's band of key blocks
   {
     const S* KT = static_cast<const S*>(a.kt) + bgoff * a.Nb * TILE;
     const S* VT = static_cast<const S*>(a.vt) + bgoff * a.Nb * TILE;
-    const int b0 = max(0, T0 - a.w + 1) >> 6, b1 = Tl >> 6;
-    float mw[TPW], lw[TPW];
+    const int b0 = max(0, T0 - a.w + 1) >> 6, b1 = Tl >> 6, nb = b1 - b0 + 1;
+    float mw[TPW], alpha_w[TPW];
+    f32x4 lw[TPW];
 #pragma unroll
     for (int qt = 0; qt < TPW; ++qt) {
       mw[qt] = kNegBig;
-      lw[qt] = 0.f;
+      lw[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    stg.issue(KT + static_cast<int64_t>(b0) * TILE, VT + static_cast<int64_t>(b0) * TILE, nullptr, tid);
-    stg.commit(stage, stage + TILE, nullptr, tid);
-    __syncthreads();
-    // INNER: both halves of the block lie inside the window of every token of
-    // the workgroup (no band test, no masks); the band's edge blocks take
-    // the general body. Three loops, so each body is straight-line code.
-    auto stepw = [&](auto inner_c, int blk) __attribute__((always_inline)) {
-      constexpr bool INNER = decltype(inner_c)::value;
-      const int buf = (blk - b0) & 1;
-      const bool more = blk < b1;
-      if (more)
-        stg.issue(KT + static_cast<int64_t>(blk + 1) * TILE, VT + static_cast<int64_t>(blk + 1) * TILE, nullptr,
-                  tid);
-      const S* kt = stage + buf * BUF;
-      const S* vt = kt + TILE;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int kb = 64 * blk + 32 * s2;
-        if (!INNER && (kb > tw + TPW - 1 || kb + 31 < tw - a.w + 1)) continue;  // outside this wave's band
-        Frag<T> kf[2][KS];
-        Frag<T> vf[DT];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-          for (int s = 0; s < KS; ++s) kf[h2][s] = frag_load<T>(kt + ktile_frag(2 * s2 + h2, s, lane, D));
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vf[dt] = frag_load<T>(vt + vtile_frag(dt, s2, lane));
-        // all 32 keys inside every token's window: no masks needed
-        const bool full = INNER || (kb >= tw + TPW - a.w && kb + 31 <= tw && tw + TPW - 1 < Le);
-#pragma unroll
-        for (int qt = 0; qt < TPW; ++qt) {
-          const int t = tw + qt;
-          f32x4 st[2];
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            st[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KS; ++s) mma(st[h2], kf[h2][s], qf[qt][s]);
-          }
-          if (full)
-            online_step<T, DT, false>(st, kb, 0, 0, grp, sl2, mw[qt], lw[qt], oacc[qt], vf);
-          else
-            online_step<T, DT, true>(st, kb, t - a.w + 1, t < Le ? t : -1, grp, sl2, mw[qt], lw[qt],
-                                     oacc[qt], vf);
-        }
-      }
-      if (more) stg.commit(stage + (buf ^ 1) * BUF, stage + (buf ^ 1) * BUF + TILE, nullptr, tid);
-      __syncthreads();
-    };
-    // inner blocks: 64 blk >= (last token + 1) - w and 64 blk + 63 <= first token
+    // inner blocks [lo, hi]: inside the window of every token of the
+    // workgroup (64 blk >= last token + 1 - w and 64 blk + 63 <= first token)
     int lo = b1 + 1, hi = b1;
     if (T0 + TPW * NW - 1 < Le) {
       const int x = T0 + TPW * NW - a.w;  // lowest first key of an inner block
@@ -541,182 +648,255 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       hi = T0 >= 63 ? min(b1, (T0 - 63) >> 6) : -1;
       if (lo > hi) lo = hi + 1;
     }
-    int blk = b0;
-    for (; blk < lo && blk <= b1; ++blk) stepw(std::integral_constant<bool, false>{}, blk);
-    for (; blk <= hi; ++blk) stepw(std::integral_constant<bool, true>{}, blk);
-    for (; blk <= b1; ++blk) stepw(std::integral_constant<bool, false>{}, blk);
+    auto stage_w = [&](int y, bool commit) __attribute__((always_inline)) {
+      const int64_t yk = b0 + min(y, nb - 1), yv = b0 + max(min(y - 1, nb - 1), 0);
+      S* sl = stage + (y & 1) * BUF;
+      S* slv = stage + ((y + 1) & 1) * BUF + TILE;
+      if (y == 0) {
+        if (!commit)
+          stg.issue(KT + yk * TILE, VT + yk * TILE, nullptr, tid);
+        else
+          stg.commit(sl, sl + TILE, nullptr, tid);
+      } else if (!commit) {
+        stg.issue(KT + yk * TILE, y == 1 ? nullptr : VT + yv * TILE, nullptr, tid);
+      } else {
+        stg.commit(sl, y == 1 ? nullptr : slv, nullptr, tid);
+      }
+    };
+    auto qk_w = [&](int x) __attribute__((always_inline)) { qk_chunk(stage + (x & 1) * BUF, nullptr, nolo, zero4, st); };
+    // keys outside a token's window [t - w + 1, t] are masked on the edge
+    // blocks; the running maxima rise lazily (kLazyMax), so the rescale is rare
+    auto sm_w = [&](auto mask_c, int blk) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_c)::value;
+      float lmx[TPW];
+#pragma unroll
+      for (int qt = 0; qt < TPW; ++qt) {
+        const int t = tw + qt, klo = t - a.w + 1, khi = t < Le ? t : -1;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = st[qt][kt][i];
+            if constexpr (MASK) {  // key 64 blk + 16 kt + i + g4 inside [klo, khi]; bounds uniform
+              const int kb = 64 * blk + 16 * kt + i;
+              x = (g4 >= klo - kb && g4 <= khi - kb) ? x : -INFINITY;
+            }
+            st[qt][kt][i] = x;
+            mx = fmaxf(mx, x);
+          }
+        lmx[qt] = fmaxf(mx * sl2, kNegBig);
+      }
+      // each token decides alone (its wave partner differs between tilings
+      // of the query rows, and the rows must not depend on the tiling); the
+      // accumulators are rescaled in segment 2, ahead of the products
+#pragma unroll
+      for (int qt = 0; qt < TPW; ++qt) {
+        alpha_w[qt] = 1.f;
+        if (wave_any(lmx[qt] > mw[qt] + kLazyMax)) {
+          const float mn = fmaxf(mw[qt], col_max4(lmx[qt]));
+          alpha_w[qt] = fast_exp2(mw[qt] - mn);
+          lw[qt] *= alpha_w[qt];
+          mw[qt] = mn;
+        }
+      }
+#pragma unroll
+      for (int qt = 0; qt < TPW; ++qt) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st[qt][kt][i] = fast_exp2(fmaf(st[qt][kt][i], sl2, -mw[qt]));
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) pf[qt][s2] = pack_p<T>(st[qt][2 * s2], st[qt][2 * s2 + 1]);
+      }
+    };
+    auto seg1_w = [&](int x) __attribute__((always_inline)) {
+      const int blk = b0 + x;
+      if (blk >= lo && blk <= hi)
+        sm_w(kF, blk);
+      else
+        sm_w(kT, blk);
+    };
+    auto seg2_w = [&](int x) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qt = 0; qt < TPW; ++qt)
+        if (wave_any(alpha_w[qt] != 1.f)) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] *= alpha_w[qt];
+        }
+      pv_chunk(stage + (x & 1) * BUF + TILE, pf, &lw);
+    };
+    run_phase(nb, stage_w, qk_w, seg1_w, seg2_w);
 #pragma unroll
     for (int qt = 0; qt < TPW; ++qt) {
-      const float lt = col_sum4(lw[qt]);
-      const float f = lt > 0.f ? gwin[qt] / lt : 0.f;
+      const float lt = lw[qt][0];
+      const float f = lt > 0.f ? gwin[qt] / (lt * gc[qt]) : 0.f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] *= f;
     }
   }
 
-  // ---- compressed branch
+  // ---- compressed branch. The tiles of the block means of K hold them
+  // scaled by softmax_scale * log2(e), so Q.K products are log2-domain logits.
   const int nch = (nvis_of(a, Tl) + 63) >> 6;
   const S* KC = static_cast<const S*>(a.kct) + bgoff * a.NcT * TILE;
   const S* KCL = kSplitKc<T> ? static_cast<const S*>(a.kclt) + bgoff * a.NcT * TILE : nullptr;
   const S* VC = static_cast<const S*>(a.vct) + bgoff * a.NcT * TILE;
+  // chunks [0, nfull) are visible to both tokens in full (no masks)
+  const int nfull = __builtin_amdgcn_readfirstlane(min(nch, nvis[0] >> 6));
 
   // pass 1: log-sum-exp (log2 domain) from the high part of the block means.
   // An error e_h in a head's log-sum-exp scales all of that head's
   // probabilities by exp(-e_h); the differences between block scores, which
-  // the selection compares, move only in second order. Pass 2 uses the full
-  // precision logits.
-  float m[TPW], ls[TPW];
-#pragma unroll
-  for (int qt = 0; qt < TPW; ++qt) {
-    m[qt] = kNegBig;
-    ls[qt] = 0.f;
-  }
+  // the selection compares, move only in second order. The logits are kept
+  // relative to a per-head offset m (the products start from -m), which
+  // rises lazily; the sums run on the matrix unit.
+  float lse2[TPW];
   if (nch > 0) {
-    stg.issue(KC, nullptr, nullptr, tid);
-    stg.commit(stage, nullptr, nullptr, tid);
-    __syncthreads();
-  }
-  // Fully visible chunks first, then the partial ones, each loop one
-  // straight-line body (FULL drops the masks).
-  auto step1 = [&](auto full_c, int c) __attribute__((always_inline)) {
-    constexpr bool FULL = decltype(full_c)::value;
-    const int buf = c & 1;
-    const bool more = c + 1 < nch;
-    if (more) stg.issue(KC + static_cast<int64_t>(c + 1) * TILE, nullptr, nullptr, tid);
-    const S* kc = stage + buf * BUF;
-    f32x4 st[TPW][4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      Frag<T> kf[KS];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) kf[s] = frag_load<T>(kc + ktile_frag(kt, s, lane, D));
-#pragma unroll
-      for (int qt = 0; qt < TPW; ++qt) {
-        st[qt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) mma(st[qt][kt], kf[s], qf[qt][s]);
-      }
-    }
+    float m[TPW];
+    f32x4 negm[TPW], l1[TPW];
 #pragma unroll
     for (int qt = 0; qt < TPW; ++qt) {
-      // maximum over the raw scores (sl2 > 0); the scaling goes into the exponent
-      float lmx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = (FULL || 64 * c + 16 * kt + 4 * grp + i < nvis[qt]) ? st[qt][kt][i] : -INFINITY;
-          st[qt][kt][i] = x;
-          lmx = fmaxf(lmx, x);
-        }
-      lmx = fmaxf(lmx * sl2, kNegBig);
-      if (wave_any(lmx > m[qt] + kLazyMax)) {
-        const float mn = fmaxf(m[qt], col_max4(lmx));
-        ls[qt] *= fast_exp2(m[qt] - mn);
-        m[qt] = mn;
-      }
-      float sum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sum += fast_exp2(fmaf(st[qt][kt][i], sl2, -m[qt]));
-      ls[qt] += sum;
+      m[qt] = 0.f;
+      negm[qt] = zero4[qt];
+      l1[qt] = zero4[qt];
     }
-    if (more) stg.commit(stage + (buf ^ 1) * BUF, nullptr, nullptr, tid);
-    __syncthreads();
-  };
-  // chunks [0, nfull) are visible to both tokens in full
-  const int nfull = __builtin_amdgcn_readfirstlane(min(nch, nvis[0] >> 6));
-  {
-    int c = 0;
-    for (; c < nfull; ++c) step1(std::integral_constant<bool, true>{}, c);
-    for (; c < nch; ++c) step1(std::integral_constant<bool, false>{}, c);
-  }
-  float lse2[TPW];
+    auto stage_1 = [&](int y, bool commit) __attribute__((always_inline)) {
+      if (!commit)
+        stg.issue(KC + static_cast<int64_t>(min(y, nch - 1)) * TILE, nullptr, nullptr, tid);
+      else
+        stg.commit(stage + (y & 1) * BUF, nullptr, nullptr, tid);
+    };
+    auto qk_1 = [&](int x) __attribute__((always_inline)) {
+      qk_chunk(stage + (x & 1) * BUF, nullptr, nolo, negm, st);
+    };
+    auto sm_1 = [&](auto full_c, int x) __attribute__((always_inline)) {
+      constexpr bool FULL = decltype(full_c)::value;
+      float lmx[TPW];
 #pragma unroll
-  for (int qt = 0; qt < TPW; ++qt) {
-    const float tot = col_sum4(ls[qt]);
-    lse2[qt] = (nvis[qt] > 0 && colv) ? m[qt] + fast_log2(tot) : INFINITY;
-  }
-
-  // pass 2: probabilities, gate_cmp * P . Vc into the accumulators, block scores
-  float* sc = scb + static_cast<size_t>(wave) * TPW * NcPad;
-  if (nch > 0) {
-    stg.issue(KC, VC, LOLDS ? KCL : nullptr, tid);
-    stg.commit(stage, stage + TILE, LOLDS ? stage + 2 * TILE : nullptr, tid);
-    __syncthreads();
-  }
-  // One 64-key chunk; FULL: every key visible to both tokens (no masks).
-  // The full chunks come first and run as one loop, the partial ones as a
-  // second: each loop body is straight-line code (no branch between the QK
-  // products, the softmax and the PV products) that the compiler schedules
-  // as one region. The block scores are computed even when the caller
-  // injects the selection (they are then unused).
-  auto chunk2 = [&](auto full_c, int c, const S* kc, const S* vc, const S* kcl) __attribute__((always_inline)) {
-    constexpr bool FULL = decltype(full_c)::value;
+      for (int qt = 0; qt < TPW; ++qt) {
+        float mx = -INFINITY;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      f32x4 st[TPW][2];
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        Frag<T> kf[KS], kl[KS];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          kf[s] = frag_load<T>(kc + ktile_frag(2 * s2 + h2, s, lane, D));
-          if (kSplitKc<T>) kl[s] = frag_load<T>(kcl + ktile_frag(2 * s2 + h2, s, lane, D));
-        }
-#pragma unroll
-        for (int qt = 0; qt < TPW; ++qt) {
-          st[qt][h2] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < KS; ++s) {
-            mma(st[qt][h2], kf[s], qf[qt][s]);
-            if (kSplitKc<T>) mma(st[qt][h2], kl[s], qf[qt][s]);
+          for (int i = 0; i < 4; ++i) {
+            const float v = (FULL || g4 < nvis[qt] - (64 * x + 16 * kt + i)) ? st[qt][kt][i] : -INFINITY;
+            st[qt][kt][i] = v;
+            mx = fmaxf(mx, v);
           }
+        lmx[qt] = mx;
+      }
+      // raise the offsets: on the first chunk to its maxima (block 0 is
+      // visible to every token that sees any block; one that sees none keeps
+      // 0), later only when a logit passes the offset by kLazyMax (rare);
+      // each token decides alone
+#pragma unroll
+      for (int qt = 0; qt < TPW; ++qt) {
+        if (x == 0 || wave_any(lmx[qt] > kLazyMax)) {
+          const float cm = col_max4(lmx[qt]);
+          const float d = x == 0 ? (cm == -INFINITY ? 0.f : cm) : fmaxf(cm, 0.f);
+          l1[qt] *= fast_exp2(-d);
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) st[qt][kt] -= d;
+          m[qt] += d;
+          negm[qt] = f32x4{-m[qt], -m[qt], -m[qt], -m[qt]};
         }
       }
-      Frag<T> vf[DT];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) vf[dt] = frag_load<T>(vc + vtile_frag(dt, s2, lane));
 #pragma unroll
       for (int qt = 0; qt < TPW; ++qt) {
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st[qt][kt][i] = fast_exp2(st[qt][kt][i]);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) pf[qt][s2] = pack_p<T>(st[qt][2 * s2], st[qt][2 * s2 + 1]);
+      }
+    };
+    auto seg1_1 = [&](int x) __attribute__((always_inline)) {
+      if (x < nfull)
+        sm_1(kT, x);
+      else
+        sm_1(kF, x);
+    };
+    auto seg2_1 = [&](int) __attribute__((always_inline)) { sum_chunk(pf, l1); };
+    run_phase(nch, stage_1, qk_1, seg1_1, seg2_1);
+#pragma unroll
+    for (int qt = 0; qt < TPW; ++qt) lse2[qt] = (nvis[qt] > 0 && colv) ? m[qt] + fast_log2(l1[qt][0]) : INFINITY;
+  }
+
+  // pass 2: probabilities (the products start from -lse), P . Vc into the
+  // accumulators, block scores (computed even when the caller injects the
+  // selection; they are then unused). The low parts of the means enter the
+  // products only where a query sees fewer than kLoMinBlocks blocks or the
+  // geometry is general.
+  float* sc = scb + static_cast<size_t>(wave) * TPW * NcPad;
+  if (nch > 0) {
+    f32x4 negl[TPW];
+#pragma unroll
+    for (int qt = 0; qt < TPW; ++qt) negl[qt] = f32x4{-lse2[qt], -lse2[qt], -lse2[qt], -lse2[qt]};
+    // The low parts are added by a token iff it sees fewer than kLoMinBlocks
+    // blocks (or the geometry is general), never by the tiling of the query
+    // rows; the workgroup stages them in LDS (slo) if any of its tokens adds
+    // them. A token past the last query row follows token 0 of its wave; nvis
+    // grows with the token, so lo[1] implies lo[0].
+    bool lo[TPW];
+    lo[0] = kSplitKc<T> && (!a.cmp_in_prep || nvis[0] < kLoMinBlocks);
+    lo[1] = tw + 1 < Le ? kSplitKc<T> && (!a.cmp_in_prep || nvis[1] < kLoMinBlocks) : lo[0];
+    const bool slo = kSplitKc<T> && LOLDS && (!a.cmp_in_prep || nvis_of(a, T0) < kLoMinBlocks);
+    auto stage_2 = [&](int y, bool commit) __attribute__((always_inline)) {
+      const int64_t yk = min(y, nch - 1), yv = max(min(y - 1, nch - 1), 0);
+      S* sl = stage + (y & 1) * BUF;
+      S* slv = stage + ((y + 1) & 1) * BUF + TILE;
+      if (y == 0) {
+        if (!commit)
+          stg.issue(KC + yk * TILE, VC + yk * TILE, slo ? KCL + yk * TILE : nullptr, tid);
+        else
+          stg.commit(sl, sl + TILE, slo ? sl + 2 * TILE : nullptr, tid);
+      } else if (!commit) {
+        stg.issue(KC + yk * TILE, y == 1 ? nullptr : VC + yv * TILE, slo ? KCL + yk * TILE : nullptr, tid);
+      } else {
+        stg.commit(sl, y == 1 ? nullptr : slv, slo ? sl + 2 * TILE : nullptr, tid);
+      }
+    };
+    auto qk_2 = [&](int x) __attribute__((always_inline)) {
+      const S* kl = slo ? stage + (x & 1) * BUF + 2 * TILE : KCL + static_cast<int64_t>(x) * TILE;
+      qk_chunk(stage + (x & 1) * BUF, kl, lo, negl, st);
+    };
+    auto sm_2 = [&](auto full_c, int x) __attribute__((always_inline)) {
+      constexpr bool FULL = decltype(full_c)::value;
+#pragma unroll
+      for (int qt = 0; qt < TPW; ++qt) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float p = fast_exp2(st[qt][h2][i] * sl2 - lse2[qt]);
-            st[qt][h2][i] = (FULL || 64 * c + 32 * s2 + 16 * h2 + 4 * grp + i < nvis[qt]) ? p : 0.f;
+            const float p = fast_exp2(st[qt][kt][i]);
+            st[qt][kt][i] = (FULL || g4 < nvis[qt] - (64 * x + 16 * kt + i)) ? p : 0.f;
           }
-        {
-          // the head sum of key 16·c₃ + 4·grp + 2·c₀ + c₁ of this half (c = col)
-          const float r = row_scatter_sum8(st[qt], col);
-          sc[qt * NcPad + 64 * c + 32 * s2 + 16 * ((col >> 3) & 1) + 4 * grp + 2 * (col & 1) + ((col >> 1) & 1)] = r;
-        }
-        const Frag<T> pf = pack_p<T>(st[qt][0] * gcmp[qt], st[qt][1] * gcmp[qt]);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) mma(oacc[qt][dt], vf[dt], pf);
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const f32x4 pr[2] = {st[qt][2 * s2], st[qt][2 * s2 + 1]};
+          // head sum of key 16·c₃ + 4·grp + 2·c₀ + c₁ of the half (c = col)
+          sc[qt * NcPad + 64 * x + 32 * s2 + 16 * ((col >> 3) & 1) + 4 * grp + 2 * (col & 1) + ((col >> 1) & 1)] =
+              row_scatter_sum8(pr, col);
+          pf[qt][s2] = pack_p<T>(pr[0], pr[1]);
+        }
       }
-    }
-  };
-  auto step2 = [&](auto full_c, int c) __attribute__((always_inline)) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nch;
-    if (more)
-      stg.issue(KC + static_cast<int64_t>(c + 1) * TILE, VC + static_cast<int64_t>(c + 1) * TILE,
-                LOLDS ? KCL + static_cast<int64_t>(c + 1) * TILE : nullptr, tid);
-    const S* kc = stage + buf * BUF;
-    const S* vc = kc + TILE;
-    // low parts (bf16 inputs only): staged after V, or read from L2
-    const S* kcl = LOLDS ? vc + TILE : kSplitKc<T> ? KCL + static_cast<int64_t>(c) * TILE : nullptr;
-    chunk2(full_c, c, kc, vc, kcl);
-    if (more)
-      stg.commit(stage + (buf ^ 1) * BUF, stage + (buf ^ 1) * BUF + TILE,
-                 LOLDS ? stage + (buf ^ 1) * BUF + 2 * TILE : nullptr, tid);
-    __syncthreads();
-  };
-  int c = 0;
-  for (; c < nfull; ++c) step2(std::integral_constant<bool, true>{}, c);
-  for (; c < nch; ++c) step2(std::integral_constant<bool, false>{}, c);
+    };
+    auto seg1_2 = [&](int x) __attribute__((always_inline)) {
+      if (x < nfull)
+        sm_2(kT, x);
+      else
+        sm_2(kF, x);
+    };
+    auto seg2_2 = [&](int x) __attribute__((always_inline)) { pv_chunk(stage + (x & 1) * BUF + TILE, pf, nullptr); };
+    run_phase(nch, stage_2, qk_2, seg1_2, seg2_2);
+  }
+#pragma unroll
+  for (int qt = 0; qt < TPW; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] *= gc[qt];
+
 
   // ---- gate_win * O_win + gate_cmp * O_cmp -> out (fp32 output) or the fp32
   // partial rows (bf16 output); k_sel adds the selected branch, so a bf16
