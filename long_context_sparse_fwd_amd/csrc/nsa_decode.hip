@@ -20,6 +20,8 @@
 // K rows feed the S^T = K Q^T product straight from the caches. V rows are
 // written to LDS row-major (padded so that reads do not conflict) and each
 // lane gathers the 8 keys of its V^T operand fragment from there.
+#include <hip/hip_ext.h>
+
 #include "nsa_device.h"
 #include "nsa_internal.h"
 #include "nsa_topk.h"
@@ -632,10 +634,6 @@ size_t dec_lds_bytes(int NmaxPad, int D, bool bf16, bool logits_lds) {
          (logits_lds ? 16 * static_cast<size_t>(NmaxPad + 4) * sizeof(float) : 0);
 }
 
-static hipError_t record(hipEvent_t* ev, int i, hipStream_t st) {
-  return ev != nullptr ? hipEventRecord(ev[i], st) : hipSuccess;
-}
-
 template <class T, class O, int D, bool LGL, bool PARK>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st, hipEvent_t* ev) {
   constexpr bool kBf16 = sizeof(typename T::storage) == 2;
@@ -644,9 +642,15 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st, hipEvent_
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec<T, O, D, RING, LGL, PARK>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  if ((e = record(ev, 0, st)) != hipSuccess) return e;
+  if (ev != nullptr) {
+    // the dispatch itself records the events at the kernel's start and end,
+    // so the interval is the kernel's own duration (no launch latency)
+    void* args[] = {const_cast<DecodeArgs*>(&a)};
+    e = hipExtLaunchKernel(reinterpret_cast<const void*>(&k_dec<T, O, D, RING, LGL, PARK>), dim3(a.B * a.G),
+                           dim3(64 * kDecWaves), args, lds, st, ev[0], ev[1], 0);
+    return e != hipSuccess ? e : hipGetLastError();
+  }
   hipLaunchKernelGGL((k_dec<T, O, D, RING, LGL, PARK>), dim3(a.B * a.G), dim3(64 * kDecWaves), lds, st, a);
-  if ((e = record(ev, 1, st)) != hipSuccess) return e;
   return hipGetLastError();
 }
 
