@@ -69,7 +69,7 @@ struct DItem {
 
 // Rows outside [klo, khi] are loaded from the nearest row inside: their
 // logits are masked to -inf, so they get probability 0 and only have to be
-// finite.
+// finite. A call reads each cache row once, so the loads are non-temporal.
 template <class T, int D>
 __device__ __forceinline__ void dhalf_load(DHalf<T, D>& c, const DItem<T>& it, int lane) {
   const int col = lane & 15, grp = lane >> 4;
@@ -78,12 +78,12 @@ __device__ __forceinline__ void dhalf_load(DHalf<T, D>& c, const DItem<T>& it, i
     const int key = min(max(it.key0 + 16 * kt + col, it.klo), it.khi);
     const typename T::storage* p = it.kr + static_cast<int64_t>(key) * it.kst + 8 * grp;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) c.k[kt][s] = frag_load<T>(p + 32 * s);
+    for (int s = 0; s < D / 32; ++s) c.k[kt][s] = frag_load_nt<T>(p + 32 * s);
   }
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) {
     const int key = min(max(it.key0 + v_row<T, D>(lane, i), it.klo), it.khi);
-    c.v[i] = frag_load<T>(it.vr + static_cast<int64_t>(key) * it.vst + v_col<D>(lane));
+    c.v[i] = frag_load_nt<T>(it.vr + static_cast<int64_t>(key) * it.vst + v_col<D>(lane));
   }
 }
 
