@@ -12,11 +12,14 @@
 //               registers, then the sum over the 4 lanes of a column with
 //               the gfx950 lane swaps. Scores are written to a triangular
 //               float32 buffer.
-//  k_dsa_topk   one workgroup per query row: an exact radix select of the
-//               top-k (12 + 12 + 8 bits of an order-preserving key; the row
-//               cached in LDS up to a capacity), ties to the lower token,
-//               then an ordered ballot compaction that writes the chosen
-//               tokens ascending, padded with -1.
+//  k_dsa_topk_fast   one workgroup per query row: a threshold from a
+//               sample of the row, one read of the row that keeps the keys
+//               above it in LDS, an exact radix select of the top-k among
+//               them (ties to the lower token) and an ordered write of the
+//               chosen tokens, ascending, padded with -1. A row whose sample
+//               misses (too few or too many keys kept) is marked and left to
+//  k_dsa_topk_exact  an exact radix select over the whole row (16 bits of
+//               every order-preserving key cached in LDS).
 //  k_dsa_attn   one workgroup per query token: the chosen tokens' K rows
 //               (re-laid in MFMA-fragment order) and V rows (transposed) are
 //               staged in LDS 32 at a time, double-buffered, and every wave
@@ -299,6 +302,7 @@ constexpr int kTopkCand = 1024;   // exact keys kept for the candidates sharing 
 // Exclusive prefix sum of v over the workgroup (thread order) and its total.
 // wsum: kTopkWaves words of LDS; synchronises once, and the caller must
 // synchronise again before wsum is reused.
+template <int NW = kTopkWaves>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total, int lane, int wave) {
   uint32_t x = v;
 #pragma unroll
@@ -310,7 +314,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
   lds_barrier();
   uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     if (w < wave) before += wsum[w];
     tot += wsum[w];
   }
@@ -325,10 +329,11 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
 // bins), an exclusive scan gives the count above each slice, and the thread
 // whose slice holds the element writes result[0..1]. The caller synchronises
 // before reading result or reusing wsum.
+template <int NTH = kTopkThreads>
 __device__ void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* wsum, uint32_t* result, int tid,
                          int lane, int wave) {
-  const int per = nb > kTopkThreads ? nb / kTopkThreads : 1;
-  const int lo = (kTopkThreads - 1 - tid) * per, hi = min(nb, lo + per);
+  const int per = nb > NTH ? nb / NTH : 1;
+  const int lo = (NTH - 1 - tid) * per, hi = min(nb, lo + per);
   uint32_t c[8];
   uint32_t sum = 0;
   if (per == 8) {
@@ -341,7 +346,7 @@ __device__ void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* 
 #pragma unroll
   for (int j = 0; j < 8; ++j) sum += c[j];
   uint32_t tot;
-  uint32_t above = block_excl_scan(sum, wsum, &tot, lane, wave);
+  uint32_t above = block_excl_scan<NTH / 64>(sum, wsum, &tot, lane, wave);
 #pragma unroll
   for (int j = 7; j >= 0; --j) {
     if (lo + j < hi && above < need && need <= above + c[j]) {
@@ -352,17 +357,237 @@ __device__ void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* 
   }
 }
 
-// Exact top-k of one row of indexer scores: the chosen tokens are the k
-// largest 64-bit keys (orderable score, complement of the token), so equal
-// scores go to the lower token. The top 16 bits of every key are kept in LDS
-// (the row is read from memory once, up to 65536 candidates); a 12-bit and a
-// 4-bit digit find the top-16-bit value P of the k-th key; the candidates
-// whose top 16 bits equal P (few, on these inputs) are re-read, ranked by a
-// sort of their exact keys and the chosen ones marked in a bitmap. With more
-// than kTopkCand such candidates (heavy ties), the remaining 48 key bits are
-// resolved by 8-bit digits instead. Then an ordered compaction writes the
-// chosen tokens ascending.
-__global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
+constexpr int kFastThreads = 256, kFastWaves = kFastThreads / 64;
+constexpr int kFastCap = 4096;     // candidate keys a row may keep
+constexpr int kFastSample = 4096;  // sampled scores: 16 evenly spaced runs of kFastThreads
+constexpr int kTopkRedo = -2;      // first entry of a row the sampled pass leaves to the exact one
+constexpr int kRedoRows = 256;     // rows whose markers one exact-pass workgroup checks
+static_assert(kFastSample == 16 * kFastThreads, "one sampled score per thread and run");
+static_assert(2 * kDsaMaxTopK <= kFastCap, "the threshold aims between top_k and the capacity");
+
+// Top-k of one row of indexer scores by a sampled threshold (one workgroup
+// per row; the chosen set is the exact one, as in k_dsa_topk_exact).
+// 1. Rows longer than kFastCap: the orderable keys of 16 evenly spaced runs
+//    of 256 scores; two 11-bit digits of a radix select give a threshold
+//    theta (a 22-bit prefix) at or below the sample's r-th largest key, with
+//    r chosen so that about (top_k + kFastCap) / 2 keys of the row are
+//    expected at or above it. Shorter rows keep every key (theta = 0).
+// 2. One read of the row: every key >= theta goes to an LDS list as a 64-bit
+//    key (orderable score, complement of the token), each lane counting its
+//    keys first so that a wave takes its places with one atomic.
+// 3. If the list holds fewer than top_k keys, or more than kFastCap, the
+//    sample missed: the row's first entry is set to kTopkRedo and the exact
+//    pass redoes the row. Otherwise the top_k largest keys of the row are
+//    the top_k largest of the list (all of them pass theta): the k-th is
+//    found by radix digits of 11, 11 and 10 bits over the score (then over
+//    the token complement, only when the k-th score is shared by candidates
+//    not all chosen), the chosen tokens marked in a bitmap of the row and
+//    written ascending by a workgroup scan of the bitmap's popcounts.
+__global__ __launch_bounds__(kFastThreads) void k_dsa_topk_fast(DsaArgs a) {
+  extern __shared__ __align__(16) unsigned char tf_lds[];
+  uint64_t* cand = reinterpret_cast<uint64_t*>(tf_lds);                  // kFastCap keys; first the sample
+  uint32_t* hist = reinterpret_cast<uint32_t*>(tf_lds + kFastCap * 8);  // 2048 bins; later the row's bitmap
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t wsum[kFastWaves];
+  __shared__ uint32_t ncand;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int b = static_cast<int>(row / a.L), t = static_cast<int>(row % a.L);
+  const int n = t + 1, k = a.topk;
+  int32_t* out = a.idx + row * k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kFastThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  const float* S = a.scores + score_row(a, b, t);
+
+  // one radix digit over `items` entries: dig(i) is the digit of entry i, or
+  // -1 for an entry outside the known prefix; returns the bin of the
+  // need-th largest, its rank inside the bin and the bin's count
+  auto radix = [&](int items, int nbins, auto&& dig, uint32_t need, uint32_t& bin, uint32_t& rank,
+                   uint32_t& cnt) __attribute__((always_inline)) {
+    for (int i = tid; i < nbins; i += kFastThreads) hist[i] = 0u;
+    lds_barrier();
+    for (int i = tid; i < items; i += kFastThreads) {
+      const int d = dig(i);
+      if (d >= 0) atomicAdd(&hist[d], 1u);
+    }
+    lds_barrier();
+    find_bin<kFastThreads>(hist, nbins, need, wsum, res, tid, lane, wave);
+    lds_barrier();
+    bin = res[0];
+    rank = res[1];
+    cnt = hist[bin];
+    lds_barrier();   // before hist and res are written again
+  };
+
+  // 1. the threshold
+  uint32_t theta = 0u;
+  if (n > kFastCap) {
+    uint32_t* skey = reinterpret_cast<uint32_t*>(cand);
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = S[r * (n - kFastThreads) / 15 + tid];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) skey[r * kFastThreads + tid] = orderable(x[r]);
+    const uint32_t aim = static_cast<uint32_t>(k + kFastCap) / 2;
+    const uint32_t r = min(static_cast<uint32_t>(kFastSample),
+                           (aim * kFastSample + static_cast<uint32_t>(n) - 1) / static_cast<uint32_t>(n));
+    uint32_t d1, r1, c1, d2, r2, c2;
+    radix(kFastSample, 2048, [&](int i) { return static_cast<int>(skey[i] >> 21); }, r, d1, r1, c1);
+    radix(kFastSample, 2048, [&](int i) {
+      const uint32_t u = skey[i];
+      return (u >> 21) == d1 ? static_cast<int>((u >> 10) & 2047u) : -1;
+    }, r1, d2, r2, c2);
+    theta = (d1 << 21) | (d2 << 10);
+  }
+
+  // 2. the candidates: one read of the row (a scalar head up to 16-byte
+  // alignment, 16-byte loads, a scalar tail)
+  if (tid == 0) ncand = 0u;
+  lds_barrier();
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  // the lane's passing keys in order, with its place from the wave's prefix
+  // of the per-lane counts and one atomic per wave
+  auto append = [&](uint32_t cnt, auto&& emit) __attribute__((always_inline)) {
+    uint32_t pre = 0, tot = 0;
+#pragma unroll
+    for (int bit = 0; bit < 6; ++bit) {   // counts below 64
+      const uint64_t bal = __ballot((cnt >> bit) & 1u);
+      pre += static_cast<uint32_t>(__popcll(bal & below)) << bit;
+      tot += static_cast<uint32_t>(__popcll(bal)) << bit;
+    }
+    if (tot == 0u) return;
+    uint32_t base = 0u;
+    if (lane == 0) base = atomicAdd(&ncand, tot);
+    base = __shfl(base, 0, 64) + pre;
+    emit(base);
+  };
+  auto key_of = [](uint32_t u, int i) -> uint64_t {
+    return (static_cast<uint64_t>(u) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(i));
+  };
+  const int head = min(n, static_cast<int>((4 - ((reinterpret_cast<uintptr_t>(S) >> 2) & 3)) & 3));
+  const int nv = (n - head) >> 2;   // whole float4s after the head
+  const int tail0 = head + 4 * nv;
+  {
+    // head and tail: at most 3 + 3 scores, by threads 0..5
+    const int i = tid < 3 ? tid : tail0 + tid - 3;
+    const bool ok = tid < 3 ? tid < head : (tid < 6 && i < n);
+    const float xi = S[ok ? i : 0];
+    const uint32_t u = ok ? orderable(xi) : 0u;
+    const bool pass = ok && u >= theta;
+    append(pass ? 1u : 0u, [&](uint32_t pos) {
+      if (pass && pos < static_cast<uint32_t>(kFastCap)) cand[pos] = key_of(u, i);
+    });
+  }
+  const f32x4* S4 = reinterpret_cast<const f32x4*>(S + head);
+  constexpr int UNR = 8;
+  for (int base = 0; base < nv; base += kFastThreads * UNR) {
+    f32x4 v[UNR];
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int q4 = min(base + tid + kFastThreads * j, nv - 1);   // clamped: masked below
+      v[j] = S4[q4];
+    }
+    uint32_t u[UNR][4], msk = 0u;
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const bool in = base + tid + kFastThreads * j < nv;
+      const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        u[j][c] = orderable(e[c]);
+        msk |= (in && u[j][c] >= theta) ? 1u << (4 * j + c) : 0u;
+      }
+    }
+    append(static_cast<uint32_t>(__popc(msk)), [&](uint32_t pos) {
+#pragma unroll
+      for (int j = 0; j < UNR; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if ((msk >> (4 * j + c)) & 1u) {
+            if (pos < static_cast<uint32_t>(kFastCap))
+              cand[pos] = key_of(u[j][c], head + 4 * (base + tid + kFastThreads * j) + c);
+            ++pos;
+          }
+    });
+  }
+  lds_barrier();
+  const uint32_t nc = ncand;
+  if (nc < static_cast<uint32_t>(k) || nc > static_cast<uint32_t>(kFastCap)) {
+    if (tid == 0) out[0] = kTopkRedo;
+    return;
+  }
+
+  // 3. the k-th largest candidate key, digit by digit
+  const int nci = static_cast<int>(nc);
+  uint64_t pre = 0;
+  uint32_t need = static_cast<uint32_t>(k), cnt = nc;
+  bool whole_score = false;   // every candidate with the k-th score is chosen
+  {
+    constexpr int kLo[6] = {53, 42, 32, 21, 10, 0}, kW[6] = {11, 11, 10, 11, 11, 10};
+#pragma unroll
+    for (int p = 0; p < 6; ++p) {
+      if (p == 3 && cnt == need) {
+        whole_score = true;
+        break;
+      }
+      const int lo = kLo[p], w = kW[p];
+      uint32_t d, rk;
+      radix(nci, 1 << w, [&](int i) {
+        const uint64_t x = cand[i];
+        return (p == 0 || (x >> (lo + w)) == pre) ? static_cast<int>((x >> lo) & ((1u << w) - 1u)) : -1;
+      }, need, d, rk, cnt);
+      pre = (pre << w) | d;
+      need = rk;
+    }
+  }
+  const uint64_t kth = whole_score ? pre << 32 : pre;
+
+  // 4. the chosen tokens in a bitmap of the row (over the histogram), then
+  // written ascending
+  uint32_t* bits = hist;
+  const int nwords = (n + 31) >> 5;
+  for (int i = tid; i < nwords; i += kFastThreads) bits[i] = 0u;
+  lds_barrier();
+  for (int i = tid; i < nci; i += kFastThreads) {
+    const uint64_t x = cand[i];
+    if (x >= kth) {
+      const uint32_t tok = 0xFFFFFFFFu - static_cast<uint32_t>(x);
+      atomicOr(&bits[tok >> 5], 1u << (tok & 31));
+    }
+  }
+  lds_barrier();
+  const int per = (nwords + kFastThreads - 1) / kFastThreads;
+  const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
+  uint32_t mine = 0;
+  for (int w = w0; w < w1; ++w) mine += static_cast<uint32_t>(__popc(bits[w]));
+  uint32_t tot;
+  uint32_t pos = block_excl_scan<kFastWaves>(mine, wsum, &tot, lane, wave);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t m = bits[w];
+    while (m != 0u) {
+      const int bit = __ffs(m) - 1;
+      m &= m - 1u;
+      if (pos < static_cast<uint32_t>(k)) out[pos] = 32 * w + bit;   // exactly k are chosen; the test bounds the store
+      ++pos;
+    }
+  }
+}
+
+// Exact top-k of one row of indexer scores, for the rows the sampled pass
+// (k_dsa_topk_fast) left undone (first entry kTopkRedo): the chosen tokens
+// are the k largest 64-bit keys (orderable score, complement of the token),
+// so equal scores go to the lower token. The top 16 bits of every key are
+// kept in LDS (the row is read from memory once, up to 65536 candidates); a
+// 12-bit and a 4-bit digit find the top-16-bit value P of the k-th key; the
+// candidates whose top 16 bits equal P are re-read, ranked by their exact
+// keys and the chosen ones marked in a bitmap. With more than kTopkCand such
+// candidates (heavy ties), the remaining 48 key bits are resolved by 8-bit
+// digits instead. Then an ordered compaction writes the chosen tokens
+// ascending. Each workgroup checks the markers of kRedoRows consecutive rows
+// and runs the flagged ones in turn.
+__global__ __launch_bounds__(kTopkThreads) void k_dsa_topk_exact(DsaArgs a) {
   extern __shared__ __align__(16) unsigned char tk_lds[];
   uint32_t* hist = reinterpret_cast<uint32_t*>(tk_lds);                 // 4096 bins; later the bitmap
   uint64_t* cand = reinterpret_cast<uint64_t*>(tk_lds + 4096 * 4);     // kTopkCand exact keys
@@ -372,212 +597,224 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(DsaArgs a) {
   __shared__ uint32_t ncand;
   __shared__ uint64_t kth_sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t row = blockIdx.x;
-  const int b = static_cast<int>(row / a.L), t = static_cast<int>(row % a.L);
-  const int n = t + 1, k = a.topk;
-  int32_t* out = a.idx + row * k;
-  if (n <= k) {
-    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
-    return;
-  }
-  const float* S = a.scores + score_row(a, b, t);
-  const int cap = a.topk_cache;   // c16 holds candidates [0, min(n, cap))
-  auto top16 = [&](int i) -> uint32_t { return i < cap ? c16[i] : (orderable(S[i]) >> 16); };
-  auto key64 = [&](int i) -> uint64_t {
-    return (static_cast<uint64_t>(orderable(S[i])) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(i));
-  };
-
-  // digit 1 (bits 31..20): one read of the row, sixteen loads in flight per thread
-  for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0u;
-  if (tid == 0) ncand = 0u;
+  __shared__ int redo[kRedoRows];
+  __shared__ int nredo;
+  const int64_t rows = static_cast<int64_t>(a.B) * a.L, r0 = static_cast<int64_t>(blockIdx.x) * kRedoRows;
+  if (tid == 0) nredo = 0;
   lds_barrier();
-  auto take = [&](int i, float x) {
-    const uint32_t u = orderable(x);
-    if (i < cap) c16[i] = static_cast<uint16_t>(u >> 16);
-    atomicAdd(&hist[u >> 20], 1u);
-  };
-  // the row starts at an arbitrary float: a scalar head up to 16-byte
-  // alignment, then 16-byte loads (sixteen in flight per thread), a scalar tail
-  const int head = min(n, static_cast<int>((4 - ((reinterpret_cast<uintptr_t>(S) >> 2) & 3)) & 3));
-  if (tid < head) take(tid, S[tid]);
-  const int nv = (n - head) >> 2;   // whole float4s after the head
-  const f32x4* S4 = reinterpret_cast<const f32x4*>(S + head);
-  constexpr int UNR = 16;
-  for (int base = 0; base < nv; base += kTopkThreads * UNR) {
-    f32x4 v[UNR];
-#pragma unroll
-    for (int j = 0; j < UNR; ++j) {
-      const int q4 = base + tid + kTopkThreads * j;
-      v[j] = q4 < nv ? S4[q4] : f32x4{0.f, 0.f, 0.f, 0.f};
+  if (tid < kRedoRows && r0 + tid < rows && a.idx[(r0 + tid) * a.topk] == kTopkRedo)
+    redo[atomicAdd(&nredo, 1)] = tid;
+  lds_barrier();
+  const int nr = nredo;
+  for (int f = 0; f < nr; ++f) {
+    const int64_t row = r0 + redo[f];
+    const int b = static_cast<int>(row / a.L), t = static_cast<int>(row % a.L);
+    const int n = t + 1, k = a.topk;
+    int32_t* out = a.idx + row * k;
+    if (n <= k) {
+      for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+      continue;
     }
-#pragma unroll
-    for (int j = 0; j < UNR; ++j) {
-      const int q4 = base + tid + kTopkThreads * j;
-      if (q4 < nv) {
-        const int i = head + 4 * q4;
-        take(i, v[j].x);
-        take(i + 1, v[j].y);
-        take(i + 2, v[j].z);
-        take(i + 3, v[j].w);
+    const float* S = a.scores + score_row(a, b, t);
+    const int cap = a.topk_cache;   // c16 holds candidates [0, min(n, cap))
+    auto top16 = [&](int i) -> uint32_t { return i < cap ? c16[i] : (orderable(S[i]) >> 16); };
+    auto key64 = [&](int i) -> uint64_t {
+      return (static_cast<uint64_t>(orderable(S[i])) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(i));
+    };
+
+    // digit 1 (bits 31..20): one read of the row, sixteen loads in flight per thread
+    for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0u;
+    if (tid == 0) ncand = 0u;
+    lds_barrier();
+    auto take = [&](int i, float x) {
+      const uint32_t u = orderable(x);
+      if (i < cap) c16[i] = static_cast<uint16_t>(u >> 16);
+      atomicAdd(&hist[u >> 20], 1u);
+    };
+    // the row starts at an arbitrary float: a scalar head up to 16-byte
+    // alignment, then 16-byte loads (sixteen in flight per thread), a scalar tail
+    const int head = min(n, static_cast<int>((4 - ((reinterpret_cast<uintptr_t>(S) >> 2) & 3)) & 3));
+    if (tid < head) take(tid, S[tid]);
+    const int nv = (n - head) >> 2;   // whole float4s after the head
+    const f32x4* S4 = reinterpret_cast<const f32x4*>(S + head);
+    constexpr int UNR = 16;
+    for (int base = 0; base < nv; base += kTopkThreads * UNR) {
+      f32x4 v[UNR];
+  #pragma unroll
+      for (int j = 0; j < UNR; ++j) {
+        const int q4 = base + tid + kTopkThreads * j;
+        v[j] = q4 < nv ? S4[q4] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+  #pragma unroll
+      for (int j = 0; j < UNR; ++j) {
+        const int q4 = base + tid + kTopkThreads * j;
+        if (q4 < nv) {
+          const int i = head + 4 * q4;
+          take(i, v[j].x);
+          take(i + 1, v[j].y);
+          take(i + 2, v[j].z);
+          take(i + 3, v[j].w);
+        }
       }
     }
-  }
-  for (int i = head + 4 * nv + tid; i < n; i += kTopkThreads) take(i, S[i]);
-  lds_barrier();
-  find_bin(hist, 4096, static_cast<uint32_t>(k), wsum, res, tid, lane, wave);
-  lds_barrier();
-  const uint32_t d1 = res[0], need1 = res[1];
-  // passes over the cached top 16 bits, eight keys (one 16-byte word) at a time
-  const int nq = min(n, cap) >> 3;   // whole words in the cache
-  auto for_top16 = [&](auto&& f) {
-    for (int q = tid; q < nq; q += kTopkThreads) {
-      const uint4 w4 = *reinterpret_cast<const uint4*>(c16 + 8 * q);
-      const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) f(8 * q + j, (ww[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-    }
-    for (int i = 8 * nq + tid; i < n; i += kTopkThreads) f(i, top16(i));
-  };
-  // digit 2 (bits 19..16) among the keys of bin d1
-  if (tid < 16) hist[tid] = 0u;
-  lds_barrier();
-  for_top16([&](int, uint32_t c) {
-    if ((c >> 4) == d1) atomicAdd(&hist[c & 15u], 1u);
-  });
-  lds_barrier();
-  find_bin(hist, 16, need1, wsum, res, tid, lane, wave);
-  lds_barrier();
-  const uint32_t P = (d1 << 4) | res[0];
-  uint32_t need = res[1];   // rank of the k-th key among the keys whose top 16 bits are P
-  // the candidates sharing P: their exact keys
-  for_top16([&](int i, uint32_t c) {
-    if (c == P) {
-      const uint32_t pos = atomicAdd(&ncand, 1u);
-      if (pos < static_cast<uint32_t>(kTopkCand)) cand[pos] = key64(i);
-    }
-  });
-  lds_barrier();
-  const uint32_t nc = ncand;
-  uint64_t kth;   // the k-th largest key of the row
-  if (nc <= 256u) {
-    // few candidates (the usual case): the k-th key is the one with exactly
-    // need - 1 larger candidates (keys are distinct: they hold the token)
-    for (int i = tid; i < static_cast<int>(nc); i += kTopkThreads) {
-      const uint64_t x = cand[i];
-      uint32_t above = 0;
-      for (int j = 0; j < static_cast<int>(nc); ++j) above += cand[j] > x ? 1u : 0u;
-      if (above == need - 1) kth_sh = x;
-    }
+    for (int i = head + 4 * nv + tid; i < n; i += kTopkThreads) take(i, S[i]);
     lds_barrier();
-    kth = kth_sh;
-  } else if (nc <= static_cast<uint32_t>(kTopkCand)) {
-    // bitonic sort of the candidates, descending (zero keys pad to a power of two)
-    int Pn = 1;
-    while (Pn < static_cast<int>(nc)) Pn <<= 1;
-    for (int i = static_cast<int>(nc) + tid; i < Pn; i += kTopkThreads) cand[i] = 0ull;
+    find_bin(hist, 4096, static_cast<uint32_t>(k), wsum, res, tid, lane, wave);
     lds_barrier();
-    for (int size = 2; size <= Pn; size <<= 1)
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < Pn / 2; i += kTopkThreads) {
-          const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
-          const bool desc = (lo & size) == 0;
-          const uint64_t x = cand[lo], y = cand[hi];
-          if ((x < y) == desc) {
-            cand[lo] = y;
-            cand[hi] = x;
+    const uint32_t d1 = res[0], need1 = res[1];
+    // passes over the cached top 16 bits, eight keys (one 16-byte word) at a time
+    const int nq = min(n, cap) >> 3;   // whole words in the cache
+    auto for_top16 = [&](auto&& f) {
+      for (int q = tid; q < nq; q += kTopkThreads) {
+        const uint4 w4 = *reinterpret_cast<const uint4*>(c16 + 8 * q);
+        const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+  #pragma unroll
+        for (int j = 0; j < 8; ++j) f(8 * q + j, (ww[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+      }
+      for (int i = 8 * nq + tid; i < n; i += kTopkThreads) f(i, top16(i));
+    };
+    // digit 2 (bits 19..16) among the keys of bin d1
+    if (tid < 16) hist[tid] = 0u;
+    lds_barrier();
+    for_top16([&](int, uint32_t c) {
+      if ((c >> 4) == d1) atomicAdd(&hist[c & 15u], 1u);
+    });
+    lds_barrier();
+    find_bin(hist, 16, need1, wsum, res, tid, lane, wave);
+    lds_barrier();
+    const uint32_t P = (d1 << 4) | res[0];
+    uint32_t need = res[1];   // rank of the k-th key among the keys whose top 16 bits are P
+    // the candidates sharing P: their exact keys
+    for_top16([&](int i, uint32_t c) {
+      if (c == P) {
+        const uint32_t pos = atomicAdd(&ncand, 1u);
+        if (pos < static_cast<uint32_t>(kTopkCand)) cand[pos] = key64(i);
+      }
+    });
+    lds_barrier();
+    const uint32_t nc = ncand;
+    uint64_t kth;   // the k-th largest key of the row
+    if (nc <= 256u) {
+      // few candidates (the usual case): the k-th key is the one with exactly
+      // need - 1 larger candidates (keys are distinct: they hold the token)
+      for (int i = tid; i < static_cast<int>(nc); i += kTopkThreads) {
+        const uint64_t x = cand[i];
+        uint32_t above = 0;
+        for (int j = 0; j < static_cast<int>(nc); ++j) above += cand[j] > x ? 1u : 0u;
+        if (above == need - 1) kth_sh = x;
+      }
+      lds_barrier();
+      kth = kth_sh;
+    } else if (nc <= static_cast<uint32_t>(kTopkCand)) {
+      // bitonic sort of the candidates, descending (zero keys pad to a power of two)
+      int Pn = 1;
+      while (Pn < static_cast<int>(nc)) Pn <<= 1;
+      for (int i = static_cast<int>(nc) + tid; i < Pn; i += kTopkThreads) cand[i] = 0ull;
+      lds_barrier();
+      for (int size = 2; size <= Pn; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          for (int i = tid; i < Pn / 2; i += kTopkThreads) {
+            const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
+            const bool desc = (lo & size) == 0;
+            const uint64_t x = cand[lo], y = cand[hi];
+            if ((x < y) == desc) {
+              cand[lo] = y;
+              cand[hi] = x;
+            }
           }
+          lds_barrier();
         }
+      kth = cand[need - 1];
+    } else {
+      // heavy ties: resolve the remaining 48 bits of the key by 8-bit digits
+      uint64_t pre = P;   // the known high bits of the k-th key
+      for (int shift = 40; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0u;
+        lds_barrier();
+        for (int i = tid; i < n; i += kTopkThreads)
+          if (top16(i) == P) {
+            const uint64_t kk = key64(i);
+            if ((kk >> (shift + 8)) == pre) atomicAdd(&hist[(kk >> shift) & 0xFFu], 1u);
+          }
+        lds_barrier();
+        find_bin(hist, 256, need, wsum, res, tid, lane, wave);
+        lds_barrier();
+        pre = (pre << 8) | res[0];
+        need = res[1];
         lds_barrier();
       }
-    kth = cand[need - 1];
-  } else {
-    // heavy ties: resolve the remaining 48 bits of the key by 8-bit digits
-    uint64_t pre = P;   // the known high bits of the k-th key
-    for (int shift = 40; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0u;
-      lds_barrier();
-      for (int i = tid; i < n; i += kTopkThreads)
-        if (top16(i) == P) {
-          const uint64_t kk = key64(i);
-          if ((kk >> (shift + 8)) == pre) atomicAdd(&hist[(kk >> shift) & 0xFFu], 1u);
+      kth = pre;
+    }
+    lds_barrier();
+    // bitmap (over the histogram) of the chosen candidates sharing P
+    uint32_t* bits = hist;
+    const int nwords = (n + 31) >> 5;
+    for (int i = tid; i < nwords; i += kTopkThreads) bits[i] = 0u;
+    lds_barrier();
+    if (nc <= static_cast<uint32_t>(kTopkCand)) {
+      for (int i = tid; i < static_cast<int>(nc); i += kTopkThreads) {
+        const uint64_t kk = cand[i];
+        if (kk >= kth) {
+          const uint32_t tok = 0xFFFFFFFFu - static_cast<uint32_t>(kk);
+          atomicOr(&bits[tok >> 5], 1u << (tok & 31));
         }
-      lds_barrier();
-      find_bin(hist, 256, need, wsum, res, tid, lane, wave);
-      lds_barrier();
-      pre = (pre << 8) | res[0];
-      need = res[1];
-      lds_barrier();
-    }
-    kth = pre;
-  }
-  lds_barrier();
-  // bitmap (over the histogram) of the chosen candidates sharing P
-  uint32_t* bits = hist;
-  const int nwords = (n + 31) >> 5;
-  for (int i = tid; i < nwords; i += kTopkThreads) bits[i] = 0u;
-  lds_barrier();
-  if (nc <= static_cast<uint32_t>(kTopkCand)) {
-    for (int i = tid; i < static_cast<int>(nc); i += kTopkThreads) {
-      const uint64_t kk = cand[i];
-      if (kk >= kth) {
-        const uint32_t tok = 0xFFFFFFFFu - static_cast<uint32_t>(kk);
-        atomicOr(&bits[tok >> 5], 1u << (tok & 31));
       }
+    } else {
+      for (int i = tid; i < n; i += kTopkThreads)
+        if (top16(i) == P && key64(i) >= kth) atomicOr(&bits[i >> 5], 1u << (i & 31));
     }
-  } else {
-    for (int i = tid; i < n; i += kTopkThreads)
-      if (top16(i) == P && key64(i) >= kth) atomicOr(&bits[i >> 5], 1u << (i & 31));
-  }
-  lds_barrier();
-  // ordered compaction: wave w takes the candidates [w * span, (w + 1) * span),
-  // eight consecutive ones per lane and round; one workgroup scan of the wave
-  // counts, then wave-level prefix sums
-  const int span = ((n + 8 * kTopkThreads - 1) / (8 * kTopkThreads)) * 512;
-  auto chosen8 = [&](int i0) -> uint32_t {   // bit j: candidate i0 + j is chosen
-    uint32_t sel = 0;
-    if (i0 < n) {
-      uint16_t cc[8];
-      if (i0 + 8 <= min(n, cap)) {
-        const uint4 w4 = *reinterpret_cast<const uint4*>(c16 + i0);
-        const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) cc[j] = static_cast<uint16_t>(ww[j >> 1] >> (16 * (j & 1)));
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) cc[j] = i0 + j < n ? static_cast<uint16_t>(top16(i0 + j)) : 0;
+    lds_barrier();
+    // ordered compaction: wave w takes the candidates [w * span, (w + 1) * span),
+    // eight consecutive ones per lane and round; one workgroup scan of the wave
+    // counts, then wave-level prefix sums
+    const int span = ((n + 8 * kTopkThreads - 1) / (8 * kTopkThreads)) * 512;
+    auto chosen8 = [&](int i0) -> uint32_t {   // bit j: candidate i0 + j is chosen
+      uint32_t sel = 0;
+      if (i0 < n) {
+        uint16_t cc[8];
+        if (i0 + 8 <= min(n, cap)) {
+          const uint4 w4 = *reinterpret_cast<const uint4*>(c16 + i0);
+          const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) cc[j] = static_cast<uint16_t>(ww[j >> 1] >> (16 * (j & 1)));
+        } else {
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) cc[j] = i0 + j < n ? static_cast<uint16_t>(top16(i0 + j)) : 0;
+        }
+        const uint32_t mb = (bits[i0 >> 5] >> (i0 & 31)) & 0xFFu;
+  #pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (i0 + j < n && (cc[j] > P || (cc[j] == P && ((mb >> j) & 1u)))) sel |= 1u << j;
       }
-      const uint32_t mb = (bits[i0 >> 5] >> (i0 & 31)) & 0xFFu;
-#pragma unroll
+      return sel;
+    };
+    const int w0 = wave * span, w1 = min(n, w0 + span);
+    uint32_t cnt = 0;
+    for (int i0 = w0 + 8 * lane; i0 < w1; i0 += 512) cnt += static_cast<uint32_t>(__popc(chosen8(i0)));
+    uint32_t tot;
+    // the scan at lane 0 of a wave counts the chosen candidates of the lower waves
+    uint32_t pos = __shfl(block_excl_scan(cnt, wsum, &tot, lane, wave), 0, 64);
+    for (int r0 = w0; r0 < w1; r0 += 512) {
+      const int i0 = r0 + 8 * lane;
+      const uint32_t sel = i0 < w1 ? chosen8(i0) : 0u;
+      const uint32_t c = static_cast<uint32_t>(__popc(sel));
+      // inclusive prefix over the lanes of this round
+      uint32_t x = c;
+  #pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      uint32_t p = pos + x - c;
+  #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (i0 + j < n && (cc[j] > P || (cc[j] == P && ((mb >> j) & 1u)))) sel |= 1u << j;
+        if ((sel >> j) & 1u) {
+          if (p < static_cast<uint32_t>(k)) out[p] = i0 + j;   // exactly k are chosen; the test only bounds the store
+          ++p;
+        }
+      pos += __shfl(x, 63, 64);
     }
-    return sel;
-  };
-  const int w0 = wave * span, w1 = min(n, w0 + span);
-  uint32_t cnt = 0;
-  for (int i0 = w0 + 8 * lane; i0 < w1; i0 += 512) cnt += static_cast<uint32_t>(__popc(chosen8(i0)));
-  uint32_t tot;
-  // the scan at lane 0 of a wave counts the chosen candidates of the lower waves
-  uint32_t pos = __shfl(block_excl_scan(cnt, wsum, &tot, lane, wave), 0, 64);
-  for (int r0 = w0; r0 < w1; r0 += 512) {
-    const int i0 = r0 + 8 * lane;
-    const uint32_t sel = i0 < w1 ? chosen8(i0) : 0u;
-    const uint32_t c = static_cast<uint32_t>(__popc(sel));
-    // inclusive prefix over the lanes of this round
-    uint32_t x = c;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
-    uint32_t p = pos + x - c;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if ((sel >> j) & 1u) {
-        if (p < static_cast<uint32_t>(k)) out[p] = i0 + j;   // exactly k are chosen; the test only bounds the store
-        ++p;
-      }
-    pos += __shfl(x, 63, 64);
+    lds_barrier();   // the next row rewrites the LDS this one read
   }
 }
 
@@ -837,13 +1074,17 @@ hipError_t launch_dsa_t(const DsaArgs& a, hipStream_t st, hipEvent_t* ev) {
                      : wpg == 2 ? reinterpret_cast<const void*>(&k_dsa_attn<T, O, D, 2>)
                      : wpg == 3 ? reinterpret_cast<const void*>(&k_dsa_attn<T, O, D, 3>)
                                 : reinterpret_cast<const void*>(&k_dsa_attn<T, O, D, 4>);
-  const void* topk = reinterpret_cast<const void*>(&k_dsa_topk);
+  const void* topk = reinterpret_cast<const void*>(&k_dsa_topk_exact);
+  const void* topk_fast = reinterpret_cast<const void*>(&k_dsa_topk_fast);
   const size_t attn_lds = dsa_attn_lds_bytes(a.gpw, D, kBf16, a.topk);
   const size_t topk_lds = dsa_topk_lds_bytes(a.topk_cache);
+  constexpr size_t kFastLds = kFastCap * sizeof(uint64_t) + 4096 * sizeof(uint32_t);
   hipError_t e;
   if ((e = hipFuncSetAttribute(attn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(attn_lds))) !=
           hipSuccess ||
       (e = hipFuncSetAttribute(topk, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(topk_lds))) !=
+          hipSuccess ||
+      (e = hipFuncSetAttribute(topk_fast, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kFastLds))) !=
           hipSuccess)
     return e;
   const unsigned rows = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.L);
@@ -853,7 +1094,11 @@ hipError_t launch_dsa_t(const DsaArgs& a, hipStream_t st, hipEvent_t* ev) {
                       st, a)) != hipSuccess)
     return e;
   if ((e = record(ev, 1, st)) != hipSuccess) return e;
-  if (!a.inject && (e = launch_one(topk, dim3(rows), dim3(kTopkThreads), topk_lds, st, a)) != hipSuccess) return e;
+  // the sampled pass over every row, then the exact pass over the rows it left
+  if (!a.inject && ((e = launch_one(topk_fast, dim3(rows), dim3(kFastThreads), kFastLds, st, a)) != hipSuccess ||
+                    (e = launch_one(topk, dim3((rows + kRedoRows - 1) / kRedoRows), dim3(kTopkThreads), topk_lds,
+                                    st, a)) != hipSuccess))
+    return e;
   if ((e = record(ev, 2, st)) != hipSuccess) return e;
   if ((e = launch_one(attn, dim3(rows * a.parts), dim3(64 * a.wg_waves), attn_lds, st, a)) != hipSuccess) return e;
   if ((e = record(ev, 3, st)) != hipSuccess) return e;

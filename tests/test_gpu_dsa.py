@@ -163,3 +163,25 @@ def test_dsa_full_size_sampled_rows(name, n_rows):
     rng = np.random.default_rng(7)
     rows = sorted({0, 1, 2046, 2047, 2048, 2049, L // 2, L - 2, L - 1, *rng.integers(0, L, n_rows).tolist()})
     run_dsa(cfg, rows=rows)
+
+
+def test_dsa_rows_past_the_candidate_capacity_with_ties():
+    # zero indexer head weights: every score is 0. Rows of up to 4096 tokens
+    # keep all their keys as candidates; longer rows pass every key through
+    # the sampled threshold, overflow the 4096-key candidate list and are
+    # redone by the exact pass. Both must take the first top_k tokens.
+    cfg = inputs.DsaConfig("redo-ties", 1, 4700, 16, 1, 64, 4, 64, "bf16", top_k=64, seed=34)
+    rows = [0, 63, 64, 4094, 4095, 4096, 4097, 4400, 4699]
+    gi, _ = run_dsa(cfg, rows=rows, w_override=lambda w: np.zeros_like(w))
+    for t in rows:
+        n = min(64, t + 1)
+        assert list(gi[0, t, :n]) == list(range(n)) and all(x == -1 for x in gi[0, t, n:])
+
+
+def test_dsa_sampled_threshold_rows():
+    # rows longer than the 4096-key candidate list take the sampled threshold;
+    # every row from 4000 on is checked against the oracle, with top_k of
+    # 256 and of the largest supported 2048
+    for k in (256, 2048):
+        cfg = inputs.DsaConfig(f"sampled-k{k}", 1, 5200, 16, 1, 64, 8, 64, "bf16", top_k=k, seed=35)
+        run_dsa(cfg, rows=list(range(4000, 5200)), check_c=False)
