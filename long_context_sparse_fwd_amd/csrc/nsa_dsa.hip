@@ -358,12 +358,12 @@ __device__ void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* 
 }
 
 constexpr int kFastThreads = 256, kFastWaves = kFastThreads / 64;
-constexpr int kFastCap = 4096;     // candidate keys a row may keep
+constexpr int kFastCap = 3584;     // candidate keys a row may keep
 constexpr int kFastSample = 4096;  // sampled scores: 16 evenly spaced runs of kFastThreads
 constexpr int kTopkRedo = -2;      // first entry of a row the sampled pass leaves to the exact one
 constexpr int kRedoRows = 256;     // rows whose markers one exact-pass workgroup checks
 static_assert(kFastSample == 16 * kFastThreads, "one sampled score per thread and run");
-static_assert(2 * kDsaMaxTopK <= kFastCap, "the threshold aims between top_k and the capacity");
+static_assert(kDsaMaxTopK < kFastCap && kFastSample * 4 <= kFastCap * 8, "capacity above top_k; the sample fits the list");
 
 // Top-k of one row of indexer scores by a sampled threshold (one workgroup
 // per row; the chosen set is the exact one, as in k_dsa_topk_exact).
@@ -386,7 +386,7 @@ static_assert(2 * kDsaMaxTopK <= kFastCap, "the threshold aims between top_k and
 __global__ __launch_bounds__(kFastThreads) void k_dsa_topk_fast(DsaArgs a) {
   extern __shared__ __align__(16) unsigned char tf_lds[];
   uint64_t* cand = reinterpret_cast<uint64_t*>(tf_lds);                  // kFastCap keys; first the sample
-  uint32_t* hist = reinterpret_cast<uint32_t*>(tf_lds + kFastCap * 8);  // 2048 bins; later the row's bitmap
+  uint32_t* hist = reinterpret_cast<uint32_t*>(tf_lds + kFastCap * 8);  // 2048 bins; later the row's bitmap (L / 32 words)
   __shared__ uint32_t res[2];
   __shared__ uint32_t wsum[kFastWaves];
   __shared__ uint32_t ncand;
@@ -421,6 +421,20 @@ __global__ __launch_bounds__(kFastThreads) void k_dsa_topk_fast(DsaArgs a) {
     lds_barrier();   // before hist and res are written again
   };
 
+  // the row as a scalar head up to 16-byte alignment, 16-byte loads in
+  // rounds of UNR per thread, a scalar tail
+  const int head = min(n, static_cast<int>((4 - ((reinterpret_cast<uintptr_t>(S) >> 2) & 3)) & 3));
+  const int nv = (n - head) >> 2;   // whole float4s after the head
+  const int tail0 = head + 4 * nv;
+  const f32x4* S4 = reinterpret_cast<const f32x4*>(S + head);
+  constexpr int UNR = 4;
+  // one round, at clamped indices (entries past nv are masked by the caller)
+  auto load_round = [&](int base, f32x4 (&v)[UNR]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) v[j] = S4[max(0, min(base + tid + kFastThreads * j, nv - 1))];
+  };
+  f32x4 va[UNR];
+
   // 1. the threshold
   uint32_t theta = 0u;
   if (n > kFastCap) {
@@ -428,6 +442,7 @@ __global__ __launch_bounds__(kFastThreads) void k_dsa_topk_fast(DsaArgs a) {
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = S[r * (n - kFastThreads) / 15 + tid];
+    load_round(0, va);   // the row's first round stays in flight across the sample's digits
 #pragma unroll
     for (int r = 0; r < 16; ++r) skey[r * kFastThreads + tid] = orderable(x[r]);
     const uint32_t aim = static_cast<uint32_t>(k + kFastCap) / 2;
@@ -440,6 +455,8 @@ __global__ __launch_bounds__(kFastThreads) void k_dsa_topk_fast(DsaArgs a) {
       return (u >> 21) == d1 ? static_cast<int>((u >> 10) & 2047u) : -1;
     }, r1, d2, r2, c2);
     theta = (d1 << 21) | (d2 << 10);
+  } else if (nv > 0) {
+    load_round(0, va);
   }
 
   // 2. the candidates: one read of the row (a scalar head up to 16-byte
@@ -452,7 +469,7 @@ __global__ __launch_bounds__(kFastThreads) void k_dsa_topk_fast(DsaArgs a) {
   auto append = [&](uint32_t cnt, auto&& emit) __attribute__((always_inline)) {
     uint32_t pre = 0, tot = 0;
 #pragma unroll
-    for (int bit = 0; bit < 6; ++bit) {   // counts below 64
+    for (int bit = 0; bit < 7; ++bit) {   // counts up to 64
       const uint64_t bal = __ballot((cnt >> bit) & 1u);
       pre += static_cast<uint32_t>(__popcll(bal & below)) << bit;
       tot += static_cast<uint32_t>(__popcll(bal)) << bit;
@@ -466,9 +483,6 @@ __global__ __launch_bounds__(kFastThreads) void k_dsa_topk_fast(DsaArgs a) {
   auto key_of = [](uint32_t u, int i) -> uint64_t {
     return (static_cast<uint64_t>(u) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(i));
   };
-  const int head = min(n, static_cast<int>((4 - ((reinterpret_cast<uintptr_t>(S) >> 2) & 3)) & 3));
-  const int nv = (n - head) >> 2;   // whole float4s after the head
-  const int tail0 = head + 4 * nv;
   {
     // head and tail: at most 3 + 3 scores, by threads 0..5
     const int i = tid < 3 ? tid : tail0 + tid - 3;
@@ -480,16 +494,16 @@ __global__ __launch_bounds__(kFastThreads) void k_dsa_topk_fast(DsaArgs a) {
       if (pass && pos < static_cast<uint32_t>(kFastCap)) cand[pos] = key_of(u, i);
     });
   }
-  const f32x4* S4 = reinterpret_cast<const f32x4*>(S + head);
-  constexpr int UNR = 8;
   for (int base = 0; base < nv; base += kFastThreads * UNR) {
+    // the next round in flight while this one is sorted out (unconditional:
+    // the last round reloads its own tail, so every path has the same loads
+    // outstanding and the wait below is for this round's only)
     f32x4 v[UNR];
 #pragma unroll
-    for (int j = 0; j < UNR; ++j) {
-      const int q4 = min(base + tid + kFastThreads * j, nv - 1);   // clamped: masked below
-      v[j] = S4[q4];
-    }
-    uint32_t u[UNR][4], msk = 0u;
+    for (int j = 0; j < UNR; ++j) v[j] = va[j];
+    load_round(base + kFastThreads * UNR, va);
+    uint32_t u[UNR][4];
+    uint64_t msk = 0u;
 #pragma unroll
     for (int j = 0; j < UNR; ++j) {
       const bool in = base + tid + kFastThreads * j < nv;
@@ -497,15 +511,15 @@ __global__ __launch_bounds__(kFastThreads) void k_dsa_topk_fast(DsaArgs a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         u[j][c] = orderable(e[c]);
-        msk |= (in && u[j][c] >= theta) ? 1u << (4 * j + c) : 0u;
+        msk |= (in && u[j][c] >= theta) ? 1ull << (4 * j + c) : 0ull;
       }
     }
-    append(static_cast<uint32_t>(__popc(msk)), [&](uint32_t pos) {
+    append(static_cast<uint32_t>(__popcll(msk)), [&](uint32_t pos) {
 #pragma unroll
       for (int j = 0; j < UNR; ++j)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          if ((msk >> (4 * j + c)) & 1u) {
+          if ((msk >> (4 * j + c)) & 1ull) {
             if (pos < static_cast<uint32_t>(kFastCap))
               cand[pos] = key_of(u[j][c], head + 4 * (base + tid + kFastThreads * j) + c);
             ++pos;
@@ -637,7 +651,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk_exact(DsaArgs a) {
     if (tid < head) take(tid, S[tid]);
     const int nv = (n - head) >> 2;   // whole float4s after the head
     const f32x4* S4 = reinterpret_cast<const f32x4*>(S + head);
-    constexpr int UNR = 16;
+    constexpr int UNR = 4;
     for (int base = 0; base < nv; base += kTopkThreads * UNR) {
       f32x4 v[UNR];
   #pragma unroll
@@ -1078,13 +1092,14 @@ hipError_t launch_dsa_t(const DsaArgs& a, hipStream_t st, hipEvent_t* ev) {
   const void* topk_fast = reinterpret_cast<const void*>(&k_dsa_topk_fast);
   const size_t attn_lds = dsa_attn_lds_bytes(a.gpw, D, kBf16, a.topk);
   const size_t topk_lds = dsa_topk_lds_bytes(a.topk_cache);
-  constexpr size_t kFastLds = kFastCap * sizeof(uint64_t) + 4096 * sizeof(uint32_t);
+  // the candidate list, then the histogram or the row's bitmap
+  const size_t fast_lds = kFastCap * sizeof(uint64_t) + std::max(2048, (a.L + 31) / 32) * sizeof(uint32_t);
   hipError_t e;
   if ((e = hipFuncSetAttribute(attn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(attn_lds))) !=
           hipSuccess ||
       (e = hipFuncSetAttribute(topk, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(topk_lds))) !=
           hipSuccess ||
-      (e = hipFuncSetAttribute(topk_fast, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kFastLds))) !=
+      (e = hipFuncSetAttribute(topk_fast, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(fast_lds))) !=
           hipSuccess)
     return e;
   const unsigned rows = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.L);
@@ -1095,7 +1110,7 @@ hipError_t launch_dsa_t(const DsaArgs& a, hipStream_t st, hipEvent_t* ev) {
     return e;
   if ((e = record(ev, 1, st)) != hipSuccess) return e;
   // the sampled pass over every row, then the exact pass over the rows it left
-  if (!a.inject && ((e = launch_one(topk_fast, dim3(rows), dim3(kFastThreads), kFastLds, st, a)) != hipSuccess ||
+  if (!a.inject && ((e = launch_one(topk_fast, dim3(rows), dim3(kFastThreads), fast_lds, st, a)) != hipSuccess ||
                     (e = launch_one(topk, dim3((rows + kRedoRows - 1) / kRedoRows), dim3(kTopkThreads), topk_lds,
                                     st, a)) != hipSuccess))
     return e;

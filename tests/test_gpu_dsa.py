@@ -166,9 +166,9 @@ def test_dsa_full_size_sampled_rows(name, n_rows):
 
 
 def test_dsa_rows_past_the_candidate_capacity_with_ties():
-    # zero indexer head weights: every score is 0. Rows of up to 4096 tokens
+    # zero indexer head weights: every score is 0. Rows of up to 3584 tokens
     # keep all their keys as candidates; longer rows pass every key through
-    # the sampled threshold, overflow the 4096-key candidate list and are
+    # the sampled threshold, overflow the 3584-key candidate list and are
     # redone by the exact pass. Both must take the first top_k tokens.
     cfg = inputs.DsaConfig("redo-ties", 1, 4700, 16, 1, 64, 4, 64, "bf16", top_k=64, seed=34)
     rows = [0, 63, 64, 4094, 4095, 4096, 4097, 4400, 4699]
@@ -179,7 +179,7 @@ def test_dsa_rows_past_the_candidate_capacity_with_ties():
 
 
 def test_dsa_sampled_threshold_rows():
-    # rows longer than the 4096-key candidate list take the sampled threshold;
+    # rows longer than the 3584-key candidate list take the sampled threshold;
     # every row from 4000 on is checked against the oracle, with top_k of
     # 256 and of the largest supported 2048
     for k in (256, 2048):
