@@ -567,7 +567,8 @@ def bench_dsa(cfg, steps, warmup, torch, inputs, nsa):
                           "gathered_bytes": gathered,
                           "gathered_TBps": gathered / (stage_ms["attention"] * 1e-3) / 1e12},
             "dtype": "bf16 (indexer and attention operands), fp32 scores and accumulation",
-            "traffic": {kn: committed_traffic(kn, cfg.name, "dsa") for kn in ("k_dsa_index", "k_dsa_topk", "k_dsa_attn")}}
+            "traffic": {kn: committed_traffic(kn, cfg.name, "dsa")
+                        for kn in ("k_dsa_index", "k_dsa_topk_fast", "k_dsa_topk_exact", "k_dsa_attn")}}
 
 
 def bench_decode(cfg, steps, warmup, torch, inputs, nsa):
