@@ -295,6 +295,35 @@ nsa_status_t nsa_fwd_decode(const nsa_decode_desc_t* desc, const nsa_params_t* p
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nsa_fwd_decode with the general geometry of nsa_fwd_prefill_general (the
+ * [model.nsa] fields of the NSA how-to, qwbw.cn/news/106443, section 3, list
+ * compress_block_size and select_block_size separately, and its gate_type
+ * is "learned"): compress_stride d (1 <= d <= l), selection blocks of
+ * l' = select_block_size tokens (a multiple of 32, l <= l', top_k * l' <=
+ * 4096) scored by the compressed-attention mass on their tokens, and
+ * optionally the gate layer gate_w, gate_b (then `gates` may be NULL; the
+ * gates are computed in float32 into the workspace). kc_cache / vc_cache hold
+ * the representations of the compressed blocks [i*d, i*d + l) that lie wholly
+ * inside each sequence, used as given: max_blocks must be at least
+ * (max_seqlen - l) / d + 1, and how the representations were made (block
+ * means, a learned compressor) does not matter here, so wk, bk, wv, bv are
+ * not used. The query at position t = seqlens[b] - 1 sees compressed blocks
+ * i with i*d + l - 1 <= t; its own selection block is t / l'; idx holds
+ * selection-block indices. Workspace from nsa_decode_general_workspace_bytes
+ * (general may be NULL: the plain stride, gates given). Errors as for
+ * nsa_fwd_decode, plus NSA_ERR_INVALID_ARGUMENT for a stride outside [1, l]
+ * or a gate layer with one of its two arrays missing.
+ */
+nsa_status_t nsa_decode_general_workspace_bytes(const nsa_decode_desc_t* desc, const nsa_params_t* params,
+                                                const nsa_general_t* general, size_t* bytes);
+nsa_status_t nsa_fwd_decode_general(const nsa_decode_desc_t* desc, const nsa_params_t* params,
+                                    const nsa_general_t* general, const void* q, const void* k_cache,
+                                    const void* v_cache, const void* kc_cache, const void* vc_cache,
+                                    const int32_t* seqlens, const void* gates, void* out, int32_t* idx,
+                                    nsa_idx_mode_t idx_mode, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/*
  * nsa_fwd_decode for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation):
  * no workspace argument; the scratch the decode kernel needs (the selection

@@ -312,20 +312,29 @@ nsa_status_t plan_backward(const nsa_prefill_desc_t* d, const nsa_params_t* p, B
 struct DecodePlan {
   int NmaxPad;
   bool logits_lds;
-  size_t off_logits, off_idx, total;
+  size_t off_logits, off_idx, off_gates, total;
 };
 
-nsa_status_t plan_decode(const nsa_decode_desc_t* d, const nsa_params_t* p, DecodePlan* pl) {
+// general: the general-geometry entry points (gen may then be NULL: the
+// plain stride, gates given); geo_out receives the geometry.
+nsa_status_t plan_decode(const nsa_decode_desc_t* d, const nsa_params_t* p, DecodePlan* pl, bool general = false,
+                         const nsa_general_t* gen = nullptr, Geometry* geo_out = nullptr) {
   if (d == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "desc is NULL");
   if (d->batch < 0) return fail(NSA_ERR_INVALID_ARGUMENT, "batch must be >= 0");
   if (d->max_seqlen < 1) return fail(NSA_ERR_INVALID_ARGUMENT, "max_seqlen must be >= 1");
   if (d->max_blocks < 0) return fail(NSA_ERR_INVALID_ARGUMENT, "max_blocks must be >= 0");
   NSA_TRY(check_heads(d->n_q_heads, d->n_kv_heads, d->head_dim));
   NSA_TRY(check_dtypes(d->in_dtype, d->out_dtype));
-  NSA_TRY(check_params(p, d->head_dim));
-  if (d->max_blocks < d->max_seqlen / 64)
-    return fail(NSA_ERR_INVALID_ARGUMENT, "max_blocks (%d) < max_seqlen / 64 (%d)", d->max_blocks,
-                d->max_seqlen / 64);
+  NSA_TRY(check_params(p, d->head_dim, general));
+  Geometry geo;
+  NSA_TRY(check_general(p, general ? gen : nullptr, &geo));
+  if (geo_out != nullptr) *geo_out = geo;
+  // compressed blocks of the longest sequence (the cache rows a call may read)
+  const int cl = p->compress_block_size;
+  const int nv = d->max_seqlen >= cl ? (d->max_seqlen - cl) / geo.stride + 1 : 0;
+  if (d->max_blocks < nv)
+    return fail(NSA_ERR_INVALID_ARGUMENT, "max_blocks (%d) < the %d compressed blocks of max_seqlen %d",
+                d->max_blocks, nv, d->max_seqlen);
   NSA_TRY(check_strides("q", d->q_stride, 2, true));
   NSA_TRY(check_strides("k_cache", d->k_stride, 3, true));
   NSA_TRY(check_strides("v_cache", d->v_stride, 3, true));
@@ -334,7 +343,6 @@ nsa_status_t plan_decode(const nsa_decode_desc_t* d, const nsa_params_t* p, Deco
   NSA_TRY(check_strides("gates", d->g_stride, 2, false));
   NSA_TRY(check_strides("out", d->o_stride, 2, false));
   const int64_t B = d->batch, G = d->n_kv_heads, D = d->head_dim;
-  const int nv = d->max_seqlen / 64;
   pl->NmaxPad = (nv + 63) / 64 * 64;
   if (B * G > INT32_MAX / 16)
     return fail(NSA_ERR_UNSUPPORTED, "batch * n_kv_heads too large");
@@ -349,6 +357,9 @@ nsa_status_t plan_decode(const nsa_decode_desc_t* d, const nsa_params_t* p, Deco
   if (!pl->logits_lds) off = align_up(off + static_cast<size_t>(B * G) * 16 * pl->NmaxPad * sizeof(float));
   pl->off_idx = off;
   off = align_up(off + static_cast<size_t>(B * G) * p->select_top_k * sizeof(int32_t));
+  // gate layer: its fp32 gates of every sequence and head
+  pl->off_gates = off;
+  if (geo.gate_layer()) off = align_up(off + static_cast<size_t>(B * d->n_q_heads) * 3 * sizeof(float));
   pl->total = off;
   return NSA_OK;
 }
@@ -956,9 +967,10 @@ static nsa_status_t decode_impl(const nsa_decode_desc_t* desc, const nsa_params_
                                 const void* kc_cache, const void* vc_cache, const int32_t* seqlens,
                                 const void* gates, void* out, int32_t* idx, nsa_idx_mode_t idx_mode,
                                 void* workspace, size_t workspace_bytes, void* stream,
-                                void* const* events) {
+                                void* const* events, bool general = false, const nsa_general_t* gen = nullptr) {
   DecodePlan pl;
-  NSA_TRY(plan_decode(desc, params, &pl));
+  Geometry geo;
+  NSA_TRY(plan_decode(desc, params, &pl, general, gen, &geo));
   if (idx_mode != NSA_IDX_COMPUTE && idx_mode != NSA_IDX_INJECT)
     return fail(NSA_ERR_INVALID_ARGUMENT, "unknown idx_mode %d", static_cast<int>(idx_mode));
   if (desc->batch == 0) return ok();
@@ -968,7 +980,7 @@ static nsa_status_t decode_impl(const nsa_decode_desc_t* desc, const nsa_params_
   NSA_TRY(check_ptr("kc_cache", kc_cache, true));
   NSA_TRY(check_ptr("vc_cache", vc_cache, true));
   NSA_TRY(check_ptr("seqlens", seqlens, false));
-  NSA_TRY(check_ptr("gates", gates, false));
+  if (!geo.gate_layer()) NSA_TRY(check_ptr("gates", gates, false));
   NSA_TRY(check_ptr("out", out, false));
   NSA_TRY(check_ptr("workspace", workspace, true));
   if (idx_mode == NSA_IDX_INJECT && idx == nullptr)
@@ -1004,6 +1016,16 @@ static nsa_status_t decode_impl(const nsa_decode_desc_t* desc, const nsa_params_
   a.logits_lds = pl.logits_lds ? 1 : 0;
   a.logits = reinterpret_cast<float*>(ws + pl.off_logits);
   a.idx = idx != nullptr ? idx : reinterpret_cast<int32_t*>(ws + pl.off_idx);
+  a.gen = general ? 1 : 0;
+  a.cl = params->compress_block_size;
+  a.cd = geo.stride;
+  a.ls = params->select_block_size;
+  a.inv_cl = 1.0f / static_cast<float>(a.cl);
+  if (geo.gate_layer()) {
+    a.gate_w = gen->gate_w;
+    a.gate_b = gen->gate_b;
+    a.gates32 = reinterpret_cast<float*>(ws + pl.off_gates);
+  }
   for (int i = 0; i < 2; ++i) {
     a.qs[i] = desc->q_stride[i];
     a.gs[i] = desc->g_stride[i];
@@ -1088,6 +1110,25 @@ nsa_status_t nsa_fwd_decode(const nsa_decode_desc_t* desc, const nsa_params_t* p
                             void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(desc, params, q, k_cache, v_cache, kc_cache, vc_cache, seqlens, gates, out, idx,
                      idx_mode, workspace, workspace_bytes, stream, nullptr);
+}
+
+nsa_status_t nsa_decode_general_workspace_bytes(const nsa_decode_desc_t* desc, const nsa_params_t* params,
+                                                const nsa_general_t* general, size_t* bytes) {
+  if (bytes == nullptr) return fail(NSA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  DecodePlan pl;
+  NSA_TRY(plan_decode(desc, params, &pl, true, general));
+  *bytes = pl.total;
+  return ok();
+}
+
+nsa_status_t nsa_fwd_decode_general(const nsa_decode_desc_t* desc, const nsa_params_t* params,
+                                    const nsa_general_t* general, const void* q, const void* k_cache,
+                                    const void* v_cache, const void* kc_cache, const void* vc_cache,
+                                    const int32_t* seqlens, const void* gates, void* out, int32_t* idx,
+                                    nsa_idx_mode_t idx_mode, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  return decode_impl(desc, params, q, k_cache, v_cache, kc_cache, vc_cache, seqlens, gates, out, idx, idx_mode,
+                     workspace, workspace_bytes, stream, nullptr, true, general);
 }
 
 nsa_status_t nsa_fwd_decode_timed(const nsa_decode_desc_t* desc, const nsa_params_t* params,

@@ -378,6 +378,60 @@ __device__ __forceinline__ void merge_into(float* parts, float m, float l, const
   lds_barrier();
 }
 
+// General geometry: the selection-block scores from the compressed-block
+// scores, in place (sc[0 .. own) on return): the compressed-attention mass on
+// each selection block's tokens, every compressed block's probability spread
+// evenly over its cl tokens. Selection block j reads compressed blocks i >= j
+// only (cd <= cl <= ls), so rounds of 64 blocks can overwrite the scores they
+// have consumed. One wave, uniform arguments.
+__device__ inline void dec_selection_scores(const DecodeArgs& a, float* sc, int own, int nv, int lane) {
+  for (int r0 = 0; r0 < own; r0 += 64) {
+    const int j = r0 + lane;
+    float sum = 0.f;
+    if (j < own) {
+      const int lo = j * a.ls, hi = lo + a.ls;
+      const int x = lo - a.cl + 1;
+      const int i0 = x <= 0 ? 0 : (x + a.cd - 1) / a.cd;
+      const int i1 = min(nv - 1, (hi - 1) / a.cd);
+      for (int i = i0; i <= i1; ++i) {
+        const int blo = i * a.cd;
+        sum = fmaf(sc[i], static_cast<float>(min(blo + a.cl, hi) - max(blo, lo)), sum);
+      }
+      sum *= a.inv_cl;
+    }
+    wave_lds_sync();
+    if (j < own) sc[j] = sum;
+    wave_lds_sync();
+  }
+}
+
+// Gate layer of the decode: gates32[b][h][c] = sigmoid(q[b][h] . gate_w[h][:, c]
+// + gate_b[h][c]) in fp32, one thread per (sequence, head). The gates of the
+// three branches are learned (NSA how-to, qwbw.cn/news/106443, section 3,
+// gate_type learned); here a one-layer map of the head's query, as in the
+// prefill.
+template <class T, int D>
+__global__ __launch_bounds__(256) void k_dgate(DecodeArgs a) {
+  using S = typename T::storage;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= a.B * a.Hq) return;
+  const int b = e / a.Hq, h = e % a.Hq;
+  const S* q = static_cast<const S*>(a.q) + b * a.qs[0] + h * a.qs[1];
+  const S* w = static_cast<const S*>(a.gate_w) + static_cast<int64_t>(h) * D * 3;
+  const S* bg = static_cast<const S*>(a.gate_b) + 3 * h;
+  float z0 = to_f32<T>(bg[0]), z1 = to_f32<T>(bg[1]), z2 = to_f32<T>(bg[2]);
+  for (int d = 0; d < D; ++d) {
+    const float x = to_f32<T>(q[d]);
+    z0 = fmaf(x, to_f32<T>(w[3 * d]), z0);
+    z1 = fmaf(x, to_f32<T>(w[3 * d + 1]), z1);
+    z2 = fmaf(x, to_f32<T>(w[3 * d + 2]), z2);
+  }
+  float* o = a.gates32 + static_cast<int64_t>(e) * 3;
+  o[0] = 1.0f / (1.0f + fast_exp2(-z0 * kLog2e));
+  o[1] = 1.0f / (1.0f + fast_exp2(-z1 * kLog2e));
+  o[2] = 1.0f / (1.0f + fast_exp2(-z2 * kLog2e));
+}
+
 constexpr int kDecWaves = 8;
 
 template <class T, int D>
@@ -388,7 +442,9 @@ __host__ __device__ constexpr size_t dec_big_bytes() {
 
 // LGL: the compressed logits stay in LDS. PARK (requires LGL): the logits
 // region, free once the block scores are done, holds the 7 window states.
-template <class T, class O, int D, int RING, bool LGL, bool PARK>
+// GEN: the general geometry (stride, selection blocks of ls tokens, gates
+// from the gate layer); without it the plain one (blocks of 64, stride 64).
+template <class T, class O, int D, int RING, bool LGL, bool PARK, bool GEN>
 __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_dec(DecodeArgs a) {
   using S = typename T::storage;
   using SO = typename O::storage;
@@ -423,7 +479,10 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     if (!a.inject && tid < a.n) idxo[tid] = -1;
     return;
   }
-  const int t = s_raw - 1, nvis = s_raw >> 6, own = t >> 6;
+  // visible compressed blocks and the own selection block
+  const int t = s_raw - 1;
+  const int nvis = GEN ? (s_raw >= a.cl ? (s_raw - a.cl) / a.cd + 1 : 0) : s_raw >> 6;
+  const int own = GEN ? t / a.ls : t >> 6;
   const int wlo = max(0, s_raw - a.w);
   const float sl2 = a.scale_log2;
   void* lv = smem + wave * VStage<T, D>::kBytes;
@@ -468,7 +527,9 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   };
   int nD = -1;  // known once wave 0 has published the selected half blocks
   auto d_real = [&](int q) {
-    const int u = hl[q], j = u >> 1;
+    const int u = hl[q];   // the half block of keys [32 u, 32 u + 32)
+    if constexpr (GEN) return DItem<T>{Kr, Vr, a.ks[2], a.vs[2], 32 * u, 32 * u, t, nullptr};
+    const int j = u >> 1;
     return DItem<T>{Kr, Vr, a.ks[2], a.vs[2], 64 * j + 32 * (u & 1), 64 * j, t, nullptr};
   };
   auto d_item = [&](int k) {
@@ -497,7 +558,15 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) qv[s] = frag_load_if<T>(Q + 32 * s, col < a.Hg);
     const int h = lane & 15, i = min(lane >> 4, 2);
-    const float gg = to_f32<T>(static_cast<const S*>(a.gates)[b * a.gs[0] + (g * a.Hg + min(h, a.Hg - 1)) * a.gs[1] + i]);
+    float gg;
+    if constexpr (GEN) {
+      if (a.gates32 != nullptr)
+        gg = a.gates32[(static_cast<int64_t>(b) * a.Hq + g * a.Hg + min(h, a.Hg - 1)) * 3 + i];
+      else
+        gg = to_f32<T>(static_cast<const S*>(a.gates)[b * a.gs[0] + (g * a.Hg + min(h, a.Hg - 1)) * a.gs[1] + i]);
+    } else {
+      gg = to_f32<T>(static_cast<const S*>(a.gates)[b * a.gs[0] + (g * a.Hg + min(h, a.Hg - 1)) * a.gs[1] + i]);
+    }
     gv = lane < 48 && h < a.Hg ? gg : 0.f;
   }
   ds.prime(a_item, lane);
@@ -533,7 +602,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
 
   // ---- C: block scores
   if (!a.inject) {
-    block_scores(lg, ld, own, hs, sc, tid, NT);
+    block_scores(lg, ld, GEN ? nvis : own, hs, sc, tid, NT);
   }
   lds_barrier();  // sc written; parts read, so the V staging is free again
   // waves 1..7 issue their first window loads; their streams cover the top-k
@@ -543,6 +612,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   //      waves stream the sliding window
   if (wave == 0) {
     if (!a.inject) {
+      if constexpr (GEN) dec_selection_scores(a, sc, own, nvis, lane);
       topk_wave(sc, own, a.n, selo, surv, selb, lane);
       wave_lds_sync();
       if (lane < a.n) idxo[lane] = selo[lane];
@@ -557,20 +627,38 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     if (a.inject)
       for (int k = 0; k < a.n; ++k) rep |= k < lane && __builtin_amdgcn_readlane(j, k) == j;
     const bool h0 = j >= 0 && j <= own && !rep;
-    const bool h1 = h0 && 64 * j + 32 <= t;
-    const uint64_t b0 = __ballot(h0), b1 = __ballot(h1);
-    const uint64_t below = (uint64_t{1} << lane) - 1;
     // The own block goes first: its keys end the sliding window, which the
     // other waves have just streamed, so its reads still hit L2 (listed last
     // it was read again from HBM, ~8 MB per call at d64k).
     const bool isown = h0 && j == own;
-    const uint64_t bo = __ballot(isown);
-    const int nown = bo != 0 ? 1 + ((__ballot(isown && h1) != 0) ? 1 : 0) : 0;
-    const uint64_t rest = below & ~bo;
-    const int pos = isown ? 0 : nown + __popcll(b0 & rest) + __popcll(b1 & rest);
-    if (h0) hl[pos] = 2 * j;
-    if (h1) hl[pos + 1] = 2 * j + 1;
-    if (lane == 0) *nhl = __popcll(b0) + __popcll(b1);
+    if constexpr (GEN) {
+      // block j's half blocks j * hpb .. that start at or before t
+      const int hpb = a.ls >> 5;
+      const int cnt = h0 ? min(hpb, (t >> 5) - j * hpb + 1) : 0;
+      const int other = isown ? 0 : cnt;
+      int incl = other;   // inclusive prefix over the lanes
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      const uint64_t bo = __ballot(isown);
+      const int nown = bo != 0 ? __shfl(cnt, static_cast<int>(__builtin_ctzll(bo)), 64) : 0;
+      const int pos = isown ? 0 : nown + incl - other;
+      for (int i = 0; i < cnt; ++i) hl[pos + i] = j * hpb + i;
+      if (lane == 63) *nhl = nown + incl;
+    } else {
+      const bool h1 = h0 && 64 * j + 32 <= t;
+      const uint64_t b0 = __ballot(h0), b1 = __ballot(h1);
+      const uint64_t below = (uint64_t{1} << lane) - 1;
+      const uint64_t bo = __ballot(isown);
+      const int nown = bo != 0 ? 1 + ((__ballot(isown && h1) != 0) ? 1 : 0) : 0;
+      const uint64_t rest = below & ~bo;
+      const int pos = isown ? 0 : nown + __popcll(b0 & rest) + __popcll(b1 & rest);
+      if (h0) hl[pos] = 2 * j;
+      if (h1) hl[pos + 1] = 2 * j + 1;
+      if (lane == 0) *nhl = __popcll(b0) + __popcll(b1);
+    }
     wave_lds_sync();  // every lane's hl entries before the flag
     if (lane == 0) __hip_atomic_store(hl_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
@@ -641,32 +729,42 @@ size_t dec_lds_bytes(int NmaxPad, int D, bool bf16, bool logits_lds) {
          (logits_lds ? 16 * static_cast<size_t>(NmaxPad + 4) * sizeof(float) : 0);
 }
 
-template <class T, class O, int D, bool LGL, bool PARK>
+template <class T, class O, int D, bool LGL, bool PARK, bool GEN>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st, hipEvent_t* ev) {
   constexpr bool kBf16 = sizeof(typename T::storage) == 2;
   constexpr int RING = kBf16 ? 2 : 1;
   const size_t lds = dec_lds_bytes(a.NmaxPad, D, kBf16, LGL);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec<T, O, D, RING, LGL, PARK>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec<T, O, D, RING, LGL, PARK, GEN>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
+  if (GEN && a.gates32 != nullptr) {
+    hipLaunchKernelGGL((k_dgate<T, D>), dim3((a.B * a.Hq + 255) / 256), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (ev != nullptr) {
     // the dispatch itself records the events at the kernel's start and end,
     // so the interval is the kernel's own duration (no launch latency)
     void* args[] = {const_cast<DecodeArgs*>(&a)};
-    e = hipExtLaunchKernel(reinterpret_cast<const void*>(&k_dec<T, O, D, RING, LGL, PARK>), dim3(a.B * a.G),
+    e = hipExtLaunchKernel(reinterpret_cast<const void*>(&k_dec<T, O, D, RING, LGL, PARK, GEN>), dim3(a.B * a.G),
                            dim3(64 * kDecWaves), args, lds, st, ev[0], ev[1], 0);
     return e != hipSuccess ? e : hipGetLastError();
   }
-  hipLaunchKernelGGL((k_dec<T, O, D, RING, LGL, PARK>), dim3(a.B * a.G), dim3(64 * kDecWaves), lds, st, a);
+  hipLaunchKernelGGL((k_dec<T, O, D, RING, LGL, PARK, GEN>), dim3(a.B * a.G), dim3(64 * kDecWaves), lds, st, a);
   return hipGetLastError();
+}
+
+template <class T, class O, int D, bool GEN>
+static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t st, hipEvent_t* ev) {
+  if (!a.logits_lds) return launch_decode_t<T, O, D, false, false, GEN>(a, st, ev);
+  const bool park =
+      16 * static_cast<size_t>(a.NmaxPad + 4) >= (kDecWaves - 1) * static_cast<size_t>(dec_slot_floats(D));
+  return park ? launch_decode_t<T, O, D, true, true, GEN>(a, st, ev)
+              : launch_decode_t<T, O, D, true, false, GEN>(a, st, ev);
 }
 
 template <class T, class O, int D>
 static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t st, hipEvent_t* ev) {
-  if (!a.logits_lds) return launch_decode_t<T, O, D, false, false>(a, st, ev);
-  const bool park =
-      16 * static_cast<size_t>(a.NmaxPad + 4) >= (kDecWaves - 1) * static_cast<size_t>(dec_slot_floats(D));
-  return park ? launch_decode_t<T, O, D, true, true>(a, st, ev) : launch_decode_t<T, O, D, true, false>(a, st, ev);
+  return a.gen ? launch_decode_g<T, O, D, true>(a, st, ev) : launch_decode_g<T, O, D, false>(a, st, ev);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool in_bf16, bool out_bf16, hipStream_t st,

@@ -100,6 +100,17 @@ struct DecodeArgs {
   int logits_lds;  // 1: the compressed logits stay in LDS; 0: in `logits`
   float* logits;   // compressed logits (log2 domain), [B*G][16][NmaxPad], if !logits_lds
   int64_t qs[2], ks[3], vs[3], kcs[3], vcs[3], gs[2], os[2];
+  // General geometry (gen = 1): compressed block i covers tokens [i*cd,
+  // i*cd + cl) and is visible once i*cd + cl - 1 <= t; selection blocks hold
+  // ls tokens, scored by the compressed-attention mass on their tokens. With
+  // a gate layer (gate_w, gate_b: [Hq][D][3], [Hq][3] in the input type),
+  // k_dgate writes the fp32 gates [B][Hq][3] into gates32 and the decode
+  // reads those instead of `gates`.
+  int gen, cl, cd, ls;
+  float inv_cl;
+  const void* gate_w;
+  const void* gate_b;
+  float* gates32;
 };
 
 // ev (nullable): kPrefillStages+1 / kDecodeStages+1 events recorded on st

@@ -109,6 +109,12 @@ def lib() -> ctypes.CDLL:
     L.nsa_fwd_decode.restype = ctypes.c_int
     L.nsa_fwd_decode.argtypes = [P(DecodeDesc), P(NsaParams), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                  c_vp, c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
+    L.nsa_decode_general_workspace_bytes.restype = ctypes.c_int
+    L.nsa_decode_general_workspace_bytes.argtypes = [P(DecodeDesc), P(NsaParams), P(NsaGeneral),
+                                                     P(ctypes.c_size_t)]
+    L.nsa_fwd_decode_general.restype = ctypes.c_int
+    L.nsa_fwd_decode_general.argtypes = [P(DecodeDesc), P(NsaParams), P(NsaGeneral), c_vp, c_vp, c_vp, c_vp,
+                                         c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_int, c_vp, ctypes.c_size_t, c_vp]
     L.nsa_fwd_decode_noalloc.restype = ctypes.c_int
     L.nsa_fwd_decode_noalloc.argtypes = [P(DecodeDesc), P(NsaParams), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                          c_vp, c_vp, c_vp, ctypes.c_int, c_vp]
@@ -538,6 +544,54 @@ def decode(q, k_cache, v_cache, kc_cache, vc_cache, seqlens, gates, *, top_k: in
                             _ptr(gates), _ptr(out), _ptr(idx),
                             NSA_IDX_INJECT if inject else NSA_IDX_COMPUTE, _ptr(workspace),
                             workspace.numel(), _stream_of(q)))
+    if idx is not None:
+        return out, idx
+    return out
+
+
+def decode_general(q, k_cache, v_cache, kc_cache, vc_cache, seqlens, gates, *, top_k: int, window: int,
+                   block: int = 64, select_block=None, stride=None, gate_layer=None, scale: float = 0.0,
+                   out=None, out_dtype=None, idx=None, inject: bool = False, return_idx: bool = False,
+                   workspace=None):
+    """NSA decode with the general geometry (nsa_fwd_decode_general): the
+    block caches hold the representations of the blocks [i*stride,
+    i*stride + block) of each sequence; selection blocks of select_block
+    tokens; a gate layer (gate_w [Hq,D,3], gate_b [Hq,3]), with which gates
+    may be None."""
+    tensors = [q, k_cache, v_cache, kc_cache, vc_cache] + ([gates] if gates is not None else [])
+    _require_gpu(*tensors)
+    B, Hq, D = q.shape
+    G = k_cache.shape[1]
+    if seqlens.dtype != torch.int32 or not seqlens.is_cuda or seqlens.shape != (B,):
+        raise ValueError("seqlens must be an int32 device tensor of shape [B]")
+    if gates is None and gate_layer is None:
+        raise ValueError("gates are needed unless a gate layer computes them")
+    for t in list(gate_layer or ()):
+        if t.dtype != q.dtype:
+            raise TypeError("the gate layer must share the inputs' dtype")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if inject and idx is None:
+        raise ValueError("inject=True needs idx")
+    if idx is None and return_idx:
+        idx = torch.empty((B, G, top_k), dtype=torch.int32, device=q.device)
+    if idx is not None and (idx.dtype != torch.int32 or not idx.is_contiguous()
+                            or tuple(idx.shape) != (B, G, top_k)):
+        raise ValueError("idx must be a contiguous int32 [B, G, top_k] tensor")
+    desc = decode_desc(q, k_cache, v_cache, kc_cache, vc_cache, gates if gates is not None else q[..., :3], out)
+    params = make_params(top_k, window, block, select_block, scale)
+    gen = make_general(block if stride is None else stride, None, gate_layer)
+    L_ = lib()
+    nbytes = ctypes.c_size_t()
+    check(L_.nsa_decode_general_workspace_bytes(ctypes.byref(desc), ctypes.byref(params), ctypes.byref(gen),
+                                                ctypes.byref(nbytes)))
+    if workspace is None or workspace.numel() < nbytes.value:
+        workspace = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=q.device)
+    check(L_.nsa_fwd_decode_general(ctypes.byref(desc), ctypes.byref(params), ctypes.byref(gen), _ptr(q),
+                                    _ptr(k_cache), _ptr(v_cache), _ptr(kc_cache), _ptr(vc_cache), _ptr(seqlens),
+                                    _ptr(gates), _ptr(out), _ptr(idx),
+                                    NSA_IDX_INJECT if inject else NSA_IDX_COMPUTE, _ptr(workspace),
+                                    workspace.numel(), _stream_of(q)))
     if idx is not None:
         return out, idx
     return out

@@ -165,6 +165,43 @@ def test_general_entry_checks(L):
                                   n.value, None) == UNS
 
 
+def test_general_decode_entry_checks(L):
+    # blocks of 32 with stride 16 over a 4096-token cache: 255 compressed blocks
+    d, p = ddesc(B=2, Lm=4096, nmax=255), nsa.make_params(16, 512, block=32, select_block=64)
+    n = ctypes.c_size_t()
+    ws = lambda g: L.nsa_decode_general_workspace_bytes(ctypes.byref(d), ctypes.byref(p), g, ctypes.byref(n))
+    g = nsa.NsaGeneral()
+    g.compress_stride = 16
+    assert ws(ctypes.byref(g)) == OK
+    plain = n.value
+    d.max_blocks = 254                            # fewer cache rows than compressed blocks
+    assert ws(ctypes.byref(g)) == INV
+    d.max_blocks = 255
+    for bad in (0, 33):                           # stride outside [1, compress_block_size]
+        g.compress_stride = bad
+        assert ws(ctypes.byref(g)) == INV
+    g.compress_stride = 16
+    g.gate_w = FAKE                               # gate layer without its bias
+    assert ws(ctypes.byref(g)) == INV
+    g.gate_b = FAKE
+    assert ws(ctypes.byref(g)) == OK
+    assert n.value == plain + 2 * 64 * 3 * 4       # + the fp32 gates of 2 sequences x 64 heads
+    # with a gate layer the gates argument may be NULL; the workspace must cover the gates
+    call = lambda gates, nb: L.nsa_fwd_decode_general(ctypes.byref(d), ctypes.byref(p), ctypes.byref(g), FAKE,
+                                                      FAKE, FAKE, FAKE, FAKE, FAKE, gates, FAKE, None, 0, FAKE,
+                                                      nb, None)
+    assert call(None, n.value - 1) == WS
+    g.gate_w = g.gate_b = None
+    assert call(None, n.value) == INV             # no gate layer: gates are required
+    # the plain decode still needs blocks and selection blocks of 64
+    assert L.nsa_decode_workspace_bytes(ctypes.byref(d), ctypes.byref(p), ctypes.byref(n)) == UNS
+    # selection blocks below the compressed blocks, or top_k * select_block above 4096
+    for bad in (nsa.make_params(16, 512, block=64, select_block=32), nsa.make_params(64, 512, block=32,
+                                                                                      select_block=128)):
+        assert L.nsa_decode_general_workspace_bytes(ctypes.byref(d), ctypes.byref(bad), None,
+                                                    ctypes.byref(n)) == UNS
+
+
 def test_prefill_pointer_and_workspace_checks(L):
     d, p = pdesc(Lq=4096), nsa.make_params(16, 512)
     _, need = ws_prefill(L, d, p)
