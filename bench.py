@@ -61,21 +61,25 @@ def prefill_flops(cfg):
     return {"cmp": cmp * per_pair, "slc": slc * per_pair, "win": win * per_pair}
 
 
-def decode_unique_bytes(cfg, idx: np.ndarray, lens: np.ndarray) -> int:
-    """Bytes the decode step must touch: block-mean cache, selected blocks
-    (tokens inside the window counted once), window, q, gates, out, idx."""
+def decode_unique_bytes(cfg, idx: np.ndarray, lens: np.ndarray, cl=None, cd=None, ls=None) -> int:
+    """Bytes the decode step must touch: block cache (the visible compressed
+    blocks [i*cd, i*cd + cl)), selected blocks of ls tokens (tokens inside the
+    window counted once), window, q, gates, out, idx."""
+    cl = cl or cfg.block
+    cd = cd or cl
+    ls = ls or cfg.block
     D, G, Hq, el = cfg.head_dim, cfg.n_kv_heads, cfg.n_q_heads, 2
     total = 0
     for b in range(cfg.batch):
         s = int(lens[b])
         t = s - 1
         wlo = max(0, s - cfg.window)
-        nvis = s // cfg.block
+        nvis = (s - cl) // cd + 1 if s >= cl else 0
         for g in range(G):
             toks = set(range(wlo, s))
             for j in idx[b, g]:
-                if 0 <= j <= t // cfg.block:
-                    toks.update(range(j * cfg.block, min(j * cfg.block + cfg.block, s)))
+                if 0 <= j <= t // ls:
+                    toks.update(range(j * ls, min(j * ls + ls, s)))
             total += (nvis * D * 2 + len(toks) * D * 2) * el
         total += Hq * D * el * 2 + Hq * 3 * el + G * cfg.top_k * 4
     return total
@@ -571,7 +575,7 @@ def bench_dsa(cfg, steps, warmup, torch, inputs, nsa):
                         for kn in ("k_dsa_index", "k_dsa_topk_fast", "k_dsa_topk_exact", "k_dsa_attn")}}
 
 
-def bench_decode(cfg, steps, warmup, torch, inputs, nsa):
+def bench_decode(cfg, steps, warmup, torch, inputs, nsa, general=False):
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
     raw = inputs.make_decode_inputs(cfg)
@@ -615,10 +619,77 @@ def bench_decode(cfg, steps, warmup, torch, inputs, nsa):
     ms = float(np.median(step_ms))
     gbps = ubytes / (ms * 1e-3) / 1e9
     log(f"[bench] decode {cfg.name}: {ms * 1e3:.1f} us/step, {gbps:.0f} GB/s")
-    return {"workload": cfg.name, "ms_per_step": ms, "step_ms_samples": step_ms,
-            "sequences_per_s": cfg.batch / (ms * 1e-3), "unique_bytes_per_step": ubytes,
-            "achieved_GBps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS, "kernels_ms": stage_ms,
-            "traffic": committed_traffic("k_dec", cfg.name), "cache_flush": "1 GiB read between steps"}
+    res = {"workload": cfg.name, "ms_per_step": ms, "step_ms_samples": step_ms,
+           "sequences_per_s": cfg.batch / (ms * 1e-3), "unique_bytes_per_step": ubytes,
+           "achieved_GBps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS, "kernels_ms": stage_ms,
+           "traffic": committed_traffic("k_dec", cfg.name), "cache_flush": "1 GiB read between steps"}
+    if general:
+        res["general"] = bench_decode_general(cfg, q, kc, vc, lens, g, flush, raw["seqlens"], steps, torch, nsa)
+    return res
+
+
+GENERAL = {"block": 32, "stride": 16, "select_block": 64}   # the overlapping geometry the general legs time
+
+
+def bench_decode_general(cfg, q, kc, vc, lens, g, flush, seqlens, steps, torch, nsa):
+    """The decode with the general geometry (nsa_fwd_decode_general) on the
+    same caches: blocks of 32 tokens at stride 16 (their means built once with
+    torch, outside the timing), selection blocks of 64; HIP events around
+    each call after the 1 GiB flush."""
+    l, d, ls = GENERAL["block"], GENERAL["stride"], GENERAL["select_block"]
+
+    def block_means(c):   # blocks of 2d tokens at stride d: the average of two neighbouring d-token means
+        B, G, L, D = c.shape
+        m = c.view(B, G, L // d, d, D).float().mean(3)
+        return ((m[:, :, :-1] + m[:, :, 1:]) * 0.5).to(torch.bfloat16).contiguous()
+
+    assert l == 2 * d and cfg.max_seqlen % d == 0
+    kb, vb = block_means(kc), block_means(vc)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    idx = torch.empty((cfg.batch, cfg.n_kv_heads, cfg.top_k), dtype=torch.int32, device=q.device)
+    call = lambda: nsa.decode_general(q, kc, vc, kb, vb, lens, g, top_k=cfg.top_k, window=cfg.window, block=l,
+                                      select_block=ls, stride=d, out=out, idx=idx)
+    for _ in range(3):
+        call()
+    times = []
+    for _ in range(steps):
+        flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    ubytes = decode_unique_bytes(cfg, idx.cpu().numpy(), seqlens, cl=l, cd=d, ls=ls)
+    gbps = ubytes / (ms * 1e-3) / 1e9
+    log(f"[bench] decode {cfg.name}, general geometry {GENERAL}: {ms * 1e3:.1f} us/step, {gbps:.0f} GB/s")
+    return {"entry": "nsa_fwd_decode_general", "geometry": dict(GENERAL), "ms_per_step": ms,
+            "unique_bytes_per_step": ubytes, "achieved_GBps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS,
+            "timing": "HIP events around each call (launch included), 1 GiB read between calls"}
+
+
+def bench_prefill_general(cfg, raw, steps, torch, nsa):
+    """The prefill with the general geometry (nsa_fwd_prefill_general) on the
+    main config's inputs: blocks of 32 tokens at stride 16 (twice the
+    compressed blocks, overlapping), selection blocks of 64, block means."""
+    dev = torch.device("cuda:0")
+    l, d, ls = GENERAL["block"], GENERAL["stride"], GENERAL["select_block"]
+    up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v, g = (up(raw[n]) for n in ("q", "k", "v", "gates"))
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    call = lambda: nsa.prefill_general(q, k, v, g, top_k=cfg.top_k, window=cfg.window, block=l, select_block=ls,
+                                       stride=d, out=out)
+    call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    log(f"[bench] prefill {cfg.name}, general geometry {GENERAL}: {ms:.3f} ms/step")
+    return {"entry": "nsa_fwd_prefill_general", "geometry": dict(GENERAL), "ms_per_step": ms,
+            "tokens_per_s": cfg.batch * cfg.seqlen / (ms * 1e-3)}
 
 
 def main():
@@ -641,6 +712,8 @@ def main():
     ap.add_argument("--dsa", default="dsa64k", help="token-level sparse attention workload also timed ('' to skip)")
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-general", action="store_true",
+                    help="skip the prefill and decode with the general geometry (blocks of 32 at stride 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -752,8 +825,11 @@ def main():
         result["backward"] = bench_backward(cfg, raw, max(1, min(args.steps, 5)), torch, nsa)
     if args.dsa:
         result["dsa"] = bench_dsa(inputs.DSA_CONFIGS[args.dsa], max(1, min(args.steps, 5)), 1, torch, inputs, nsa)
+    if not args.no_general:
+        result["general_prefill"] = bench_prefill_general(cfg, raw, max(1, min(args.steps, 5)), torch, nsa)
     if not args.no_decode:
-        result["decode"] = bench_decode(inputs.CONFIGS["d64k"], args.decode_steps, 3, torch, inputs, nsa)
+        result["decode"] = bench_decode(inputs.CONFIGS["d64k"], args.decode_steps, 3, torch, inputs, nsa,
+                                        general=not args.no_general)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         up = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
