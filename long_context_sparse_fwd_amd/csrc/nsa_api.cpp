@@ -148,8 +148,8 @@ nsa_status_t check_ptr(const char* name, const void* p, bool need16) {
 // ------------------------------------------------------------------ prefill
 
 struct PrefillPlan {
-  int Nb, Nc, NcT, cmp_waves, cmp_lo_lds, cmp_tiles, sel_tiles, sel_pf;
-  size_t off_kt, off_vt, off_kct, off_kclt, off_vct, off_idx, off_part, off_gates, total;
+  int Nb, Nc, NcT, cmp_waves, cmp_lo_lds, cmp_gsc, cmp_tiles, sel_tiles, sel_pf;
+  size_t off_kt, off_vt, off_kct, off_kclt, off_vct, off_idx, off_part, off_gates, off_cmp_sc, total;
 };
 
 // q_offset: the queries are positions [q_offset, seqlen) (0 for a whole
@@ -180,22 +180,22 @@ nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, Pr
   pl->NcT = (pl->Nc + 63) / 64;
   if (B * G * static_cast<int64_t>(pl->NcT) * 64 > INT32_MAX)
     return fail(NSA_ERR_UNSUPPORTED, "problem too large for 32-bit work indexing");
-  // the widest compressed-kernel workgroup whose LDS fits; at 8 waves the
-  // low parts of the K means go through LDS as well when that still fits
-  pl->cmp_waves = 0;
+  // the compressed kernel runs 8 waves per workgroup (its two-segment
+  // schedule); the low parts of the K means go through LDS as well when that
+  // still fits, and the tokens' block-score rows stay in LDS when they fit,
+  // else in the workspace
+  pl->cmp_waves = 8;
   pl->cmp_lo_lds = 0;
+  pl->cmp_gsc = 1;
   const bool bf16 = d->in_dtype == NSA_BF16;
-  for (int w = 8; w >= 1 && pl->cmp_waves == 0; w /= 2)
-    for (int lol = (w == 8 && bf16) ? 1 : 0; lol >= 0; --lol)
-      if (nsa::cmpwin_lds_bytes(w, pl->NcT, static_cast<int>(D), bf16, lol != 0) <=
+  for (int gsc = 0; gsc <= 1 && pl->cmp_gsc == 1; ++gsc)
+    for (int lol = bf16 ? 1 : 0; lol >= 0; --lol)
+      if (nsa::cmpwin_lds_bytes(8, gsc ? 0 : pl->NcT, static_cast<int>(D), bf16, lol != 0) <=
           static_cast<size_t>(nsa::kMaxLds)) {
-        pl->cmp_waves = w;
         pl->cmp_lo_lds = lol;
+        pl->cmp_gsc = gsc;
         break;
       }
-  if (pl->cmp_waves == 0)
-    return fail(NSA_ERR_UNSUPPORTED, "seqlen %lld needs more LDS for block scores than a CU has",
-                static_cast<long long>(L));
   const size_t sel_stat = nsa::sel_static_lds_bytes(static_cast<int>(D), d->in_dtype == NSA_BF16);
   pl->sel_pf = nsa::sel_lds_bytes(pl->Nb, static_cast<int>(D), d->in_dtype == NSA_BF16, true) + sel_stat <=
                        static_cast<size_t>(nsa::kMaxLds)
@@ -232,6 +232,9 @@ nsa_status_t plan_prefill(const nsa_prefill_desc_t* d, const nsa_params_t* p, Pr
   // gate layer: its fp32 gates of every query row
   pl->off_gates = off;
   if (geo.gate_layer()) off = align_up(off + static_cast<size_t>(B * L * d->n_q_heads) * 3 * sizeof(float));
+  // block-score rows of the compressed kernel when they do not fit LDS
+  pl->off_cmp_sc = off;
+  if (pl->cmp_gsc) off = align_up(off + static_cast<size_t>(B * G) * (L + 2) * pl->NcT * 64 * sizeof(float));
   pl->total = off;
   return NSA_OK;
 }
@@ -539,6 +542,7 @@ static nsa_status_t prefill_impl(const nsa_prefill_desc_t* desc, const nsa_param
   a.kct = ws + pl.off_kct;
   a.kclt = ws + pl.off_kclt;
   a.vct = ws + pl.off_vct;
+  a.cmp_sc = pl.cmp_gsc ? reinterpret_cast<float*>(ws + pl.off_cmp_sc) : nullptr;
   for (int i = 0; i < 3; ++i) {
     a.qs[i] = desc->q_stride[i];
     a.ks[i] = desc->k_stride[i];

@@ -81,6 +81,10 @@ struct PrefillArgs {
   // [B][Lq][Hq] (-inf for no usable block), for the backward pass.
   void* save_o;
   float* save_lse;
+  // Compressed kernel: each token's block-score row in the workspace,
+  // [B][G][Lq + 2][NcT * 64] (two spare rows for the tokens past the last
+  // query row), when the rows of 8 waves do not fit LDS; null: in LDS.
+  float* cmp_sc;
 };
 
 struct DecodeArgs {

@@ -416,7 +416,7 @@ struct TileStager {
 
 // ------------------------------------------------------------------ k_cmpwin
 
-template <class T, class O, int D, int NW, bool LOL>
+template <class T, class O, int D, int NW, bool LOL, bool GSC>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_cmpwin(PrefillArgs a) {
   using S = typename T::storage;
   using SO = typename O::storage;
@@ -829,7 +829,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // selection; they are then unused). The low parts of the means enter the
   // products only where a query sees fewer than kLoMinBlocks blocks or the
   // geometry is general.
-  float* sc = scb + static_cast<size_t>(wave) * TPW * NcPad;
+  // the wave's two score rows: in LDS, or (GSC) the rows of its tokens in the
+  // workspace (a wave past the last query row writes the spare rows)
+  float* sc;
+  if constexpr (GSC)
+    sc = a.cmp_sc + ((static_cast<int64_t>(b) * a.G + g) * (a.Lq + 2) + min(tw - t0q, a.Lq)) * NcPad;
+  else
+    sc = scb + static_cast<size_t>(wave) * TPW * NcPad;
   if (nch > 0) {
     f32x4 negl[TPW];
 #pragma unroll
@@ -928,6 +934,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // ---- selection
   if (!a.inject) {
     wave_lds_sync();
+    // score rows in the workspace: the wave's stores complete before its
+    // lanes read each other's entries (the CU's L1 serves the reads)
+    if constexpr (GSC) __threadfence_block();
     uint64_t* surv = survb + static_cast<size_t>(wave) * kSurvCap;
     int* selb = selbb + wave * 64;
 #pragma unroll 1
@@ -936,7 +945,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (t >= Le) break;
       int32_t* row = a.idx + ((static_cast<int64_t>(b) * a.Lq + (t - t0q)) * a.G + g) * a.n;
       const int own = t / a.ls;
-      if (a.sel_map) map_selection_scores(a, sc + qt * NcPad, own, nvis[qt], lane);
+      if (a.sel_map) {
+        map_selection_scores(a, sc + qt * NcPad, own, nvis[qt], lane);
+        if constexpr (GSC) __threadfence_block();
+      }
       topk_wave(sc + qt * NcPad, own, a.n, row, surv, selb, lane);
     }
   }
@@ -1292,13 +1304,14 @@ static hipError_t record(hipEvent_t* ev, int i, hipStream_t st) {
 }
 
 template <class T, class O, int D>
+// The 8-wave form (its two-segment schedule); score rows in LDS, or in the
+// workspace when 8 waves' rows do not fit.
 static const void* cmpwin_kernel(const PrefillArgs& a) {
-  if (a.cmp_waves == 8)
-    return a.cmp_lo_lds ? reinterpret_cast<const void*>(&k_cmpwin<T, O, D, 8, true>)
-                        : reinterpret_cast<const void*>(&k_cmpwin<T, O, D, 8, false>);
-  if (a.cmp_waves == 4) return reinterpret_cast<const void*>(&k_cmpwin<T, O, D, 4, false>);
-  if (a.cmp_waves == 2) return reinterpret_cast<const void*>(&k_cmpwin<T, O, D, 2, false>);
-  return reinterpret_cast<const void*>(&k_cmpwin<T, O, D, 1, false>);
+  if (a.cmp_sc != nullptr)
+    return a.cmp_lo_lds ? reinterpret_cast<const void*>(&k_cmpwin<T, O, D, 8, true, true>)
+                        : reinterpret_cast<const void*>(&k_cmpwin<T, O, D, 8, false, true>);
+  return a.cmp_lo_lds ? reinterpret_cast<const void*>(&k_cmpwin<T, O, D, 8, true, false>)
+                      : reinterpret_cast<const void*>(&k_cmpwin<T, O, D, 8, false, false>);
 }
 
 static hipError_t launch_one(const void* fn, dim3 grid, dim3 block, size_t lds, hipStream_t st,
@@ -1312,7 +1325,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st, hipEven
   constexpr bool kBf16 = sizeof(typename T::storage) == 2;
   // every kernel attribute is set before the first launch
   const void* cmp_fn = cmpwin_kernel<T, O, D>(a);
-  const size_t cmp_lds = cmpwin_lds_bytes(a.cmp_waves, a.NcT, D, kBf16, a.cmp_lo_lds != 0);
+  const size_t cmp_lds = cmpwin_lds_bytes(a.cmp_waves, a.cmp_sc != nullptr ? 0 : a.NcT, D, kBf16, a.cmp_lo_lds != 0);
   const void* sel_fn =
       a.save_o != nullptr
           ? (a.sel_pf ? reinterpret_cast<const void*>(&k_sel<T, O, D, true, true>)
