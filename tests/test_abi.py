@@ -202,6 +202,19 @@ def test_general_decode_entry_checks(L):
                                                     ctypes.byref(n)) == UNS
 
 
+def test_prefill_score_rows_move_to_the_workspace_past_what_lds_holds(L):
+    # The compressed kernel keeps 8 waves x 2 tokens of block-score rows (NcT * 64
+    # floats each) in LDS next to its 64 KiB staging while that fits: up to 24
+    # chunks of 64 blocks (98304 tokens). One token more, and the rows of every
+    # query row ([B][G][L + 2][NcT * 64] floats) go to the workspace.
+    p = nsa.make_params(16, 512)
+    st0, below = ws_prefill(L, pdesc(Lq=98304), p)
+    st1, above = ws_prefill(L, pdesc(Lq=98368), p)
+    assert st0 == OK and st1 == OK
+    rows = 4 * (98368 + 2) * 25 * 64 * 4
+    assert 0 <= above - below - rows < 16 << 20   # the rest grows by 64 tokens' worth
+
+
 def test_prefill_pointer_and_workspace_checks(L):
     d, p = pdesc(Lq=4096), nsa.make_params(16, 512)
     _, need = ws_prefill(L, d, p)
